@@ -1,0 +1,140 @@
+/*
+ * sgemm_oracle.c -- plain CPU reference for row-major single-precision GEMM.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the oracle that the GPU library is
+ * checked against.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark load it.  It shares no code, header or constant with the
+ * GPU library, and the GPU library never calls it.
+ *
+ * What it computes (the plain definition, nothing faster):
+ *
+ *   C = alpha * (A * B) + beta * C0
+ *
+ * with A an M x K matrix, B a K x N matrix and C0, C M x N matrices, all stored
+ * row-major ("Learn: Optimizing GEMM", section 3 "Rung 0 -- Naive (recap)": the
+ * listing's header comment states the operation and the three row-major shapes;
+ * "How a Matmul Kernel Gets Fast", section 1 "The problem, and what cuBLAS is":
+ * the two scalars scale the product and the existing C).  Element (i, j) is one
+ * length-K dot product of row i of A with column j of B ("How a Matmul Kernel
+ * Gets Fast", section 8 "Kernel 4: 1D blocktiling", which writes C[i][j] as the
+ * sum over k of A[i][k] * B[k][j]).  The pages verify a GPU result against a
+ * float64 dot product computed on the CPU ("Writing a Fast Matmul in CUDA, Step
+ * by Step", section "Step 1: the problem and the yardstick"), so every sum here
+ * is accumulated in double precision.
+ *
+ * Element addressing follows the row-major rule "base + row * stride + col"
+ * ("CUDA Matrix Multiplication Optimization: From Naive to Near-cuBLAS", section
+ * "Why Naive is Cache-Hostile"), with the stride of each matrix passed in
+ * explicitly (lda, ldb, ldc) instead of being fixed to K and N.
+ *
+ * Readings where the pages are silent (each is listed in the design notes):
+ *   - beta == 0: C0 is not read at all (so an uninitialised or NaN-filled C0
+ *     gives a finite result), the usual BLAS convention.
+ *   - alpha == 0 or K == 0: the product term is exactly zero and A, B are not
+ *     read.
+ *   - Per element the products are added in the order k = 0, 1, ..., K-1.
+ *     The product of two floats converted to double is exact (24 + 24 < 53
+ *     significand bits), so whether the compiler fuses multiply and add does
+ *     not change the accumulated value.
+ *
+ * Alongside C the oracle returns |A|*|B| (the sum over k of |A[i][k]*B[k][j]|),
+ * which scales the element-wise error bound that real-valued results are held
+ * to.
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <omp.h>
+
+/* Number of OpenMP threads the full-matrix routine will use. */
+int oracle_num_threads(void) { return omp_get_max_threads(); }
+
+/*
+ * Full product.  Cref and absab (absab may be NULL) are M x N row-major double
+ * arrays with row stride N.  Returns 0 on success, -1 if scratch memory could
+ * not be allocated, 1 on a negative size.
+ */
+int oracle_sgemm_f64(int M, int N, int K, float alpha,
+                     const float *A, long lda,
+                     const float *B, long ldb,
+                     float beta, const float *C0, long ldc,
+                     double *Cref, double *absab)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (M == 0 || N == 0) return 0;
+    const int use_product = (alpha != 0.0f) && (K > 0);
+    const double a_s = (double)alpha;
+    const double b_s = (double)beta;
+    int failed = 0;
+
+#pragma omp parallel
+    {
+        double *acc = (double *)malloc(sizeof(double) * (size_t)N);
+        double *aac = (double *)malloc(sizeof(double) * (size_t)N);
+        if (acc == NULL || aac == NULL) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < M; ++i) {
+            if (acc == NULL || aac == NULL) continue;
+            for (int j = 0; j < N; ++j) { acc[j] = 0.0; aac[j] = 0.0; }
+            if (use_product) {
+                for (int k = 0; k < K; ++k) {
+                    const double a = (double)A[(long)i * lda + k];
+                    const float *brow = B + (long)k * ldb;
+                    for (int j = 0; j < N; ++j) {
+                        const double p = a * (double)brow[j];
+                        acc[j] += p;
+                        aac[j] += fabs(p);
+                    }
+                }
+            }
+            for (int j = 0; j < N; ++j) {
+                const double prod = use_product ? a_s * acc[j] : 0.0;
+                const double old = (beta == 0.0f) ? 0.0 : b_s * (double)C0[(long)i * ldc + j];
+                Cref[(long)i * N + j] = prod + old;
+                if (absab != NULL) absab[(long)i * N + j] = use_product ? aac[j] : 0.0;
+            }
+        }
+        free(acc);
+        free(aac);
+    }
+    return failed ? -1 : 0;
+}
+
+/*
+ * Selected entries only: for t in [0, n) computes element (rows[t], cols[t]) of
+ * the same product, with the same k order, into out[t] (and absab[t] when
+ * absab is not NULL).  Used to check results of products too large to form in
+ * full on the CPU.  Returns 1 if an index is out of range.
+ */
+int oracle_sgemm_f64_entries(int M, int N, int K, float alpha,
+                             const float *A, long lda,
+                             const float *B, long ldb,
+                             float beta, const float *C0, long ldc,
+                             long n, const long *rows, const long *cols,
+                             double *out, double *absab)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    for (long t = 0; t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return 1;
+    const int use_product = (alpha != 0.0f) && (K > 0);
+
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < n; ++t) {
+        const long i = rows[t], j = cols[t];
+        double acc = 0.0, aac = 0.0;
+        if (use_product) {
+            for (int k = 0; k < K; ++k) {
+                const double p = (double)A[i * lda + k] * (double)B[(long)k * ldb + j];
+                acc += p;
+                aac += fabs(p);
+            }
+        }
+        const double prod = use_product ? (double)alpha * acc : 0.0;
+        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];
+        out[t] = prod + old;
+        if (absab != NULL) absab[t] = use_product ? aac : 0.0;
+    }
+    return 0;
+}

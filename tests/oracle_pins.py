@@ -1,0 +1,241 @@
+"""Pins for the CPU oracle: checks against facts fixed outside the oracle itself.
+
+Each pin takes an object ``o`` with the oracle API (``sgemm_ref``,
+``sgemm_ref_entries``) so that the same pins can be run against a copy of the
+oracle with a planted mistake, which at least one of them must catch.
+
+What fixes each expected value (none is produced by the code under test):
+  * hand-worked products (tests/golden), worked out on paper;
+  * identity and permutation matrices: the product copies or permutes the other
+    operand exactly (every other term is an exact zero);
+  * (AB)^T = B^T A^T: a structural identity of the product;
+  * exact rational arithmetic (Python ``fractions``) on tiny shapes;
+  * integer matrices: numpy's int64 matmul is exact;
+  * rank-one integer factors: C_ij = u_i w_j (s . t) in closed form;
+  * all-ones operands: every entry equals K*alpha + beta*C0 exactly;
+  * alpha = 0 and beta = 0: the unused operands are not read (NaN stays out);
+  * the float64 library matmul on random inputs, to within float64 rounding;
+  * the standard deviation sqrt(K/9) of a dot product of uniform[-1,1) vectors,
+    which gives the "typical size 21" of entries at n = 4096 that "Writing a
+    Fast Matmul in CUDA, Step by Step" reports in its "Step 1" section.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+
+from golden_io import load_cases
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _uniform(rng, shape):
+    return (rng.random(shape, dtype=np.float32) * 2 - 1).astype(np.float32)
+
+
+def _bits(x):
+    return np.asarray(x, dtype=np.float64).view(np.uint64)
+
+
+def pin_golden(o):
+    for fname in ("hand_2x2.txt", "hand_3x3.txt"):
+        for c in load_cases(fname):
+            Cref, _ = o.sgemm_ref(c["A"], c["B"], c["alpha"], c["beta"], c["C0"])
+            assert np.array_equal(Cref, c["C"]), (fname, c["name"], Cref, c["C"])
+
+
+def pin_identity(o):
+    rng = _rng(1)
+    for (m, k) in [(5, 7), (13, 4), (1, 9)]:
+        A = _uniform(rng, (m, k))
+        I = np.eye(k, dtype=np.float32)
+        Cref, _ = o.sgemm_ref(A, I)
+        assert np.array_equal(Cref, A.astype(np.float64)), "A*I != A"
+        Il = np.eye(m, dtype=np.float32)
+        Cref, _ = o.sgemm_ref(Il, A)
+        assert np.array_equal(Cref, A.astype(np.float64)), "I*A != A"
+
+
+def pin_permutation(o):
+    rng = _rng(2)
+    K, N = 9, 6
+    B = _uniform(rng, (K, N))
+    perm = rng.permutation(K)
+    P = np.zeros((K, K), dtype=np.float32)
+    P[np.arange(K), perm] = 1.0          # (P B)[i] = B[perm[i]]
+    Cref, _ = o.sgemm_ref(P, B)
+    assert np.array_equal(Cref, B[perm].astype(np.float64)), "P*B row permutation"
+    permc = rng.permutation(N)
+    Q = np.zeros((N, N), dtype=np.float32)
+    Q[permc, np.arange(N)] = 1.0         # (B Q)[:, j] = B[:, permc[j]]
+    Cref, _ = o.sgemm_ref(B, Q)
+    assert np.array_equal(Cref, B[:, permc].astype(np.float64)), "B*Q column permutation"
+
+
+def pin_transpose(o):
+    rng = _rng(3)
+    M, N, K = 7, 5, 11
+    A = _uniform(rng, (M, K))
+    B = _uniform(rng, (K, N))
+    C1, _ = o.sgemm_ref(A, B)
+    C2, _ = o.sgemm_ref(np.ascontiguousarray(B.T), np.ascontiguousarray(A.T))
+    assert np.array_equal(_bits(C1.T), _bits(C2)), "(AB)^T != B^T A^T"
+
+
+def _exact(A, B, alpha, beta, C0):
+    M, K = A.shape
+    N = B.shape[1]
+    out = np.empty((M, N), dtype=object)
+    for i in range(M):
+        for j in range(N):
+            s = Fraction(0)
+            for k in range(K):
+                s += Fraction(float(A[i, k])) * Fraction(float(B[k, j]))
+            v = Fraction(float(np.float32(alpha))) * s
+            if np.float32(beta) != 0:
+                v += Fraction(float(np.float32(beta))) * Fraction(float(C0[i, j]))
+            out[i, j] = v
+    return out
+
+
+def pin_exact_rational(o):
+    rng = _rng(4)
+    shapes = [(0, 3, 2), (3, 0, 2), (2, 3, 0), (1, 1, 1), (2, 3, 4), (4, 1, 5),
+              (3, 5, 8), (8, 8, 3), (5, 7, 6)]
+    for (M, N, K) in shapes:
+        for (alpha, beta) in [(1.0, 0.0), (-0.75, 1.25), (3.0, -2.0)]:
+            A = _uniform(rng, (M, K))
+            B = _uniform(rng, (K, N))
+            C0 = _uniform(rng, (M, N))
+            Cref, absab = o.sgemm_ref(A, B, alpha, beta, C0)
+            ex = _exact(A, B, alpha, beta, C0)
+            for i in range(M):
+                for j in range(N):
+                    mag = abs(alpha) * sum(abs(float(A[i, k]) * float(B[k, j])) for k in range(K))
+                    mag += abs(beta) * abs(float(C0[i, j])) if beta != 0 else 0.0
+                    tol = (K + 3) * 2.0 ** -52 * mag
+                    err = abs(Fraction(float(Cref[i, j])) - ex[i, j])
+                    assert float(err) <= tol, ((M, N, K), (i, j), float(err), tol)
+
+
+def pin_integer_exact(o):
+    rng = _rng(5)
+    M, N, K = 19, 23, 37
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    C0 = rng.integers(-9, 10, (M, N)).astype(np.float32)
+    Cref, absab = o.sgemm_ref(A, B, 1.5, -0.5, C0)
+    Ai, Bi, Ci = A.astype(np.int64), B.astype(np.int64), C0.astype(np.int64)
+    want = 1.5 * (Ai @ Bi).astype(np.float64) - 0.5 * Ci.astype(np.float64)
+    assert np.array_equal(Cref, want), "integer product not exact"
+    assert np.array_equal(absab, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64)), "|A||B|"
+
+
+def pin_rank_one(o):
+    M, N, K = 6, 9, 8
+    u = np.arange(1, M + 1, dtype=np.int64)            # rows of A scale
+    s = np.array([1, -2, 3, 0, 5, -1, 2, 4], dtype=np.int64)
+    t = np.array([2, 1, -1, 7, 1, 3, -2, 1], dtype=np.int64)
+    w = np.arange(-4, N - 4, dtype=np.int64)
+    A = np.outer(u, s).astype(np.float32)             # A[i][k] = u_i s_k
+    B = np.outer(t, w).astype(np.float32)             # B[k][j] = t_k w_j
+    Cref, _ = o.sgemm_ref(A, B)
+    st = int(np.dot(s, t))
+    want = np.outer(u, w).astype(np.float64) * st
+    assert np.array_equal(Cref, want), "rank-one closed form"
+
+
+def pin_all_ones(o):
+    M, N, K = 5, 4, 33
+    A = np.ones((M, K), np.float32)
+    B = np.ones((K, N), np.float32)
+    rng = _rng(6)
+    C0 = rng.integers(-5, 6, (M, N)).astype(np.float32)
+    Cref, _ = o.sgemm_ref(A, B, 1.5, -0.5, C0)
+    assert np.array_equal(Cref, K * 1.5 - 0.5 * C0.astype(np.float64)), "ones"
+
+
+def pin_scalar_special_cases(o):
+    rng = _rng(7)
+    M, N, K = 4, 6, 5
+    A = np.full((M, K), np.nan, np.float32)
+    B = np.full((K, N), np.nan, np.float32)
+    C0 = _uniform(rng, (M, N))
+    Cref, absab = o.sgemm_ref(A, B, 0.0, -0.5, C0)   # alpha = 0: A, B unread
+    assert np.array_equal(Cref, -0.5 * C0.astype(np.float64)), "alpha = 0"
+    assert np.array_equal(absab, np.zeros((M, N))), "alpha = 0 magnitude"
+    A = _uniform(rng, (M, K))
+    B = _uniform(rng, (K, N))
+    Cn = np.full((M, N), np.nan, np.float32)
+    Cref, _ = o.sgemm_ref(A, B, 1.0, 0.0, Cn)        # beta = 0: C0 unread
+    assert np.all(np.isfinite(Cref)), "beta = 0 read C0"
+    Cref0, _ = o.sgemm_ref(A[:, :0].copy(), B[:0, :].copy(), 2.0, 3.0, C0)  # K = 0
+    assert np.array_equal(Cref0, 3.0 * C0.astype(np.float64)), "K = 0"
+    Cz, _ = o.sgemm_ref(np.zeros((M, K), np.float32), B, 1.0, 1.0, C0)
+    assert np.array_equal(Cz, C0.astype(np.float64)), "A = 0, beta = 1 leaves C"
+
+
+def pin_library_matmul(o):
+    rng = _rng(8)
+    M, N, K = 37, 29, 301
+    A = _uniform(rng, (M, K))
+    B = _uniform(rng, (K, N))
+    C0 = _uniform(rng, (M, N))
+    alpha, beta = 1.25, -0.75
+    Cref, absab = o.sgemm_ref(A, B, alpha, beta, C0)
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    want = alpha * (A64 @ B64) + beta * C0.astype(np.float64)
+    mag = abs(alpha) * (np.abs(A64) @ np.abs(B64)) + abs(beta) * np.abs(C0)
+    assert np.all(np.abs(Cref - want) <= 2 * (K + 3) * 2.0 ** -53 * mag), "vs float64 matmul"
+    assert np.all(np.abs(absab - np.abs(A64) @ np.abs(B64))
+                  <= 2 * K * 2.0 ** -53 * (np.abs(A64) @ np.abs(B64))), "absab"
+
+
+def pin_leading_dims(o):
+    rng = _rng(9)
+    M, N, K = 9, 10, 12
+    Ap = np.full((M, K + 5), np.nan, np.float32)
+    Bp = np.full((K, N + 3), np.nan, np.float32)
+    Cp = np.full((M, N + 7), np.nan, np.float32)
+    Ap[:, :K] = _uniform(rng, (M, K))
+    Bp[:, :N] = _uniform(rng, (K, N))
+    Cp[:, :N] = _uniform(rng, (M, N))
+    A, B, C0 = Ap[:, :K], Bp[:, :N], Cp[:, :N]
+    C1, _ = o.sgemm_ref(A, B, 1.0, 2.0, C0)
+    C2, _ = o.sgemm_ref(A.copy(), B.copy(), 1.0, 2.0, C0.copy())
+    assert np.all(np.isfinite(C1)), "padding read"
+    assert np.array_equal(C1, C2), "row strides change the result"
+
+
+def pin_entries_match(o):
+    rng = _rng(10)
+    M, N, K = 17, 13, 40
+    A = _uniform(rng, (M, K))
+    B = _uniform(rng, (K, N))
+    C0 = _uniform(rng, (M, N))
+    Cref, absab = o.sgemm_ref(A, B, -1.5, 0.25, C0)
+    r = rng.integers(0, M, 50)
+    c = rng.integers(0, N, 50)
+    v, av = o.sgemm_ref_entries(A, B, r, c, -1.5, 0.25, C0)
+    assert np.array_equal(_bits(v), _bits(Cref[r, c])), "entries != full"
+    assert np.array_equal(_bits(av), _bits(absab[r, c])), "entry magnitudes"
+
+
+def pin_uniform_statistics(o):
+    rng = _rng(11)
+    M, N, K = 32, 64, 4096
+    A = _uniform(rng, (M, K))
+    B = _uniform(rng, (K, N))
+    Cref, _ = o.sgemm_ref(A, B)
+    sd = float(np.std(Cref))
+    want = (K / 9.0) ** 0.5                           # about 21.3 at K = 4096
+    assert abs(sd / want - 1) < 0.05, (sd, want)
+
+
+PINS = [pin_golden, pin_identity, pin_permutation, pin_transpose, pin_exact_rational,
+        pin_integer_exact, pin_rank_one, pin_all_ones, pin_scalar_special_cases,
+        pin_library_matmul, pin_leading_dims, pin_entries_match,
+        pin_uniform_statistics]

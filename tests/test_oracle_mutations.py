@@ -1,0 +1,48 @@
+"""Plant plausible mistakes in copies of the oracle source; the pins must catch each.
+
+Every mutation is compiled from a modified copy of the oracle's C source into a
+temporary directory (CPU only); the real oracle is untouched.
+"""
+import os
+
+import pytest
+
+from oracle_pins import PINS
+
+MUTATIONS = {
+    # name: list of (original text, replacement)
+    "drop_beta_term": [("const double old = (beta == 0.0f) ? 0.0 : b_s * (double)C0[(long)i * ldc + j];",
+                        "const double old = 0.0;")],
+    "sign_of_beta_term": [("Cref[(long)i * N + j] = prod + old;", "Cref[(long)i * N + j] = prod - old;")],
+    "ignore_alpha": [("const double prod = use_product ? a_s * acc[j] : 0.0;",
+                      "const double prod = use_product ? acc[j] : 0.0;")],
+    "drop_last_k": [("for (int k = 0; k < K; ++k) {\n                    const double a",
+                     "for (int k = 0; k < K - 1; ++k) {\n                    const double a")],
+    "reversed_k_in_A": [("const double a = (double)A[(long)i * lda + k];",
+                         "const double a = (double)A[(long)i * lda + (K - 1 - k)];")],
+    "float_accumulation": [("acc[j] += p;", "acc[j] = (float)(acc[j] + p);")],
+    "signed_magnitude": [("aac[j] += fabs(p);", "aac[j] += p;")],
+    "beta_one_ignored_when_alpha_zero": [("const int use_product = (alpha != 0.0f) && (K > 0);\n    const double a_s",
+                                          "const int use_product = 1;\n    const double a_s")],
+    "row_stride_of_A_is_K": [("const double a = (double)A[(long)i * lda + k];",
+                              "const double a = (double)A[(long)i * K + k];")],
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(oracle_mod, tmp_path, name):
+    src = open(oracle_mod.SOURCE_PATH).read()
+    for old, new in MUTATIONS[name]:
+        assert src.count(old) >= 1, f"mutation {name} no longer applies"
+        src = src.replace(old, new)
+    path = tmp_path / f"mut_{name}.c"
+    path.write_text(src)
+    lib = oracle_mod.compile_source(str(path), str(tmp_path / f"lib_{name}.so"))
+    mutant = oracle_mod.BoundOracle(lib)
+    caught = []
+    for pin in PINS:
+        try:
+            pin(mutant)
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutation {name}"
