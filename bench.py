@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark: FP32 SGEMM throughput on one MI355X.
+
+One step is one call of the library's C entry point ``sgemm_f32`` on the
+4096 x 4096 x 4096 workload (A, B, C standard normal, C = 1.5*A*B - 0.5*C, in
+place), with all inputs resident in device memory.  Prints one JSON line.
+
+Timing: W untimed warm-up steps, then K timed steps bracketed by device
+synchronisation; each launch is also bracketed by HIP events recorded on the
+stream the kernel runs on, which give the kernel's average duration for the
+roofline figure.  The FLOP count is 2*M*N*K per step (the scaling by alpha and
+beta is not counted, "How a Matmul Kernel Gets Fast", section 1 and "Writing a
+Fast Matmul in CUDA, Step by Step", section "Step 1").
+
+The CPU baseline is the float64 oracle timed on the host's cores on a bounded
+sample of the same product (its first rows), reported beside the GPU number.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
+PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector and matrix), datasheet
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_mfma.hip", "fp32_sgemm_amd/csrc/gemm_internal.hpp")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_large_square4096_ab.txt")
+
+
+# --- closed-form work and byte counts ------------------------------------------------
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """Multiply-adds counted as 2 FLOP each: 2*M*N*K."""
+    return 2 * M * N * K
+
+
+def gemm_min_bytes(M: int, N: int, K: int, reads_c: bool, elem: int = 4) -> int:
+    """Bytes that must cross HBM at least once: read A and B, write C, and read
+    C too when beta != 0 ("How a Matmul Kernel Gets Fast", section 2)."""
+    return elem * (M * K + K * N + M * N * (2 if reads_c else 1))
+
+
+def arithmetic_intensity(M: int, N: int, K: int, reads_c: bool) -> float:
+    return gemm_flops(M, N, K) / gemm_min_bytes(M, N, K, reads_c)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when that summary is missing or was taken on other kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.lstrip().startswith("#"):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# --- CPU baseline (the oracle on a bounded sample) -----------------------------------
+def cpu_baseline(A, B, C0, alpha, beta, target_s: float):
+    import oracle
+
+    M, K = A.shape
+    N = B.shape[1]
+    cores = oracle.num_threads()
+    rows = min(M, max(cores, 8))
+    t0 = time.perf_counter()
+    oracle.sgemm_ref(A[:rows], B, alpha, beta, None if C0 is None else C0[:rows])
+    dt = time.perf_counter() - t0
+    per_row = dt / rows
+    R = int(min(M, max(rows, target_s / max(per_row, 1e-9))))
+    R = max(cores, (R // cores) * cores) if R >= cores else R
+    R = min(R, M)
+    t0 = time.perf_counter()
+    oracle.sgemm_ref(A[:R], B, alpha, beta, None if C0 is None else C0[:R])
+    dt = time.perf_counter() - t0
+    return {
+        "value": round(gemm_flops(R, N, K) / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"rows 0..{R - 1} of the {M}x{N}x{K} product ({R * N} outputs, "
+                  f"float64 accumulation, {dt:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None, help="workload name (default: the 4096^3 headline)")
+    ap.add_argument("--variant", default="auto",
+                    help="auto | mfma_large | mfma_small | valu | skinny | mfma_scalar")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp32_sgemm_amd as sg
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    names = {sg.sgemm_f32_variant_name(i): i for i in range(sg.NUM_VARIANTS)}
+    if args.variant not in names:
+        sys.exit(f"unknown variant {args.variant}")
+    variant = names[args.variant]
+
+    w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    A, B, C0 = workloads.make_inputs(w)
+    dev = torch.device("cuda:0")
+    dA = torch.from_numpy(A).to(dev)
+    dB = torch.from_numpy(B).to(dev)
+    dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty(w.M, w.N, device=dev)
+    lda, ldb, ldc = w.K, w.N, w.N
+    stream = torch.cuda.Stream(dev)
+    s_handle = stream.cuda_stream
+    chosen = variant if variant else sg.sgemm_f32_select(w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                                         lda, dB.data_ptr(), ldb)
+
+    def step():
+        st = sg.sgemm_f32_variant(variant, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
+                                  dB.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
+        if st != 0:
+            raise RuntimeError(f"sgemm_f32 returned {st}")
+
+    torch.cuda.synchronize(dev)
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize(dev)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+
+    elapsed = t1 - t0
+    flops = gemm_flops(w.M, w.N, w.K)
+    value = flops * args.steps / elapsed / 1e12
+    kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    achieved = flops / kern_avg_s / 1e12
+
+    memory_bound = arithmetic_intensity(w.M, w.N, w.K, w.beta != 0) < PEAK_FP32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if memory_bound:
+        ach_gbs = gemm_min_bytes(w.M, w.N, w.K, w.beta != 0) / kern_avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(ach_gbs, 2), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4)}
+    else:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
+                    "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4)}
+    roofline["traffic"] = measured_traffic() if (w.name == workloads.HEADLINE and chosen == 1) else None
+    roofline["kernel_avg_ms"] = round(kern_avg_s * 1e3, 5)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "pct_of_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
+        "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
+                   "beta": w.beta, "inputs": w.dist, "variant": sg.sgemm_f32_variant_name(chosen),
+                   "parallelism": "single GPU"},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(A, B, C0, w.alpha, w.beta, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,127 @@
+"""Python binding of the gfx950 FP32 GEMM library (``libsgemm_f32.so``).
+
+Argument marshalling only: every step of ``C = alpha*A*B + beta*C`` runs in the
+library's HIP kernels.  The functions mirror the C interface in
+``include/sgemm_f32.h`` one to one (same names, same argument order, device
+pointers passed as integers, status codes returned unchanged).  ``sgemm``
+adds a convenience form over PyTorch tensors, which serve only as device memory
+and streams.
+
+Importing this package loads the library; if it has not been built the import
+fails with an error rather than falling back to any other implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import _build
+
+LIB_PATH = _build.LIB_PATH
+
+AUTO = 0
+MFMA_LARGE = 1
+MFMA_SMALL = 2
+VALU = 3
+SKINNY = 4
+MFMA_SCALAR = 5
+NUM_VARIANTS = 6
+
+ERR_VARIANT = 20
+ERR_NOT_APPLICABLE = 21
+ERR_TOO_LARGE = 22
+
+EXPORTED = ("sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select",
+            "sgemm_f32_variant_name", "sgemm_f32_version")
+
+
+class SgemmError(RuntimeError):
+    def __init__(self, status: int, what: str = "sgemm_f32"):
+        super().__init__(f"{what} returned status {status}")
+        self.status = status
+
+
+def _load_library():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(LIB_PATH)
+    i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+    gemm_args = [i, i, i, f, p, i, p, i, f, p, i, p]
+    lib.sgemm_f32.argtypes = gemm_args
+    lib.sgemm_f32.restype = i
+    lib.sgemm_f32_variant.argtypes = [i] + gemm_args
+    lib.sgemm_f32_variant.restype = i
+    lib.sgemm_f32_select.argtypes = [i, i, i, f, p, i, p, i]
+    lib.sgemm_f32_select.restype = i
+    lib.sgemm_f32_variant_name.argtypes = [i]
+    lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
+    lib.sgemm_f32_version.argtypes = []
+    lib.sgemm_f32_version.restype = i
+    return lib
+
+
+_lib = _load_library()
+
+
+def sgemm_f32(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int,
+              beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    """The C entry point: raw device pointers and a hipStream_t as integers."""
+    return _lib.sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_variant(variant: int, M: int, N: int, K: int, alpha: float, A: int, lda: int,
+                      B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    return _lib.sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_select(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int,
+                     ldb: int) -> int:
+    return _lib.sgemm_f32_select(M, N, K, alpha, A, lda, B, ldb)
+
+
+def sgemm_f32_variant_name(variant: int) -> str | None:
+    r = _lib.sgemm_f32_variant_name(variant)
+    return None if r is None else r.decode()
+
+
+def sgemm_f32_version() -> int:
+    return _lib.sgemm_f32_version()
+
+
+def _row_stride(t, name: str) -> int:
+    import torch
+
+    if t.dtype != torch.float32:
+        raise TypeError(f"{name} must be float32")
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit column stride")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    return max(int(t.stride(0)), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+
+
+def sgemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = AUTO,
+          stream=None) -> None:
+    """C = alpha*A@B + beta*C in place on device tensors (row-major views).
+
+    ``stream`` is a ``torch.cuda.Stream`` (default: the current stream).  The
+    call is asynchronous on that stream.  Raises ``SgemmError`` on a non-zero
+    status.
+    """
+    import torch
+
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
+    lda, ldb, ldc = _row_stride(A, "A"), _row_stride(B, "B"), _row_stride(C, "C")
+    if stream is None:
+        stream = torch.cuda.current_stream(C.device)
+    st = sgemm_f32_variant(variant, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+                           float(beta), C.data_ptr(), ldc, stream.cuda_stream)
+    if st != 0:
+        raise SgemmError(st)

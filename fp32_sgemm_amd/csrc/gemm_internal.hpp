@@ -1,0 +1,67 @@
+// Internal declarations shared by the kernels and the host dispatcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace sgemm {
+
+// Arguments of one C = alpha*A*B + beta*C call, row-major, strides in elements.
+struct GemmArgs {
+    int M, N, K;
+    float alpha, beta;
+    const float *A;
+    const float *B;
+    float *C;
+    int64_t lda, ldb, ldc;
+};
+
+// Launchers: each enqueues its kernel(s) on `stream` and returns the HIP error
+// of the launch.  Callers have validated the arguments, excluded M == 0,
+// N == 0, and routed alpha == 0 / K == 0 to launch_scale_c.
+hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream);
+hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream);
+hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
+hipError_t launch_skinny(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);
+
+// Tile counts that each launcher's grid uses (host side, for the size check).
+int64_t mfma_large_grid(int M, int N);
+int64_t mfma_small_grid(int M, int N);
+int64_t valu_grid(int M, int N);
+int64_t skinny_grid(int M, int N);
+
+// Largest M the skinny kernel handles.
+constexpr int kSkinnyMaxM = 16;
+
+// ---------------------------------------------------------------------------
+// Work-group to output-tile mapping.
+//
+// The hardware hands consecutive work-group ids to the 8 XCDs in turn
+// (id % 8 picks the XCD), and each XCD has its own L2.  The mapping first
+// renumbers ids so that each XCD receives one contiguous run of tile numbers,
+// then walks tile numbers in groups of `group_m` tile rows, column by column
+// inside a group, so that the work-groups resident on one XCD at the same time
+// cover a compact block of C and share the A row-panels and B column-panels
+// they stream through that XCD's L2.
+// ---------------------------------------------------------------------------
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
+                                              int group_m, int &tm, int &tn) {
+    const int total = tiles_m * tiles_n;
+    const int per = total / kNumXcd;
+    const int rem = total % kNumXcd;
+    const int xcd = bid % kNumXcd;
+    const int local = bid / kNumXcd;
+    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int in_group = group_m * tiles_n;
+    const int g = t / in_group;
+    const int first_m = g * group_m;
+    const int gm = (tiles_m - first_m) < group_m ? (tiles_m - first_m) : group_m;
+    const int r = t - g * in_group;
+    tm = first_m + r % gm;
+    tn = r / gm;
+}
+
+}  // namespace sgemm

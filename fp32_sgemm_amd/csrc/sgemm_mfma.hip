@@ -1,0 +1,255 @@
+// FP32 GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x2_f32).
+//
+// One work-group computes a BM x BN tile of C.  Its waves each own a WM x WN
+// sub-tile held as (WM/32) x (WN/32) blocks of 32x32 FP32 accumulators.  The
+// reduction dimension is walked in slices of BK: each slice of A (BM x BK) and
+// B (BK x BN) is staged once in LDS and then read by every wave of the group.
+// That is the shared-memory tiling of "Learn: Optimizing GEMM" section 5 and
+// "How a Matmul Kernel Gets Fast" section 6, the per-thread register tile of
+// their sections 6 and 9 (here the accumulator block of an MFMA), and the
+// warp-level tiling of "How a Matmul Kernel Gets Fast" section 13 (here one
+// 64-lane wave per sub-tile).
+//
+// Staging.  Global loads are 16-byte (global_load_dwordx4) where the operands
+// are 16-byte aligned with row strides that are multiples of 4, four-byte loads
+// otherwise.  The loads of slice t+1 are issued into registers before the
+// matrix-core work on slice t and written to the other of two LDS buffers after
+// it, so one barrier per slice separates producers from consumers (the double
+// buffering of "Writing a Fast Matmul in CUDA, Step by Step", section "Bank
+// conflicts and double buffering").
+//
+// LDS layouts.  A 32x32x2 MFMA takes, in lane l, A(l % 32, k) and B(k, l % 32)
+// for one of two k values picked by l / 32.  Inside a slice the kernel assigns
+// lane half h = l / 32 the k range [h*BK/2, (h+1)*BK/2), so a lane walks a
+// contiguous run of k for a fixed row of A.  A is therefore kept K-major in LDS
+// exactly as it sits in memory (row stride BK + 4 floats, so the 16-byte reads
+// of 16 consecutive rows fall in distinct banks) and read with ds_read_b128,
+// four k steps per read.  B is kept N-major as in memory and read with
+// ds_read_b32: the two half-waves read rows k and k + BK/2, and the second half
+// of the slice's rows is shifted by 32 floats so those two rows sit in opposite
+// halves of the bank space.
+//
+// Edges.  Tiles that cross the M or N edge and the last slice when K is not a
+// multiple of BK load through a guarded path that writes zeros for elements
+// outside the matrices (adding exact zeros changes no sum), and edge tiles mask
+// their stores.  The choice between guarded and plain loads is uniform across
+// the work-group, so no barrier sits under divergent control flow.
+//
+// Epilogue.  C = alpha * acc + beta * C, where C is read only when beta != 0.
+#include "gemm_internal.hpp"
+
+namespace sgemm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_>
+struct MfmaTile {
+    static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int WAVES_N = BN / WN;
+    static constexpr int NT = (BM / WM) * WAVES_N * 64;
+    static constexpr int MB = WM / 32;          // 32x32 accumulator blocks per wave, along M
+    static constexpr int NB = WN / 32;          // ... along N
+    static constexpr int HALF = BK / 2;         // k values per lane half in one slice
+    static constexpr int LDA_S = BK + 4;        // LDS row stride of the A slice (floats)
+    static constexpr int B_SHIFT = 32;          // offset of B rows [HALF, BK) in LDS
+    static constexpr int A_STAGE = BM * LDA_S;
+    static constexpr int B_STAGE = BK * BN + B_SHIFT;
+    static constexpr int STAGE = A_STAGE + B_STAGE;
+    static constexpr int A_VECS = BM * BK / 4 / NT;   // 4-float groups per thread per slice
+    static constexpr int B_VECS = BK * BN / 4 / NT;
+    static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
+    static_assert(BK % 8 == 0, "BK must be a multiple of 8");
+    static_assert((BM * BK) % (4 * NT) == 0 && (BK * BN) % (4 * NT) == 0, "load split");
+    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS");
+};
+
+// Loads one 4-float group of a row-major matrix at (row, col..col+3).  With
+// GUARD, elements with row >= rows or col + e >= cols read as zero and are not
+// accessed.  VEC selects one 16-byte load (requires 16-byte alignment of the
+// group) over four 4-byte loads.
+template <bool VEC, bool GUARD>
+__device__ __forceinline__ float4 load4(const float *__restrict__ base, int64_t ld,
+                                        int row, int col, int rows, int cols) {
+    const float *p = base + (int64_t)row * ld + col;
+    if (!GUARD) {
+        if (VEC) return *reinterpret_cast<const float4 *>(p);
+        return make_float4(p[0], p[1], p[2], p[3]);
+    }
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (row < rows) {
+        if (VEC && col + 3 < cols) {
+            v = *reinterpret_cast<const float4 *>(p);
+        } else {
+            if (col + 0 < cols) v.x = p[0];
+            if (col + 1 < cols) v.y = p[1];
+            if (col + 2 < cols) v.z = p[2];
+            if (col + 3 < cols) v.w = p[3];
+        }
+    }
+    return v;
+}
+
+template <class T, bool VEC, bool GUARD>
+__device__ __forceinline__ void load_slice(const GemmArgs &g, int m0, int n0, int k0, int tid,
+                                           float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
+#pragma unroll
+    for (int i = 0; i < T::A_VECS; ++i) {
+        const int q = tid + i * T::NT;
+        const int r = q / (T::BK / 4), c = (q % (T::BK / 4)) * 4;
+        ra[i] = load4<VEC, GUARD>(g.A, g.lda, m0 + r, k0 + c, g.M, g.K);
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_VECS; ++i) {
+        const int q = tid + i * T::NT;
+        const int r = q / (T::BN / 4), c = (q % (T::BN / 4)) * 4;
+        rb[i] = load4<VEC, GUARD>(g.B, g.ldb, k0 + r, n0 + c, g.K, g.N);
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void store_slice(float *stage, int tid,
+                                            const float4 (&ra)[T::A_VECS],
+                                            const float4 (&rb)[T::B_VECS]) {
+    float *As = stage;
+    float *Bs = stage + T::A_STAGE;
+#pragma unroll
+    for (int i = 0; i < T::A_VECS; ++i) {
+        const int q = tid + i * T::NT;
+        const int r = q / (T::BK / 4), c = (q % (T::BK / 4)) * 4;
+        *reinterpret_cast<float4 *>(As + r * T::LDA_S + c) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::B_VECS; ++i) {
+        const int q = tid + i * T::NT;
+        const int r = q / (T::BN / 4), c = (q % (T::BN / 4)) * 4;
+        *reinterpret_cast<float4 *>(Bs + r * T::BN + (r >= T::HALF ? T::B_SHIFT : 0) + c) = rb[i];
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn, int lane,
+                                              f32x16 (&acc)[T::MB][T::NB]) {
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const float *As = stage + (wm * T::WM + l32) * T::LDA_S + h * T::HALF;
+    const float *Bs = stage + T::A_STAGE + h * (T::HALF * T::BN + T::B_SHIFT) + wn * T::WN + l32;
+#pragma unroll
+    for (int c = 0; c < T::HALF / 4; ++c) {
+        float4 a[T::MB];
+        float b[T::NB][4];
+#pragma unroll
+        for (int ib = 0; ib < T::MB; ++ib)
+            a[ib] = *reinterpret_cast<const float4 *>(As + ib * 32 * T::LDA_S + 4 * c);
+#pragma unroll
+        for (int jb = 0; jb < T::NB; ++jb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                b[jb][e] = Bs[(4 * c + e) * T::BN + jb * 32];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < T::NB; ++jb) {
+                    const float av = e == 0 ? a[ib].x : e == 1 ? a[ib].y : e == 2 ? a[ib].z : a[ib].w;
+                    acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[jb][e], acc[ib][jb], 0, 0, 0);
+                }
+    }
+}
+
+template <class T, bool VEC>
+__global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n,
+                                                           int group_m) {
+    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / T::WAVES_N, wn = wave % T::WAVES_N;
+
+    f32x16 acc[T::MB][T::NB];
+#pragma unroll
+    for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < T::NB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[ib][jb][r] = 0.f;
+
+    const bool edge_mn = (m0 + T::BM > g.M) || (n0 + T::BN > g.N);
+    const int nk = (g.K + T::BK - 1) / T::BK;
+    float4 ra[T::A_VECS], rb[T::B_VECS];
+
+    if (edge_mn || T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, 0, tid, ra, rb);
+    else load_slice<T, VEC, false>(g, m0, n0, 0, tid, ra, rb);
+    store_slice<T>(smem, tid, ra, rb);
+    __syncthreads();
+
+    for (int t = 0; t < nk; ++t) {
+        const bool more = t + 1 < nk;
+        if (more) {
+            const int k0 = (t + 1) * T::BK;
+            if (edge_mn || k0 + T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, k0, tid, ra, rb);
+            else load_slice<T, VEC, false>(g, m0, n0, k0, tid, ra, rb);
+        }
+        compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
+        if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
+        __syncthreads();
+    }
+
+    // Epilogue.  Accumulator register r of a 32x32 block holds, in lane l,
+    // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < T::NB; ++jb) {
+            const int col = n0 + wn * T::WN + jb * 32 + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (edge_mn && (row >= g.M || col >= g.N)) continue;
+                float *p = g.C + (int64_t)row * g.ldc + col;
+                float v = alpha * acc[ib][jb][r];
+                if (beta != 0.f) v = fmaf(beta, *p, v);
+                *p = v;
+            }
+        }
+}
+
+using LargeTile = MfmaTile<128, 128, 32, 64, 64>;
+using SmallTile = MfmaTile<64, 64, 32, 32, 32>;
+
+template <class T>
+hipError_t launch_tile(const GemmArgs &g, bool vec, int group_m, hipStream_t stream) {
+    const int tiles_m = (g.M + T::BM - 1) / T::BM;
+    const int tiles_n = (g.N + T::BN - 1) / T::BN;
+    const dim3 grid(tiles_m * tiles_n), block(T::NT);
+    if (vec) hipLaunchKernelGGL((sgemm_mfma_kernel<T, true>), grid, block, 0, stream, g, tiles_m, tiles_n, group_m);
+    else hipLaunchKernelGGL((sgemm_mfma_kernel<T, false>), grid, block, 0, stream, g, tiles_m, tiles_n, group_m);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t mfma_large_grid(int M, int N) {
+    return (int64_t)((M + LargeTile::BM - 1) / LargeTile::BM) * ((N + LargeTile::BN - 1) / LargeTile::BN);
+}
+int64_t mfma_small_grid(int M, int N) {
+    return (int64_t)((M + SmallTile::BM - 1) / SmallTile::BM) * ((N + SmallTile::BN - 1) / SmallTile::BN);
+}
+
+hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
+    return launch_tile<LargeTile>(g, vec_loads, 8, stream);
+}
+
+hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
+    return launch_tile<SmallTile>(g, vec_loads, 8, stream);
+}
+
+}  // namespace sgemm

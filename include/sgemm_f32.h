@@ -1,0 +1,119 @@
+/*
+ * sgemm_f32.h -- C interface of the single-precision GEMM library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation ("Learn: Optimizing GEMM", section 3 "Rung 0 -- Naive (recap)",
+ * whose listing header states the operation and the three row-major shapes;
+ * "How a Matmul Kernel Gets Fast", section 1 "The problem, and what cuBLAS is",
+ * on the two scalars):
+ *
+ *     C = alpha * A * B + beta * C
+ *
+ * A is M x K, B is K x N, C is M x N, every matrix row-major with an explicit
+ * row stride (leading dimension) in elements:
+ *
+ *     A(i, k) = A[i * lda + k],  B(k, j) = B[k * ldb + j],  C(i, j) = C[i * ldc + j]
+ *
+ * ("CUDA Matrix Multiplication Optimization: From Naive to Near-cuBLAS",
+ * section "Why Naive is Cache-Hostile", addresses element (i, j) as
+ * base + i * stride + j; the pages fix the strides to K and N, this interface
+ * takes them as arguments.)
+ *
+ * Arithmetic is IEEE single precision throughout: FP32 products accumulated in
+ * FP32 on the matrix cores (or on the vector ALUs in the comparison variant).
+ * The summation order over k is not specified; results agree with a float64
+ * evaluation to within 2e-5 * (|alpha| * (|A|*|B|)_ij + |beta| * |C_ij|), and are
+ * exact whenever every partial sum is exactly representable in FP32 (e.g. small
+ * integers).
+ *
+ * Ownership and execution:
+ *   - A, B and C are device pointers owned by the caller.  The library never
+ *     frees or retains them.  C must not overlap A or B.
+ *   - The work is enqueued on `stream` (0 = the null stream) and the call
+ *     returns without waiting for it.  No host or device synchronisation.
+ *   - The functions hold no per-call state and may be called from several host
+ *     threads at once.
+ *
+ * Special cases:
+ *   - M == 0 or N == 0: nothing is done, returns 0.
+ *   - alpha == 0 or K == 0: C = beta * C, A and B are not read.
+ *   - beta == 0: C is output only and is never read (NaN or garbage in C does
+ *     not propagate).
+ *
+ * Return value:
+ *     0                      success (work enqueued)
+ *     1, 2, 3                M, N, K negative
+ *     5, 7, 10               A, B, C is NULL although it must be accessed
+ *     6, 8, 11               lda < max(1, K), ldb < max(1, N), ldc < max(1, N)
+ *     SGEMM_F32_ERR_VARIANT  (sgemm_f32_variant only) unknown variant number
+ *     SGEMM_F32_ERR_NOT_APPLICABLE  (sgemm_f32_variant only) the forced variant
+ *                            cannot run this shape or alignment
+ *     SGEMM_F32_ERR_TOO_LARGE  the tile grid exceeds the launch limits
+ *     < 0                    -(hipError_t) reported by the HIP runtime for the
+ *                            launch; the contents of C are then unspecified
+ * Nothing is printed and no exception crosses the interface.
+ */
+#ifndef SGEMM_F32_H
+#define SGEMM_F32_H
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SGEMM_F32_ERR_VARIANT 20
+#define SGEMM_F32_ERR_NOT_APPLICABLE 21
+#define SGEMM_F32_ERR_TOO_LARGE 22
+
+/* Kernel variants that sgemm_f32_variant can force. */
+enum sgemm_f32_variant_id {
+    SGEMM_F32_AUTO = 0,           /* the same selection sgemm_f32 makes */
+    SGEMM_F32_MFMA_LARGE = 1,     /* FP32 MFMA, 128x128 block tile */
+    SGEMM_F32_MFMA_SMALL = 2,     /* FP32 MFMA, 64x64 block tile (small shapes) */
+    SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
+    SGEMM_F32_SKINNY = 4,         /* M <= 16: FP32 MFMA streaming kernel */
+    SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
+    SGEMM_F32_NUM_VARIANTS = 6
+};
+
+/*
+ * C = alpha * A * B + beta * C on `stream` (see above).
+ * M, N, K: matrix sizes (>= 0).  alpha, beta: host scalars, by value.
+ * A: device, M x K, row stride lda.  B: device, K x N, row stride ldb.
+ * C: device, M x N, row stride ldc, read (if beta != 0) and written.
+ */
+int sgemm_f32(int M, int N, int K, float alpha,
+              const float *A, int lda, const float *B, int ldb,
+              float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * The same operation computed by one forced kernel variant, for comparisons
+ * between variants and for tests.  Arguments after `variant` are those of
+ * sgemm_f32.  Returns SGEMM_F32_ERR_NOT_APPLICABLE when the variant cannot
+ * handle the request (SGEMM_F32_SKINNY with M > 16; a vector-load variant with
+ * a pointer not 16-byte aligned or lda, ldb not multiples of 4).
+ */
+int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * The variant sgemm_f32 would use for these arguments (an
+ * sgemm_f32_variant_id), or 0 when it would launch no GEMM kernel (empty
+ * output, or alpha == 0 / K == 0 which only scales C).  Host only; no HIP call.
+ */
+int sgemm_f32_select(int M, int N, int K, float alpha,
+                     const float *A, int lda, const float *B, int ldb);
+
+/* Short static name of a variant ("mfma_large", ...), or NULL if unknown. */
+const char *sgemm_f32_variant_name(int variant);
+
+/* Library version, e.g. 100 for 0.1.0. */
+int sgemm_f32_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGEMM_F32_H */

@@ -1,0 +1,269 @@
+"""GPU parity: the HIP library, called through its C interface, against the oracle.
+
+Real-valued inputs must satisfy |C - Cref| <= 2e-5 * (|alpha|*(|A||B|)_ij +
+|beta|*|C0_ij|) element by element; integer-valued inputs (exact in FP32) must
+match bit for bit.  Sizes span several tiles with ragged tails; the full-size
+workloads are checked on sampled entries (plus whole rows and columns) that the
+oracle computes one by one, and on row and column sums of the whole result.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_helpers import (check_full, check_row_col_sums, check_sampled, run_lib,
+                         sample_positions, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sg():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import fp32_sgemm_amd
+    return fp32_sgemm_amd
+
+
+GENERAL = ["auto", "mfma_large", "mfma_small", "valu", "mfma_scalar"]
+VID = {"auto": 0, "mfma_large": 1, "mfma_small": 2, "valu": 3, "skinny": 4, "mfma_scalar": 5}
+
+RAGGED = [(1, 1, 1), (2, 3, 5), (17, 31, 33), (63, 65, 127), (129, 127, 65),
+          (300, 260, 70), (257, 129, 1000), (128, 128, 128), (64, 64, 32), (96, 200, 31),
+          (33, 17, 1), (130, 70, 9)]
+
+
+def _inputs(M, N, K, dist, seed, c0=True):
+    w = workloads.custom(M, N, K, dist=dist, seed=seed, c0_dist=("normal" if dist != "int4" else "int4") if c0 else None)
+    return workloads.make_inputs(w)
+
+
+@pytest.mark.parametrize("variant", GENERAL)
+@pytest.mark.parametrize("shape", RAGGED, ids=[f"{m}x{n}x{k}" for m, n, k in RAGGED])
+def test_ragged_real(sg, variant, shape):
+    M, N, K = shape
+    say(f"[ragged_real] {variant} {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 100 + M + N + K)
+    st, C, _ = run_lib(sg, VID[variant], A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.25, -0.5, C0)
+    assert ok, info
+
+
+@pytest.mark.parametrize("variant", GENERAL)
+@pytest.mark.parametrize("shape", RAGGED, ids=[f"{m}x{n}x{k}" for m, n, k in RAGGED])
+def test_ragged_integer_bitexact(sg, variant, shape):
+    M, N, K = shape
+    say(f"[ragged_int] {variant} {shape}")
+    A, B, C0 = _inputs(M, N, K, "int4", 200 + M + N + K)
+    st, C, _ = run_lib(sg, VID[variant], A, B, C0, 1.5, -0.5)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.5, -0.5, C0, exact=True)
+    assert ok, info
+
+
+SKINNY = [(1, 1, 1), (16, 16, 16), (16, 4096, 64), (3, 33, 100), (16, 100, 4099),
+          (7, 257, 513), (16, 16, 17), (12, 64, 2000)]
+
+
+@pytest.mark.parametrize("variant", ["skinny", "auto", "mfma_scalar", "valu"])
+@pytest.mark.parametrize("shape", SKINNY, ids=[f"{m}x{n}x{k}" for m, n, k in SKINNY])
+def test_skinny_shapes(sg, variant, shape):
+    M, N, K = shape
+    say(f"[skinny] {variant} {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 300 + M + N + K)
+    st, C, _ = run_lib(sg, VID[variant], A, B, C0, -0.75, 2.0)
+    assert st == 0
+    ok, info = check_full(C, A, B, -0.75, 2.0, C0)
+    assert ok, info
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 400 + M + N + K, c0=False)
+    st, C, _ = run_lib(sg, VID[variant], Ai, Bi, None, 1.0, 0.0)
+    assert st == 0
+    ok, info = check_full(C, Ai, Bi, 1.0, 0.0, None, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("variant", GENERAL + ["skinny"])
+def test_beta_zero_ignores_nan_c(sg, variant):
+    M = 16 if variant == "skinny" else 150
+    A, B, _ = _inputs(M, 140, 90, "uniform", 11, c0=False)
+    st, C, _ = run_lib(sg, VID[variant], A, B, None, 1.0, 0.0, c_fill=np.nan)
+    assert st == 0
+    assert np.all(np.isfinite(C))
+    ok, info = check_full(C, A, B, 1.0, 0.0, None)
+    assert ok, info
+
+
+@pytest.mark.parametrize("variant", GENERAL + ["skinny"])
+def test_guard_bands_untouched(sg, variant):
+    """C lives inside a larger buffer with row stride ldc > N and an offset:
+    every float outside the M x N window keeps its sentinel bits."""
+    M = 13 if variant == "skinny" else 133
+    N, K, ldc, off = 75, 41, 83, 4
+    A, B, C0 = _inputs(M, N, K, "uniform", 12)
+    st, C, Cbuf = run_lib(sg, VID[variant], A, B, C0, 1.0, 1.0, ldc=ldc, offs=(0, 0, off))
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.0, 1.0, C0)
+    assert ok, info
+    mask = np.ones(Cbuf.shape, bool)
+    for i in range(M):
+        mask[off + i * ldc: off + i * ldc + N] = False
+    assert np.all(Cbuf[mask].view(np.uint32) == np.float32(-7.25).view(np.uint32))
+
+
+@pytest.mark.parametrize("variant", ["auto", "mfma_scalar", "valu", "skinny"])
+def test_odd_strides_and_misaligned_pointers(sg, variant):
+    M = 9 if variant == "skinny" else 140
+    N, K = 97, 61
+    A, B, C0 = _inputs(M, N, K, "uniform", 13)
+    st, C, _ = run_lib(sg, VID[variant], A, B, C0, 0.5, 0.25, lda=K + 1, ldb=N + 3, ldc=N + 2,
+                       offs=(1, 3, 1))
+    assert st == 0
+    ok, info = check_full(C, A, B, 0.5, 0.25, C0)
+    assert ok, info
+
+
+def test_vector_variants_refuse_misaligned(sg):
+    A, B, C0 = _inputs(64, 64, 64, "uniform", 14)
+    for v in ("mfma_large", "mfma_small"):
+        st, _, _ = run_lib(sg, VID[v], A, B, C0, 1.0, 0.0, lda=65)
+        assert st == sg.ERR_NOT_APPLICABLE
+        st, _, _ = run_lib(sg, VID[v], A, B, C0, 1.0, 0.0, offs=(1, 0, 0))
+        assert st == sg.ERR_NOT_APPLICABLE
+    st, _, _ = run_lib(sg, VID["skinny"], A, B, C0, 1.0, 0.0)
+    assert st == sg.ERR_NOT_APPLICABLE
+
+
+def test_alpha_zero_and_k_zero(sg):
+    M, N, K = 70, 90, 30
+    rng = np.random.default_rng(1)
+    C0 = rng.standard_normal((M, N)).astype(np.float32)
+    A = np.full((M, K), np.nan, np.float32)
+    B = np.full((K, N), np.nan, np.float32)
+    st, C, _ = run_lib(sg, 0, A, B, C0, 0.0, -0.5)
+    assert st == 0
+    assert np.array_equal(C, (np.float32(-0.5) * C0))
+    A0 = np.zeros((M, 0), np.float32)
+    B0 = np.zeros((0, N), np.float32)
+    st, C, _ = run_lib(sg, 0, A0, B0, C0, 2.0, 3.0)
+    assert st == 0
+    assert np.array_equal(C, np.float32(3.0) * C0)
+    st, C, _ = run_lib(sg, 0, A0, B0, None, 2.0, 0.0, c_fill=np.nan)
+    assert st == 0
+    assert np.array_equal(C, np.zeros((M, N), np.float32))
+    st, C, _ = run_lib(sg, 0, A, B, C0, 0.0, 1.0)
+    assert st == 0 and np.array_equal(C, C0)
+
+
+def test_empty_output_is_noop(sg):
+    A, B, _ = _inputs(0, 5, 7, "uniform", 15, c0=False)
+    st, C, _ = run_lib(sg, 0, A, B, None, 1.0, 0.0)
+    assert st == 0 and C.shape == (0, 5)
+    A, B, _ = _inputs(5, 0, 7, "uniform", 15, c0=False)
+    st, C, _ = run_lib(sg, 0, A, B, None, 1.0, 0.0)
+    assert st == 0 and C.shape == (5, 0)
+
+
+def test_invalid_arguments(sg):
+    dC = torch.zeros(16, device="cuda:0")
+    p = dC.data_ptr()
+    assert sg.sgemm_f32(-1, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 1
+    assert sg.sgemm_f32(2, -1, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 2
+    assert sg.sgemm_f32(2, 2, -1, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 3
+    assert sg.sgemm_f32(2, 2, 2, 1.0, 0, 2, p, 2, 0.0, p, 2, 0) == 5
+    assert sg.sgemm_f32(2, 2, 3, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 6
+    assert sg.sgemm_f32(2, 2, 2, 1.0, p, 2, 0, 2, 0.0, p, 2, 0) == 7
+    assert sg.sgemm_f32(2, 3, 2, 1.0, p, 2, p, 2, 0.0, p, 3, 0) == 8
+    assert sg.sgemm_f32(2, 2, 2, 1.0, p, 2, p, 2, 0.0, 0, 2, 0) == 10
+    assert sg.sgemm_f32(2, 3, 2, 1.0, p, 2, p, 3, 0.0, p, 2, 0) == 11
+    assert sg.sgemm_f32_variant(99, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
+    torch.cuda.synchronize()
+    assert torch.all(dC == 0)
+
+
+@pytest.mark.parametrize("variant", GENERAL + ["skinny"])
+def test_repeat_runs_bitwise_identical(sg, variant):
+    M = 16 if variant == "skinny" else 700
+    N, K = 900, 1100
+    A, B, C0 = _inputs(M, N, K, "uniform", 16)
+    st1, C1, _ = run_lib(sg, VID[variant], A, B, C0, 1.0, 0.5)
+    st2, C2, _ = run_lib(sg, VID[variant], A, B, C0, 1.0, 0.5)
+    assert st1 == 0 and st2 == 0
+    assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+
+
+def test_non_default_stream_ordering(sg):
+    """Work queued before the call on a side stream is seen by the kernel."""
+    M, N, K = 300, 400, 500
+    A, B, _ = _inputs(M, N, K, "uniform", 17, c0=False)
+    s = torch.cuda.Stream()
+    dA = torch.from_numpy(A).cuda()
+    dB = torch.from_numpy(B).cuda()
+    dC = torch.empty(M, N, device="cuda:0")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        dC.fill_(1.0)            # queued on s before the GEMM
+        dA2 = dA * 2.0           # also on s
+        st = sg.sgemm_f32(M, N, K, 0.5, dA2.data_ptr(), K, dB.data_ptr(), N, 1.0,
+                          dC.data_ptr(), N, s.cuda_stream)
+    s.synchronize()
+    assert st == 0
+    C = dC.cpu().numpy()
+    ones = np.ones((M, N), np.float32)
+    A2 = (A * np.float32(2.0)).astype(np.float32)
+    ok, info = check_full(C, A2, B, 0.5, 1.0, ones)
+    assert ok, info
+
+
+# ---------------------------------------------------------------------------
+# The named workloads at their full sizes, through sgemm_f32 (the launch the
+# benchmark times).
+# ---------------------------------------------------------------------------
+SMALL_FULL = ["square128", "square128_int", "square1024", "skinny16x4096x4096"]
+LARGE_SAMPLED = ["square4092", "square4096_ab", "square8192", "wide4096x11008x512"]
+
+
+def _run_workload(sg, w, dist=None):
+    if dist is not None:
+        w = workloads.Workload(w.name + "_int", w.M, w.N, w.K, dist, w.alpha, w.beta, w.cid + 900,
+                               "int4" if w.c0_dist else None)
+    A, B, C0 = workloads.make_inputs(w)
+    st, C, _ = run_lib(sg, 0, A, B, C0, w.alpha, w.beta, c_fill=np.nan)
+    assert st == 0
+    return w, A, B, C0, C
+
+
+@pytest.mark.parametrize("name", SMALL_FULL)
+def test_workload_full_oracle(sg, name):
+    w = workloads.WORKLOADS[name]
+    say(f"[workload_full] {name}")
+    w, A, B, C0, C = _run_workload(sg, w)
+    ok, info = check_full(C, A, B, w.alpha, w.beta, C0, exact=(w.dist == "int4"))
+    assert ok, info
+
+
+@pytest.mark.parametrize("name", LARGE_SAMPLED)
+def test_workload_sampled(sg, name):
+    w = workloads.WORKLOADS[name]
+    say(f"[workload_sampled] {name}")
+    w, A, B, C0, C = _run_workload(sg, w)
+    assert np.all(np.isfinite(C)), "unwritten or non-finite entries"
+    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
+    ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols)
+    assert ok, info
+    ok, info = check_row_col_sums(C, A, B, w.alpha, w.beta, C0)
+    assert ok, info
+
+
+@pytest.mark.parametrize("name", ["square4096_ab", "square4092"])
+def test_workload_integer_bitexact_sampled(sg, name):
+    """Integer-valued inputs of the full shape: every partial sum stays below
+    2**24, so the GPU result is exact and must match bit for bit."""
+    w = workloads.WORKLOADS[name]
+    say(f"[workload_int] {name}")
+    w, A, B, C0, C = _run_workload(sg, w, dist="int4")
+    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
+    ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols, exact=True)
+    assert ok, info
