@@ -117,6 +117,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, run 10 plain device copies of MIB MiB "
+                         "(x*1 elementwise) to calibrate HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -134,6 +137,17 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration * 1024 * 1024 // 4
+        src = torch.randn(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(10):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": 4 * n, "copy_calibration_bytes_written": 4 * n,
+                          "launches": 10}), flush=True)
+        return
     names = {sg.sgemm_f32_variant_name(i): i for i in range(sg.NUM_VARIANTS)}
     if args.variant not in names:
         sys.exit(f"unknown variant {args.variant}")

@@ -47,7 +47,7 @@ constexpr int kSkinnyMaxM = 16;
 // ---------------------------------------------------------------------------
 constexpr int kNumXcd = 8;
 
-__device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
+__host__ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
                                               int group_m, int &tm, int &tn) {
     const int total = tiles_m * tiles_n;
     const int per = total / kNumXcd;

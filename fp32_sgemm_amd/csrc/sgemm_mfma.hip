@@ -43,9 +43,10 @@ namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_>
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int PF_ = 1>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
+    static constexpr int PF = PF_;             // slices loaded ahead of the one being computed
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NT = (BM / WM) * WAVES_N * 64;
     static constexpr int MB = WM / 32;          // 32x32 accumulator blocks per wave, along M
@@ -107,6 +108,16 @@ __device__ __forceinline__ void load_slice(const GemmArgs &g, int m0, int n0, in
     }
 }
 
+// Loads slice t, through the guarded path when the tile crosses the M or N
+// edge or the slice crosses the K edge.
+template <class T, bool VEC>
+__device__ __forceinline__ void load_any(const GemmArgs &g, int m0, int n0, int t, bool edge_mn, int tid,
+                                         float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
+    const int k0 = t * T::BK;
+    if (edge_mn || k0 + T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, k0, tid, ra, rb);
+    else load_slice<T, VEC, false>(g, m0, n0, k0, tid, ra, rb);
+}
+
 template <class T>
 __device__ __forceinline__ void store_slice(float *stage, int tid,
                                             const float4 (&ra)[T::A_VECS],
@@ -127,6 +138,42 @@ __device__ __forceinline__ void store_slice(float *stage, int tid,
     }
 }
 
+// Fragments of one chunk (4 k steps) of a slice: for each 32-row block of the
+// wave's A sub-tile one float4 (4 consecutive k of this lane's row), and for
+// each 32-column block of B four values (the same 4 k, this lane's column).
+template <class T>
+struct Frag {
+    float4 a[T::MB];
+    float b[T::NB][4];
+};
+
+template <class T>
+__device__ __forceinline__ void read_frag(const float *As, const float *Bs, int c, Frag<T> &f) {
+#pragma unroll
+    for (int ib = 0; ib < T::MB; ++ib)
+        f.a[ib] = *reinterpret_cast<const float4 *>(As + ib * 32 * T::LDA_S + 4 * c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int jb = 0; jb < T::NB; ++jb)
+            f.b[jb][e] = Bs[(4 * c + e) * T::BN + jb * 32];
+}
+
+template <class T>
+__device__ __forceinline__ void mfma_frag(const Frag<T> &f, f32x16 (&acc)[T::MB][T::NB]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < T::NB; ++jb) {
+                const float av = e == 0 ? f.a[ib].x : e == 1 ? f.a[ib].y : e == 2 ? f.a[ib].z : f.a[ib].w;
+                acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f.b[jb][e], acc[ib][jb], 0, 0, 0);
+            }
+}
+
+// All MFMAs of one slice.  The LDS reads of chunk c+1 are issued before the
+// MFMAs of chunk c, so their latency hides behind matrix-core work.
 template <class T>
 __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn, int lane,
                                               f32x16 (&acc)[T::MB][T::NB]) {
@@ -134,32 +181,22 @@ __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn
     const int l32 = lane & 31;
     const float *As = stage + (wm * T::WM + l32) * T::LDA_S + h * T::HALF;
     const float *Bs = stage + T::A_STAGE + h * (T::HALF * T::BN + T::B_SHIFT) + wn * T::WN + l32;
+    constexpr int CH = T::HALF / 4;
+    Frag<T> f[2];
+    read_frag<T>(As, Bs, 0, f[0]);
 #pragma unroll
-    for (int c = 0; c < T::HALF / 4; ++c) {
-        float4 a[T::MB];
-        float b[T::NB][4];
-#pragma unroll
-        for (int ib = 0; ib < T::MB; ++ib)
-            a[ib] = *reinterpret_cast<const float4 *>(As + ib * 32 * T::LDA_S + 4 * c);
-#pragma unroll
-        for (int jb = 0; jb < T::NB; ++jb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                b[jb][e] = Bs[(4 * c + e) * T::BN + jb * 32];
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-            for (int ib = 0; ib < T::MB; ++ib)
-#pragma unroll
-                for (int jb = 0; jb < T::NB; ++jb) {
-                    const float av = e == 0 ? a[ib].x : e == 1 ? a[ib].y : e == 2 ? a[ib].z : a[ib].w;
-                    acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, b[jb][e], acc[ib][jb], 0, 0, 0);
-                }
+    for (int c = 0; c < CH; ++c) {
+        if (c + 1 < CH) read_frag<T>(As, Bs, c + 1, f[(c + 1) & 1]);
+        // Keep the compiler from sinking those reads below the MFMAs.
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_frag<T>(f[c & 1], acc);
     }
 }
 
+// At least two waves per SIMD: with one wave per SIMD the matrix core idles
+// whenever that wave waits at a barrier or on memory.
 template <class T, bool VEC>
-__global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n,
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n,
                                                            int group_m) {
     __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
 
@@ -181,23 +218,37 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs g, int tiles
 
     const bool edge_mn = (m0 + T::BM > g.M) || (n0 + T::BN > g.N);
     const int nk = (g.K + T::BK - 1) / T::BK;
-    float4 ra[T::A_VECS], rb[T::B_VECS];
-
-    if (edge_mn || T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, 0, tid, ra, rb);
-    else load_slice<T, VEC, false>(g, m0, n0, 0, tid, ra, rb);
-    store_slice<T>(smem, tid, ra, rb);
-    __syncthreads();
-
-    for (int t = 0; t < nk; ++t) {
-        const bool more = t + 1 < nk;
-        if (more) {
-            const int k0 = (t + 1) * T::BK;
-            if (edge_mn || k0 + T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, k0, tid, ra, rb);
-            else load_slice<T, VEC, false>(g, m0, n0, k0, tid, ra, rb);
-        }
-        compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
-        if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
+    if (T::PF == 1) {
+        float4 ra[T::A_VECS], rb[T::B_VECS];
+        load_any<T, VEC>(g, m0, n0, 0, edge_mn, tid, ra, rb);
+        store_slice<T>(smem, tid, ra, rb);
         __syncthreads();
+        for (int t = 0; t < nk; ++t) {
+            const bool more = t + 1 < nk;
+            if (more) load_any<T, VEC>(g, m0, n0, t + 1, edge_mn, tid, ra, rb);
+            compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
+            if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
+            __syncthreads();
+        }
+    } else {
+        // Two register sets: while slice t is computed from LDS, slice t+1
+        // waits in registers for its LDS buffer and slice t+2 is in flight.
+        float4 ra0[T::A_VECS], rb0[T::B_VECS], ra1[T::A_VECS], rb1[T::B_VECS];
+        load_any<T, VEC>(g, m0, n0, 0, edge_mn, tid, ra0, rb0);
+        store_slice<T>(smem, tid, ra0, rb0);
+        if (nk > 1) load_any<T, VEC>(g, m0, n0, 1, edge_mn, tid, ra1, rb1);
+        __syncthreads();
+        for (int t = 0; t < nk; t += 2) {
+            if (t + 2 < nk) load_any<T, VEC>(g, m0, n0, t + 2, edge_mn, tid, ra0, rb0);
+            compute_slice<T>(smem, wm, wn, lane, acc);
+            if (t + 1 < nk) store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
+            __syncthreads();
+            if (t + 1 >= nk) break;
+            if (t + 3 < nk) load_any<T, VEC>(g, m0, n0, t + 3, edge_mn, tid, ra1, rb1);
+            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc);
+            if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
+            __syncthreads();
+        }
     }
 
     // Epilogue.  Accumulator register r of a 32x32 block holds, in lane l,
@@ -222,16 +273,20 @@ __global__ __launch_bounds__(T::NT) void sgemm_mfma_kernel(GemmArgs g, int tiles
         }
 }
 
-using LargeTile = MfmaTile<128, 128, 32, 64, 64>;
+// 128x128 tiles: two slices in flight with 16-byte loads; one with 4-byte
+// loads (whose staging registers would not fit two sets at two waves per SIMD).
+using LargeTile = MfmaTile<128, 128, 32, 64, 64, 2>;
+using LargeTileScalar = MfmaTile<128, 128, 32, 64, 64, 1>;
 using SmallTile = MfmaTile<64, 64, 32, 32, 32>;
 
-template <class T>
+template <class TV, class TS>
 hipError_t launch_tile(const GemmArgs &g, bool vec, int group_m, hipStream_t stream) {
-    const int tiles_m = (g.M + T::BM - 1) / T::BM;
-    const int tiles_n = (g.N + T::BN - 1) / T::BN;
-    const dim3 grid(tiles_m * tiles_n), block(T::NT);
-    if (vec) hipLaunchKernelGGL((sgemm_mfma_kernel<T, true>), grid, block, 0, stream, g, tiles_m, tiles_n, group_m);
-    else hipLaunchKernelGGL((sgemm_mfma_kernel<T, false>), grid, block, 0, stream, g, tiles_m, tiles_n, group_m);
+    static_assert(TV::BM == TS::BM && TV::BN == TS::BN, "same tile");
+    const int tiles_m = (g.M + TV::BM - 1) / TV::BM;
+    const int tiles_n = (g.N + TV::BN - 1) / TV::BN;
+    const dim3 grid(tiles_m * tiles_n);
+    if (vec) hipLaunchKernelGGL((sgemm_mfma_kernel<TV, true>), grid, dim3(TV::NT), 0, stream, g, tiles_m, tiles_n, group_m);
+    else hipLaunchKernelGGL((sgemm_mfma_kernel<TS, false>), grid, dim3(TS::NT), 0, stream, g, tiles_m, tiles_n, group_m);
     return hipGetLastError();
 }
 
@@ -245,11 +300,11 @@ int64_t mfma_small_grid(int M, int N) {
 }
 
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_tile<LargeTile>(g, vec_loads, 8, stream);
+    return launch_tile<LargeTile, LargeTileScalar>(g, vec_loads, 8, stream);
 }
 
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_tile<SmallTile>(g, vec_loads, 8, stream);
+    return launch_tile<SmallTile, SmallTile>(g, vec_loads, 8, stream);
 }
 
 }  // namespace sgemm

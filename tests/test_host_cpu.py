@@ -1,0 +1,197 @@
+"""CPU-only checks: the C library loads and exports what its header declares,
+host-side argument handling and kernel selection, the tile mapping, the
+benchmark's closed-form work/byte model, and the input generators.  No GPU
+compute is launched here."""
+from __future__ import annotations
+
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm_f32\w*)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def sg():
+    import fp32_sgemm_amd
+    return fp32_sgemm_amd
+
+
+def test_header_declares_the_interface():
+    names = _declared_functions()
+    assert {"sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select", "sgemm_f32_variant_name",
+            "sgemm_f32_version"} <= set(names), names
+
+
+def test_library_exports_every_declared_symbol(sg):
+    out = subprocess.run(["nm", "-D", "--defined-only", sg.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    for name in _declared_functions():
+        assert name in exported, f"{name} declared in sgemm_f32.h but not exported"
+        assert hasattr(sg._lib, name)
+    assert set(sg.EXPORTED) == set(_declared_functions())
+
+
+def test_binding_mirrors_the_c_names(sg):
+    for name in _declared_functions():
+        assert callable(getattr(sg, name)), name
+
+
+def test_argument_errors_without_touching_the_gpu(sg):
+    p = 0x1000  # never dereferenced: every call below fails validation first
+    f = sg.sgemm_f32
+    assert f(-1, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 1
+    assert f(2, -1, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 2
+    assert f(2, 2, -1, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 3
+    assert f(2, 2, 2, 1.0, 0, 2, p, 2, 0.0, p, 2, 0) == 5
+    assert f(2, 2, 3, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 6
+    assert f(2, 2, 2, 1.0, p, 2, 0, 2, 0.0, p, 2, 0) == 7
+    assert f(2, 3, 2, 1.0, p, 2, p, 2, 0.0, p, 3, 0) == 8
+    assert f(2, 2, 2, 1.0, p, 2, p, 2, 0.0, 0, 2, 0) == 10
+    assert f(2, 3, 2, 1.0, p, 2, p, 3, 0.0, p, 2, 0) == 11
+    assert f(2, 2, 0, 1.0, 0, 1, 0, 2, 0.0, 0, 2, 0) == 10   # K = 0 still writes C
+    assert sg.sgemm_f32_variant(-1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
+    assert sg.sgemm_f32_variant(sg.NUM_VARIANTS, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
+
+
+def test_empty_outputs_return_without_work(sg):
+    # M == 0 or N == 0: success without any launch (NULL pointers are fine).
+    assert sg.sgemm_f32(0, 5, 7, 1.0, 0, 7, 0, 5, 0.0, 0, 5, 0) == 0
+    assert sg.sgemm_f32(5, 0, 7, 1.0, 0, 7, 0, 1, 0.0, 0, 1, 0) == 0
+
+
+def test_kernel_selection(sg):
+    al = 0x100000          # 16-byte aligned stand-in pointers (never dereferenced)
+    assert sg.sgemm_f32_select(4096, 4096, 4096, 1.5, al, 4096, al, 4096) == sg.MFMA_LARGE
+    assert sg.sgemm_f32_select(4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
+    assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) == sg.MFMA_SMALL
+    assert sg.sgemm_f32_select(128, 128, 128, 1.0, al, 128, al, 128) == sg.MFMA_SMALL
+    assert sg.sgemm_f32_select(16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
+    assert sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096) == sg.MFMA_SCALAR
+    assert sg.sgemm_f32_select(4096, 4096, 4097, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
+    assert sg.sgemm_f32_select(4096, 4096, 4096, 0.0, al, 4096, al, 4096) == 0
+    assert sg.sgemm_f32_select(4096, 4096, 0, 1.0, al, 1, al, 4096) == 0
+
+
+def test_variant_names_and_version(sg):
+    names = [sg.sgemm_f32_variant_name(i) for i in range(sg.NUM_VARIANTS)]
+    assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar"]
+    assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
+    assert sg.sgemm_f32_version() >= 100
+
+
+def test_tile_mapping_is_a_bijection(tmp_path):
+    exe = tmp_path / "tile_map_check"
+    src = os.path.join(ROOT, "tests", "host", "tile_map_check.cpp")
+    inc = os.path.join(ROOT, "fp32_sgemm_amd", "csrc")
+    subprocess.run(["/opt/rocm/bin/hipcc", "-x", "hip", "--offload-arch=gfx950", "-O1",
+                    "-I", inc, src, "-o", str(exe)], check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0 and out.stdout.strip() == "ok", out.stdout
+
+
+def test_build_flags_disable_packed_fp32():
+    from fp32_sgemm_amd import _build
+    flags = " ".join(_build.COMMON_FLAGS)
+    assert "-target-feature -Xclang -packed-fp32-ops" in flags
+    assert "--offload-arch=gfx950" in flags
+    assert "fast-math" not in flags
+
+
+def test_product_package_does_not_touch_the_oracle():
+    pkg = os.path.join(ROOT, "fp32_sgemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "oracle" not in text.lower(), f"{fn} mentions the oracle"
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """A copy of the package without its built library must refuse to import."""
+    dst = tmp_path / "fp32_sgemm_amd"
+    shutil.copytree(os.path.join(ROOT, "fp32_sgemm_amd"), dst,
+                    ignore=shutil.ignore_patterns("_lib", "__pycache__"))
+    r = subprocess.run([sys.executable, "-c", "import fp32_sgemm_amd"], cwd=tmp_path,
+                       capture_output=True, text=True)
+    assert r.returncode != 0 and "ImportError" in r.stderr
+
+
+# --- the benchmark's closed-form model against the pages' own figures -------
+def test_flop_and_byte_counts_match_the_pages():
+    import bench
+    # "Writing a Fast Matmul in CUDA, Step by Step", Step 1: 2 x 4096^3 = 137.4
+    # billion FLOPs; 3 x n^2 x 4 bytes = 201 MB; at most 683 FLOPs per byte.
+    assert bench.gemm_flops(4096, 4096, 4096) == 137_438_953_472
+    assert round(bench.gemm_min_bytes(4096, 4096, 4096, reads_c=False) / 1e6) == 201
+    assert round(bench.arithmetic_intensity(4096, 4096, 4096, reads_c=False)) == 683
+    # "How a Matmul Kernel Gets Fast", section 1 and 2: 2 x 4092^3 ~ 137 GFLOP;
+    # read A, B and read+write C ~ 268 MB.
+    assert round(bench.gemm_flops(4092, 4092, 4092) / 1e9) == 137
+    assert round(bench.gemm_min_bytes(4092, 4092, 4092, reads_c=True) / 1e6) == 268
+    # "Learn: Optimizing GEMM": the ideal intensity with 3n^2 traffic is n/6.
+    assert abs(bench.arithmetic_intensity(4092, 4092, 4092, reads_c=False) - 4092 / 6) < 1e-9
+
+
+def test_roofline_classification():
+    import bench
+    ridge = bench.PEAK_FP32_TFLOPS * 1e12 / (bench.PEAK_HBM_GBS * 1e9)
+    assert 19 < ridge < 20
+    assert bench.arithmetic_intensity(16, 4096, 4096, False) < ridge      # skinny: HBM-bound
+    assert bench.arithmetic_intensity(4096, 4096, 4096, True) > ridge     # square: compute-bound
+    assert bench.arithmetic_intensity(4096, 11008, 512, False) > ridge
+
+
+def test_bench_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+# --- input generators ----------------------------------------------------------
+def test_generators_are_deterministic_and_distinct():
+    import workloads
+    w = workloads.custom(37, 29, 41, "uniform", seed=3, beta=1.0, c0_dist="normal")
+    A1, B1, C1 = workloads.make_inputs(w)
+    A2, B2, C2 = workloads.make_inputs(w)
+    assert np.array_equal(A1, A2) and np.array_equal(B1, B2) and np.array_equal(C1, C2)
+    assert not np.array_equal(A1[:29, :29], B1[:29, :29])
+    w2 = workloads.custom(37, 29, 41, "uniform", seed=4)
+    assert not np.array_equal(workloads.make_inputs(w2)[0], A1)
+
+
+def test_generator_distributions():
+    import workloads
+    u = workloads.draw((512, 512), "uniform", 1)
+    assert u.dtype == np.float32 and u.min() >= -1.0 and u.max() < 1.0
+    assert abs(float(u.mean())) < 0.01 and abs(float(u.std()) - (1 / 3) ** 0.5) < 0.01
+    i = workloads.draw((512, 512), "int4", 2)
+    assert set(np.unique(i).tolist()) == set(float(v) for v in range(-4, 5))
+    n = workloads.draw((512, 512), "normal", 3)
+    assert abs(float(n.mean())) < 0.01 and abs(float(n.std()) - 1.0) < 0.01
+    p = workloads.draw((8, 5), "uniform", 4, pad_cols=3)
+    assert p.shape == (8, 5) and p.strides[0] == 8 * 4
+
+
+def test_named_workloads_match_the_configured_shapes():
+    import workloads
+    W = workloads.WORKLOADS
+    assert (W["square4096_ab"].M, W["square4096_ab"].alpha, W["square4096_ab"].beta) == (4096, 1.5, -0.5)
+    assert W["square4096_ab"].dist == "normal" and W["square4096_ab"].c0_dist == "normal"
+    assert (W["skinny16x4096x4096"].M, W["skinny16x4096x4096"].N, W["skinny16x4096x4096"].K) == (16, 4096, 4096)
+    assert (W["wide4096x11008x512"].N, W["wide4096x11008x512"].K) == (11008, 512)
+    assert W["square128_int"].dist == "int4"
+    assert workloads.HEADLINE == "square4096_ab"
