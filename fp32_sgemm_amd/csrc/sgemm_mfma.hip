@@ -65,57 +65,88 @@ struct MfmaTile {
     static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS");
 };
 
-// Loads one 4-float group of a row-major matrix at (row, col..col+3).  With
-// GUARD, elements with row >= rows or col + e >= cols read as zero and are not
-// accessed.  VEC selects one 16-byte load (requires 16-byte alignment of the
-// group) over four 4-byte loads.
-template <bool VEC, bool GUARD>
-__device__ __forceinline__ float4 load4(const float *__restrict__ base, int64_t ld,
-                                        int row, int col, int rows, int cols) {
-    const float *p = base + (int64_t)row * ld + col;
-    if (!GUARD) {
-        if (VEC) return *reinterpret_cast<const float4 *>(p);
-        return make_float4(p[0], p[1], p[2], p[3]);
-    }
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (row < rows) {
-        if (VEC && col + 3 < cols) {
-            v = *reinterpret_cast<const float4 *>(p);
-        } else {
-            if (col + 0 < cols) v.x = p[0];
-            if (col + 1 < cols) v.y = p[1];
-            if (col + 2 < cols) v.z = p[2];
-            if (col + 3 < cols) v.w = p[3];
+// Per-thread addressing of the 4-float groups a thread stages for every slice:
+// group i of A is row ar[i], columns ac[i]..ac[i]+3 of the slice; group i of B
+// is row br[i], columns bc[i]..bc[i]+3.  The row pointers are formed once.
+template <class T>
+struct Stager {
+    const float *pa[T::A_VECS];
+    const float *pb[T::B_VECS];
+    int ar[T::A_VECS], ac[T::A_VECS];
+    int br[T::B_VECS], bc[T::B_VECS];
+
+    __device__ __forceinline__ Stager(const GemmArgs &g, int m0, int n0, int tid) {
+#pragma unroll
+        for (int i = 0; i < T::A_VECS; ++i) {
+            const int q = tid + i * T::NT;
+            ar[i] = q / (T::BK / 4);
+            ac[i] = (q % (T::BK / 4)) * 4;
+            pa[i] = g.A + (int64_t)(m0 + ar[i]) * g.lda + ac[i];
+        }
+#pragma unroll
+        for (int i = 0; i < T::B_VECS; ++i) {
+            const int q = tid + i * T::NT;
+            br[i] = q / (T::BN / 4);
+            bc[i] = (q % (T::BN / 4)) * 4;
+            pb[i] = g.B + (int64_t)br[i] * g.ldb + n0 + bc[i];
         }
     }
-    return v;
+};
+
+template <bool VEC>
+__device__ __forceinline__ float4 ld4(const float *p) {
+    if (VEC) return *reinterpret_cast<const float4 *>(p);
+    return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-template <class T, bool VEC, bool GUARD>
-__device__ __forceinline__ void load_slice(const GemmArgs &g, int m0, int n0, int k0, int tid,
+// Loads the slice starting at column k0 of A / row k0 of B.  GMN: the tile
+// crosses the M or N edge, so rows of A beyond M and columns of B beyond N read
+// as zero.  GK: the slice crosses the K edge, so k >= K reads as zero.  Nothing
+// outside the matrices is accessed.
+template <class T, bool VEC, bool GMN, bool GK>
+__device__ __forceinline__ void load_slice(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
                                            float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int i = 0; i < T::A_VECS; ++i) {
-        const int q = tid + i * T::NT;
-        const int r = q / (T::BK / 4), c = (q % (T::BK / 4)) * 4;
-        ra[i] = load4<VEC, GUARD>(g.A, g.lda, m0 + r, k0 + c, g.M, g.K);
+        const float *p = s.pa[i] + k0;
+        const bool row_ok = !GMN || (m0 + s.ar[i] < g.M);
+        if (!GK) {
+            ra[i] = row_ok ? ld4<VEC>(p) : zero;
+        } else {
+            const int k = k0 + s.ac[i];
+            float4 v = zero;
+            if (row_ok) {
+                if (k + 0 < g.K) v.x = p[0];
+                if (k + 1 < g.K) v.y = p[1];
+                if (k + 2 < g.K) v.z = p[2];
+                if (k + 3 < g.K) v.w = p[3];
+            }
+            ra[i] = v;
+        }
     }
 #pragma unroll
     for (int i = 0; i < T::B_VECS; ++i) {
-        const int q = tid + i * T::NT;
-        const int r = q / (T::BN / 4), c = (q % (T::BN / 4)) * 4;
-        rb[i] = load4<VEC, GUARD>(g.B, g.ldb, k0 + r, n0 + c, g.K, g.N);
+        const float *p = s.pb[i] + (int64_t)k0 * g.ldb;
+        const bool row_ok = !GK || (k0 + s.br[i] < g.K);
+        if (!GMN) {
+            rb[i] = row_ok ? ld4<VEC>(p) : zero;
+        } else {
+            const int n = n0 + s.bc[i];
+            float4 v = zero;
+            if (row_ok) {
+                if (VEC && n + 3 < g.N) {
+                    v = ld4<true>(p);
+                } else {
+                    if (n + 0 < g.N) v.x = p[0];
+                    if (n + 1 < g.N) v.y = p[1];
+                    if (n + 2 < g.N) v.z = p[2];
+                    if (n + 3 < g.N) v.w = p[3];
+                }
+            }
+            rb[i] = v;
+        }
     }
-}
-
-// Loads slice t, through the guarded path when the tile crosses the M or N
-// edge or the slice crosses the K edge.
-template <class T, bool VEC>
-__device__ __forceinline__ void load_any(const GemmArgs &g, int m0, int n0, int t, bool edge_mn, int tid,
-                                         float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
-    const int k0 = t * T::BK;
-    if (edge_mn || k0 + T::BK > g.K) load_slice<T, VEC, true>(g, m0, n0, k0, tid, ra, rb);
-    else load_slice<T, VEC, false>(g, m0, n0, k0, tid, ra, rb);
 }
 
 template <class T>
@@ -193,11 +224,63 @@ __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn
     }
 }
 
+// The K loop of one tile.  Slices are processed in the order: the partial
+// slice at the K edge first (when K is not a multiple of BK), then the full
+// slices from k = 0 up, so only the first slice ever needs the K guard.
+template <class T, bool VEC, bool GMN>
+__device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int tid, int wm, int wn,
+                                       int lane, float *smem, f32x16 (&acc)[T::MB][T::NB]) {
+    const Stager<T> s(g, m0, n0, tid);
+    const int nkf = g.K / T::BK;
+    const bool tail = nkf * T::BK != g.K;
+    const int nk = nkf + (tail ? 1 : 0);
+    // k0 of the slice processed at position idx >= 1 (position 0 is the tail
+    // slice when there is one).
+    const int shift = tail ? 1 : 0;
+    auto k0_of = [&](int idx) { return (idx - shift) * T::BK; };
+
+    if (T::PF == 1) {
+        float4 ra[T::A_VECS], rb[T::B_VECS];
+        if (tail) load_slice<T, VEC, GMN, true>(g, s, m0, n0, nkf * T::BK, ra, rb);
+        else load_slice<T, VEC, GMN, false>(g, s, m0, n0, 0, ra, rb);
+        store_slice<T>(smem, tid, ra, rb);
+        __syncthreads();
+        for (int t = 0; t < nk; ++t) {
+            const bool more = t + 1 < nk;
+            if (more) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 1), ra, rb);
+            compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
+            if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
+            __syncthreads();
+        }
+    } else {
+        // Two register sets: while slice t is computed from LDS, slice t+1
+        // waits in registers for its LDS buffer and slice t+2 is in flight.
+        float4 ra0[T::A_VECS], rb0[T::B_VECS], ra1[T::A_VECS], rb1[T::B_VECS];
+        if (tail) load_slice<T, VEC, GMN, true>(g, s, m0, n0, nkf * T::BK, ra0, rb0);
+        else load_slice<T, VEC, GMN, false>(g, s, m0, n0, 0, ra0, rb0);
+        store_slice<T>(smem, tid, ra0, rb0);
+        if (nk > 1) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(1), ra1, rb1);
+        __syncthreads();
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            if (t + 2 < nk) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 2), ra0, rb0);
+            compute_slice<T>(smem, wm, wn, lane, acc);
+            store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
+            __syncthreads();
+            if (t + 3 < nk) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 3), ra1, rb1);
+            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc);
+            if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
+            __syncthreads();
+        }
+        if (t < nk) compute_slice<T>(smem, wm, wn, lane, acc);
+    }
+}
+
 // At least two waves per SIMD: with one wave per SIMD the matrix core idles
 // whenever that wave waits at a barrier or on memory.
 template <class T, bool VEC>
-__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(GemmArgs g, int tiles_m, int tiles_n,
-                                                           int group_m) {
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
+    GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
 
     int tm, tn;
@@ -217,39 +300,8 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int r = 0; r < 16; ++r) acc[ib][jb][r] = 0.f;
 
     const bool edge_mn = (m0 + T::BM > g.M) || (n0 + T::BN > g.N);
-    const int nk = (g.K + T::BK - 1) / T::BK;
-    if (T::PF == 1) {
-        float4 ra[T::A_VECS], rb[T::B_VECS];
-        load_any<T, VEC>(g, m0, n0, 0, edge_mn, tid, ra, rb);
-        store_slice<T>(smem, tid, ra, rb);
-        __syncthreads();
-        for (int t = 0; t < nk; ++t) {
-            const bool more = t + 1 < nk;
-            if (more) load_any<T, VEC>(g, m0, n0, t + 1, edge_mn, tid, ra, rb);
-            compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
-            if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
-            __syncthreads();
-        }
-    } else {
-        // Two register sets: while slice t is computed from LDS, slice t+1
-        // waits in registers for its LDS buffer and slice t+2 is in flight.
-        float4 ra0[T::A_VECS], rb0[T::B_VECS], ra1[T::A_VECS], rb1[T::B_VECS];
-        load_any<T, VEC>(g, m0, n0, 0, edge_mn, tid, ra0, rb0);
-        store_slice<T>(smem, tid, ra0, rb0);
-        if (nk > 1) load_any<T, VEC>(g, m0, n0, 1, edge_mn, tid, ra1, rb1);
-        __syncthreads();
-        for (int t = 0; t < nk; t += 2) {
-            if (t + 2 < nk) load_any<T, VEC>(g, m0, n0, t + 2, edge_mn, tid, ra0, rb0);
-            compute_slice<T>(smem, wm, wn, lane, acc);
-            if (t + 1 < nk) store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
-            __syncthreads();
-            if (t + 1 >= nk) break;
-            if (t + 3 < nk) load_any<T, VEC>(g, m0, n0, t + 3, edge_mn, tid, ra1, rb1);
-            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc);
-            if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
-            __syncthreads();
-        }
-    }
+    if (edge_mn) k_loop<T, VEC, true>(g, m0, n0, tid, wm, wn, lane, smem, acc);
+    else k_loop<T, VEC, false>(g, m0, n0, tid, wm, wn, lane, smem, acc);
 
     // Epilogue.  Accumulator register r of a 32x32 block holds, in lane l,
     // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.
