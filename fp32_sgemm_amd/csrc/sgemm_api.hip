@@ -31,9 +31,16 @@ int validate(int M, int N, int K, float alpha, const float *A, int lda, const fl
     return 0;
 }
 
+// The 16-byte-load kernels need 16-byte aligned operands with row strides that
+// are multiples of 4 floats, and address one slice of a tile with 32-bit byte
+// offsets: 128 rows of A and 32 rows of B must span less than 2 GiB.
 bool vec_aligned(const float *A, int lda, const float *B, int ldb) {
-    return (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0) &&
-           (lda % 4 == 0) && (ldb % 4 == 0);
+    const bool aligned = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
+                         (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (lda % 4 == 0) && (ldb % 4 == 0);
+    const int64_t limit = (int64_t)1 << 31;
+    const bool offsets_fit = (int64_t)(127 * (int64_t)lda + 32) * 4 < limit &&
+                             (int64_t)(31 * (int64_t)ldb + 128) * 4 < limit;
+    return aligned && offsets_fit;
 }
 
 // Large 128x128 tiles unless they leave most compute units idle and the

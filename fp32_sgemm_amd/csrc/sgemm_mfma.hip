@@ -42,6 +42,19 @@ namespace sgemm {
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+
+// 16-byte buffer load: base and extent come from a buffer resource in scalar
+// registers, the per-lane part is one 32-bit byte offset.  Accesses at or past
+// the resource's extent return zeros instead of touching memory.
+__device__ f32x4v raw_buffer_load_v4f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+
+// Buffer resource over [base, base + bytes): raw (untyped) access with the
+// 32-bit data format, so every lane's offset is checked against `bytes`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, 0x00020000);
+}
 
 template <int BM_, int BN_, int BK_, int WM_, int WN_, int PF_ = 1>
 struct MfmaTile {
@@ -67,13 +80,16 @@ struct MfmaTile {
 
 // Per-thread addressing of the 4-float groups a thread stages for every slice:
 // group i of A is row ar[i], columns ac[i]..ac[i]+3 of the slice; group i of B
-// is row br[i], columns bc[i]..bc[i]+3.  The row pointers are formed once.
+// is row br[i], columns bc[i]..bc[i]+3.  The row pointers (guarded loads) and
+// the byte offsets from the slice origin (buffer loads of interior slices) are
+// formed once.
 template <class T>
 struct Stager {
     const float *pa[T::A_VECS];
     const float *pb[T::B_VECS];
     int ar[T::A_VECS], ac[T::A_VECS];
     int br[T::B_VECS], bc[T::B_VECS];
+    int oa[T::A_VECS], ob[T::B_VECS];
 
     __device__ __forceinline__ Stager(const GemmArgs &g, int m0, int n0, int tid) {
 #pragma unroll
@@ -82,6 +98,7 @@ struct Stager {
             ar[i] = q / (T::BK / 4);
             ac[i] = (q % (T::BK / 4)) * 4;
             pa[i] = g.A + (int64_t)(m0 + ar[i]) * g.lda + ac[i];
+            oa[i] = (ar[i] * (int)g.lda + ac[i]) * 4;
         }
 #pragma unroll
         for (int i = 0; i < T::B_VECS; ++i) {
@@ -89,6 +106,7 @@ struct Stager {
             br[i] = q / (T::BN / 4);
             bc[i] = (q % (T::BN / 4)) * 4;
             pb[i] = g.B + (int64_t)br[i] * g.ldb + n0 + bc[i];
+            ob[i] = (br[i] * (int)g.ldb + bc[i]) * 4;
         }
     }
 };
@@ -99,54 +117,86 @@ __device__ __forceinline__ float4 ld4(const float *p) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-// Loads the slice starting at column k0 of A / row k0 of B.  GMN: the tile
-// crosses the M or N edge, so rows of A beyond M and columns of B beyond N read
-// as zero.  GK: the slice crosses the K edge, so k >= K reads as zero.  Nothing
-// outside the matrices is accessed.
+// Loads 4-float group p of the slice starting at column k0 of A / row k0 of
+// B: groups 0 .. A_VECS-1 are A's, the rest B's.  GMN: the tile crosses the M
+// or N edge, so rows of A beyond M and columns of B beyond N read as zero.
+// GK: the slice crosses the K edge, so k >= K reads as zero.  Nothing outside
+// the matrices is accessed.
+// Resources covering exactly the A and B elements of the slice at k0 of an
+// interior tile (used with 16-byte loads only).
+struct SliceRsrc {
+    __amdgpu_buffer_rsrc_t a, b;
+};
+
+template <class T>
+__device__ __forceinline__ SliceRsrc slice_rsrc(const GemmArgs &g, int m0, int n0, int k0) {
+    SliceRsrc r;
+    r.a = make_rsrc(g.A + (int64_t)m0 * g.lda + k0, (int)(((T::BM - 1) * g.lda + T::BK) * 4));
+    r.b = make_rsrc(g.B + (int64_t)k0 * g.ldb + n0, (int)(((T::BK - 1) * g.ldb + T::BN) * 4));
+    return r;
+}
+
+// Interior tiles with 16-byte loads go through the buffer resources `r`; the
+// other cases through the row pointers.
 template <class T, bool VEC, bool GMN, bool GK>
-__device__ __forceinline__ void load_slice(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
-                                           float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
+__device__ __forceinline__ void load_part(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
+                                          const SliceRsrc &r, int p, float4 (&ra)[T::A_VECS],
+                                          float4 (&rb)[T::B_VECS]) {
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-    for (int i = 0; i < T::A_VECS; ++i) {
-        const float *p = s.pa[i] + k0;
+    constexpr bool BUF = VEC && !GMN && !GK;
+    if (p < T::A_VECS) {
+        const int i = p;
+        const float *ptr = s.pa[i] + k0;
         const bool row_ok = !GMN || (m0 + s.ar[i] < g.M);
-        if (!GK) {
-            ra[i] = row_ok ? ld4<VEC>(p) : zero;
+        if (BUF) {
+            const f32x4v v = raw_buffer_load_v4f32(r.a, s.oa[i], 0, 0);
+            ra[i] = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (!GK) {
+            ra[i] = row_ok ? ld4<VEC>(ptr) : zero;
         } else {
             const int k = k0 + s.ac[i];
             float4 v = zero;
             if (row_ok) {
-                if (k + 0 < g.K) v.x = p[0];
-                if (k + 1 < g.K) v.y = p[1];
-                if (k + 2 < g.K) v.z = p[2];
-                if (k + 3 < g.K) v.w = p[3];
+                if (k + 0 < g.K) v.x = ptr[0];
+                if (k + 1 < g.K) v.y = ptr[1];
+                if (k + 2 < g.K) v.z = ptr[2];
+                if (k + 3 < g.K) v.w = ptr[3];
             }
             ra[i] = v;
         }
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_VECS; ++i) {
-        const float *p = s.pb[i] + (int64_t)k0 * g.ldb;
+    } else {
+        const int i = p - T::A_VECS;
+        const float *ptr = s.pb[i] + (int64_t)k0 * g.ldb;
         const bool row_ok = !GK || (k0 + s.br[i] < g.K);
-        if (!GMN) {
-            rb[i] = row_ok ? ld4<VEC>(p) : zero;
+        if (BUF) {
+            const f32x4v v = raw_buffer_load_v4f32(r.b, s.ob[i], 0, 0);
+            rb[i] = make_float4(v[0], v[1], v[2], v[3]);
+        } else if (!GMN) {
+            rb[i] = row_ok ? ld4<VEC>(ptr) : zero;
         } else {
             const int n = n0 + s.bc[i];
             float4 v = zero;
             if (row_ok) {
                 if (VEC && n + 3 < g.N) {
-                    v = ld4<true>(p);
+                    v = ld4<true>(ptr);
                 } else {
-                    if (n + 0 < g.N) v.x = p[0];
-                    if (n + 1 < g.N) v.y = p[1];
-                    if (n + 2 < g.N) v.z = p[2];
-                    if (n + 3 < g.N) v.w = p[3];
+                    if (n + 0 < g.N) v.x = ptr[0];
+                    if (n + 1 < g.N) v.y = ptr[1];
+                    if (n + 2 < g.N) v.z = ptr[2];
+                    if (n + 3 < g.N) v.w = ptr[3];
                 }
             }
             rb[i] = v;
         }
     }
+}
+
+template <class T, bool VEC, bool GMN, bool GK>
+__device__ __forceinline__ void load_slice(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
+                                           float4 (&ra)[T::A_VECS], float4 (&rb)[T::B_VECS]) {
+    const SliceRsrc r = slice_rsrc<T>(g, m0, n0, k0);
+#pragma unroll
+    for (int p = 0; p < T::A_VECS + T::B_VECS; ++p) load_part<T, VEC, GMN, GK>(g, s, m0, n0, k0, r, p, ra, rb);
 }
 
 template <class T>
@@ -204,10 +254,16 @@ __device__ __forceinline__ void mfma_frag(const Frag<T> &f, f32x16 (&acc)[T::MB]
 }
 
 // All MFMAs of one slice.  The LDS reads of chunk c+1 are issued before the
-// MFMAs of chunk c, so their latency hides behind matrix-core work.
-template <class T>
+// MFMAs of chunk c, so their latency hides behind matrix-core work.  `issue(c)`
+// runs at the top of chunk c; the K loop uses it to spread the global loads of
+// a later slice over the slice's MFMAs instead of issuing them in one burst.
+struct NoIssue {
+    __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <class T, class Issue>
 __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn, int lane,
-                                              f32x16 (&acc)[T::MB][T::NB]) {
+                                              f32x16 (&acc)[T::MB][T::NB], const Issue &issue) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const float *As = stage + (wm * T::WM + l32) * T::LDA_S + h * T::HALF;
@@ -217,11 +273,18 @@ __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn
     read_frag<T>(As, Bs, 0, f[0]);
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
+        issue(c);
         if (c + 1 < CH) read_frag<T>(As, Bs, c + 1, f[(c + 1) & 1]);
         // Keep the compiler from sinking those reads below the MFMAs.
         __builtin_amdgcn_sched_barrier(0);
         mfma_frag<T>(f[c & 1], acc);
     }
+}
+
+template <class T>
+__device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn, int lane,
+                                              f32x16 (&acc)[T::MB][T::NB]) {
+    compute_slice<T>(stage, wm, wn, lane, acc, NoIssue());
 }
 
 // The K loop of one tile.  Slices are processed in the order: the partial
@@ -262,13 +325,29 @@ __device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int ti
         if (nk > 1) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(1), ra1, rb1);
         __syncthreads();
         int t = 0;
+        constexpr int PARTS = T::A_VECS + T::B_VECS;
+        constexpr int PER = (PARTS + T::HALF / 4 - 1) / (T::HALF / 4);   // groups per chunk
+        // The loads are unconditional: past the end they re-read the last slice
+        // (never stored), so the wait counts stay exact on every path.
         for (; t + 1 < nk; t += 2) {
-            if (t + 2 < nk) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 2), ra0, rb0);
-            compute_slice<T>(smem, wm, wn, lane, acc);
+            const int k2 = k0_of(t + 2 < nk ? t + 2 : nk - 1);
+            const SliceRsrc r2 = slice_rsrc<T>(g, m0, n0, k2);
+            compute_slice<T>(smem, wm, wn, lane, acc, [&](int c) {
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (c * PER + j < PARTS)
+                        load_part<T, VEC, GMN, false>(g, s, m0, n0, k2, r2, c * PER + j, ra0, rb0);
+            });
             store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
             __syncthreads();
-            if (t + 3 < nk) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 3), ra1, rb1);
-            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc);
+            const int k3 = k0_of(t + 3 < nk ? t + 3 : nk - 1);
+            const SliceRsrc r3 = slice_rsrc<T>(g, m0, n0, k3);
+            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc, [&](int c) {
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (c * PER + j < PARTS)
+                        load_part<T, VEC, GMN, false>(g, s, m0, n0, k3, r3, c * PER + j, ra1, rb1);
+            });
             if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
             __syncthreads();
         }

@@ -92,7 +92,8 @@ int sgemm_f32(int M, int N, int K, float alpha,
  * between variants and for tests.  Arguments after `variant` are those of
  * sgemm_f32.  Returns SGEMM_F32_ERR_NOT_APPLICABLE when the variant cannot
  * handle the request (SGEMM_F32_SKINNY with M > 16; a vector-load variant with
- * a pointer not 16-byte aligned or lda, ldb not multiples of 4).
+ * a pointer not 16-byte aligned, lda or ldb not a multiple of 4, or row strides
+ * so large that 128 rows of A or 32 rows of B span 2 GiB or more).
  */
 int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
                       const float *A, int lda, const float *B, int ldb,
