@@ -49,6 +49,12 @@ typedef float f32x4v __attribute__((ext_vector_type(4)));
 // the resource's extent return zeros instead of touching memory.
 __device__ f32x4v raw_buffer_load_v4f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+__device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+
+// A lane offset past every resource extent used here (extents stay below
+// 2^31 bytes): the load returns zero and touches no memory.
+constexpr int kOutOfRange = (int)0x80000000u;
 
 // Buffer resource over [base, base + bytes): raw (untyped) access with the
 // 32-bit data format, so every lane's offset is checked against `bytes`.
@@ -122,28 +128,32 @@ __device__ __forceinline__ float4 ld4(const float *p) {
 // or N edge, so rows of A beyond M and columns of B beyond N read as zero.
 // GK: the slice crosses the K edge, so k >= K reads as zero.  Nothing outside
 // the matrices is accessed.
-// Resources covering exactly the A and B elements of the slice at k0 of an
-// interior tile (used with 16-byte loads only).
+// Resources over the A and B elements of the slice at k0 that lie inside the
+// matrices: the rows of A below M, and B up to its last valid column in the
+// slice's last row.  A rows past M therefore read as zeros by themselves; B
+// columns past N need an out-of-range lane offset (load_part).
 struct SliceRsrc {
     __amdgpu_buffer_rsrc_t a, b;
 };
 
 template <class T>
 __device__ __forceinline__ SliceRsrc slice_rsrc(const GemmArgs &g, int m0, int n0, int k0) {
+    const int rows = min(T::BM, g.M - m0);
+    const int cols = min(T::BN, g.N - n0);
     SliceRsrc r;
-    r.a = make_rsrc(g.A + (int64_t)m0 * g.lda + k0, (int)(((T::BM - 1) * g.lda + T::BK) * 4));
-    r.b = make_rsrc(g.B + (int64_t)k0 * g.ldb + n0, (int)(((T::BK - 1) * g.ldb + T::BN) * 4));
+    r.a = make_rsrc(g.A + (int64_t)m0 * g.lda + k0, (int)(((rows - 1) * g.lda + T::BK) * 4));
+    r.b = make_rsrc(g.B + (int64_t)k0 * g.ldb + n0, (int)(((T::BK - 1) * g.ldb + cols) * 4));
     return r;
 }
 
-// Interior tiles with 16-byte loads go through the buffer resources `r`; the
-// other cases through the row pointers.
+// Slices that do not cross the K edge are loaded with 16-byte buffer loads
+// when VEC; the K-edge slice (GK) and 4-byte loads go through row pointers.
 template <class T, bool VEC, bool GMN, bool GK>
 __device__ __forceinline__ void load_part(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
                                           const SliceRsrc &r, int p, float4 (&ra)[T::A_VECS],
                                           float4 (&rb)[T::B_VECS]) {
     const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr bool BUF = VEC && !GMN && !GK;
+    constexpr bool BUF = VEC && !GK;
     if (p < T::A_VECS) {
         const int i = p;
         const float *ptr = s.pa[i] + k0;
@@ -169,8 +179,18 @@ __device__ __forceinline__ void load_part(const GemmArgs &g, const Stager<T> &s,
         const float *ptr = s.pb[i] + (int64_t)k0 * g.ldb;
         const bool row_ok = !GK || (k0 + s.br[i] < g.K);
         if (BUF) {
-            const f32x4v v = raw_buffer_load_v4f32(r.b, s.ob[i], 0, 0);
-            rb[i] = make_float4(v[0], v[1], v[2], v[3]);
+            const int n = n0 + s.bc[i];
+            const int off = (!GMN || n + 3 < g.N) ? s.ob[i] : kOutOfRange;
+            const f32x4v v = raw_buffer_load_v4f32(r.b, off, 0, 0);
+            float4 w = make_float4(v[0], v[1], v[2], v[3]);
+            if (GMN && n < g.N && n + 3 >= g.N) {
+                // The group straddles column N (only when N is not a multiple of 4).
+                w.x = raw_buffer_load_f32(r.b, s.ob[i], 0, 0);
+                w.y = raw_buffer_load_f32(r.b, n + 1 < g.N ? s.ob[i] + 4 : kOutOfRange, 0, 0);
+                w.z = raw_buffer_load_f32(r.b, n + 2 < g.N ? s.ob[i] + 8 : kOutOfRange, 0, 0);
+                w.w = 0.f;
+            }
+            rb[i] = w;
         } else if (!GMN) {
             rb[i] = row_ok ? ld4<VEC>(ptr) : zero;
         } else {
