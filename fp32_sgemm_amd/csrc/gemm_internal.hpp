@@ -22,8 +22,13 @@ struct GemmArgs {
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
-hipError_t launch_skinny(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);
+
+// The workspace of `stream` on the current device, at least `bytes` long.  It
+// stays valid for work queued on that stream until the next call that asks
+// for more.
+hipError_t stream_workspace(size_t bytes, hipStream_t stream, void **out);
 
 // Tile counts that each launcher's grid uses (host side, for the size check).
 int64_t mfma_large_grid(int M, int N);
@@ -31,8 +36,10 @@ int64_t mfma_small_grid(int M, int N);
 int64_t valu_grid(int M, int N);
 int64_t skinny_grid(int M, int N);
 
-// Largest M the skinny kernel handles.
+// Largest M the skinny kernel handles, and whether its 32-bit offsets cover
+// the strides.
 constexpr int kSkinnyMaxM = 16;
+bool skinny_fits(int lda, int ldb);
 
 // ---------------------------------------------------------------------------
 // Work-group to output-tile mapping.

@@ -50,8 +50,13 @@ bool prefer_small_tiles(int M, int N) {
     return large < 256;
 }
 
+bool aligned16(const float *A, int lda, const float *B, int ldb) {
+    return (reinterpret_cast<uintptr_t>(A) % 16 == 0) && (reinterpret_cast<uintptr_t>(B) % 16 == 0) &&
+           (lda % 4 == 0) && (ldb % 4 == 0);
+}
+
 int auto_variant(int M, int N, const float *A, int lda, const float *B, int ldb) {
-    if (M <= sgemm::kSkinnyMaxM) return SGEMM_F32_SKINNY;
+    if (M <= sgemm::kSkinnyMaxM && sgemm::skinny_fits(lda, ldb)) return SGEMM_F32_SKINNY;
     if (!vec_aligned(A, lda, B, ldb)) return SGEMM_F32_MFMA_SCALAR;
     return prefer_small_tiles(M, N) ? SGEMM_F32_MFMA_SMALL : SGEMM_F32_MFMA_LARGE;
 }
@@ -100,9 +105,9 @@ int run(int variant, int M, int N, int K, float alpha, const float *A, int lda, 
             if (sgemm::valu_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
             return to_status(sgemm::launch_valu(g, vec, stream));
         case SGEMM_F32_SKINNY:
-            if (M > sgemm::kSkinnyMaxM) return SGEMM_F32_ERR_NOT_APPLICABLE;
+            if (M > sgemm::kSkinnyMaxM || !sgemm::skinny_fits(lda, ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
             if (sgemm::skinny_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-            return to_status(sgemm::launch_skinny(g, stream));
+            return to_status(sgemm::launch_skinny(g, aligned16(A, lda, B, ldb), stream));
         default:
             return SGEMM_F32_ERR_VARIANT;
     }

@@ -1,0 +1,74 @@
+// Workspace for kernels that need one (the split reduction of the M <= 16
+// kernel).  The library keeps one workspace per (device, stream): work on one
+// stream runs in order, so successive calls on a stream can reuse the same
+// memory without further synchronisation, while calls on different streams
+// never share it.  A stream's workspace is allocated on its first use and
+// grown when a call needs more (growing waits for the stream's pending work
+// before freeing the old block); it is held until the process ends.  A new
+// block starts zero-filled, and kernels that keep counters in it leave them at
+// zero when they finish.
+#include <cstdint>
+#include <mutex>
+#include <vector>
+
+#include "gemm_internal.hpp"
+
+namespace sgemm {
+namespace {
+
+struct Entry {
+    int device;
+    hipStream_t stream;
+    void *ptr;
+    size_t bytes;
+};
+
+std::mutex g_mutex;
+std::vector<Entry> g_entries;
+
+constexpr size_t kMinBytes = (size_t)4 << 20;
+
+}  // namespace
+
+hipError_t stream_workspace(size_t bytes, hipStream_t stream, void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(g_mutex);
+    Entry *slot = nullptr;
+    for (Entry &x : g_entries)
+        if (x.device == dev && x.stream == stream) slot = &x;
+    if (slot != nullptr && slot->bytes >= bytes) {
+        *out = slot->ptr;
+        return hipSuccess;
+    }
+    size_t want = bytes < kMinBytes ? kMinBytes : bytes;
+    if (slot != nullptr) {
+        if (want < 2 * slot->bytes) want = 2 * slot->bytes;
+        // The old block may still be in use by work queued on this stream.
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return e;
+        e = hipFree(slot->ptr);
+        if (e != hipSuccess) return e;
+        slot->ptr = nullptr;
+        slot->bytes = 0;
+    }
+    void *p = nullptr;
+    e = hipMalloc(&p, want);
+    if (e != hipSuccess) return e;
+    e = hipMemset(p, 0, want);
+    if (e != hipSuccess) {
+        hipFree(p);
+        return e;
+    }
+    if (slot == nullptr) {
+        g_entries.push_back(Entry{dev, stream, p, want});
+    } else {
+        slot->ptr = p;
+        slot->bytes = want;
+    }
+    *out = p;
+    return hipSuccess;
+}
+
+}  // namespace sgemm

@@ -2,21 +2,36 @@
 //
 // With M = 16 and N = K = 4096 the product does 8 FLOP per byte of B it must
 // stream, below the MI355X ridge point of about 20 FLOP per byte, so the kernel
-// is bound by HBM bandwidth: its job is to stream B exactly once with enough
-// loads in flight.  (Decode-time GEMV-like shapes sit on the bandwidth roof,
-// "Writing a Fast Matmul in CUDA, Step by Step", section "In the real world";
-// too few output tiles to fill the machine is the case where the reduction is
-// split, "How a Matmul Kernel Gets Fast", section 15.)
+// is bound by HBM bandwidth: its job is to stream B exactly once, in row
+// segments long enough for the memory system (256 bytes) and with enough loads
+// in flight.  (Decode-time GEMV-like shapes sit on the bandwidth roof, "Writing
+// a Fast Matmul in CUDA, Step by Step", section "In the real world"; too few
+// output tiles to fill the machine is where the reduction is split, "How a
+// Matmul Kernel Gets Fast", section 15.)
 //
-// Each work-group owns a 16-column strip of C and all M <= 16 rows.  Its NW
-// waves split K into contiguous ranges; each wave streams its rows of the strip
-// straight from global memory into MFMA operand registers (no LDS staging: no
-// element of B is used by more than one wave).  For a group of 16 k values a
-// lane loads A(l % 16, k0 + 4*(l/16) + 0..3) as one 16-byte load and the four
-// B values B(k0 + 4*(l/16) + e, n0 + l % 16), e = 0..3, then issues four
-// v_mfma_f32_16x16x4_f32 in which lane l supplies k = k0 + 4*(l/16) + e.  The
-// per-wave partial 16x16 tiles are added in LDS in a fixed wave order, so the
-// result does not depend on timing.
+// Work decomposition.  A work-group owns a 64-column strip of C and one of
+// `splits` contiguous ranges of K; its 4 waves split that range again.  The
+// partial strips of the splits go to the stream's workspace and a second
+// kernel adds them in split order and finishes C (with one split, the first
+// kernel finishes C itself).  A single-kernel form in which the last arriving
+// work-group of a strip adds the partials measured 3x slower: the device-wide
+// fences it needs to see the other XCDs' partials write back and invalidate
+// whole L2 caches.
+//
+// Inner step.  For a block of 16 rows of B starting at kb, lane l (h = l/16,
+// j = l%16) loads columns 4j..4j+3 of rows kb + 4h + q, q = 0..3 (four 16-byte
+// loads: 4 rows x 256 bytes per wave instruction), and A(j, kb + 4h .. +3) (one
+// 16-byte load).  Element e of the B group is the operand of the e-th of four
+// v_mfma_f32_16x16x4_f32 that accumulate columns 4j + e of the strip, so no
+// data is reshuffled: the MFMA's column index j stands for strip column 4j + e.
+// In the q-th step lane l supplies k = kb + 4h + q, with A from component q of
+// its A group.
+//
+// All loads are buffer loads against resources that end at the last valid
+// element of the batch: rows of A past M and rows of B past the split's range
+// read as zeros by themselves; groups past column N of B or past the range's
+// last k of A get an out-of-range lane offset, and groups that straddle those
+// edges are loaded element by element.  Nothing outside the matrices is read.
 #include "gemm_internal.hpp"
 
 namespace sgemm {
@@ -24,74 +39,176 @@ namespace {
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 
-constexpr int SK_NW = 8;                 // waves per work-group
-constexpr int SK_NT = SK_NW * 64;
-constexpr int SK_BN = 16;                // columns of C per work-group
-constexpr int SK_UNROLL = 8;             // 16-row groups in flight per wave
+__device__ f32x4v sk_buffer_load_v4f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
+__device__ float sk_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
 
-__device__ __forceinline__ void skinny_group(const GemmArgs &g, int n0, int kg, int lane,
-                                             bool guard, f32x4v &acc) {
-    const int i = lane & 15;                       // row of A / column of the strip
-    const int kq = kg + 4 * (lane >> 4);           // first of this lane's 4 k values
-    float a[4], b[4];
-    if (!guard) {
-        const float *pa = g.A + (int64_t)i * g.lda + kq;
-        a[0] = pa[0]; a[1] = pa[1]; a[2] = pa[2]; a[3] = pa[3];
-        const float *pb = g.B + (int64_t)kq * g.ldb + n0 + i;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) b[e] = pb[e * g.ldb];
-    } else {
-        const bool rin = i < g.M, cin = n0 + i < g.N;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const bool kin = kq + e < g.K;
-            a[e] = (rin && kin) ? g.A[(int64_t)i * g.lda + kq + e] : 0.f;
-            b[e] = (cin && kin) ? g.B[(int64_t)(kq + e) * g.ldb + n0 + i] : 0.f;
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+constexpr int kOff = (int)0x80000000u;   // past every extent used here: reads zero, no access
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, 0x00020000);
 }
 
-__global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(GemmArgs g, int tiles_n) {
-    __shared__ float red[SK_NW][16 * 16];
-    int tm, tn;
-    tile_of_block(blockIdx.x, 1, tiles_n, 1, tm, tn);
-    const int n0 = tn * SK_BN;
+constexpr int SK_NW = 4;                 // waves per work-group
+constexpr int SK_NT = SK_NW * 64;
+constexpr int SK_BN = 64;                // columns of C per work-group
+constexpr int SK_U = 2;                  // 16-row blocks per batch
+constexpr int SK_ROWS = SK_U * 16;       // rows of B per batch
+
+struct SkinnyArgs {
+    GemmArgs g;
+    float *ws;            // splits x M x N partial sums (unused with one split)
+    int splits;
+    int split_rows;       // rows of K per split, a multiple of SK_ROWS
+};
+
+// Four consecutive elements of one row at byte offset `off` of resource `r`,
+// starting `col` elements into the row; elements at or past `limit` read as
+// zero.  VEC: one 16-byte load when the group lies inside.
+template <bool VEC>
+__device__ __forceinline__ float4 load_group(__amdgpu_buffer_rsrc_t r, int off, int col, int limit) {
+    float4 v;
+    if (VEC && col + 3 < limit) {
+        const f32x4v w = sk_buffer_load_v4f32(r, off, 0, 0);
+        v = make_float4(w[0], w[1], w[2], w[3]);
+    } else if (VEC && col >= limit) {
+        v = make_float4(0.f, 0.f, 0.f, 0.f);
+    } else {
+        v.x = sk_buffer_load_f32(r, col + 0 < limit ? off + 0 : kOff, 0, 0);
+        v.y = sk_buffer_load_f32(r, col + 1 < limit ? off + 4 : kOff, 0, 0);
+        v.z = sk_buffer_load_f32(r, col + 2 < limit ? off + 8 : kOff, 0, 0);
+        v.w = sk_buffer_load_f32(r, col + 3 < limit ? off + 12 : kOff, 0, 0);
+    }
+    return v;
+}
+
+struct Batch {
+    float4 a[SK_U];
+    float4 b[SK_U][4];
+};
+
+// Loads the batch whose first row of B (column of A) is kb; rows at or past
+// kend belong to another split or lie past K and read as zero.
+template <bool VEC>
+__device__ __forceinline__ void load_batch(const GemmArgs &g, int n0, int kb, int kend, int lane, Batch &bt) {
+    const int rows = min(SK_ROWS, kend - kb);
+    const int cols = min(SK_BN, g.N - n0);
+    const __amdgpu_buffer_rsrc_t rb = sk_rsrc(g.B + (int64_t)kb * g.ldb + n0,
+                                              (int)(((int64_t)(rows - 1) * g.ldb + cols) * 4));
+    const __amdgpu_buffer_rsrc_t ra = sk_rsrc(g.A + kb, (int)(((int64_t)(g.M - 1) * g.lda + rows) * 4));
+    const int h = lane >> 4, j = lane & 15;
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = u * 16 + 4 * h + q;                  // row of B within the batch
+            bt.b[u][q] = load_group<VEC>(rb, (int)((r * g.ldb + 4 * j) * 4), 4 * j, r < rows ? cols : 0);
+        }
+        const int k = u * 16 + 4 * h;                          // first k of this lane's A group
+        bt.a[u] = load_group<VEC>(ra, (int)((j * g.lda + k) * 4), k, j < g.M ? rows : 0);
+    }
+}
+
+__device__ __forceinline__ void consume_batch(const Batch &bt, f32x4v (&acc)[4]) {
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+        const float av[4] = {bt.a[u].x, bt.a[u].y, bt.a[u].z, bt.a[u].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float4 b = bt.b[u][q];
+            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.x, acc[0], 0, 0, 0);
+            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.y, acc[1], 0, 0, 0);
+            acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.z, acc[2], 0, 0, 0);
+            acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.w, acc[3], 0, 0, 0);
+        }
+    }
+}
+
+template <bool VEC>
+__global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(SkinnyArgs sa, int strips) {
+    __shared__ float red[SK_NW][16 * SK_BN];
+    const GemmArgs &g = sa.g;
+    // Work-group -> (split, strip); consecutive strips stay on one XCD.
+    int split, strip;
+    tile_of_block(blockIdx.x, sa.splits, strips, 1, split, strip);
+    const int n0 = strip * SK_BN;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
 
-    // Contiguous K range of this wave, in whole groups of 16.
-    const int groups = (g.K + 15) / 16;
-    const int per_wave = (groups + SK_NW - 1) / SK_NW;
-    const int gbeg = wave * per_wave;
-    const int gend = min(groups, gbeg + per_wave);
-    const bool edge = (g.M < 16) || (n0 + SK_BN > g.N);
+    const int kbeg = split * sa.split_rows;
+    const int kend = min(g.K, kbeg + sa.split_rows);
+    // Contiguous part of the split for this wave, in whole batches.
+    const int batches = (kend - kbeg + SK_ROWS - 1) / SK_ROWS;
+    const int per_wave = (batches + SK_NW - 1) / SK_NW;
+    const int bbeg = wave * per_wave;
+    const int bend = min(batches, bbeg + per_wave);
 
-    f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-    int gi = gbeg;
-    for (; gi + SK_UNROLL <= gend; gi += SK_UNROLL) {
-        const bool guard = edge || (gi + SK_UNROLL) * 16 > g.K;
+    f32x4v acc[4];
 #pragma unroll
-        for (int u = 0; u < SK_UNROLL; ++u) skinny_group(g, n0, (gi + u) * 16, lane, guard, acc);
+    for (int e = 0; e < 4; ++e) acc[e] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    Batch b0, b1;
+    int b = bbeg;
+    if (b < bend) load_batch<VEC>(g, n0, kbeg + b * SK_ROWS, kend, lane, b0);
+    // The loads in the loop are unconditional (past the end they re-read the
+    // wave's last batch, which is then not consumed) so the wait counts stay
+    // exact.
+    for (; b + 1 < bend; b += 2) {
+        load_batch<VEC>(g, n0, kbeg + (b + 1) * SK_ROWS, kend, lane, b1);
+        consume_batch(b0, acc);
+        load_batch<VEC>(g, n0, kbeg + (b + 2 < bend ? b + 2 : bend - 1) * SK_ROWS, kend, lane, b0);
+        consume_batch(b1, acc);
     }
-    for (; gi < gend; ++gi) skinny_group(g, n0, gi * 16, lane, true, acc);
+    if (b < bend) consume_batch(b0, acc);
 
-    // Accumulator register r holds row 4*(l/16) + r, column l % 16.
+    // acc[e] register r of lane l holds row 4*(l/16) + r, strip column
+    // 4*(l%16) + e.  Add the waves' partials in wave order.
+    const int h = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red[wave][(4 * (lane >> 4) + r) * 16 + (lane & 15)] = acc[r];
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][(4 * h + r) * SK_BN + 4 * j + e] = acc[e][r];
     __syncthreads();
-    if (threadIdx.x < 256) {
-        const int row = threadIdx.x >> 4, col = threadIdx.x & 15;
+    constexpr int PER_T = 16 * SK_BN / SK_NT;   // strip elements per thread
+    float part[PER_T];
+#pragma unroll
+    for (int t = 0; t < PER_T; ++t) {
+        const int idx = threadIdx.x + t * SK_NT;
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < SK_NW; ++w) s += red[w][threadIdx.x];
+        for (int w = 0; w < SK_NW; ++w) s += red[w][idx];
+        part[t] = s;
+    }
+
+#pragma unroll
+    for (int t = 0; t < PER_T; ++t) {
+        const int idx = threadIdx.x + t * SK_NT;
+        const int row = idx / SK_BN, col = idx % SK_BN;
         if (row < g.M && n0 + col < g.N) {
-            float *p = g.C + (int64_t)row * g.ldc + n0 + col;
-            float v = g.alpha * s;
-            if (g.beta != 0.f) v = fmaf(g.beta, *p, v);
-            *p = v;
+            if (sa.splits > 1) {
+                sa.ws[((int64_t)split * g.M + row) * g.N + n0 + col] = part[t];
+            } else {
+                float *p = g.C + (int64_t)row * g.ldc + n0 + col;
+                float v = g.alpha * part[t];
+                if (g.beta != 0.f) v = fmaf(g.beta, *p, v);
+                *p = v;
+            }
         }
+    }
+}
+
+// C = alpha * (sum of the split partials, in split order) + beta * C.
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, const float *ws, int splits) {
+    const int64_t total = (int64_t)g.M * g.N;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        float s = 0.f;
+        for (int sp = 0; sp < splits; ++sp) s += ws[sp * total + t];
+        const int64_t i = t / g.N, jj = t - i * g.N;
+        float *p = g.C + i * g.ldc + jj;
+        float v = g.alpha * s;
+        if (g.beta != 0.f) v = fmaf(g.beta, *p, v);
+        *p = v;
     }
 }
 
@@ -102,10 +219,47 @@ int64_t skinny_grid(int M, int N) {
     return (N + SK_BN - 1) / SK_BN;
 }
 
-hipError_t launch_skinny(const GemmArgs &g, hipStream_t stream) {
-    const int tiles_n = (g.N + SK_BN - 1) / SK_BN;
-    hipLaunchKernelGGL(sgemm_skinny_kernel, dim3(tiles_n), dim3(SK_NT), 0, stream, g, tiles_n);
-    return hipGetLastError();
+bool skinny_fits(int lda, int ldb) {
+    // One batch of B and all 16 rows of A must be addressable with 32-bit
+    // byte offsets.
+    const int64_t limit = (int64_t)1 << 31;
+    return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < limit && ((int64_t)16 * lda + SK_ROWS) * 4 < limit;
+}
+
+hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
+    const int strips = (g.N + SK_BN - 1) / SK_BN;
+    // Aim for about two work-groups per compute unit; keep every split at
+    // least 256 rows long.
+    const int want = (512 + strips - 1) / strips;
+    const int max_splits = (g.K + 255) / 256;
+    int splits = want < max_splits ? want : max_splits;
+    if (splits < 1) splits = 1;
+    int split_rows = (g.K + splits - 1) / splits;
+    split_rows = (split_rows + SK_ROWS - 1) / SK_ROWS * SK_ROWS;
+    splits = (g.K + split_rows - 1) / split_rows;
+
+    SkinnyArgs sa;
+    sa.g = g;
+    sa.ws = nullptr;
+    sa.splits = splits;
+    sa.split_rows = splits > 1 ? split_rows : g.K;
+    if (splits > 1) {
+        hipError_t e = stream_workspace((size_t)splits * g.M * g.N * sizeof(float), stream,
+                                        reinterpret_cast<void **>(&sa.ws));
+        if (e != hipSuccess) return e;
+    }
+    const dim3 grid(strips * splits);
+    if (vec_loads) hipLaunchKernelGGL(sgemm_skinny_kernel<true>, grid, dim3(SK_NT), 0, stream, sa, strips);
+    else hipLaunchKernelGGL(sgemm_skinny_kernel<false>, grid, dim3(SK_NT), 0, stream, sa, strips);
+    hipError_t e = hipGetLastError();
+    if (splits > 1 && e == hipSuccess) {
+        const int64_t total = (int64_t)g.M * g.N;
+        int64_t blocks = (total + 255) / 256;
+        if (blocks > 4096) blocks = 4096;
+        hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, sa.ws, splits);
+        e = hipGetLastError();
+    }
+    return e;
 }
 
 }  // namespace sgemm

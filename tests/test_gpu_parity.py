@@ -65,7 +65,8 @@ def test_ragged_integer_bitexact(sg, variant, shape):
 
 
 SKINNY = [(1, 1, 1), (16, 16, 16), (16, 4096, 64), (3, 33, 100), (16, 100, 4099),
-          (7, 257, 513), (16, 16, 17), (12, 64, 2000)]
+          (7, 257, 513), (16, 16, 17), (12, 64, 2000), (5, 130, 777), (16, 65, 1000),
+          (1, 1, 5000), (16, 4096, 300), (16, 2050, 8191)]
 
 
 @pytest.mark.parametrize("variant", ["skinny", "auto", "mfma_scalar", "valu"])
@@ -192,6 +193,30 @@ def test_repeat_runs_bitwise_identical(sg, variant):
     st2, C2, _ = run_lib(sg, VID[variant], A, B, C0, 1.0, 0.5)
     assert st1 == 0 and st2 == 0
     assert np.array_equal(C1.view(np.uint32), C2.view(np.uint32))
+
+
+def test_skinny_concurrent_streams(sg):
+    """Two M <= 16 products with split reductions in flight on two streams at
+    once: each call's scratch memory is its own."""
+    M, N, K = 16, 2048, 4096
+    A1, B1, _ = _inputs(M, N, K, "uniform", 31, c0=False)
+    A2, B2, _ = _inputs(M, N, K, "uniform", 32, c0=False)
+    d = [torch.from_numpy(x).cuda() for x in (A1, B1, A2, B2)]
+    C1 = torch.zeros(M, N, device="cuda:0")
+    C2 = torch.zeros(M, N, device="cuda:0")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        st1 = sg.sgemm_f32_variant(4, M, N, K, 1.0, d[0].data_ptr(), K, d[1].data_ptr(), N, 0.0,
+                                   C1.data_ptr(), N, s1.cuda_stream)
+        st2 = sg.sgemm_f32_variant(4, M, N, K, 1.0, d[2].data_ptr(), K, d[3].data_ptr(), N, 0.0,
+                                   C2.data_ptr(), N, s2.cuda_stream)
+        assert st1 == 0 and st2 == 0
+    torch.cuda.synchronize()
+    ok, info = check_full(C1.cpu().numpy(), A1, B1, 1.0, 0.0, None)
+    assert ok, info
+    ok, info = check_full(C2.cpu().numpy(), A2, B2, 1.0, 0.0, None)
+    assert ok, info
 
 
 def test_non_default_stream_ordering(sg):
