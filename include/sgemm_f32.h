@@ -33,6 +33,11 @@
  *     returns without waiting for it.  No host or device synchronisation.
  *   - The functions hold no per-call state and may be called from several host
  *     threads at once.
+ *   - Device memory: none for M > 16.  For M <= 16 with a split reduction the
+ *     library keeps one workspace per (device, stream), allocated with
+ *     hipMalloc on the first such call on that stream (a few MiB, grown when a
+ *     call needs more, which waits for that stream's pending work) and held
+ *     until the process ends.  Calls on different streams never share it.
  *
  * Special cases:
  *   - M == 0 or N == 0: nothing is done, returns 0.
