@@ -403,10 +403,28 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     else k_loop<T, VEC, false>(g, m0, n0, tid, wm, wn, lane, smem, acc);
 
     // Epilogue.  Accumulator register r of a 32x32 block holds, in lane l,
-    // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.
+    // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.  C is read in
+    // a pass of its own before the first store: with a store between two C
+    // loads the second load would have to wait for the first (the compiler
+    // cannot tell their addresses apart), one memory round trip per element.
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const float alpha = g.alpha, beta = g.beta;
+    float cv[T::MB][T::NB][16];
+    if (beta != 0.f) {
+#pragma unroll
+        for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < T::NB; ++jb) {
+                const int col = n0 + wn * T::WN + jb * 32 + l32;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int row = m0 + wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool ok = !edge_mn || (row < g.M && col < g.N);
+                    cv[ib][jb][r] = ok ? g.C[(int64_t)row * g.ldc + col] : 0.f;
+                }
+            }
+    }
 #pragma unroll
     for (int ib = 0; ib < T::MB; ++ib)
 #pragma unroll
@@ -416,10 +434,9 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
             for (int r = 0; r < 16; ++r) {
                 const int row = m0 + wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (edge_mn && (row >= g.M || col >= g.N)) continue;
-                float *p = g.C + (int64_t)row * g.ldc + col;
                 float v = alpha * acc[ib][jb][r];
-                if (beta != 0.f) v = fmaf(beta, *p, v);
-                *p = v;
+                if (beta != 0.f) v = fmaf(beta, cv[ib][jb][r], v);
+                g.C[(int64_t)row * g.ldc + col] = v;
             }
         }
 }
