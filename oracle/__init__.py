@@ -1,4 +1,5 @@
-"""CPU oracle for row-major FP32 GEMM, ``C = alpha*A*B + beta*C0``.
+"""CPU oracle for row-major FP32 GEMM, ``C = alpha*A*B + beta*C0``, and for its
+form with transposed operands, ``C = alpha*op(A)*op(B) + beta*C0``.
 
 TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
 CPU-baseline leg may import this package.  The GPU library never imports it and
@@ -65,6 +66,11 @@ def _bind(path: str):
     lib.oracle_sgemm_f64_entries.argtypes = [i, i, i, f, p, l, p, l, f, p, l,
                                              l, p, p, p, p]
     lib.oracle_sgemm_f64_entries.restype = i
+    lib.oracle_sgemm_op_f64.argtypes = [i, i, i, i, i, f, p, l, p, l, f, p, l, p, p]
+    lib.oracle_sgemm_op_f64.restype = i
+    lib.oracle_sgemm_op_f64_entries.argtypes = [i, i, i, i, i, f, p, l, p, l, f,
+                                                p, l, l, p, p, p, p]
+    lib.oracle_sgemm_op_f64_entries.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
     return lib
@@ -163,6 +169,72 @@ def sgemm_ref_entries(A: np.ndarray, B: np.ndarray, rows, cols,
     return out, absab
 
 
+def _op_shapes(A, B, trans_a, trans_b):
+    """(M, N, K) of op(A) * op(B) for stored arrays A and B."""
+    M, Ka = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    Kb, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    if Ka != Kb:
+        raise ValueError("inner dimensions differ")
+    return M, N, Ka
+
+
+def _c0_ld(C0, M, N, beta, check_shape=True):
+    if C0 is not None:
+        if check_shape and C0.shape != (M, N):
+            raise ValueError("C0 shape")
+        return _ld(C0, "C0")
+    if np.float32(beta) != 0:
+        raise ValueError("beta != 0 needs C0")
+    return max(N, 1)
+
+
+def sgemm_ref_op(A: np.ndarray, B: np.ndarray, trans_a: bool = False,
+                 trans_b: bool = False, alpha: float = 1.0, beta: float = 0.0,
+                 C0: np.ndarray | None = None, _lib_override=None):
+    """Full float64 product ``alpha * op(A) * op(B) + beta * C0``.
+
+    ``A`` and ``B`` are the stored arrays: A is M x K, or K x M when
+    ``trans_a`` (then op(A) is its transpose); B is K x N, or N x K when
+    ``trans_b``.  Returns ``(Cref, absAB)``, both M x N float64.
+    """
+    M, N, K = _op_shapes(A, B, trans_a, trans_b)
+    lda, ldb = _ld(A, "A"), _ld(B, "B")
+    ldc = _c0_ld(C0, M, N, beta)
+    Cref = np.empty((M, N), dtype=np.float64)
+    absab = np.empty((M, N), dtype=np.float64)
+    lib = _lib_override or _load()
+    rc = lib.oracle_sgemm_op_f64(int(bool(trans_a)), int(bool(trans_b)), M, N, K,
+                                 float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                 float(beta), _ptr(C0), ldc, _ptr(Cref), _ptr(absab))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sgemm_op_f64 failed with {rc}")
+    return Cref, absab
+
+
+def sgemm_ref_op_entries(A: np.ndarray, B: np.ndarray, rows, cols,
+                         trans_a: bool = False, trans_b: bool = False,
+                         alpha: float = 1.0, beta: float = 0.0,
+                         C0: np.ndarray | None = None, _lib_override=None):
+    """Selected entries ``(rows[t], cols[t])`` of ``sgemm_ref_op``'s product."""
+    M, N, K = _op_shapes(A, B, trans_a, trans_b)
+    lda, ldb = _ld(A, "A"), _ld(B, "B")
+    ldc = _c0_ld(C0, M, N, beta, check_shape=False)
+    r = np.ascontiguousarray(rows, dtype=np.int64)
+    c = np.ascontiguousarray(cols, dtype=np.int64)
+    if r.shape != c.shape or r.ndim != 1:
+        raise ValueError("rows and cols must be equal-length vectors")
+    out = np.empty(r.shape[0], dtype=np.float64)
+    absab = np.empty(r.shape[0], dtype=np.float64)
+    lib = _lib_override or _load()
+    rc = lib.oracle_sgemm_op_f64_entries(int(bool(trans_a)), int(bool(trans_b)), M, N, K,
+                                         float(alpha), _ptr(A), lda, _ptr(B), ldb,
+                                         float(beta), _ptr(C0), ldc, r.shape[0],
+                                         _ptr(r), _ptr(c), _ptr(out), _ptr(absab))
+    if rc != 0:
+        raise RuntimeError(f"oracle_sgemm_op_f64_entries failed with {rc}")
+    return out, absab
+
+
 def error_bound(absab: np.ndarray, alpha: float, beta: float,
                 c0_vals: np.ndarray | None, rel: float = REL_TOL) -> np.ndarray:
     """Element-wise bound rel * (|alpha|*absAB + |beta|*|C0|) in float64."""
@@ -221,6 +293,14 @@ class BoundOracle:
     def sgemm_ref_entries(self, A, B, rows, cols, alpha=1.0, beta=0.0, C0=None):
         return sgemm_ref_entries(A, B, rows, cols, alpha, beta, C0,
                                  _lib_override=self._lib)
+
+    def sgemm_ref_op(self, A, B, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, C0=None):
+        return sgemm_ref_op(A, B, trans_a, trans_b, alpha, beta, C0, _lib_override=self._lib)
+
+    def sgemm_ref_op_entries(self, A, B, rows, cols, trans_a=False, trans_b=False,
+                             alpha=1.0, beta=0.0, C0=None):
+        return sgemm_ref_op_entries(A, B, rows, cols, trans_a, trans_b, alpha, beta, C0,
+                                    _lib_override=self._lib)
 
 
 SOURCE_PATH = _SRC

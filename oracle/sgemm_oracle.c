@@ -138,3 +138,89 @@ int oracle_sgemm_f64_entries(int M, int N, int K, float alpha,
     }
     return 0;
 }
+
+/*
+ * Transposed operands.  The library the pages compare against handles every
+ * transpose of its operands, and its kernel names carry the operand forms
+ * ("nn": neither operand transposed) ("Writing a Fast Matmul in CUDA, Step by
+ * Step", section "In the real world").  Here op(A) is the M x K left operand
+ * and op(B) the K x N right operand of the same product:
+ *
+ *   trans_a == 0:  A is stored M x K and op(A)(i, k) = A[i*lda + k]
+ *   trans_a != 0:  A is stored K x M and op(A)(i, k) = A[k*lda + i]
+ *   trans_b == 0:  B is stored K x N and op(B)(k, j) = B[k*ldb + j]
+ *   trans_b != 0:  B is stored N x K and op(B)(k, j) = B[j*ldb + k]
+ *
+ * C = alpha * op(A) * op(B) + beta * C0, with C0 and C M x N row-major as
+ * above, the same special cases, and the same k order.  Written element by
+ * element through op_elem, with no reordering for speed.
+ */
+static double op_elem(const float *X, long ld, int trans, long r, long c)
+{
+    return (double)(trans ? X[c * ld + r] : X[r * ld + c]);
+}
+
+static void op_dot(int trans_a, int trans_b, int K, const float *A, long lda,
+                   const float *B, long ldb, long i, long j,
+                   double *acc_out, double *aac_out)
+{
+    double acc = 0.0, aac = 0.0;
+    for (int k = 0; k < K; ++k) {
+        const double p = op_elem(A, lda, trans_a, i, k) * op_elem(B, ldb, trans_b, k, j);
+        acc += p;
+        aac += fabs(p);
+    }
+    *acc_out = acc;
+    *aac_out = aac;
+}
+
+/* Full product with transposed operands; Cref and absab as in oracle_sgemm_f64. */
+int oracle_sgemm_op_f64(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, long lda,
+                        const float *B, long ldb,
+                        float beta, const float *C0, long ldc,
+                        double *Cref, double *absab)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    if (M == 0 || N == 0) return 0;
+    const int use_product = (alpha != 0.0f) && (K > 0);
+
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < M; ++i) {
+        for (int j = 0; j < N; ++j) {
+            double acc = 0.0, aac = 0.0;
+            if (use_product) op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);
+            const double prod = use_product ? (double)alpha * acc : 0.0;
+            const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[(long)i * ldc + j];
+            Cref[(long)i * N + j] = prod + old;
+            if (absab != NULL) absab[(long)i * N + j] = use_product ? aac : 0.0;
+        }
+    }
+    return 0;
+}
+
+/* Selected entries of the product with transposed operands. */
+int oracle_sgemm_op_f64_entries(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                                const float *A, long lda,
+                                const float *B, long ldb,
+                                float beta, const float *C0, long ldc,
+                                long n, const long *rows, const long *cols,
+                                double *out, double *absab)
+{
+    if (M < 0 || N < 0 || K < 0) return 1;
+    for (long t = 0; t < n; ++t)
+        if (rows[t] < 0 || rows[t] >= M || cols[t] < 0 || cols[t] >= N) return 1;
+    const int use_product = (alpha != 0.0f) && (K > 0);
+
+#pragma omp parallel for schedule(static)
+    for (long t = 0; t < n; ++t) {
+        const long i = rows[t], j = cols[t];
+        double acc = 0.0, aac = 0.0;
+        if (use_product) op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);
+        const double prod = use_product ? (double)alpha * acc : 0.0;
+        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];
+        out[t] = prod + old;
+        if (absab != NULL) absab[t] = use_product ? aac : 0.0;
+    }
+    return 0;
+}

@@ -23,10 +23,13 @@ def load_cases(fname):
         name = head.split(None, 1)[1]
         M, N, K = (int(v) for v in lines.pop(0).split(":")[1].split())
         alpha, beta = (float(v) for v in lines.pop(0).split(":")[1].split())
+        ta = tb = 0
+        if lines[0].startswith("trans:"):
+            ta, tb = (int(v) for v in lines.pop(0).split(":")[1].split())
         assert lines.pop(0) == "A:"
-        A = _rows(lines, M)
+        A = _rows(lines, K if ta else M)
         assert lines.pop(0) == "B:"
-        B = _rows(lines, K)
+        B = _rows(lines, N if tb else K)
         c0h = lines.pop(0)
         C0 = None
         if c0h != "C0: none":
@@ -36,5 +39,5 @@ def load_cases(fname):
         C = _rows(lines, M).astype(np.float64)
         assert lines.pop(0) == "end"
         cases.append(dict(name=name, M=M, N=N, K=K, alpha=alpha, beta=beta,
-                          A=A, B=B, C0=C0, C=C))
+                          A=A, B=B, C0=C0, C=C, trans_a=bool(ta), trans_b=bool(tb)))
     return cases

@@ -1,7 +1,7 @@
 """Pins for the CPU oracle: checks against facts fixed outside the oracle itself.
 
 Each pin takes an object ``o`` with the oracle API (``sgemm_ref``,
-``sgemm_ref_entries``) so that the same pins can be run against a copy of the
+``sgemm_ref_entries``, ``sgemm_ref_op``, ``sgemm_ref_op_entries``) so that the same pins can be run against a copy of the
 oracle with a planted mistake, which at least one of them must catch.
 
 What fixes each expected value (none is produced by the code under test):
@@ -15,6 +15,9 @@ What fixes each expected value (none is produced by the code under test):
   * all-ones operands: every entry equals K*alpha + beta*C0 exactly;
   * alpha = 0 and beta = 0: the unused operands are not read (NaN stays out);
   * the float64 library matmul on random inputs, to within float64 rounding;
+  * for the transposed-operand form: its own hand-worked fixture, numpy's exact
+    int64 matmul of the explicitly transposed integer operands, the float64
+    library matmul, and (op(A) op(B))^T = op(B)^T op(A)^T;
   * the standard deviation sqrt(K/9) of a dot product of uniform[-1,1) vectors,
     which gives the "typical size 21" of entries at n = 4096 that "Writing a
     Fast Matmul in CUDA, Step by Step" reports in its "Step 1" section.
@@ -235,7 +238,86 @@ def pin_uniform_statistics(o):
     assert abs(sd / want - 1) < 0.05, (sd, want)
 
 
+_FORMS = [(False, False), (False, True), (True, False), (True, True)]
+
+
+def _stored(x, trans):
+    """The array whose transposed reading is x (a fresh row-major copy)."""
+    return np.ascontiguousarray(x.T) if trans else x
+
+
+def pin_op_golden(o):
+    for c in load_cases("hand_trans.txt"):
+        Cref, _ = o.sgemm_ref_op(c["A"], c["B"], c["trans_a"], c["trans_b"],
+                                 c["alpha"], c["beta"], c["C0"])
+        assert np.array_equal(Cref, c["C"]), (c["name"], Cref, c["C"])
+
+
+def pin_op_integer_exact(o):
+    # Rectangular and all different (M, N, K), so a swapped extent or index shows.
+    rng = _rng(21)
+    M, N, K = 7, 5, 11
+    Ai = rng.integers(-4, 5, size=(M, K))
+    Bi = rng.integers(-4, 5, size=(K, N))
+    want = (Ai @ Bi).astype(np.float64)              # exact in int64
+    for ta, tb in _FORMS:
+        A = _stored(Ai.astype(np.float32), ta)
+        B = _stored(Bi.astype(np.float32), tb)
+        Cref, absab = o.sgemm_ref_op(A, B, ta, tb)
+        assert np.array_equal(Cref, want), ("integer product", ta, tb)
+        assert np.array_equal(absab, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64)), ("|A||B|", ta, tb)
+
+
+def pin_op_library_matmul(o):
+    # Padded views (row stride larger than the width) for every stored operand.
+    rng = _rng(22)
+    M, N, K = 9, 6, 13
+    X = _uniform(rng, (M, K))
+    Y = _uniform(rng, (K, N))
+    C0 = _uniform(rng, (M, N))
+    want = 1.25 * (X.astype(np.float64) @ Y.astype(np.float64)) - 0.75 * C0.astype(np.float64)
+    for ta, tb in _FORMS:
+        A = _stored(X, ta)
+        B = _stored(Y, tb)
+        Ap = np.zeros((A.shape[0], A.shape[1] + 3), np.float32); Ap[:, :A.shape[1]] = A
+        Bp = np.zeros((B.shape[0], B.shape[1] + 5), np.float32); Bp[:, :B.shape[1]] = B
+        Cref, _ = o.sgemm_ref_op(Ap[:, :A.shape[1]], Bp[:, :B.shape[1]], ta, tb, 1.25, -0.75, C0)
+        assert np.allclose(Cref, want, rtol=1e-13, atol=1e-13), ("library matmul", ta, tb)
+
+
+def pin_op_transpose_identity(o):
+    # C^T = op(B)^T op(A)^T: the stored B read transposed is the left operand.
+    rng = _rng(23)
+    M, N, K = 6, 10, 7
+    X = _uniform(rng, (M, K))
+    Y = _uniform(rng, (K, N))
+    for ta, tb in _FORMS:
+        A = _stored(X, ta)
+        B = _stored(Y, tb)
+        C, _ = o.sgemm_ref_op(A, B, ta, tb)
+        Ct, _ = o.sgemm_ref_op(B, A, not tb, not ta)
+        assert np.array_equal(_bits(C.T), _bits(Ct)), ("(AB)^T", ta, tb)
+
+
+def pin_op_entries_match(o):
+    rng = _rng(24)
+    M, N, K = 8, 12, 9
+    X = _uniform(rng, (M, K))
+    Y = _uniform(rng, (K, N))
+    C0 = _uniform(rng, (M, N))
+    r = rng.integers(0, M, size=20)
+    c = rng.integers(0, N, size=20)
+    for ta, tb in _FORMS:
+        A = _stored(X, ta)
+        B = _stored(Y, tb)
+        Cref, absab = o.sgemm_ref_op(A, B, ta, tb, 0.5, 2.0, C0)
+        v, av = o.sgemm_ref_op_entries(A, B, r, c, ta, tb, 0.5, 2.0, C0)
+        assert np.array_equal(_bits(v), _bits(Cref[r, c])), ("entries != full", ta, tb)
+        assert np.array_equal(_bits(av), _bits(absab[r, c])), ("entry magnitudes", ta, tb)
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_transpose, pin_exact_rational,
         pin_integer_exact, pin_rank_one, pin_all_ones, pin_scalar_special_cases,
         pin_library_matmul, pin_leading_dims, pin_entries_match,
-        pin_uniform_statistics]
+        pin_uniform_statistics, pin_op_golden, pin_op_integer_exact,
+        pin_op_library_matmul, pin_op_transpose_identity, pin_op_entries_match]

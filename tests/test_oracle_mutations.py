@@ -13,7 +13,10 @@ MUTATIONS = {
     # name: list of (original text, replacement)
     "drop_beta_term": [("const double old = (beta == 0.0f) ? 0.0 : b_s * (double)C0[(long)i * ldc + j];",
                         "const double old = 0.0;")],
-    "sign_of_beta_term": [("Cref[(long)i * N + j] = prod + old;", "Cref[(long)i * N + j] = prod - old;")],
+    "sign_of_beta_term": [("b_s * (double)C0[(long)i * ldc + j];\n                Cref[(long)i * N + j] = prod + old;",
+                           "b_s * (double)C0[(long)i * ldc + j];\n                Cref[(long)i * N + j] = prod - old;")],
+    "op_sign_of_beta_term": [("(double)beta * (double)C0[(long)i * ldc + j];\n            Cref[(long)i * N + j] = prod + old;",
+                              "(double)beta * (double)C0[(long)i * ldc + j];\n            Cref[(long)i * N + j] = prod - old;")],
     "ignore_alpha": [("const double prod = use_product ? a_s * acc[j] : 0.0;",
                       "const double prod = use_product ? acc[j] : 0.0;")],
     "drop_last_k": [("for (int k = 0; k < K; ++k) {\n                    const double a",
@@ -24,6 +27,19 @@ MUTATIONS = {
     "signed_magnitude": [("aac[j] += fabs(p);", "aac[j] += p;")],
     "beta_one_ignored_when_alpha_zero": [("const int use_product = (alpha != 0.0f) && (K > 0);\n    const double a_s",
                                           "const int use_product = 1;\n    const double a_s")],
+    "op_transposed_reading_swapped": [("return (double)(trans ? X[c * ld + r] : X[r * ld + c]);",
+                                       "return (double)(trans ? X[r * ld + c] : X[c * ld + r]);")],
+    "op_B_indices_swapped": [("op_elem(B, ldb, trans_b, k, j)", "op_elem(B, ldb, trans_b, j, k)")],
+    "op_A_uses_ldb": [("op_elem(A, lda, trans_a, i, k)", "op_elem(A, ldb, trans_a, i, k)")],
+    "op_ignores_trans_b": [("op_elem(B, ldb, trans_b, k, j)", "op_elem(B, ldb, 0, k, j)")],
+    "op_drop_first_k": [("for (int k = 0; k < K; ++k) {\n        const double p = op_elem",
+                         "for (int k = 1; k < K; ++k) {\n        const double p = op_elem")],
+    "op_entries_beta_dropped": [("op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);\n"
+                                 "        const double prod = use_product ? (double)alpha * acc : 0.0;\n"
+                                 "        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];",
+                                 "op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);\n"
+                                 "        const double prod = use_product ? (double)alpha * acc : 0.0;\n"
+                                 "        const double old = 0.0;")],
     "row_stride_of_A_is_K": [("const double a = (double)A[(long)i * lda + k];",
                               "const double a = (double)A[(long)i * K + k];")],
 }
@@ -33,7 +49,7 @@ MUTATIONS = {
 def test_pins_catch_planted_mistake(oracle_mod, tmp_path, name):
     src = open(oracle_mod.SOURCE_PATH).read()
     for old, new in MUTATIONS[name]:
-        assert src.count(old) >= 1, f"mutation {name} no longer applies"
+        assert src.count(old) == 1, f"mutation {name} does not apply to exactly one place"
         src = src.replace(old, new)
     path = tmp_path / f"mut_{name}.c"
     path.write_text(src)
