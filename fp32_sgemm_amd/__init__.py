@@ -1,7 +1,7 @@
 """Python binding of the gfx950 FP32 GEMM library (``libsgemm_f32.so``).
 
-Argument marshalling only: every step of ``C = alpha*A*B + beta*C`` runs in the
-library's HIP kernels.  The functions mirror the C interface in
+Argument marshalling only: every step of ``C = alpha*op(A)*op(B) + beta*C``
+runs in the library's HIP kernels.  The functions mirror the C interface in
 ``include/sgemm_f32.h`` one to one (same names, same argument order, device
 pointers passed as integers, status codes returned unchanged).  ``sgemm``
 adds a convenience form over PyTorch tensors, which serve only as device memory
@@ -30,8 +30,10 @@ NUM_VARIANTS = 6
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21
 ERR_TOO_LARGE = 22
+ERR_TRANS = 23
 
 EXPORTED = ("sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select",
+            "sgemm_f32_ex", "sgemm_f32_ex_variant", "sgemm_f32_ex_select",
             "sgemm_f32_variant_name", "sgemm_f32_version")
 
 
@@ -55,6 +57,12 @@ def _load_library():
     lib.sgemm_f32_variant.restype = i
     lib.sgemm_f32_select.argtypes = [i, i, i, f, p, i, p, i]
     lib.sgemm_f32_select.restype = i
+    lib.sgemm_f32_ex.argtypes = [i, i] + gemm_args
+    lib.sgemm_f32_ex.restype = i
+    lib.sgemm_f32_ex_variant.argtypes = [i, i, i] + gemm_args
+    lib.sgemm_f32_ex_variant.restype = i
+    lib.sgemm_f32_ex_select.argtypes = [i, i, i, i, i, f, p, i, p, i]
+    lib.sgemm_f32_ex_select.restype = i
     lib.sgemm_f32_variant_name.argtypes = [i]
     lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
     lib.sgemm_f32_version.argtypes = []
@@ -81,6 +89,24 @@ def sgemm_f32_select(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: 
     return _lib.sgemm_f32_select(M, N, K, alpha, A, lda, B, ldb)
 
 
+def sgemm_f32_ex(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int,
+                 lda: int, B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    """C = alpha*op(A)*op(B) + beta*C; a flag of 1 means the operand is stored transposed."""
+    return _lib.sgemm_f32_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_ex_variant(variant: int, trans_a: int, trans_b: int, M: int, N: int, K: int,
+                         alpha: float, A: int, lda: int, B: int, ldb: int, beta: float, C: int,
+                         ldc: int, stream: int = 0) -> int:
+    return _lib.sgemm_f32_ex_variant(variant, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                     beta, C, ldc, stream)
+
+
+def sgemm_f32_ex_select(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float,
+                        A: int, lda: int, B: int, ldb: int) -> int:
+    return _lib.sgemm_f32_ex_select(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb)
+
+
 def sgemm_f32_variant_name(variant: int) -> str | None:
     r = _lib.sgemm_f32_variant_name(variant)
     return None if r is None else r.decode()
@@ -90,27 +116,49 @@ def sgemm_f32_version() -> int:
     return _lib.sgemm_f32_version()
 
 
-def _row_stride(t, name: str) -> int:
+def _check_tensor(t, name: str) -> None:
     import torch
 
     if t.dtype != torch.float32:
         raise TypeError(f"{name} must be float32")
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
-    if t.shape[1] > 1 and t.stride(1) != 1:
-        raise ValueError(f"{name} must be row-major with unit column stride")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+
+
+def _row_stride(t, name: str) -> int:
+    _check_tensor(t, name)
+    if t.shape[1] > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} must be row-major with unit column stride")
     return max(int(t.stride(0)), 1) if t.shape[0] > 1 else max(int(t.shape[1]), 1)
+
+
+def _operand(t, name: str):
+    """(leading dimension, transpose flag) of an operand view.
+
+    A row-major view is passed as stored (flag 0).  A view with unit row stride
+    is the transpose of a row-major matrix (``X.t()``), passed as that stored
+    matrix with flag 1.
+    """
+    _check_tensor(t, name)
+    rows, cols = int(t.shape[0]), int(t.shape[1])
+    if cols <= 1 or t.stride(1) == 1:
+        return (max(int(t.stride(0)), 1) if rows > 1 else max(cols, 1)), 0
+    if rows <= 1 or t.stride(0) == 1:
+        return (max(int(t.stride(1)), 1) if cols > 1 else max(rows, 1)), 1
+    raise ValueError(f"{name} must be row-major or the transpose of a row-major matrix")
 
 
 def sgemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = AUTO,
           stream=None) -> None:
-    """C = alpha*A@B + beta*C in place on device tensors (row-major views).
+    """C = alpha*A@B + beta*C in place on device tensors.
 
-    ``stream`` is a ``torch.cuda.Stream`` (default: the current stream).  The
-    call is asynchronous on that stream.  Raises ``SgemmError`` on a non-zero
-    status.
+    ``A`` and ``B`` may each be a row-major view or the transpose view of one
+    (``X.t()``); the latter is passed to the library as a transposed operand.
+    ``C`` must be row-major.  ``stream`` is a ``torch.cuda.Stream`` (default:
+    the current stream).  The call is asynchronous on that stream.  Raises
+    ``SgemmError`` on a non-zero status.
     """
     import torch
 
@@ -118,10 +166,12 @@ def sgemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = AUTO,
     K2, N = B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, C {tuple(C.shape)}")
-    lda, ldb, ldc = _row_stride(A, "A"), _row_stride(B, "B"), _row_stride(C, "C")
+    lda, ta = _operand(A, "A")
+    ldb, tb = _operand(B, "B")
+    ldc = _row_stride(C, "C")
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
-    st = sgemm_f32_variant(variant, M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
-                           float(beta), C.data_ptr(), ldc, stream.cuda_stream)
+    st = sgemm_f32_ex_variant(variant, ta, tb, M, N, K, float(alpha), A.data_ptr(), lda,
+                              B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream.cuda_stream)
     if st != 0:
         raise SgemmError(st)

@@ -6,7 +6,10 @@
 
 namespace sgemm {
 
-// Arguments of one C = alpha*A*B + beta*C call, row-major, strides in elements.
+// Arguments of one C = alpha*op(A)*op(B) + beta*C call, row-major, strides in
+// elements.  trans_a == 0: A is stored M x K; otherwise K x M and op(A) is its
+// transpose.  trans_b == 0: B is stored K x N; otherwise N x K.  Only the MFMA
+// kernels take transposed operands.
 struct GemmArgs {
     int M, N, K;
     float alpha, beta;
@@ -14,6 +17,7 @@ struct GemmArgs {
     const float *B;
     float *C;
     int64_t lda, ldb, ldc;
+    int trans_a = 0, trans_b = 0;
 };
 
 // Launchers: each enqueues its kernel(s) on `stream` and returns the HIP error

@@ -21,13 +21,15 @@
 // LDS layouts.  A 32x32x2 MFMA takes, in lane l, A(l % 32, k) and B(k, l % 32)
 // for one of two k values picked by l / 32.  Inside a slice the kernel assigns
 // lane half h = l / 32 the k range [h*BK/2, (h+1)*BK/2), so a lane walks a
-// contiguous run of k for a fixed row of A.  A is therefore kept K-major in LDS
-// exactly as it sits in memory (row stride BK + 4 floats, so the 16-byte reads
-// of 16 consecutive rows fall in distinct banks) and read with ds_read_b128,
-// four k steps per read.  B is kept N-major as in memory and read with
-// ds_read_b32: the two half-waves read rows k and k + BK/2, and the second half
-// of the slice's rows is shifted by 32 floats so those two rows sit in opposite
-// halves of the bank space.
+// contiguous run of k for a fixed row of A and column of B.  Each operand is
+// kept in LDS in its memory layout: one that is contiguous along k (A as given,
+// B given transposed) keeps rows of k with a stride of BK + 4 floats and is
+// read with ds_read_b128, four k steps per read; one that is contiguous along M
+// or N (B as given, A given transposed) keeps rows of M or N and is read with
+// ds_read_b32, the second half of the slice's k rows shifted by 32 floats so
+// the two half-waves read opposite halves of the bank space.  The four operand
+// forms (A and B each as given or transposed) are four instances of the same
+// kernel.
 //
 // Edges.  Tiles that cross the M or N edge and the last slice when K is not a
 // multiple of BK load through a guarded path that writes zeros for elements
@@ -62,7 +64,34 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const float *base, i
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, 0x00020000);
 }
 
-template <int BM_, int BN_, int BK_, int WM_, int WN_, int PF_ = 1>
+// Memory layouts of an operand.  Both operands reach the matrix core in the
+// same form: lane l supplies element (x = l % 32 of a block, k) of its operand,
+// where x runs along M for A and along N for B.  They differ only in which
+// index is contiguous in memory:
+//   kKMajor: element (x, k) at X[x * ld + k]  (A as given; B given transposed)
+//   kXMajor: element (x, k) at X[k * ld + x]  (B as given; A given transposed)
+enum Layout : int { kKMajor = 0, kXMajor = 1 };
+
+// Geometry of one operand's slice (BX values of x by BK values of k) as staged
+// by NT threads, and its LDS form.  A kKMajor slice keeps its memory rows (one
+// per x) with a row stride of BK + 4 floats, so the 16-byte fragment reads of 16
+// consecutive rows fall in distinct banks.  A kXMajor slice keeps its memory
+// rows (one per k) with the second half of the k rows shifted by 32 floats, so
+// the two half-waves, which read rows k and k + BK/2, hit opposite halves of
+// the bank space.
+template <int BX_, int BK_, int NT_, int L_>
+struct PanelGeom {
+    static constexpr int X = BX_, BK = BK_, NT = NT_, L = L_;
+    static constexpr int VECS = X * BK / 4 / NT;                    // 4-float groups per thread
+    static constexpr int PER_ROW = (L == kKMajor ? BK : X) / 4;     // groups per memory row
+    static constexpr int HALF = BK / 2;
+    static constexpr int ROW_S = BK + 4;                            // kKMajor LDS row stride
+    static constexpr int SHIFT = 32;                                // kXMajor offset of rows >= HALF
+    static constexpr int STAGE = L == kKMajor ? X * ROW_S : BK * X + SHIFT;
+    static_assert((X * BK) % (4 * NT) == 0, "load split");
+};
+
+template <int BM_, int BN_, int BK_, int WM_, int WN_, int PF_, int LA_, int LB_>
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int PF = PF_;             // slices loaded ahead of the one being computed
@@ -71,50 +100,44 @@ struct MfmaTile {
     static constexpr int MB = WM / 32;          // 32x32 accumulator blocks per wave, along M
     static constexpr int NB = WN / 32;          // ... along N
     static constexpr int HALF = BK / 2;         // k values per lane half in one slice
-    static constexpr int LDA_S = BK + 4;        // LDS row stride of the A slice (floats)
-    static constexpr int B_SHIFT = 32;          // offset of B rows [HALF, BK) in LDS
-    static constexpr int A_STAGE = BM * LDA_S;
-    static constexpr int B_STAGE = BK * BN + B_SHIFT;
+    using PA = PanelGeom<BM, BK, NT, LA_>;
+    using PB = PanelGeom<BN, BK, NT, LB_>;
+    static constexpr int A_VECS = PA::VECS, B_VECS = PB::VECS;
+    static constexpr int A_STAGE = PA::STAGE, B_STAGE = PB::STAGE;
     static constexpr int STAGE = A_STAGE + B_STAGE;
-    static constexpr int A_VECS = BM * BK / 4 / NT;   // 4-float groups per thread per slice
-    static constexpr int B_VECS = BK * BN / 4 / NT;
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert((BM * BK) % (4 * NT) == 0 && (BK * BN) % (4 * NT) == 0, "load split");
     static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS");
 };
 
-// Per-thread addressing of the 4-float groups a thread stages for every slice:
-// group i of A is row ar[i], columns ac[i]..ac[i]+3 of the slice; group i of B
-// is row br[i], columns bc[i]..bc[i]+3.  The row pointers (guarded loads) and
-// the byte offsets from the slice origin (buffer loads of interior slices) are
-// formed once.
-template <class T>
-struct Stager {
-    const float *pa[T::A_VECS];
-    const float *pb[T::B_VECS];
-    int ar[T::A_VECS], ac[T::A_VECS];
-    int br[T::B_VECS], bc[T::B_VECS];
-    int oa[T::A_VECS], ob[T::B_VECS];
+// Per-thread addressing of the 4-float groups a thread stages from one operand
+// for every slice: group i is memory row r[i], columns c[i]..c[i]+3 of the
+// slice.  The row pointers (guarded loads) and the byte offsets from the slice
+// origin (buffer loads of interior slices) are formed once.
+template <class P>
+struct Panel {
+    const float *p[P::VECS];
+    int r[P::VECS], c[P::VECS];
+    int o[P::VECS];
 
-    __device__ __forceinline__ Stager(const GemmArgs &g, int m0, int n0, int tid) {
+    __device__ __forceinline__ Panel(const float *X, int64_t ld, int x0, int tid) {
 #pragma unroll
-        for (int i = 0; i < T::A_VECS; ++i) {
-            const int q = tid + i * T::NT;
-            ar[i] = q / (T::BK / 4);
-            ac[i] = (q % (T::BK / 4)) * 4;
-            pa[i] = g.A + (int64_t)(m0 + ar[i]) * g.lda + ac[i];
-            oa[i] = (ar[i] * (int)g.lda + ac[i]) * 4;
-        }
-#pragma unroll
-        for (int i = 0; i < T::B_VECS; ++i) {
-            const int q = tid + i * T::NT;
-            br[i] = q / (T::BN / 4);
-            bc[i] = (q % (T::BN / 4)) * 4;
-            pb[i] = g.B + (int64_t)br[i] * g.ldb + n0 + bc[i];
-            ob[i] = (br[i] * (int)g.ldb + bc[i]) * 4;
+        for (int i = 0; i < P::VECS; ++i) {
+            const int q = tid + i * P::NT;
+            r[i] = q / P::PER_ROW;
+            c[i] = (q % P::PER_ROW) * 4;
+            p[i] = P::L == kKMajor ? X + (int64_t)(x0 + r[i]) * ld + c[i] : X + (int64_t)r[i] * ld + x0 + c[i];
+            o[i] = (r[i] * (int)ld + c[i]) * 4;
         }
     }
+};
+
+template <class T>
+struct Stager {
+    Panel<typename T::PA> a;
+    Panel<typename T::PB> b;
+    __device__ __forceinline__ Stager(const GemmArgs &g, int m0, int n0, int tid)
+        : a(g.A, g.lda, m0, tid), b(g.B, g.ldb, n0, tid) {}
 };
 
 template <bool VEC>
@@ -123,92 +146,101 @@ __device__ __forceinline__ float4 ld4(const float *p) {
     return make_float4(p[0], p[1], p[2], p[3]);
 }
 
-// Loads 4-float group p of the slice starting at column k0 of A / row k0 of
-// B: groups 0 .. A_VECS-1 are A's, the rest B's.  GMN: the tile crosses the M
-// or N edge, so rows of A beyond M and columns of B beyond N read as zero.
-// GK: the slice crosses the K edge, so k >= K reads as zero.  Nothing outside
-// the matrices is accessed.
-// Resources over the A and B elements of the slice at k0 that lie inside the
-// matrices: the rows of A below M, and B up to its last valid column in the
-// slice's last row.  A rows past M therefore read as zeros by themselves; B
-// columns past N need an out-of-range lane offset (load_part).
+// Resource over the elements of an operand's slice at k0 that lie inside the
+// matrix: up to the last valid x (xn is the operand's extent along x).  For a
+// kKMajor slice, rows past xn lie beyond the extent and read as zeros by
+// themselves; in a kXMajor slice, columns past xn need an out-of-range lane
+// offset (panel_load).
+template <class P>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const float *X, int64_t ld, int x0, int xn, int k0) {
+    const int xs = min(P::X, xn - x0);
+    if (P::L == kKMajor) return make_rsrc(X + (int64_t)x0 * ld + k0, (int)(((xs - 1) * ld + P::BK) * 4));
+    return make_rsrc(X + (int64_t)k0 * ld + x0, (int)(((P::BK - 1) * ld + xs) * 4));
+}
+
 struct SliceRsrc {
     __amdgpu_buffer_rsrc_t a, b;
 };
 
 template <class T>
 __device__ __forceinline__ SliceRsrc slice_rsrc(const GemmArgs &g, int m0, int n0, int k0) {
-    const int rows = min(T::BM, g.M - m0);
-    const int cols = min(T::BN, g.N - n0);
     SliceRsrc r;
-    r.a = make_rsrc(g.A + (int64_t)m0 * g.lda + k0, (int)(((rows - 1) * g.lda + T::BK) * 4));
-    r.b = make_rsrc(g.B + (int64_t)k0 * g.ldb + n0, (int)(((T::BK - 1) * g.ldb + cols) * 4));
+    r.a = panel_rsrc<typename T::PA>(g.A, g.lda, m0, g.M, k0);
+    r.b = panel_rsrc<typename T::PB>(g.B, g.ldb, n0, g.N, k0);
     return r;
 }
 
-// Slices that do not cross the K edge are loaded with 16-byte buffer loads
-// when VEC; the K-edge slice (GK) and 4-byte loads go through row pointers.
+// Loads 4-float group i of an operand's slice starting at k0.  GX: the tile
+// crosses the M or N edge, so x >= xn reads as zero.  GK: the slice crosses the
+// K edge, so k >= K reads as zero.  Nothing outside the matrix is accessed.
+// Slices that do not cross the K edge are loaded with 16-byte buffer loads when
+// VEC; the K-edge slice and 4-byte loads go through row pointers.
+template <class P, bool VEC, bool GX, bool GK>
+__device__ __forceinline__ float4 panel_load(const Panel<P> &s, __amdgpu_buffer_rsrc_t rs, int i, int64_t ld,
+                                             int x0, int xn, int K, int k0) {
+    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
+    constexpr bool BUF = VEC && !GK;
+    if (P::L == kKMajor) {
+        const float *ptr = s.p[i] + k0;
+        const bool row_ok = !GX || (x0 + s.r[i] < xn);
+        if (BUF) {
+            const f32x4v v = raw_buffer_load_v4f32(rs, s.o[i], 0, 0);
+            return make_float4(v[0], v[1], v[2], v[3]);
+        }
+        if (!GK) return row_ok ? ld4<VEC>(ptr) : zero;
+        const int k = k0 + s.c[i];
+        float4 v = zero;
+        if (row_ok) {
+            if (k + 0 < K) v.x = ptr[0];
+            if (k + 1 < K) v.y = ptr[1];
+            if (k + 2 < K) v.z = ptr[2];
+            if (k + 3 < K) v.w = ptr[3];
+        }
+        return v;
+    } else {
+        const float *ptr = s.p[i] + (int64_t)k0 * ld;
+        const bool row_ok = !GK || (k0 + s.r[i] < K);
+        if (BUF) {
+            const int x = x0 + s.c[i];
+            const int off = (!GX || x + 3 < xn) ? s.o[i] : kOutOfRange;
+            const f32x4v v = raw_buffer_load_v4f32(rs, off, 0, 0);
+            float4 w = make_float4(v[0], v[1], v[2], v[3]);
+            if (GX && x < xn && x + 3 >= xn) {
+                // The group straddles the edge (only when xn is not a multiple of 4).
+                w.x = raw_buffer_load_f32(rs, s.o[i], 0, 0);
+                w.y = raw_buffer_load_f32(rs, x + 1 < xn ? s.o[i] + 4 : kOutOfRange, 0, 0);
+                w.z = raw_buffer_load_f32(rs, x + 2 < xn ? s.o[i] + 8 : kOutOfRange, 0, 0);
+                w.w = 0.f;
+            }
+            return w;
+        }
+        if (!GX) return row_ok ? ld4<VEC>(ptr) : zero;
+        const int x = x0 + s.c[i];
+        float4 v = zero;
+        if (row_ok) {
+            if (VEC && x + 3 < xn) {
+                v = ld4<true>(ptr);
+            } else {
+                if (x + 0 < xn) v.x = ptr[0];
+                if (x + 1 < xn) v.y = ptr[1];
+                if (x + 2 < xn) v.z = ptr[2];
+                if (x + 3 < xn) v.w = ptr[3];
+            }
+        }
+        return v;
+    }
+}
+
+// Loads 4-float group p of the slice at k0: groups 0 .. A_VECS-1 are A's, the
+// rest B's.  GMN: the tile crosses the M or N edge.
 template <class T, bool VEC, bool GMN, bool GK>
 __device__ __forceinline__ void load_part(const GemmArgs &g, const Stager<T> &s, int m0, int n0, int k0,
                                           const SliceRsrc &r, int p, float4 (&ra)[T::A_VECS],
                                           float4 (&rb)[T::B_VECS]) {
-    const float4 zero = make_float4(0.f, 0.f, 0.f, 0.f);
-    constexpr bool BUF = VEC && !GK;
-    if (p < T::A_VECS) {
-        const int i = p;
-        const float *ptr = s.pa[i] + k0;
-        const bool row_ok = !GMN || (m0 + s.ar[i] < g.M);
-        if (BUF) {
-            const f32x4v v = raw_buffer_load_v4f32(r.a, s.oa[i], 0, 0);
-            ra[i] = make_float4(v[0], v[1], v[2], v[3]);
-        } else if (!GK) {
-            ra[i] = row_ok ? ld4<VEC>(ptr) : zero;
-        } else {
-            const int k = k0 + s.ac[i];
-            float4 v = zero;
-            if (row_ok) {
-                if (k + 0 < g.K) v.x = ptr[0];
-                if (k + 1 < g.K) v.y = ptr[1];
-                if (k + 2 < g.K) v.z = ptr[2];
-                if (k + 3 < g.K) v.w = ptr[3];
-            }
-            ra[i] = v;
-        }
-    } else {
-        const int i = p - T::A_VECS;
-        const float *ptr = s.pb[i] + (int64_t)k0 * g.ldb;
-        const bool row_ok = !GK || (k0 + s.br[i] < g.K);
-        if (BUF) {
-            const int n = n0 + s.bc[i];
-            const int off = (!GMN || n + 3 < g.N) ? s.ob[i] : kOutOfRange;
-            const f32x4v v = raw_buffer_load_v4f32(r.b, off, 0, 0);
-            float4 w = make_float4(v[0], v[1], v[2], v[3]);
-            if (GMN && n < g.N && n + 3 >= g.N) {
-                // The group straddles column N (only when N is not a multiple of 4).
-                w.x = raw_buffer_load_f32(r.b, s.ob[i], 0, 0);
-                w.y = raw_buffer_load_f32(r.b, n + 1 < g.N ? s.ob[i] + 4 : kOutOfRange, 0, 0);
-                w.z = raw_buffer_load_f32(r.b, n + 2 < g.N ? s.ob[i] + 8 : kOutOfRange, 0, 0);
-                w.w = 0.f;
-            }
-            rb[i] = w;
-        } else if (!GMN) {
-            rb[i] = row_ok ? ld4<VEC>(ptr) : zero;
-        } else {
-            const int n = n0 + s.bc[i];
-            float4 v = zero;
-            if (row_ok) {
-                if (VEC && n + 3 < g.N) {
-                    v = ld4<true>(ptr);
-                } else {
-                    if (n + 0 < g.N) v.x = ptr[0];
-                    if (n + 1 < g.N) v.y = ptr[1];
-                    if (n + 2 < g.N) v.z = ptr[2];
-                    if (n + 3 < g.N) v.w = ptr[3];
-                }
-            }
-            rb[i] = v;
-        }
-    }
+    if (p < T::A_VECS)
+        ra[p] = panel_load<typename T::PA, VEC, GMN, GK>(s.a, r.a, p, g.lda, m0, g.M, g.K, k0);
+    else
+        rb[p - T::A_VECS] = panel_load<typename T::PB, VEC, GMN, GK>(s.b, r.b, p - T::A_VECS, g.ldb, n0, g.N, g.K, k0);
 }
 
 template <class T, bool VEC, bool GMN, bool GK>
@@ -219,45 +251,65 @@ __device__ __forceinline__ void load_slice(const GemmArgs &g, const Stager<T> &s
     for (int p = 0; p < T::A_VECS + T::B_VECS; ++p) load_part<T, VEC, GMN, GK>(g, s, m0, n0, k0, r, p, ra, rb);
 }
 
-template <class T>
-__device__ __forceinline__ void store_slice(float *stage, int tid,
-                                            const float4 (&ra)[T::A_VECS],
-                                            const float4 (&rb)[T::B_VECS]) {
-    float *As = stage;
-    float *Bs = stage + T::A_STAGE;
+template <class P>
+__device__ __forceinline__ void panel_store(float *S, int tid, const float4 (&v)[P::VECS]) {
 #pragma unroll
-    for (int i = 0; i < T::A_VECS; ++i) {
-        const int q = tid + i * T::NT;
-        const int r = q / (T::BK / 4), c = (q % (T::BK / 4)) * 4;
-        *reinterpret_cast<float4 *>(As + r * T::LDA_S + c) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < T::B_VECS; ++i) {
-        const int q = tid + i * T::NT;
-        const int r = q / (T::BN / 4), c = (q % (T::BN / 4)) * 4;
-        *reinterpret_cast<float4 *>(Bs + r * T::BN + (r >= T::HALF ? T::B_SHIFT : 0) + c) = rb[i];
+    for (int i = 0; i < P::VECS; ++i) {
+        const int q = tid + i * P::NT;
+        const int r = q / P::PER_ROW, c = (q % P::PER_ROW) * 4;
+        float *dst = P::L == kKMajor ? S + r * P::ROW_S + c : S + r * P::X + (r >= P::HALF ? P::SHIFT : 0) + c;
+        *reinterpret_cast<float4 *>(dst) = v[i];
     }
 }
 
-// Fragments of one chunk (4 k steps) of a slice: for each 32-row block of the
-// wave's A sub-tile one float4 (4 consecutive k of this lane's row), and for
-// each 32-column block of B four values (the same 4 k, this lane's column).
+template <class T>
+__device__ __forceinline__ void store_slice(float *stage, int tid, const float4 (&ra)[T::A_VECS],
+                                            const float4 (&rb)[T::B_VECS]) {
+    panel_store<typename T::PA>(stage, tid, ra);
+    panel_store<typename T::PB>(stage + T::A_STAGE, tid, rb);
+}
+
+// LDS address of a lane's first fragment element in an operand's stage: x =
+// xw + l % 32 (xw is the wave's offset along x) and k = h * BK/2, h = l / 32.
+template <class P>
+__device__ __forceinline__ const float *panel_lane(const float *S, int xw, int l32, int h) {
+    if (P::L == kKMajor) return S + (xw + l32) * P::ROW_S + h * P::HALF;
+    return S + h * (P::HALF * P::X + P::SHIFT) + xw + l32;
+}
+
+// Chunk c (4 k steps) of a lane's fragments for NBLK 32-wide blocks along x:
+// f[b][e] is the element at x + 32 b and k + 4 c + e.  A kKMajor stage gives the
+// four k in one 16-byte read, a kXMajor stage one float per k.
+template <class P, int NBLK>
+__device__ __forceinline__ void panel_frag(const float *base, int c, float (&f)[NBLK][4]) {
+    if (P::L == kKMajor) {
+#pragma unroll
+        for (int b = 0; b < NBLK; ++b) {
+            const float4 v = *reinterpret_cast<const float4 *>(base + b * 32 * P::ROW_S + 4 * c);
+            f[b][0] = v.x;
+            f[b][1] = v.y;
+            f[b][2] = v.z;
+            f[b][3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int b = 0; b < NBLK; ++b) f[b][e] = base[(4 * c + e) * P::X + b * 32];
+    }
+}
+
+// Fragments of one chunk of a slice for all of the wave's blocks.
 template <class T>
 struct Frag {
-    float4 a[T::MB];
+    float a[T::MB][4];
     float b[T::NB][4];
 };
 
 template <class T>
 __device__ __forceinline__ void read_frag(const float *As, const float *Bs, int c, Frag<T> &f) {
-#pragma unroll
-    for (int ib = 0; ib < T::MB; ++ib)
-        f.a[ib] = *reinterpret_cast<const float4 *>(As + ib * 32 * T::LDA_S + 4 * c);
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-#pragma unroll
-        for (int jb = 0; jb < T::NB; ++jb)
-            f.b[jb][e] = Bs[(4 * c + e) * T::BN + jb * 32];
+    panel_frag<typename T::PA, T::MB>(As, c, f.a);
+    panel_frag<typename T::PB, T::NB>(Bs, c, f.b);
 }
 
 template <class T>
@@ -267,10 +319,8 @@ __device__ __forceinline__ void mfma_frag(const Frag<T> &f, f32x16 (&acc)[T::MB]
 #pragma unroll
         for (int ib = 0; ib < T::MB; ++ib)
 #pragma unroll
-            for (int jb = 0; jb < T::NB; ++jb) {
-                const float av = e == 0 ? f.a[ib].x : e == 1 ? f.a[ib].y : e == 2 ? f.a[ib].z : f.a[ib].w;
-                acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av, f.b[jb][e], acc[ib][jb], 0, 0, 0);
-            }
+            for (int jb = 0; jb < T::NB; ++jb)
+                acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[ib][e], f.b[jb][e], acc[ib][jb], 0, 0, 0);
 }
 
 // All MFMAs of one slice.  The LDS reads of chunk c+1 are issued before the
@@ -286,8 +336,8 @@ __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn
                                               f32x16 (&acc)[T::MB][T::NB], const Issue &issue) {
     const int h = lane >> 5;
     const int l32 = lane & 31;
-    const float *As = stage + (wm * T::WM + l32) * T::LDA_S + h * T::HALF;
-    const float *Bs = stage + T::A_STAGE + h * (T::HALF * T::BN + T::B_SHIFT) + wn * T::WN + l32;
+    const float *As = panel_lane<typename T::PA>(stage, wm * T::WM, l32, h);
+    const float *Bs = panel_lane<typename T::PB>(stage + T::A_STAGE, wn * T::WN, l32, h);
     constexpr int CH = T::HALF / 4;
     Frag<T> f[2];
     read_frag<T>(As, Bs, 0, f[0]);
@@ -443,9 +493,12 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 
 // 128x128 tiles: two slices in flight with 16-byte loads; one with 4-byte
 // loads (whose staging registers would not fit two sets at two waves per SIMD).
-using LargeTile = MfmaTile<128, 128, 32, 64, 64, 2>;
-using LargeTileScalar = MfmaTile<128, 128, 32, 64, 64, 1>;
-using SmallTile = MfmaTile<64, 64, 32, 32, 32>;
+template <int LA, int LB>
+using LargeTile = MfmaTile<128, 128, 32, 64, 64, 2, LA, LB>;
+template <int LA, int LB>
+using LargeTileScalar = MfmaTile<128, 128, 32, 64, 64, 1, LA, LB>;
+template <int LA, int LB>
+using SmallTile = MfmaTile<64, 64, 32, 32, 32, 1, LA, LB>;
 
 template <class TV, class TS>
 hipError_t launch_tile(const GemmArgs &g, bool vec, int group_m, hipStream_t stream) {
@@ -458,21 +511,38 @@ hipError_t launch_tile(const GemmArgs &g, bool vec, int group_m, hipStream_t str
     return hipGetLastError();
 }
 
+template <int LA, int LB>
+hipError_t launch_layouts(const GemmArgs &g, bool large, bool vec, hipStream_t stream) {
+    if (large) return launch_tile<LargeTile<LA, LB>, LargeTileScalar<LA, LB>>(g, vec, 8, stream);
+    return launch_tile<SmallTile<LA, LB>, SmallTile<LA, LB>>(g, vec, 8, stream);
+}
+
+// A as given is kKMajor and B kXMajor; a transposed operand swaps its layout.
+hipError_t launch_mfma(const GemmArgs &g, bool large, bool vec, hipStream_t stream) {
+    const bool ta = g.trans_a != 0, tb = g.trans_b != 0;
+    if (!ta && !tb) return launch_layouts<kKMajor, kXMajor>(g, large, vec, stream);
+    if (!ta && tb) return launch_layouts<kKMajor, kKMajor>(g, large, vec, stream);
+    if (ta && !tb) return launch_layouts<kXMajor, kXMajor>(g, large, vec, stream);
+    return launch_layouts<kXMajor, kKMajor>(g, large, vec, stream);
+}
+
 }  // namespace
 
 int64_t mfma_large_grid(int M, int N) {
-    return (int64_t)((M + LargeTile::BM - 1) / LargeTile::BM) * ((N + LargeTile::BN - 1) / LargeTile::BN);
+    using T = LargeTile<kKMajor, kXMajor>;
+    return (int64_t)((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
 }
 int64_t mfma_small_grid(int M, int N) {
-    return (int64_t)((M + SmallTile::BM - 1) / SmallTile::BM) * ((N + SmallTile::BN - 1) / SmallTile::BN);
+    using T = SmallTile<kKMajor, kXMajor>;
+    return (int64_t)((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
 }
 
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_tile<LargeTile, LargeTileScalar>(g, vec_loads, 8, stream);
+    return launch_mfma(g, true, vec_loads, stream);
 }
 
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_tile<SmallTile, SmallTile>(g, vec_loads, 8, stream);
+    return launch_mfma(g, false, vec_loads, stream);
 }
 
 }  // namespace sgemm

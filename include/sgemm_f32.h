@@ -54,6 +54,7 @@
  *     SGEMM_F32_ERR_NOT_APPLICABLE  (sgemm_f32_variant only) the forced variant
  *                            cannot run this shape or alignment
  *     SGEMM_F32_ERR_TOO_LARGE  the tile grid exceeds the launch limits
+ *     SGEMM_F32_ERR_TRANS    (the _ex functions) a transpose flag other than 0 or 1
  *     < 0                    -(hipError_t) reported by the HIP runtime for the
  *                            launch; the contents of C are then unspecified
  * Nothing is printed and no exception crosses the interface.
@@ -70,6 +71,7 @@ extern "C" {
 #define SGEMM_F32_ERR_VARIANT 20
 #define SGEMM_F32_ERR_NOT_APPLICABLE 21
 #define SGEMM_F32_ERR_TOO_LARGE 22
+#define SGEMM_F32_ERR_TRANS 23
 
 /* Kernel variants that sgemm_f32_variant can force. */
 enum sgemm_f32_variant_id {
@@ -112,10 +114,52 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha,
 int sgemm_f32_select(int M, int N, int K, float alpha,
                      const float *A, int lda, const float *B, int ldb);
 
+/*
+ * Transposed operands ("Writing a Fast Matmul in CUDA, Step by Step", section
+ * "In the real world": the library the pages compare against takes every
+ * transpose of its operands, and the "nn" in its kernel names marks the form
+ * with neither transposed):
+ *
+ *     C = alpha * op(A) * op(B) + beta * C
+ *
+ * op(A) is M x K and op(B) is K x N; C is M x N row-major as above.
+ *   trans_a == 0: A is stored M x K, op(A)(i, k) = A[i * lda + k], lda >= max(1, K)
+ *   trans_a == 1: A is stored K x M, op(A)(i, k) = A[k * lda + i], lda >= max(1, M)
+ *   trans_b == 0: B is stored K x N, op(B)(k, j) = B[k * ldb + j], ldb >= max(1, N)
+ *   trans_b == 1: B is stored N x K, op(B)(k, j) = B[j * ldb + k], ldb >= max(1, K)
+ * Any other flag value returns SGEMM_F32_ERR_TRANS.  Everything else (special
+ * cases, ownership, stream, accuracy, return codes) is as for sgemm_f32, and
+ * sgemm_f32_ex(0, 0, ...) is sgemm_f32(...).
+ *
+ * Column-major callers: a column-major C = op(A) * op(B) is, read row-major,
+ * C^T = op(B)^T * op(A)^T, so it is
+ *     sgemm_f32_ex(tb, ta, N, M, K, alpha, B, ldb, A, lda, beta, C, ldc, stream)
+ * with the column-major leading dimensions.
+ *
+ * Transposed operands run on the MFMA variants (SGEMM_F32_MFMA_LARGE, _SMALL,
+ * _SCALAR); SGEMM_F32_VALU and SGEMM_F32_SKINNY take neither operand
+ * transposed and return SGEMM_F32_ERR_NOT_APPLICABLE otherwise.  For the
+ * 16-byte-load variants the stored rows one slice touches must span less than
+ * 2 GiB: 128 rows of an operand stored along K (A as given, B transposed) and
+ * 32 rows of one stored along M or N (B as given, A transposed).
+ */
+int sgemm_f32_ex(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                 const float *A, int lda, const float *B, int ldb,
+                 float beta, float *C, int ldc, hipStream_t stream);
+
+/* sgemm_f32_variant with transposed operands. */
+int sgemm_f32_ex_variant(int variant, int trans_a, int trans_b, int M, int N, int K,
+                         float alpha, const float *A, int lda, const float *B, int ldb,
+                         float beta, float *C, int ldc, hipStream_t stream);
+
+/* sgemm_f32_select with transposed operands (0 for invalid flags as well). */
+int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const float *A, int lda, const float *B, int ldb);
+
 /* Short static name of a variant ("mfma_large", ...), or NULL if unknown. */
 const char *sgemm_f32_variant_name(int variant);
 
-/* Library version, e.g. 100 for 0.1.0. */
+/* Library version, e.g. 200 for 0.2.0. */
 int sgemm_f32_version(void);
 
 #ifdef __cplusplus

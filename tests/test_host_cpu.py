@@ -86,11 +86,51 @@ def test_kernel_selection(sg):
     assert sg.sgemm_f32_select(4096, 4096, 0, 1.0, al, 1, al, 4096) == 0
 
 
+def test_transposed_argument_errors_without_touching_the_gpu(sg):
+    p = 0x1000
+    f = sg.sgemm_f32_ex
+    # Flags other than 0 and 1.
+    assert f(2, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_TRANS
+    assert f(0, -1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_TRANS
+    # A stored K x M when transposed: lda >= M; B stored N x K: ldb >= K.
+    assert f(1, 0, 5, 2, 3, 1.0, p, 4, p, 2, 0.0, p, 2, 0) == 6      # lda 4 < M 5
+    assert f(0, 1, 2, 5, 3, 1.0, p, 3, p, 2, 0.0, p, 5, 0) == 8      # ldb 2 < K 3
+    assert f(0, 1, 2, 5, 3, 1.0, p, 3, p, 3, 0.0, p, 4, 0) == 11     # ldc 4 < N 5
+    # The widths the untransposed forms would need are not required.
+    assert f(1, 1, 2, 5, 9, 1.0, p, 2, p, 9, 0.0, 0, 5, 0) == 10     # only C is missing
+    assert sg.sgemm_f32_ex_variant(sg.NUM_VARIANTS, 1, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
+    # The VALU and M <= 16 kernels take neither operand transposed.
+    al = 0x100000
+    for ta, tb in ((1, 0), (0, 1), (1, 1)):
+        for v in (sg.VALU, sg.SKINNY):
+            assert sg.sgemm_f32_ex_variant(v, ta, tb, 16, 64, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+                == sg.ERR_NOT_APPLICABLE, (v, ta, tb)
+
+
+def test_transposed_kernel_selection(sg):
+    al = 0x100000
+    sel = sg.sgemm_f32_ex_select
+    for ta, tb in ((0, 1), (1, 0), (1, 1)):
+        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_LARGE
+        assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) == sg.MFMA_SMALL
+        assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_SMALL
+        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
+    assert sel(0, 0, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
+    assert sel(0, 0, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == \
+        sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al, 4096, al, 4096)
+    assert sel(2, 0, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == 0
+    # 2 GiB rule: an operand stored along K spans 128 rows per slice, one
+    # stored along M or N 32 rows.
+    big = (1 << 31) // 4 // 100          # 128 rows of this stride exceed 2 GiB, 32 rows do not
+    assert sel(0, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_SCALAR
+    assert sel(1, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_LARGE
+
+
 def test_variant_names_and_version(sg):
     names = [sg.sgemm_f32_variant_name(i) for i in range(sg.NUM_VARIANTS)]
     assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
-    assert sg.sgemm_f32_version() >= 100
+    assert sg.sgemm_f32_version() >= 200
 
 
 def test_tile_mapping_is_a_bijection(tmp_path):
