@@ -4,6 +4,8 @@
 One step is one call of the library's C entry point ``sgemm_f32`` on the
 4096 x 4096 x 4096 workload (A, B, C standard normal, C = 1.5*A*B - 0.5*C, in
 place), with all inputs resident in device memory.  Prints one JSON line.
+``--operands nt|tn|tt`` stores A and/or B transposed and times ``sgemm_f32_ex``
+on the same product.
 
 Timing: W untimed warm-up steps, then K timed steps bracketed by device
 synchronisation; each launch is also bracketed by HIP events recorded on the
@@ -114,6 +116,9 @@ def main():
     ap.add_argument("--workload", default=None, help="workload name (default: the 4096^3 headline)")
     ap.add_argument("--variant", default="auto",
                     help="auto | mfma_large | mfma_small | valu | skinny | mfma_scalar")
+    ap.add_argument("--operands", default="nn", choices=["nn", "nt", "tn", "tt"],
+                    help="operand forms: t = stored transposed (A as K x M, B as N x K), "
+                         "timed through sgemm_f32_ex")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -158,24 +163,31 @@ def main():
 
     w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     A, B, C0 = workloads.make_inputs(w)
+    ta, tb = int(args.operands[0] == "t"), int(args.operands[1] == "t")
+    As = np.ascontiguousarray(A.T) if ta else A
+    Bs = np.ascontiguousarray(B.T) if tb else B
     dev = torch.device("cuda:0")
-    dA = torch.from_numpy(A).to(dev)
-    dBs = [torch.from_numpy(B).to(dev) for _ in range(max(1, args.rotate))]
+    dA = torch.from_numpy(As).to(dev)
+    dBs = [torch.from_numpy(Bs).to(dev) for _ in range(max(1, args.rotate))]
     dB = dBs[0]
     dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty(w.M, w.N, device=dev)
-    lda, ldb, ldc = w.K, w.N, w.N
+    lda, ldb, ldc = As.shape[1], Bs.shape[1], w.N
     stream = torch.cuda.Stream(dev)
     s_handle = stream.cuda_stream
-    chosen = variant if variant else sg.sgemm_f32_select(w.M, w.N, w.K, w.alpha, dA.data_ptr(),
-                                                         lda, dB.data_ptr(), ldb)
+    chosen = variant if variant else sg.sgemm_f32_ex_select(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                                                            lda, dB.data_ptr(), ldb)
 
     counter = [0]
 
     def step():
         b = dBs[counter[0] % len(dBs)]
         counter[0] += 1
-        st = sg.sgemm_f32_variant(variant, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
-                                  b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
+        if ta or tb:
+            st = sg.sgemm_f32_ex_variant(variant, ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
+                                         b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
+        else:
+            st = sg.sgemm_f32_variant(variant, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
+                                      b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
         if st != 0:
             raise RuntimeError(f"sgemm_f32 returned {st}")
 
@@ -215,7 +227,8 @@ def main():
         bound = "alu" if chosen == sg.VALU else "mfma"
         roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4)}
-    roofline["traffic"] = measured_traffic() if (w.name == workloads.HEADLINE and chosen == 1) else None
+    headline_kernel = w.name == workloads.HEADLINE and chosen == 1 and not (ta or tb)
+    roofline["traffic"] = measured_traffic() if headline_kernel else None
     roofline["kernel_avg_ms"] = round(kern_avg_s * 1e3, 5)
 
     out = {
@@ -233,7 +246,8 @@ def main():
         "data": "synthetic",
         "pct_of_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
-                   "beta": w.beta, "inputs": w.dist, "variant": sg.sgemm_f32_variant_name(chosen),
+                   "beta": w.beta, "inputs": w.dist, "operands": args.operands,
+                   "variant": sg.sgemm_f32_variant_name(chosen),
                    "b_copies": len(dBs), "parallelism": "single GPU"},
         "roofline": roofline,
     }
