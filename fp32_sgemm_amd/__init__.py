@@ -25,16 +25,26 @@ MFMA_SMALL = 2
 VALU = 3
 SKINNY = 4
 MFMA_SCALAR = 5
-NUM_VARIANTS = 6
+MFMA_TUNED = 6
+NUM_VARIANTS = 7
+
+CFG_128x128 = 0
+CFG_64x64 = 1
+CFG_128x64 = 2
+CFG_64x128 = 3
+CFG_64x64_PF2 = 4
+NUM_CONFIGS = 5
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21
 ERR_TOO_LARGE = 22
 ERR_TRANS = 23
+ERR_CONFIG = 24
 
 EXPORTED = ("sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select",
             "sgemm_f32_ex", "sgemm_f32_ex_variant", "sgemm_f32_ex_select",
-            "sgemm_f32_variant_name", "sgemm_f32_version")
+            "sgemm_f32_ex_plan", "sgemm_f32_ex_config", "sgemm_f32_config_name",
+            "sgemm_f32_tuning_table_present", "sgemm_f32_variant_name", "sgemm_f32_version")
 
 
 class SgemmError(RuntimeError):
@@ -63,6 +73,15 @@ def _load_library():
     lib.sgemm_f32_ex_variant.restype = i
     lib.sgemm_f32_ex_select.argtypes = [i, i, i, i, i, f, p, i, p, i]
     lib.sgemm_f32_ex_select.restype = i
+    ip = ctypes.POINTER(ctypes.c_int)
+    lib.sgemm_f32_ex_plan.argtypes = [i, i, i, i, i, f, p, i, p, i, ip, ip, ip, ip]
+    lib.sgemm_f32_ex_plan.restype = i
+    lib.sgemm_f32_ex_config.argtypes = [i, i, i, i, i] + gemm_args
+    lib.sgemm_f32_ex_config.restype = i
+    lib.sgemm_f32_config_name.argtypes = [i]
+    lib.sgemm_f32_config_name.restype = ctypes.c_char_p
+    lib.sgemm_f32_tuning_table_present.argtypes = []
+    lib.sgemm_f32_tuning_table_present.restype = i
     lib.sgemm_f32_variant_name.argtypes = [i]
     lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
     lib.sgemm_f32_version.argtypes = []
@@ -105,6 +124,31 @@ def sgemm_f32_ex_variant(variant: int, trans_a: int, trans_b: int, M: int, N: in
 def sgemm_f32_ex_select(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float,
                         A: int, lda: int, B: int, ldb: int) -> int:
     return _lib.sgemm_f32_ex_select(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb)
+
+
+def sgemm_f32_ex_plan(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int,
+                      lda: int, B: int, ldb: int):
+    """Returns (status, variant, config, group_m, splits) of the automatic choice."""
+    out = [ctypes.c_int(0) for _ in range(4)]
+    st = _lib.sgemm_f32_ex_plan(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                *[ctypes.byref(o) for o in out])
+    return (st,) + tuple(o.value for o in out)
+
+
+def sgemm_f32_ex_config(config: int, group_m: int, splits: int, trans_a: int, trans_b: int, M: int,
+                        N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, beta: float,
+                        C: int, ldc: int, stream: int = 0) -> int:
+    return _lib.sgemm_f32_ex_config(config, group_m, splits, trans_a, trans_b, M, N, K, alpha, A, lda,
+                                    B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_config_name(config: int) -> str | None:
+    r = _lib.sgemm_f32_config_name(config)
+    return None if r is None else r.decode()
+
+
+def sgemm_f32_tuning_table_present() -> int:
+    return _lib.sgemm_f32_tuning_table_present()
 
 
 def sgemm_f32_variant_name(variant: int) -> str | None:

@@ -25,6 +25,21 @@ struct GemmArgs {
 // N == 0, and routed alpha == 0 / K == 0 to launch_scale_c.
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream);
+
+// MFMA tile configurations: 0 = 128x128 (the large tile), 1 = 64x64 (the
+// small tile), 2 = 128x64, 3 = 64x128, 4 = 64x64 with two slices in flight.
+// Configurations 2-4 exist with 16-byte loads only.  `group_m` is the number
+// of tile rows walked together by the tile order; `splits` divides K over
+// work-groups (the partial sums go through the stream's workspace and a
+// reduction kernel).
+constexpr int kNumMfmaConfigs = 5;
+hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
+                              hipStream_t stream);
+int64_t mfma_config_tiles(int config, int M, int N);
+bool mfma_config_scalar_ok(int config);
+// Number of non-empty splits of K actually used for a requested count, and the
+// K extent of each (a multiple of the tile depth).
+int mfma_effective_splits(int K, int splits, int *k_per);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);

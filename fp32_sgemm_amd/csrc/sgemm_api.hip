@@ -66,16 +66,88 @@ bool aligned16(const float *A, int lda, const float *B, int ldb) {
            (lda % 4 == 0) && (ldb % 4 == 0);
 }
 
-// Transposed operands go to the MFMA kernels only.
-int auto_variant(int ta, int tb, int M, int N, const float *A, int lda, const float *B, int ldb) {
-    if (!ta && !tb && M <= sgemm::kSkinnyMaxM && sgemm::skinny_fits(lda, ldb)) return SGEMM_F32_SKINNY;
-    if (!vec_aligned(ta, tb, A, lda, B, ldb)) return SGEMM_F32_MFMA_SCALAR;
-    return prefer_small_tiles(M, N) ? SGEMM_F32_MFMA_SMALL : SGEMM_F32_MFMA_LARGE;
+// ---------------------------------------------------------------------------
+// Tuning table.  The autotuning sweep of "How a Matmul Kernel Gets Fast"
+// (section "Kernel 9: autotuning") and the shape-keyed kernel choice of a
+// vendor library ("Writing a Fast Matmul in CUDA, Step by Step", section "In
+// the real world") become a table from shape classes to an MFMA tile
+// configuration, a tile-row grouping and a K split, measured on the GPU by the
+// package's tuning script and compiled in.  Class c of an extent x is the first
+// c with x <= kClassBound[c]; larger extents use the last class.
+// ---------------------------------------------------------------------------
+struct TunedEntry {
+    signed char config, group_m, splits;
+};
+constexpr int kNumClasses = 8;
+constexpr int kClassBound[kNumClasses] = {64, 128, 256, 512, 1024, 2048, 4096, 8192};
+
+#include "sgemm_tuning_table.inc"   // kHaveTunedTable, kTunedTable[m][n][k]
+
+int shape_class(int x) {
+    for (int c = 0; c < kNumClasses; ++c)
+        if (x <= kClassBound[c]) return c;
+    return kNumClasses - 1;
+}
+
+// Bytes of split partials a plan may keep in the stream's workspace.
+constexpr int64_t kMaxSplitBytes = (int64_t)1 << 30;
+
+struct Plan {
+    int variant;   // sgemm_f32_variant_id that runs
+    int config;    // MFMA tile configuration (MFMA variants)
+    int group_m;
+    int splits;
+};
+
+Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const float *B, int ldb) {
+    if (!ta && !tb && M <= sgemm::kSkinnyMaxM && sgemm::skinny_fits(lda, ldb))
+        return Plan{SGEMM_F32_SKINNY, 0, 0, 0};
+    const int config = prefer_small_tiles(M, N) ? 1 : 0;
+    if (!vec_aligned(ta, tb, A, lda, B, ldb)) return Plan{SGEMM_F32_MFMA_SCALAR, config, 8, 1};
+    return Plan{config ? SGEMM_F32_MFMA_SMALL : SGEMM_F32_MFMA_LARGE, config, 8, 1};
+}
+
+// The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
+// default_plan; for 16-byte-aligned operands the tuning table's entry for the
+// shape class when there is one (reported as SGEMM_F32_MFMA_TUNED when it
+// differs from the default).  Transposed operands use the same entries.
+Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
+    const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
+    if (!kHaveTunedTable || (d.variant != SGEMM_F32_MFMA_LARGE && d.variant != SGEMM_F32_MFMA_SMALL)) return d;
+    const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
+    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1) return d;
+    int k_per = 0;
+    int splits = sgemm::mfma_effective_splits(K, e.splits, &k_per);
+    if ((int64_t)splits * M * N * 4 > kMaxSplitBytes) splits = 1;
+    Plan p{SGEMM_F32_MFMA_TUNED, e.config, e.group_m, splits};
+    if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) return d;
+    return p;
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
 
 constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// One MFMA launch (plus the split reduction) after its plan is known.
+int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
+    if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
+    int k_per = 0;
+    const int eff = sgemm::mfma_effective_splits(g.K, splits, &k_per);
+    if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
+    if (eff > 1 && (int64_t)eff * g.M * g.N * 4 > kMaxSplitBytes) return SGEMM_F32_ERR_TOO_LARGE;
+    return to_status(sgemm::launch_mfma_config(g, config, vec, group_m, eff, stream));
+}
+
+GemmArgs make_args(int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda, const float *B,
+                   int ldb, float beta, float *C, int ldc) {
+    GemmArgs g;
+    g.M = M; g.N = N; g.K = K;
+    g.alpha = alpha; g.beta = beta;
+    g.A = A; g.B = B; g.C = C;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+    g.trans_a = ta; g.trans_b = tb;
+    return g;
+}
 
 int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda,
         const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
@@ -84,37 +156,32 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
     if (bad) return bad;
     if (M == 0 || N == 0) return 0;
 
-    GemmArgs g;
-    g.M = M; g.N = N; g.K = K;
-    g.alpha = alpha; g.beta = beta;
-    g.A = A; g.B = B; g.C = C;
-    g.lda = lda; g.ldb = ldb; g.ldc = ldc;
-    g.trans_a = ta; g.trans_b = tb;
-
+    const GemmArgs g = make_args(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
     if (alpha == 0.f || K == 0) {
         if ((int64_t)M * N > (int64_t)1 << 62) return SGEMM_F32_ERR_TOO_LARGE;
         return to_status(sgemm::launch_scale_c(g, stream));
     }
 
-    if (variant == SGEMM_F32_AUTO) variant = auto_variant(ta, tb, M, N, A, lda, B, ldb);
     const bool vec = vec_aligned(ta, tb, A, lda, B, ldb);
     const bool plain = !ta && !tb;
-    switch (variant) {
+    Plan p{variant, 0, 8, 1};
+    if (variant == SGEMM_F32_AUTO) {
+        p = auto_plan(ta, tb, M, N, K, A, lda, B, ldb);
+    } else if (variant == SGEMM_F32_MFMA_TUNED) {
+        if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
+        p = auto_plan(ta, tb, M, N, K, A, lda, B, ldb);
+    }
+    switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
-            if (sgemm::mfma_large_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-            return to_status(sgemm::launch_mfma_large(g, true, stream));
+            return run_mfma(g, 0, true, 8, 1, stream);
         case SGEMM_F32_MFMA_SMALL:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
-            if (sgemm::mfma_small_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-            return to_status(sgemm::launch_mfma_small(g, true, stream));
+            return run_mfma(g, 1, true, 8, 1, stream);
+        case SGEMM_F32_MFMA_TUNED:
+            return run_mfma(g, p.config, vec, p.group_m, p.splits, stream);
         case SGEMM_F32_MFMA_SCALAR:
-            if (prefer_small_tiles(M, N)) {
-                if (sgemm::mfma_small_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-                return to_status(sgemm::launch_mfma_small(g, false, stream));
-            }
-            if (sgemm::mfma_large_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-            return to_status(sgemm::launch_mfma_large(g, false, stream));
+            return run_mfma(g, prefer_small_tiles(M, N) ? 1 : 0, false, 8, 1, stream);
         case SGEMM_F32_VALU:
             if (!plain) return SGEMM_F32_ERR_NOT_APPLICABLE;
             if (sgemm::valu_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
@@ -128,6 +195,8 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
             return SGEMM_F32_ERR_VARIANT;
     }
 }
+
+bool flags_ok(int ta, int tb) { return (ta == 0 || ta == 1) && (tb == 0 || tb == 1); }
 
 }  // namespace
 
@@ -146,7 +215,7 @@ int sgemm_f32_variant(int variant, int M, int N, int K, float alpha, const float
 int sgemm_f32_select(int M, int N, int K, float alpha, const float *A, int lda, const float *B,
                      int ldb) {
     if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.f) return 0;
-    return auto_variant(0, 0, M, N, A, lda, B, ldb);
+    return auto_plan(0, 0, M, N, K, A, lda, B, ldb).variant;
 }
 
 int sgemm_f32_ex(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A, int lda,
@@ -162,9 +231,56 @@ int sgemm_f32_ex_variant(int variant, int trans_a, int trans_b, int M, int N, in
 
 int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A, int lda,
                         const float *B, int ldb) {
-    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return 0;
+    if (!flags_ok(trans_a, trans_b)) return 0;
     if (M <= 0 || N <= 0 || K <= 0 || alpha == 0.f) return 0;
-    return auto_variant(trans_a, trans_b, M, N, A, lda, B, ldb);
+    return auto_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb).variant;
+}
+
+int sgemm_f32_ex_plan(int trans_a, int trans_b, int M, int N, int K, float alpha, const float *A, int lda,
+                      const float *B, int ldb, int *variant, int *config, int *group_m, int *splits) {
+    if (variant == nullptr || config == nullptr || group_m == nullptr || splits == nullptr)
+        return SGEMM_F32_ERR_CONFIG;
+    *variant = *config = *group_m = *splits = 0;
+    if (!flags_ok(trans_a, trans_b)) return SGEMM_F32_ERR_TRANS;
+    if (M < 0) return 1;
+    if (N < 0) return 2;
+    if (K < 0) return 3;
+    if (M == 0 || N == 0 || K == 0 || alpha == 0.f) return 0;
+    const Plan p = auto_plan(trans_a, trans_b, M, N, K, A, lda, B, ldb);
+    *variant = p.variant;
+    if (p.variant == SGEMM_F32_SKINNY || p.variant == SGEMM_F32_VALU) return 0;
+    *config = p.config;
+    *group_m = p.group_m;
+    int k_per = 0;
+    *splits = sgemm::mfma_effective_splits(K, p.splits, &k_per);
+    return 0;
+}
+
+int sgemm_f32_ex_config(int config, int group_m, int splits, int trans_a, int trans_b, int M, int N, int K,
+                        float alpha, const float *A, int lda, const float *B, int ldb, float beta, float *C,
+                        int ldc, hipStream_t stream) {
+    if (config < 0 || config >= sgemm::kNumMfmaConfigs || group_m < 1 || group_m > 64 || splits < 1 ||
+        splits > 64)
+        return SGEMM_F32_ERR_CONFIG;
+    const int bad = validate(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, C, ldc);
+    if (bad) return bad;
+    if (M == 0 || N == 0) return 0;
+    const GemmArgs g = make_args(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    if (alpha == 0.f || K == 0) return to_status(sgemm::launch_scale_c(g, stream));
+    return run_mfma(g, config, vec_aligned(trans_a, trans_b, A, lda, B, ldb), group_m, splits, stream);
+}
+
+int sgemm_f32_tuning_table_present(void) { return kHaveTunedTable ? 1 : 0; }
+
+const char *sgemm_f32_config_name(int config) {
+    switch (config) {
+        case 0: return "128x128";
+        case 1: return "64x64";
+        case 2: return "128x64";
+        case 3: return "64x128";
+        case 4: return "64x64_pf2";
+        default: return nullptr;
+    }
 }
 
 const char *sgemm_f32_variant_name(int variant) {
@@ -175,10 +291,11 @@ const char *sgemm_f32_variant_name(int variant) {
         case SGEMM_F32_VALU: return "valu";
         case SGEMM_F32_SKINNY: return "skinny";
         case SGEMM_F32_MFMA_SCALAR: return "mfma_scalar";
+        case SGEMM_F32_MFMA_TUNED: return "mfma_tuned";
         default: return nullptr;
     }
 }
 
-int sgemm_f32_version(void) { return 200; }
+int sgemm_f32_version(void) { return 300; }
 
 }  // extern "C"

@@ -425,15 +425,43 @@ __device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int ti
     }
 }
 
+// Split of the reduction over work-groups (split-K, "Writing a Fast Matmul in
+// CUDA, Step by Step", section "In the real world": too few output tiles to
+// fill the GPU, so the K loop is divided and the partial results added).  Split
+// s of `splits` covers k in [s*k_per, min(K, (s+1)*k_per)), k_per a multiple of
+// BK, and writes its unscaled partial product to ws + s*M*N (row-major, row
+// stride N); splitk_reduce_kernel then adds the partials in split order.
+struct SplitK {
+    int splits;
+    int k_per;
+    float *ws;
+};
+
 // At least two waves per SIMD: with one wave per SIMD the matrix core idles
 // whenever that wave waits at a barrier or on memory.
 template <class T, bool VEC>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
-    GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    GemmArgs g, int tiles_m, int tiles_n, int group_m, SplitK sk) {
     __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
 
+    int bid = blockIdx.x;
+    if (sk.splits > 1) {
+        // Work-groups [s*tiles, (s+1)*tiles) compute split s: the same
+        // product on a K range, with its operands' origins moved along k.
+        const int tiles = tiles_m * tiles_n;
+        const int sp = bid / tiles;
+        bid -= sp * tiles;
+        const int kb = sp * sk.k_per;
+        g.A += T::PA::L == kKMajor ? (int64_t)kb : (int64_t)kb * g.lda;
+        g.B += T::PB::L == kXMajor ? (int64_t)kb * g.ldb : (int64_t)kb;
+        g.K = min(sk.k_per, g.K - kb);
+        g.C = sk.ws + (int64_t)sp * g.M * g.N;
+        g.ldc = g.N;
+        g.alpha = 1.f;
+        g.beta = 0.f;
+    }
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    tile_of_block(bid, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * T::BM, n0 = tn * T::BN;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -491,58 +519,155 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         }
 }
 
-// 128x128 tiles: two slices in flight with 16-byte loads; one with 4-byte
-// loads (whose staging registers would not fit two sets at two waves per SIMD).
+// C = alpha * (the split partials added in split order) + beta * C.  VEC4: N,
+// ldc and C allow 16-byte accesses, so each thread takes four columns.
+template <bool VEC4>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, const float *ws, int splits) {
+    const int64_t total = (int64_t)g.M * g.N;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const float alpha = g.alpha, beta = g.beta;
+    if (VEC4) {
+        for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total / 4; q += stride) {
+            const int64_t t = 4 * q;
+            float4 sum = *reinterpret_cast<const float4 *>(ws + t);
+            for (int sp = 1; sp < splits; ++sp) {
+                const float4 v = *reinterpret_cast<const float4 *>(ws + sp * total + t);
+                sum.x += v.x;
+                sum.y += v.y;
+                sum.z += v.z;
+                sum.w += v.w;
+            }
+            const int64_t i = t / g.N, j = t - i * g.N;
+            float4 *p = reinterpret_cast<float4 *>(g.C + i * g.ldc + j);
+            float4 r = make_float4(alpha * sum.x, alpha * sum.y, alpha * sum.z, alpha * sum.w);
+            if (beta != 0.f) {
+                const float4 c = *p;
+                r = make_float4(fmaf(beta, c.x, r.x), fmaf(beta, c.y, r.y), fmaf(beta, c.z, r.z),
+                                fmaf(beta, c.w, r.w));
+            }
+            *p = r;
+        }
+    } else {
+        for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
+            float sum = ws[t];
+            for (int sp = 1; sp < splits; ++sp) sum += ws[sp * total + t];
+            const int64_t i = t / g.N, j = t - i * g.N;
+            float *p = g.C + i * g.ldc + j;
+            float v = alpha * sum;
+            if (beta != 0.f) v = fmaf(beta, *p, v);
+            *p = v;
+        }
+    }
+}
+
+// Tile configurations.  128x128: two slices in flight with 16-byte loads, one
+// with 4-byte loads (whose staging registers would not fit two sets at two
+// waves per SIMD).  The others are shapes for grids that 128x128 tiles would
+// leave short of work-groups.
 template <int LA, int LB>
 using LargeTile = MfmaTile<128, 128, 32, 64, 64, 2, LA, LB>;
 template <int LA, int LB>
 using LargeTileScalar = MfmaTile<128, 128, 32, 64, 64, 1, LA, LB>;
 template <int LA, int LB>
 using SmallTile = MfmaTile<64, 64, 32, 32, 32, 1, LA, LB>;
+template <int LA, int LB>
+using TallTile = MfmaTile<128, 64, 32, 64, 32, 2, LA, LB>;
+template <int LA, int LB>
+using WideTile = MfmaTile<64, 128, 32, 32, 64, 2, LA, LB>;
+template <int LA, int LB>
+using SmallTile2 = MfmaTile<64, 64, 32, 32, 32, 2, LA, LB>;
 
-template <class TV, class TS>
-hipError_t launch_tile(const GemmArgs &g, bool vec, int group_m, hipStream_t stream) {
-    static_assert(TV::BM == TS::BM && TV::BN == TS::BN, "same tile");
-    const int tiles_m = (g.M + TV::BM - 1) / TV::BM;
-    const int tiles_n = (g.N + TV::BN - 1) / TV::BN;
-    const dim3 grid(tiles_m * tiles_n);
-    if (vec) hipLaunchKernelGGL((sgemm_mfma_kernel<TV, true>), grid, dim3(TV::NT), 0, stream, g, tiles_m, tiles_n, group_m);
-    else hipLaunchKernelGGL((sgemm_mfma_kernel<TS, false>), grid, dim3(TS::NT), 0, stream, g, tiles_m, tiles_n, group_m);
+constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64};
+constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64};
+constexpr int kTileBK = 32;
+
+template <class T, bool VEC>
+hipError_t launch_one(const GemmArgs &g, int group_m, const SplitK &sk, hipStream_t stream) {
+    const int tiles_m = (g.M + T::BM - 1) / T::BM;
+    const int tiles_n = (g.N + T::BN - 1) / T::BN;
+    const dim3 grid(tiles_m * tiles_n * sk.splits);
+    hipLaunchKernelGGL((sgemm_mfma_kernel<T, VEC>), grid, dim3(T::NT), 0, stream, g, tiles_m, tiles_n, group_m, sk);
     return hipGetLastError();
 }
 
 template <int LA, int LB>
-hipError_t launch_layouts(const GemmArgs &g, bool large, bool vec, hipStream_t stream) {
-    if (large) return launch_tile<LargeTile<LA, LB>, LargeTileScalar<LA, LB>>(g, vec, 8, stream);
-    return launch_tile<SmallTile<LA, LB>, SmallTile<LA, LB>>(g, vec, 8, stream);
+hipError_t launch_layouts(const GemmArgs &g, int config, bool vec, int group_m, const SplitK &sk,
+                          hipStream_t stream) {
+    switch (config) {
+        case 0:
+            return vec ? launch_one<LargeTile<LA, LB>, true>(g, group_m, sk, stream)
+                       : launch_one<LargeTileScalar<LA, LB>, false>(g, group_m, sk, stream);
+        case 1:
+            return vec ? launch_one<SmallTile<LA, LB>, true>(g, group_m, sk, stream)
+                       : launch_one<SmallTile<LA, LB>, false>(g, group_m, sk, stream);
+        case 2: return launch_one<TallTile<LA, LB>, true>(g, group_m, sk, stream);
+        case 3: return launch_one<WideTile<LA, LB>, true>(g, group_m, sk, stream);
+        case 4: return launch_one<SmallTile2<LA, LB>, true>(g, group_m, sk, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 // A as given is kKMajor and B kXMajor; a transposed operand swaps its layout.
-hipError_t launch_mfma(const GemmArgs &g, bool large, bool vec, hipStream_t stream) {
+hipError_t launch_kernel(const GemmArgs &g, int config, bool vec, int group_m, const SplitK &sk,
+                         hipStream_t stream) {
     const bool ta = g.trans_a != 0, tb = g.trans_b != 0;
-    if (!ta && !tb) return launch_layouts<kKMajor, kXMajor>(g, large, vec, stream);
-    if (!ta && tb) return launch_layouts<kKMajor, kKMajor>(g, large, vec, stream);
-    if (ta && !tb) return launch_layouts<kXMajor, kXMajor>(g, large, vec, stream);
-    return launch_layouts<kXMajor, kKMajor>(g, large, vec, stream);
+    if (!ta && !tb) return launch_layouts<kKMajor, kXMajor>(g, config, vec, group_m, sk, stream);
+    if (!ta && tb) return launch_layouts<kKMajor, kKMajor>(g, config, vec, group_m, sk, stream);
+    if (ta && !tb) return launch_layouts<kXMajor, kXMajor>(g, config, vec, group_m, sk, stream);
+    return launch_layouts<kXMajor, kKMajor>(g, config, vec, group_m, sk, stream);
 }
 
 }  // namespace
 
-int64_t mfma_large_grid(int M, int N) {
-    using T = LargeTile<kKMajor, kXMajor>;
-    return (int64_t)((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
+int64_t mfma_config_tiles(int config, int M, int N) {
+    if (config < 0 || config >= kNumMfmaConfigs) return -1;
+    return (int64_t)((M + kTileBM[config] - 1) / kTileBM[config]) * ((N + kTileBN[config] - 1) / kTileBN[config]);
 }
-int64_t mfma_small_grid(int M, int N) {
-    using T = SmallTile<kKMajor, kXMajor>;
-    return (int64_t)((M + T::BM - 1) / T::BM) * ((N + T::BN - 1) / T::BN);
+int64_t mfma_large_grid(int M, int N) { return mfma_config_tiles(0, M, N); }
+int64_t mfma_small_grid(int M, int N) { return mfma_config_tiles(1, M, N); }
+
+bool mfma_config_scalar_ok(int config) { return config == 0 || config == 1; }
+
+int mfma_effective_splits(int K, int splits, int *k_per) {
+    if (splits < 1) splits = 1;
+    int per = (K + splits - 1) / splits;
+    per = (per + kTileBK - 1) / kTileBK * kTileBK;
+    if (per < kTileBK) per = kTileBK;
+    *k_per = per;
+    return (K + per - 1) / per;
+}
+
+hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
+                              hipStream_t stream) {
+    SplitK sk;
+    sk.splits = mfma_effective_splits(g.K, splits, &sk.k_per);
+    sk.ws = nullptr;
+    if (sk.splits <= 1) {
+        sk.splits = 1;
+        sk.k_per = g.K;
+        return launch_kernel(g, config, vec_loads, group_m, sk, stream);
+    }
+    hipError_t e = stream_workspace((size_t)sk.splits * g.M * g.N * sizeof(float), stream,
+                                    reinterpret_cast<void **>(&sk.ws));
+    if (e != hipSuccess) return e;
+    e = launch_kernel(g, config, vec_loads, group_m, sk, stream);
+    if (e != hipSuccess) return e;
+    const int64_t total = (int64_t)g.M * g.N;
+    const bool vec4 = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
+    int64_t blocks = ((vec4 ? total / 4 : total) + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    if (blocks < 1) blocks = 1;
+    if (vec4) hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws, sk.splits);
+    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws, sk.splits);
+    return hipGetLastError();
 }
 
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_mfma(g, true, vec_loads, stream);
+    return launch_mfma_config(g, 0, vec_loads, 8, 1, stream);
 }
 
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    return launch_mfma(g, false, vec_loads, stream);
+    return launch_mfma_config(g, 1, vec_loads, 8, 1, stream);
 }
 
 }  // namespace sgemm

@@ -33,11 +33,14 @@
  *     returns without waiting for it.  No host or device synchronisation.
  *   - The functions hold no per-call state and may be called from several host
  *     threads at once.
- *   - Device memory: none for M > 16.  For M <= 16 with a split reduction the
- *     library keeps one workspace per (device, stream), allocated with
- *     hipMalloc on the first such call on that stream (a few MiB, grown when a
- *     call needs more, which waits for that stream's pending work) and held
- *     until the process ends.  Calls on different streams never share it.
+ *   - Device memory: none unless the reduction over K is split across
+ *     work-groups (the M <= 16 kernel, and MFMA plans with splits > 1 from the
+ *     tuning table or sgemm_f32_ex_config).  Those keep one workspace per
+ *     (device, stream), allocated with hipMalloc on the first such call on
+ *     that stream (at least 4 MiB, at most splits * M * N floats, 1 GiB cap for
+ *     MFMA plans; grown when a call needs more, which waits for that stream's
+ *     pending work) and held until the process ends.  Calls on different
+ *     streams never share it.
  *
  * Special cases:
  *   - M == 0 or N == 0: nothing is done, returns 0.
@@ -55,6 +58,8 @@
  *                            cannot run this shape or alignment
  *     SGEMM_F32_ERR_TOO_LARGE  the tile grid exceeds the launch limits
  *     SGEMM_F32_ERR_TRANS    (the _ex functions) a transpose flag other than 0 or 1
+ *     SGEMM_F32_ERR_CONFIG   (sgemm_f32_ex_config, sgemm_f32_ex_plan) a configuration,
+ *                            grouping or split count out of range, or a NULL output
  *     < 0                    -(hipError_t) reported by the HIP runtime for the
  *                            launch; the contents of C are then unspecified
  * Nothing is printed and no exception crosses the interface.
@@ -72,6 +77,7 @@ extern "C" {
 #define SGEMM_F32_ERR_NOT_APPLICABLE 21
 #define SGEMM_F32_ERR_TOO_LARGE 22
 #define SGEMM_F32_ERR_TRANS 23
+#define SGEMM_F32_ERR_CONFIG 24
 
 /* Kernel variants that sgemm_f32_variant can force. */
 enum sgemm_f32_variant_id {
@@ -81,7 +87,18 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
     SGEMM_F32_SKINNY = 4,         /* M <= 16: FP32 MFMA streaming kernel */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
-    SGEMM_F32_NUM_VARIANTS = 6
+    SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the tuning table's plan (16-byte loads) */
+    SGEMM_F32_NUM_VARIANTS = 7
+};
+
+/* MFMA tile configurations (sgemm_f32_ex_config, sgemm_f32_ex_plan). */
+enum sgemm_f32_config_id {
+    SGEMM_F32_CFG_128x128 = 0,    /* the SGEMM_F32_MFMA_LARGE tile */
+    SGEMM_F32_CFG_64x64 = 1,      /* the SGEMM_F32_MFMA_SMALL tile */
+    SGEMM_F32_CFG_128x64 = 2,     /* 16-byte loads only */
+    SGEMM_F32_CFG_64x128 = 3,     /* 16-byte loads only */
+    SGEMM_F32_CFG_64x64_PF2 = 4,  /* 64x64, two slices in flight; 16-byte loads only */
+    SGEMM_F32_NUM_CONFIGS = 5
 };
 
 /*
@@ -156,10 +173,54 @@ int sgemm_f32_ex_variant(int variant, int trans_a, int trans_b, int M, int N, in
 int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alpha,
                         const float *A, int lda, const float *B, int ldb);
 
+/*
+ * Tuned selection.  Tiling parameters are tuned per problem shape ("How a
+ * Matmul Kernel Gets Fast", section "Kernel 9: autotuning"; the vendor library
+ * chooses among shape-specialised kernels, "Writing a Fast Matmul in CUDA, Step
+ * by Step", section "In the real world").  The library carries a table from
+ * shape classes of (M, N, K) (class bounds 64, 128, ..., 8192 per extent) to a
+ * plan: a tile configuration, a tile-row grouping of the work-group order and
+ * a split of K over work-groups.  The table is measured on the GPU by the
+ * package's tuning script (fp32_sgemm_amd/tune.py) and compiled in; for
+ * 16-byte-aligned operands sgemm_f32 and sgemm_f32_ex follow it (other cases as
+ * before).  A split plan sums its partials in split order, so results are
+ * deterministic, and may differ in the last bits from an unsplit plan.
+ *
+ * sgemm_f32_ex_plan: the plan sgemm_f32_ex would run, host only, no HIP call:
+ * *variant (an sgemm_f32_variant_id; 0 when no GEMM kernel runs), and for MFMA
+ * variants *config, *group_m and *splits (the split count after rounding each
+ * split's K extent up to a multiple of 32).  Returns 0, a positional error for
+ * negative sizes, SGEMM_F32_ERR_TRANS, or SGEMM_F32_ERR_CONFIG for a NULL
+ * output pointer.
+ *
+ * sgemm_f32_ex_config: runs one MFMA configuration with the given grouping
+ * (1..64 tile rows) and requested split count (1..64; K is cut into extents
+ * that are multiples of 32, so fewer splits may run).  Configurations 2-4 need
+ * the 16-byte-load conditions of SGEMM_F32_MFMA_LARGE and return
+ * SGEMM_F32_ERR_NOT_APPLICABLE otherwise; 0 and 1 fall back to 4-byte loads.
+ * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
+ * Other arguments and return codes are those of sgemm_f32_ex.
+ */
+int sgemm_f32_ex_plan(int trans_a, int trans_b, int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      int *variant, int *config, int *group_m, int *splits);
+
+int sgemm_f32_ex_config(int config, int group_m, int splits, int trans_a, int trans_b,
+                        int M, int N, int K, float alpha, const float *A, int lda,
+                        const float *B, int ldb, float beta, float *C, int ldc,
+                        hipStream_t stream);
+
+/* Short static name of a configuration ("128x128", ...), or NULL if unknown. */
+const char *sgemm_f32_config_name(int config);
+
+/* 1 when a measured tuning table is compiled in, 0 when every shape uses the
+   default choice. */
+int sgemm_f32_tuning_table_present(void);
+
 /* Short static name of a variant ("mfma_large", ...), or NULL if unknown. */
 const char *sgemm_f32_variant_name(int variant);
 
-/* Library version, e.g. 200 for 0.2.0. */
+/* Library version, e.g. 300 for 0.3.0. */
 int sgemm_f32_version(void);
 
 #ifdef __cplusplus

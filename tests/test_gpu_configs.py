@@ -1,0 +1,179 @@
+"""GPU parity of every MFMA tile configuration, tile-row grouping and K split
+that the tuning table can choose (sgemm_f32_ex_config), in all four operand
+forms, against the oracle; and of the automatic plan on shapes whose class has
+a tuned entry."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import check_sampled, from_device_padded, sample_positions, say, to_device_padded
+
+pytestmark = pytest.mark.gpu
+
+FORMS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+FORM_IDS = ["nn", "nt", "tn", "tt"]
+
+
+@pytest.fixture(scope="module")
+def sg():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import fp32_sgemm_amd
+    return fp32_sgemm_amd
+
+
+def _stored(x, t):
+    return np.ascontiguousarray(x.T) if t else x
+
+
+def _inputs(M, N, K, dist, seed):
+    w = workloads.custom(M, N, K, dist=dist, seed=seed, c0_dist="normal" if dist != "int4" else "int4")
+    return workloads.make_inputs(w)
+
+
+def run_cfg(sg, cfg, gm, splits, ta, tb, A, B, C0, alpha, beta, stream=None):
+    M, K = A.shape
+    N = B.shape[1]
+    As, Bs = _stored(A, ta), _stored(B, tb)
+    r4 = lambda x: (max(x, 1) + 3) // 4 * 4
+    lda, ldb, ldc = r4(As.shape[1]), r4(Bs.shape[1]), N
+    bA, pA, _ = to_device_padded(As, lda)
+    bB, pB, _ = to_device_padded(Bs, ldb)
+    bC, pC, _ = to_device_padded(C0, ldc, fill=np.float32(-7.25))
+    s = stream or torch.cuda.current_stream()
+    st = sg.sgemm_f32_ex_config(cfg, gm, splits, ta, tb, M, N, K, float(alpha), pA, lda, pB, ldb,
+                                float(beta), pC, ldc, s.cuda_stream)
+    torch.cuda.synchronize()
+    return st, from_device_padded(bC, M, N, ldc), As, Bs
+
+
+def check(C, As, Bs, ta, tb, alpha, beta, C0, exact):
+    Cref, absab = oracle.sgemm_ref_op(As, Bs, ta, tb, alpha, beta, C0)
+    if exact:
+        return oracle.check_bitexact(C, Cref)
+    return oracle.check_within_bound(C, Cref, oracle.error_bound(absab, alpha, beta, C0))
+
+
+SHAPES = [(129, 127, 65), (300, 260, 700), (64, 64, 32), (257, 129, 1000), (130, 70, 9), (65, 200, 333)]
+
+
+@pytest.mark.parametrize("splits", [1, 2, 5])
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+def test_config_real(sg, cfg, splits, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[cfg_real] cfg={cfg} splits={splits} {form} {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 700 + M + N + K)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, splits, ta, tb, A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 1.25, -0.5, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+def test_config_integer_bitexact(sg, cfg, splits, form):
+    """Integer-valued inputs are exact in FP32 in any summation order, so a
+    split reduction must match bit for bit too."""
+    M, N, K = 201, 157, 611
+    ta, tb = form
+    say(f"[cfg_int] cfg={cfg} splits={splits} {form}")
+    A, B, C0 = _inputs(M, N, K, "int4", 800 + cfg)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, splits, ta, tb, A, B, C0, 2.0, -1.0)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 2.0, -1.0, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("gm", [1, 3, 16, 64])
+@pytest.mark.parametrize("cfg", range(5))
+def test_tile_row_grouping(sg, cfg, gm):
+    M, N, K = 1000, 900, 96
+    say(f"[cfg_group] cfg={cfg} gm={gm}")
+    A, B, C0 = _inputs(M, N, K, "int4", 900 + gm)
+    st, C, As, Bs = run_cfg(sg, cfg, gm, 1, 0, 0, A, B, C0, 1.0, 1.0)
+    assert st == 0
+    ok, info = check(C, As, Bs, 0, 0, 1.0, 1.0, C0, exact=True)
+    assert ok, info
+
+
+def test_split_beta_zero_ignores_nan_c(sg):
+    M, N, K = 130, 66, 400
+    A, B, _ = _inputs(M, N, K, "uniform", 31)
+    C0 = np.full((M, N), np.nan, np.float32)
+    st, C, As, Bs = run_cfg(sg, 0, 8, 4, 0, 0, A, B, C0, 1.0, 0.0)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check(C, As, Bs, 0, 0, 1.0, 0.0, None, exact=False)
+    assert ok, info
+
+
+def test_split_odd_n_scalar_reduction(sg):
+    """N not a multiple of 4 takes the element-wise reduction."""
+    M, N, K = 77, 63, 500
+    A, B, C0 = _inputs(M, N, K, "uniform", 32)
+    st, C, As, Bs = run_cfg(sg, 0, 8, 3, 0, 0, A, B, C0, 0.5, 2.0)
+    assert st == 0
+    ok, info = check(C, As, Bs, 0, 0, 0.5, 2.0, C0, exact=False)
+    assert ok, info
+
+
+def test_split_plans_on_two_streams(sg):
+    """Two split products in flight on two streams: each stream's partials
+    live in its own workspace."""
+    M, N, K = 512, 512, 4096
+    A1, B1, _ = _inputs(M, N, K, "uniform", 33)
+    A2, B2, _ = _inputs(M, N, K, "uniform", 34)
+    d = [torch.from_numpy(x).cuda() for x in (A1, B1, A2, B2)]
+    C1 = torch.zeros(M, N, device="cuda:0")
+    C2 = torch.zeros(M, N, device="cuda:0")
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        assert sg.sgemm_f32_ex_config(0, 8, 4, 0, 0, M, N, K, 1.0, d[0].data_ptr(), K, d[1].data_ptr(), N,
+                                      0.0, C1.data_ptr(), N, s1.cuda_stream) == 0
+        assert sg.sgemm_f32_ex_config(2, 8, 8, 0, 0, M, N, K, 1.0, d[2].data_ptr(), K, d[3].data_ptr(), N,
+                                      0.0, C2.data_ptr(), N, s2.cuda_stream) == 0
+    torch.cuda.synchronize()
+    for C, A, B in ((C1, A1, B1), (C2, A2, B2)):
+        Cref, absab = oracle.sgemm_ref(A, B)
+        ok, info = oracle.check_within_bound(C.cpu().numpy(), Cref, oracle.error_bound(absab, 1.0, 0.0, None))
+        assert ok, info
+
+
+def test_split_repeat_bitwise_identical(sg):
+    M, N, K = 300, 400, 3000
+    A, B, C0 = _inputs(M, N, K, "uniform", 35)
+    r1 = run_cfg(sg, 3, 8, 6, 0, 1, A, B, C0, 1.0, 0.5)
+    r2 = run_cfg(sg, 3, 8, 6, 0, 1, A, B, C0, 1.0, 0.5)
+    assert r1[0] == 0 and r2[0] == 0
+    assert np.array_equal(r1[1].view(np.uint32), r2[1].view(np.uint32))
+
+
+TUNED_SHAPES = [(1024, 1024, 1024), (2048, 2048, 2048), (512, 512, 8192), (4096, 1024, 256),
+                (256, 4096, 4096), (2048, 2048, 512)]
+
+
+@pytest.mark.parametrize("shape", TUNED_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in TUNED_SHAPES])
+def test_automatic_plan(sg, shape):
+    """sgemm_f32 on shapes across the table's classes, whatever plan the table
+    gives, checked on sampled entries."""
+    M, N, K = shape
+    A, B, C0 = _inputs(M, N, K, "uniform", 36 + M // 64)
+    st_p = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.5, 0x100000, K, 0x100000, N)
+    say(f"[auto_plan] {shape} plan={st_p}")
+    dA, dB, dC = (torch.from_numpy(x).cuda() for x in (A, B, C0))
+    st = sg.sgemm_f32(M, N, K, 1.5, dA.data_ptr(), K, dB.data_ptr(), N, -0.5, dC.data_ptr(), N,
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    C = dC.cpu().numpy()
+    rows, cols = sample_positions(M, N, 3000, seed=M + N + K)
+    ok, info = check_sampled(C, A, B, 1.5, -0.5, C0, rows, cols)
+    assert ok, info

@@ -77,8 +77,9 @@ def test_kernel_selection(sg):
     al = 0x100000          # 16-byte aligned stand-in pointers (never dereferenced)
     assert sg.sgemm_f32_select(4096, 4096, 4096, 1.5, al, 4096, al, 4096) == sg.MFMA_LARGE
     assert sg.sgemm_f32_select(4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
-    assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) == sg.MFMA_SMALL
-    assert sg.sgemm_f32_select(128, 128, 128, 1.0, al, 128, al, 128) == sg.MFMA_SMALL
+    # Shapes with few 128x128 tiles: the small tile, or the tuning table's plan.
+    assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
+    assert sg.sgemm_f32_select(128, 128, 128, 1.0, al, 128, al, 128) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
     assert sg.sgemm_f32_select(16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
     assert sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096) == sg.MFMA_SCALAR
     assert sg.sgemm_f32_select(4096, 4096, 4097, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
@@ -112,8 +113,8 @@ def test_transposed_kernel_selection(sg):
     sel = sg.sgemm_f32_ex_select
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_LARGE
-        assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) == sg.MFMA_SMALL
-        assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_SMALL
+        assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
+        assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
     assert sel(0, 0, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
     assert sel(0, 0, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == \
@@ -128,9 +129,70 @@ def test_transposed_kernel_selection(sg):
 
 def test_variant_names_and_version(sg):
     names = [sg.sgemm_f32_variant_name(i) for i in range(sg.NUM_VARIANTS)]
-    assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar"]
+    assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar", "mfma_tuned"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
-    assert sg.sgemm_f32_version() >= 200
+    cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
+    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2"]
+    assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
+    assert sg.sgemm_f32_version() >= 300
+
+
+def test_config_and_plan_argument_errors_without_touching_the_gpu(sg):
+    p = 0x1000
+    f = sg.sgemm_f32_ex_config
+    for bad in [(-1, 8, 1), (sg.NUM_CONFIGS, 8, 1), (0, 0, 1), (0, 65, 1), (0, 8, 0), (0, 8, 65)]:
+        assert f(*bad, 0, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_CONFIG, bad
+    assert f(0, 8, 1, 0, 0, -1, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 1
+    assert f(0, 8, 1, 3, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_TRANS
+    assert f(0, 8, 1, 0, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, 0, 2, 0) == 10
+    assert f(0, 8, 1, 0, 0, 0, 2, 2, 1.0, 0, 2, 0, 2, 0.0, 0, 2, 0) == 0        # empty output
+    # The 16-byte-only configurations refuse misaligned operands before any launch.
+    for cfg in (2, 3, 4):
+        assert f(cfg, 8, 1, 0, 0, 64, 64, 64, 1.0, p + 4, 64, p, 64, 0.0, p, 64, 0) == sg.ERR_NOT_APPLICABLE
+    # A split plan whose partials exceed 1 GiB is refused before any launch.
+    assert f(0, 8, 64, 0, 0, 8192, 8192, 8192, 1.0, p, 8192, p, 8192, 0.0, p, 8192, 0) == sg.ERR_TOO_LARGE
+    assert sg.sgemm_f32_ex_plan(2, 0, 4, 4, 4, 1.0, p, 4, p, 4)[0] == sg.ERR_TRANS
+    assert sg.sgemm_f32_ex_plan(0, 0, 4, -4, 4, 1.0, p, 4, p, 4)[0] == 2
+    assert sg.sgemm_f32_ex_plan(0, 0, 4, 4, 0, 1.0, p, 4, p, 4) == (0, 0, 0, 0, 0)
+
+
+def test_plan_follows_the_tuning_table(sg):
+    """The automatic plan for aligned operands is the tuning table's entry of
+    the shape class (or the default choice when no table is compiled in)."""
+    import json
+    import os
+    al = 0x100000
+    st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 16, 4096, 4096, 1.0, al, 4096, al, 4096)
+    assert (st, v) == (0, sg.SKINNY)
+    st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4097, 1.0, al, 4097, al, 4096)
+    assert (st, v, sp) == (0, sg.MFMA_SCALAR, 1)
+    path = os.path.join(os.path.dirname(sg.__file__), "tuning_table.json")
+    if not sg.sgemm_f32_tuning_table_present():
+        assert not os.path.exists(path)
+        for shape in [(4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024)]:
+            st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, *shape, 1.0, al, shape[2], al, shape[1])
+            assert v in (sg.MFMA_LARGE, sg.MFMA_SMALL) and gm == 8 and sp == 1
+        return
+    table = json.load(open(path))
+    bounds = table["class_bounds"]
+    assert bounds == [64, 128, 256, 512, 1024, 2048, 4096, 8192]
+    for e in table["entries"]:
+        M, N, K = e["shape"]
+        st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, al, K, al, N)
+        if M <= 16:
+            assert v == sg.SKINNY
+            continue
+        assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
+        assert (cfg, gm) == (e["config"], e["group_m"]), e
+        k_per = -(-K // e["splits"])
+        k_per = -(-k_per // 32) * 32
+        assert sp == -(-K // k_per), e
+        # Every extent in the class maps to the same entry.
+        st2, v2, cfg2, gm2, sp2 = sg.sgemm_f32_ex_plan(0, 0, M - 1 if M > 64 else M, N, K, 1.0, al, K, al, N)
+        assert (cfg2, gm2) == (cfg, gm)
+
+
+
 
 
 def test_tile_mapping_is_a_bijection(tmp_path):
