@@ -33,7 +33,8 @@ CFG_64x64 = 1
 CFG_128x64 = 2
 CFG_64x128 = 3
 CFG_64x64_PF2 = 4
-NUM_CONFIGS = 5
+CFG_128x128_STREAMK = 5
+NUM_CONFIGS = 6
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

@@ -27,16 +27,19 @@ hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stre
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 
 // MFMA tile configurations: 0 = 128x128 (the large tile), 1 = 64x64 (the
-// small tile), 2 = 128x64, 3 = 64x128, 4 = 64x64 with two slices in flight.
-// Configurations 2-4 exist with 16-byte loads only.  `group_m` is the number
-// of tile rows walked together by the tile order; `splits` divides K over
-// work-groups (the partial sums go through the stream's workspace and a
-// reduction kernel).
-constexpr int kNumMfmaConfigs = 5;
+// small tile), 2 = 128x64, 3 = 64x128, 4 = 64x64 with two slices in flight,
+// 5 = 128x128 persistent with stream-K (resident work-groups take whole tiles
+// in rounds, then equal shares of the remaining tiles' K slices; split tiles
+// are summed by a fix-up kernel).  Configurations 2-5 exist with 16-byte loads
+// only.  `group_m` is the number of tile rows walked together by the tile
+// order; `splits` divides K over work-groups (the partial sums go through the
+// stream's workspace and a reduction kernel; not with configuration 5).
+constexpr int kNumMfmaConfigs = 6;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
 int64_t mfma_config_tiles(int config, int M, int N);
 bool mfma_config_scalar_ok(int config);
+bool mfma_config_splits_ok(int config);
 // Number of non-empty splits of K actually used for a requested count, and the
 // K extent of each (a multiple of the tile depth).
 int mfma_effective_splits(int K, int splits, int *k_per);
@@ -73,14 +76,10 @@ bool skinny_fits(int lda, int ldb);
 // ---------------------------------------------------------------------------
 constexpr int kNumXcd = 8;
 
-__host__ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
-                                              int group_m, int &tm, int &tn) {
-    const int total = tiles_m * tiles_n;
-    const int per = total / kNumXcd;
-    const int rem = total % kNumXcd;
-    const int xcd = bid % kNumXcd;
-    const int local = bid / kNumXcd;
-    const int t = xcd * per + (xcd < rem ? xcd : rem) + local;
+// Tile t of the grouped order: groups of `group_m` tile rows, column by column
+// inside a group.
+__host__ __device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int group_m, int &tm,
+                                                     int &tn) {
     const int in_group = group_m * tiles_n;
     const int g = t / in_group;
     const int first_m = g * group_m;
@@ -88,6 +87,21 @@ __host__ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int
     const int r = t - g * in_group;
     tm = first_m + r % gm;
     tn = r / gm;
+}
+
+// Work-group id -> position in an XCD-contiguous order: XCD x (= id % 8)
+// receives positions [x*per + min(x, rem), ...) in launch order.
+__host__ __device__ __forceinline__ int xcd_position(int bid, int total) {
+    const int per = total / kNumXcd;
+    const int rem = total % kNumXcd;
+    const int xcd = bid % kNumXcd;
+    const int local = bid / kNumXcd;
+    return xcd * per + (xcd < rem ? xcd : rem) + local;
+}
+
+__host__ __device__ __forceinline__ void tile_of_block(int bid, int tiles_m, int tiles_n,
+                                              int group_m, int &tm, int &tn) {
+    tile_coords(xcd_position(bid, tiles_m * tiles_n), tiles_m, tiles_n, group_m, tm, tn);
 }
 
 }  // namespace sgemm

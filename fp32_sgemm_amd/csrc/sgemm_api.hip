@@ -132,7 +132,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
-    const int eff = sgemm::mfma_effective_splits(g.K, splits, &k_per);
+    const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
     if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
     if (eff > 1 && (int64_t)eff * g.M * g.N * 4 > kMaxSplitBytes) return SGEMM_F32_ERR_TOO_LARGE;
     return to_status(sgemm::launch_mfma_config(g, config, vec, group_m, eff, stream));
@@ -260,7 +260,7 @@ int sgemm_f32_ex_config(int config, int group_m, int splits, int trans_a, int tr
                         float alpha, const float *A, int lda, const float *B, int ldb, float beta, float *C,
                         int ldc, hipStream_t stream) {
     if (config < 0 || config >= sgemm::kNumMfmaConfigs || group_m < 1 || group_m > 64 || splits < 1 ||
-        splits > 64)
+        splits > 64 || (splits > 1 && !sgemm::mfma_config_splits_ok(config)))
         return SGEMM_F32_ERR_CONFIG;
     const int bad = validate(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (bad) return bad;
@@ -279,6 +279,7 @@ const char *sgemm_f32_config_name(int config) {
         case 2: return "128x64";
         case 3: return "64x128";
         case 4: return "64x64_pf2";
+        case 5: return "128x128_streamk";
         default: return nullptr;
     }
 }

@@ -38,6 +38,8 @@
 // the work-group, so no barrier sits under divergent control flow.
 //
 // Epilogue.  C = alpha * acc + beta * C, where C is read only when beta != 0.
+#include <atomic>
+
 #include "gemm_internal.hpp"
 
 namespace sgemm {
@@ -437,32 +439,21 @@ struct SplitK {
     float *ws;
 };
 
-// At least two waves per SIMD: with one wave per SIMD the matrix core idles
-// whenever that wave waits at a barrier or on memory.
-template <class T, bool VEC>
-__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
-    GemmArgs g, int tiles_m, int tiles_n, int group_m, SplitK sk) {
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+// Operands moved to the K range [kb, kb + klen) of the product.
+template <class T>
+__device__ __forceinline__ void shift_k(GemmArgs &g, int kb, int klen) {
+    g.A += T::PA::L == kKMajor ? (int64_t)kb : (int64_t)kb * g.lda;
+    g.B += T::PB::L == kXMajor ? (int64_t)kb * g.ldb : (int64_t)kb;
+    g.K = klen;
+}
 
-    int bid = blockIdx.x;
-    if (sk.splits > 1) {
-        // Work-groups [s*tiles, (s+1)*tiles) compute split s: the same
-        // product on a K range, with its operands' origins moved along k.
-        const int tiles = tiles_m * tiles_n;
-        const int sp = bid / tiles;
-        bid -= sp * tiles;
-        const int kb = sp * sk.k_per;
-        g.A += T::PA::L == kKMajor ? (int64_t)kb : (int64_t)kb * g.lda;
-        g.B += T::PB::L == kXMajor ? (int64_t)kb * g.ldb : (int64_t)kb;
-        g.K = min(sk.k_per, g.K - kb);
-        g.C = sk.ws + (int64_t)sp * g.M * g.N;
-        g.ldc = g.N;
-        g.alpha = 1.f;
-        g.beta = 0.f;
-    }
-    int tm, tn;
-    tile_of_block(bid, tiles_m, tiles_n, group_m, tm, tn);
-    const int m0 = tm * T::BM, n0 = tn * T::BN;
+// One output tile at (m0, n0) over g's K range: Cb = alpha * acc + beta * Cb,
+// where Cb points at the tile's first element with row stride ldc (C itself,
+// or a partial-sum slot).  Elements outside M x N are neither read nor
+// written.
+template <class T, bool VEC>
+__device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, float *smem, float *Cb,
+                                             int64_t ldc, float alpha, float beta) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -487,19 +478,19 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     // cannot tell their addresses apart), one memory round trip per element.
     const int h = lane >> 5;
     const int l32 = lane & 31;
-    const float alpha = g.alpha, beta = g.beta;
+    const int rows = g.M - m0, cols = g.N - n0;
     float cv[T::MB][T::NB][16];
     if (beta != 0.f) {
 #pragma unroll
         for (int ib = 0; ib < T::MB; ++ib)
 #pragma unroll
             for (int jb = 0; jb < T::NB; ++jb) {
-                const int col = n0 + wn * T::WN + jb * 32 + l32;
+                const int c = wn * T::WN + jb * 32 + l32;
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool ok = !edge_mn || (row < g.M && col < g.N);
-                    cv[ib][jb][r] = ok ? g.C[(int64_t)row * g.ldc + col] : 0.f;
+                    const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const bool ok = !edge_mn || (rr < rows && c < cols);
+                    cv[ib][jb][r] = ok ? Cb[(int64_t)rr * ldc + c] : 0.f;
                 }
             }
     }
@@ -507,16 +498,156 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
     for (int ib = 0; ib < T::MB; ++ib)
 #pragma unroll
         for (int jb = 0; jb < T::NB; ++jb) {
-            const int col = n0 + wn * T::WN + jb * 32 + l32;
+            const int c = wn * T::WN + jb * 32 + l32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (edge_mn && (row >= g.M || col >= g.N)) continue;
+                const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (edge_mn && (rr >= rows || c >= cols)) continue;
                 float v = alpha * acc[ib][jb][r];
                 if (beta != 0.f) v = fmaf(beta, cv[ib][jb][r], v);
-                g.C[(int64_t)row * g.ldc + col] = v;
+                Cb[(int64_t)rr * ldc + c] = v;
             }
         }
+}
+
+// At least two waves per SIMD: with one wave per SIMD the matrix core idles
+// whenever that wave waits at a barrier or on memory.
+// `ntiles`: the launch covers tiles [0, ntiles) of the grouped tile order (all
+// of them, or the whole rounds ahead of a stream-K part).
+template <class T, bool VEC>
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
+    GemmArgs g, int tiles_m, int tiles_n, int group_m, int ntiles, SplitK sk) {
+    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+
+    int bid = blockIdx.x;
+    float *Cbase = g.C;
+    int64_t ldc = g.ldc;
+    float alpha = g.alpha, beta = g.beta;
+    if (sk.splits > 1) {
+        // Work-groups [s*ntiles, (s+1)*ntiles) compute split s: the same
+        // product on a K range, written unscaled to the split's partial slab.
+        const int sp = bid / ntiles;
+        bid -= sp * ntiles;
+        const int kb = sp * sk.k_per;
+        shift_k<T>(g, kb, min(sk.k_per, g.K - kb));
+        Cbase = sk.ws + (int64_t)sp * g.M * g.N;
+        ldc = g.N;
+        alpha = 1.f;
+        beta = 0.f;
+    }
+    int tm, tn;
+    tile_coords(xcd_position(bid, ntiles), tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * T::BM, n0 = tn * T::BN;
+    compute_tile<T, VEC>(g, m0, n0, smem, Cbase + (int64_t)m0 * ldc + n0, ldc, alpha, beta);
+}
+
+// ---------------------------------------------------------------------------
+// Persistent, tile-scheduled form (data-parallel rounds plus stream-K).
+//
+// With T tiles and P resident work-groups, whole rounds of P tiles leave a
+// last round only partly filled ("Writing a Fast Matmul in CUDA, Step by
+// Step", section "Size effects": a second wave that runs a third full).  Here
+// Whole rounds of P tiles run first as an ordinary grid (floor(T/P) rounds,
+// one fewer when T/P leaves a remainder).  Then P work-groups stay resident
+// and each takes an equal share of the remaining tiles' K slices ("units", ipt
+// per tile), a contiguous range that may begin or end inside a tile.  A tile computed whole writes C; a piece of a tile writes its
+// unscaled partial sum to one of two slots of its work-group (slot 0: the
+// piece that starts the work-group's range inside a tile begun by an earlier
+// work-group; slot 1: the piece that ends the range inside a tile continued by
+// a later one), and streamk_fixup_kernel adds each split tile's pieces in K
+// order.  No work-group ever waits for another.
+// ---------------------------------------------------------------------------
+struct StreamK {
+    int P;              // resident work-groups (a multiple of 8)
+    int rounds;         // whole-tile rounds (run by the grid kernel first)
+    int ipt;            // K slices per tile
+    int rem_begin;      // first tile of the stream-K part
+    int64_t units;      // K slices of the stream-K part: (tiles - rounds*P) * ipt
+    float *ws;          // 2 * P slots of BM*BN floats
+};
+
+// Work-group w's units of the stream-K part: [unit_begin(w), unit_begin(w+1)).
+__host__ __device__ __forceinline__ int64_t unit_begin(const StreamK &sk, int w) {
+    return (int64_t)w * sk.units / sk.P;
+}
+// The work-group whose range holds unit u.
+__host__ __device__ __forceinline__ int owner_of_unit(const StreamK &sk, int64_t u) {
+    return (int)(((u + 1) * sk.P - 1) / sk.units);
+}
+
+template <class T, bool VEC>
+__global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_streamk_kernel(
+    GemmArgs g, int tiles_m, int tiles_n, int group_m, StreamK sk) {
+    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+    // Work-groups resident on one XCD take consecutive positions, so they
+    // work on neighbouring tiles and share their panels in that XCD's L2.
+    const int w = xcd_position(blockIdx.x, sk.P);
+    const int64_t u1 = unit_begin(sk, w + 1);
+    for (int64_t u = unit_begin(sk, w); u < u1;) {
+        const int rt = (int)(u / sk.ipt);
+        const int j0 = (int)(u - (int64_t)rt * sk.ipt);
+        const int j1 = (int)min((int64_t)sk.ipt, j0 + (u1 - u));
+        const int t = sk.rem_begin + rt;
+        u += j1 - j0;
+        int tm, tn;
+        tile_coords(t, tiles_m, tiles_n, group_m, tm, tn);
+        const int m0 = tm * T::BM, n0 = tn * T::BN;
+        GemmArgs gs = g;
+        const int kb = j0 * T::BK;
+        shift_k<T>(gs, kb, min(g.K, j1 * T::BK) - kb);
+        const bool whole = j0 == 0 && j1 == sk.ipt;
+        float *Cb = whole ? g.C + (int64_t)m0 * g.ldc + n0
+                          : sk.ws + (int64_t)(2 * w + (j0 > 0 ? 0 : 1)) * (T::BM * T::BN);
+        compute_tile<T, VEC>(gs, m0, n0, smem, Cb, whole ? g.ldc : (int64_t)T::BN, whole ? g.alpha : 1.f,
+                             whole ? g.beta : 0.f);
+        __syncthreads();
+    }
+}
+
+// One work-group per boundary between work-groups w-1 and w of the stream-K
+// part that falls inside a tile; only the first such boundary of a tile does
+// the work: C = alpha * (pieces in K order) + beta * C over the tile.
+template <int BM, int BN>
+__global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m,
+                                                            StreamK sk) {
+    const int w = blockIdx.x + 1;
+    const int64_t b = unit_begin(sk, w);
+    if (b >= sk.units || b % sk.ipt == 0) return;
+    const int64_t first = b / sk.ipt * sk.ipt;
+    if (unit_begin(sk, w - 1) > first) return;
+    const int wf = w - 1;
+    const int wl = owner_of_unit(sk, first + sk.ipt - 1);
+    int tm, tn;
+    tile_coords(sk.rem_begin + (int)(b / sk.ipt), tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int rows = min(BM, g.M - m0), cols = min(BN, g.N - n0);
+    constexpr int SLOT = BM * BN;
+    static_assert(BN % 4 == 0, "groups of 4 columns");
+    // Each thread adds groups of 4 columns (16-byte reads of the slots).
+    for (int e = 4 * threadIdx.x; e < SLOT; e += 4 * 256) {
+        const int r = e / BN, c = e % BN;
+        if (r >= rows || c >= cols) continue;
+        float4 s = *reinterpret_cast<const float4 *>(sk.ws + (int64_t)(2 * wf + 1) * SLOT + e);
+        // Work-groups with an empty range (fewer units than work-groups) hold
+        // no piece.
+        for (int v = wf + 1; v <= wl; ++v) {
+            if (unit_begin(sk, v) == unit_begin(sk, v + 1)) continue;
+            const float4 x = *reinterpret_cast<const float4 *>(sk.ws + (int64_t)(2 * v) * SLOT + e);
+            s.x += x.x;
+            s.y += x.y;
+            s.z += x.z;
+            s.w += x.w;
+        }
+        const float sv[4] = {s.x, s.y, s.z, s.w};
+        float *p = g.C + (int64_t)(m0 + r) * g.ldc + n0 + c;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (c + q >= cols) break;
+            float out = g.alpha * sv[q];
+            if (g.beta != 0.f) out = fmaf(g.beta, p[q], out);
+            p[q] = out;
+        }
+    }
 }
 
 // C = alpha * (the split partials added in split order) + beta * C.  VEC4: N,
@@ -577,8 +708,8 @@ using WideTile = MfmaTile<64, 128, 32, 32, 64, 2, LA, LB>;
 template <int LA, int LB>
 using SmallTile2 = MfmaTile<64, 64, 32, 32, 32, 2, LA, LB>;
 
-constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64};
-constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64};
+constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128};
+constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128};
 constexpr int kTileBK = 32;
 
 template <class T, bool VEC>
@@ -586,7 +717,75 @@ hipError_t launch_one(const GemmArgs &g, int group_m, const SplitK &sk, hipStrea
     const int tiles_m = (g.M + T::BM - 1) / T::BM;
     const int tiles_n = (g.N + T::BN - 1) / T::BN;
     const dim3 grid(tiles_m * tiles_n * sk.splits);
-    hipLaunchKernelGGL((sgemm_mfma_kernel<T, VEC>), grid, dim3(T::NT), 0, stream, g, tiles_m, tiles_n, group_m, sk);
+    hipLaunchKernelGGL((sgemm_mfma_kernel<T, VEC>), grid, dim3(T::NT), 0, stream, g, tiles_m, tiles_n, group_m,
+                       tiles_m * tiles_n, sk);
+    return hipGetLastError();
+}
+
+// Work-groups of the persistent kernel that fit on the device at once (a
+// multiple of 8, one share per XCD), cached per device.
+template <class T>
+hipError_t resident_groups(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sgemm_mfma_streamk_kernel<T, true>, T::NT, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    int P = per_cu * cus / kNumXcd * kNumXcd;
+    if (P < kNumXcd) P = kNumXcd;
+    if (dev >= 0 && dev < 64) cache[dev].store(P, std::memory_order_relaxed);
+    *out = P;
+    return hipSuccess;
+}
+
+template <class T>
+hipError_t launch_streamk(const GemmArgs &g, int group_m, hipStream_t stream) {
+    const int tiles_m = (g.M + T::BM - 1) / T::BM;
+    const int tiles_n = (g.N + T::BN - 1) / T::BN;
+    const int tiles = tiles_m * tiles_n;
+    StreamK sk;
+    hipError_t e = resident_groups<T>(&sk.P);
+    if (e != hipSuccess) return e;
+    sk.ipt = (g.K + T::BK - 1) / T::BK;
+    // With a remainder, the last whole round joins the stream-K part, so each
+    // work-group's share is at least one tile's K slices and a tile is cut at
+    // most once ("data-parallel plus one-tile stream-K").
+    sk.rounds = tiles / sk.P;
+    if (sk.rounds > 0 && tiles % sk.P != 0) sk.rounds -= 1;
+    sk.rem_begin = sk.rounds * sk.P;
+    sk.units = (int64_t)(tiles - sk.rem_begin) * sk.ipt;
+    sk.ws = nullptr;
+    // The whole rounds run as an ordinary grid over their tiles (the grid
+    // kernel keeps fewer registers live than the persistent loop); the
+    // persistent kernel takes the stream-K part only.
+    if (sk.rounds > 0) {
+        SplitK none{1, g.K, nullptr};
+        hipLaunchKernelGGL((sgemm_mfma_kernel<T, true>), dim3(sk.rounds * sk.P), dim3(T::NT), 0, stream, g,
+                           tiles_m, tiles_n, group_m, sk.rounds * sk.P, none);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (sk.units == 0) return hipSuccess;
+    sk.rounds = 0;
+    e = stream_workspace((size_t)2 * sk.P * T::BM * T::BN * sizeof(float), stream, reinterpret_cast<void **>(&sk.ws));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((sgemm_mfma_streamk_kernel<T, true>), dim3(sk.P), dim3(T::NT), 0, stream, g, tiles_m,
+                       tiles_n, group_m, sk);
+    e = hipGetLastError();
+    if (e != hipSuccess || sk.P < 2) return e;
+    hipLaunchKernelGGL((streamk_fixup_kernel<T::BM, T::BN>), dim3(sk.P - 1), dim3(256), 0, stream, g, tiles_m,
+                       tiles_n, group_m, sk);
     return hipGetLastError();
 }
 
@@ -603,6 +802,7 @@ hipError_t launch_layouts(const GemmArgs &g, int config, bool vec, int group_m, 
         case 2: return launch_one<TallTile<LA, LB>, true>(g, group_m, sk, stream);
         case 3: return launch_one<WideTile<LA, LB>, true>(g, group_m, sk, stream);
         case 4: return launch_one<SmallTile2<LA, LB>, true>(g, group_m, sk, stream);
+        case 5: return launch_streamk<LargeTile<LA, LB>>(g, group_m, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -627,6 +827,7 @@ int64_t mfma_large_grid(int M, int N) { return mfma_config_tiles(0, M, N); }
 int64_t mfma_small_grid(int M, int N) { return mfma_config_tiles(1, M, N); }
 
 bool mfma_config_scalar_ok(int config) { return config == 0 || config == 1; }
+bool mfma_config_splits_ok(int config) { return config != 5; }
 
 int mfma_effective_splits(int K, int splits, int *k_per) {
     if (splits < 1) splits = 1;

@@ -52,8 +52,8 @@ def default_plan(M, N):
 
 
 def tiles_of(config, M, N):
-    bm = {0: 128, 1: 64, 2: 128, 3: 64, 4: 64}[config]
-    bn = {0: 128, 1: 64, 2: 64, 3: 128, 4: 64}[config]
+    bm = {0: 128, 1: 64, 2: 128, 3: 64, 4: 64, 5: 128}[config]
+    bn = {0: 128, 1: 64, 2: 64, 3: 128, 4: 64, 5: 128}[config]
     return -(-M // bm) * -(-N // bn)
 
 
@@ -65,9 +65,11 @@ def effective_splits(K, s):
 
 def candidates(M, N, K):
     out = []
-    for cfg in range(5):
+    for cfg in range(6):
         tiles = tiles_of(cfg, M, N)
         for s in SPLITS:
+            if cfg == 5 and s > 1:
+                continue     # the persistent configuration takes no split
             if s > 1:
                 es = effective_splits(K, s)
                 # Split only where the grid is short of work-groups and each

@@ -98,7 +98,8 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_128x64 = 2,     /* 16-byte loads only */
     SGEMM_F32_CFG_64x128 = 3,     /* 16-byte loads only */
     SGEMM_F32_CFG_64x64_PF2 = 4,  /* 64x64, two slices in flight; 16-byte loads only */
-    SGEMM_F32_NUM_CONFIGS = 5
+    SGEMM_F32_CFG_128x128_STREAMK = 5, /* 128x128, persistent with stream-K; 16-byte loads only */
+    SGEMM_F32_NUM_CONFIGS = 6
 };
 
 /*
@@ -195,9 +196,18 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  *
  * sgemm_f32_ex_config: runs one MFMA configuration with the given grouping
  * (1..64 tile rows) and requested split count (1..64; K is cut into extents
- * that are multiples of 32, so fewer splits may run).  Configurations 2-4 need
+ * that are multiples of 32, so fewer splits may run).  Configurations 2-5 need
  * the 16-byte-load conditions of SGEMM_F32_MFMA_LARGE and return
  * SGEMM_F32_ERR_NOT_APPLICABLE otherwise; 0 and 1 fall back to 4-byte loads.
+ *
+ * Configuration 5 is persistent and tile-scheduled: as many work-groups as fit
+ * on the device at once take whole tiles in rounds, then equal shares of the
+ * K slices of the tiles left over, so the last round is not left partly idle
+ * (wave quantization, "Writing a Fast Matmul in CUDA, Step by Step", section
+ * "Size effects"); tiles shared by several work-groups are summed in K order
+ * by a second kernel.  It takes no split count (splits must be 1) and uses
+ * the stream's workspace (2 * 128 * 128 floats per resident work-group, 64 MiB
+ * on MI355X) when tiles are shared.
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -177,3 +177,85 @@ def test_automatic_plan(sg, shape):
     rows, cols = sample_positions(M, N, 3000, seed=M + N + K)
     ok, info = check_sampled(C, A, B, 1.5, -0.5, C0, rows, cols)
     assert ok, info
+
+
+# ---------------------------------------------------------------------------
+# Persistent stream-K configuration (5): whole-tile rounds, then K-slice
+# shares; shapes with fewer tiles than resident work-groups (most work-groups
+# idle, tiles shared by several), with whole rounds plus a remainder, and with
+# a K tail inside shared tiles.
+# ---------------------------------------------------------------------------
+SK_SMALL = [(129, 127, 65), (300, 260, 700), (64, 64, 32), (1000, 900, 96), (257, 4000, 1000),
+            (640, 640, 4099)]
+SK_LARGE = [(3000, 3000, 700), (4092, 2900, 333), (2900, 4100, 64)]
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SK_SMALL, ids=[f"{m}x{n}x{k}" for m, n, k in SK_SMALL])
+def test_streamk_real(sg, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[streamk_real] {form} {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 1100 + M + N + K)
+    st, C, As, Bs = run_cfg(sg, 5, 8, 1, ta, tb, A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 1.25, -0.5, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SK_SMALL + SK_LARGE, ids=[f"{m}x{n}x{k}" for m, n, k in SK_SMALL + SK_LARGE])
+def test_streamk_integer_bitexact(sg, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[streamk_int] {form} {shape}")
+    A, B, C0 = _inputs(M, N, K, "int4", 1200 + M + N + K)
+    st, C, As, Bs = run_cfg(sg, 5, 8, 1, ta, tb, A, B, C0, 1.0, 2.0)
+    assert st == 0
+    if M * N * K <= 3e8:
+        ok, info = check(C, As, Bs, ta, tb, 1.0, 2.0, C0, exact=True)
+    else:
+        rows, cols = sample_positions(M, N, 3000, seed=M + K)
+        vals, _ = oracle.sgemm_ref_op_entries(As, Bs, rows, cols, ta, tb, 1.0, 2.0, C0)
+        ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    assert ok, info
+
+
+@pytest.mark.parametrize("shape", SK_LARGE, ids=[f"{m}x{n}x{k}" for m, n, k in SK_LARGE])
+def test_streamk_real_sampled(sg, shape):
+    M, N, K = shape
+    say(f"[streamk_real_sampled] {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 1300 + M + N + K)
+    st, C, As, Bs = run_cfg(sg, 5, 8, 1, 0, 0, A, B, C0, 1.5, -0.5)
+    assert st == 0
+    rows, cols = sample_positions(M, N, 4000, seed=M + N)
+    ok, info = check_sampled(C, A, B, 1.5, -0.5, C0, rows, cols)
+    assert ok, info
+
+
+def test_streamk_wide_workload_sampled(sg):
+    """The 4096 x 11008 x 512 workload (2752 tiles: five whole rounds and a
+    partial one on 512 resident work-groups) through the persistent kernel."""
+    w = workloads.WORKLOADS["wide4096x11008x512"]
+    say("[streamk_wide]")
+    A, B, C0 = workloads.make_inputs(w)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    dC = torch.full((w.M, w.N), float("nan"), device="cuda:0")
+    st = sg.sgemm_f32_ex_config(5, 8, 1, 0, 0, w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.K, dB.data_ptr(), w.N,
+                                w.beta, dC.data_ptr(), w.N, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    C = dC.cpu().numpy()
+    assert np.all(np.isfinite(C))
+    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
+    ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols)
+    assert ok, info
+
+
+def test_streamk_repeat_bitwise_identical(sg):
+    M, N, K = 3000, 3000, 700
+    A, B, C0 = _inputs(M, N, K, "uniform", 37)
+    r1 = run_cfg(sg, 5, 8, 1, 0, 0, A, B, C0, 1.0, 0.5)
+    r2 = run_cfg(sg, 5, 8, 1, 0, 0, A, B, C0, 1.0, 0.5)
+    assert r1[0] == 0 and r2[0] == 0
+    assert np.array_equal(r1[1].view(np.uint32), r2[1].view(np.uint32))

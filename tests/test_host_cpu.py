@@ -132,7 +132,7 @@ def test_variant_names_and_version(sg):
     assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar", "mfma_tuned"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
-    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2"]
+    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -147,8 +147,10 @@ def test_config_and_plan_argument_errors_without_touching_the_gpu(sg):
     assert f(0, 8, 1, 0, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, 0, 2, 0) == 10
     assert f(0, 8, 1, 0, 0, 0, 2, 2, 1.0, 0, 2, 0, 2, 0.0, 0, 2, 0) == 0        # empty output
     # The 16-byte-only configurations refuse misaligned operands before any launch.
-    for cfg in (2, 3, 4):
+    for cfg in (2, 3, 4, 5):
         assert f(cfg, 8, 1, 0, 0, 64, 64, 64, 1.0, p + 4, 64, p, 64, 0.0, p, 64, 0) == sg.ERR_NOT_APPLICABLE
+    # The persistent configuration takes no split count.
+    assert f(5, 8, 2, 0, 0, 64, 64, 64, 1.0, p, 64, p, 64, 0.0, p, 64, 0) == sg.ERR_CONFIG
     # A split plan whose partials exceed 1 GiB is refused before any launch.
     assert f(0, 8, 64, 0, 0, 8192, 8192, 8192, 1.0, p, 8192, p, 8192, 0.0, p, 8192, 0) == sg.ERR_TOO_LARGE
     assert sg.sgemm_f32_ex_plan(2, 0, 4, 4, 4, 1.0, p, 4, p, 4)[0] == sg.ERR_TRANS
