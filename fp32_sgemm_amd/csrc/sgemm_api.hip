@@ -6,6 +6,7 @@
 // kernels ("Learn: Optimizing GEMM", section 8; "Writing a Fast Matmul in CUDA,
 // Step by Step", section "In the real world"); this library picks among its own
 // few kernels by shape and operand alignment, on the host, before one launch.
+#include <cmath>
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -107,21 +108,57 @@ Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const f
     return Plan{config ? SGEMM_F32_MFMA_SMALL : SGEMM_F32_MFMA_LARGE, config, 8, 1};
 }
 
+// Wave quantization of the 128x128 grid.  About kResidentLargeTiles of its
+// work-groups are resident at once (two per compute unit on the 256 compute
+// units of MI355X), so a grid of T tiles runs ceil(T / 512) rounds, the last
+// possibly far from full.  The persistent stream-K configuration removes that
+// idle time at a cost of its own (pipeline restarts and partial tiles written,
+// re-read and added by a second kernel), which weighs less as K, the work per
+// tile, grows.  It takes the plan over when the idle part of the rounds,
+// rounds - load with load = (M/128)(N/128)/512 counting edge tiles by their
+// area, exceeds that cost, modelled as 0.9 * sqrt(1000 / K) rounds plus a
+// margin of 0.05.  The model is fitted to per-launch timings on MI355X
+// (TFLOP/s, grid -> stream-K): 3000^3 98.8 -> 121.1 and 3500^3 101.5 -> 121.9
+// (taken), 5000 x 5000 x 1000 110.1 -> 112.8 (taken), 2900 x 4100 x 2048 128.2
+// -> 118.7, 4096 x 11008 x 512 113.0 -> 111.3 and 6144 x 6144 x 2048 140.4 ->
+// 135.7 (not taken).  The table's classes cannot express it: the idle part
+// depends on the exact extents, not on their octaves.
+constexpr int kResidentLargeTiles = 512;
+
+bool stream_k_pays(int M, int N, int K) {
+    const int64_t tiles = sgemm::mfma_config_tiles(0, M, N);
+    if (tiles <= kResidentLargeTiles || K <= 0) return false;
+    const double rounds = (double)((tiles + kResidentLargeTiles - 1) / kResidentLargeTiles);
+    const double load = (M / 128.0) * (N / 128.0) / kResidentLargeTiles;
+    const double cost = 0.9 * std::sqrt(1000.0 / K);
+    return rounds - load > cost + 0.05;
+}
+
+Plan quantization_plan(const Plan &p, int M, int N, int K) {
+    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
+        return p;
+    if (!stream_k_pays(M, N, K)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 5, p.group_m, 1};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
-// shape class when there is one (reported as SGEMM_F32_MFMA_TUNED when it
-// differs from the default).  Transposed operands use the same entries.
+// shape class when there is one, then the stream-K switch for 128x128 grids
+// that fill their last round poorly (reported as SGEMM_F32_MFMA_TUNED when the
+// plan differs from the default).  Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
-    if (!kHaveTunedTable || (d.variant != SGEMM_F32_MFMA_LARGE && d.variant != SGEMM_F32_MFMA_SMALL)) return d;
+    if (d.variant != SGEMM_F32_MFMA_LARGE && d.variant != SGEMM_F32_MFMA_SMALL) return d;
+    if (!kHaveTunedTable) return quantization_plan(d, M, N, K);
     const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
-    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1) return d;
+    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1)
+        return quantization_plan(d, M, N, K);
     int k_per = 0;
     int splits = sgemm::mfma_effective_splits(K, e.splits, &k_per);
     if ((int64_t)splits * M * N * 4 > kMaxSplitBytes) splits = 1;
     Plan p{SGEMM_F32_MFMA_TUNED, e.config, e.group_m, splits};
-    if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) return d;
-    return p;
+    if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) p = d;
+    return quantization_plan(p, M, N, K);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
