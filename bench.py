@@ -114,6 +114,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the 4096^3 headline)")
+    ap.add_argument("--shape", default=None, metavar="MxNxK",
+                    help="time another shape instead (uniform[-1,1) inputs, alpha 1, beta 0)")
     ap.add_argument("--variant", default="auto",
                     help="auto | mfma_large | mfma_small | valu | skinny | mfma_scalar")
     ap.add_argument("--operands", default="nn", choices=["nn", "nt", "tn", "tt"],
@@ -161,7 +163,11 @@ def main():
         sys.exit(f"unknown variant {args.variant}")
     variant = names[args.variant]
 
-    w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
+    if args.shape:
+        M, N, K = (int(v) for v in args.shape.lower().split("x"))
+        w = workloads.custom(M, N, K, dist="uniform", seed=99, name=f"shape{M}x{N}x{K}")
+    else:
+        w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     A, B, C0 = workloads.make_inputs(w)
     ta, tb = int(args.operands[0] == "t"), int(args.operands[1] == "t")
     As = np.ascontiguousarray(A.T) if ta else A
@@ -177,6 +183,12 @@ def main():
     chosen = variant if variant else sg.sgemm_f32_ex_select(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
                                                             lda, dB.data_ptr(), ldb)
 
+    plan = None
+    if variant in (0, sg.MFMA_TUNED):
+        st, pv, pc, pg, ps = sg.sgemm_f32_ex_plan(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
+                                                  dB.data_ptr(), ldb)
+        if st == 0 and pv not in (0, sg.SKINNY, sg.VALU):
+            plan = {"config": sg.sgemm_f32_config_name(pc), "group_m": pg, "splits": ps}
     counter = [0]
 
     def step():
@@ -247,7 +259,7 @@ def main():
         "pct_of_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
                    "beta": w.beta, "inputs": w.dist, "operands": args.operands,
-                   "variant": sg.sgemm_f32_variant_name(chosen),
+                   "variant": sg.sgemm_f32_variant_name(chosen), "plan": plan,
                    "b_copies": len(dBs), "parallelism": "single GPU"},
         "roofline": roofline,
     }
