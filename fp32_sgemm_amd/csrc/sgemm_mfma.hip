@@ -546,7 +546,10 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
 //
 // With T tiles and P resident work-groups, whole rounds of P tiles leave a
 // last round only partly filled ("Writing a Fast Matmul in CUDA, Step by
-// Step", section "Size effects": a second wave that runs a third full).  Here
+// Step", section "Size effects": a second wave that runs a third full).  A
+// persistent kernel keeps its work-groups alive across several output tiles
+// ("CUDA Matrix Multiplication Optimization: From Naive to Near-cuBLAS",
+// section "Beyond Tiling: Async, Tensor Cores, and Scheduling").  Here
 // Whole rounds of P tiles run first as an ordinary grid (floor(T/P) rounds,
 // one fewer when T/P leaves a remainder).  Then P work-groups stay resident
 // and each takes an equal share of the remaining tiles' K slices ("units", ipt
