@@ -71,6 +71,8 @@ def _bind(path: str):
     lib.oracle_sgemm_op_f64_entries.argtypes = [i, i, i, i, i, f, p, l, p, l, f,
                                                 p, l, l, p, p, p, p]
     lib.oracle_sgemm_op_f64_entries.restype = i
+    lib.oracle_decode_16.argtypes = [i, p, l, p]
+    lib.oracle_decode_16.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
     return lib
@@ -235,6 +237,39 @@ def sgemm_ref_op_entries(A: np.ndarray, B: np.ndarray, rows, cols,
     return out, absab
 
 
+BF16 = 1
+F16 = 2
+
+
+def decode_16(bits: np.ndarray, kind: int, _lib_override=None) -> np.ndarray:
+    """Values of 16-bit patterns (uint16 array) as float32: kind BF16 or F16."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib = _lib_override or _load()
+    if b.size and lib.oracle_decode_16(int(kind), _ptr(b), b.size, _ptr(out)) != 0:
+        raise ValueError(f"unknown 16-bit kind {kind}")
+    return out
+
+
+def sgemm_ref_lowp(A_bits: np.ndarray, B_bits: np.ndarray, kind: int, trans_a: bool = False,
+                   trans_b: bool = False, alpha: float = 1.0, beta: float = 0.0,
+                   C0: np.ndarray | None = None, _lib_override=None):
+    """``alpha * op(A) * op(B) + beta * C0`` for 16-bit inputs (stored as in
+    ``sgemm_ref_op``), C0 and the result float: the inputs are decoded exactly
+    and multiplied by the float64 oracle.  Returns ``(Cref, absAB)``."""
+    A = decode_16(A_bits, kind, _lib_override)
+    B = decode_16(B_bits, kind, _lib_override)
+    return sgemm_ref_op(A, B, trans_a, trans_b, alpha, beta, C0, _lib_override=_lib_override)
+
+
+def sgemm_ref_lowp_entries(A_bits, B_bits, kind, rows, cols, trans_a=False, trans_b=False,
+                           alpha=1.0, beta=0.0, C0=None, _lib_override=None):
+    A = decode_16(A_bits, kind, _lib_override)
+    B = decode_16(B_bits, kind, _lib_override)
+    return sgemm_ref_op_entries(A, B, rows, cols, trans_a, trans_b, alpha, beta, C0,
+                                _lib_override=_lib_override)
+
+
 def error_bound(absab: np.ndarray, alpha: float, beta: float,
                 c0_vals: np.ndarray | None, rel: float = REL_TOL) -> np.ndarray:
     """Element-wise bound rel * (|alpha|*absAB + |beta|*|C0|) in float64."""
@@ -293,6 +328,14 @@ class BoundOracle:
     def sgemm_ref_entries(self, A, B, rows, cols, alpha=1.0, beta=0.0, C0=None):
         return sgemm_ref_entries(A, B, rows, cols, alpha, beta, C0,
                                  _lib_override=self._lib)
+
+    def decode_16(self, bits, kind):
+        return decode_16(bits, kind, _lib_override=self._lib)
+
+    def sgemm_ref_lowp(self, A_bits, B_bits, kind, trans_a=False, trans_b=False, alpha=1.0,
+                       beta=0.0, C0=None):
+        return sgemm_ref_lowp(A_bits, B_bits, kind, trans_a, trans_b, alpha, beta, C0,
+                              _lib_override=self._lib)
 
     def sgemm_ref_op(self, A, B, trans_a=False, trans_b=False, alpha=1.0, beta=0.0, C0=None):
         return sgemm_ref_op(A, B, trans_a, trans_b, alpha, beta, C0, _lib_override=self._lib)

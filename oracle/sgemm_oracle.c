@@ -224,3 +224,45 @@ int oracle_sgemm_op_f64_entries(int trans_a, int trans_b, int M, int N, int K, f
     }
     return 0;
 }
+
+/*
+ * 16-bit input formats for the lower-precision form of the product (the pages'
+ * endpoint: matrix units that take 16-bit inputs and accumulate in FP32, "CUDA
+ * Matrix Multiplication Optimization: From Naive to Near-cuBLAS", its list of
+ * lessons, which ends on dedicated matrix hardware and 16-bit inputs; "Writing
+ * a Fast Matmul in CUDA, Step by Step", section "Why LLMs use tensor cores
+ * instead").  Decoded here from the field layouts of the formats, value by
+ * value, into float (every value of either format is exactly a float):
+ *
+ *   bfloat16: sign (1 bit), exponent (8, bias 127), fraction (7)
+ *   binary16: sign (1 bit), exponent (5, bias 15),  fraction (10)
+ *
+ * exponent 0 is zero or subnormal (2^(1-bias) * fraction / 2^bits), all ones
+ * is infinity (fraction 0) or NaN.  The product then is the float64 oracle
+ * above on the decoded matrices: the decoded values are exact, so the
+ * reference carries no rounding of the inputs.
+ */
+static float decode_16(unsigned v, int exp_bits, int frac_bits, int bias)
+{
+    const unsigned sign = v >> (exp_bits + frac_bits);
+    const unsigned e = (v >> frac_bits) & ((1u << exp_bits) - 1u);
+    const unsigned f = v & ((1u << frac_bits) - 1u);
+    const double scale = (double)(1u << frac_bits);
+    double x;
+    if (e == (1u << exp_bits) - 1u)
+        x = f ? NAN : INFINITY;
+    else if (e == 0)
+        x = ldexp((double)f / scale, 1 - bias);
+    else
+        x = ldexp(1.0 + (double)f / scale, (int)e - bias);
+    return (float)(sign ? -x : x);
+}
+
+/* kind 1: bfloat16, kind 2: binary16.  Returns 1 for another kind. */
+int oracle_decode_16(int kind, const unsigned short *in, long n, float *out)
+{
+    if (kind != 1 && kind != 2) return 1;
+    for (long t = 0; t < n; ++t)
+        out[t] = kind == 1 ? decode_16(in[t], 8, 7, 127) : decode_16(in[t], 5, 10, 15);
+    return 0;
+}

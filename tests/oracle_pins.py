@@ -18,6 +18,10 @@ What fixes each expected value (none is produced by the code under test):
   * for the transposed-operand form: its own hand-worked fixture, numpy's exact
     int64 matmul of the explicitly transposed integer operands, the float64
     library matmul, and (op(A) op(B))^T = op(B)^T op(A)^T;
+  * for the 16-bit inputs: values of hand-decoded bit patterns of both formats,
+    numpy's own binary16 conversion for all 65536 patterns, the bfloat16 rule
+    "upper half of a binary32" for all 65536 patterns, and exact integer
+    products of 16-bit integer-valued inputs;
   * the standard deviation sqrt(K/9) of a dot product of uniform[-1,1) vectors,
     which gives the "typical size 21" of entries at n = 4096 that "Writing a
     Fast Matmul in CUDA, Step by Step" reports in its "Step 1" section.
@@ -316,8 +320,66 @@ def pin_op_entries_match(o):
         assert np.array_equal(_bits(av), _bits(absab[r, c])), ("entry magnitudes", ta, tb)
 
 
+# (pattern, value) pairs decoded by hand from the field layouts.
+_BF16_HAND = [(0x0000, 0.0), (0x3F80, 1.0), (0xC000, -2.0), (0x3E80, 0.25), (0x4049, 3.140625),
+              (0x0080, 2.0 ** -126), (0x0001, 2.0 ** -133), (0x7F7F, (2 - 2.0 ** -7) * 2.0 ** 127),
+              (0x7F80, np.inf), (0xFF80, -np.inf), (0x4300, 128.0), (0xC2C8, -100.0)]
+_F16_HAND = [(0x0000, 0.0), (0x3C00, 1.0), (0xC000, -2.0), (0x3555, 1365 / 4096), (0x7BFF, 65504.0),
+             (0x0400, 2.0 ** -14), (0x0001, 2.0 ** -24), (0x7C00, np.inf), (0xFC00, -np.inf),
+             (0x5640, 100.0), (0xD800, -128.0), (0x3800, 0.5)]
+
+
+def pin_decode_hand(o):
+    for kind, table in ((1, _BF16_HAND), (2, _F16_HAND)):
+        bits = np.array([b for b, _ in table], np.uint16)
+        got = o.decode_16(bits, kind).astype(np.float64)
+        want = np.array([v for _, v in table], np.float64)
+        assert np.array_equal(got, want), (kind, got, want)
+        nan = o.decode_16(np.array([0x7FC0 if kind == 1 else 0x7E00], np.uint16), kind)
+        assert np.isnan(nan[0])
+    neg0 = o.decode_16(np.array([0x8000], np.uint16), 1)
+    assert neg0[0] == 0 and np.signbit(neg0[0])
+
+
+def pin_decode_all_patterns(o):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    f16 = o.decode_16(bits, 2)
+    ref = bits.view(np.float16).astype(np.float32)              # numpy's binary16
+    same = (f16 == ref) | (np.isnan(f16) & np.isnan(ref))
+    assert same.all() and np.array_equal(np.signbit(f16), np.signbit(ref)), "binary16 decode"
+    bf = o.decode_16(bits, 1)
+    ref = (bits.astype(np.uint32) << 16).view(np.float32)      # upper half of a binary32
+    same = (bf == ref) | (np.isnan(bf) & np.isnan(ref))
+    assert same.all() and np.array_equal(np.signbit(bf), np.signbit(ref)), "bfloat16 decode"
+
+
+def _to16(x, kind):
+    """Integer-valued float32 -> 16-bit patterns (exact for the small integers used)."""
+    x = np.asarray(x, np.float32)
+    if kind == 2:
+        return x.astype(np.float16).view(np.uint16)
+    return (x.view(np.uint32) >> 16).astype(np.uint16)
+
+
+def pin_lowp_integer_exact(o):
+    rng = _rng(31)
+    M, N, K = 9, 7, 40
+    Ai = rng.integers(-8, 9, size=(M, K))
+    Bi = rng.integers(-8, 9, size=(K, N))
+    C0 = rng.integers(-5, 6, size=(M, N)).astype(np.float32)
+    want = (2 * (Ai @ Bi) - 3 * C0.astype(np.int64)).astype(np.float64)
+    for kind in (1, 2):
+        for ta, tb in _FORMS:
+            A = _stored(_to16(Ai, kind).reshape(M, K), ta)
+            B = _stored(_to16(Bi, kind).reshape(K, N), tb)
+            Cref, absab = o.sgemm_ref_lowp(A, B, kind, ta, tb, 2.0, -3.0, C0)
+            assert np.array_equal(Cref, want), ("lowp integer", kind, ta, tb)
+            assert np.array_equal(absab, (np.abs(Ai) @ np.abs(Bi)).astype(np.float64))
+
+
 PINS = [pin_golden, pin_identity, pin_permutation, pin_transpose, pin_exact_rational,
         pin_integer_exact, pin_rank_one, pin_all_ones, pin_scalar_special_cases,
         pin_library_matmul, pin_leading_dims, pin_entries_match,
         pin_uniform_statistics, pin_op_golden, pin_op_integer_exact,
-        pin_op_library_matmul, pin_op_transpose_identity, pin_op_entries_match]
+        pin_op_library_matmul, pin_op_transpose_identity, pin_op_entries_match,
+        pin_decode_hand, pin_decode_all_patterns, pin_lowp_integer_exact]

@@ -40,6 +40,12 @@ MUTATIONS = {
                                  "op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);\n"
                                  "        const double prod = use_product ? (double)alpha * acc : 0.0;\n"
                                  "        const double old = 0.0;")],
+    "bf16_bias_126": [("decode_16(in[t], 8, 7, 127)", "decode_16(in[t], 8, 7, 126)")],
+    "f16_no_subnormals": [("x = ldexp((double)f / scale, 1 - bias);", "x = 0.0;")],
+    "subnormal_exponent_off_by_one": [("x = ldexp((double)f / scale, 1 - bias);", "x = ldexp((double)f / scale, -bias);")],
+    "implicit_one_dropped": [("x = ldexp(1.0 + (double)f / scale, (int)e - bias);", "x = ldexp((double)f / scale, (int)e - bias);")],
+    "sign_ignored": [("return (float)(sign ? -x : x);", "return (float)x;")],
+    "f16_fraction_bits_9": [("decode_16(in[t], 5, 10, 15)", "decode_16(in[t], 5, 9, 15)")],
     "row_stride_of_A_is_K": [("const double a = (double)A[(long)i * lda + k];",
                               "const double a = (double)A[(long)i * K + k];")],
 }

@@ -99,3 +99,23 @@ def custom(M: int, N: int, K: int, dist: str = "uniform", seed: int = 7,
     """A workload of any shape (parity cases: ragged tails, tiny sizes)."""
     return Workload(name or f"custom{M}x{N}x{K}", M, N, K, dist, alpha, beta,
                     seed, c0_dist)
+
+
+BF16 = 1
+F16 = 2
+
+
+def to_16bit(x: np.ndarray, kind: int) -> np.ndarray:
+    """Stores float32 values in a 16-bit input format (kind 1 bfloat16, kind 2
+    binary16), rounding to nearest even, as a uint16 array of bit patterns.
+    Input preparation only: the conversion is torch's own."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    dt = torch.bfloat16 if kind == BF16 else torch.float16
+    return t.to(dt).view(torch.int16).numpy().view(np.uint16)
+
+
+def make_inputs_16bit(w: Workload, kind: int):
+    """(A bits, B bits, C0) for the 16-bit-input form of a workload: the same
+    draws as ``make_inputs``, A and B stored in the 16-bit format, C0 float32."""
+    A, B, C0 = make_inputs(w)
+    return to_16bit(A, kind), to_16bit(B, kind), C0
