@@ -32,6 +32,8 @@ if ROOT not in sys.path:
 
 METRIC = "FP32 SGEMM TFLOP/s at 4096^3 on 1 MI355X; % of FP32 peak"
 PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector and matrix), datasheet
+PEAK_16BIT_TFLOPS = 2500.0        # MI355X dense BF16 / FP16 matrix, datasheet
+METRIC_16 = "GEMM TFLOP/s with {} inputs and FP32 accumulation at {} on 1 MI355X"
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_mfma.hip", "fp32_sgemm_amd/csrc/gemm_internal.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_large_square4096_ab.txt")
@@ -121,6 +123,9 @@ def main():
     ap.add_argument("--operands", default="nn", choices=["nn", "nt", "tn", "tt"],
                     help="operand forms: t = stored transposed (A as K x M, B as N x K), "
                          "timed through sgemm_f32_ex")
+    ap.add_argument("--inputs16", default=None, choices=["bf16", "f16"],
+                    help="time gemm16_f32 instead: A and B stored in this 16-bit format, "
+                         "FP32 accumulation and C")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -170,11 +175,15 @@ def main():
         w = workloads.WORKLOADS[args.workload or workloads.HEADLINE]
     A, B, C0 = workloads.make_inputs(w)
     ta, tb = int(args.operands[0] == "t"), int(args.operands[1] == "t")
+    kind16 = {"bf16": 1, "f16": 2}.get(args.inputs16)
+    if kind16:
+        A, B = workloads.to_16bit(A, kind16), workloads.to_16bit(B, kind16)
     As = np.ascontiguousarray(A.T) if ta else A
     Bs = np.ascontiguousarray(B.T) if tb else B
     dev = torch.device("cuda:0")
-    dA = torch.from_numpy(As).to(dev)
-    dBs = [torch.from_numpy(Bs).to(dev) for _ in range(max(1, args.rotate))]
+    to_dev = (lambda x: torch.from_numpy(x.view(np.int16)).to(dev)) if kind16 else (lambda x: torch.from_numpy(x).to(dev))
+    dA = to_dev(As)
+    dBs = [to_dev(Bs) for _ in range(max(1, args.rotate))]
     dB = dBs[0]
     dC = torch.from_numpy(C0).to(dev) if C0 is not None else torch.empty(w.M, w.N, device=dev)
     lda, ldb, ldc = As.shape[1], Bs.shape[1], w.N
@@ -194,7 +203,10 @@ def main():
     def step():
         b = dBs[counter[0] % len(dBs)]
         counter[0] += 1
-        if ta or tb:
+        if kind16:
+            st = sg.gemm16_f32(kind16, ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, b.data_ptr(), ldb,
+                               w.beta, dC.data_ptr(), ldc, s_handle)
+        elif ta or tb:
             st = sg.sgemm_f32_ex_variant(variant, ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
                                          b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
         else:
@@ -228,8 +240,12 @@ def main():
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
     achieved = flops / kern_avg_s / 1e12
 
-    memory_bound = arithmetic_intensity(w.M, w.N, w.K, w.beta != 0) < PEAK_FP32_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
-    if memory_bound:
+    peak = PEAK_16BIT_TFLOPS if kind16 else PEAK_FP32_TFLOPS
+    memory_bound = arithmetic_intensity(w.M, w.N, w.K, w.beta != 0) < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if kind16 and not memory_bound:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4)}
+    elif memory_bound:
         ach_gbs = gemm_min_bytes(w.M, w.N, w.K, w.beta != 0) / kern_avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach_gbs, 2), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4)}
@@ -239,12 +255,17 @@ def main():
         bound = "alu" if chosen == sg.VALU else "mfma"
         roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4)}
-    headline_kernel = w.name == workloads.HEADLINE and chosen == 1 and not (ta or tb)
+    headline_kernel = w.name == workloads.HEADLINE and chosen == 1 and not (ta or tb) and not kind16
     roofline["traffic"] = measured_traffic() if headline_kernel else None
     roofline["kernel_avg_ms"] = round(kern_avg_s * 1e3, 5)
 
+    if kind16:
+        chosen_name = "gemm16_" + args.inputs16
+        plan = None
+    else:
+        chosen_name = sg.sgemm_f32_variant_name(chosen)
     out = {
-        "metric": METRIC,
+        "metric": METRIC_16.format(args.inputs16, f"{w.M}x{w.N}x{w.K}") if kind16 else METRIC,
         "value": round(value, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -254,16 +275,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": args.inputs16 + " in, f32 accumulate" if kind16 else "f32",
         "data": "synthetic",
-        "pct_of_fp32_peak": round(100 * value / PEAK_FP32_TFLOPS, 2),
+        "pct_of_fp32_peak": None if kind16 else round(100 * value / PEAK_FP32_TFLOPS, 2),
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "alpha": w.alpha,
                    "beta": w.beta, "inputs": w.dist, "operands": args.operands,
-                   "variant": sg.sgemm_f32_variant_name(chosen), "plan": plan,
+                   "variant": chosen_name, "plan": plan,
                    "b_copies": len(dBs), "parallelism": "single GPU"},
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not kind16:
         out["cpu_baseline"] = cpu_baseline(A, B, C0, w.alpha, w.beta, args.cpu_seconds)
     print(json.dumps(out), flush=True)
 

@@ -42,10 +42,16 @@ ERR_TOO_LARGE = 22
 ERR_TRANS = 23
 ERR_CONFIG = 24
 
+GEMM16_BF16 = 1
+GEMM16_F16 = 2
+GEMM16_ERR_ALIGN = 21
+GEMM16_ERR_TYPE = 25
+
 EXPORTED = ("sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select",
             "sgemm_f32_ex", "sgemm_f32_ex_variant", "sgemm_f32_ex_select",
             "sgemm_f32_ex_plan", "sgemm_f32_ex_config", "sgemm_f32_config_name",
-            "sgemm_f32_tuning_table_present", "sgemm_f32_variant_name", "sgemm_f32_version")
+            "sgemm_f32_tuning_table_present", "sgemm_f32_variant_name", "sgemm_f32_version",
+            "gemm16_f32")
 
 
 class SgemmError(RuntimeError):
@@ -83,6 +89,8 @@ def _load_library():
     lib.sgemm_f32_config_name.restype = ctypes.c_char_p
     lib.sgemm_f32_tuning_table_present.argtypes = []
     lib.sgemm_f32_tuning_table_present.restype = i
+    lib.gemm16_f32.argtypes = [i, i, i] + gemm_args
+    lib.gemm16_f32.restype = i
     lib.sgemm_f32_variant_name.argtypes = [i]
     lib.sgemm_f32_variant_name.restype = ctypes.c_char_p
     lib.sgemm_f32_version.argtypes = []
@@ -150,6 +158,13 @@ def sgemm_f32_config_name(config: int) -> str | None:
 
 def sgemm_f32_tuning_table_present() -> int:
     return _lib.sgemm_f32_tuning_table_present()
+
+
+def gemm16_f32(in_type: int, trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int,
+               lda: int, B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    """C (float) = alpha*op(A)*op(B) + beta*C with A, B of 16-bit values
+    (GEMM16_BF16 or GEMM16_F16 bit patterns), FP32 accumulation."""
+    return _lib.gemm16_f32(in_type, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_variant_name(variant: int) -> str | None:

@@ -1,0 +1,344 @@
+// GEMM with 16-bit inputs (bfloat16 or binary16) on the CDNA4 matrix cores,
+// FP32 accumulation and FP32 output: C = alpha * op(A) * op(B) + beta * C.
+//
+// This is the end point the pages point to once FP32 tiling is exhausted:
+// matrix units that take 16-bit inputs and accumulate in FP32, keeping the
+// same block tiles, shared-memory staging and pipelining ("Writing a Fast
+// Matmul in CUDA, Step by Step", section "Why LLMs use tensor cores instead").
+// On gfx950 one v_mfma_f32_32x32x16_{bf16,f16} multiplies a 32x16 by a 16x32
+// block: lane l supplies A(l % 32, 8*(l/32) + i) and B(8*(l/32) + i, l % 32)
+// for i < 8, eight consecutive k in one 16-byte register group, and returns
+// the 32x32 accumulator block in the same layout as the FP32 instruction.
+//
+// Layout.  The kernel reads both operands as rows of k ("K-major"): A as
+// given (M x K) and B given transposed (N x K, the form of a weight matrix
+// stored as [out][in]).  Then a lane's eight k are 16 contiguous bytes in
+// memory and in LDS, and every fragment is one ds_read_b128.  Other operand
+// forms, operands that are not 16-byte aligned, and K not a multiple of the
+// 64-deep slice are first packed by pack16_kernel into a K-major copy with K
+// padded by zeros (adding exact zeros changes no sum), in the stream's
+// workspace.
+//
+// Tiles.  A work-group computes a 128 x 128 tile of C with 4 waves of 64 x 64
+// (2 x 2 blocks of 32 x 32).  Slices of 64 k are staged in LDS, double
+// buffered, with the next slice's global loads in registers during the MFMAs
+// of the current one.  A slice row is 128 bytes (8 chunks of 16 bytes); chunk
+// c of row r is stored at chunk c ^ ((r >> 1) & 7), so the 16-byte reads of
+// eight consecutive rows at one chunk, and the writes of one row's chunks,
+// fall in distinct banks.
+#include <cstdint>
+
+#include "gemm_internal.hpp"
+#include "gemm16_f32.h"
+
+namespace sgemm {
+namespace {
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ i32x4 raw_buffer_load_v4i32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.v4i32");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc16(const uint16_t *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, bytes, 0x00020000);
+}
+
+constexpr int BM = 128, BN = 128, BK = 64;       // BK in elements
+constexpr int NT = 256;
+constexpr int ROW_BYTES = BK * 2;                // 128
+constexpr int CHUNKS = ROW_BYTES / 16;           // 8
+constexpr int A_STAGE = BM * ROW_BYTES;          // bytes
+constexpr int B_STAGE = BN * ROW_BYTES;
+constexpr int STAGE = A_STAGE + B_STAGE;         // 32 KB
+constexpr int LOADS = (BM * CHUNKS) / NT;        // 16-byte groups per thread per operand: 4
+
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
+
+// Operand slice addressing: group j of this thread is row (tid / 8) + 32 j,
+// chunk tid % 8 of the slice.
+struct Loader {
+    int off[LOADS];      // byte offsets from the slice origin
+    int lds[LOADS];      // byte offsets in the operand's stage
+    __device__ __forceinline__ Loader(int64_t ld, int tid) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) {
+            const int r = tid / CHUNKS + (NT / CHUNKS) * j;
+            const int c = tid % CHUNKS;
+            off[j] = (r * (int)ld + c * 8) * 2;
+            lds[j] = r * ROW_BYTES + swz(r, c) * 16;
+        }
+    }
+};
+
+struct Args16 {
+    int M, N, K;            // K: multiple of BK (packed or checked)
+    float alpha, beta;
+    const uint16_t *A;      // M x K, K-major, row stride lda (multiple of 8)
+    const uint16_t *B;      // N x K, K-major, row stride ldb
+    float *C;
+    int64_t lda, ldb, ldc;
+};
+
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma16(i32x4 a, i32x4 b, f32x16 acc) {
+    if (F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      acc, 0, 0, 0);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                   acc, 0, 0, 0);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm16_kernel(Args16 g, int tiles_m,
+                                                                                          int tiles_n) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 8, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const Loader la(g.lda, tid), lb(g.ldb, tid);
+    const int rows_a = min(BM, g.M - m0), rows_b = min(BN, g.N - n0);
+    const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
+    const uint16_t *Bb = g.B + (int64_t)n0 * g.ldb;
+    // Rows past M (N) lie beyond the resource's extent and read as zeros.
+    auto load = [&](int k0, i32x4 (&ra)[LOADS], i32x4 (&rb)[LOADS]) {
+        const __amdgpu_buffer_rsrc_t rsa = rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + BK) * 2));
+        const __amdgpu_buffer_rsrc_t rsb = rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + BK) * 2));
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) ra[j] = raw_buffer_load_v4i32(rsa, la.off[j], 0, 0);
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) rb[j] = raw_buffer_load_v4i32(rsb, lb.off[j], 0, 0);
+    };
+    auto store = [&](unsigned char *st, const i32x4 (&ra)[LOADS], const i32x4 (&rb)[LOADS]) {
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) *reinterpret_cast<i32x4 *>(st + la.lds[j]) = ra[j];
+#pragma unroll
+        for (int j = 0; j < LOADS; ++j) *reinterpret_cast<i32x4 *>(st + A_STAGE + lb.lds[j]) = rb[j];
+    };
+
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragment rows of this lane: A rows wm*64 + 32 ib + l32, B rows wn*64 + 32 jb + l32.
+    int ra_row[2], rb_row[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        ra_row[b] = wm * 64 + 32 * b + l32;
+        rb_row[b] = wn * 64 + 32 * b + l32;
+    }
+    auto compute = [&](const unsigned char *st) {
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            const int c = 2 * s + h;
+            i32x4 fa[2], fb[2];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                fa[b] = *reinterpret_cast<const i32x4 *>(st + ra_row[b] * ROW_BYTES + swz(ra_row[b], c) * 16);
+                fb[b] = *reinterpret_cast<const i32x4 *>(st + A_STAGE + rb_row[b] * ROW_BYTES +
+                                                          swz(rb_row[b], c) * 16);
+            }
+#pragma unroll
+            for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma16<F16>(fa[ib], fb[jb], acc[ib][jb]);
+        }
+    };
+
+    const int nk = g.K / BK;
+    i32x4 ra[LOADS], rb[LOADS];
+    load(0, ra, rb);
+    store(smem, ra, rb);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        const bool more = t + 1 < nk;
+        if (more) load((t + 1) * BK, ra, rb);
+        compute(smem + (t & 1) * STAGE);
+        if (more) store(smem + ((t + 1) & 1) * STAGE, ra, rb);
+        __syncthreads();
+    }
+
+    // Epilogue: C read in a pass of its own before the stores (see the FP32
+    // kernel), elements outside M x N neither read nor written.
+    const bool edge = rows_a < BM || rows_b < BN;
+    const float alpha = g.alpha, beta = g.beta;
+    float cv[2][2][16];
+    if (beta != 0.f) {
+#pragma unroll
+        for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = wm * 64 + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int cc = wn * 64 + 32 * jb + l32;
+                    const bool ok = !edge || (rr < rows_a && cc < rows_b);
+                    cv[ib][jb][r] = ok ? g.C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] : 0.f;
+                }
+    }
+#pragma unroll
+    for (int ib = 0; ib < 2; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = wm * 64 + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int cc = wn * 64 + 32 * jb + l32;
+                if (edge && (rr >= rows_a || cc >= rows_b)) continue;
+                float v = alpha * acc[ib][jb][r];
+                if (beta != 0.f) v = fmaf(beta, cv[ib][jb][r], v);
+                g.C[(int64_t)(m0 + rr) * g.ldc + n0 + cc] = v;
+            }
+}
+
+// K-major, K-padded copy of a 16-bit operand: dst[x * Kp + k] = op(x, k) for
+// k < K, zero for K <= k < Kp.  XMAJOR: the source holds (x, k) at
+// src[k * ld + x] (A given transposed, B as given), and 64 x 64 blocks go
+// through LDS so that both the reads (along x) and the writes (along k) are
+// contiguous; otherwise at src[x * ld + k].
+template <bool XMAJOR>
+__global__ __launch_bounds__(256) void pack16_kernel(const uint16_t *src, int64_t ld, int X, int K, uint16_t *dst,
+                                                     int Kp) {
+    __shared__ uint16_t tile[64][65];
+    const int x0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+    const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;   // 64 x 4
+    if (XMAJOR) {
+        for (int kk = ty; kk < 64; kk += 4) {
+            const int k = k0 + kk, x = x0 + tx;
+            tile[kk][tx] = (k < K && x < X) ? src[(int64_t)k * ld + x] : (uint16_t)0;
+        }
+        __syncthreads();
+        for (int xx = ty; xx < 64; xx += 4) {
+            const int x = x0 + xx, k = k0 + tx;
+            if (x < X && k < Kp) dst[(int64_t)x * Kp + k] = tile[tx][xx];
+        }
+    } else {
+        for (int xx = ty; xx < 64; xx += 4) {
+            const int x = x0 + xx, k = k0 + tx;
+            if (x < X && k < Kp) dst[(int64_t)x * Kp + k] = k < K ? src[(int64_t)x * ld + k] : (uint16_t)0;
+        }
+    }
+}
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+// A K-major operand can be read in place: 16-byte aligned, row stride a
+// multiple of 8 elements, K a multiple of the slice, and 128 rows addressable
+// with 32-bit byte offsets.
+bool direct_ok(const void *p, int64_t ld, int K) {
+    return aligned16(p) && ld % 8 == 0 && K % BK == 0 && (127 * ld + BK) * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint16_t *dst, int Kp,
+                hipStream_t stream) {
+    const dim3 grid((X + 63) / 64, (Kp + 63) / 64);
+    if (xmajor) hipLaunchKernelGGL(pack16_kernel<true>, grid, dim3(256), 0, stream, src, ld, X, K, dst, Kp);
+    else hipLaunchKernelGGL(pack16_kernel<false>, grid, dim3(256), 0, stream, src, ld, X, K, dst, Kp);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+
+int64_t gemm16_workspace_bytes(int ta, int tb, int M, int N, int K, const void *A, int64_t lda, const void *B,
+                               int64_t ldb) {
+    const int64_t Kp = (int64_t)(K + BK - 1) / BK * BK;
+    int64_t bytes = 0;
+    if (ta || !direct_ok(A, lda, K)) bytes += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
+    if (!tb || !direct_ok(B, ldb, K)) bytes += ((int64_t)N * Kp * 2 + 255) / 256 * 256;
+    return bytes;
+}
+
+hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
+    const int ta = g16.trans_a, tb = g16.trans_b;
+    const void *A = g16.A, *B = g16.B;
+    const int M = g16.M, N = g16.N, K = g16.K;
+    const int Kp = (K + BK - 1) / BK * BK;
+    const bool pa = ta || !direct_ok(A, g16.lda, K);
+    const bool pb = !tb || !direct_ok(B, g16.ldb, K);
+    Args16 a;
+    a.M = M; a.N = N; a.K = Kp;
+    a.alpha = g16.alpha; a.beta = g16.beta;
+    a.C = g16.C; a.ldc = g16.ldc;
+    a.A = static_cast<const uint16_t *>(A); a.lda = g16.lda;
+    a.B = static_cast<const uint16_t *>(B); a.ldb = g16.ldb;
+    if (pa || pb) {
+        void *ws = nullptr;
+        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb);
+        hipError_t e = stream_workspace((size_t)bytes, stream, &ws);
+        if (e != hipSuccess) return e;
+        unsigned char *p = static_cast<unsigned char *>(ws);
+        if (pa) {
+            uint16_t *dst = reinterpret_cast<uint16_t *>(p);
+            e = pack(static_cast<const uint16_t *>(A), g16.lda, ta != 0, M, K, dst, Kp, stream);
+            if (e != hipSuccess) return e;
+            a.A = dst;
+            a.lda = Kp;
+            p += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
+        }
+        if (pb) {
+            uint16_t *dst = reinterpret_cast<uint16_t *>(p);
+            // B as given is K x N: (n, k) at B[k * ldb + n], M/N-major.
+            e = pack(static_cast<const uint16_t *>(B), g16.ldb, tb == 0, N, K, dst, Kp, stream);
+            if (e != hipSuccess) return e;
+            a.B = dst;
+            a.ldb = Kp;
+        }
+    }
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const dim3 grid(tiles_m * tiles_n);
+    if (kind == GEMM16_F32_F16)
+        hipLaunchKernelGGL(gemm16_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+    else
+        hipLaunchKernelGGL(gemm16_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace sgemm
+
+extern "C" int gemm16_f32(int in_type, int trans_a, int trans_b, int M, int N, int K, float alpha, const void *A,
+                          int lda, const void *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+    if (in_type != GEMM16_F32_BF16 && in_type != GEMM16_F32_F16) return GEMM16_F32_ERR_TYPE;
+    if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return 23;
+    if (M < 0) return 1;
+    if (N < 0) return 2;
+    if (K < 0) return 3;
+    const auto one = [](int v) { return v > 1 ? v : 1; };
+    const bool need_ab = M > 0 && N > 0 && K > 0 && alpha != 0.f;
+    if (need_ab && A == nullptr) return 5;
+    if (lda < one(trans_a ? M : K)) return 6;
+    if (need_ab && B == nullptr) return 7;
+    if (ldb < one(trans_b ? K : N)) return 8;
+    if (M > 0 && N > 0 && C == nullptr) return 10;
+    if (ldc < one(N)) return 11;
+    if (M == 0 || N == 0) return 0;
+    sgemm::GemmArgs g;
+    g.M = M; g.N = N; g.K = K;
+    g.alpha = alpha; g.beta = beta;
+    g.A = static_cast<const float *>(A);    // carried as raw pointers; read as 16-bit
+    g.B = static_cast<const float *>(B);
+    g.C = C;
+    g.lda = lda; g.ldb = ldb; g.ldc = ldc;
+    g.trans_a = trans_a; g.trans_b = trans_b;
+    hipError_t e;
+    if (alpha == 0.f || K == 0) {
+        e = sgemm::launch_scale_c(g, stream);
+        return e == hipSuccess ? 0 : -static_cast<int>(e);
+    }
+    if (reinterpret_cast<uintptr_t>(A) % 2 || reinterpret_cast<uintptr_t>(B) % 2) return GEMM16_F32_ERR_ALIGN;
+    if (K > 4000000 || sgemm::gemm16_grid(M, N) > 0x7fffffff) return 22;
+    e = sgemm::launch_gemm16(in_type, g, stream);
+    return e == hipSuccess ? 0 : -static_cast<int>(e);
+}

@@ -47,6 +47,11 @@ hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);
 
+// 16-bit-input GEMM (gemm16.hip).  The GemmArgs pointers A and B carry the
+// 16-bit operands; kind is GEMM16_F32_BF16 or GEMM16_F32_F16.
+hipError_t launch_gemm16(int kind, const GemmArgs &g, hipStream_t stream);
+int64_t gemm16_grid(int M, int N);
+
 // The workspace of `stream` on the current device, at least `bytes` long.  It
 // stays valid for work queued on that stream until the next call that asks
 // for more.

@@ -1,0 +1,168 @@
+"""GPU parity of the 16-bit-input GEMM (gemm16_f32) against the oracle's
+16-bit-input form: the same 16-bit patterns decoded exactly and multiplied in
+float64.  Real-valued inputs within 2e-5 * (|alpha|*(|op(A)||op(B)|)_ij +
+|beta|*|C0_ij|) per element; integer-valued inputs (exact products and sums)
+bit for bit.  Both formats, all four operand forms, the in-place (NT,
+aligned, K a multiple of 64) and the packed paths."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from gpu_helpers import from_device_padded, sample_positions, say, to_device_padded
+
+pytestmark = pytest.mark.gpu
+
+FORMS = [(0, 0), (0, 1), (1, 0), (1, 1)]
+FORM_IDS = ["nn", "nt", "tn", "tt"]
+KINDS = [1, 2]
+KIND_IDS = ["bf16", "f16"]
+
+
+@pytest.fixture(scope="module")
+def sg():
+    if not torch.cuda.is_available():
+        pytest.fail("no GPU visible")
+    import fp32_sgemm_amd
+    return fp32_sgemm_amd
+
+
+def _stored(x, t):
+    return np.ascontiguousarray(x.T) if t else x
+
+
+def _dev16(X, ld, offset=0):
+    """Copies a uint16 host matrix into a device buffer with row stride ld and
+    the first element `offset` elements in; returns (buffer, pointer)."""
+    rows, cols = X.shape
+    total = offset + (rows - 1) * ld + cols if rows > 0 else offset + 1
+    host = np.full(max(total, 1), 0x7FC0, dtype=np.uint16)      # NaN patterns around the matrix
+    if rows and cols:
+        np.lib.stride_tricks.as_strided(host[offset:], shape=(rows, cols), strides=(ld * 2, 2))[...] = X
+    buf = torch.from_numpy(host.view(np.int16)).cuda()
+    return buf, buf.data_ptr() + 2 * offset
+
+
+def run16(sg, kind, ta, tb, A, B, C0, alpha, beta, pad=(0, 0), offs=(0, 0), c_fill=np.nan):
+    """A (M x K) and B (K x N) are op(A) and op(B) as uint16 patterns."""
+    M, K = A.shape
+    N = B.shape[1]
+    As, Bs = _stored(A, ta), _stored(B, tb)
+    lda, ldb = max(As.shape[1], 1) + pad[0], max(Bs.shape[1], 1) + pad[1]
+    bA, pA = _dev16(As, lda, offs[0])
+    bB, pB = _dev16(Bs, ldb, offs[1])
+    Cinit = C0 if C0 is not None else np.full((M, N), c_fill, np.float32)
+    bC, pC, _ = to_device_padded(Cinit, max(N, 1), fill=np.float32(-7.25))
+    st = sg.gemm16_f32(kind, ta, tb, M, N, K, float(alpha), pA, lda, pB, ldb, float(beta), pC, max(N, 1),
+                       torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    return st, from_device_padded(bC, M, N, max(N, 1)), As, Bs
+
+
+def _inputs16(M, N, K, dist, kind, seed):
+    w = workloads.custom(M, N, K, dist=dist, seed=seed, c0_dist="normal" if dist != "int4" else "int4")
+    return workloads.make_inputs_16bit(w, kind)
+
+
+def check16(C, As, Bs, kind, ta, tb, alpha, beta, C0, exact):
+    Cref, absab = oracle.sgemm_ref_lowp(As, Bs, kind, ta, tb, alpha, beta, C0)
+    if exact:
+        return oracle.check_bitexact(C, Cref)
+    return oracle.check_within_bound(C, Cref, oracle.error_bound(absab, alpha, beta, C0))
+
+
+SHAPES = [(1, 1, 1), (17, 31, 33), (129, 127, 65), (300, 260, 700), (128, 128, 128), (64, 64, 64),
+          (257, 129, 1000), (130, 70, 9), (256, 256, 4096), (200, 136, 192)]
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+def test_gemm16_real(sg, kind, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[g16_real] kind={kind} {form} {shape}")
+    A, B, C0 = _inputs16(M, N, K, "uniform", kind, 1500 + M + N + K)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check16(C, As, Bs, kind, ta, tb, 1.25, -0.5, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
+def test_gemm16_integer_bitexact(sg, kind, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[g16_int] kind={kind} {form} {shape}")
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 1600 + M + N + K)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 2.0, -1.0)
+    assert st == 0
+    ok, info = check16(C, As, Bs, kind, ta, tb, 2.0, -1.0, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+def test_gemm16_misaligned_and_padded_strides(sg, kind):
+    """NT with strides that are not multiples of 8 and pointers off 16 bytes:
+    the packed path."""
+    M, N, K = 150, 90, 256
+    A, B, C0 = _inputs16(M, N, K, "uniform", kind, 41)
+    st, C, As, Bs = run16(sg, kind, 0, 1, A, B, C0, 0.5, 0.25, pad=(3, 5), offs=(1, 3))
+    assert st == 0
+    ok, info = check16(C, As, Bs, kind, 0, 1, 0.5, 0.25, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+def test_gemm16_beta_zero_ignores_nan_c(sg, kind):
+    A, B, _ = _inputs16(140, 130, 128, "uniform", kind, 42)
+    st, C, As, Bs = run16(sg, kind, 0, 1, A, B, None, 1.0, 0.0, c_fill=np.nan)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check16(C, As, Bs, kind, 0, 1, 1.0, 0.0, None, exact=False)
+    assert ok, info
+
+
+def test_gemm16_alpha_zero_and_k_zero(sg):
+    M, N = 70, 90
+    C0 = np.random.default_rng(3).standard_normal((M, N)).astype(np.float32)
+    A = np.full((M, 30), 0x7FC0, np.uint16)
+    B = np.full((30, N), 0x7FC0, np.uint16)
+    st, C, _, _ = run16(sg, 1, 0, 0, A, B, C0, 0.0, -0.5)
+    assert st == 0 and np.array_equal(C, np.float32(-0.5) * C0)
+    st, C, _, _ = run16(sg, 2, 0, 1, np.zeros((M, 0), np.uint16), np.zeros((0, N), np.uint16), C0, 2.0, 3.0)
+    assert st == 0 and np.array_equal(C, np.float32(3.0) * C0)
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
+def test_gemm16_headline_shape_sampled(sg, kind, form):
+    """4096^3 with alpha 1.5, beta -0.5 on N(0,1) inputs stored in 16 bits: NT
+    read in place, NN through the packed path."""
+    ta, tb = form
+    w = workloads.WORKLOADS["square4096_ab"]
+    say(f"[g16_headline] kind={kind} {form}")
+    A, B, C0 = workloads.make_inputs_16bit(w, kind)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, w.alpha, w.beta)
+    assert st == 0 and np.all(np.isfinite(C))
+    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid + kind)
+    vals, absab = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, ta, tb, w.alpha, w.beta, C0)
+    ok, info = oracle.check_within_bound(C[rows, cols], vals,
+                                         oracle.error_bound(absab, w.alpha, w.beta, C0[rows, cols]))
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+def test_gemm16_ragged_large_integer_sampled(sg, kind):
+    M, N, K = 4092, 3000, 4100
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 43)
+    st, C, As, Bs = run16(sg, kind, 1, 0, A, B, C0, 1.0, 1.0)
+    assert st == 0
+    rows, cols = sample_positions(M, N, 3000, seed=44)
+    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 1, 0, 1.0, 1.0, C0)
+    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    assert ok, info

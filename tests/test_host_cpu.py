@@ -4,6 +4,7 @@ benchmark's closed-form work/byte model, and the input generators.  No GPU
 compute is launched here."""
 from __future__ import annotations
 
+import glob
 import os
 import re
 import shutil
@@ -17,10 +18,15 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgemm_f32.h")
 
 
+HEADERS = sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h")))
+
+
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(sgemm_f32\w*)\s*\(", text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -32,7 +38,8 @@ def sg():
 def test_header_declares_the_interface():
     names = _declared_functions()
     assert {"sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select", "sgemm_f32_variant_name",
-            "sgemm_f32_version"} <= set(names), names
+            "sgemm_f32_version", "gemm16_f32"} <= set(names), names
+    assert len(HEADERS) == 2, HEADERS
 
 
 def test_library_exports_every_declared_symbol(sg):
@@ -40,7 +47,7 @@ def test_library_exports_every_declared_symbol(sg):
                          text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
     for name in _declared_functions():
-        assert name in exported, f"{name} declared in sgemm_f32.h but not exported"
+        assert name in exported, f"{name} declared in include/ but not exported"
         assert hasattr(sg._lib, name)
     assert set(sg.EXPORTED) == set(_declared_functions())
 
@@ -125,6 +132,23 @@ def test_transposed_kernel_selection(sg):
     big = (1 << 31) // 4 // 100          # 128 rows of this stride exceed 2 GiB, 32 rows do not
     assert sel(0, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_SCALAR
     assert sel(1, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_LARGE
+
+
+def test_gemm16_argument_errors_without_touching_the_gpu(sg):
+    p = 0x1000
+    f = sg.gemm16_f32
+    assert f(0, 0, 1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.GEMM16_ERR_TYPE
+    assert f(3, 0, 1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.GEMM16_ERR_TYPE
+    assert f(1, 2, 1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_TRANS
+    assert f(1, 0, 1, -1, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == 1
+    assert f(1, 0, 1, 2, 2, 2, 1.0, 0, 2, p, 2, 0.0, p, 2, 0) == 5
+    assert f(1, 0, 1, 2, 2, 3, 1.0, p, 2, p, 3, 0.0, p, 2, 0) == 6          # A is 2 x 3: lda >= 3
+    assert f(1, 0, 1, 2, 5, 3, 1.0, p, 3, p, 2, 0.0, p, 5, 0) == 8          # B stored 5 x 3: ldb >= 3
+    assert f(2, 0, 0, 2, 5, 3, 1.0, p, 3, p, 4, 0.0, p, 5, 0) == 8          # B stored 3 x 5: ldb >= 5
+    assert f(1, 0, 1, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, 0, 2, 0) == 10
+    assert f(1, 0, 1, 2, 2, 2, 1.0, p + 1, 2, p, 2, 0.0, p, 2, 0) == sg.GEMM16_ERR_ALIGN
+    assert f(1, 0, 1, 2, 2, 4000001, 1.0, p, 4000001, p, 4000001, 0.0, p, 2, 0) == sg.ERR_TOO_LARGE
+    assert f(1, 0, 1, 0, 2, 2, 1.0, 0, 2, 0, 2, 0.0, 0, 2, 0) == 0          # empty output
 
 
 def test_variant_names_and_version(sg):
