@@ -21,8 +21,9 @@
 //
 // Tiles.  A work-group computes a 128 x 128 tile of C with 4 waves of 64 x 64
 // (2 x 2 blocks of 32 x 32).  Slices of 64 k are staged in LDS, double
-// buffered, with the next slice's global loads in registers during the MFMAs
-// of the current one.  A slice row is 128 bytes (8 chunks of 16 bytes); chunk
+// buffered, with two later slices in registers or in flight during the MFMAs
+// of the current one, and each k step's fragments read from LDS one step
+// ahead of its MFMAs.  A slice row is 128 bytes (8 chunks of 16 bytes); chunk
 // c of row r is stored at chunk c ^ ((r >> 1) & 7), so the 16-byte reads of
 // eight consecutive rows at one chunk, and the writes of one row's chunks,
 // fall in distinct banks.
@@ -138,36 +139,64 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
         ra_row[b] = wm * 64 + 32 * b + l32;
         rb_row[b] = wn * 64 + 32 * b + l32;
     }
-    auto compute = [&](const unsigned char *st) {
+    // Fragments of k step s (16 k): one 16-byte read per 32-row block.
+    auto read_frags = [&](const unsigned char *st, int s, i32x4 (&fa)[2], i32x4 (&fb)[2]) {
+        const int c = 2 * s + h;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            fa[b] = *reinterpret_cast<const i32x4 *>(st + ra_row[b] * ROW_BYTES + swz(ra_row[b], c) * 16);
+            fb[b] = *reinterpret_cast<const i32x4 *>(st + A_STAGE + rb_row[b] * ROW_BYTES + swz(rb_row[b], c) * 16);
+        }
+    };
+    // All MFMAs of one slice; the reads of step s+1 are issued before the
+    // MFMAs of step s, and issue(s) (global loads of a later slice) runs at the
+    // top of step s.
+    auto compute = [&](const unsigned char *st, auto issue) {
+        i32x4 fa[2][2], fb[2][2];
+        read_frags(st, 0, fa[0], fb[0]);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
-            const int c = 2 * s + h;
-            i32x4 fa[2], fb[2];
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-                fa[b] = *reinterpret_cast<const i32x4 *>(st + ra_row[b] * ROW_BYTES + swz(ra_row[b], c) * 16);
-                fb[b] = *reinterpret_cast<const i32x4 *>(st + A_STAGE + rb_row[b] * ROW_BYTES +
-                                                          swz(rb_row[b], c) * 16);
-            }
+            issue(s);
+            if (s + 1 < BK / 16) read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int ib = 0; ib < 2; ++ib)
 #pragma unroll
-                for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma16<F16>(fa[ib], fb[jb], acc[ib][jb]);
+                for (int jb = 0; jb < 2; ++jb)
+                    acc[ib][jb] = mfma16<F16>(fa[s & 1][ib], fb[s & 1][jb], acc[ib][jb]);
         }
     };
+    auto no_issue = [](int) {};
+    // Loads of one slice spread over the 4 k steps: 2 of the 8 groups each.
+    auto slice_loader = [&](int k0, i32x4 (&ra)[LOADS], i32x4 (&rb)[LOADS]) {
+        const __amdgpu_buffer_rsrc_t rsa = rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + BK) * 2));
+        const __amdgpu_buffer_rsrc_t rsb = rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + BK) * 2));
+        return [&, rsa, rsb](int s) {
+            ra[s] = raw_buffer_load_v4i32(rsa, la.off[s], 0, 0);
+            rb[s] = raw_buffer_load_v4i32(rsb, lb.off[s], 0, 0);
+        };
+    };
 
+    // Two slices in flight: while slice t is computed from LDS, slice t+1
+    // waits in registers for its buffer and slice t+2 is being loaded.  The
+    // loads are unconditional (past the end they re-read the last slice, never
+    // stored), so the wait counts are the same on every path.
     const int nk = g.K / BK;
-    i32x4 ra[LOADS], rb[LOADS];
-    load(0, ra, rb);
-    store(smem, ra, rb);
+    i32x4 ra0[LOADS], rb0[LOADS], ra1[LOADS], rb1[LOADS];
+    load(0, ra0, rb0);
+    store(smem, ra0, rb0);
+    if (nk > 1) load(BK, ra1, rb1);
     __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        const bool more = t + 1 < nk;
-        if (more) load((t + 1) * BK, ra, rb);
-        compute(smem + (t & 1) * STAGE);
-        if (more) store(smem + ((t + 1) & 1) * STAGE, ra, rb);
+    int t = 0;
+    for (; t + 1 < nk; t += 2) {
+        compute(smem, slice_loader((t + 2 < nk ? t + 2 : nk - 1) * BK, ra0, rb0));
+        store(smem + STAGE, ra1, rb1);
+        __syncthreads();
+        compute(smem + STAGE, slice_loader((t + 3 < nk ? t + 3 : nk - 1) * BK, ra1, rb1));
+        if (t + 2 < nk) store(smem, ra0, rb0);
         __syncthreads();
     }
+    if (t < nk) compute(smem, no_issue);
 
     // Epilogue: C read in a pass of its own before the stores (see the FP32
     // kernel), elements outside M x N neither read nor written.
