@@ -39,6 +39,7 @@
 //
 // Epilogue.  C = alpha * acc + beta * C, where C is read only when beta != 0.
 #include <atomic>
+#include <type_traits>
 
 #include "gemm_internal.hpp"
 
@@ -55,6 +56,10 @@ __device__ f32x4v raw_buffer_load_v4f32(__amdgpu_buffer_rsrc_t rsrc, int voffset
     __asm("llvm.amdgcn.raw.ptr.buffer.load.v4f32");
 __device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+// 4-byte vector-memory buffer store: offsets at or past the extent are
+// dropped without a write.
+__device__ void raw_buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.store.f32");
 
 // A lane offset past every resource extent used here (extents stay below
 // 2^31 bytes): the load returns zero and touches no memory.
@@ -479,8 +484,40 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
     const int h = lane >> 5;
     const int l32 = lane & 31;
     const int rows = g.M - m0, cols = g.N - n0;
-    float cv[T::MB][T::NB][16];
-    if (beta != 0.f) {
+    // Interior tiles take a copy of the epilogue without any per-element
+    // guard: straight-line code lets the compiler wait for each C load only
+    // as far as needed, instead of for all outstanding loads at every guarded
+    // element.  Edge tiles keep it branch-free too, through a buffer resource
+    // over the tile's valid part of C: rows past M lie beyond its extent and
+    // columns past N get an out-of-range offset, so their loads read zero and
+    // their stores are dropped.  (When 128 rows of C span 2 GiB or more, edge
+    // tiles fall back to guarded pointer accesses.)
+    const bool buf_edge = (int64_t)(T::BM - 1) * ldc * 4 + T::BN * 4 < ((int64_t)1 << 31);
+    auto epilogue = [&](auto mode_tag) {
+        constexpr int MODE = decltype(mode_tag)::value;   // 0 interior, 1 edge via buffer, 2 edge guarded
+        const __amdgpu_buffer_rsrc_t rc =
+            make_rsrc(Cb, MODE == 1 ? (int)(((int64_t)(min(rows, T::BM) - 1) * ldc + min(cols, T::BN)) * 4) : 0);
+        float cv[T::MB][T::NB][16];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < T::NB; ++jb) {
+                    const int c = wn * T::WN + jb * 32 + l32;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (MODE == 0) {
+                            cv[ib][jb][r] = Cb[(int64_t)rr * ldc + c];
+                        } else if (MODE == 1) {
+                            cv[ib][jb][r] = raw_buffer_load_f32(rc, c < cols ? (int)((rr * ldc + c) * 4) : kOutOfRange, 0, 0);
+                        } else {
+                            const bool ok = rr < rows && c < cols;
+                            cv[ib][jb][r] = ok ? Cb[(int64_t)rr * ldc + c] : 0.f;
+                        }
+                    }
+                }
+        }
 #pragma unroll
         for (int ib = 0; ib < T::MB; ++ib)
 #pragma unroll
@@ -489,25 +526,21 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const bool ok = !edge_mn || (rr < rows && c < cols);
-                    cv[ib][jb][r] = ok ? Cb[(int64_t)rr * ldc + c] : 0.f;
+                    float v = alpha * acc[ib][jb][r];
+                    if (beta != 0.f) v = fmaf(beta, cv[ib][jb][r], v);
+                    if (MODE == 0) {
+                        Cb[(int64_t)rr * ldc + c] = v;
+                    } else if (MODE == 1) {
+                        raw_buffer_store_f32(v, rc, c < cols ? (int)((rr * ldc + c) * 4) : kOutOfRange, 0, 0);
+                    } else if (rr < rows && c < cols) {
+                        Cb[(int64_t)rr * ldc + c] = v;
+                    }
                 }
             }
-    }
-#pragma unroll
-    for (int ib = 0; ib < T::MB; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < T::NB; ++jb) {
-            const int c = wn * T::WN + jb * 32 + l32;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-                if (edge_mn && (rr >= rows || c >= cols)) continue;
-                float v = alpha * acc[ib][jb][r];
-                if (beta != 0.f) v = fmaf(beta, cv[ib][jb][r], v);
-                Cb[(int64_t)rr * ldc + c] = v;
-            }
-        }
+    };
+    if (!edge_mn) epilogue(std::integral_constant<int, 0>());
+    else if (buf_edge) epilogue(std::integral_constant<int, 1>());
+    else epilogue(std::integral_constant<int, 2>());
 }
 
 // At least two waves per SIMD: with one wave per SIMD the matrix core idles
