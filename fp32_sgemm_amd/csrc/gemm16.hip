@@ -28,6 +28,7 @@
 // eight consecutive rows at one chunk, and the writes of one row's chunks,
 // fall in distinct banks.
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm_internal.hpp"
 #include "gemm16_f32.h"
@@ -42,6 +43,12 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 __device__ i32x4 raw_buffer_load_v4i32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.ptr.buffer.load.v4i32");
+__device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+// Vector-memory buffer store: offsets at or past the extent are dropped.
+__device__ void raw_buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.store.f32");
+constexpr int kOutOfRange = (int)0x80000000u;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc16(const uint16_t *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(base), (short)0, bytes, 0x00020000);
@@ -231,6 +238,173 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
             }
 }
 
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles for grids that still fill the device: 4 waves of 128 x 128
+// (4 x 4 blocks of 32 x 32, 256 accumulators per lane, kept in the
+// accumulation registers), one work-group per CU.  Per MFMA a wave reads half
+// the fragment bytes of a 64 x 64 wave tile and the slice writes are spread
+// over four times the MFMAs, so the LDS traffic (about 96 bytes per clock at
+// the MFMA rate, against 128) no longer binds; with one wave per SIMD the
+// latency is hidden inside the wave: fragment reads one k step ahead and the
+// next slice's global loads spread over the k steps.
+// ---------------------------------------------------------------------------
+namespace big {
+constexpr int BM = 256, BN = 256;
+constexpr int A_STAGE = BM * ROW_BYTES;          // 32 KB
+constexpr int B_STAGE = BN * ROW_BYTES;
+constexpr int STAGE = A_STAGE + B_STAGE;         // 64 KB
+constexpr int LOADS = (BM * CHUNKS) / NT;        // 8 per operand per thread
+constexpr int WT = 128;                          // wave tile
+constexpr int BLK = WT / 32;                     // 4 blocks per wave and direction
+}  // namespace big
+
+struct BigLoader {
+    int off[big::LOADS];
+    int lds[big::LOADS];
+    __device__ __forceinline__ BigLoader(int64_t ld, int tid) {
+#pragma unroll
+        for (int j = 0; j < big::LOADS; ++j) {
+            const int r = tid / CHUNKS + (NT / CHUNKS) * j;
+            const int c = tid % CHUNKS;
+            off[j] = (r * (int)ld + c * 8) * 2;
+            lds[j] = r * ROW_BYTES + swz(r, c) * 16;
+        }
+    }
+};
+
+template <bool F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_big_kernel(
+    Args16 g, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * big::STAGE];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * big::BM, n0 = tn * big::BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const BigLoader la(g.lda, tid), lb(g.ldb, tid);
+    const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
+    const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
+    const uint16_t *Bb = g.B + (int64_t)n0 * g.ldb;
+    i32x4 ra[big::LOADS], rb[big::LOADS];
+    auto rsrc_a = [&](int k0) { return rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + BK) * 2)); };
+    auto rsrc_b = [&](int k0) { return rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + BK) * 2)); };
+    auto store = [&](unsigned char *st) {
+#pragma unroll
+        for (int j = 0; j < big::LOADS; ++j) *reinterpret_cast<i32x4 *>(st + la.lds[j]) = ra[j];
+#pragma unroll
+        for (int j = 0; j < big::LOADS; ++j) *reinterpret_cast<i32x4 *>(st + big::A_STAGE + lb.lds[j]) = rb[j];
+    };
+
+    f32x16 acc[big::BLK][big::BLK];
+#pragma unroll
+    for (int i = 0; i < big::BLK; ++i)
+#pragma unroll
+        for (int j = 0; j < big::BLK; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    int ra_row[big::BLK], rb_row[big::BLK];
+#pragma unroll
+    for (int b = 0; b < big::BLK; ++b) {
+        ra_row[b] = wm * big::WT + 32 * b + l32;
+        rb_row[b] = wn * big::WT + 32 * b + l32;
+    }
+    auto read_frags = [&](const unsigned char *st, int s, i32x4 (&fa)[big::BLK], i32x4 (&fb)[big::BLK]) {
+        const int c = 2 * s + h;
+#pragma unroll
+        for (int b = 0; b < big::BLK; ++b) {
+            fa[b] = *reinterpret_cast<const i32x4 *>(st + ra_row[b] * ROW_BYTES + swz(ra_row[b], c) * 16);
+            fb[b] = *reinterpret_cast<const i32x4 *>(st + big::A_STAGE + rb_row[b] * ROW_BYTES + swz(rb_row[b], c) * 16);
+        }
+    };
+    constexpr int STEPS = BK / 16;
+    constexpr int PER_STEP = big::LOADS / STEPS;     // 2 groups of each operand per k step
+    // One slice from LDS; during its k steps the next slice (k0n) is loaded.
+    auto compute = [&](const unsigned char *st, int k0n) {
+        const __amdgpu_buffer_rsrc_t rsa = rsrc_a(k0n), rsb = rsrc_b(k0n);
+        i32x4 fa[2][big::BLK], fb[2][big::BLK];
+        read_frags(st, 0, fa[0], fb[0]);
+#pragma unroll
+        for (int s = 0; s < STEPS; ++s) {
+#pragma unroll
+            for (int j = 0; j < PER_STEP; ++j) {
+                ra[s * PER_STEP + j] = raw_buffer_load_v4i32(rsa, la.off[s * PER_STEP + j], 0, 0);
+                rb[s * PER_STEP + j] = raw_buffer_load_v4i32(rsb, lb.off[s * PER_STEP + j], 0, 0);
+            }
+            if (s + 1 < STEPS) read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int ib = 0; ib < big::BLK; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < big::BLK; ++jb)
+                    acc[ib][jb] = mfma16<F16>(fa[s & 1][ib], fb[s & 1][jb], acc[ib][jb]);
+        }
+    };
+
+    const int nk = g.K / BK;
+    {
+        const __amdgpu_buffer_rsrc_t rsa = rsrc_a(0), rsb = rsrc_b(0);
+#pragma unroll
+        for (int j = 0; j < big::LOADS; ++j) {
+            ra[j] = raw_buffer_load_v4i32(rsa, la.off[j], 0, 0);
+            rb[j] = raw_buffer_load_v4i32(rsb, lb.off[j], 0, 0);
+        }
+    }
+    store(smem);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        // The loads are unconditional: past the end they re-read the last
+        // slice (never stored), so the wait counts are the same on every path.
+        compute(smem + (t & 1) * big::STAGE, (t + 1 < nk ? t + 1 : t) * BK);
+        if (t + 1 < nk) store(smem + ((t + 1) & 1) * big::STAGE);
+        __syncthreads();
+    }
+
+    // Epilogue in four passes of one block row (4 blocks, 64 values per lane):
+    // the C reads of a pass are issued together before its stores.  Edge
+    // tiles go through a buffer resource over the tile's valid part of C
+    // (rows past M beyond its extent, columns past N out-of-range offsets).
+    const bool edge = rows_a < big::BM || rows_b < big::BN;
+    float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc = rsrc16(reinterpret_cast<const uint16_t *>(Cb),
+                                             (int)(((int64_t)(rows_a - 1) * g.ldc + rows_b) * 4));
+    const float alpha = g.alpha, beta = g.beta;
+    auto pass = [&](int ib, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        float cv[big::BLK][16];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int jb = 0; jb < big::BLK; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int cc = wn * big::WT + 32 * jb + l32;
+                    cv[jb][r] = EDGE ? raw_buffer_load_f32(rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0)
+                                     : Cb[(int64_t)rr * g.ldc + cc];
+                }
+        }
+#pragma unroll
+        for (int jb = 0; jb < big::BLK; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int cc = wn * big::WT + 32 * jb + l32;
+                float v = alpha * acc[ib][jb][r];
+                if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
+                if (EDGE) raw_buffer_store_f32(v, rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0);
+                else Cb[(int64_t)rr * g.ldc + cc] = v;
+            }
+    };
+#pragma unroll
+    for (int ib = 0; ib < big::BLK; ++ib) {
+        if (edge) pass(ib, std::true_type());
+        else pass(ib, std::false_type());
+    }
+}
+
 // K-major, K-padded copy of a 16-bit operand: dst[x * Kp + k] = op(x, k) for
 // k < K, zero for K <= k < Kp.  XMAJOR: the source holds (x, k) at
 // src[k * ld + x] (A given transposed, B as given), and 64 x 64 blocks go
@@ -263,10 +437,10 @@ __global__ __launch_bounds__(256) void pack16_kernel(const uint16_t *src, int64_
 bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
 
 // A K-major operand can be read in place: 16-byte aligned, row stride a
-// multiple of 8 elements, K a multiple of the slice, and 128 rows addressable
-// with 32-bit byte offsets.
+// multiple of 8 elements, K a multiple of the slice, and 256 rows (the larger
+// tile) addressable with 32-bit byte offsets.
 bool direct_ok(const void *p, int64_t ld, int K) {
-    return aligned16(p) && ld % 8 == 0 && K % BK == 0 && (127 * ld + BK) * 2 < ((int64_t)1 << 31);
+    return aligned16(p) && ld % 8 == 0 && K % BK == 0 && (255 * ld + BK) * 2 < ((int64_t)1 << 31);
 }
 
 hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint16_t *dst, int Kp,
@@ -278,6 +452,13 @@ hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint
 }
 
 }  // namespace
+
+// 256 x 256 tiles when they still give every one of the 256 CUs a tile, and
+// 256 rows of C are addressable with 32-bit byte offsets (edge epilogue).
+bool use_big_tiles(int M, int N, int64_t ldc) {
+    const int64_t tiles = (int64_t)((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
+    return tiles >= 256 && (255 * ldc + big::BN) * 4 < ((int64_t)1 << 31);
+}
 
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
@@ -325,6 +506,15 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             a.B = dst;
             a.ldb = Kp;
         }
+    }
+    if (use_big_tiles(M, N, g16.ldc)) {
+        const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
+        const dim3 grid(tiles_m * tiles_n);
+        if (kind == GEMM16_F32_F16)
+            hipLaunchKernelGGL(gemm16_big_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        else
+            hipLaunchKernelGGL(gemm16_big_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        return hipGetLastError();
     }
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     const dim3 grid(tiles_m * tiles_n);

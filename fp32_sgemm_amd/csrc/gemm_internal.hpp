@@ -51,6 +51,8 @@ hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);
 // 16-bit operands; kind is GEMM16_F32_BF16 or GEMM16_F32_F16.
 hipError_t launch_gemm16(int kind, const GemmArgs &g, hipStream_t stream);
 int64_t gemm16_grid(int M, int N);
+// Whether the 256 x 256 tile kernel takes the product (else 128 x 128).
+bool use_big_tiles(int M, int N, int64_t ldc);
 
 // The workspace of `stream` on the current device, at least `bytes` long.  It
 // stays valid for work queued on that stream until the next call that asks

@@ -166,3 +166,34 @@ def test_gemm16_ragged_large_integer_sampled(sg, kind):
     vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 1, 0, 1.0, 1.0, C0)
     ok, info = oracle.check_bitexact(C[rows, cols], vals)
     assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+def test_gemm16_big_tiles_with_edges(sg, kind, form):
+    """Shapes with at least 256 tiles of 256 x 256 (the larger-tile kernel)
+    whose M and N are not tile multiples, beta != 0 (the edge epilogue reads
+    and writes C through the buffer resource), checked on samples that include
+    the first and last rows and columns."""
+    ta, tb = form
+    M, N, K = 4100, 4000, 256
+    say(f"[g16_big_edges] kind={kind} {form}")
+    A, B, C0 = _inputs16(M, N, K, "uniform", kind, 45 + 2 * ta + tb)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0 and np.all(np.isfinite(C))
+    rows, cols = sample_positions(M, N, 3000, seed=46)
+    vals, absab = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, ta, tb, 1.5, -0.5, C0)
+    ok, info = oracle.check_within_bound(C[rows, cols], vals, oracle.error_bound(absab, 1.5, -0.5, C0[rows, cols]))
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+def test_gemm16_big_tiles_integer_bitexact(sg, kind):
+    M, N, K = 4350, 3900, 520
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 47)
+    st, C, As, Bs = run16(sg, kind, 0, 1, A, B, C0, 1.0, -1.0)
+    assert st == 0
+    rows, cols = sample_positions(M, N, 3000, seed=48)
+    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 0, 1, 1.0, -1.0, C0)
+    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    assert ok, info
