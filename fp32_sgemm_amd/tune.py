@@ -12,7 +12,9 @@ autotuning step that "How a Matmul Kernel Gets Fast" describes in its section
 problem), applied to the configurations this library compiles.
 
 Each plan is timed as the benchmark times a step: single launches, each
-between its own pair of events, median of at least 11.  A candidate replaces
+between its own pair of events, median of at least 11; the candidates of a
+class are timed in three interleaved passes and compared by the median of
+those.  A candidate replaces
 the default plan of its class only when it is faster by more than
 ``--min-gain`` (5 % by default), so run-to-run noise does not move the table.
 Every adopted plan's result is compared against the default plan's result on
@@ -120,6 +122,18 @@ class Timer:
         return ms[len(ms) // 2] * 1e3
 
 
+def measure(timer, plans, M, N, K, rounds):
+    """Median time of each plan over `rounds` passes that each time every plan
+    once, so that a drift of the GPU's state during the sweep does not favour
+    the plans timed first."""
+    import statistics
+    samples = {p: [] for p in plans}
+    for _ in range(rounds):
+        for p in plans:
+            samples[p].append(timer.time(p, M, N, K))
+    return {p: statistics.median(v) for p, v in samples.items()}
+
+
 def dump_table(out):
     """JSON with one line per entry."""
     head = {k: v for k, v in out.items() if k != "entries"}
@@ -169,6 +183,7 @@ def main():
     ap = argparse.ArgumentParser(description="measure the tuning table")
     ap.add_argument("--classes", default="0-7", help="range of classes per extent, e.g. 3-6")
     ap.add_argument("--min-gain", type=float, default=0.05)
+    ap.add_argument("--rounds", type=int, default=3, help="interleaved timing passes per class")
     ap.add_argument("--dry-run", action="store_true", help="measure and print, write nothing")
     ap.add_argument("--out-dir", default=None,
                     help="write tuning_table.json and sgemm_tuning_table.inc here instead of "
@@ -199,18 +214,15 @@ def main():
             for kc in range(lo, hi + 1):
                 M, N, K = CLASS_BOUNDS[mc], CLASS_BOUNDS[nc], CLASS_BOUNDS[kc]
                 d = default_plan(M, N)
-                t_def = timer.time(d, M, N, K)
-                results = {d: t_def}
-                for plan in candidates(M, N, K):
-                    if plan not in results:
-                        results[plan] = timer.time(plan, M, N, K)
+                plans = [d] + [c for c in candidates(M, N, K) if c != d]
+                results = measure(timer, plans, M, N, K, args.rounds)
                 best = min(results, key=results.get)
                 if tiles_of(best[0], M, N) * best[2] >= 256:
-                    for gm in GROUPS:
-                        plan = (best[0], gm, best[2])
-                        if plan not in results:
-                            results[plan] = timer.time(plan, M, N, K)
+                    extra = [(best[0], gm, best[2]) for gm in GROUPS if (best[0], gm, best[2]) not in results]
+                    if extra:
+                        results.update(measure(timer, [d, best] + extra, M, N, K, args.rounds))
                     best = min(results, key=results.get)
+                t_def = results[d]
                 if results[best] > t_def * (1 - args.min_gain):
                     best = d
                 # The adopted plan must give the default plan's values (up to
