@@ -12,6 +12,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import workloads
 from gpu_helpers import (check_full, check_row_col_sums, check_sampled, run_lib,
                          sample_positions, say)
@@ -292,3 +293,63 @@ def test_workload_integer_bitexact_sampled(sg, name):
     rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
     ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols, exact=True)
     assert ok, info
+
+
+# ---------------------------------------------------------------------------
+# Degenerate and limit cases.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("variant", ["auto", "mfma_scalar", "valu", "skinny"])
+def test_nan_and_inf_propagate(sg, variant):
+    """IEEE propagation: a NaN row of A makes that row of C NaN, an infinite
+    column of B (with nonzero A entries of both signs) makes that column of C
+    non-finite; every other entry is unaffected and within the bound."""
+    M = 9 if variant == "skinny" else 140
+    N, K = 70, 33
+    A, B, C0 = _inputs(M, N, K, "uniform", 60)
+    A = A.copy(); B = B.copy()
+    A[3, :] = np.nan
+    B[:, 5] = np.inf
+    st, C, _ = run_lib(sg, VID[variant], A, B, C0, 1.0, 0.5)
+    assert st == 0
+    assert np.all(np.isnan(C[3, :]))
+    assert not np.any(np.isfinite(C[:, 5]))
+    keep_r = np.array([i for i in range(M) if i != 3])
+    keep_c = np.array([j for j in range(N) if j != 5])
+    Cref, absab = oracle.sgemm_ref(A, B, 1.0, 0.5, C0)
+    sub = np.ix_(keep_r, keep_c)
+    ok, info = oracle.check_within_bound(C[sub], Cref[sub], oracle.error_bound(absab[sub], 1.0, 0.5, C0[sub]))
+    assert ok, info
+
+
+def test_leading_dimension_past_32bit_offsets(sg):
+    """lda so large that 128 rows of A span more than 2 GiB: the 16-byte-load
+    kernels cannot address a slice with 32-bit offsets, the automatic choice
+    falls back to the 4-byte-load kernel, and the forced vector variants
+    refuse."""
+    M, N, K = 130, 70, 60
+    lda = (1 << 31) // 4 // 127 + 8          # multiple of 4, 127 * lda * 4 > 2^31
+    A, B, C0 = _inputs(M, N, K, "int4", 61)
+    assert sg.sgemm_f32_select(M, N, K, 1.0, 0x100000, lda, 0x100000, N) == sg.MFMA_SCALAR
+    say(f"[huge_lda] lda={lda} ({M * lda * 4 / 2**30:.2f} GiB for A)")
+    st, C, _ = run_lib(sg, 0, A, B, C0, 1.0, 1.0, lda=lda)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.0, 1.0, C0, exact=True)
+    assert ok, info
+    st, _, _ = run_lib(sg, VID["mfma_large"], A, B, C0, 1.0, 1.0, lda=lda)
+    assert st == sg.ERR_NOT_APPLICABLE
+    torch.cuda.empty_cache()
+
+
+def test_c_leading_dimension_past_32bit_offsets(sg):
+    """ldc so large that 128 rows of C span more than 2 GiB: edge tiles write C
+    through guarded pointers instead of a buffer resource."""
+    M, N, K = 130, 70, 64
+    ldc = (1 << 31) // 4 // 127 + 8
+    A, B, C0 = _inputs(M, N, K, "int4", 62)
+    say(f"[huge_ldc] ldc={ldc} ({M * ldc * 4 / 2**30:.2f} GiB for C)")
+    st, C, Cbuf = run_lib(sg, VID["mfma_large"], A, B, C0, 1.0, -1.0, ldc=ldc)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.0, -1.0, C0, exact=True)
+    assert ok, info
+    del Cbuf
+    torch.cuda.empty_cache()
