@@ -1,12 +1,13 @@
-// Workspace for kernels that need one (the split reduction of the M <= 16
-// kernel).  The library keeps one workspace per (device, stream): work on one
-// stream runs in order, so successive calls on a stream can reuse the same
-// memory without further synchronisation, while calls on different streams
-// never share it.  A stream's workspace is allocated on its first use and
-// grown when a call needs more (growing waits for the stream's pending work
-// before freeing the old block); it is held until the process ends.  A new
-// block starts zero-filled, and kernels that keep counters in it leave them at
-// zero when they finish.
+// Workspace for kernels that need one (split partial sums of the M <= 16
+// kernel, of split-K and stream-K plans, and the packed operands of the
+// 16-bit-input GEMM).  The library keeps one workspace per (device, stream):
+// work on one stream runs in order, so successive calls on a stream can reuse
+// the same memory without further synchronisation, while calls on different
+// streams never share it.  A stream's workspace is allocated on its first use
+// and grown when a call needs more (growing waits for the stream's pending
+// work before freeing the old block); it is held until the process ends.
+// Every kernel writes the part of the workspace it later reads, so the memory
+// is not cleared.
 #include <cstdint>
 #include <mutex>
 #include <vector>
@@ -56,11 +57,6 @@ hipError_t stream_workspace(size_t bytes, hipStream_t stream, void **out) {
     void *p = nullptr;
     e = hipMalloc(&p, want);
     if (e != hipSuccess) return e;
-    e = hipMemset(p, 0, want);
-    if (e != hipSuccess) {
-        hipFree(p);
-        return e;
-    }
     if (slot == nullptr) {
         g_entries.push_back(Entry{dev, stream, p, want});
     } else {
