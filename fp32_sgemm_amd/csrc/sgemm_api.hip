@@ -6,7 +6,6 @@
 // kernels ("Learn: Optimizing GEMM", section 8; "Writing a Fast Matmul in CUDA,
 // Step by Step", section "In the real world"); this library picks among its own
 // few kernels by shape and operand alignment, on the host, before one launch.
-#include <cmath>
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -111,40 +110,43 @@ Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const f
 // Wave quantization of the 128x128 grid.  About kResidentLargeTiles of its
 // work-groups are resident at once (two per compute unit on the 256 compute
 // units of MI355X), so a grid of T tiles runs ceil(T / 512) rounds, the last
-// possibly far from full.  The persistent stream-K configuration removes that
-// idle time at a cost of its own (pipeline restarts and partial tiles written,
-// re-read and added by a second kernel), which weighs less as K, the work per
-// tile, grows.  It takes the plan over when the idle part of the rounds,
-// rounds - load with load = (M/128)(N/128)/512 counting edge tiles by their
-// area, exceeds that cost, modelled as 0.9 * sqrt(1000 / K) rounds plus a
-// margin of 0.05.  The model is fitted to per-launch timings on MI355X
-// (TFLOP/s, grid -> stream-K): 3000^3 98.8 -> 121.1 and 3500^3 101.5 -> 121.9
-// (taken), 5000 x 5000 x 1000 110.1 -> 112.8 (taken), 2900 x 4100 x 2048 128.2
-// -> 118.7, 4096 x 11008 x 512 113.0 -> 111.3 and 6144 x 6144 x 2048 140.4 ->
-// 135.7 (not taken).  The table's classes cannot express it: the idle part
-// depends on the exact extents, not on their octaves.
+// possibly far from full.  When the tiles fill less than kFillBelow of their
+// rounds, the plan moves to 64x64 tiles with two slices in flight (four
+// times the tiles, four resident per compute unit, a last round that costs
+// far less).  Per-launch timings on MI355X (TFLOP/s, 128x128 -> 64x64 two
+// slices ahead, group 8; fill of the 128x128 rounds in brackets): 3000^3
+// (0.56) 100.4 -> 128.8, 3072^3 (0.56) 106.9 -> 135.7, 3500^3 (0.77) 103.1
+// -> 131.0, 5000 x 5000 x 1000 (0.78) 113.9 -> 122.6, 5120 x 5120 x 2048
+// (0.78) 128.1 -> 136.8, 4608 x 4608 x 2048 (0.84) 120.4 -> 133.7, 7168 x 7168
+// x 1024 (0.88) 131.1 -> 135.3; and the other way: 4096 x 11008 x 512 (0.90)
+// 125.3 / 126.9, 6144 x 6144 x 2048 (0.90) 142.7 / 138.3, 10240 x 10240 x 1024
+// (0.96) 139.1 / 136.1, 4096^3 (1.0) 143.1 / 139.4.  The persistent stream-K
+// configuration was slower than the 64x64 tiles on every one of these shapes
+// (e.g. 3000^3 124.1, 5000 x 5000 x 1000 115.8), so it is not chosen
+// automatically.  The table's octave classes cannot express this: the fill
+// depends on the exact tile count.
 constexpr int kResidentLargeTiles = 512;
+constexpr double kFillBelow = 0.88;
 
-bool stream_k_pays(int M, int N, int K) {
+bool rounds_poorly_filled(int M, int N) {
     const int64_t tiles = sgemm::mfma_config_tiles(0, M, N);
-    if (tiles <= kResidentLargeTiles || K <= 0) return false;
-    const double rounds = (double)((tiles + kResidentLargeTiles - 1) / kResidentLargeTiles);
-    const double load = (M / 128.0) * (N / 128.0) / kResidentLargeTiles;
-    const double cost = 0.9 * std::sqrt(1000.0 / K);
-    return rounds - load > cost + 0.05;
+    if (tiles <= kResidentLargeTiles) return false;
+    const int64_t rounds = (tiles + kResidentLargeTiles - 1) / kResidentLargeTiles;
+    return (double)tiles < kFillBelow * (double)(rounds * kResidentLargeTiles);
 }
 
 Plan quantization_plan(const Plan &p, int M, int N, int K) {
+    (void)K;
     if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
         return p;
-    if (!stream_k_pays(M, N, K)) return p;
-    return Plan{SGEMM_F32_MFMA_TUNED, 5, p.group_m, 1};
+    if (!rounds_poorly_filled(M, N)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 4, 8, 1};
 }
 
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
-// shape class when there is one, then the stream-K switch for 128x128 grids
-// that fill their last round poorly (reported as SGEMM_F32_MFMA_TUNED when the
+// shape class when there is one, then the switch to 64x64 tiles for 128x128
+// grids that fill their rounds poorly (reported as SGEMM_F32_MFMA_TUNED when the
 // plan differs from the default).  Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);

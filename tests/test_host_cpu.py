@@ -182,20 +182,24 @@ def test_config_and_plan_argument_errors_without_touching_the_gpu(sg):
     assert sg.sgemm_f32_ex_plan(0, 0, 4, 4, 0, 1.0, p, 4, p, 4) == (0, 0, 0, 0, 0)
 
 
-def test_stream_k_for_poorly_filled_rounds(sg):
-    """128x128 grids whose idle share of their rounds of 512 resident
-    work-groups exceeds the modelled stream-K cost 0.9*sqrt(1000/K) + 0.05
-    take the persistent stream-K configuration."""
+def test_small_tiles_for_poorly_filled_rounds(sg):
+    """128x128 grids of more than 512 tiles that fill less than 0.88 of their
+    rounds of 512 resident work-groups move to 64x64 tiles with two slices in
+    flight; well-filled grids keep 128x128."""
     al = 0x100000
     plan = lambda M, N, K, ta=0, tb=0: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, M if ta else K, al,
                                                             K if tb else N)
-    for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000)]:
-        assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_STREAMK), shape
-    assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_STREAMK)
+    for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
+                  (7168, 7168, 1024)]:
+        assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
+    assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092), (6144, 6144, 2048),
-                  (2900, 4100, 2048), (4096, 11008, 512), (2048, 2048, 2048)]:
+                  (4096, 11008, 512), (10240, 10240, 1024)]:
+        assert plan(*shape)[2] == sg.CFG_128x128, shape
+    # The persistent stream-K configuration is never chosen automatically.
+    for shape in [(3000, 3000, 3000), (2900, 4100, 2048), (5000, 5000, 1000)]:
         assert plan(*shape)[2] != sg.CFG_128x128_STREAMK, shape
-    # 4-byte loads never take it.
+    # 4-byte loads keep their kernel.
     st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 3000, 3000, 3001, 1.0, al, 3001, al, 3000)
     assert (v, cfg) == (sg.MFMA_SCALAR, 0)
 
@@ -227,8 +231,8 @@ def test_plan_follows_the_tuning_table(sg):
             assert v == sg.SKINNY
             continue
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
-        if cfg == sg.CFG_128x128_STREAMK and e["config"] == 0:
-            continue        # the stream-K switch for poorly filled rounds
+        if cfg == sg.CFG_64x64_PF2 and e["config"] == 0:
+            continue        # the switch to 64x64 tiles for poorly filled rounds
         assert (cfg, gm) == (e["config"], e["group_m"]), e
         k_per = -(-K // e["splits"])
         k_per = -(-k_per // 32) * 32
