@@ -364,6 +364,48 @@ __device__ __forceinline__ void compute_slice(const float *stage, int wm, int wn
     compute_slice<T>(stage, wm, wn, lane, acc, NoIssue());
 }
 
+// As compute_slice, with the MFMAs of each slice's last chunk held back: on
+// entry f[1] holds the previous slice's last chunk (zeros before the first
+// slice), whose MFMAs run right after this slice's first LDS reads are issued,
+// so that the matrix cores stay busy while those reads are in flight (after
+// the barrier that precedes every slice); on return f[1] holds this slice's
+// last chunk, not yet multiplied.  The caller runs it after the last slice.
+template <class T, class Issue>
+__device__ __forceinline__ void compute_slice_held(const float *stage, int wm, int wn, int lane,
+                                                   f32x16 (&acc)[T::MB][T::NB], const Issue &issue,
+                                                   Frag<T> (&f)[2]) {
+    const int h = lane >> 5;
+    const int l32 = lane & 31;
+    const float *As = panel_lane<typename T::PA>(stage, wm * T::WM, l32, h);
+    const float *Bs = panel_lane<typename T::PB>(stage + T::A_STAGE, wn * T::WN, l32, h);
+    constexpr int CH = T::HALF / 4;
+    static_assert(CH % 2 == 0, "held chunk must land in f[1]");
+    read_frag<T>(As, Bs, 0, f[0]);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_frag<T>(f[1], acc);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+        issue(c);
+        if (c + 1 < CH) {
+            read_frag<T>(As, Bs, c + 1, f[(c + 1) & 1]);
+            __builtin_amdgcn_sched_barrier(0);
+            mfma_frag<T>(f[c & 1], acc);
+        }
+    }
+}
+
+template <class T>
+__device__ __forceinline__ void zero_frag(Frag<T> &f) {
+#pragma unroll
+    for (int b = 0; b < T::MB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.a[b][e] = 0.f;
+#pragma unroll
+    for (int b = 0; b < T::NB; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f.b[b][e] = 0.f;
+}
+
 // The K loop of one tile.  Slices are processed in the order: the partial
 // slice at the K edge first (when K is not a multiple of BK), then the full
 // slices from k = 0 up, so only the first slice ever needs the K guard.
@@ -380,18 +422,34 @@ __device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int ti
     auto k0_of = [&](int idx) { return (idx - shift) * T::BK; };
 
     if (T::PF == 1) {
+        // One register set: slice t+1 is loaded during slice t's MFMAs and
+        // stored into the other LDS stage after them.
         float4 ra[T::A_VECS], rb[T::B_VECS];
         if (tail) load_slice<T, VEC, GMN, true>(g, s, m0, n0, nkf * T::BK, ra, rb);
         else load_slice<T, VEC, GMN, false>(g, s, m0, n0, 0, ra, rb);
         store_slice<T>(smem, tid, ra, rb);
         __syncthreads();
+        if (nk == 1) {
+            compute_slice<T>(smem, wm, wn, lane, acc);
+            return;
+        }
+        constexpr int PARTS = T::A_VECS + T::B_VECS;
+        constexpr int PER = (PARTS + T::HALF / 4 - 1) / (T::HALF / 4);   // groups per chunk
+        Frag<T> f[2];
+        zero_frag<T>(f[1]);
         for (int t = 0; t < nk; ++t) {
-            const bool more = t + 1 < nk;
-            if (more) load_slice<T, VEC, GMN, false>(g, s, m0, n0, k0_of(t + 1), ra, rb);
-            compute_slice<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc);
-            if (more) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
+            // Past the end the last slice is loaded again and never stored.
+            const int k1 = k0_of(t + 1 < nk ? t + 1 : nk - 1);
+            const SliceRsrc r1 = slice_rsrc<T>(g, m0, n0, k1);
+            compute_slice_held<T>(smem + (t & 1) * T::STAGE, wm, wn, lane, acc, [&](int c) {
+#pragma unroll
+                for (int j = 0; j < PER; ++j)
+                    if (c * PER + j < PARTS) load_part<T, VEC, GMN, false>(g, s, m0, n0, k1, r1, c * PER + j, ra, rb);
+            }, f);
+            if (t + 1 < nk) store_slice<T>(smem + ((t + 1) & 1) * T::STAGE, tid, ra, rb);
             __syncthreads();
         }
+        mfma_frag<T>(f[1], acc);
     } else {
         // Two register sets: while slice t is computed from LDS, slice t+1
         // waits in registers for its LDS buffer and slice t+2 is in flight.
@@ -404,31 +462,34 @@ __device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int ti
         int t = 0;
         constexpr int PARTS = T::A_VECS + T::B_VECS;
         constexpr int PER = (PARTS + T::HALF / 4 - 1) / (T::HALF / 4);   // groups per chunk
+        Frag<T> f[2];
+        zero_frag<T>(f[1]);
         // The loads are unconditional: past the end they re-read the last slice
         // (never stored), so the wait counts stay exact on every path.
         for (; t + 1 < nk; t += 2) {
             const int k2 = k0_of(t + 2 < nk ? t + 2 : nk - 1);
             const SliceRsrc r2 = slice_rsrc<T>(g, m0, n0, k2);
-            compute_slice<T>(smem, wm, wn, lane, acc, [&](int c) {
+            compute_slice_held<T>(smem, wm, wn, lane, acc, [&](int c) {
 #pragma unroll
                 for (int j = 0; j < PER; ++j)
                     if (c * PER + j < PARTS)
                         load_part<T, VEC, GMN, false>(g, s, m0, n0, k2, r2, c * PER + j, ra0, rb0);
-            });
+            }, f);
             store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
             __syncthreads();
             const int k3 = k0_of(t + 3 < nk ? t + 3 : nk - 1);
             const SliceRsrc r3 = slice_rsrc<T>(g, m0, n0, k3);
-            compute_slice<T>(smem + T::STAGE, wm, wn, lane, acc, [&](int c) {
+            compute_slice_held<T>(smem + T::STAGE, wm, wn, lane, acc, [&](int c) {
 #pragma unroll
                 for (int j = 0; j < PER; ++j)
                     if (c * PER + j < PARTS)
                         load_part<T, VEC, GMN, false>(g, s, m0, n0, k3, r3, c * PER + j, ra1, rb1);
-            });
+            }, f);
             if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
             __syncthreads();
         }
-        if (t < nk) compute_slice<T>(smem, wm, wn, lane, acc);
+        if (t < nk) compute_slice_held<T>(smem, wm, wn, lane, acc, NoIssue(), f);
+        mfma_frag<T>(f[1], acc);
     }
 }
 
