@@ -16,6 +16,10 @@ Fast Matmul in CUDA, Step by Step", section "Step 1").
 
 The CPU baseline is the float64 oracle timed on the host's cores on a bounded
 sample of the same product (its first rows), reported beside the GPU number.
+As context (not the product), the same product on the same inputs and stream
+through rocBLAS ``sgemm`` and through torch's FP32 ``addmm`` (hipBLASLt), and
+the GPU's shader clock read with amd-smi while the kernel runs, which gives the
+clock-adjusted FP32 peak (256 CUs x 256 FLOP per clock x clock).
 """
 from __future__ import annotations
 
@@ -82,6 +86,144 @@ def measured_traffic():
         return None
 
 
+# --- vendor libraries on the same GPU (context, not the product) ---------------------
+def _time_launches(torch, stream, call, steps, warmup):
+    """Mean and median per-launch duration (ms), each launch between its own
+    pair of events on `stream`."""
+    with torch.cuda.stream(stream):
+        for _ in range(warmup):
+            call()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for a, b in evs:
+            a.record(stream)
+            call()
+            b.record(stream)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream, steps, warmup):
+    """rocBLAS sgemm and torch's FP32 matmul (hipBLASLt) on the same product,
+    inputs and stream.  rocBLAS is column-major: the row-major product
+    C = op(A) op(B) is the column-major C^T = op(B)^T op(A)^T, so B is passed
+    first with its own transpose flag (rocBLAS operation 111 = none, 112 =
+    transpose).  Each library call takes the next of the B copies in turn, as
+    the timed steps do."""
+    import ctypes
+
+    flops = gemm_flops(w.M, w.N, w.K)
+    out = {}
+    dB = dBs[0]
+    turn = [0]
+
+    def next_b():
+        b = dBs[turn[0] % len(dBs)]
+        turn[0] += 1
+        return b
+    dC = (torch.from_numpy(C0).to(dA.device) if C0 is not None
+          else torch.zeros(w.M, w.N, device=dA.device))
+    try:
+        lib = ctypes.CDLL("librocblas.so")
+        handle = ctypes.c_void_p()
+        if lib.rocblas_create_handle(ctypes.byref(handle)) != 0:
+            raise RuntimeError("rocblas_create_handle failed")
+        lib.rocblas_set_stream(handle, ctypes.c_void_p(stream.cuda_stream))
+        i, p = ctypes.c_int, ctypes.c_void_p
+        lib.rocblas_sgemm.argtypes = [p, i, i, i, i, i, p, p, i, p, i, p, p, i]
+        al, be = ctypes.c_float(w.alpha), ctypes.c_float(w.beta)
+        op_a, op_b = (112 if ta else 111), (112 if tb else 111)
+
+        def roc():
+            st = lib.rocblas_sgemm(handle, op_b, op_a, w.N, w.M, w.K, ctypes.byref(al), next_b().data_ptr(), ldb,
+                                   dA.data_ptr(), lda, ctypes.byref(be), dC.data_ptr(), w.N)
+            if st != 0:
+                raise RuntimeError(f"rocblas_sgemm returned {st}")
+
+        mean, med = _time_launches(torch, stream, roc, steps, warmup)
+        # The operand mapping is checked once: rocBLAS with beta 0 against
+        # torch's product of the same views.
+        z = ctypes.c_float(0.0)
+        with torch.cuda.stream(stream):
+            lib.rocblas_sgemm(handle, op_b, op_a, w.N, w.M, w.K, ctypes.byref(al), dB.data_ptr(), ldb,
+                              dA.data_ptr(), lda, ctypes.byref(z), dC.data_ptr(), w.N)
+            ref = w.alpha * ((dA.t() if ta else dA) @ (dB.t() if tb else dB))
+        torch.cuda.synchronize()
+        agree = bool(((dC - ref).abs().max() <= 1e-3 * ref.abs().max().clamp_min(1e-30)).item())
+        lib.rocblas_destroy_handle(handle)
+        out["rocblas_sgemm"] = {"value": round(flops / mean / 1e9, 3), "median_launch": round(flops / med / 1e9, 3),
+                                "unit": "TFLOP/s", "kernel_avg_ms": round(mean, 5), "same_product": agree}
+        del ref
+    except (OSError, AttributeError, RuntimeError) as e:
+        out["rocblas_sgemm"] = {"error": str(e)}
+    Aop = dA.t() if ta else dA
+    torch.backends.cuda.matmul.allow_tf32 = False
+
+    def tm():
+        b = next_b()
+        dC.addmm_(Aop, b.t() if tb else b, beta=w.beta, alpha=w.alpha)
+
+    mean, med = _time_launches(torch, stream, tm, steps, warmup)
+    out["torch_addmm"] = {"value": round(flops / mean / 1e9, 3), "median_launch": round(flops / med / 1e9, 3),
+                          "unit": "TFLOP/s", "kernel_avg_ms": round(mean, 5)}
+    return out
+
+
+def gfx_clock_mhz(torch, step, stream, kern_s):
+    """Shader clock of the GPU while the benchmarked kernel runs back to back:
+    a second thread keeps launching it for about 2 s while amd-smi reads the
+    current clock of each XCD after 1.2 s and 1.6 s (its figure lags the
+    hardware by up to about a second).  Returns (mean MHz over XCDs and
+    readings, the readings) or (None, reason)."""
+    import shutil
+    import subprocess
+    import threading
+
+    tool = shutil.which("amd-smi")
+    if tool is None:
+        return None, "amd-smi not found"
+    stop = threading.Event()
+    batch = int(min(1000, max(1, 0.01 / max(kern_s, 1e-6))))
+
+    def feeder():
+        while not stop.is_set():
+            for _ in range(batch):
+                step()
+            stream.synchronize()
+
+    th = threading.Thread(target=feeder, daemon=True)
+    readings, err = [], None
+    t_start = time.perf_counter()
+    th.start()
+    try:
+        for at in (1.2, 1.6):
+            time.sleep(max(0.0, at - (time.perf_counter() - t_start)))
+            p = subprocess.run([tool, "metric", "-g", "0", "-c", "--json"], capture_output=True, text=True,
+                               timeout=30)
+            d = json.loads(p.stdout)
+            g = d[0] if isinstance(d, list) else d
+            if isinstance(g, dict) and "gpu_data" in g:
+                g = g["gpu_data"][0]
+            clk = g["clock"]
+            vals = [v["clk"]["value"] for k, v in clk.items()
+                    if k.startswith("gfx") and isinstance(v, dict) and isinstance(v.get("clk"), dict)]
+            if vals:
+                readings.append(vals)
+    except (subprocess.SubprocessError, ValueError, KeyError, IndexError, TypeError) as e:
+        err = f"amd-smi: {e}"
+    stop.set()
+    th.join()
+    torch.cuda.synchronize()
+    if err is not None:
+        return None, err
+    if not readings:
+        return None, "no gfx clock in amd-smi output"
+    flat = [v for r in readings for v in r]
+    return sum(flat) / len(flat), readings
+
+
 # --- CPU baseline (the oracle on a bounded sample) -----------------------------------
 def cpu_baseline(A, B, C0, alpha, beta, target_s: float):
     import oracle
@@ -129,6 +271,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-context", action="store_true",
+                    help="skip the rocBLAS / torch timings and the clock reading")
     ap.add_argument("--rotate", type=int, default=1, metavar="COPIES",
                     help="cycle the steps over this many copies of B (with 5 or more, the "
                          "copies exceed the 256 MB Infinity Cache for the skinny workload)")
@@ -284,6 +428,19 @@ def main():
                    "b_copies": len(dBs), "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    if not args.no_context:
+        mhz, readings = gfx_clock_mhz(torch, step, stream, kern_avg_s)
+        if mhz is not None:
+            # 256 CUs x 4 matrix-core SIMDs x 64 FP32 FLOP per clock each.
+            adj = 256 * 256 * mhz * 1e6 / 1e12
+            out["clock"] = {"gfx_mhz": round(mhz, 1), "clock_adjusted_fp32_peak": round(adj, 2),
+                            "frac_of_clock_adjusted_peak": None if kind16 else round(achieved / adj, 4),
+                            "readings": readings}
+        else:
+            out["clock"] = {"gfx_mhz": None, "note": readings}
+        if not kind16:
+            out["context"] = library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream,
+                                             min(args.steps, 50), 5)
     if not args.no_cpu_baseline and not kind16:
         out["cpu_baseline"] = cpu_baseline(A, B, C0, w.alpha, w.beta, args.cpu_seconds)
     print(json.dumps(out), flush=True)
