@@ -34,7 +34,8 @@ CFG_128x64 = 2
 CFG_64x128 = 3
 CFG_64x64_PF2 = 4
 CFG_128x128_STREAMK = 5
-NUM_CONFIGS = 6
+CFG_64x64_BK64 = 6
+NUM_CONFIGS = 7
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

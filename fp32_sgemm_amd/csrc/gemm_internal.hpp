@@ -34,7 +34,7 @@ hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stre
 // only.  `group_m` is the number of tile rows walked together by the tile
 // order; `splits` divides K over work-groups (the partial sums go through the
 // stream's workspace and a reduction kernel; not with configuration 5).
-constexpr int kNumMfmaConfigs = 6;
+constexpr int kNumMfmaConfigs = 7;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
 int64_t mfma_config_tiles(int config, int M, int N);

@@ -48,6 +48,15 @@ bool slice_fits(bool k_major, int ld) {
     return span * 4 < limit;
 }
 
+// Configuration 6 stages slices of 64 values of k: an operand stored along M
+// or N then spans 64 stored rows per slice.
+bool config_fits(int config, int ta, int tb, int lda, int ldb) {
+    if (config != 6) return true;
+    const int64_t limit = (int64_t)1 << 31;
+    auto fits = [&](int64_t ld) { return (63 * ld + 128) * 4 < limit; };
+    return fits(lda) && fits(ldb);
+}
+
 bool vec_aligned(int ta, int tb, const float *A, int lda, const float *B, int ldb) {
     const bool aligned = (reinterpret_cast<uintptr_t>(A) % 16 == 0) &&
                          (reinterpret_cast<uintptr_t>(B) % 16 == 0) && (lda % 4 == 0) && (ldb % 4 == 0);
@@ -104,7 +113,11 @@ Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const f
         return Plan{SGEMM_F32_SKINNY, 0, 0, 0};
     const int config = prefer_small_tiles(M, N) ? 1 : 0;
     if (!vec_aligned(ta, tb, A, lda, B, ldb)) return Plan{SGEMM_F32_MFMA_SCALAR, config, 8, 1};
-    return Plan{config ? SGEMM_F32_MFMA_SMALL : SGEMM_F32_MFMA_LARGE, config, 8, 1};
+    // With 16-byte loads the small tile keeps two slices in flight
+    // (configuration 4): one work-group per compute unit or fewer leaves the
+    // memory latency to the pipeline alone.
+    if (config) return Plan{SGEMM_F32_MFMA_TUNED, 4, 8, 1};
+    return Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
 }
 
 // Wave quantization of the 128x128 grid.  About kResidentLargeTiles of its
@@ -150,10 +163,11 @@ Plan quantization_plan(const Plan &p, int M, int N, int K) {
 // plan differs from the default).  Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
-    if (d.variant != SGEMM_F32_MFMA_LARGE && d.variant != SGEMM_F32_MFMA_SMALL) return d;
+    if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
     if (!kHaveTunedTable) return quantization_plan(d, M, N, K);
     const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
-    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1)
+    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1 ||
+        !config_fits(e.config, ta, tb, lda, ldb))
         return quantization_plan(d, M, N, K);
     int k_per = 0;
     int splits = sgemm::mfma_effective_splits(K, e.splits, &k_per);
@@ -170,6 +184,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 // One MFMA launch (plus the split reduction) after its plan is known.
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
+    if (!config_fits(config, g.trans_a, g.trans_b, g.lda, g.ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
     const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
     if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
@@ -319,6 +334,7 @@ const char *sgemm_f32_config_name(int config) {
         case 3: return "64x128";
         case 4: return "64x64_pf2";
         case 5: return "128x128_streamk";
+        case 6: return "64x64_bk64";
         default: return nullptr;
     }
 }

@@ -804,9 +804,14 @@ template <int LA, int LB>
 using WideTile = MfmaTile<64, 128, 32, 32, 64, 2, LA, LB>;
 template <int LA, int LB>
 using SmallTile2 = MfmaTile<64, 64, 32, 32, 32, 2, LA, LB>;
+// 64x64 with slices of 64: twice the MFMA work per slice, so the two slices in
+// flight cover twice the memory latency (grids of at most one work-group per
+// compute unit, where no other work-group hides it).
+template <int LA, int LB>
+using SmallTileK64 = MfmaTile<64, 64, 64, 32, 32, 2, LA, LB>;
 
-constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128};
-constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128};
+constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128, 64};
+constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128, 64};
 constexpr int kTileBK = 32;
 
 template <class T, bool VEC>
@@ -900,6 +905,7 @@ hipError_t launch_layouts(const GemmArgs &g, int config, bool vec, int group_m, 
         case 3: return launch_one<WideTile<LA, LB>, true>(g, group_m, sk, stream);
         case 4: return launch_one<SmallTile2<LA, LB>, true>(g, group_m, sk, stream);
         case 5: return launch_streamk<LargeTile<LA, LB>>(g, group_m, stream);
+        case 6: return launch_one<SmallTileK64<LA, LB>, true>(g, group_m, sk, stream);
         default: return hipErrorInvalidValue;
     }
 }

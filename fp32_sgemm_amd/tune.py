@@ -48,15 +48,19 @@ TABLE_INC = os.path.join(HERE, "csrc", "sgemm_tuning_table.inc")
 
 def default_plan(M, N):
     """The library's choice without a table: 128x128 tiles unless they give
-    fewer than 256 tiles, then 64x64; group 8; no split."""
+    fewer than 256 tiles, then 64x64 with two slices in flight; group 8; no
+    split."""
     tiles = -(-M // 128) * -(-N // 128)
-    return (0 if tiles >= 256 else 1, 8, 1)
+    return (0 if tiles >= 256 else 4, 8, 1)
+
+
+NUM_CONFIGS = 7
+TILE_BM = {0: 128, 1: 64, 2: 128, 3: 64, 4: 64, 5: 128, 6: 64}
+TILE_BN = {0: 128, 1: 64, 2: 64, 3: 128, 4: 64, 5: 128, 6: 64}
 
 
 def tiles_of(config, M, N):
-    bm = {0: 128, 1: 64, 2: 128, 3: 64, 4: 64, 5: 128}[config]
-    bn = {0: 128, 1: 64, 2: 64, 3: 128, 4: 64, 5: 128}[config]
-    return -(-M // bm) * -(-N // bn)
+    return -(-M // TILE_BM[config]) * -(-N // TILE_BN[config])
 
 
 def effective_splits(K, s):
@@ -67,7 +71,7 @@ def effective_splits(K, s):
 
 def candidates(M, N, K):
     out = []
-    for cfg in range(6):
+    for cfg in range(NUM_CONFIGS):
         tiles = tiles_of(cfg, M, N)
         for s in SPLITS:
             if cfg == 5 and s > 1:

@@ -87,7 +87,8 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
     SGEMM_F32_SKINNY = 4,         /* M <= 16: FP32 MFMA streaming kernel */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
-    SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the tuning table's plan (16-byte loads) */
+    SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's, or
+                                     64x64 tiles with two slices in flight (16-byte loads) */
     SGEMM_F32_NUM_VARIANTS = 7
 };
 
@@ -99,7 +100,8 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_64x128 = 3,     /* 16-byte loads only */
     SGEMM_F32_CFG_64x64_PF2 = 4,  /* 64x64, two slices in flight; 16-byte loads only */
     SGEMM_F32_CFG_128x128_STREAMK = 5, /* 128x128, persistent with stream-K; 16-byte loads only */
-    SGEMM_F32_NUM_CONFIGS = 6
+    SGEMM_F32_CFG_64x64_BK64 = 6, /* 64x64, slices of 64, two in flight; 16-byte loads only */
+    SGEMM_F32_NUM_CONFIGS = 7
 };
 
 /*
@@ -196,9 +198,12 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  *
  * sgemm_f32_ex_config: runs one MFMA configuration with the given grouping
  * (1..64 tile rows) and requested split count (1..64; K is cut into extents
- * that are multiples of 32, so fewer splits may run).  Configurations 2-5 need
+ * that are multiples of 32, so fewer splits may run).  Configurations 2-6 need
  * the 16-byte-load conditions of SGEMM_F32_MFMA_LARGE and return
  * SGEMM_F32_ERR_NOT_APPLICABLE otherwise; 0 and 1 fall back to 4-byte loads.
+ * Configuration 6 stages 64 values of k per slice, so it also needs 64 stored
+ * rows of each operand to span less than 2 GiB (SGEMM_F32_ERR_NOT_APPLICABLE
+ * otherwise; the automatic choice then keeps its default plan).
  *
  * Configuration 5 is persistent and tile-scheduled: as many work-groups as fit
  * on the device at once take whole tiles in rounds, then equal shares of the

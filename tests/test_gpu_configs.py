@@ -59,10 +59,12 @@ def check(C, As, Bs, ta, tb, alpha, beta, C0, exact):
 
 
 SHAPES = [(129, 127, 65), (300, 260, 700), (64, 64, 32), (257, 129, 1000), (130, 70, 9), (65, 200, 333)]
+# Grid configurations (5, the persistent one, has tests of its own below).
+GRID_CFGS = [0, 1, 2, 3, 4, 6]
 
 
 @pytest.mark.parametrize("splits", [1, 2, 5])
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg", GRID_CFGS)
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("shape", SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SHAPES])
 def test_config_real(sg, cfg, splits, form, shape):
@@ -77,7 +79,7 @@ def test_config_real(sg, cfg, splits, form, shape):
 
 
 @pytest.mark.parametrize("splits", [1, 3])
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg", GRID_CFGS)
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_config_integer_bitexact(sg, cfg, splits, form):
     """Integer-valued inputs are exact in FP32 in any summation order, so a
@@ -93,7 +95,7 @@ def test_config_integer_bitexact(sg, cfg, splits, form):
 
 
 @pytest.mark.parametrize("gm", [1, 3, 16, 64])
-@pytest.mark.parametrize("cfg", range(5))
+@pytest.mark.parametrize("cfg", GRID_CFGS)
 def test_tile_row_grouping(sg, cfg, gm):
     M, N, K = 1000, 900, 96
     say(f"[cfg_group] cfg={cfg} gm={gm}")

@@ -156,7 +156,7 @@ def test_variant_names_and_version(sg):
     assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar", "mfma_tuned"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
-    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk"]
+    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -180,6 +180,18 @@ def test_config_and_plan_argument_errors_without_touching_the_gpu(sg):
     assert sg.sgemm_f32_ex_plan(2, 0, 4, 4, 4, 1.0, p, 4, p, 4)[0] == sg.ERR_TRANS
     assert sg.sgemm_f32_ex_plan(0, 0, 4, -4, 4, 1.0, p, 4, p, 4)[0] == 2
     assert sg.sgemm_f32_ex_plan(0, 0, 4, 4, 0, 1.0, p, 4, p, 4) == (0, 0, 0, 0, 0)
+
+
+def test_config6_needs_64_rows_within_2gib(sg):
+    """Configuration 6 stages 64 values of k per slice: an operand stored along
+    N (B as given) whose 64 rows span 2 GiB or more is refused (no launch),
+    where the 32-row configurations still run."""
+    al = 0x100000
+    big_ldb = 10_000_000          # 31 rows fit in 2 GiB of offsets, 63 do not
+    st = sg.sgemm_f32_ex_config(6, 8, 1, 0, 0, 64, 64, 64, 1.0, al, 64, al, big_ldb, 0.0, al, 64, 0)
+    assert st == sg.ERR_NOT_APPLICABLE
+    st = sg.sgemm_f32_ex_config(6, 8, 1, 1, 0, 64, 64, 64, 1.0, al, big_ldb, al, 64, 0.0, al, 64, 0)
+    assert st == sg.ERR_NOT_APPLICABLE
 
 
 def test_small_tiles_for_poorly_filled_rounds(sg):
@@ -219,7 +231,8 @@ def test_plan_follows_the_tuning_table(sg):
         assert not os.path.exists(path)
         for shape in [(4096, 4096, 4096), (2048, 2048, 2048), (1024, 1024, 1024)]:
             st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, *shape, 1.0, al, shape[2], al, shape[1])
-            assert v in (sg.MFMA_LARGE, sg.MFMA_SMALL) and gm == 8 and sp == 1
+            assert (v, cfg) in ((sg.MFMA_LARGE, sg.CFG_128x128), (sg.MFMA_TUNED, sg.CFG_64x64_PF2))
+            assert gm == 8 and sp == 1
         return
     table = json.load(open(path))
     bounds = table["class_bounds"]
