@@ -133,17 +133,22 @@ Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const f
 // (0.78) 128.1 -> 136.8, 4608 x 4608 x 2048 (0.84) 120.4 -> 133.7, 7168 x 7168
 // x 1024 (0.88) 131.1 -> 135.3; and the other way: 4096 x 11008 x 512 (0.90)
 // 125.3 / 126.9, 6144 x 6144 x 2048 (0.90) 142.7 / 138.3, 10240 x 10240 x 1024
-// (0.96) 139.1 / 136.1, 4096^3 (1.0) 143.1 / 139.4.  The persistent stream-K
-// configuration was slower than the 64x64 tiles on every one of these shapes
-// (e.g. 3000^3 124.1, 5000 x 5000 x 1000 115.8), so it is not chosen
-// automatically.  The table's octave classes cannot express this: the fill
-// depends on the exact tile count.
+// (0.96) 139.1 / 136.1, 4096^3 (1.0) 143.1 / 139.4.  A single partial round
+// (256 to 511 tiles: some compute units run two work-groups, the others one)
+// costs as much as a full one: 2048 x 2560 x 2048 (0.63) 87 -> 123-129, 2304 x
+// 2304 x 4096 (0.63) 90 -> 119, 2048 x 3072 x 1024 (0.75) 100 -> 123-128,
+// 2560^3 (0.78) 109 -> 123, 2048^3 (0.5) 122-125 -> 127-130; 2816^3 (0.95)
+// 131.5 / 130.  The persistent stream-K configuration was slower than the
+// 64x64 tiles on the multi-round shapes (e.g. 3000^3 124.1, 5000 x 5000 x 1000
+// 115.8), so this rule does not choose it.  The table's octave classes cannot
+// express this: the fill depends on the exact tile count.
 constexpr int kResidentLargeTiles = 512;
 constexpr double kFillBelow = 0.88;
 
 bool rounds_poorly_filled(int M, int N) {
     const int64_t tiles = sgemm::mfma_config_tiles(0, M, N);
-    if (tiles <= kResidentLargeTiles) return false;
+    // Fewer than 256 tiles take the small tiles by default (prefer_small_tiles).
+    if (tiles < kResidentLargeTiles / 2) return false;
     const int64_t rounds = (tiles + kResidentLargeTiles - 1) / kResidentLargeTiles;
     return (double)tiles < kFillBelow * (double)(rounds * kResidentLargeTiles);
 }

@@ -195,18 +195,19 @@ def test_config6_needs_64_rows_within_2gib(sg):
 
 
 def test_small_tiles_for_poorly_filled_rounds(sg):
-    """128x128 grids of more than 512 tiles that fill less than 0.88 of their
-    rounds of 512 resident work-groups move to 64x64 tiles with two slices in
-    flight; well-filled grids keep 128x128."""
+    """128x128 grids of at least 256 tiles that fill less than 0.88 of their
+    rounds of 512 resident work-groups (a single partial round included) move
+    to 64x64 tiles with two slices in flight; well-filled grids keep 128x128."""
     al = 0x100000
     plan = lambda M, N, K, ta=0, tb=0: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, M if ta else K, al,
                                                             K if tb else N)
     for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
-                  (7168, 7168, 1024)]:
+                  (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
+                  (2560, 2560, 2560)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092), (6144, 6144, 2048),
-                  (4096, 11008, 512), (10240, 10240, 1024)]:
+                  (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128, shape
     # The persistent stream-K configuration is never chosen automatically.
     for shape in [(3000, 3000, 3000), (2900, 4100, 2048), (5000, 5000, 1000)]:
