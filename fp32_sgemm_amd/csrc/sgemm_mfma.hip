@@ -747,6 +747,29 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmArgs g, int tile
     }
 }
 
+// Sum of the partials ws[sp * total + t], sp = 0 .. splits-1, added in split
+// order.  The loads go out eight at a time before their additions (with a
+// run-time loop bound each addition would otherwise wait for its own load,
+// one memory round trip per split); indices past the last split re-read it
+// and are not added.
+template <class V>
+__device__ __forceinline__ V add_splits(const float *ws, int64_t total, int64_t t, int splits) {
+    constexpr int B = 8;
+    V sum = *reinterpret_cast<const V *>(ws + t);
+    for (int sp0 = 1; sp0 < splits; sp0 += B) {
+        V v[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            const int sp = sp0 + j < splits ? sp0 + j : splits - 1;
+            v[j] = *reinterpret_cast<const V *>(ws + sp * total + t);
+        }
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if (sp0 + j < splits) sum = sum + v[j];
+    }
+    return sum;
+}
+
 // C = alpha * (the split partials added in split order) + beta * C.  VEC4: N,
 // ldc and C allow 16-byte accesses, so each thread takes four columns.
 template <bool VEC4>
@@ -757,14 +780,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, const fl
     if (VEC4) {
         for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total / 4; q += stride) {
             const int64_t t = 4 * q;
-            float4 sum = *reinterpret_cast<const float4 *>(ws + t);
-            for (int sp = 1; sp < splits; ++sp) {
-                const float4 v = *reinterpret_cast<const float4 *>(ws + sp * total + t);
-                sum.x += v.x;
-                sum.y += v.y;
-                sum.z += v.z;
-                sum.w += v.w;
-            }
+            const float4 sum = add_splits<float4>(ws, total, t, splits);
             const int64_t i = t / g.N, j = t - i * g.N;
             float4 *p = reinterpret_cast<float4 *>(g.C + i * g.ldc + j);
             float4 r = make_float4(alpha * sum.x, alpha * sum.y, alpha * sum.z, alpha * sum.w);
@@ -777,8 +793,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g, const fl
         }
     } else {
         for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total; t += stride) {
-            float sum = ws[t];
-            for (int sp = 1; sp < splits; ++sp) sum += ws[sp * total + t];
+            const float sum = add_splits<float>(ws, total, t, splits);
             const int64_t i = t / g.N, j = t - i * g.N;
             float *p = g.C + i * g.ldc + j;
             float v = alpha * sum;

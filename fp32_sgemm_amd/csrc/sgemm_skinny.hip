@@ -197,13 +197,24 @@ __global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(SkinnyArgs sa, int 
     }
 }
 
-// C = alpha * (sum of the split partials, in split order) + beta * C.
+// C = alpha * (sum of the split partials, in split order) + beta * C.  The
+// partials' loads go out eight at a time before their additions (with a
+// run-time loop bound each addition would wait for its own load, one memory
+// round trip per split); indices past the last split re-read it and are not
+// added.
 __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, const float *ws, int splits) {
     const int64_t total = (int64_t)g.M * g.N;
     for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
          t += (int64_t)gridDim.x * blockDim.x) {
         float s = 0.f;
-        for (int sp = 0; sp < splits; ++sp) s += ws[sp * total + t];
+        for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = ws[(sp0 + j < splits ? sp0 + j : splits - 1) * total + t];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) s += v[j];
+        }
         const int64_t i = t / g.N, jj = t - i * g.N;
         float *p = g.C + i * g.ldc + jj;
         float v = g.alpha * s;
