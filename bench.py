@@ -270,6 +270,8 @@ def main():
                          "FP32 accumulation and C")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--plan", default=None, metavar="CONFIG[:GROUP[:SPLITS]]",
+                    help="run one MFMA plan through sgemm_f32_ex_config instead of the automatic choice")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the rocBLAS / torch timings and the clock reading")
@@ -337,7 +339,16 @@ def main():
                                                             lda, dB.data_ptr(), ldb)
 
     plan = None
-    if variant in (0, sg.MFMA_TUNED):
+    forced = None
+    if args.plan:
+        parts = [int(v) for v in args.plan.split(":")]
+        forced = (parts + [8, 1][len(parts) - 1:])[:3]
+        if kind16:
+            sys.exit("--plan applies to the FP32 path only")
+        chosen = sg.MFMA_TUNED
+        plan = {"config": sg.sgemm_f32_config_name(forced[0]), "group_m": forced[1], "splits": forced[2],
+                "forced": True}
+    elif variant in (0, sg.MFMA_TUNED):
         st, pv, pc, pg, ps = sg.sgemm_f32_ex_plan(ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
                                                   dB.data_ptr(), ldb)
         if st == 0 and pv not in (0, sg.SKINNY, sg.VALU):
@@ -350,6 +361,9 @@ def main():
         if kind16:
             st = sg.gemm16_f32(kind16, ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda, b.data_ptr(), ldb,
                                w.beta, dC.data_ptr(), ldc, s_handle)
+        elif forced is not None:
+            st = sg.sgemm_f32_ex_config(forced[0], forced[1], forced[2], ta, tb, w.M, w.N, w.K, w.alpha,
+                                        dA.data_ptr(), lda, b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
         elif ta or tb:
             st = sg.sgemm_f32_ex_variant(variant, ta, tb, w.M, w.N, w.K, w.alpha, dA.data_ptr(), lda,
                                          b.data_ptr(), ldb, w.beta, dC.data_ptr(), ldc, s_handle)
