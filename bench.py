@@ -59,11 +59,16 @@ def arithmetic_intensity(M: int, N: int, K: int, reads_c: bool) -> float:
     return gemm_flops(M, N, K) / gemm_min_bytes(M, N, K, reads_c)
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources with // comments and blank lines removed, so
+    that editing a comment does not invalidate the recorded counters."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        text = sources[rel] if sources else open(os.path.join(ROOT, rel), encoding="utf-8").read()
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -10,13 +10,18 @@
 // warp-level tiling of "How a Matmul Kernel Gets Fast" section 13 (here one
 // 64-lane wave per sub-tile).
 //
-// Staging.  Global loads are 16-byte (global_load_dwordx4) where the operands
-// are 16-byte aligned with row strides that are multiples of 4, four-byte loads
-// otherwise.  The loads of slice t+1 are issued into registers before the
-// matrix-core work on slice t and written to the other of two LDS buffers after
-// it, so one barrier per slice separates producers from consumers (the double
-// buffering of "Writing a Fast Matmul in CUDA, Step by Step", section "Bank
-// conflicts and double buffering").
+// Staging.  Global loads are 16-byte buffer loads (buffer_load_dwordx4) where
+// the operands are 16-byte aligned with row strides that are multiples of 4,
+// four-byte loads otherwise.  Two LDS buffers alternate between slices (the
+// double buffering of "Writing a Fast Matmul in CUDA, Step by Step", section
+// "Bank conflicts and double buffering"): while the MFMAs of slice t read one
+// buffer, the loads of a later slice are issued into registers, spread over
+// slice t's MFMAs, and the next slice is written to the other buffer after
+// them, so one barrier per slice separates producers from consumers.  The
+// 16-byte configurations keep two slices in registers (t+1 waiting for its
+// buffer, t+2 in flight), the others one.  The MFMAs of each slice's last
+// chunk of fragments are issued after that barrier, while the next slice's
+// first LDS reads are in flight.
 //
 // LDS layouts.  A 32x32x2 MFMA takes, in lane l, A(l % 32, k) and B(k, l % 32)
 // for one of two k values picked by l / 32.  Inside a slice the kernel assigns

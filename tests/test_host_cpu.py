@@ -361,3 +361,19 @@ def test_named_workloads_match_the_configured_shapes():
     assert (W["wide4096x11008x512"].N, W["wide4096x11008x512"].K) == (11008, 512)
     assert W["square128_int"].dist == "int4"
     assert workloads.HEADLINE == "square4096_ab"
+
+
+def test_traffic_hash_ignores_comments_not_code():
+    """bench.py reports the recorded HBM traffic only while the kernel source
+    it was measured on is unchanged; comments and blank lines do not count."""
+    import bench
+    srcs = {rel: open(os.path.join(ROOT, rel), encoding="utf-8").read() for rel in bench.KERNEL_SOURCES}
+    h = bench.kernel_source_hash(srcs)
+    assert h == bench.kernel_source_hash()
+    first = bench.KERNEL_SOURCES[0]
+    commented = dict(srcs)
+    commented[first] = "// a note\n\n" + srcs[first].replace("\n", "  // trailing note\n", 3)
+    assert bench.kernel_source_hash(commented) == h
+    changed = dict(srcs)
+    changed[first] = srcs[first] + "\nint extra_symbol = 0;\n"
+    assert bench.kernel_source_hash(changed) != h
