@@ -247,6 +247,16 @@ def cpu_baseline(A, B, C0, alpha, beta, target_s: float):
     t0 = time.perf_counter()
     oracle.sgemm_ref(A[:R], B, alpha, beta, None if C0 is None else C0[:R])
     dt = time.perf_counter() - t0
+    # Per-core reference: the same routine on one thread, on about a tenth of
+    # the time budget.
+    oracle.set_num_threads(1)
+    try:
+        r1 = int(min(M, max(1, (target_s / 10) / max(dt / R * cores, 1e-9))))
+        t0 = time.perf_counter()
+        oracle.sgemm_ref(A[:r1], B, alpha, beta, None if C0 is None else C0[:r1])
+        dt1 = time.perf_counter() - t0
+    finally:
+        oracle.set_num_threads(cores)
     return {
         "value": round(gemm_flops(R, N, K) / dt / 1e12, 6),
         "unit": "TFLOP/s",
@@ -254,6 +264,8 @@ def cpu_baseline(A, B, C0, alpha, beta, target_s: float):
         "kind": "oracle",
         "sample": f"rows 0..{R - 1} of the {M}x{N}x{K} product ({R * N} outputs, "
                   f"float64 accumulation, {dt:.1f} s)",
+        "single_core": {"value": round(gemm_flops(r1, N, K) / dt1 / 1e12, 6), "unit": "TFLOP/s",
+                        "sample": f"rows 0..{r1 - 1} of the same product on one thread ({dt1:.1f} s)"},
     }
 
 

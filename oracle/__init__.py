@@ -75,6 +75,8 @@ def _bind(path: str):
     lib.oracle_decode_16.restype = i
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i
+    lib.oracle_set_num_threads.argtypes = [i]
+    lib.oracle_set_num_threads.restype = None
     return lib
 
 
@@ -106,6 +108,11 @@ def _ptr(x):
 
 def num_threads() -> int:
     return int(_load().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the full-matrix routines from now on (timing only)."""
+    _load().oracle_set_num_threads(int(n))
 
 
 def sgemm_ref(A: np.ndarray, B: np.ndarray, alpha: float = 1.0,

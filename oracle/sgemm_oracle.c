@@ -48,6 +48,11 @@
 /* Number of OpenMP threads the full-matrix routine will use. */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
 
+/* Sets that number (n >= 1; used to time the oracle on a single core). */
+void oracle_set_num_threads(int n) {
+    if (n >= 1) omp_set_num_threads(n);
+}
+
 /*
  * Full product.  Cref and absab (absab may be NULL) are M x N row-major double
  * arrays with row stride N.  Returns 0 on success, -1 if scratch memory could
