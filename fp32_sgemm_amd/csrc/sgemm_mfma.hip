@@ -119,7 +119,17 @@ struct MfmaTile {
     static constexpr int STAGE = A_STAGE + B_STAGE;
     static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile");
     static_assert(BK % 8 == 0, "BK must be a multiple of 8");
-    static_assert(2 * STAGE * 4 <= 160 * 1024, "LDS");
+    // Epilogue through LDS (interior tiles): the accumulators are written
+    // row by row with a row stride of BN + 8 floats (rows four apart, which the
+    // two half-waves write together, fall in opposite halves of the bank
+    // space) and read back as 4-float groups, EPI_PARTS per thread,
+    // consecutive threads along a row.
+    static constexpr int EPI_S = BN + 8;
+    static constexpr int EPI_PARTS = BM * BN / 4 / NT;
+    static constexpr int EPI = BN >= 128 ? BM * EPI_S : 0;
+    static constexpr int SMEM = 2 * STAGE > EPI ? 2 * STAGE : EPI;
+    static_assert(SMEM * 4 <= 160 * 1024, "LDS");
+    static_assert((BM * BN / 4) % NT == 0 && NT % (BN / 4) == 0, "epilogue groups");
 };
 
 // Per-thread addressing of the 4-float groups a thread stages from one operand
@@ -522,7 +532,7 @@ __device__ __forceinline__ void shift_k(GemmArgs &g, int kb, int klen) {
 // where Cb points at the tile's first element with row stride ldc (C itself,
 // or a partial-sum slot).  Elements outside M x N are neither read nor
 // written.
-template <class T, bool VEC>
+template <class T, bool VEC, bool LDS_EPI = true>
 __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, float *smem, float *Cb,
                                              int64_t ldc, float alpha, float beta) {
     const int tid = threadIdx.x;
@@ -541,6 +551,49 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
     const bool edge_mn = (m0 + T::BM > g.M) || (n0 + T::BN > g.N);
     if (edge_mn) k_loop<T, VEC, true>(g, m0, n0, tid, wm, wn, lane, smem, acc);
     else k_loop<T, VEC, false>(g, m0, n0, tid, wm, wn, lane, smem, acc);
+
+    // Interior tiles 128 wide of a 16-byte aligned C whose row stride is a
+    // multiple of 4 (and whose tile spans less than 2 GiB) go through LDS, so
+    // C is read and written in 4-float groups along its rows: 512-byte row
+    // segments per half-wave instead of 128-byte ones (64-wide tiles gained
+    // nothing).  Not in the persistent kernel, whose registers it would crowd.
+    if (LDS_EPI && T::BN >= 128 && !edge_mn && (reinterpret_cast<uintptr_t>(Cb) % 16 == 0) && (ldc % 4 == 0) &&
+        (int64_t)(T::BM - 1) * ldc * 4 + T::BN * 4 < ((int64_t)1 << 31)) {
+        constexpr int GPR = T::BN / 4;            // 4-float groups per tile row
+        constexpr int GROWS = T::NT / GPR;        // tile rows per group index
+        const int grow = tid / GPR, gcol = 4 * (tid % GPR);
+        const int h = lane >> 5, l32 = lane & 31;
+        __syncthreads();   // every wave is done reading the LDS stages
+#pragma unroll
+        for (int ib = 0; ib < T::MB; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < T::NB; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = wm * T::WM + ib * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                    smem[rr * T::EPI_S + wn * T::WN + jb * 32 + l32] = acc[ib][jb][r];
+                }
+        __syncthreads();
+        float4 cv[T::EPI_PARTS];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int p = 0; p < T::EPI_PARTS; ++p)
+                cv[p] = *reinterpret_cast<const float4 *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol);
+        }
+#pragma unroll
+        for (int p = 0; p < T::EPI_PARTS; ++p) {
+            const float4 a = *reinterpret_cast<const float4 *>(smem + (p * GROWS + grow) * T::EPI_S + gcol);
+            float4 v = make_float4(alpha * a.x, alpha * a.y, alpha * a.z, alpha * a.w);
+            if (beta != 0.f) {
+                v.x = fmaf(beta, cv[p].x, v.x);
+                v.y = fmaf(beta, cv[p].y, v.y);
+                v.z = fmaf(beta, cv[p].z, v.z);
+                v.w = fmaf(beta, cv[p].w, v.w);
+            }
+            *reinterpret_cast<float4 *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol) = v;
+        }
+        return;
+    }
 
     // Epilogue.  Accumulator register r of a 32x32 block holds, in lane l,
     // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the block.  C is read in
@@ -616,7 +669,7 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
 template <class T, bool VEC>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
     GemmArgs g, int tiles_m, int tiles_n, int group_m, int ntiles, SplitK sk) {
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
 
     int bid = blockIdx.x;
     float *Cbase = g.C;
@@ -680,7 +733,7 @@ __host__ __device__ __forceinline__ int owner_of_unit(const StreamK &sk, int64_t
 template <class T, bool VEC>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_streamk_kernel(
     GemmArgs g, int tiles_m, int tiles_n, int group_m, StreamK sk) {
-    __shared__ __attribute__((aligned(16))) float smem[2 * T::STAGE];
+    __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
     // Work-groups resident on one XCD take consecutive positions, so they
     // work on neighbouring tiles and share their panels in that XCD's L2.
     const int w = xcd_position(blockIdx.x, sk.P);
@@ -700,8 +753,8 @@ __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void
         const bool whole = j0 == 0 && j1 == sk.ipt;
         float *Cb = whole ? g.C + (int64_t)m0 * g.ldc + n0
                           : sk.ws + (int64_t)(2 * w + (j0 > 0 ? 0 : 1)) * (T::BM * T::BN);
-        compute_tile<T, VEC>(gs, m0, n0, smem, Cb, whole ? g.ldc : (int64_t)T::BN, whole ? g.alpha : 1.f,
-                             whole ? g.beta : 0.f);
+        compute_tile<T, VEC, false>(gs, m0, n0, smem, Cb, whole ? g.ldc : (int64_t)T::BN,
+                                    whole ? g.alpha : 1.f, whole ? g.beta : 0.f);
         __syncthreads();
     }
 }
