@@ -563,6 +563,14 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
         constexpr int GROWS = T::NT / GPR;        // tile rows per group index
         const int grow = tid / GPR, gcol = 4 * (tid % GPR);
         const int h = lane >> 5, l32 = lane & 31;
+        // C's groups are requested first, so their latency overlaps the
+        // accumulators' trip through LDS.
+        float4 cv[T::EPI_PARTS];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int p = 0; p < T::EPI_PARTS; ++p)
+                cv[p] = *reinterpret_cast<const float4 *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol);
+        }
         __syncthreads();   // every wave is done reading the LDS stages
 #pragma unroll
         for (int ib = 0; ib < T::MB; ++ib)
@@ -574,12 +582,6 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
                     smem[rr * T::EPI_S + wn * T::WN + jb * 32 + l32] = acc[ib][jb][r];
                 }
         __syncthreads();
-        float4 cv[T::EPI_PARTS];
-        if (beta != 0.f) {
-#pragma unroll
-            for (int p = 0; p < T::EPI_PARTS; ++p)
-                cv[p] = *reinterpret_cast<const float4 *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol);
-        }
 #pragma unroll
         for (int p = 0; p < T::EPI_PARTS; ++p) {
             const float4 a = *reinterpret_cast<const float4 *>(smem + (p * GROWS + grow) * T::EPI_S + gcol);
