@@ -4,8 +4,11 @@
 // work on one stream runs in order, so successive calls on a stream can reuse
 // the same memory without further synchronisation, while calls on different
 // streams never share it.  A stream's workspace is allocated on its first use
-// and grown when a call needs more (growing waits for the stream's pending
-// work before freeing the old block); it is held until the process ends.
+// and replaced by a block at least twice as large when a call needs more.  The
+// old block is kept, not freed: work already queued on the stream, or a call
+// from another host thread that obtained it a moment earlier, may still use
+// it, and keeping it needs no synchronisation (the kept blocks together stay
+// smaller than the current one).  Everything is held until the process ends.
 // Every kernel writes the part of the workspace it later reads, so the memory
 // is not cleared.
 #include <cstdint>
@@ -26,6 +29,7 @@ struct Entry {
 
 std::mutex g_mutex;
 std::vector<Entry> g_entries;
+std::vector<void *> g_retired;   // replaced blocks, kept until the process ends
 
 constexpr size_t kMinBytes = (size_t)4 << 20;
 
@@ -44,22 +48,14 @@ hipError_t stream_workspace(size_t bytes, hipStream_t stream, void **out) {
         return hipSuccess;
     }
     size_t want = bytes < kMinBytes ? kMinBytes : bytes;
-    if (slot != nullptr) {
-        if (want < 2 * slot->bytes) want = 2 * slot->bytes;
-        // The old block may still be in use by work queued on this stream.
-        e = hipStreamSynchronize(stream);
-        if (e != hipSuccess) return e;
-        e = hipFree(slot->ptr);
-        if (e != hipSuccess) return e;
-        slot->ptr = nullptr;
-        slot->bytes = 0;
-    }
+    if (slot != nullptr && want < 2 * slot->bytes) want = 2 * slot->bytes;
     void *p = nullptr;
     e = hipMalloc(&p, want);
     if (e != hipSuccess) return e;
     if (slot == nullptr) {
         g_entries.push_back(Entry{dev, stream, p, want});
     } else {
+        g_retired.push_back(slot->ptr);
         slot->ptr = p;
         slot->bytes = want;
     }

@@ -38,9 +38,10 @@
  *     tuning table or sgemm_f32_ex_config).  Those keep one workspace per
  *     (device, stream), allocated with hipMalloc on the first such call on
  *     that stream (at least 4 MiB, at most splits * M * N floats, 1 GiB cap for
- *     MFMA plans; grown when a call needs more, which waits for that stream's
- *     pending work) and held until the process ends.  Calls on different
- *     streams never share it.
+ *     MFMA plans).  A call that needs more allocates a block at least twice as
+ *     large; the replaced block is kept, not freed (work queued earlier may
+ *     still use it), so growing never waits for the stream.  All of it is held
+ *     until the process ends.  Calls on different streams never share it.
  *
  * Special cases:
  *   - M == 0 or N == 0: nothing is done, returns 0.
