@@ -101,44 +101,61 @@ def _load_library():
 
 _lib = _load_library()
 
+_INT_MIN, _INT_MAX = -(1 << 31), (1 << 31) - 1
+
+
+def _ints(*vals) -> None:
+    """ctypes wraps an out-of-range int silently (K = 2**32 + 5 would arrive as 5),
+    so every integer argument of the C interface is range-checked first."""
+    for v in vals:
+        if not _INT_MIN <= int(v) <= _INT_MAX:
+            raise OverflowError(f"{v} does not fit the C interface's 32-bit int")
+
 
 def sgemm_f32(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int,
               beta: float, C: int, ldc: int, stream: int = 0) -> int:
     """The C entry point: raw device pointers and a hipStream_t as integers."""
+    _ints(M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_variant(variant: int, M: int, N: int, K: int, alpha: float, A: int, lda: int,
                       B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    _ints(variant, M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_select(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int,
                      ldb: int) -> int:
+    _ints(M, N, K, lda, ldb)
     return _lib.sgemm_f32_select(M, N, K, alpha, A, lda, B, ldb)
 
 
 def sgemm_f32_ex(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int,
                  lda: int, B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
     """C = alpha*op(A)*op(B) + beta*C; a flag of 1 means the operand is stored transposed."""
+    _ints(trans_a, trans_b, M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32_ex(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_ex_variant(variant: int, trans_a: int, trans_b: int, M: int, N: int, K: int,
                          alpha: float, A: int, lda: int, B: int, ldb: int, beta: float, C: int,
                          ldc: int, stream: int = 0) -> int:
+    _ints(variant, trans_a, trans_b, M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32_ex_variant(variant, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
                                      beta, C, ldc, stream)
 
 
 def sgemm_f32_ex_select(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float,
                         A: int, lda: int, B: int, ldb: int) -> int:
+    _ints(trans_a, trans_b, M, N, K, lda, ldb)
     return _lib.sgemm_f32_ex_select(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb)
 
 
 def sgemm_f32_ex_plan(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha: float, A: int,
                       lda: int, B: int, ldb: int):
     """Returns (status, variant, config, group_m, splits) of the automatic choice."""
+    _ints(trans_a, trans_b, M, N, K, lda, ldb)
     out = [ctypes.c_int(0) for _ in range(4)]
     st = _lib.sgemm_f32_ex_plan(trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
                                 *[ctypes.byref(o) for o in out])
@@ -148,11 +165,13 @@ def sgemm_f32_ex_plan(trans_a: int, trans_b: int, M: int, N: int, K: int, alpha:
 def sgemm_f32_ex_config(config: int, group_m: int, splits: int, trans_a: int, trans_b: int, M: int,
                         N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int, beta: float,
                         C: int, ldc: int, stream: int = 0) -> int:
+    _ints(config, group_m, splits, trans_a, trans_b, M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32_ex_config(config, group_m, splits, trans_a, trans_b, M, N, K, alpha, A, lda,
                                     B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_config_name(config: int) -> str | None:
+    _ints(config)
     r = _lib.sgemm_f32_config_name(config)
     return None if r is None else r.decode()
 
@@ -165,10 +184,12 @@ def gemm16_f32(in_type: int, trans_a: int, trans_b: int, M: int, N: int, K: int,
                lda: int, B: int, ldb: int, beta: float, C: int, ldc: int, stream: int = 0) -> int:
     """C (float) = alpha*op(A)*op(B) + beta*C with A, B of 16-bit values
     (GEMM16_BF16 or GEMM16_F16 bit patterns), FP32 accumulation."""
+    _ints(in_type, trans_a, trans_b, M, N, K, lda, ldb, ldc)
     return _lib.gemm16_f32(in_type, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_variant_name(variant: int) -> str | None:
+    _ints(variant)
     r = _lib.sgemm_f32_variant_name(variant)
     return None if r is None else r.decode()
 
@@ -230,9 +251,15 @@ def sgemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant: int = AUTO,
     lda, ta = _operand(A, "A")
     ldb, tb = _operand(B, "B")
     ldc = _row_stride(C, "C")
+    if A.device != C.device or B.device != C.device:
+        raise ValueError(f"A, B and C must be on one device: {A.device}, {B.device}, {C.device}")
     if stream is None:
         stream = torch.cuda.current_stream(C.device)
-    st = sgemm_f32_ex_variant(variant, ta, tb, M, N, K, float(alpha), A.data_ptr(), lda,
-                              B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc, stream.cuda_stream)
+    # The library launches on the current device (and keeps its workspace per
+    # device), so C's device is made current for the call.
+    with torch.cuda.device(C.device):
+        st = sgemm_f32_ex_variant(variant, ta, tb, M, N, K, float(alpha), A.data_ptr(), lda,
+                                  B.data_ptr(), ldb, float(beta), C.data_ptr(), ldc,
+                                  stream.cuda_stream)
     if st != 0:
         raise SgemmError(st)

@@ -74,6 +74,20 @@ def test_argument_errors_without_touching_the_gpu(sg):
     assert sg.sgemm_f32_variant(sg.NUM_VARIANTS, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
 
 
+def test_binding_rejects_ints_that_ctypes_would_wrap(sg):
+    # 2**32 + 5 would reach the library as 5 and silently compute another product.
+    p = 0x1000
+    with pytest.raises(OverflowError):
+        sg.sgemm_f32(2, 2, 2**32 + 5, 1.0, p, 2**32 + 5, p, 2, 0.0, p, 2, 0)
+    with pytest.raises(OverflowError):
+        sg.sgemm_f32_ex(0, 0, 2, 2, 2, 1.0, p, 2, p, 2**31, 0.0, p, 2, 0)
+    with pytest.raises(OverflowError):
+        sg.sgemm_f32_ex_config(0, 8, 1, 0, 0, -(2**31) - 1, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0)
+    with pytest.raises(OverflowError):
+        sg.gemm16_f32(sg.GEMM16_BF16, 0, 0, 2, 2**31, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0)
+    assert sg.sgemm_f32(2**31 - 1, 2, 2, 1.0, 0, 2, p, 2, 0.0, p, 2, 0) == 5   # in range: C checks
+
+
 def test_empty_outputs_return_without_work(sg):
     # M == 0 or N == 0: success without any launch (NULL pointers are fine).
     assert sg.sgemm_f32(0, 5, 7, 1.0, 0, 7, 0, 5, 0.0, 0, 5, 0) == 0
