@@ -592,7 +592,10 @@ __device__ __forceinline__ void compute_tile(const GemmArgs &g, int m0, int n0, 
                 v.z = fmaf(beta, cv[p].z, v.z);
                 v.w = fmaf(beta, cv[p].w, v.w);
             }
-            *reinterpret_cast<float4 *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol) = v;
+            // C is written once and not read again here: a non-temporal
+            // store keeps it from displacing the A and B panels in L2.
+            const f32x4v w = {v.x, v.y, v.z, v.w};
+            __builtin_nontemporal_store(w, reinterpret_cast<f32x4v *>(Cb + (int64_t)(p * GROWS + grow) * ldc + gcol));
         }
         return;
     }
