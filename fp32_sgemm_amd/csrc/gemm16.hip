@@ -272,6 +272,50 @@ struct BigLoader {
     }
 };
 
+// Epilogue of a 256 x 256 tile in four passes of one block row (4 blocks, 64
+// values per lane): the C reads of a pass are issued together before its
+// stores.  Edge tiles go through a buffer resource over the tile's valid part
+// of C (rows past M beyond its extent, columns past N out-of-range offsets).
+__device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, int rows_a, int rows_b, int wm, int wn,
+                                             int h, int l32, const f32x16 (&acc)[big::BLK][big::BLK]) {
+    const bool edge = rows_a < big::BM || rows_b < big::BN;
+    float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
+    const __amdgpu_buffer_rsrc_t rc = rsrc16(reinterpret_cast<const uint16_t *>(Cb),
+                                             (int)(((int64_t)(rows_a - 1) * g.ldc + rows_b) * 4));
+    const float alpha = g.alpha, beta = g.beta;
+    auto pass = [&](int ib, auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        float cv[big::BLK][16];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int jb = 0; jb < big::BLK; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int cc = wn * big::WT + 32 * jb + l32;
+                    cv[jb][r] = EDGE ? raw_buffer_load_f32(rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0)
+                                     : Cb[(int64_t)rr * g.ldc + cc];
+                }
+        }
+#pragma unroll
+        for (int jb = 0; jb < big::BLK; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int cc = wn * big::WT + 32 * jb + l32;
+                float v = alpha * acc[ib][jb][r];
+                if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
+                if (EDGE) raw_buffer_store_f32(v, rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0);
+                else __builtin_nontemporal_store(v, &Cb[(int64_t)rr * g.ldc + cc]);   // C is not read again here
+            }
+    };
+#pragma unroll
+    for (int ib = 0; ib < big::BLK; ++ib) {
+        if (edge) pass(ib, std::true_type());
+        else pass(ib, std::false_type());
+    }
+}
+
 template <bool F16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_big_kernel(
     Args16 g, int tiles_m, int tiles_n) {
@@ -363,46 +407,173 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         __syncthreads();
     }
 
-    // Epilogue in four passes of one block row (4 blocks, 64 values per lane):
-    // the C reads of a pass are issued together before its stores.  Edge
-    // tiles go through a buffer resource over the tile's valid part of C
-    // (rows past M beyond its extent, columns past N out-of-range offsets).
-    const bool edge = rows_a < big::BM || rows_b < big::BN;
-    float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
-    const __amdgpu_buffer_rsrc_t rc = rsrc16(reinterpret_cast<const uint16_t *>(Cb),
-                                             (int)(((int64_t)(rows_a - 1) * g.ldc + rows_b) * 4));
-    const float alpha = g.alpha, beta = g.beta;
-    auto pass = [&](int ib, auto edge_tag) {
-        constexpr bool EDGE = decltype(edge_tag)::value;
-        float cv[big::BLK][16];
-        if (beta != 0.f) {
+    big_epilogue(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
+}
+
+// ---------------------------------------------------------------------------
+// 256 x 256 tiles with the operands copied from memory straight into LDS
+// (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the instruction's
+// LDS base + 16 * lane, without passing through registers).  With no staging
+// registers the slices can be fetched further ahead: slices of 32 k in four
+// LDS stages of 32 KB, the loads of slice t+3 issued while slice t is
+// multiplied, so a load has three slices of MFMA work (about 3000 clocks) to
+// arrive instead of part of one.  With one wave per SIMD that latency is not
+// hidden by any other wave.
+//
+// A slice row is 64 bytes (4 chunks of 16).  One load instruction fills 1 KB
+// of LDS: 16 rows.  Chunk c of row r is stored at position c ^ ((r >> 2) & 3),
+// which leaves the fragment reads (32 rows at one chunk per half-wave) free of
+// bank conflicts (LDS bank-conflict counter: zero; without the swizzle, or
+// with one that changes every row or every second row, 50-75 % of the LDS
+// cycles were conflicts); a lane of a load instruction fetches the chunk that
+// belongs at its position.
+//
+// Ordering without __syncthreads (whose fence would wait for every load in
+// flight): at the top of slice t each wave waits until at most the 16 loads
+// of slices t+1 and t+2 are outstanding (vector-memory counts complete in
+// order), and for its own LDS reads, then joins an s_barrier; past it every
+// wave's part of slice t is in LDS and every wave is done with the stage that
+// slice t+3 is loaded into.
+// ---------------------------------------------------------------------------
+namespace dl {
+constexpr int BK = 32;                           // slice depth in elements
+constexpr int ROW = BK * 2;                      // 64 bytes
+constexpr int A_STAGE = big::BM * ROW;           // 16 KB
+constexpr int STAGE = A_STAGE + big::BN * ROW;   // 32 KB
+constexpr int NST = 4;                           // stages
+constexpr int RPI = 1024 / ROW;                  // rows per load instruction: 16
+constexpr int LPO = big::BM / 4 / RPI;           // load instructions per wave and operand per slice: 4
+constexpr int LPS = 2 * LPO;                     // per slice: 8
+static_assert(NST * STAGE <= 160 * 1024, "LDS");
+}  // namespace dl
+
+__device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 2) & 3); }
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
+template <bool F16>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
+    Args16 g, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NST * dl::STAGE];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * big::BM, n0 = tn * big::BN;
+    const int tid = threadIdx.x;
+    // The wave index is uniform: kept in a scalar register, the LDS bases of
+    // the loads need no per-load transfer from a vector register.
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+    const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
+    const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
+    const uint16_t *Bb = g.B + (int64_t)n0 * g.ldb;
+
+    // Load instruction j of this wave covers rows wave*64 + 16 j + lane/4; the
+    // lane's position lane % 4 in its row holds chunk dl_pos(row, lane % 4).
+    int offa[dl::LPO], offb[dl::LPO];
 #pragma unroll
-            for (int jb = 0; jb < big::BLK; ++jb)
+    for (int j = 0; j < dl::LPO; ++j) {
+        const int r = wave * 64 + dl::RPI * j + (lane >> 2);
+        const int c = dl_pos(r, lane & 3);
+        offa[j] = (r * (int)g.lda + c * 8) * 2;
+        offb[j] = (r * (int)g.ldb + c * 8) * 2;
+    }
+    // Rows past M (N) lie beyond the resource's extent and arrive as zeros.
+    // Load i (< LPS) of a slice into a stage: A's first, then B's.
+    auto issue_one = [&](int slice, int stage, int i) {
+        const int k0 = slice * dl::BK;
+        unsigned char *st = smem + stage * dl::STAGE + wave * 64 * dl::ROW;
+        if (i < dl::LPO) {
+            const __amdgpu_buffer_rsrc_t rsa = rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
+            lds_dma16(rsa, st + i * 1024, offa[i]);
+        } else {
+            const __amdgpu_buffer_rsrc_t rsb = rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + dl::BK) * 2));
+            lds_dma16(rsb, st + dl::A_STAGE + (i - dl::LPO) * 1024, offb[i - dl::LPO]);
+        }
+    };
+    auto issue = [&](int slice, int stage) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int cc = wn * big::WT + 32 * jb + l32;
-                    cv[jb][r] = EDGE ? raw_buffer_load_f32(rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0)
-                                     : Cb[(int64_t)rr * g.ldc + cc];
-                }
+        for (int i = 0; i < dl::LPS; ++i) issue_one(slice, stage, i);
+    };
+
+    f32x16 acc[big::BLK][big::BLK];
+#pragma unroll
+    for (int i = 0; i < big::BLK; ++i)
+#pragma unroll
+        for (int j = 0; j < big::BLK; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    // Fragment addresses (stage-relative) of k step s: row x, chunk 2 s + h.
+    int fa_off[2][big::BLK], fb_off[2][big::BLK];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int b = 0; b < big::BLK; ++b) {
+            const int ra = wm * big::WT + 32 * b + l32, rb = wn * big::WT + 32 * b + l32;
+            fa_off[s][b] = ra * dl::ROW + dl_pos(ra, 2 * s + h) * 16;
+            fb_off[s][b] = dl::A_STAGE + rb * dl::ROW + dl_pos(rb, 2 * s + h) * 16;
+        }
+    auto read_blk = [&](const unsigned char *st, int s, int b, i32x4 (&fa)[big::BLK], i32x4 (&fb)[big::BLK]) {
+        fa[b] = *reinterpret_cast<const i32x4 *>(st + fa_off[s][b]);
+        fb[b] = *reinterpret_cast<const i32x4 *>(st + fb_off[s][b]);
+    };
+    auto mfma_one = [&](const i32x4 (&fa)[big::BLK], const i32x4 (&fb)[big::BLK], int i) {
+        acc[i / big::BLK][i % big::BLK] = mfma16<F16>(fa[i / big::BLK], fb[i % big::BLK], acc[i / big::BLK][i % big::BLK]);
+    };
+
+    const int nk = g.K / dl::BK;
+    // Slices past the end are loaded again as the last one, into stages that
+    // are never read, so every slice issues the same number of loads.
+#pragma unroll
+    for (int s = 0; s < dl::NST - 1; ++s) issue(s < nk ? s : nk - 1, s);
+
+    i32x4 f0a[big::BLK], f0b[big::BLK], f1a[big::BLK], f1b[big::BLK];
+#pragma unroll
+    for (int b = 0; b < big::BLK; ++b) {
+        f1a[b] = i32x4{0, 0, 0, 0};
+        f1b[b] = i32x4{0, 0, 0, 0};
+    }
+    // One wave per SIMD issues in order, so every other instruction of a
+    // slice is placed right after an MFMA and goes out while the matrix core
+    // works; sched_barrier keeps the compiler from regrouping them.
+    //   phase 1: the MFMAs of the previous slice's last k step (zeros before
+    //            the first slice), followed by this slice's first-step
+    //            fragment reads and the loads of slice t+3;
+    //   phase 2: the MFMAs of the first k step, followed by the reads of the
+    //            second, whose MFMAs are held over to the next slice.
+    for (int t = 0; t < nk; ++t) {
+        // vmcnt(16) (two slices still in flight) and lgkmcnt(0); expcnt not waited on.
+        __builtin_amdgcn_s_waitcnt((1 << 14) | (0 << 8) | (7 << 4) | 0);
+        __builtin_amdgcn_s_barrier();
+        const int ld_slice = t + dl::NST - 1 < nk ? t + dl::NST - 1 : nk - 1;
+        const int ld_stage = (t + dl::NST - 1) % dl::NST;
+        const unsigned char *st = smem + (t % dl::NST) * dl::STAGE;
+#pragma unroll
+        for (int i = 0; i < big::BLK * big::BLK; ++i) {
+            mfma_one(f1a, f1b, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < big::BLK) read_blk(st, 0, i, f0a, f0b);
+            else if (i < big::BLK + dl::LPS) issue_one(ld_slice, ld_stage, i - big::BLK);
+            __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int jb = 0; jb < big::BLK; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int cc = wn * big::WT + 32 * jb + l32;
-                float v = alpha * acc[ib][jb][r];
-                if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
-                if (EDGE) raw_buffer_store_f32(v, rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0);
-                else Cb[(int64_t)rr * g.ldc + cc] = v;
-            }
-    };
-#pragma unroll
-    for (int ib = 0; ib < big::BLK; ++ib) {
-        if (edge) pass(ib, std::true_type());
-        else pass(ib, std::false_type());
+        for (int i = 0; i < big::BLK * big::BLK; ++i) {
+            mfma_one(f0a, f0b, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < big::BLK) read_blk(st, 1, i, f1a, f1b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
+#pragma unroll
+    for (int i = 0; i < big::BLK * big::BLK; ++i) mfma_one(f1a, f1b, i);
+    // Every load issued (including the repeated last slice) has landed before
+    // the work-group can end and its LDS be given to another.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    big_epilogue(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
 }
 
 // K-major, K-padded copy of a 16-bit operand: dst[x * Kp + k] = op(x, k) for
@@ -511,9 +682,9 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
         const dim3 grid(tiles_m * tiles_n);
         if (kind == GEMM16_F32_F16)
-            hipLaunchKernelGGL(gemm16_big_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+            hipLaunchKernelGGL(gemm16_dl_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
         else
-            hipLaunchKernelGGL(gemm16_big_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+            hipLaunchKernelGGL(gemm16_dl_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
         return hipGetLastError();
     }
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
