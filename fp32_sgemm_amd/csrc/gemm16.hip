@@ -244,33 +244,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void ge
 // accumulation registers), one work-group per CU.  Per MFMA a wave reads half
 // the fragment bytes of a 64 x 64 wave tile and the slice writes are spread
 // over four times the MFMAs, so the LDS traffic (about 96 bytes per clock at
-// the MFMA rate, against 128) no longer binds; with one wave per SIMD the
-// latency is hidden inside the wave: fragment reads one k step ahead and the
-// next slice's global loads spread over the k steps.
+// the MFMA rate, against 128) no longer binds.
 // ---------------------------------------------------------------------------
 namespace big {
 constexpr int BM = 256, BN = 256;
-constexpr int A_STAGE = BM * ROW_BYTES;          // 32 KB
-constexpr int B_STAGE = BN * ROW_BYTES;
-constexpr int STAGE = A_STAGE + B_STAGE;         // 64 KB
-constexpr int LOADS = (BM * CHUNKS) / NT;        // 8 per operand per thread
 constexpr int WT = 128;                          // wave tile
 constexpr int BLK = WT / 32;                     // 4 blocks per wave and direction
 }  // namespace big
-
-struct BigLoader {
-    int off[big::LOADS];
-    int lds[big::LOADS];
-    __device__ __forceinline__ BigLoader(int64_t ld, int tid) {
-#pragma unroll
-        for (int j = 0; j < big::LOADS; ++j) {
-            const int r = tid / CHUNKS + (NT / CHUNKS) * j;
-            const int c = tid % CHUNKS;
-            off[j] = (r * (int)ld + c * 8) * 2;
-            lds[j] = r * ROW_BYTES + swz(r, c) * 16;
-        }
-    }
-};
 
 // Epilogue of a 256 x 256 tile in four passes of one block row (4 blocks, 64
 // values per lane): the C reads of a pass are issued together before its
@@ -314,100 +294,6 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
         if (edge) pass(ib, std::true_type());
         else pass(ib, std::false_type());
     }
-}
-
-template <bool F16>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_big_kernel(
-    Args16 g, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * big::STAGE];
-    int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * big::BM, n0 = tn * big::BN;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    const int h = lane >> 5, l32 = lane & 31;
-
-    const BigLoader la(g.lda, tid), lb(g.ldb, tid);
-    const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
-    const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
-    const uint16_t *Bb = g.B + (int64_t)n0 * g.ldb;
-    i32x4 ra[big::LOADS], rb[big::LOADS];
-    auto rsrc_a = [&](int k0) { return rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + BK) * 2)); };
-    auto rsrc_b = [&](int k0) { return rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + BK) * 2)); };
-    auto store = [&](unsigned char *st) {
-#pragma unroll
-        for (int j = 0; j < big::LOADS; ++j) *reinterpret_cast<i32x4 *>(st + la.lds[j]) = ra[j];
-#pragma unroll
-        for (int j = 0; j < big::LOADS; ++j) *reinterpret_cast<i32x4 *>(st + big::A_STAGE + lb.lds[j]) = rb[j];
-    };
-
-    f32x16 acc[big::BLK][big::BLK];
-#pragma unroll
-    for (int i = 0; i < big::BLK; ++i)
-#pragma unroll
-        for (int j = 0; j < big::BLK; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-    int ra_row[big::BLK], rb_row[big::BLK];
-#pragma unroll
-    for (int b = 0; b < big::BLK; ++b) {
-        ra_row[b] = wm * big::WT + 32 * b + l32;
-        rb_row[b] = wn * big::WT + 32 * b + l32;
-    }
-    auto read_frags = [&](const unsigned char *st, int s, i32x4 (&fa)[big::BLK], i32x4 (&fb)[big::BLK]) {
-        const int c = 2 * s + h;
-#pragma unroll
-        for (int b = 0; b < big::BLK; ++b) {
-            fa[b] = *reinterpret_cast<const i32x4 *>(st + ra_row[b] * ROW_BYTES + swz(ra_row[b], c) * 16);
-            fb[b] = *reinterpret_cast<const i32x4 *>(st + big::A_STAGE + rb_row[b] * ROW_BYTES + swz(rb_row[b], c) * 16);
-        }
-    };
-    constexpr int STEPS = BK / 16;
-    constexpr int PER_STEP = big::LOADS / STEPS;     // 2 groups of each operand per k step
-    // One slice from LDS; during its k steps the next slice (k0n) is loaded.
-    auto compute = [&](const unsigned char *st, int k0n) {
-        const __amdgpu_buffer_rsrc_t rsa = rsrc_a(k0n), rsb = rsrc_b(k0n);
-        i32x4 fa[2][big::BLK], fb[2][big::BLK];
-        read_frags(st, 0, fa[0], fb[0]);
-#pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-#pragma unroll
-            for (int j = 0; j < PER_STEP; ++j) {
-                ra[s * PER_STEP + j] = raw_buffer_load_v4i32(rsa, la.off[s * PER_STEP + j], 0, 0);
-                rb[s * PER_STEP + j] = raw_buffer_load_v4i32(rsb, lb.off[s * PER_STEP + j], 0, 0);
-            }
-            if (s + 1 < STEPS) read_frags(st, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int ib = 0; ib < big::BLK; ++ib)
-#pragma unroll
-                for (int jb = 0; jb < big::BLK; ++jb)
-                    acc[ib][jb] = mfma16<F16>(fa[s & 1][ib], fb[s & 1][jb], acc[ib][jb]);
-        }
-    };
-
-    const int nk = g.K / BK;
-    {
-        const __amdgpu_buffer_rsrc_t rsa = rsrc_a(0), rsb = rsrc_b(0);
-#pragma unroll
-        for (int j = 0; j < big::LOADS; ++j) {
-            ra[j] = raw_buffer_load_v4i32(rsa, la.off[j], 0, 0);
-            rb[j] = raw_buffer_load_v4i32(rsb, lb.off[j], 0, 0);
-        }
-    }
-    store(smem);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        // The loads are unconditional: past the end they re-read the last
-        // slice (never stored), so the wait counts are the same on every path.
-        compute(smem + (t & 1) * big::STAGE, (t + 1 < nk ? t + 1 : t) * BK);
-        if (t + 1 < nk) store(smem + ((t + 1) & 1) * big::STAGE);
-        __syncthreads();
-    }
-
-    big_epilogue(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
 }
 
 // ---------------------------------------------------------------------------
