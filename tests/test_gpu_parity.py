@@ -220,6 +220,55 @@ def test_skinny_concurrent_streams(sg):
     assert ok, info
 
 
+def test_workspace_growth_and_host_threads(sg):
+    """Split plans need the stream's workspace: a larger product on the same
+    stream grows it (the replaced block stays valid for work already queued),
+    and host threads calling on their own streams at the same time each get
+    their own workspace."""
+    import threading
+    cases = [(256, 256, 4096, 41), (512, 512, 8192, 42), (256, 256, 4096, 43)]
+    data = []
+    for M, N, K, seed in cases:
+        A, B, _ = _inputs(M, N, K, "uniform", seed, c0=False)
+        data.append((M, N, K, A, B, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+                     torch.zeros(M, N, device="cuda:0")))
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    # configuration 4 (64x64, two slices in flight) with 8 K splits: 8*M*N floats of partials
+    for M, N, K, _, _, dA, dB, dC in data:
+        say(f"[ws_growth] {M}x{N}x{K} splits 8")
+        assert sg.sgemm_f32_ex_config(4, 8, 8, 0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                                      dC.data_ptr(), N, s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    for M, N, K, A, B, _, _, dC in data:
+        ok, info = check_full(dC.cpu().numpy(), A, B, 1.0, 0.0, None)
+        assert ok, info
+
+    errors = []
+
+    def worker(idx):
+        M, N, K, A, B, dA, dB, _ = data[idx]
+        st = torch.cuda.Stream()
+        out = torch.zeros(M, N, device="cuda:0")
+        for _ in range(4):
+            rc = sg.sgemm_f32_ex_config(4, 8, 8, 0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                                        out.data_ptr(), N, st.cuda_stream)
+            if rc != 0:
+                errors.append(rc)
+        st.synchronize()
+        ok, info = check_full(out.cpu().numpy(), A, B, 1.0, 0.0, None)
+        if not ok:
+            errors.append(info)
+
+    say("[ws_threads] three host threads, three streams")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(3)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+
+
 def test_non_default_stream_ordering(sg):
     """Work queued before the call on a side stream is seen by the kernel."""
     M, N, K = 300, 400, 500
