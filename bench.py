@@ -39,7 +39,8 @@ PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector and matrix), datas
 PEAK_16BIT_TFLOPS = 2500.0        # MI355X dense BF16 / FP16 matrix, datasheet
 METRIC_16 = "GEMM TFLOP/s with {} inputs and FP32 accumulation at {} on 1 MI355X"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_mfma.hip", "fp32_sgemm_amd/csrc/gemm_internal.hpp")
+KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_big.hip", "fp32_sgemm_amd/csrc/sgemm_mfma.hip",
+                  "fp32_sgemm_amd/csrc/gemm_internal.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_large_square4096_ab.txt")
 
 
@@ -455,7 +456,8 @@ def main():
         bound = "alu" if chosen == sg.VALU else "mfma"
         roofline = {"bound": bound, "achieved": round(achieved, 3), "peak": PEAK_FP32_TFLOPS,
                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_FP32_TFLOPS, 4)}
-    headline_kernel = w.name == workloads.HEADLINE and chosen == 1 and not (ta or tb) and not kind16
+    headline_kernel = (w.name == workloads.HEADLINE and variant == 0 and forced is None and not (ta or tb)
+                       and not kind16 and len(dBs) == 1)
     roofline["traffic"] = measured_traffic() if headline_kernel else None
     roofline["kernel_avg_ms"] = round(kern_avg_s * 1e3, 5)
 

@@ -35,7 +35,8 @@ CFG_64x128 = 3
 CFG_64x64_PF2 = 4
 CFG_128x128_STREAMK = 5
 CFG_64x64_BK64 = 6
-NUM_CONFIGS = 7
+CFG_256x256 = 7
+NUM_CONFIGS = 8
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

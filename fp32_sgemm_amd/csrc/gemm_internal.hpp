@@ -30,11 +30,13 @@ hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stre
 // small tile), 2 = 128x64, 3 = 64x128, 4 = 64x64 with two slices in flight,
 // 5 = 128x128 persistent with stream-K (resident work-groups take whole tiles
 // in rounds, then equal shares of the remaining tiles' K slices; split tiles
-// are summed by a fix-up kernel).  Configurations 2-5 exist with 16-byte loads
-// only.  `group_m` is the number of tile rows walked together by the tile
-// order; `splits` divides K over work-groups (the partial sums go through the
-// stream's workspace and a reduction kernel; not with configuration 5).
-constexpr int kNumMfmaConfigs = 7;
+// are summed by a fix-up kernel), 6 = 64x64 with slices of 64, 7 = 256x256
+// (sgemm_big.hip: whole tiles only, one work-group per CU).  Configurations 2-7
+// exist with 16-byte loads only.  `group_m` is the number of tile rows walked
+// together by the tile order (configuration 7 uses 4); `splits` divides K over
+// work-groups (the partial sums go through the stream's workspace and a
+// reduction kernel; not with configurations 5 and 7).
+constexpr int kNumMfmaConfigs = 8;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
 int64_t mfma_config_tiles(int config, int M, int N);
@@ -43,6 +45,12 @@ bool mfma_config_splits_ok(int config);
 // Number of non-empty splits of K actually used for a requested count, and the
 // K extent of each (a multiple of the tile depth).
 int mfma_effective_splits(int K, int splits, int *k_per);
+// 256 x 256 tiles, one work-group per CU (sgemm_big.hip): whether the
+// product fits them (whole tiles, aligned operands), their count, and the
+// launcher.
+bool big_tile_fits(const GemmArgs &g);
+int64_t big_tiles(int M, int N);
+hipError_t launch_big(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);

@@ -161,25 +161,53 @@ Plan quantization_plan(const Plan &p, int M, int N, int K) {
     return Plan{SGEMM_F32_MFMA_TUNED, 4, 8, 1};
 }
 
+// 256x256 tiles (configuration 7) for grids of whole tiles that fill their
+// rounds: one work-group per compute unit, so kResidentBigTiles per round.
+// Same-box per-launch medians (TFLOP/s, 128x128 -> 256x256): 4096^3 with
+// alpha 1.5, beta -0.5 143.2 -> 147.1, NT 144.6 -> 147.1; 8192^3 147.2 ->
+// 149.1; 4096 x 4096 x 1024 136.6 -> 140.4.
+constexpr int kResidentBigTiles = 256;
+constexpr double kBigFill = 0.95;
+
+Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B,
+                   int ldb) {
+    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
+        return p;
+    sgemm::GemmArgs g;
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.B = B;
+    g.lda = lda; g.ldb = ldb;
+    g.trans_a = ta; g.trans_b = tb;
+    if (!sgemm::big_tile_fits(g)) return p;
+    const int64_t tiles = sgemm::big_tiles(M, N);
+    if (tiles < kResidentBigTiles) return p;
+    const int64_t rounds = (tiles + kResidentBigTiles - 1) / kResidentBigTiles;
+    if ((double)tiles < kBigFill * (double)(rounds * kResidentBigTiles)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 7, 4, 1};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
-// grids that fill their rounds poorly (reported as SGEMM_F32_MFMA_TUNED when the
+// grids that fill their rounds poorly, and to 256x256 tiles for grids of whole
+// 256x256 tiles that fill theirs (reported as SGEMM_F32_MFMA_TUNED when the
 // plan differs from the default).  Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
     if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
-    if (!kHaveTunedTable) return quantization_plan(d, M, N, K);
-    const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
-    if (e.config < 0 || e.config >= sgemm::kNumMfmaConfigs || e.group_m < 1 || e.splits < 1 ||
-        !config_fits(e.config, ta, tb, lda, ldb))
-        return quantization_plan(d, M, N, K);
-    int k_per = 0;
-    int splits = sgemm::mfma_effective_splits(K, e.splits, &k_per);
-    if ((int64_t)splits * M * N * 4 > kMaxSplitBytes) splits = 1;
-    Plan p{SGEMM_F32_MFMA_TUNED, e.config, e.group_m, splits};
-    if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) p = d;
-    return quantization_plan(p, M, N, K);
+    Plan p = d;
+    if (kHaveTunedTable) {
+        const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
+        if (e.config >= 0 && e.config < sgemm::kNumMfmaConfigs && e.group_m >= 1 && e.splits >= 1 &&
+            config_fits(e.config, ta, tb, lda, ldb)) {
+            int k_per = 0;
+            int splits = sgemm::mfma_effective_splits(K, e.splits, &k_per);
+            if ((int64_t)splits * M * N * 4 > kMaxSplitBytes) splits = 1;
+            p = Plan{SGEMM_F32_MFMA_TUNED, e.config, e.group_m, splits};
+            if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) p = d;
+        }
+    }
+    return big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
@@ -190,6 +218,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     if (!config_fits(config, g.trans_a, g.trans_b, g.lda, g.ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
+    if (config == 7 && !sgemm::big_tile_fits(g)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
     const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
     if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
@@ -340,6 +369,7 @@ const char *sgemm_f32_config_name(int config) {
         case 4: return "64x64_pf2";
         case 5: return "128x128_streamk";
         case 6: return "64x64_bk64";
+        case 7: return "256x256";
         default: return nullptr;
     }
 }

@@ -1,0 +1,302 @@
+// FP32 GEMM on 256 x 256 tiles for grids that fill every CU with whole tiles.
+//
+// One work-group per CU, 4 waves of 128 x 128 (4 x 4 blocks of 32x32x2 MFMA,
+// 256 accumulators per lane, kept in the accumulation registers): per MFMA a
+// wave reads half the fragment bytes of a 64 x 64 wave tile, and per output
+// element the operands are read from L2 half as often as with 128 x 128 tiles
+// (the larger block tiles of "How a Matmul Kernel Gets Fast", section 9, and
+// the warp tiles of its section 13, here one 64-lane wave per sub-tile).
+//
+// The operands go from memory straight into LDS (buffer_load_dwordx4 with the
+// lds flag: each lane's 16 bytes land at the instruction's LDS base + 16 *
+// lane), so no registers stage them: slices of 16 k in four LDS stages of
+// 32 KB, the loads of slice t+3 issued while slice t is multiplied.  With one
+// wave per SIMD nothing else hides a stall, and a wave issues in order, so
+// every load, fragment read and address computation is placed right after an
+// MFMA, where it goes out while the matrix core works.
+//
+// Ordering without __syncthreads (its fence would wait for every load in
+// flight): at the top of slice t each wave waits until at most the 16 loads
+// of slices t+1 and t+2 are outstanding (vector-memory counts complete in
+// order) and for its own LDS reads, then joins an s_barrier; past it every
+// wave's part of slice t is in LDS and every wave is done with the stage that
+// slice t+3 is loaded into.
+//
+// LDS layouts, per operand and slice (16 KB):
+//   rows of k (A as given, B given transposed): 256 rows of 16 floats (64
+//   bytes, 4 chunks of 4 floats); chunk c of row x sits at position
+//   c ^ ((x >> 2) & 3), which keeps the 16-byte fragment reads free of bank
+//   conflicts.  One load instruction fills 16 rows.
+//   rows of x (B as given, A given transposed): 16 rows of 256 floats (1 KB,
+//   one load instruction each); rows 8..15, read by the second half-wave,
+//   are rotated by 32 floats so that the two half-waves, which read rows
+//   k and k + 8 at the same x, fall in opposite halves of the bank space.
+#include <cstdint>
+
+#include "gemm_internal.hpp"
+
+namespace sgemm {
+namespace {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+enum : int { kKRows = 0, kXRows = 1 };   // rows of k (x-major pairs) / rows of x
+
+constexpr int BM = 256, BN = 256, BK = 16;
+constexpr int NT = 256;
+constexpr int WT = 128;                  // wave tile
+constexpr int BLK = WT / 32;             // 32x32 blocks per wave and direction
+constexpr int PANEL = 256 * BK * 4;      // bytes per operand and slice
+constexpr int STAGE = 2 * PANEL;         // 32 KB
+constexpr int NST = 4;                   // stages
+constexpr int LPO = 4;                   // load instructions per wave, operand and slice
+constexpr int LPS = 2 * LPO;
+static_assert(NST * STAGE <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float *base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, int voffset) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
+// One operand's staging: the per-lane byte offsets of its load instructions
+// (from the slice origin), the LDS bytes of each instruction's destination
+// (from the panel start), and the slice-origin resource.
+template <int L>
+struct Operand {
+    const float *X;      // first element of the tile's x range at k = 0
+    int64_t ld;
+    int off[LPO];
+    int dst[LPO];
+
+    __device__ __forceinline__ Operand(const float *base, int64_t ld_, int x0, int wave, int lane) : ld(ld_) {
+        X = L == kKRows ? base + (int64_t)x0 * ld_ : base + x0;
+#pragma unroll
+        for (int j = 0; j < LPO; ++j) {
+            if (L == kKRows) {
+                const int x = wave * 64 + 16 * j + (lane >> 2);
+                const int c = (lane & 3) ^ ((x >> 2) & 3);
+                off[j] = (x * (int)ld_ + 4 * c) * 4;
+                dst[j] = (wave * 64 + 16 * j) * BK * 4;
+            } else {
+                const int k = wave * LPO + j;
+                const int c = k >= BK / 2 ? (lane + 8) & 63 : lane;
+                off[j] = (k * (int)ld_ + 4 * c) * 4;
+                dst[j] = k * 256 * 4;
+            }
+        }
+    }
+    __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice(int k0) const {
+        if (L == kKRows) return rsrc(X + k0, (int)((255 * ld + BK) * 4));
+        return rsrc(X + (int64_t)k0 * ld, (int)(((BK - 1) * ld + 256) * 4));
+    }
+};
+
+// Fragment addresses of one operand for the lane: x = xw + 32 b + l % 32, the
+// half h = l / 32 owns k = 8 h .. 8 h + 7 of each slice.  frag(e-half j)
+// returns the four k steps 4 j .. 4 j + 3 of every block.
+template <int L>
+struct FragAddr {
+    int a[BLK];          // rows of k: byte address of the lane's chunk 2 h (chunk 2 h + 1 is a[b] ^ 16)
+                         // rows of x: byte address of row 8 h, column x (rotated for h = 1)
+    __device__ __forceinline__ FragAddr(int xw, int h, int l32) {
+#pragma unroll
+        for (int b = 0; b < BLK; ++b) {
+            const int x = xw + 32 * b + l32;
+            if (L == kKRows) a[b] = x * BK * 4 + ((2 * h) ^ ((x >> 2) & 3)) * 16;
+            else a[b] = (8 * h) * 1024 + ((x - 32 * h) & 255) * 4;
+        }
+    }
+};
+
+struct Frag {
+    float a[BLK][4];
+    float b[BLK][4];
+};
+
+// Piece q (0 .. 4 + 4 BLK - 1 for one operand of each layout) of the fragment
+// reads of half j: for rows of k, piece b reads block b's 16-byte chunk; for
+// rows of x, piece 4 b + e reads block b at k step e.
+template <int L>
+__device__ __forceinline__ void read_piece(const unsigned char *panel, const FragAddr<L> &fa, int j, int q,
+                                           float (&f)[BLK][4]) {
+    if (L == kKRows) {
+        // chunk 2 h + j: positions of chunks 2h and 2h+1 differ in bit 0 of the position only
+        const int addr = fa.a[q] ^ (j * 16);
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(panel + addr);
+        f[q][0] = v[0];
+        f[q][1] = v[1];
+        f[q][2] = v[2];
+        f[q][3] = v[3];
+    } else {
+        const int b = q >> 2, e = q & 3;
+        f[b][e] = *reinterpret_cast<const float *>(panel + fa.a[b] + (4 * j + e) * 1024);
+    }
+}
+
+template <int L>
+constexpr int pieces() { return L == kKRows ? BLK : 4 * BLK; }
+
+template <int LA, int LB>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sgemm_big_kernel(
+    GemmArgs g, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, l32 = lane & 31;
+
+    const Operand<LA> opa(g.A, g.lda, m0, wave, lane);
+    const Operand<LB> opb(g.B, g.ldb, n0, wave, lane);
+    auto issue_one = [&](int slice, int stage, int i) {
+        const int k0 = slice * BK;
+        unsigned char *st = smem + stage * STAGE;
+        if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.off[i]);
+        else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.off[i - LPO]);
+    };
+
+    f32x16 acc[BLK][BLK];
+#pragma unroll
+    for (int i = 0; i < BLK; ++i)
+#pragma unroll
+        for (int j = 0; j < BLK; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+    const FragAddr<LA> fra(wm * WT, h, l32);
+    const FragAddr<LB> frb(wn * WT, h, l32);
+    constexpr int PA = pieces<LA>(), PB = pieces<LB>();
+    auto read = [&](const unsigned char *st, int j, int q, Frag &f) {
+        if (q < PA) read_piece<LA>(st, fra, j, q, f.a);
+        else read_piece<LB>(st + PANEL, frb, j, q - PA, f.b);
+    };
+    // MFMA i of a half: k step e = i / 16, block (i / 4) % 4, (i % 4).
+    auto mfma_one = [&](const Frag &f, int i) {
+        const int e = i / (BLK * BLK), ib = (i / BLK) % BLK, jb = i % BLK;
+        acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[ib][e], f.b[jb][e], acc[ib][jb], 0, 0, 0);
+    };
+
+    const int nk = g.K / BK;
+    // Slices past the end are loaded again as the last one, into stages that
+    // are never read, so every slice issues the same number of loads.
+#pragma unroll
+    for (int s = 0; s < NST - 1; ++s)
+#pragma unroll
+        for (int i = 0; i < LPS; ++i) issue_one(s < nk ? s : nk - 1, s, i);
+
+    Frag f0, f1;
+#pragma unroll
+    for (int b = 0; b < BLK; ++b)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            f1.a[b][e] = 0.f;
+            f1.b[b][e] = 0.f;
+        }
+    constexpr int MF = 4 * BLK * BLK;   // MFMAs per half slice: 64
+    static_assert(PA + PB + LPS <= MF, "every other instruction follows an MFMA");
+    //   phase 1: the MFMAs of the previous slice's second half (zeros before
+    //            the first slice), each followed by one fragment read of this
+    //            slice's first half or one load of slice t+3;
+    //   phase 2: the MFMAs of the first half, followed by the reads of the
+    //            second half, whose MFMAs are held over to the next slice.
+    for (int t = 0; t < nk; ++t) {
+        // vmcnt(16) (two slices still in flight) and lgkmcnt(0); expcnt not waited on.
+        __builtin_amdgcn_s_waitcnt((1 << 14) | (0 << 8) | (7 << 4) | 0);
+        __builtin_amdgcn_s_barrier();
+        const int ld_slice = t + NST - 1 < nk ? t + NST - 1 : nk - 1;
+        const int ld_stage = (t + NST - 1) % NST;
+        const unsigned char *st = smem + (t % NST) * STAGE;
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            mfma_one(f1, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < PA + PB) read(st, 0, i, f0);
+            else if (i < PA + PB + LPS) issue_one(ld_slice, ld_stage, i - PA - PB);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+            mfma_one(f0, i);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < PA + PB) read(st, 1, i, f1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < MF; ++i) mfma_one(f1, i);
+    // Every load issued (including the repeated last slice) has landed before
+    // the work-group can end and its LDS be given to another.
+    __builtin_amdgcn_s_waitcnt(0);
+
+    // Epilogue in four passes of one block row (4 blocks, 64 values per
+    // lane): the C reads of a pass are issued together before its stores,
+    // which are non-temporal (C is not read again here).  Accumulator register
+    // r of a block holds row 8 (r / 4) + 4 h + r % 4, column l % 32.
+    float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
+    const float alpha = g.alpha, beta = g.beta;
+#pragma unroll
+    for (int ib = 0; ib < BLK; ++ib) {
+        float cv[BLK][16];
+        if (beta != 0.f) {
+#pragma unroll
+            for (int jb = 0; jb < BLK; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int rr = wm * WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                    cv[jb][r] = Cb[(int64_t)rr * g.ldc + wn * WT + 32 * jb + l32];
+                }
+        }
+#pragma unroll
+        for (int jb = 0; jb < BLK; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int rr = wm * WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                float v = alpha * acc[ib][jb][r];
+                if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
+                __builtin_nontemporal_store(v, &Cb[(int64_t)rr * g.ldc + wn * WT + 32 * jb + l32]);
+            }
+    }
+}
+
+template <int LA, int LB>
+hipError_t launch(const GemmArgs &g, hipStream_t stream) {
+    const int tiles_m = g.M / BM, tiles_n = g.N / BN;
+    hipLaunchKernelGGL((sgemm_big_kernel<LA, LB>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, g, tiles_m,
+                       tiles_n);
+    return hipGetLastError();
+}
+
+bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
+}  // namespace
+
+// Whole 256 x 256 tiles only (M and N multiples of 256, K of 16), 16-byte
+// aligned operands with row strides that are multiples of 4, and offsets that
+// fit the 32-bit buffer offsets.
+bool big_tile_fits(const GemmArgs &g) {
+    if (g.M % BM || g.N % BN || g.K % BK || g.K < BK) return false;
+    if (!aligned16(g.A) || !aligned16(g.B) || g.lda % 4 || g.ldb % 4) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    auto span = [&](bool krows, int64_t ld) { return krows ? (255 * ld + BK) * 4 : ((BK - 1) * ld + 256) * 4; };
+    return span(!g.trans_a, g.lda) < lim && span(g.trans_b, g.ldb) < lim;
+}
+
+int64_t big_tiles(int M, int N) { return (int64_t)(M / BM) * (N / BN); }
+
+hipError_t launch_big(const GemmArgs &g, hipStream_t stream) {
+    // A as given has rows of k; B as given has rows of x (N); a transposed
+    // operand swaps.
+    const bool ta = g.trans_a != 0, tb = g.trans_b != 0;
+    if (!ta && !tb) return launch<kKRows, kXRows>(g, stream);
+    if (!ta && tb) return launch<kKRows, kKRows>(g, stream);
+    if (ta && !tb) return launch<kXRows, kXRows>(g, stream);
+    return launch<kXRows, kKRows>(g, stream);
+}
+
+}  // namespace sgemm

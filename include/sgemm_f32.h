@@ -88,8 +88,9 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
     SGEMM_F32_SKINNY = 4,         /* M <= 16: FP32 MFMA streaming kernel */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
-    SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's, or
-                                     64x64 tiles with two slices in flight (16-byte loads) */
+    SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
+                                     64x64 tiles with two slices in flight, or 256x256 tiles
+                                     (16-byte loads) */
     SGEMM_F32_NUM_VARIANTS = 7
 };
 
@@ -102,7 +103,10 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_64x64_PF2 = 4,  /* 64x64, two slices in flight; 16-byte loads only */
     SGEMM_F32_CFG_128x128_STREAMK = 5, /* 128x128, persistent with stream-K; 16-byte loads only */
     SGEMM_F32_CFG_64x64_BK64 = 6, /* 64x64, slices of 64, two in flight; 16-byte loads only */
-    SGEMM_F32_NUM_CONFIGS = 7
+    SGEMM_F32_CFG_256x256 = 7,    /* 256x256, one work-group per CU, operands loaded straight into
+                                     LDS; whole tiles only (M and N multiples of 256, K of 16),
+                                     16-byte loads, no K split, group_m ignored (4 is used) */
+    SGEMM_F32_NUM_CONFIGS = 8
 };
 
 /*
@@ -214,6 +218,15 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * by a second kernel.  It takes no split count (splits must be 1) and uses
  * the stream's workspace (2 * 128 * 128 floats per resident work-group, 64 MiB
  * on MI355X) when tiles are shared.
+ * Configuration 7 computes 256 x 256 tiles, one work-group per compute unit,
+ * with the operands copied from memory straight into LDS; it covers whole tiles
+ * only: M and N multiples of 256, K a multiple of 16, the 16-byte-load
+ * conditions, and 256 stored rows of an operand read along k (16 of one read
+ * along M or N) spanning less than 2 GiB; SGEMM_F32_ERR_NOT_APPLICABLE
+ * otherwise.  Its split count and grouping are ignored.  The automatic choice
+ * takes it for such shapes when the 256 x 256 grid fills at least 95 % of its
+ * rounds of 256 tiles and the plan would otherwise be the 128 x 128 grid
+ * without a split.
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -261,3 +261,70 @@ def test_streamk_repeat_bitwise_identical(sg):
     r2 = run_cfg(sg, 5, 8, 1, 0, 0, A, B, C0, 1.0, 0.5)
     assert r1[0] == 0 and r2[0] == 0
     assert np.array_equal(r1[1].view(np.uint32), r2[1].view(np.uint32))
+
+
+# ---------------------------------------------------------------------------
+# Configuration 7: 256x256 tiles, operands copied straight into LDS.  Whole
+# tiles only; K a multiple of 16 (one slice is 16 deep, three are fetched
+# ahead, so short K exercises the repeated loads past the end).
+# ---------------------------------------------------------------------------
+BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024)]
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", BIG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in BIG_SHAPES])
+def test_config7_real(sg, form, shape):
+    M, N, K = shape
+    ta, tb = form
+    say(f"[cfg7_real] {form} {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 900 + M + N + K)
+    st, C, As, Bs = run_cfg(sg, 7, 8, 1, ta, tb, A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 1.25, -0.5, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+def test_config7_integer_bitexact(sg, form):
+    M, N, K = 512, 768, 400
+    ta, tb = form
+    say(f"[cfg7_int] {form}")
+    A, B, C0 = _inputs(M, N, K, "int4", 910)
+    st, C, As, Bs = run_cfg(sg, 7, 8, 1, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 1.5, -0.5, C0, exact=True)
+    assert ok, info
+
+
+def test_config7_beta_zero_ignores_nan_c(sg):
+    M, N, K = 512, 512, 64
+    A, B, _ = _inputs(M, N, K, "uniform", 911)
+    C0 = np.full((M, N), np.nan, np.float32)
+    st, C, As, Bs = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check(C, As, Bs, 0, 0, 1.0, 0.0, None, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("form", [(0, 0), (1, 1)], ids=["nn", "tt"])
+def test_config7_padded_strides(sg, form):
+    """Row strides wider than the stored rows (multiples of 4), C included."""
+    M, N, K = 512, 512, 96
+    ta, tb = form
+    A, B, C0 = _inputs(M, N, K, "uniform", 912)
+    As, Bs = _stored(A, ta), _stored(B, tb)
+    lda, ldb, ldc = As.shape[1] + 12, Bs.shape[1] + 4, N + 20
+    bA, pA, _ = to_device_padded(As, lda)
+    bB, pB, _ = to_device_padded(Bs, ldb)
+    bC, pC, _ = to_device_padded(C0, ldc, fill=np.float32(-7.25))
+    st = sg.sgemm_f32_ex_config(7, 8, 1, ta, tb, M, N, K, 0.75, pA, lda, pB, ldb, 0.5, pC, ldc,
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    host = bC.cpu().numpy()
+    C = from_device_padded(bC, M, N, ldc)
+    ok, info = check(C, As, Bs, ta, tb, 0.75, 0.5, C0, exact=False)
+    assert ok, info
+    # the padding between rows of C is untouched
+    gaps = np.lib.stride_tricks.as_strided(host[N:], shape=(M - 1, ldc - N), strides=(ldc * 4, 4))
+    assert np.all(gaps == np.float32(-7.25))

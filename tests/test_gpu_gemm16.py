@@ -197,3 +197,19 @@ def test_gemm16_big_tiles_integer_bitexact(sg, kind):
     vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 0, 1, 1.0, -1.0, C0)
     ok, info = oracle.check_bitexact(C[rows, cols], vals)
     assert ok, info
+
+
+@pytest.mark.parametrize("K", [8, 64, 192])
+def test_gemm16_big_tiles_short_k_bitexact(sg, K):
+    """The larger-tile kernel fetches three 32-deep slices ahead; with only
+    two to six slices (K padded to 64 or 192) the loads past the end repeat
+    the last slice into stages that are never read."""
+    M, N = 4096, 4096
+    say(f"[g16_big_short_k] K={K}")
+    A, B, C0 = _inputs16(M, N, K, "int4", 1, 60 + K)
+    st, C, As, Bs = run16(sg, 1, 0, 1, A, B, C0, 1.0, -1.0)
+    assert st == 0
+    rows, cols = sample_positions(M, N, 3000, seed=61)
+    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, 1, rows, cols, 0, 1, 1.0, -1.0, C0)
+    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    assert ok, info

@@ -96,7 +96,8 @@ def test_empty_outputs_return_without_work(sg):
 
 def test_kernel_selection(sg):
     al = 0x100000          # 16-byte aligned stand-in pointers (never dereferenced)
-    assert sg.sgemm_f32_select(4096, 4096, 4096, 1.5, al, 4096, al, 4096) == sg.MFMA_LARGE
+    # 4096^3: whole 256x256 tiles filling one round (configuration 7, reported as the tuned plan)
+    assert sg.sgemm_f32_select(4096, 4096, 4096, 1.5, al, 4096, al, 4096) == sg.MFMA_TUNED
     assert sg.sgemm_f32_select(4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
     # Shapes with few 128x128 tiles: the small tile, or the tuning table's plan.
     assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
@@ -133,7 +134,8 @@ def test_transposed_kernel_selection(sg):
     al = 0x100000
     sel = sg.sgemm_f32_ex_select
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
-        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_LARGE
+        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_TUNED
+        assert sel(ta, tb, 4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
         assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
@@ -145,7 +147,11 @@ def test_transposed_kernel_selection(sg):
     # stored along M or N 32 rows.
     big = (1 << 31) // 4 // 100          # 128 rows of this stride exceed 2 GiB, 32 rows do not
     assert sel(0, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_SCALAR
-    assert sel(1, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_LARGE
+    # A stored transposed (along M): 16-byte loads; the 256x256 tiles read 16 of its rows per slice.
+    ld = big - big % 4
+    assert sel(1, 0, 4096, 4096, 4096, 1.0, al, ld, al, 4096) == sg.MFMA_TUNED
+    assert sg.sgemm_f32_ex_plan(1, 0, 4096, 4096, 4096, 1.0, al, ld, al, 4096)[2] == sg.CFG_256x256
+    assert sel(1, 0, 4092, 4092, 4092, 1.0, al, ld, al, 4092) == sg.MFMA_LARGE
 
 
 def test_gemm16_argument_errors_without_touching_the_gpu(sg):
@@ -170,7 +176,7 @@ def test_variant_names_and_version(sg):
     assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar", "mfma_tuned"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
-    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64"]
+    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64", "256x256"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -220,9 +226,12 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
                   (2560, 2560, 2560)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
-    for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092), (6144, 6144, 2048),
-                  (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
+    for shape in [(4092, 4092, 4092), (6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024),
+                  (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128, shape
+    # Whole, well-filled 256x256 grids take the larger tile.
+    for shape in [(4096, 4096, 4096), (8192, 8192, 8192)]:
+        assert plan(*shape)[2] == sg.CFG_256x256, shape
     # The persistent stream-K configuration is never chosen automatically.
     for shape in [(3000, 3000, 3000), (2900, 4100, 2048), (5000, 5000, 1000)]:
         assert plan(*shape)[2] != sg.CFG_128x128_STREAMK, shape
@@ -261,6 +270,8 @@ def test_plan_follows_the_tuning_table(sg):
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
         if cfg == sg.CFG_64x64_PF2 and e["config"] == 0:
             continue        # the switch to 64x64 tiles for poorly filled rounds
+        if cfg == sg.CFG_256x256 and e["config"] == 0 and e["splits"] == 1:
+            continue        # whole, well-filled 256x256 grids
         assert (cfg, gm) == (e["config"], e["group_m"]), e
         k_per = -(-K // e["splits"])
         k_per = -(-k_per // 32) * 32
@@ -391,3 +402,29 @@ def test_traffic_hash_ignores_comments_not_code():
     changed = dict(srcs)
     changed[first] = srcs[first] + "\nint extra_symbol = 0;\n"
     assert bench.kernel_source_hash(changed) != h
+
+
+def test_big_tiles_for_whole_filled_grids(sg):
+    """Configuration 7 (256x256) is chosen for grids of whole 256x256 tiles that
+    fill at least 95 % of their rounds of 256, and only where the plan would
+    otherwise be the plain 128x128 grid; forced on a shape it cannot cover it
+    refuses before any launch."""
+    al = 0x100000
+    plan = lambda ta, tb, M, N, K, lda, ldb: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, lda, al, ldb)
+    for ta, tb in ((0, 0), (0, 1), (1, 0), (1, 1)):
+        st, v, c, gm, s = plan(ta, tb, 4096, 4096, 4096, 4096, 4096)
+        assert (st, v, c, s) == (0, sg.MFMA_TUNED, sg.CFG_256x256, 1), (ta, tb)
+    for M, N, K in ((8192, 8192, 8192), (4096, 8192, 4096), (8192, 4096, 1024)):
+        assert plan(0, 0, M, N, K, K, N)[2] == sg.CFG_256x256, (M, N, K)
+    # Not whole tiles, K not a multiple of 16, misaligned, too few or poorly filled rounds.
+    assert plan(0, 0, 4092, 4092, 4092, 4092, 4092)[2] != sg.CFG_256x256
+    assert plan(0, 0, 4096, 4096, 4104, 4104, 4096)[2] != sg.CFG_256x256
+    assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096)[1] == sg.MFMA_SCALAR
+    assert plan(0, 0, 2048, 2048, 2048, 2048, 2048)[2] != sg.CFG_256x256
+    assert plan(0, 0, 6144, 6144, 2048, 2048, 6144)[2] != sg.CFG_256x256     # 576 tiles: 75 % of 3 rounds
+    p = 0x100000
+    for M, N, K in ((4092, 4096, 4096), (4096, 4100, 4096), (4096, 4096, 4100), (4096, 4096, 8)):
+        assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, M, N, K, 1.0, p, K, p, N, 0.0, p, N, 0) \
+            == sg.ERR_NOT_APPLICABLE, (M, N, K)
+    assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, 512, 512, 64, 1.0, p + 4, 64, p, 512, 0.0, p, 512, 0) \
+        == sg.ERR_NOT_APPLICABLE
