@@ -41,7 +41,7 @@ METRIC_16 = "GEMM TFLOP/s with {} inputs and FP32 accumulation at {} on 1 MI355X
 PEAK_HBM_GBS = 8000.0
 KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_big.hip", "fp32_sgemm_amd/csrc/sgemm_mfma.hip",
                   "fp32_sgemm_amd/csrc/gemm_internal.hpp")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_large_square4096_ab.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_big_square4096_ab.txt")
 
 
 # --- closed-form work and byte counts ------------------------------------------------
