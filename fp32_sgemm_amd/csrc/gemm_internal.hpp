@@ -48,7 +48,8 @@ int mfma_effective_splits(int K, int splits, int *k_per);
 // 256 x 256 tiles, one work-group per CU (sgemm_big.hip): whether the
 // product fits them (whole tiles, aligned operands), their count, and the
 // launcher.
-bool big_tile_fits(const GemmArgs &g);
+bool big_tile_fits(const GemmArgs &g);   // operands (C's stride: big_tile_c_fits)
+bool big_tile_c_fits(int64_t ldc);
 int64_t big_tiles(int M, int N);
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);

@@ -173,7 +173,7 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
                    int ldb) {
     if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
         return p;
-    sgemm::GemmArgs g;
+    sgemm::GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.B = B;
     g.lda = lda; g.ldb = ldb;
@@ -218,7 +218,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     if (!config_fits(config, g.trans_a, g.trans_b, g.lda, g.ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
-    if (config == 7 && !sgemm::big_tile_fits(g)) return SGEMM_F32_ERR_NOT_APPLICABLE;
+    if (config == 7 && !(sgemm::big_tile_fits(g) && sgemm::big_tile_c_fits(g.ldc))) return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
     const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
     if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
@@ -259,6 +259,9 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
         p = auto_plan(ta, tb, M, N, K, A, lda, B, ldb);
     }
+    // The plan does not see C: a row stride of C too wide for the 256x256
+    // tiles' 32-bit offsets keeps the 128x128 grid.
+    if (p.config == 7 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
     switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;

@@ -54,6 +54,12 @@ constexpr int LPO = 4;                   // load instructions per wave, operand 
 constexpr int LPS = 2 * LPO;
 static_assert(NST * STAGE <= 160 * 1024, "LDS");
 
+__device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
+// Vector-memory buffer store: offsets at or past the extent are dropped.
+__device__ void raw_buffer_store_f32(float v, __amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
+    __asm("llvm.amdgcn.raw.ptr.buffer.store.f32");
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const float *base, int bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(base), (short)0, bytes, 0x00020000);
 }
@@ -62,17 +68,28 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned ch
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
 }
 
+// A lane offset past every resource extent used here (extents stay below
+// 2^31 bytes): the load writes zeros to LDS and touches no memory.
+constexpr int kOutOfRange = (int)0x80000000u;
+
 // One operand's staging: the per-lane byte offsets of its load instructions
 // (from the slice origin), the LDS bytes of each instruction's destination
-// (from the panel start), and the slice-origin resource.
-template <int L>
+// (from the panel start), and the slice-origin resource.  EDGE: the tile
+// crosses the operand's extent along x (xs valid values of x) or the slice
+// crosses K; every group that lies outside gets an out-of-range offset, so
+// LDS receives zeros there (adding exact zeros changes no sum).
+template <int L, bool EDGE>
 struct Operand {
     const float *X;      // first element of the tile's x range at k = 0
     int64_t ld;
+    int xs, K;
     int off[LPO];
     int dst[LPO];
+    int gx[LPO];         // x of the lane's group (rows of k: its row; rows of x: its first column)
+    int gk[LPO];         // k of the lane's group (rows of k: its first k; rows of x: its row)
 
-    __device__ __forceinline__ Operand(const float *base, int64_t ld_, int x0, int wave, int lane) : ld(ld_) {
+    __device__ __forceinline__ Operand(const float *base, int64_t ld_, int x0, int xn, int K_, int wave, int lane)
+        : ld(ld_), xs(min(256, xn - x0)), K(K_) {
         X = L == kKRows ? base + (int64_t)x0 * ld_ : base + x0;
 #pragma unroll
         for (int j = 0; j < LPO; ++j) {
@@ -81,17 +98,25 @@ struct Operand {
                 const int c = (lane & 3) ^ ((x >> 2) & 3);
                 off[j] = (x * (int)ld_ + 4 * c) * 4;
                 dst[j] = (wave * 64 + 16 * j) * BK * 4;
+                gx[j] = x;
+                gk[j] = 4 * c;
             } else {
                 const int k = wave * LPO + j;
                 const int c = k >= BK / 2 ? (lane + 8) & 63 : lane;
                 off[j] = (k * (int)ld_ + 4 * c) * 4;
                 dst[j] = k * 256 * 4;
+                gx[j] = 4 * c;
+                gk[j] = k;
             }
         }
     }
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice(int k0) const {
-        if (L == kKRows) return rsrc(X + k0, (int)((255 * ld + BK) * 4));
+        if (L == kKRows) return rsrc(X + k0, (int)(((EDGE ? xs : 256) - 1) * ld + BK) * 4);
         return rsrc(X + (int64_t)k0 * ld, (int)(((BK - 1) * ld + 256) * 4));
+    }
+    __device__ __forceinline__ int offset(int j, int k0) const {
+        if (!EDGE) return off[j];
+        return gx[j] < xs && k0 + gk[j] < K ? off[j] : kOutOfRange;
     }
 };
 
@@ -140,25 +165,22 @@ __device__ __forceinline__ void read_piece(const unsigned char *panel, const Fra
 template <int L>
 constexpr int pieces() { return L == kKRows ? BLK : 4 * BLK; }
 
-template <int LA, int LB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sgemm_big_kernel(
-    GemmArgs g, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
-    int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+// One 256 x 256 tile at (m0, n0).  EDGE: the tile crosses M or N, or K is
+// not a multiple of the slice depth.
+template <int LA, int LB, bool EDGE>
+__device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem) {
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    const Operand<LA> opa(g.A, g.lda, m0, wave, lane);
-    const Operand<LB> opb(g.B, g.ldb, n0, wave, lane);
+    const Operand<LA, EDGE> opa(g.A, g.lda, m0, g.M, g.K, wave, lane);
+    const Operand<LB, EDGE> opb(g.B, g.ldb, n0, g.N, g.K, wave, lane);
     auto issue_one = [&](int slice, int stage, int i) {
         const int k0 = slice * BK;
         unsigned char *st = smem + stage * STAGE;
-        if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.off[i]);
-        else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.off[i - LPO]);
+        if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.offset(i, k0));
+        else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.offset(i - LPO, k0));
     };
 
     f32x16 acc[BLK][BLK];
@@ -182,7 +204,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[ib][e], f.b[jb][e], acc[ib][jb], 0, 0, 0);
     };
 
-    const int nk = g.K / BK;
+    const int nk = (g.K + BK - 1) / BK;
     // Slices past the end are loaded again as the last one, into stages that
     // are never read, so every slice issues the same number of loads.
 #pragma unroll
@@ -237,11 +259,25 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // Epilogue in four passes of one block row (4 blocks, 64 values per
     // lane): the C reads of a pass are issued together before its stores,
     // which are non-temporal (C is not read again here).  Accumulator register
-    // r of a block holds row 8 (r / 4) + 4 h + r % 4, column l % 32.
+    // r of a block holds row 8 (r / 4) + 4 h + r % 4, column l % 32.  Edge
+    // tiles go through a buffer resource over the tile's valid part of C: rows
+    // past M lie beyond its extent and columns past N get an out-of-range
+    // offset, so their loads read zero and their stores are dropped.
     float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
     const float alpha = g.alpha, beta = g.beta;
+    const int rows = min(BM, g.M - m0), cols = min(BN, g.N - n0);
+    const __amdgpu_buffer_rsrc_t rc = rsrc(Cb, EDGE ? (int)(((int64_t)(rows - 1) * g.ldc + cols) * 4) : 0);
+    // Edge offsets: a per-lane part for the block's first row and the lane's
+    // column (out of range past N), plus a wave-uniform part for register r.
+    auto roff = [&](int r) { return (8 * (r >> 2) + (r & 3)) * (int)g.ldc * 4; };
 #pragma unroll
     for (int ib = 0; ib < BLK; ++ib) {
+        int cbase[BLK];
+#pragma unroll
+        for (int jb = 0; jb < BLK; ++jb) {
+            const int cc = wn * WT + 32 * jb + l32;
+            cbase[jb] = cc < cols ? ((wm * WT + 32 * ib + 4 * h) * (int)g.ldc + cc) * 4 : kOutOfRange;
+        }
         float cv[BLK][16];
         if (beta != 0.f) {
 #pragma unroll
@@ -249,7 +285,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int rr = wm * WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
-                    cv[jb][r] = Cb[(int64_t)rr * g.ldc + wn * WT + 32 * jb + l32];
+                    const int cc = wn * WT + 32 * jb + l32;
+                    if (EDGE) cv[jb][r] = raw_buffer_load_f32(rc, cbase[jb] + roff(r), 0, 0);
+                    else cv[jb][r] = Cb[(int64_t)rr * g.ldc + cc];
                 }
         }
 #pragma unroll
@@ -257,16 +295,30 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int rr = wm * WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int cc = wn * WT + 32 * jb + l32;
                 float v = alpha * acc[ib][jb][r];
                 if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
-                __builtin_nontemporal_store(v, &Cb[(int64_t)rr * g.ldc + wn * WT + 32 * jb + l32]);
+                // cache-policy bit 1: non-temporal
+                if (EDGE) raw_buffer_store_f32(v, rc, cbase[jb] + roff(r), 0, 2);
+                else __builtin_nontemporal_store(v, &Cb[(int64_t)rr * g.ldc + cc]);
             }
     }
 }
 
 template <int LA, int LB>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sgemm_big_kernel(
+    GemmArgs g, int tiles_m, int tiles_n) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+    int tm, tn;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    if (m0 + BM > g.M || n0 + BN > g.N || g.K % BK != 0) big_tile<LA, LB, true>(g, m0, n0, smem);
+    else big_tile<LA, LB, false>(g, m0, n0, smem);
+}
+
+template <int LA, int LB>
 hipError_t launch(const GemmArgs &g, hipStream_t stream) {
-    const int tiles_m = g.M / BM, tiles_n = g.N / BN;
+    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
     hipLaunchKernelGGL((sgemm_big_kernel<LA, LB>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, g, tiles_m,
                        tiles_n);
     return hipGetLastError();
@@ -276,18 +328,21 @@ bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 
 }  // namespace
 
-// Whole 256 x 256 tiles only (M and N multiples of 256, K of 16), 16-byte
-// aligned operands with row strides that are multiples of 4, and offsets that
-// fit the 32-bit buffer offsets.
+// M, N and K multiples of 4 (the 16-byte groups never straddle an edge),
+// 16-byte aligned operands with row strides that are multiples of 4, and
+// operand slices that fit the 32-bit buffer offsets.
 bool big_tile_fits(const GemmArgs &g) {
-    if (g.M % BM || g.N % BN || g.K % BK || g.K < BK) return false;
+    if (g.M % 4 || g.N % 4 || g.K % 4 || g.K < 4) return false;
     if (!aligned16(g.A) || !aligned16(g.B) || g.lda % 4 || g.ldb % 4) return false;
     const int64_t lim = (int64_t)1 << 31;
     auto span = [&](bool krows, int64_t ld) { return krows ? (255 * ld + BK) * 4 : ((BK - 1) * ld + 256) * 4; };
     return span(!g.trans_a, g.lda) < lim && span(g.trans_b, g.ldb) < lim;
 }
 
-int64_t big_tiles(int M, int N) { return (int64_t)(M / BM) * (N / BN); }
+// Edge tiles address their part of C with 32-bit buffer offsets.
+bool big_tile_c_fits(int64_t ldc) { return (255 * ldc + BN) * 4 < ((int64_t)1 << 31); }
+
+int64_t big_tiles(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream) {
     // A as given has rows of k; B as given has rows of x (N); a transposed

@@ -264,11 +264,14 @@ def test_streamk_repeat_bitwise_identical(sg):
 
 
 # ---------------------------------------------------------------------------
-# Configuration 7: 256x256 tiles, operands copied straight into LDS.  Whole
-# tiles only; K a multiple of 16 (one slice is 16 deep, three are fetched
-# ahead, so short K exercises the repeated loads past the end).
+# Configuration 7: 256x256 tiles, operands copied straight into LDS.  M, N and
+# K multiples of 4; edge tiles get zeros past M, N and K in LDS and masked
+# stores.  One slice is 16 deep and three are fetched ahead, so short K
+# exercises the repeated loads past the end.
 # ---------------------------------------------------------------------------
-BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024)]
+BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024),
+              # edge tiles: M, N not multiples of 256, K not of 16 (multiples of 4)
+              (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4)]
 
 
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
@@ -286,7 +289,7 @@ def test_config7_real(sg, form, shape):
 
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_config7_integer_bitexact(sg, form):
-    M, N, K = 512, 768, 400
+    M, N, K = 516, 772, 404
     ta, tb = form
     say(f"[cfg7_int] {form}")
     A, B, C0 = _inputs(M, N, K, "int4", 910)
@@ -328,3 +331,10 @@ def test_config7_padded_strides(sg, form):
     # the padding between rows of C is untouched
     gaps = np.lib.stride_tricks.as_strided(host[N:], shape=(M - 1, ldc - N), strides=(ldc * 4, 4))
     assert np.all(gaps == np.float32(-7.25))
+
+
+def test_config7_rejects_what_it_cannot_cover(sg):
+    """M, N or K not a multiple of 4: refused before any launch."""
+    A, B, C0 = _inputs(258, 256, 64, "uniform", 913)
+    st, _, _, _ = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
+    assert st == sg.ERR_NOT_APPLICABLE

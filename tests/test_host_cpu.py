@@ -98,7 +98,8 @@ def test_kernel_selection(sg):
     al = 0x100000          # 16-byte aligned stand-in pointers (never dereferenced)
     # 4096^3: whole 256x256 tiles filling one round (configuration 7, reported as the tuned plan)
     assert sg.sgemm_f32_select(4096, 4096, 4096, 1.5, al, 4096, al, 4096) == sg.MFMA_TUNED
-    assert sg.sgemm_f32_select(4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
+    assert sg.sgemm_f32_select(4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_TUNED
+    assert sg.sgemm_f32_select(3000, 3000, 3000, 1.0, al, 3000, al, 3000) == sg.MFMA_TUNED
     # Shapes with few 128x128 tiles: the small tile, or the tuning table's plan.
     assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
     assert sg.sgemm_f32_select(128, 128, 128, 1.0, al, 128, al, 128) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
@@ -135,7 +136,8 @@ def test_transposed_kernel_selection(sg):
     sel = sg.sgemm_f32_ex_select
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_TUNED
-        assert sel(ta, tb, 4092, 4092, 4092, 1.0, al, 4092, al, 4092) == sg.MFMA_LARGE
+        assert sel(ta, tb, 6144, 6144, 2048, 1.0, al, 6144 if ta else 2048, al, 2048 if tb else 6144) \
+            == sg.MFMA_LARGE
         assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
@@ -151,7 +153,7 @@ def test_transposed_kernel_selection(sg):
     ld = big - big % 4
     assert sel(1, 0, 4096, 4096, 4096, 1.0, al, ld, al, 4096) == sg.MFMA_TUNED
     assert sg.sgemm_f32_ex_plan(1, 0, 4096, 4096, 4096, 1.0, al, ld, al, 4096)[2] == sg.CFG_256x256
-    assert sel(1, 0, 4092, 4092, 4092, 1.0, al, ld, al, 4092) == sg.MFMA_LARGE
+    assert sel(1, 0, 4094, 4092, 4092, 1.0, al, ld, al, 4092) == sg.MFMA_LARGE
 
 
 def test_gemm16_argument_errors_without_touching_the_gpu(sg):
@@ -226,11 +228,10 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
                   (2560, 2560, 2560)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
-    for shape in [(4092, 4092, 4092), (6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024),
-                  (2816, 2816, 2816)]:
+    for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128, shape
-    # Whole, well-filled 256x256 grids take the larger tile.
-    for shape in [(4096, 4096, 4096), (8192, 8192, 8192)]:
+    # Well-filled 256x256 grids take the larger tile.
+    for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092)]:
         assert plan(*shape)[2] == sg.CFG_256x256, shape
     # The persistent stream-K configuration is never chosen automatically.
     for shape in [(3000, 3000, 3000), (2900, 4100, 2048), (5000, 5000, 1000)]:
@@ -405,8 +406,8 @@ def test_traffic_hash_ignores_comments_not_code():
 
 
 def test_big_tiles_for_whole_filled_grids(sg):
-    """Configuration 7 (256x256) is chosen for grids of whole 256x256 tiles that
-    fill at least 95 % of their rounds of 256, and only where the plan would
+    """Configuration 7 (256x256) is chosen for grids of 256x256 tiles that fill
+    at least 95 % of their rounds of 256, and only where the plan would
     otherwise be the plain 128x128 grid; forced on a shape it cannot cover it
     refuses before any launch."""
     al = 0x100000
@@ -416,15 +417,18 @@ def test_big_tiles_for_whole_filled_grids(sg):
         assert (st, v, c, s) == (0, sg.MFMA_TUNED, sg.CFG_256x256, 1), (ta, tb)
     for M, N, K in ((8192, 8192, 8192), (4096, 8192, 4096), (8192, 4096, 1024)):
         assert plan(0, 0, M, N, K, K, N)[2] == sg.CFG_256x256, (M, N, K)
-    # Not whole tiles, K not a multiple of 16, misaligned, too few or poorly filled rounds.
-    assert plan(0, 0, 4092, 4092, 4092, 4092, 4092)[2] != sg.CFG_256x256
-    assert plan(0, 0, 4096, 4096, 4104, 4104, 4096)[2] != sg.CFG_256x256
+    # Edge tiles are covered when M, N and K are multiples of 4 (4092^3: 16 x 16 tiles, the last 252 wide).
+    assert plan(0, 0, 4092, 4092, 4092, 4092, 4092)[2] == sg.CFG_256x256
+    assert plan(1, 1, 4092, 4092, 4092, 4092, 4092)[2] == sg.CFG_256x256
+    # M, N or K not a multiple of 4, misaligned, too few or poorly filled rounds.
+    assert plan(0, 0, 4094, 4096, 4096, 4096, 4096)[2] != sg.CFG_256x256
+    assert plan(0, 0, 4096, 4096, 4098, 4098, 4096)[2] != sg.CFG_256x256
     assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096)[1] == sg.MFMA_SCALAR
     assert plan(0, 0, 2048, 2048, 2048, 2048, 2048)[2] != sg.CFG_256x256
     assert plan(0, 0, 6144, 6144, 2048, 2048, 6144)[2] != sg.CFG_256x256     # 576 tiles: 75 % of 3 rounds
     p = 0x100000
-    for M, N, K in ((4092, 4096, 4096), (4096, 4100, 4096), (4096, 4096, 4100), (4096, 4096, 8)):
-        assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, M, N, K, 1.0, p, K, p, N, 0.0, p, N, 0) \
+    for M, N, K in ((4094, 4096, 4096), (4096, 4098, 4096), (4096, 4096, 4098), (4096, 4096, 2)):
+        assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, M, N, K, 1.0, p, K + K % 4, p, N + N % 4, 0.0, p, N, 0) \
             == sg.ERR_NOT_APPLICABLE, (M, N, K)
     assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, 512, 512, 64, 1.0, p + 4, 64, p, 512, 0.0, p, 512, 0) \
         == sg.ERR_NOT_APPLICABLE
