@@ -161,13 +161,27 @@ Plan quantization_plan(const Plan &p, int M, int N, int K) {
     return Plan{SGEMM_F32_MFMA_TUNED, 4, 8, 1};
 }
 
-// 256x256 tiles (configuration 7) for grids of whole tiles that fill their
-// rounds: one work-group per compute unit, so kResidentBigTiles per round.
-// Same-box per-launch medians (TFLOP/s, 128x128 -> 256x256): 4096^3 with
-// alpha 1.5, beta -0.5 143.2 -> 147.1, NT 144.6 -> 147.1; 8192^3 147.2 ->
-// 149.1; 4096 x 4096 x 1024 136.6 -> 140.4.
+// 256x256 tiles (configuration 7) for grids that fill their rounds: one
+// work-group per compute unit, so kResidentBigTiles per round.  The fill is
+// the share of the rounds' tile area that lies inside C (edge tiles count for
+// their inner part), and the 256x256 grid must fill at least kBigFill and
+// within kBigMargin of the 128x128 grid's fill (its loop runs about 2-3 %
+// faster).  Same-box per-launch medians (TFLOP/s, 128x128 -> 256x256):
+// 4096^3 with alpha 1.5, beta -0.5 143.2 -> 147.1, NT 144.6 -> 147.1; 8192^3
+// 147.2 -> 149.1; 4096 x 4096 x 1024 136.6 -> 140.4; 4092^3 137.7-139.9 ->
+// 141.6, TN 135.4 -> 142.6; 4000^3 (fill 0.95) 131-135 -> 138.5, 4032^3
+// (0.97) 136.5 -> 140.8, 3968 x 3968 x 2048 (0.94) 134.0 -> 134.9; and the
+// other way 4096 x 11008 x 512 (fill 0.90) 131 -> 120, 6144 x 6144 x 2048
+// (0.75) 144 -> 111.
 constexpr int kResidentBigTiles = 256;
-constexpr double kBigFill = 0.95;
+constexpr double kBigFill = 0.93;
+constexpr double kBigMargin = 0.02;
+
+double round_fill(int M, int N, int tile, int per_round) {
+    const int64_t tiles = (int64_t)((M + tile - 1) / tile) * ((N + tile - 1) / tile);
+    const int64_t rounds = (tiles + per_round - 1) / per_round;
+    return (double)M * N / ((double)rounds * per_round * tile * tile);
+}
 
 Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B,
                    int ldb) {
@@ -178,11 +192,9 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
     g.A = A; g.B = B;
     g.lda = lda; g.ldb = ldb;
     g.trans_a = ta; g.trans_b = tb;
-    if (!sgemm::big_tile_fits(g)) return p;
-    const int64_t tiles = sgemm::big_tiles(M, N);
-    if (tiles < kResidentBigTiles) return p;
-    const int64_t rounds = (tiles + kResidentBigTiles - 1) / kResidentBigTiles;
-    if ((double)tiles < kBigFill * (double)(rounds * kResidentBigTiles)) return p;
+    if (!sgemm::big_tile_fits(g) || sgemm::big_tiles(M, N) < kResidentBigTiles) return p;
+    const double fill = round_fill(M, N, 256, kResidentBigTiles);
+    if (fill < kBigFill || fill < round_fill(M, N, 128, kResidentLargeTiles) - kBigMargin) return p;
     return Plan{SGEMM_F32_MFMA_TUNED, 7, 4, 1};
 }
 

@@ -219,14 +219,15 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * the stream's workspace (2 * 128 * 128 floats per resident work-group, 64 MiB
  * on MI355X) when tiles are shared.
  * Configuration 7 computes 256 x 256 tiles, one work-group per compute unit,
- * with the operands copied from memory straight into LDS; it covers whole tiles
- * only: M and N multiples of 256, K a multiple of 16, the 16-byte-load
- * conditions, and 256 stored rows of an operand read along k (16 of one read
- * along M or N) spanning less than 2 GiB; SGEMM_F32_ERR_NOT_APPLICABLE
- * otherwise.  Its split count and grouping are ignored.  The automatic choice
- * takes it for such shapes when the 256 x 256 grid fills at least 95 % of its
- * rounds of 256 tiles and the plan would otherwise be the 128 x 128 grid
- * without a split.
+ * with the operands copied from memory straight into LDS.  It needs M, N and K
+ * multiples of 4, the 16-byte-load conditions, 256 stored rows of an operand
+ * read along k (16 of one read along M or N) spanning less than 2 GiB, and 256
+ * rows of C spanning less than 2 GiB; SGEMM_F32_ERR_NOT_APPLICABLE otherwise.
+ * Its split count and grouping are ignored.  The automatic choice takes it when
+ * the plan would otherwise be the 128 x 128 grid without a split, the 256 x 256
+ * grid has at least 256 tiles, and the part of its rounds (256 tiles each) that
+ * lies inside C is at least 93 % and within 2 % of the 128 x 128 grid's (a C
+ * stride too wide for it at call time keeps the 128 x 128 grid).
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */
