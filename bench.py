@@ -39,8 +39,8 @@ PEAK_FP32_TFLOPS = 157.3          # MI355X dense FP32 (vector and matrix), datas
 PEAK_16BIT_TFLOPS = 2500.0        # MI355X dense BF16 / FP16 matrix, datasheet
 METRIC_16 = "GEMM TFLOP/s with {} inputs and FP32 accumulation at {} on 1 MI355X"
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_big.hip", "fp32_sgemm_amd/csrc/sgemm_mfma.hip",
-                  "fp32_sgemm_amd/csrc/gemm_internal.hpp")
+# The headline plan's kernel (configuration 7) and the tile mapping it uses.
+KERNEL_SOURCES = ("fp32_sgemm_amd/csrc/sgemm_big.hip", "fp32_sgemm_amd/csrc/gemm_internal.hpp")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_mfma_big_square4096_ab.txt")
 
 
