@@ -107,6 +107,15 @@ template <int BM_, int BN_, int BK_, int WM_, int WN_, int PF_, int LA_, int LB_
 struct MfmaTile {
     static constexpr int BM = BM_, BN = BN_, BK = BK_, WM = WM_, WN = WN_;
     static constexpr int PF = PF_;             // slices loaded ahead of the one being computed
+    // Two slices in flight: whether the next slice's LDS stores are spread over
+    // this slice's chunks (one group after each chunk's loads) instead of
+    // issued together after its MFMAs.  Taken for the 64x64 tiles, which run
+    // one work-group per CU on the grids they serve: with one wave per SIMD,
+    // in-order issue leaves the matrix core idle while a burst of stores goes
+    // out.  Same-box per-launch medians (TFLOP/s): 1024^3 80.4 -> 85.6,
+    // 1536^3 94.5 -> 99.0, 2048^3 131 -> 135.6, 512 x 512 x 8192 (8 splits)
+    // 102.3 -> 105.9; the 128x128 tile on 6144 x 6144 x 2048 lost 1 %.
+    static constexpr bool SPREAD = BM_ * BN_ <= 64 * 64;
     static constexpr int WAVES_N = BN / WN;
     static constexpr int NT = (BM / WM) * WAVES_N * 64;
     static constexpr int MB = WM / 32;          // 32x32 accumulator blocks per wave, along M
@@ -282,6 +291,21 @@ __device__ __forceinline__ void panel_store(float *S, int tid, const float4 (&v)
         float *dst = P::L == kKMajor ? S + r * P::ROW_S + c : S + r * P::X + (r >= P::HALF ? P::SHIFT : 0) + c;
         *reinterpret_cast<float4 *>(dst) = v[i];
     }
+}
+
+template <class P>
+__device__ __forceinline__ void panel_store_one(float *S, int tid, int i, const float4 &v) {
+    const int q = tid + i * P::NT;
+    const int r = q / P::PER_ROW, c = (q % P::PER_ROW) * 4;
+    float *dst = P::L == kKMajor ? S + r * P::ROW_S + c : S + r * P::X + (r >= P::HALF ? P::SHIFT : 0) + c;
+    *reinterpret_cast<float4 *>(dst) = v;
+}
+
+template <class T>
+__device__ __forceinline__ void store_part(float *stage, int tid, int p, const float4 (&ra)[T::A_VECS],
+                                           const float4 (&rb)[T::B_VECS]) {
+    if (p < T::A_VECS) panel_store_one<typename T::PA>(stage, tid, p, ra[p]);
+    else panel_store_one<typename T::PB>(stage + T::A_STAGE, tid, p - T::A_VECS, rb[p - T::A_VECS]);
 }
 
 template <class T>
@@ -487,20 +511,25 @@ __device__ __forceinline__ void k_loop(const GemmArgs &g, int m0, int n0, int ti
             compute_slice_held<T>(smem, wm, wn, lane, acc, [&](int c) {
 #pragma unroll
                 for (int j = 0; j < PER; ++j)
-                    if (c * PER + j < PARTS)
+                    if (c * PER + j < PARTS) {
+                        if (T::SPREAD) store_part<T>(smem + T::STAGE, tid, c * PER + j, ra1, rb1);
                         load_part<T, VEC, GMN, false>(g, s, m0, n0, k2, r2, c * PER + j, ra0, rb0);
+                    }
             }, f);
-            store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
+            if (!T::SPREAD) store_slice<T>(smem + T::STAGE, tid, ra1, rb1);
             __syncthreads();
             const int k3 = k0_of(t + 3 < nk ? t + 3 : nk - 1);
             const SliceRsrc r3 = slice_rsrc<T>(g, m0, n0, k3);
+            const bool st0 = t + 2 < nk;
             compute_slice_held<T>(smem + T::STAGE, wm, wn, lane, acc, [&](int c) {
 #pragma unroll
                 for (int j = 0; j < PER; ++j)
-                    if (c * PER + j < PARTS)
+                    if (c * PER + j < PARTS) {
+                        if (T::SPREAD && st0) store_part<T>(smem, tid, c * PER + j, ra0, rb0);
                         load_part<T, VEC, GMN, false>(g, s, m0, n0, k3, r3, c * PER + j, ra1, rb1);
+                    }
             }, f);
-            if (t + 2 < nk) store_slice<T>(smem, tid, ra0, rb0);
+            if (!T::SPREAD && st0) store_slice<T>(smem, tid, ra0, rb0);
             __syncthreads();
         }
         if (t < nk) compute_slice_held<T>(smem, wm, wn, lane, acc, NoIssue(), f);
