@@ -1,4 +1,5 @@
-// FP32 GEMM on 256 x 256 tiles for grids that fill every CU with whole tiles.
+// FP32 GEMM on 256 x 256 tiles, one per CU at a time, for grids whose rounds of
+// 256 tiles lie almost entirely inside C.
 //
 // One work-group per CU, 4 waves of 128 x 128 (4 x 4 blocks of 32x32x2 MFMA,
 // 256 accumulators per lane, kept in the accumulation registers): per MFMA a
@@ -31,6 +32,14 @@
 //   one load instruction each); rows 8..15, read by the second half-wave,
 //   are rotated by 32 floats so that the two half-waves, which read rows
 //   k and k + 8 at the same x, fall in opposite halves of the bank space.
+//
+// Edges.  M, N and K are multiples of 4, so a 16-byte group never straddles
+// an edge.  Tiles that cross M or N, and every tile when K is not a multiple
+// of 16, give each group outside the matrices an out-of-range lane offset: the
+// load writes zeros to LDS without touching memory (adding exact zeros changes
+// no sum).  Their epilogue stores through a buffer resource over the valid part
+// of C, whose extent drops rows past M and whose out-of-range offsets drop
+// columns past N.
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -41,7 +50,9 @@ namespace {
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-enum : int { kKRows = 0, kXRows = 1 };   // rows of k (x-major pairs) / rows of x
+// How an operand is stored: runs along k (A as given, B given transposed) or
+// runs along x (B as given, A given transposed), x being M for A and N for B.
+enum : int { kKRows = 0, kXRows = 1 };
 
 constexpr int BM = 256, BN = 256, BK = 16;
 constexpr int NT = 256;
@@ -120,9 +131,9 @@ struct Operand {
     }
 };
 
-// Fragment addresses of one operand for the lane: x = xw + 32 b + l % 32, the
-// half h = l / 32 owns k = 8 h .. 8 h + 7 of each slice.  frag(e-half j)
-// returns the four k steps 4 j .. 4 j + 3 of every block.
+// Fragment addresses of one operand for the lane: x = xw + 32 b + l % 32; the
+// half-wave h = l / 32 owns k = 8 h .. 8 h + 7 of each slice, read in two
+// halves j = 0, 1 of four k steps (k = 8 h + 4 j + e, e < 4).
 template <int L>
 struct FragAddr {
     int a[BLK];          // rows of k: byte address of the lane's chunk 2 h (chunk 2 h + 1 is a[b] ^ 16)
