@@ -338,3 +338,16 @@ def test_config7_rejects_what_it_cannot_cover(sg):
     A, B, C0 = _inputs(258, 256, 64, "uniform", 913)
     st, _, _, _ = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
     assert st == sg.ERR_NOT_APPLICABLE
+
+
+@pytest.mark.parametrize("K", [65536, 65540])
+def test_config7_long_k_bitexact(sg, K):
+    """4096 slices through the four LDS stages (and a K tail of 4): integer
+    inputs keep every partial sum below 2**24, so the result is exact."""
+    M, N = 256, 512
+    say(f"[cfg7_long_k] K={K}")
+    A, B, C0 = _inputs(M, N, K, "int4", 914 + K % 16)
+    st, C, As, Bs = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, -1.0)
+    assert st == 0
+    ok, info = check(C, As, Bs, 0, 0, 1.0, -1.0, C0, exact=True)
+    assert ok, info
