@@ -36,7 +36,8 @@ CFG_64x64_PF2 = 4
 CFG_128x128_STREAMK = 5
 CFG_64x64_BK64 = 6
 CFG_256x256 = 7
-NUM_CONFIGS = 8
+CFG_128x128_DL = 8
+NUM_CONFIGS = 9
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

@@ -31,12 +31,13 @@ hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stre
 // 5 = 128x128 persistent with stream-K (resident work-groups take whole tiles
 // in rounds, then equal shares of the remaining tiles' K slices; split tiles
 // are summed by a fix-up kernel), 6 = 64x64 with slices of 64, 7 = 256x256
-// (sgemm_big.hip: whole tiles only, one work-group per CU).  Configurations 2-7
+// (sgemm_big.hip: one work-group per CU, operands copied straight into LDS),
+// 8 = 128x128 by the same kernel (two work-groups per CU).  Configurations 2-8
 // exist with 16-byte loads only.  `group_m` is the number of tile rows walked
 // together by the tile order (configuration 7 uses 4); `splits` divides K over
 // work-groups (the partial sums go through the stream's workspace and a
-// reduction kernel; not with configurations 5 and 7).
-constexpr int kNumMfmaConfigs = 8;
+// reduction kernel; not with configurations 5, 7 and 8).
+constexpr int kNumMfmaConfigs = 9;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
 int64_t mfma_config_tiles(int config, int M, int N);
@@ -46,12 +47,13 @@ bool mfma_config_splits_ok(int config);
 // K extent of each (a multiple of the tile depth).
 int mfma_effective_splits(int K, int splits, int *k_per);
 // 256 x 256 tiles, one work-group per CU (sgemm_big.hip): whether the
-// product fits them (whole tiles, aligned operands), their count, and the
-// launcher.
+// product fits them (M, N, K multiples of 4, aligned operands), their count,
+// and the launchers of the 256 x 256 and 128 x 128 grids.
 bool big_tile_fits(const GemmArgs &g);   // operands (C's stride: big_tile_c_fits)
 bool big_tile_c_fits(int64_t ldc);
 int64_t big_tiles(int M, int N);
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_dl128(const GemmArgs &g, int group_m, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);

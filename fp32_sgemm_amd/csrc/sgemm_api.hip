@@ -198,12 +198,40 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
     return Plan{SGEMM_F32_MFMA_TUNED, 7, 4, 1};
 }
 
+// The 128x128 grid that remains goes to the kernel of the 256x256 tiles on
+// 128x128 tiles (configuration 8: operands copied straight into LDS, two
+// work-groups per compute unit) when the operands fit it, the grid has whole
+// tiles only and K is a multiple of its slice depth 16 (otherwise every tile
+// takes its edge path).  Same-box per-launch medians (TFLOP/s, configuration
+// 0 -> 8, NN unless noted): 4096 x 11008 x 512 131.2 -> 133.4, NT 131.6 ->
+// 134.2, TN 130.6 -> 131.7; 11008 x 4096 x 512 TT 128.3 -> 131.6; 6144 x 6144
+// x 2048 142.5 -> 143.5; 2816^3 132.3 -> 136.8; 8192 x 4096 x 1024 135.5 ->
+// 139.5; 16384 x 16384 x 512 132.5 -> 133.8; 3968 x 3968 x 2048 133.7 ->
+// 135.8; 5888 x 5888 x 1024 128.9 -> 130.5; and the other way, N not a
+// multiple of 128 (rows of C not 128-byte aligned, a column of edge tiles):
+// 7000 x 7000 x 1024 133.1 -> 132.1, NT 136.1 -> 131.6; 7040 x 7000 x 1024
+// 134.2 -> 132.5; 6000 x 6000 x 2048 NT 138.0 -> 135.5; K = 3000: 3000^3
+// 100.2 -> 96.9.
+Plan dl128_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B,
+                int ldb) {
+    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
+        return p;
+    sgemm::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.B = B;
+    g.lda = lda; g.ldb = ldb;
+    g.trans_a = ta; g.trans_b = tb;
+    if (M % 128 != 0 || N % 128 != 0 || K % 16 != 0 || !sgemm::big_tile_fits(g)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 8, p.group_m, 1};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
-// grids that fill their rounds poorly, and to 256x256 tiles for grids of whole
-// 256x256 tiles that fill theirs (reported as SGEMM_F32_MFMA_TUNED when the
-// plan differs from the default).  Transposed operands use the same entries.
+// grids that fill their rounds poorly, to 256x256 tiles for grids that fill
+// theirs, and from the 128x128 kernel to configuration 8 (reported as
+// SGEMM_F32_MFMA_TUNED when the plan differs from the default).  Transposed
+// operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
     if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
@@ -219,7 +247,8 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
             if (p.config == d.config && p.group_m == d.group_m && p.splits <= 1) p = d;
         }
     }
-    return big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
+    p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
+    return dl128_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
@@ -230,7 +259,8 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     if (!config_fits(config, g.trans_a, g.trans_b, g.lda, g.ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
-    if (config == 7 && !(sgemm::big_tile_fits(g) && sgemm::big_tile_c_fits(g.ldc))) return SGEMM_F32_ERR_NOT_APPLICABLE;
+    if ((config == 7 || config == 8) && !(sgemm::big_tile_fits(g) && sgemm::big_tile_c_fits(g.ldc)))
+        return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
     const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
     if (sgemm::mfma_config_tiles(config, g.M, g.N) * eff > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
@@ -271,9 +301,9 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
         p = auto_plan(ta, tb, M, N, K, A, lda, B, ldb);
     }
-    // The plan does not see C: a row stride of C too wide for the 256x256
-    // tiles' 32-bit offsets keeps the 128x128 grid.
-    if (p.config == 7 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
+    // The plan does not see C: a row stride of C too wide for the 32-bit
+    // offsets of configurations 7 and 8 keeps the 128x128 kernel.
+    if ((p.config == 7 || p.config == 8) && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
     switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
@@ -385,6 +415,7 @@ const char *sgemm_f32_config_name(int config) {
         case 5: return "128x128_streamk";
         case 6: return "64x64_bk64";
         case 7: return "256x256";
+        case 8: return "128x128_dl";
         default: return nullptr;
     }
 }

@@ -1,5 +1,7 @@
 // FP32 GEMM on 256 x 256 tiles, one per CU at a time, for grids whose rounds of
-// 256 tiles lie almost entirely inside C.
+// 256 tiles lie almost entirely inside C; the same kernel on 128 x 128 tiles
+// (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) serves
+// whole 128 x 128 grids.  The description below is that of the 256 x 256 form.
 //
 // One work-group per CU, 4 waves of 128 x 128 (4 x 4 blocks of 32x32x2 MFMA,
 // 256 accumulators per lane, kept in the accumulation registers): per MFMA a
@@ -54,16 +56,26 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 // runs along x (B as given, A given transposed), x being M for A and N for B.
 enum : int { kKRows = 0, kXRows = 1 };
 
-constexpr int BM = 256, BN = 256, BK = 16;
-constexpr int NT = 256;
-constexpr int WT = 128;                  // wave tile
-constexpr int BLK = WT / 32;             // 32x32 blocks per wave and direction
-constexpr int PANEL = 256 * BK * 4;      // bytes per operand and slice
-constexpr int STAGE = 2 * PANEL;         // 32 KB
-constexpr int NST = 4;                   // stages
-constexpr int LPO = 4;                   // load instructions per wave, operand and slice
-constexpr int LPS = 2 * LPO;
-static_assert(NST * STAGE <= 160 * 1024, "LDS");
+constexpr int BK = 16;                   // slice depth
+constexpr int NT = 256;                  // 4 waves in a 2 x 2 arrangement
+constexpr int NST = 4;                   // LDS stages
+
+// Geometry of a TS x TS tile (TS = 256: one work-group per CU; TS = 128: the
+// same kernel on 128 x 128 tiles, two work-groups per CU).
+template <int TS>
+struct Geo {
+    static constexpr int BM = TS, BN = TS;
+    static constexpr int WT = TS / 2;             // wave tile
+    static constexpr int BLK = WT / 32;           // 32x32 blocks per wave and direction
+    static constexpr int PANEL = TS * BK * 4;     // bytes per operand and slice
+    static constexpr int STAGE = 2 * PANEL;
+    static constexpr int LPO = TS / 64;           // load instructions per wave, operand and slice
+    static constexpr int LPS = 2 * LPO;
+    static constexpr int XROW = TS * 4;           // bytes of one LDS row of an operand stored along x
+    static constexpr int XLANES = TS / 4;         // lanes per such row in one load instruction
+    static constexpr int KROWS_W = TS / 4;        // rows of an operand stored along k per wave
+    static_assert(NST * STAGE <= 160 * 1024, "LDS");
+};
 
 __device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
     __asm("llvm.amdgcn.raw.ptr.buffer.load.f32");
@@ -89,41 +101,46 @@ constexpr int kOutOfRange = (int)0x80000000u;
 // crosses the operand's extent along x (xs valid values of x) or the slice
 // crosses K; every group that lies outside gets an out-of-range offset, so
 // LDS receives zeros there (adding exact zeros changes no sum).
-template <int L, bool EDGE>
+template <int L, bool EDGE, int TS>
 struct Operand {
+    using G = Geo<TS>;
     const float *X;      // first element of the tile's x range at k = 0
     int64_t ld;
     int xs, K;
-    int off[LPO];
-    int dst[LPO];
-    int gx[LPO];         // x of the lane's group (rows of k: its row; rows of x: its first column)
-    int gk[LPO];         // k of the lane's group (rows of k: its first k; rows of x: its row)
+    int off[G::LPO];
+    int dst[G::LPO];
+    int gx[G::LPO];      // x of the lane's group (rows of k: its row; rows of x: its first column)
+    int gk[G::LPO];      // k of the lane's group (rows of k: its first k; rows of x: its row)
 
     __device__ __forceinline__ Operand(const float *base, int64_t ld_, int x0, int xn, int K_, int wave, int lane)
-        : ld(ld_), xs(min(256, xn - x0)), K(K_) {
+        : ld(ld_), xs(min(TS, xn - x0)), K(K_) {
         X = L == kKRows ? base + (int64_t)x0 * ld_ : base + x0;
 #pragma unroll
-        for (int j = 0; j < LPO; ++j) {
+        for (int j = 0; j < G::LPO; ++j) {
             if (L == kKRows) {
-                const int x = wave * 64 + 16 * j + (lane >> 2);
+                // 16 rows of 64 bytes per instruction
+                const int x = wave * G::KROWS_W + 16 * j + (lane >> 2);
                 const int c = (lane & 3) ^ ((x >> 2) & 3);
                 off[j] = (x * (int)ld_ + 4 * c) * 4;
-                dst[j] = (wave * 64 + 16 * j) * BK * 4;
+                dst[j] = (wave * G::KROWS_W + 16 * j) * BK * 4;
                 gx[j] = x;
                 gk[j] = 4 * c;
             } else {
-                const int k = wave * LPO + j;
-                const int c = k >= BK / 2 ? (lane + 8) & 63 : lane;
+                // 1 KB per instruction: 1024 / XROW rows of k
+                const int row0 = (wave * G::LPO + j) * (1024 / G::XROW);
+                const int k = row0 + lane / G::XLANES;
+                const int p = lane % G::XLANES;
+                const int c = k >= BK / 2 ? (p + 8) % G::XLANES : p;
                 off[j] = (k * (int)ld_ + 4 * c) * 4;
-                dst[j] = k * 256 * 4;
+                dst[j] = row0 * G::XROW;
                 gx[j] = 4 * c;
                 gk[j] = k;
             }
         }
     }
     __device__ __forceinline__ __amdgpu_buffer_rsrc_t slice(int k0) const {
-        if (L == kKRows) return rsrc(X + k0, (int)(((EDGE ? xs : 256) - 1) * ld + BK) * 4);
-        return rsrc(X + (int64_t)k0 * ld, (int)(((BK - 1) * ld + 256) * 4));
+        if (L == kKRows) return rsrc(X + k0, (int)(((EDGE ? xs : TS) - 1) * ld + BK) * 4);
+        return rsrc(X + (int64_t)k0 * ld, (int)(((BK - 1) * ld + TS) * 4));
     }
     __device__ __forceinline__ int offset(int j, int k0) const {
         if (!EDGE) return off[j];
@@ -134,31 +151,33 @@ struct Operand {
 // Fragment addresses of one operand for the lane: x = xw + 32 b + l % 32; the
 // half-wave h = l / 32 owns k = 8 h .. 8 h + 7 of each slice, read in two
 // halves j = 0, 1 of four k steps (k = 8 h + 4 j + e, e < 4).
-template <int L>
+template <int L, int TS>
 struct FragAddr {
-    int a[BLK];          // rows of k: byte address of the lane's chunk 2 h (chunk 2 h + 1 is a[b] ^ 16)
+    using G = Geo<TS>;
+    int a[G::BLK];       // rows of k: byte address of the lane's chunk 2 h (chunk 2 h + 1 is a[b] ^ 16)
                          // rows of x: byte address of row 8 h, column x (rotated for h = 1)
     __device__ __forceinline__ FragAddr(int xw, int h, int l32) {
 #pragma unroll
-        for (int b = 0; b < BLK; ++b) {
+        for (int b = 0; b < G::BLK; ++b) {
             const int x = xw + 32 * b + l32;
             if (L == kKRows) a[b] = x * BK * 4 + ((2 * h) ^ ((x >> 2) & 3)) * 16;
-            else a[b] = (8 * h) * 1024 + ((x - 32 * h) & 255) * 4;
+            else a[b] = (8 * h) * G::XROW + ((x - 32 * h) & (TS - 1)) * 4;
         }
     }
 };
 
+template <int TS>
 struct Frag {
-    float a[BLK][4];
-    float b[BLK][4];
+    float a[Geo<TS>::BLK][4];
+    float b[Geo<TS>::BLK][4];
 };
 
 // Piece q (0 .. 4 + 4 BLK - 1 for one operand of each layout) of the fragment
 // reads of half j: for rows of k, piece b reads block b's 16-byte chunk; for
 // rows of x, piece 4 b + e reads block b at k step e.
-template <int L>
-__device__ __forceinline__ void read_piece(const unsigned char *panel, const FragAddr<L> &fa, int j, int q,
-                                           float (&f)[BLK][4]) {
+template <int L, int TS>
+__device__ __forceinline__ void read_piece(const unsigned char *panel, const FragAddr<L, TS> &fa, int j, int q,
+                                           float (&f)[Geo<TS>::BLK][4]) {
     if (L == kKRows) {
         // chunk 2 h + j: positions of chunks 2h and 2h+1 differ in bit 0 of the position only
         const int addr = fa.a[q] ^ (j * 16);
@@ -169,24 +188,27 @@ __device__ __forceinline__ void read_piece(const unsigned char *panel, const Fra
         f[q][3] = v[3];
     } else {
         const int b = q >> 2, e = q & 3;
-        f[b][e] = *reinterpret_cast<const float *>(panel + fa.a[b] + (4 * j + e) * 1024);
+        f[b][e] = *reinterpret_cast<const float *>(panel + fa.a[b] + (4 * j + e) * Geo<TS>::XROW);
     }
 }
 
-template <int L>
-constexpr int pieces() { return L == kKRows ? BLK : 4 * BLK; }
+template <int L, int TS>
+constexpr int pieces() { return L == kKRows ? Geo<TS>::BLK : 4 * Geo<TS>::BLK; }
 
-// One 256 x 256 tile at (m0, n0).  EDGE: the tile crosses M or N, or K is
-// not a multiple of the slice depth.
-template <int LA, int LB, bool EDGE>
+// One TS x TS tile at (m0, n0).  EDGE: the tile crosses M or N, or K is not
+// a multiple of the slice depth.
+template <int LA, int LB, bool EDGE, int TS>
 __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem) {
+    using G = Geo<TS>;
+    constexpr int BM = G::BM, BN = G::BN, WT = G::WT, BLK = G::BLK, PANEL = G::PANEL, STAGE = G::STAGE;
+    constexpr int LPO = G::LPO, LPS = G::LPS;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
 
-    const Operand<LA, EDGE> opa(g.A, g.lda, m0, g.M, g.K, wave, lane);
-    const Operand<LB, EDGE> opb(g.B, g.ldb, n0, g.N, g.K, wave, lane);
+    const Operand<LA, EDGE, TS> opa(g.A, g.lda, m0, g.M, g.K, wave, lane);
+    const Operand<LB, EDGE, TS> opb(g.B, g.ldb, n0, g.N, g.K, wave, lane);
     auto issue_one = [&](int slice, int stage, int i) {
         const int k0 = slice * BK;
         unsigned char *st = smem + stage * STAGE;
@@ -202,15 +224,15 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    const FragAddr<LA> fra(wm * WT, h, l32);
-    const FragAddr<LB> frb(wn * WT, h, l32);
-    constexpr int PA = pieces<LA>(), PB = pieces<LB>();
-    auto read = [&](const unsigned char *st, int j, int q, Frag &f) {
-        if (q < PA) read_piece<LA>(st, fra, j, q, f.a);
-        else read_piece<LB>(st + PANEL, frb, j, q - PA, f.b);
+    const FragAddr<LA, TS> fra(wm * WT, h, l32);
+    const FragAddr<LB, TS> frb(wn * WT, h, l32);
+    constexpr int PA = pieces<LA, TS>(), PB = pieces<LB, TS>();
+    auto read = [&](const unsigned char *st, int j, int q, Frag<TS> &f) {
+        if (q < PA) read_piece<LA, TS>(st, fra, j, q, f.a);
+        else read_piece<LB, TS>(st + PANEL, frb, j, q - PA, f.b);
     };
-    // MFMA i of a half: k step e = i / 16, block (i / 4) % 4, (i % 4).
-    auto mfma_one = [&](const Frag &f, int i) {
+    // MFMA i of a half: k step e = i / BLK^2, block (i / BLK) % BLK, i % BLK.
+    auto mfma_one = [&](const Frag<TS> &f, int i) {
         const int e = i / (BLK * BLK), ib = (i / BLK) % BLK, jb = i % BLK;
         acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[ib][e], f.b[jb][e], acc[ib][jb], 0, 0, 0);
     };
@@ -223,7 +245,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
 #pragma unroll
         for (int i = 0; i < LPS; ++i) issue_one(s < nk ? s : nk - 1, s, i);
 
-    Frag f0, f1;
+    Frag<TS> f0, f1;
 #pragma unroll
     for (int b = 0; b < BLK; ++b)
 #pragma unroll
@@ -231,16 +253,19 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
             f1.a[b][e] = 0.f;
             f1.b[b][e] = 0.f;
         }
-    constexpr int MF = 4 * BLK * BLK;   // MFMAs per half slice: 64
-    static_assert(PA + PB + LPS <= MF, "every other instruction follows an MFMA");
+    constexpr int MF = 4 * BLK * BLK;   // MFMAs per half slice: 64 (TS 256) or 16 (TS 128)
+    constexpr int ITEMS = PA + PB + LPS;
+    constexpr int PER1 = (ITEMS + MF - 1) / MF, PER2 = (PA + PB + MF - 1) / MF;   // items after each MFMA
+    // vmcnt(2 LPS): the loads of slices t+1 and t+2 may stay in flight;
+    // lgkmcnt(0); expcnt not waited on (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+    constexpr int WAIT = ((2 * LPS) & 15) | (((2 * LPS) >> 4) << 14) | (0 << 8) | (7 << 4);
     //   phase 1: the MFMAs of the previous slice's second half (zeros before
-    //            the first slice), each followed by one fragment read of this
-    //            slice's first half or one load of slice t+3;
+    //            the first slice), each followed by its share of the fragment
+    //            reads of this slice's first half and of the loads of slice t+3;
     //   phase 2: the MFMAs of the first half, followed by the reads of the
     //            second half, whose MFMAs are held over to the next slice.
     for (int t = 0; t < nk; ++t) {
-        // vmcnt(16) (two slices still in flight) and lgkmcnt(0); expcnt not waited on.
-        __builtin_amdgcn_s_waitcnt((1 << 14) | (0 << 8) | (7 << 4) | 0);
+        __builtin_amdgcn_s_waitcnt(WAIT);
         __builtin_amdgcn_s_barrier();
         const int ld_slice = t + NST - 1 < nk ? t + NST - 1 : nk - 1;
         const int ld_stage = (t + NST - 1) % NST;
@@ -249,15 +274,23 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
         for (int i = 0; i < MF; ++i) {
             mfma_one(f1, i);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < PA + PB) read(st, 0, i, f0);
-            else if (i < PA + PB + LPS) issue_one(ld_slice, ld_stage, i - PA - PB);
+#pragma unroll
+            for (int u = 0; u < PER1; ++u) {
+                const int q = i * PER1 + u;
+                if (q < PA + PB) read(st, 0, q, f0);
+                else if (q < ITEMS) issue_one(ld_slice, ld_stage, q - PA - PB);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
             mfma_one(f0, i);
             __builtin_amdgcn_sched_barrier(0);
-            if (i < PA + PB) read(st, 1, i, f1);
+#pragma unroll
+            for (int u = 0; u < PER2; ++u) {
+                const int q = i * PER2 + u;
+                if (q < PA + PB) read(st, 1, q, f1);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -267,7 +300,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     // the work-group can end and its LDS be given to another.
     __builtin_amdgcn_s_waitcnt(0);
 
-    // Epilogue in four passes of one block row (4 blocks, 64 values per
+    // Epilogue in BLK passes of one block row (BLK blocks, 16 BLK values per
     // lane): the C reads of a pass are issued together before its stores,
     // which are non-temporal (C is not read again here).  Accumulator register
     // r of a block holds row 8 (r / 4) + 4 h + r % 4, column l % 32.  Edge
@@ -316,22 +349,23 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     }
 }
 
-template <int LA, int LB>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void sgemm_big_kernel(
-    GemmArgs g, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * STAGE];
+// TS 256: one work-group per CU (256 accumulators per lane); TS 128: two.
+template <int LA, int LB, int TS>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TS == 256 ? 1 : 2, TS == 256 ? 1 : 2)))
+void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * Geo<TS>::STAGE];
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
-    if (m0 + BM > g.M || n0 + BN > g.N || g.K % BK != 0) big_tile<LA, LB, true>(g, m0, n0, smem);
-    else big_tile<LA, LB, false>(g, m0, n0, smem);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
+    const int m0 = tm * TS, n0 = tn * TS;
+    if (m0 + TS > g.M || n0 + TS > g.N || g.K % BK != 0) big_tile<LA, LB, true, TS>(g, m0, n0, smem);
+    else big_tile<LA, LB, false, TS>(g, m0, n0, smem);
 }
 
-template <int LA, int LB>
-hipError_t launch(const GemmArgs &g, hipStream_t stream) {
-    const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
-    hipLaunchKernelGGL((sgemm_big_kernel<LA, LB>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, g, tiles_m,
-                       tiles_n);
+template <int LA, int LB, int TS>
+hipError_t launch(const GemmArgs &g, int group_m, hipStream_t stream) {
+    const int tiles_m = (g.M + TS - 1) / TS, tiles_n = (g.N + TS - 1) / TS;
+    hipLaunchKernelGGL((sgemm_big_kernel<LA, LB, TS>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, g, tiles_m,
+                       tiles_n, group_m);
     return hipGetLastError();
 }
 
@@ -346,23 +380,31 @@ bool big_tile_fits(const GemmArgs &g) {
     if (g.M % 4 || g.N % 4 || g.K % 4 || g.K < 4) return false;
     if (!aligned16(g.A) || !aligned16(g.B) || g.lda % 4 || g.ldb % 4) return false;
     const int64_t lim = (int64_t)1 << 31;
+    // (the spans of 256-wide tiles bound those of 128-wide ones)
     auto span = [&](bool krows, int64_t ld) { return krows ? (255 * ld + BK) * 4 : ((BK - 1) * ld + 256) * 4; };
     return span(!g.trans_a, g.lda) < lim && span(g.trans_b, g.ldb) < lim;
 }
 
 // Edge tiles address their part of C with 32-bit buffer offsets.
-bool big_tile_c_fits(int64_t ldc) { return (255 * ldc + BN) * 4 < ((int64_t)1 << 31); }
+bool big_tile_c_fits(int64_t ldc) { return (255 * ldc + 256) * 4 < ((int64_t)1 << 31); }
 
-int64_t big_tiles(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
+int64_t big_tiles(int M, int N) { return (int64_t)((M + 255) / 256) * ((N + 255) / 256); }
 
-hipError_t launch_big(const GemmArgs &g, hipStream_t stream) {
+namespace {
+template <int TS>
+hipError_t launch_ts(const GemmArgs &g, int group_m, hipStream_t stream) {
     // A as given has rows of k; B as given has rows of x (N); a transposed
     // operand swaps.
     const bool ta = g.trans_a != 0, tb = g.trans_b != 0;
-    if (!ta && !tb) return launch<kKRows, kXRows>(g, stream);
-    if (!ta && tb) return launch<kKRows, kKRows>(g, stream);
-    if (ta && !tb) return launch<kXRows, kXRows>(g, stream);
-    return launch<kXRows, kKRows>(g, stream);
+    if (!ta && !tb) return launch<kKRows, kXRows, TS>(g, group_m, stream);
+    if (!ta && tb) return launch<kKRows, kKRows, TS>(g, group_m, stream);
+    if (ta && !tb) return launch<kXRows, kXRows, TS>(g, group_m, stream);
+    return launch<kXRows, kKRows, TS>(g, group_m, stream);
 }
+}  // namespace
+
+hipError_t launch_big(const GemmArgs &g, hipStream_t stream) { return launch_ts<256>(g, 4, stream); }
+
+hipError_t launch_dl128(const GemmArgs &g, int group_m, hipStream_t stream) { return launch_ts<128>(g, group_m, stream); }
 
 }  // namespace sgemm

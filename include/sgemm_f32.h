@@ -89,8 +89,8 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_SKINNY = 4,         /* M <= 16: FP32 MFMA streaming kernel */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
     SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
-                                     64x64 tiles with two slices in flight, or 256x256 tiles
-                                     (16-byte loads) */
+                                     64x64 tiles with two slices in flight, 256x256 tiles, or
+                                     128x128 tiles loaded straight into LDS (16-byte loads) */
     SGEMM_F32_NUM_VARIANTS = 7
 };
 
@@ -106,7 +106,9 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_256x256 = 7,    /* 256x256, one work-group per CU, operands loaded straight into
                                      LDS; whole tiles only (M and N multiples of 256, K of 16),
                                      16-byte loads, no K split, group_m ignored (4 is used) */
-    SGEMM_F32_NUM_CONFIGS = 8
+    SGEMM_F32_CFG_128x128_DL = 8, /* 128x128 by the kernel of configuration 7, two work-groups per
+                                     CU; its conditions, no K split */
+    SGEMM_F32_NUM_CONFIGS = 9
 };
 
 /*
@@ -223,11 +225,18 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * multiples of 4, the 16-byte-load conditions, 256 stored rows of an operand
  * read along k (16 of one read along M or N) spanning less than 2 GiB, and 256
  * rows of C spanning less than 2 GiB; SGEMM_F32_ERR_NOT_APPLICABLE otherwise.
- * Its split count and grouping are ignored.  The automatic choice takes it when
- * the plan would otherwise be the 128 x 128 grid without a split, the 256 x 256
- * grid has at least 256 tiles, and the part of its rounds (256 tiles each) that
- * lies inside C is at least 93 % and within 2 % of the 128 x 128 grid's (a C
- * stride too wide for it at call time keeps the 128 x 128 grid).
+ * It takes no split count (splits must be 1) and ignores the grouping.  The
+ * automatic choice takes it when the plan would otherwise be the 128 x 128
+ * grid without a split, the 256 x 256 grid has at least 256 tiles, and the
+ * part of its rounds (256 tiles each) that lies inside C is at least 93 % and
+ * within 2 % of the 128 x 128 grid's (a C stride too wide for it at call time
+ * keeps the 128 x 128 grid).
+ * Configuration 8 runs the kernel of configuration 7 on 128 x 128 tiles, two
+ * work-groups per compute unit, with the same conditions; it honours the
+ * grouping and takes no split count (splits must be 1).  The automatic choice
+ * takes it in place of the 128 x 128 grid without a split when those
+ * conditions hold, M and N are multiples of 128 and K of 16 (again, a C stride
+ * too wide at call time keeps the 128 x 128 grid).
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -264,53 +264,73 @@ def test_streamk_repeat_bitwise_identical(sg):
 
 
 # ---------------------------------------------------------------------------
-# Configuration 7: 256x256 tiles, operands copied straight into LDS.  M, N and
-# K multiples of 4; edge tiles get zeros past M, N and K in LDS and masked
-# stores.  One slice is 16 deep and three are fetched ahead, so short K
-# exercises the repeated loads past the end.
+# Configurations 7 and 8: the kernel that copies the operands straight into
+# LDS, on 256x256 and on 128x128 tiles.  M, N and K multiples of 4; edge tiles
+# get zeros past M, N and K in LDS and masked stores.  One slice is 16 deep
+# and three are fetched ahead, so short K exercises the repeated loads past
+# the end.
 # ---------------------------------------------------------------------------
-BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024),
-              # edge tiles: M, N not multiples of 256, K not of 16 (multiples of 4)
-              (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4)]
+BIG_CFGS = [7, 8]
+BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024), (128, 384, 32),
+              # edge tiles: M, N not multiples of 256 (or 128), K not of 16 (multiples of 4)
+              (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52), (124, 132, 16)]
 
 
+@pytest.mark.parametrize("cfg", BIG_CFGS)
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("shape", BIG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in BIG_SHAPES])
-def test_config7_real(sg, form, shape):
+def test_big_kernel_real(sg, cfg, form, shape):
     M, N, K = shape
     ta, tb = form
-    say(f"[cfg7_real] {form} {shape}")
+    say(f"[big_real] cfg {cfg} {form} {shape}")
     A, B, C0 = _inputs(M, N, K, "uniform", 900 + M + N + K)
-    st, C, As, Bs = run_cfg(sg, 7, 8, 1, ta, tb, A, B, C0, 1.25, -0.5)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, ta, tb, A, B, C0, 1.25, -0.5)
     assert st == 0
     ok, info = check(C, As, Bs, ta, tb, 1.25, -0.5, C0, exact=False)
     assert ok, info
 
 
+@pytest.mark.parametrize("cfg", BIG_CFGS)
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
-def test_config7_integer_bitexact(sg, form):
+def test_big_kernel_integer_bitexact(sg, cfg, form):
     M, N, K = 516, 772, 404
     ta, tb = form
-    say(f"[cfg7_int] {form}")
+    say(f"[big_int] cfg {cfg} {form}")
     A, B, C0 = _inputs(M, N, K, "int4", 910)
-    st, C, As, Bs = run_cfg(sg, 7, 8, 1, ta, tb, A, B, C0, 1.5, -0.5)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, ta, tb, A, B, C0, 1.5, -0.5)
     assert st == 0
     ok, info = check(C, As, Bs, ta, tb, 1.5, -0.5, C0, exact=True)
     assert ok, info
 
 
-def test_config7_beta_zero_ignores_nan_c(sg):
+@pytest.mark.parametrize("cfg", BIG_CFGS)
+def test_big_kernel_beta_zero_ignores_nan_c(sg, cfg):
     M, N, K = 512, 512, 64
     A, B, _ = _inputs(M, N, K, "uniform", 911)
     C0 = np.full((M, N), np.nan, np.float32)
-    st, C, As, Bs = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
     assert st == 0 and np.all(np.isfinite(C))
     ok, info = check(C, As, Bs, 0, 0, 1.0, 0.0, None, exact=False)
     assert ok, info
 
 
+def test_config8_grouping_bitwise(sg):
+    """The grouping changes only the order of the tiles: every grouping gives
+    the same bits."""
+    M, N, K = 1024, 640, 160
+    A, B, C0 = _inputs(M, N, K, "uniform", 915)
+    ref = None
+    for gm in (1, 3, 8, 64):
+        st, C, _, _ = run_cfg(sg, 8, gm, 1, 0, 0, A, B, C0, 1.0, 0.5)
+        assert st == 0
+        if ref is None:
+            ref = C
+        assert np.array_equal(C.view(np.uint32), ref.view(np.uint32)), gm
+
+
+@pytest.mark.parametrize("cfg", BIG_CFGS)
 @pytest.mark.parametrize("form", [(0, 0), (1, 1)], ids=["nn", "tt"])
-def test_config7_padded_strides(sg, form):
+def test_big_kernel_padded_strides(sg, cfg, form):
     """Row strides wider than the stored rows (multiples of 4), C included."""
     M, N, K = 512, 512, 96
     ta, tb = form
@@ -320,7 +340,7 @@ def test_config7_padded_strides(sg, form):
     bA, pA, _ = to_device_padded(As, lda)
     bB, pB, _ = to_device_padded(Bs, ldb)
     bC, pC, _ = to_device_padded(C0, ldc, fill=np.float32(-7.25))
-    st = sg.sgemm_f32_ex_config(7, 8, 1, ta, tb, M, N, K, 0.75, pA, lda, pB, ldb, 0.5, pC, ldc,
+    st = sg.sgemm_f32_ex_config(cfg, 8, 1, ta, tb, M, N, K, 0.75, pA, lda, pB, ldb, 0.5, pC, ldc,
                                 torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
@@ -333,21 +353,23 @@ def test_config7_padded_strides(sg, form):
     assert np.all(gaps == np.float32(-7.25))
 
 
-def test_config7_rejects_what_it_cannot_cover(sg):
+@pytest.mark.parametrize("cfg", BIG_CFGS)
+def test_big_kernel_rejects_what_it_cannot_cover(sg, cfg):
     """M, N or K not a multiple of 4: refused before any launch."""
     A, B, C0 = _inputs(258, 256, 64, "uniform", 913)
-    st, _, _, _ = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
+    st, _, _, _ = run_cfg(sg, cfg, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
     assert st == sg.ERR_NOT_APPLICABLE
 
 
+@pytest.mark.parametrize("cfg", BIG_CFGS)
 @pytest.mark.parametrize("K", [65536, 65540])
-def test_config7_long_k_bitexact(sg, K):
+def test_big_kernel_long_k_bitexact(sg, cfg, K):
     """4096 slices through the four LDS stages (and a K tail of 4): integer
     inputs keep every partial sum below 2**24, so the result is exact."""
     M, N = 256, 512
-    say(f"[cfg7_long_k] K={K}")
+    say(f"[big_long_k] cfg {cfg} K={K}")
     A, B, C0 = _inputs(M, N, K, "int4", 914 + K % 16)
-    st, C, As, Bs = run_cfg(sg, 7, 8, 1, 0, 0, A, B, C0, 1.0, -1.0)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, 0, 0, A, B, C0, 1.0, -1.0)
     assert st == 0
     ok, info = check(C, As, Bs, 0, 0, 1.0, -1.0, C0, exact=True)
     assert ok, info

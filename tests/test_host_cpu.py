@@ -136,7 +136,12 @@ def test_transposed_kernel_selection(sg):
     sel = sg.sgemm_f32_ex_select
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_TUNED
+        # whole 128x128 tiles: configuration 8; N = 7000 keeps the 128x128 kernel
         assert sel(ta, tb, 6144, 6144, 2048, 1.0, al, 6144 if ta else 2048, al, 2048 if tb else 6144) \
+            == sg.MFMA_TUNED
+        assert sg.sgemm_f32_ex_plan(ta, tb, 6144, 6144, 2048, 1.0, al, 6144 if ta else 2048, al,
+                                    2048 if tb else 6144)[2] == sg.CFG_128x128_DL
+        assert sel(ta, tb, 7000, 7000, 1024, 1.0, al, 7000 if ta else 1024, al, 1024 if tb else 7000) \
             == sg.MFMA_LARGE
         assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
@@ -178,7 +183,8 @@ def test_variant_names_and_version(sg):
     assert names == ["auto", "mfma_large", "mfma_small", "valu", "skinny", "mfma_scalar", "mfma_tuned"]
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
-    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64", "256x256"]
+    assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64", "256x256",
+                    "128x128_dl"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -229,6 +235,8 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
+        assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
+    for shape in [(7000, 7000, 1024), (7040, 7000, 1024), (7040, 7040, 1000)]:
         assert plan(*shape)[2] == sg.CFG_128x128, shape
     # Well-filled 256x256 grids take the larger tile.
     for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092)]:
@@ -271,8 +279,8 @@ def test_plan_follows_the_tuning_table(sg):
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
         if cfg == sg.CFG_64x64_PF2 and e["config"] == 0:
             continue        # the switch to 64x64 tiles for poorly filled rounds
-        if cfg == sg.CFG_256x256 and e["config"] == 0 and e["splits"] == 1:
-            continue        # whole, well-filled 256x256 grids
+        if cfg in (sg.CFG_256x256, sg.CFG_128x128_DL) and e["config"] == 0 and e["splits"] == 1:
+            continue        # 256x256 tiles, or the 128x128 grid loaded straight into LDS
         assert (cfg, gm) == (e["config"], e["group_m"]), e
         k_per = -(-K // e["splits"])
         k_per = -(-k_per // 32) * 32
