@@ -36,13 +36,16 @@
 //   k and k + 8 at the same x, fall in opposite halves of the bank space.
 //
 // Edges.  M, N and K are multiples of 4, so a 16-byte group never straddles
-// an edge.  Tiles that cross M or N, and every tile when K is not a multiple
-// of 16, give each group outside the matrices an out-of-range lane offset: the
-// load writes zeros to LDS without touching memory (adding exact zeros changes
-// no sum).  Their epilogue stores through a buffer resource over the valid part
-// of C, whose extent drops rows past M and whose out-of-range offsets drop
-// columns past N.
+// an edge.  Tiles that cross M or N give each group outside M or N an
+// out-of-range lane offset: the load writes zeros to LDS without touching
+// memory (adding exact zeros changes no sum).  When K is not a multiple of 16
+// the loads of the partial last slice do the same for groups past K; they are
+// issued by the last iterations of the slice loop, which run a copy of the loop
+// with that check, so the other iterations keep constant offsets.  Tiles that
+// cross M or N store through a buffer resource over the valid part of C, whose
+// extent drops rows past M and whose out-of-range offsets drop columns past N.
 #include <cstdint>
+#include <type_traits>
 
 #include "gemm_internal.hpp"
 
@@ -142,9 +145,14 @@ struct Operand {
         if (L == kKRows) return rsrc(X + k0, (int)(((EDGE ? xs : TS) - 1) * ld + BK) * 4);
         return rsrc(X + (int64_t)k0 * ld, (int)(((BK - 1) * ld + TS) * 4));
     }
+    // CK: the slice may reach past K (only the last one does).
+    template <bool CK>
     __device__ __forceinline__ int offset(int j, int k0) const {
-        if (!EDGE) return off[j];
-        return gx[j] < xs && k0 + gk[j] < K ? off[j] : kOutOfRange;
+        if (!EDGE && !CK) return off[j];
+        bool ok = true;
+        if (EDGE) ok = gx[j] < xs;
+        if (CK) ok = ok && k0 + gk[j] < K;
+        return ok ? off[j] : kOutOfRange;
     }
 };
 
@@ -195,8 +203,7 @@ __device__ __forceinline__ void read_piece(const unsigned char *panel, const Fra
 template <int L, int TS>
 constexpr int pieces() { return L == kKRows ? Geo<TS>::BLK : 4 * Geo<TS>::BLK; }
 
-// One TS x TS tile at (m0, n0).  EDGE: the tile crosses M or N, or K is not
-// a multiple of the slice depth.
+// One TS x TS tile at (m0, n0).  EDGE: the tile crosses M or N.
 template <int LA, int LB, bool EDGE, int TS>
 __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem) {
     using G = Geo<TS>;
@@ -209,11 +216,12 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
 
     const Operand<LA, EDGE, TS> opa(g.A, g.lda, m0, g.M, g.K, wave, lane);
     const Operand<LB, EDGE, TS> opb(g.B, g.ldb, n0, g.N, g.K, wave, lane);
-    auto issue_one = [&](int slice, int stage, int i) {
+    auto issue_one = [&](auto ck, int slice, int stage, int i) {
+        constexpr bool CK = decltype(ck)::value;
         const int k0 = slice * BK;
         unsigned char *st = smem + stage * STAGE;
-        if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.offset(i, k0));
-        else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.offset(i - LPO, k0));
+        if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.template offset<CK>(i, k0));
+        else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.template offset<CK>(i - LPO, k0));
     };
 
     f32x16 acc[BLK][BLK];
@@ -243,7 +251,7 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
 #pragma unroll
     for (int s = 0; s < NST - 1; ++s)
 #pragma unroll
-        for (int i = 0; i < LPS; ++i) issue_one(s < nk ? s : nk - 1, s, i);
+        for (int i = 0; i < LPS; ++i) issue_one(std::true_type{}, s < nk ? s : nk - 1, s, i);
 
     Frag<TS> f0, f1;
 #pragma unroll
@@ -264,36 +272,43 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     //            reads of this slice's first half and of the loads of slice t+3;
     //   phase 2: the MFMAs of the first half, followed by the reads of the
     //            second half, whose MFMAs are held over to the next slice.
-    for (int t = 0; t < nk; ++t) {
-        __builtin_amdgcn_s_waitcnt(WAIT);
-        __builtin_amdgcn_s_barrier();
-        const int ld_slice = t + NST - 1 < nk ? t + NST - 1 : nk - 1;
-        const int ld_stage = (t + NST - 1) % NST;
-        const unsigned char *st = smem + (t % NST) * STAGE;
+    auto slices = [&](auto ck, int t_begin, int t_end) {
+        for (int t = t_begin; t < t_end; ++t) {
+            __builtin_amdgcn_s_waitcnt(WAIT);
+            __builtin_amdgcn_s_barrier();
+            const int ld_slice = t + NST - 1 < nk ? t + NST - 1 : nk - 1;
+            const int ld_stage = (t + NST - 1) % NST;
+            const unsigned char *st = smem + (t % NST) * STAGE;
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            mfma_one(f1, i);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < MF; ++i) {
+                mfma_one(f1, i);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < PER1; ++u) {
-                const int q = i * PER1 + u;
-                if (q < PA + PB) read(st, 0, q, f0);
-                else if (q < ITEMS) issue_one(ld_slice, ld_stage, q - PA - PB);
+                for (int u = 0; u < PER1; ++u) {
+                    const int q = i * PER1 + u;
+                    if (q < PA + PB) read(st, 0, q, f0);
+                    else if (q < ITEMS) issue_one(ck, ld_slice, ld_stage, q - PA - PB);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-            mfma_one(f0, i);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int i = 0; i < MF; ++i) {
+                mfma_one(f0, i);
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int u = 0; u < PER2; ++u) {
-                const int q = i * PER2 + u;
-                if (q < PA + PB) read(st, 1, q, f1);
+                for (int u = 0; u < PER2; ++u) {
+                    const int q = i * PER2 + u;
+                    if (q < PA + PB) read(st, 1, q, f1);
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_barrier(0);
         }
-    }
+    };
+    // Iteration t loads slice min(t + 3, nk - 1): with a K tail, the
+    // iterations from nk - 4 on load the partial last slice and check k.
+    const int t_split = g.K % BK != 0 ? max(0, nk - NST) : nk;
+    slices(std::false_type{}, 0, t_split);
+    slices(std::true_type{}, t_split, nk);
 #pragma unroll
     for (int i = 0; i < MF; ++i) mfma_one(f1, i);
     // Every load issued (including the repeated last slice) has landed before
@@ -357,7 +372,7 @@ void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TS, n0 = tn * TS;
-    if (m0 + TS > g.M || n0 + TS > g.N || g.K % BK != 0) big_tile<LA, LB, true, TS>(g, m0, n0, smem);
+    if (m0 + TS > g.M || n0 + TS > g.N) big_tile<LA, LB, true, TS>(g, m0, n0, smem);
     else big_tile<LA, LB, false, TS>(g, m0, n0, smem);
 }
 
