@@ -37,7 +37,8 @@ CFG_128x128_STREAMK = 5
 CFG_64x64_BK64 = 6
 CFG_256x256 = 7
 CFG_128x128_DL = 8
-NUM_CONFIGS = 9
+CFG_64x64_DL = 9
+NUM_CONFIGS = 10
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

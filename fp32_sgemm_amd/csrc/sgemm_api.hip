@@ -212,26 +212,35 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 // 7000 x 7000 x 1024 133.1 -> 132.1, NT 136.1 -> 131.6; 7040 x 7000 x 1024
 // 134.2 -> 132.5; 6000 x 6000 x 2048 NT 138.0 -> 135.5; K = 3000: 3000^3
 // 100.2 -> 96.9.
-Plan dl128_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B,
-                int ldb) {
-    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.config != 0 || p.splits > 1)
-        return p;
+// In the same way the 64x64 grid with two slices in flight (configuration 4)
+// without a split goes to that kernel on 64x64 tiles (configuration 9, four
+// work-groups per compute unit) for whole 64x64 grids with K a multiple of 16:
+// 1024^3 87.8 -> 92.5, TN 93.6 -> 101.9; 1536^3 97.6 -> 101.5; 2048^3 TN 135.4
+// -> 139.1; 2048 x 2048 x 1024 127.0 -> 128.0; 512 x 512 x 8192 (no split)
+// 31.8 -> 33.3, TN 30.1 -> 33.6; 2560^3 127.5 -> 126.7, TN 126.8 -> 128.9;
+// 4608 x 4608 x 2048 135.8 -> 134.9, TN 135.5 -> 138.2; and with edge tiles
+// and a K tail 3000^3 130.6 -> 113.4, TN 128.5 -> 124.3.
+Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda,
+                     const float *B, int ldb) {
+    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.splits > 1) return p;
+    if (p.config != 0 && p.config != 4) return p;
+    const int tile = p.config == 0 ? 128 : 64;
     sgemm::GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.B = B;
     g.lda = lda; g.ldb = ldb;
     g.trans_a = ta; g.trans_b = tb;
-    if (M % 128 != 0 || N % 128 != 0 || K % 16 != 0 || !sgemm::big_tile_fits(g)) return p;
-    return Plan{SGEMM_F32_MFMA_TUNED, 8, p.group_m, 1};
+    if (M % tile != 0 || N % tile != 0 || K % 16 != 0 || !sgemm::big_tile_fits(g)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, p.config == 0 ? 8 : 9, p.group_m, 1};
 }
 
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill
-// theirs, and from the 128x128 kernel to configuration 8 (reported as
-// SGEMM_F32_MFMA_TUNED when the plan differs from the default).  Transposed
-// operands use the same entries.
+// theirs, and from the 128x128 and 64x64 kernels to configurations 8 and 9
+// (reported as SGEMM_F32_MFMA_TUNED when the plan differs from the default).
+// Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
     if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
@@ -248,7 +257,7 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
         }
     }
     p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
-    return dl128_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
+    return direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
@@ -259,7 +268,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 int run_mfma(const GemmArgs &g, int config, bool vec, int group_m, int splits, hipStream_t stream) {
     if (!vec && !sgemm::mfma_config_scalar_ok(config)) return SGEMM_F32_ERR_NOT_APPLICABLE;
     if (!config_fits(config, g.trans_a, g.trans_b, g.lda, g.ldb)) return SGEMM_F32_ERR_NOT_APPLICABLE;
-    if ((config == 7 || config == 8) && !(sgemm::big_tile_fits(g) && sgemm::big_tile_c_fits(g.ldc)))
+    if (config >= 7 && !(sgemm::big_tile_fits(g) && sgemm::big_tile_c_fits(g.ldc)))
         return SGEMM_F32_ERR_NOT_APPLICABLE;
     int k_per = 0;
     const int eff = sgemm::mfma_config_splits_ok(config) ? sgemm::mfma_effective_splits(g.K, splits, &k_per) : 1;
@@ -302,8 +311,9 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         p = auto_plan(ta, tb, M, N, K, A, lda, B, ldb);
     }
     // The plan does not see C: a row stride of C too wide for the 32-bit
-    // offsets of configurations 7 and 8 keeps the 128x128 kernel.
+    // offsets of configurations 7-9 keeps the register-staged kernels.
     if ((p.config == 7 || p.config == 8) && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
+    if (p.config == 9 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, 1};
     switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
@@ -416,6 +426,7 @@ const char *sgemm_f32_config_name(int config) {
         case 6: return "64x64_bk64";
         case 7: return "256x256";
         case 8: return "128x128_dl";
+        case 9: return "64x64_dl";
         default: return nullptr;
     }
 }

@@ -1,7 +1,8 @@
 // FP32 GEMM on 256 x 256 tiles, one per CU at a time, for grids whose rounds of
 // 256 tiles lie almost entirely inside C; the same kernel on 128 x 128 tiles
-// (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) serves
-// whole 128 x 128 grids.  The description below is that of the 256 x 256 form.
+// (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) and on
+// 64 x 64 tiles (4 waves of 32 x 32, four work-groups per CU) serves whole
+// grids of those tiles.  The description below is that of the 256 x 256 form.
 //
 // One work-group per CU, 4 waves of 128 x 128 (4 x 4 blocks of 32x32x2 MFMA,
 // 256 accumulators per lane, kept in the accumulation registers): per MFMA a
@@ -364,9 +365,13 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     }
 }
 
-// TS 256: one work-group per CU (256 accumulators per lane); TS 128: two.
+// Work-groups per CU: TS 256 one (256 accumulators per lane), TS 128 two,
+// TS 64 four (32 KB of LDS each).
+template <int TS>
+constexpr int kWavesPerEu = TS == 256 ? 1 : TS == 128 ? 2 : 4;
+
 template <int LA, int LB, int TS>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(TS == 256 ? 1 : 2, TS == 256 ? 1 : 2)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<TS>, kWavesPerEu<TS>)))
 void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * Geo<TS>::STAGE];
     int tm, tn;
@@ -421,5 +426,7 @@ hipError_t launch_ts(const GemmArgs &g, int group_m, hipStream_t stream) {
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream) { return launch_ts<256>(g, 4, stream); }
 
 hipError_t launch_dl128(const GemmArgs &g, int group_m, hipStream_t stream) { return launch_ts<128>(g, group_m, stream); }
+
+hipError_t launch_dl64(const GemmArgs &g, int group_m, hipStream_t stream) { return launch_ts<64>(g, group_m, stream); }
 
 }  // namespace sgemm

@@ -917,8 +917,8 @@ using SmallTile2 = MfmaTile<64, 64, 32, 32, 32, 2, LA, LB>;
 template <int LA, int LB>
 using SmallTileK64 = MfmaTile<64, 64, 64, 32, 32, 2, LA, LB>;
 
-constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128, 64, 256, 128};
-constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128, 64, 256, 128};
+constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128, 64, 256, 128, 64};
+constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128, 64, 256, 128, 64};
 constexpr int kTileBK = 32;
 
 template <class T, bool VEC>
@@ -1015,6 +1015,7 @@ hipError_t launch_layouts(const GemmArgs &g, int config, bool vec, int group_m, 
         case 6: return launch_one<SmallTileK64<LA, LB>, true>(g, group_m, sk, stream);
         case 7: return launch_big(g, stream);
         case 8: return launch_dl128(g, group_m, stream);
+        case 9: return launch_dl64(g, group_m, stream);
         default: return hipErrorInvalidValue;
     }
 }
@@ -1039,7 +1040,7 @@ int64_t mfma_large_grid(int M, int N) { return mfma_config_tiles(0, M, N); }
 int64_t mfma_small_grid(int M, int N) { return mfma_config_tiles(1, M, N); }
 
 bool mfma_config_scalar_ok(int config) { return config == 0 || config == 1; }
-bool mfma_config_splits_ok(int config) { return config != 5 && config != 7 && config != 8; }
+bool mfma_config_splits_ok(int config) { return config != 5 && config < 7; }
 
 int mfma_effective_splits(int K, int splits, int *k_per) {
     if (splits < 1) splits = 1;

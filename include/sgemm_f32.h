@@ -90,7 +90,8 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
     SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
                                      64x64 tiles with two slices in flight, 256x256 tiles, or
-                                     128x128 tiles loaded straight into LDS (16-byte loads) */
+                                     128x128 or 64x64 tiles loaded straight into LDS (16-byte
+                                     loads) */
     SGEMM_F32_NUM_VARIANTS = 7
 };
 
@@ -108,7 +109,9 @@ enum sgemm_f32_config_id {
                                      16-byte loads, no K split, group_m ignored (4 is used) */
     SGEMM_F32_CFG_128x128_DL = 8, /* 128x128 by the kernel of configuration 7, two work-groups per
                                      CU; its conditions, no K split */
-    SGEMM_F32_NUM_CONFIGS = 9
+    SGEMM_F32_CFG_64x64_DL = 9,   /* 64x64 by the kernel of configuration 7, four work-groups per
+                                     CU; its conditions, no K split */
+    SGEMM_F32_NUM_CONFIGS = 10
 };
 
 /*
@@ -231,12 +234,13 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * part of its rounds (256 tiles each) that lies inside C is at least 93 % and
  * within 2 % of the 128 x 128 grid's (a C stride too wide for it at call time
  * keeps the 128 x 128 grid).
- * Configuration 8 runs the kernel of configuration 7 on 128 x 128 tiles, two
- * work-groups per compute unit, with the same conditions; it honours the
- * grouping and takes no split count (splits must be 1).  The automatic choice
- * takes it in place of the 128 x 128 grid without a split when those
- * conditions hold, M and N are multiples of 128 and K of 16 (again, a C stride
- * too wide at call time keeps the 128 x 128 grid).
+ * Configurations 8 and 9 run the kernel of configuration 7 on 128 x 128 and on
+ * 64 x 64 tiles (two and four work-groups per compute unit) with the same
+ * conditions; they honour the grouping and take no split count (splits must
+ * be 1).  The automatic choice takes configuration 8 in place of the 128 x 128
+ * grid and 9 in place of configuration 4, each without a split, when those
+ * conditions hold, M and N are multiples of the tile size and K of 16 (again,
+ * a C stride too wide at call time keeps the plan's register-staged kernel).
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -264,16 +264,18 @@ def test_streamk_repeat_bitwise_identical(sg):
 
 
 # ---------------------------------------------------------------------------
-# Configurations 7 and 8: the kernel that copies the operands straight into
-# LDS, on 256x256 and on 128x128 tiles.  M, N and K multiples of 4; edge tiles
-# get zeros past M, N and K in LDS and masked stores.  One slice is 16 deep
-# and three are fetched ahead, so short K exercises the repeated loads past
-# the end.
+# Configurations 7, 8 and 9: the kernel that copies the operands straight
+# into LDS, on 256x256, 128x128 and 64x64 tiles.  M, N and K multiples of 4;
+# edge tiles get zeros past M, N and K in LDS and masked stores.  One slice is
+# 16 deep and three are fetched ahead, so short K exercises the repeated loads
+# past the end.
 # ---------------------------------------------------------------------------
-BIG_CFGS = [7, 8]
+BIG_CFGS = [7, 8, 9]
 BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024), (128, 384, 32),
-              # edge tiles: M, N not multiples of 256 (or 128), K not of 16 (multiples of 4)
-              (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52), (124, 132, 16)]
+              (64, 192, 64),
+              # edge tiles: M, N not multiples of the tile, K not of 16 (multiples of 4)
+              (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52), (124, 132, 16),
+              (68, 60, 28)]
 
 
 @pytest.mark.parametrize("cfg", BIG_CFGS)
@@ -314,14 +316,15 @@ def test_big_kernel_beta_zero_ignores_nan_c(sg, cfg):
     assert ok, info
 
 
-def test_config8_grouping_bitwise(sg):
+@pytest.mark.parametrize("cfg", [8, 9])
+def test_direct_lds_grouping_bitwise(sg, cfg):
     """The grouping changes only the order of the tiles: every grouping gives
     the same bits."""
     M, N, K = 1024, 640, 160
     A, B, C0 = _inputs(M, N, K, "uniform", 915)
     ref = None
     for gm in (1, 3, 8, 64):
-        st, C, _, _ = run_cfg(sg, 8, gm, 1, 0, 0, A, B, C0, 1.0, 0.5)
+        st, C, _, _ = run_cfg(sg, cfg, gm, 1, 0, 0, A, B, C0, 1.0, 0.5)
         assert st == 0
         if ref is None:
             ref = C

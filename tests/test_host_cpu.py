@@ -184,7 +184,7 @@ def test_variant_names_and_version(sg):
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
     assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64", "256x256",
-                    "128x128_dl"]
+                    "128x128_dl", "64x64_dl"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -229,10 +229,14 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     al = 0x100000
     plan = lambda M, N, K, ta=0, tb=0: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, M if ta else K, al,
                                                             K if tb else N)
-    for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
-                  (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
-                  (2560, 2560, 2560)]:
+    # 64x64 tiles: loaded straight into LDS (configuration 9) when M and N are
+    # multiples of 64 and K of 16, else with two slices in flight.
+    for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
+    for shape in [(4608, 4608, 2048), (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096),
+                  (2048, 3072, 1024), (2560, 2560, 2560)]:
+        assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_DL, 8, 1), shape
+    assert plan(4608, 4608, 2044)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
@@ -277,10 +281,12 @@ def test_plan_follows_the_tuning_table(sg):
             assert v == sg.SKINNY
             continue
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
-        if cfg == sg.CFG_64x64_PF2 and e["config"] == 0:
+        if cfg in (sg.CFG_64x64_PF2, sg.CFG_64x64_DL) and e["config"] == 0:
             continue        # the switch to 64x64 tiles for poorly filled rounds
         if cfg in (sg.CFG_256x256, sg.CFG_128x128_DL) and e["config"] == 0 and e["splits"] == 1:
             continue        # 256x256 tiles, or the 128x128 grid loaded straight into LDS
+        if cfg == sg.CFG_64x64_DL and e["config"] in (0, 4) and e["splits"] == 1:
+            continue        # the 64x64 grid loaded straight into LDS
         assert (cfg, gm) == (e["config"], e["group_m"]), e
         k_per = -(-K // e["splits"])
         k_per = -(-k_per // 32) * 32
