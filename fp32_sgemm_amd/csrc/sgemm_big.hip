@@ -317,8 +317,9 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     __builtin_amdgcn_s_waitcnt(0);
 
     // Epilogue in BLK passes of one block row (BLK blocks, 16 BLK values per
-    // lane): the C reads of a pass are issued together before its stores,
-    // which are non-temporal (C is not read again here).  Accumulator register
+    // lane): the C reads of a pass are issued together before its stores
+    // (plain stores: with rows of C not 128-byte aligned, non-temporal ones
+    // cost 1-6 %).  Accumulator register
     // r of a block holds row 8 (r / 4) + 4 h + r % 4, column l % 32.  Edge
     // tiles go through a buffer resource over the tile's valid part of C: rows
     // past M lie beyond its extent and columns past N get an out-of-range
@@ -358,9 +359,8 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
                 const int cc = wn * WT + 32 * jb + l32;
                 float v = alpha * acc[ib][jb][r];
                 if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
-                // cache-policy bit 1: non-temporal
-                if (EDGE) raw_buffer_store_f32(v, rc, cbase[jb] + roff(r), 0, 2);
-                else __builtin_nontemporal_store(v, &Cb[(int64_t)rr * g.ldc + cc]);
+                if (EDGE) raw_buffer_store_f32(v, rc, cbase[jb] + roff(r), 0, 0);
+                else Cb[(int64_t)rr * g.ldc + cc] = v;
             }
     }
 }
