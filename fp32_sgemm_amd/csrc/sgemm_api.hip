@@ -200,9 +200,8 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 
 // The 128x128 grid that remains goes to the kernel of the 256x256 tiles on
 // 128x128 tiles (configuration 8: operands copied straight into LDS, two
-// work-groups per compute unit) when the operands fit it and K is a multiple
-// of its slice depth 16.  Same-box per-launch medians (TFLOP/s, configuration
-// 0 -> 8, NN unless noted): 4096 x 11008 x 512 131.2 -> 133.4, NT 131.6 ->
+// work-groups per compute unit) when the operands fit it.  Same-box
+// per-launch medians (TFLOP/s, configuration 0 -> 8, NN unless noted): 4096 x 11008 x 512 131.2 -> 133.4, NT 131.6 ->
 // 134.2, TN 130.6 -> 131.7; 11008 x 4096 x 512 TT 128.3 -> 131.6; 6144 x 6144
 // x 2048 142.5 -> 143.5; 2816^3 132.3 -> 136.8; 8192 x 4096 x 1024 135.5 ->
 // 139.5; 16384 x 16384 x 512 132.5 -> 133.8; 3968 x 3968 x 2048 133.7 ->
@@ -213,7 +212,10 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 // 135.0 -> 138.1, NT 137.7 -> 137.5, TN 132.0 -> 137.1; 6100 x 6100 x 1024
 // 133.1 -> 138.7, TN 130.1 -> 137.3; 10000 x 10000 x 1024 134.5 -> 136.0;
 // 7000 x 7000 x 2048 with alpha 1.5, beta -0.5 136.6 -> 138.7, NT 139.5 ->
-// 138.4.  K = 3000 (every tile's last slice partial): 3000^3 100.2 -> 96.9.
+// 138.4.  With a K tail (once only the iterations that load the partial
+// slice check k): 7000 x 7000 x 1000 130.0 -> 138.4, TN 129.5 -> 137.0;
+// 4096 x 4096 x 1000 133.9 -> 138.9; 8192 x 8192 x 1020 139.9 -> 143.1;
+// 10000 x 10000 x 1012 132.5 -> 136.3; 3000^3 (forced) 100.4 -> 104.4.
 // In the same way the 64x64 grid with two slices in flight (configuration 4)
 // without a split goes to that kernel on 64x64 tiles (configuration 9, four
 // work-groups per compute unit) for whole 64x64 grids of at most
@@ -235,8 +237,9 @@ Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const f
     g.A = A; g.B = B;
     g.lda = lda; g.ldb = ldb;
     g.trans_a = ta; g.trans_b = tb;
-    if (K % 16 != 0 || !sgemm::big_tile_fits(g)) return p;
-    if (p.config == 4 && (M % 64 != 0 || N % 64 != 0 || (int64_t)(M / 64) * (N / 64) > kResidentSmallTiles))
+    if (!sgemm::big_tile_fits(g)) return p;
+    if (p.config == 4 &&
+        (K % 16 != 0 || M % 64 != 0 || N % 64 != 0 || (int64_t)(M / 64) * (N / 64) > kResidentSmallTiles))
         return p;
     return Plan{SGEMM_F32_MFMA_TUNED, p.config == 0 ? 8 : 9, p.group_m, 1};
 }

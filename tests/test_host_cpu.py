@@ -136,15 +136,15 @@ def test_transposed_kernel_selection(sg):
     sel = sg.sgemm_f32_ex_select
     for ta, tb in ((0, 1), (1, 0), (1, 1)):
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.MFMA_TUNED
-        # K a multiple of 16: configuration 8; K = 1000 keeps the 128x128 kernel
+        # configuration 8 wherever its operand conditions hold
         assert sel(ta, tb, 6144, 6144, 2048, 1.0, al, 6144 if ta else 2048, al, 2048 if tb else 6144) \
             == sg.MFMA_TUNED
         assert sg.sgemm_f32_ex_plan(ta, tb, 6144, 6144, 2048, 1.0, al, 6144 if ta else 2048, al,
                                     2048 if tb else 6144)[2] == sg.CFG_128x128_DL
         assert sg.sgemm_f32_ex_plan(ta, tb, 7000, 7000, 1024, 1.0, al, 7000 if ta else 1024, al,
                                     1024 if tb else 7000)[2] == sg.CFG_128x128_DL
-        assert sel(ta, tb, 7000, 7000, 1000, 1.0, al, 7000 if ta else 1000, al, 1000 if tb else 7000) \
-            == sg.MFMA_LARGE
+        assert sg.sgemm_f32_ex_plan(ta, tb, 7000, 7000, 1000, 1.0, al, 7000 if ta else 1000, al,
+                                    1000 if tb else 7000)[2] == sg.CFG_128x128_DL
         assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
@@ -247,7 +247,9 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     for shape in [(7000, 7000, 1024), (7040, 7000, 1024), (10000, 10000, 1024)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
     for shape in [(7040, 7040, 1000), (7000, 7000, 1000)]:
-        assert plan(*shape)[2] == sg.CFG_128x128, shape
+        assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
+    # M not a multiple of 4: the register-staged 128x128 kernel
+    assert plan(7002, 7000, 1024)[1:3] == (sg.MFMA_LARGE, sg.CFG_128x128)
     # Well-filled 256x256 grids take the larger tile.
     for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092)]:
         assert plan(*shape)[2] == sg.CFG_256x256, shape
