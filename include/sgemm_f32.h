@@ -105,8 +105,9 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_128x128_STREAMK = 5, /* 128x128, persistent with stream-K; 16-byte loads only */
     SGEMM_F32_CFG_64x64_BK64 = 6, /* 64x64, slices of 64, two in flight; 16-byte loads only */
     SGEMM_F32_CFG_256x256 = 7,    /* 256x256, one work-group per CU, operands loaded straight into
-                                     LDS; whole tiles only (M and N multiples of 256, K of 16),
-                                     16-byte loads, no K split, group_m ignored (4 is used) */
+                                     LDS; M, N and K multiples of 4 (edge tiles read zeros past
+                                     the matrices), 16-byte loads, no K split, group_m ignored
+                                     (4 is used) */
     SGEMM_F32_CFG_128x128_DL = 8, /* 128x128 by the kernel of configuration 7, two work-groups per
                                      CU; its conditions, no K split */
     SGEMM_F32_CFG_64x64_DL = 9,   /* 64x64 by the kernel of configuration 7, four work-groups per
