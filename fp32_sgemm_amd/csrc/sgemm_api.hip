@@ -219,14 +219,16 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 // In the same way the 64x64 grid with two slices in flight (configuration 4)
 // without a split goes to that kernel on 64x64 tiles (configuration 9, four
 // work-groups per compute unit) for whole 64x64 grids of at most
-// kResidentSmallTiles tiles (one round) with K a multiple of 16: 1024^3 87.8
+// kResidentSmallTiles tiles (one round): 1024^3 87.8
 // -> 92.5, TN 93.6 -> 101.9; 1536^3 97.6 -> 101.5; 2048^3 TN 135.4 -> 139.1;
 // 2048 x 2048 x 1024 127.0 -> 128.0; 512 x 512 x 8192 (no split) 31.8 -> 33.3,
 // TN 30.1 -> 33.6; 2048 x 2000 x 2048 122.6 -> 125.7, TN 121.5 -> 127.8.
 // Grids of several rounds did not gain: 2560^3 127.5 -> 126.7, TN 126.8 ->
 // 128.9; 4608 x 4608 x 2048 135.8 -> 134.9, TN 135.5 -> 138.2; 3008^3 121.4
 // -> 109.5, TN 127.8 -> 121.1; and with edge tiles and a K tail 3000^3 130.6
-// -> 113.4.
+// -> 113.4.  With a K tail: 1024 x 1024 x 1020 84.0 -> 88.0, TN 88.9 -> 96.4;
+// 1024 x 1024 x 4092 118.1 -> 124.4, TN 113.7 -> 126.1; 2048 x 1024 x 1000
+// 112.6 -> 116.4; 2048 x 2048 x 2044 TN 133.0 -> 137.2, NT 130.7 -> 129.0.
 constexpr int64_t kResidentSmallTiles = 1024;
 Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda,
                      const float *B, int ldb) {
@@ -238,8 +240,7 @@ Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const f
     g.lda = lda; g.ldb = ldb;
     g.trans_a = ta; g.trans_b = tb;
     if (!sgemm::big_tile_fits(g)) return p;
-    if (p.config == 4 &&
-        (K % 16 != 0 || M % 64 != 0 || N % 64 != 0 || (int64_t)(M / 64) * (N / 64) > kResidentSmallTiles))
+    if (p.config == 4 && (M % 64 != 0 || N % 64 != 0 || (int64_t)(M / 64) * (N / 64) > kResidentSmallTiles))
         return p;
     return Plan{SGEMM_F32_MFMA_TUNED, p.config == 0 ? 8 : 9, p.group_m, 1};
 }

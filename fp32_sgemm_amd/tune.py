@@ -62,14 +62,14 @@ TILE_BN = {0: 128, 1: 64, 2: 64, 3: 128, 4: 64, 5: 128, 6: 64}
 def runs_as(plan, M, N, K):
     """The configuration the library runs for a table plan: without a split,
     configuration 0, and configuration 4 on a whole 64x64 grid of at most 1024
-    tiles with K a multiple of 16, go to the kernel that loads the operands
+    tiles, go to the kernel that loads the operands
     straight into LDS (configurations 8 and 9).  The sweep times what will run
     and stores the table's configuration."""
     cfg, gm, s = plan
     if s == 1:
         if cfg == 0:
             return (8, gm, 1)
-        if cfg == 4 and K % 16 == 0 and M % 64 == 0 and N % 64 == 0 and (M // 64) * (N // 64) <= 1024:
+        if cfg == 4 and M % 64 == 0 and N % 64 == 0 and (M // 64) * (N // 64) <= 1024:
             return (9, gm, 1)
     return plan
 

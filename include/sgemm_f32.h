@@ -240,9 +240,9 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * conditions; they honour the grouping and take no split count (splits must
  * be 1).  The automatic choice takes configuration 8 in place of the 128 x 128
  * grid and 9 in place of configuration 4, each without a split, when those
- * conditions hold, for configuration 9 also K a multiple of 16 and M and N of
- * 64 with at most 1024 tiles (again, a C stride too wide at call time keeps
- * the plan's register-staged kernel).
+ * conditions hold, for configuration 9 also M and N multiples of 64 with at
+ * most 1024 tiles (again, a C stride too wide at call time keeps the plan's
+ * register-staged kernel).
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -232,15 +232,16 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     plan = lambda M, N, K, ta=0, tb=0: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, M if ta else K, al,
                                                             K if tb else N)
     # 64x64 tiles: loaded straight into LDS (configuration 9) when M and N are
-    # multiples of 64, K of 16 and the grid has at most 1024 tiles (one round),
-    # else with two slices in flight.
+    # multiples of 64 and the grid has at most 1024 tiles (one round), else
+    # with two slices in flight.
     for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
                   (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
                   (2560, 2560, 2560), (3008, 3008, 3008)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
     for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096)]:
         assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL), shape
-    assert plan(2048, 2048, 2044)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
+    assert plan(2048, 2048, 2044)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL)
+    assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
