@@ -29,9 +29,13 @@
  *
  * Readings where the pages are silent (each is listed in the design notes):
  *   - beta == 0: C0 is not read at all (so an uninitialised or NaN-filled C0
- *     gives a finite result), the usual BLAS convention.
- *   - alpha == 0 or K == 0: the product term is exactly zero and A, B are not
- *     read.
+ *     gives a finite result), the usual BLAS convention.  Nothing is added in
+ *     its place: the result is alpha * sum as it stands, so an exactly zero
+ *     sum times a negative alpha is -0.0 (adding +0.0 would turn it into
+ *     +0.0).
+ *   - alpha == 0 or K == 0: there is no product term and A, B are not read;
+ *     the result is beta * C0 alone (-0.0 where beta < 0 and C0 is +0.0), or
+ *     +0.0 when beta == 0 as well.
  *   - Per element the products are added in the order k = 0, 1, ..., K-1.
  *     The product of two floats converted to double is exact (24 + 24 < 53
  *     significand bits), so whether the compiler fuses multiply and add does
@@ -44,6 +48,20 @@
 #include <math.h>
 #include <stdlib.h>
 #include <omp.h>
+
+/*
+ * One element of the result from its two terms, with the special cases above:
+ * the old value C0[at] is read only when beta != 0, and a term that is absent is
+ * not added as a zero.
+ */
+static double combine(int use_product, double alpha, double acc, float beta,
+                      const float *C0, long at)
+{
+    if (beta == 0.0f)
+        return use_product ? alpha * acc : 0.0;
+    const double old = (double)beta * (double)C0[at];
+    return use_product ? alpha * acc + old : old;
+}
 
 /* Number of OpenMP threads the full-matrix routine will use. */
 int oracle_num_threads(void) { return omp_get_max_threads(); }
@@ -68,7 +86,6 @@ int oracle_sgemm_f64(int M, int N, int K, float alpha,
     if (M == 0 || N == 0) return 0;
     const int use_product = (alpha != 0.0f) && (K > 0);
     const double a_s = (double)alpha;
-    const double b_s = (double)beta;
     int failed = 0;
 
 #pragma omp parallel
@@ -95,9 +112,8 @@ int oracle_sgemm_f64(int M, int N, int K, float alpha,
                 }
             }
             for (int j = 0; j < N; ++j) {
-                const double prod = use_product ? a_s * acc[j] : 0.0;
-                const double old = (beta == 0.0f) ? 0.0 : b_s * (double)C0[(long)i * ldc + j];
-                Cref[(long)i * N + j] = prod + old;
+                Cref[(long)i * N + j] = combine(use_product, a_s, acc[j], beta, C0,
+                                                (long)i * ldc + j);
                 if (absab != NULL) absab[(long)i * N + j] = use_product ? aac[j] : 0.0;
             }
         }
@@ -136,9 +152,7 @@ int oracle_sgemm_f64_entries(int M, int N, int K, float alpha,
                 aac += fabs(p);
             }
         }
-        const double prod = use_product ? (double)alpha * acc : 0.0;
-        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];
-        out[t] = prod + old;
+        out[t] = combine(use_product, (double)alpha, acc, beta, C0, i * ldc + j);
         if (absab != NULL) absab[t] = use_product ? aac : 0.0;
     }
     return 0;
@@ -195,9 +209,8 @@ int oracle_sgemm_op_f64(int trans_a, int trans_b, int M, int N, int K, float alp
         for (int j = 0; j < N; ++j) {
             double acc = 0.0, aac = 0.0;
             if (use_product) op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);
-            const double prod = use_product ? (double)alpha * acc : 0.0;
-            const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[(long)i * ldc + j];
-            Cref[(long)i * N + j] = prod + old;
+            Cref[(long)i * N + j] = combine(use_product, (double)alpha, acc, beta, C0,
+                                            (long)i * ldc + j);
             if (absab != NULL) absab[(long)i * N + j] = use_product ? aac : 0.0;
         }
     }
@@ -222,9 +235,7 @@ int oracle_sgemm_op_f64_entries(int trans_a, int trans_b, int M, int N, int K, f
         const long i = rows[t], j = cols[t];
         double acc = 0.0, aac = 0.0;
         if (use_product) op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);
-        const double prod = use_product ? (double)alpha * acc : 0.0;
-        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];
-        out[t] = prod + old;
+        out[t] = combine(use_product, (double)alpha, acc, beta, C0, i * ldc + j);
         if (absab != NULL) absab[t] = use_product ? aac : 0.0;
     }
     return 0;

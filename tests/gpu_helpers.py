@@ -80,6 +80,26 @@ def check_full(C, A, B, alpha, beta, C0, exact=False):
     return oracle.check_within_bound(C, Cref, bound)
 
 
+def zero_sum_integers(M, N, K, seed):
+    """Integer-valued operands (values -4..4) whose product has exactly zero
+    entries: row 1 of A is zero, column 2 of B is zero, and (where the shape
+    allows) entry (0, 0) cancels (A[0, 0:2] = 1, 1 and B[0:2, 0] = 3, -3, the
+    rest of row 0 of A zero).  With alpha < 0 and beta = 0 those entries are
+    alpha * (+0) = -0 in IEEE arithmetic."""
+    rng = np.random.default_rng(seed)
+    A = rng.integers(-4, 5, (M, K)).astype(np.float32)
+    B = rng.integers(-4, 5, (K, N)).astype(np.float32)
+    if M > 1:
+        A[1, :] = 0
+    if N > 2:
+        B[:, 2] = 0
+    if K >= 2:
+        A[0, :] = 0
+        A[0, :2] = 1
+        B[:2, 0] = [3, -3]
+    return A, B
+
+
 def sample_positions(M, N, n_random, seed, full_rows=2, full_cols=2):
     """Random entries plus whole rows and columns (first/last included)."""
     rng = np.random.default_rng(seed)

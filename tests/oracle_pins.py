@@ -14,6 +14,8 @@ What fixes each expected value (none is produced by the code under test):
   * rank-one integer factors: C_ij = u_i w_j (s . t) in closed form;
   * all-ones operands: every entry equals K*alpha + beta*C0 exactly;
   * alpha = 0 and beta = 0: the unused operands are not read (NaN stays out);
+  * IEEE 754's sign rules for zero results (alpha * (+0) with alpha < 0 is -0;
+    beta * C0 alone when there is no product term);
   * the float64 library matmul on random inputs, to within float64 rounding;
   * for the transposed-operand form: its own hand-worked fixture, numpy's exact
     int64 matmul of the explicitly transposed integer operands, the float64
@@ -183,6 +185,67 @@ def pin_scalar_special_cases(o):
     assert np.array_equal(Cref0, 3.0 * C0.astype(np.float64)), "K = 0"
     Cz, _ = o.sgemm_ref(np.zeros((M, K), np.float32), B, 1.0, 1.0, C0)
     assert np.array_equal(Cz, C0.astype(np.float64)), "A = 0, beta = 1 leaves C"
+
+
+def _neg_zero_where(vals, zero_mask):
+    """vals with -0.0 wherever zero_mask holds."""
+    out = np.asarray(vals, dtype=np.float64).copy()
+    out[zero_mask] = -0.0
+    return out
+
+
+def pin_signed_zero(o):
+    # IEEE 754 fixes the sign of a zero result: (-1) * (+0) = -0, (-0.5) * (+0)
+    # = -0, (-0) + (+0) = +0 and (-0) + (-0) = -0 under round-to-nearest.  With
+    # beta = 0 the result is alpha * sum alone; with no product term (alpha = 0
+    # or K = 0) it is beta * C0 alone; beta = 0 with no product term is +0.
+    rng = _rng(12)
+    M, N, K = 6, 7, 9
+    Ai = rng.integers(-4, 5, (M, K))
+    Bi = rng.integers(-4, 5, (K, N))
+    Ai[2] = 0                       # a zero row of A: a zero sum across row 2
+    Bi[:, 4] = 0                    # a zero column of B: a zero sum down column 4
+    Ai[4, :2] = [1, 1]; Ai[4, 2:] = 0
+    Bi[:2, 1] = [3, -3]             # row 4, column 1: 3 - 3 cancels exactly
+    A, B = Ai.astype(np.float32), Bi.astype(np.float32)
+    prod = Ai @ Bi
+    zero = prod == 0
+    assert zero[2].all() and zero[:, 4].all() and zero[4, 1]
+    nanC = np.full((M, N), np.nan, np.float32)
+    want = _neg_zero_where(-prod.astype(np.float64), zero)
+    Cref, _ = o.sgemm_ref(A, B, -1.0, 0.0, nanC)
+    assert np.array_equal(_bits(Cref), _bits(want)), "alpha < 0, beta = 0: alpha * (+0) is -0"
+    for ta, tb in _FORMS:
+        Cop, _ = o.sgemm_ref_op(_stored(A, ta), _stored(B, tb), ta, tb, -1.0, 0.0, nanC)
+        assert np.array_equal(_bits(Cop), _bits(want)), ("op form, beta = 0", ta, tb)
+    r = np.array([2, 4, 0, 5]); c = np.array([3, 1, 4, 0])
+    v, _ = o.sgemm_ref_entries(A, B, r, c, -1.0, 0.0, nanC)
+    assert np.array_equal(_bits(v), _bits(want[r, c])), "entries, beta = 0"
+    v, _ = o.sgemm_ref_op_entries(A, B, r, c, False, False, -1.0, 0.0, nanC)
+    assert np.array_equal(_bits(v), _bits(want[r, c])), "op entries, beta = 0"
+
+    # beta != 0: (-0) + beta * C0 with C0 = +0 is +0 for beta > 0, -0 for beta < 0.
+    C0 = np.zeros((M, N), np.float32)
+    for beta in (1.0, -1.0):
+        Cref, _ = o.sgemm_ref(A, B, -1.0, beta, C0)
+        w = -prod.astype(np.float64)
+        w[zero] = 0.0 if beta > 0 else -0.0
+        assert np.array_equal(_bits(Cref), _bits(w)), ("-0 + beta * (+0)", beta)
+
+    # No product term: beta * C0 alone (-0.5 * +0 = -0); beta = 0 as well: +0.
+    C0 = rng.integers(-3, 4, (M, N)).astype(np.float32)
+    C0[1] = 0.0
+    nanA = np.full((M, K), np.nan, np.float32)
+    nanB = np.full((K, N), np.nan, np.float32)
+    want = _neg_zero_where(-0.5 * C0.astype(np.float64), C0 == 0)
+    Cref, _ = o.sgemm_ref(nanA, nanB, 0.0, -0.5, C0)
+    assert np.array_equal(_bits(Cref), _bits(want)), "alpha = 0: beta * C0 keeps -0"
+    Cref, _ = o.sgemm_ref_op(nanA, nanB, False, False, 0.0, -0.5, C0)
+    assert np.array_equal(_bits(Cref), _bits(want)), "op form, alpha = 0"
+    Cref, _ = o.sgemm_ref(A[:, :0].copy(), B[:0, :].copy(), 2.0, -0.5, C0)
+    assert np.array_equal(_bits(Cref), _bits(want)), "K = 0: beta * C0 keeps -0"
+    Cref, _ = o.sgemm_ref(nanA, nanB, 0.0, 0.0, nanC)
+    assert np.array_equal(_bits(Cref), _bits(np.zeros((M, N)))), "alpha = beta = 0 is +0"
 
 
 def pin_library_matmul(o):
@@ -378,7 +441,7 @@ def pin_lowp_integer_exact(o):
 
 
 PINS = [pin_golden, pin_identity, pin_permutation, pin_transpose, pin_exact_rational,
-        pin_integer_exact, pin_rank_one, pin_all_ones, pin_scalar_special_cases,
+        pin_integer_exact, pin_rank_one, pin_all_ones, pin_scalar_special_cases, pin_signed_zero,
         pin_library_matmul, pin_leading_dims, pin_entries_match,
         pin_uniform_statistics, pin_op_golden, pin_op_integer_exact,
         pin_op_library_matmul, pin_op_transpose_identity, pin_op_entries_match,

@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import from_device_padded, sample_positions, say, to_device_padded
+from gpu_helpers import from_device_padded, say, to_device_padded
 
 pytestmark = pytest.mark.gpu
 
@@ -65,6 +65,17 @@ def run16(sg, kind, ta, tb, A, B, C0, alpha, beta, pad=(0, 0), offs=(0, 0), c_fi
 def _inputs16(M, N, K, dist, kind, seed):
     w = workloads.custom(M, N, K, dist=dist, seed=seed, c0_dist="normal" if dist != "int4" else "int4")
     return workloads.make_inputs_16bit(w, kind)
+
+
+def check16_logical(C, A, B, kind, alpha, beta, C0, exact):
+    """Every element against the float64 oracle on op(A) and op(B) themselves
+    (A, B: the 16-bit patterns of the operands as they enter the product,
+    decoded exactly), for the large shapes."""
+    Cref, absab = oracle.sgemm_ref(oracle.decode_16(A, kind), oracle.decode_16(B, kind),
+                                   alpha, beta, C0)
+    if exact:
+        return oracle.check_bitexact(C, Cref)
+    return oracle.check_within_bound(C, Cref, oracle.error_bound(absab, alpha, beta, C0))
 
 
 def check16(C, As, Bs, kind, ta, tb, alpha, beta, C0, exact):
@@ -140,7 +151,7 @@ def test_gemm16_alpha_zero_and_k_zero(sg):
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
 @pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
-def test_gemm16_headline_shape_sampled(sg, kind, form):
+def test_gemm16_headline_shape(sg, kind, form):
     """4096^3 with alpha 1.5, beta -0.5 on N(0,1) inputs stored in 16 bits: NT
     read in place, NN through the packed path."""
     ta, tb = form
@@ -149,22 +160,17 @@ def test_gemm16_headline_shape_sampled(sg, kind, form):
     A, B, C0 = workloads.make_inputs_16bit(w, kind)
     st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, w.alpha, w.beta)
     assert st == 0 and np.all(np.isfinite(C))
-    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid + kind)
-    vals, absab = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, ta, tb, w.alpha, w.beta, C0)
-    ok, info = oracle.check_within_bound(C[rows, cols], vals,
-                                         oracle.error_bound(absab, w.alpha, w.beta, C0[rows, cols]))
+    ok, info = check16_logical(C, A, B, kind, w.alpha, w.beta, C0, exact=False)
     assert ok, info
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-def test_gemm16_ragged_large_integer_sampled(sg, kind):
+def test_gemm16_ragged_large_integer(sg, kind):
     M, N, K = 4092, 3000, 4100
     A, B, C0 = _inputs16(M, N, K, "int4", kind, 43)
     st, C, As, Bs = run16(sg, kind, 1, 0, A, B, C0, 1.0, 1.0)
     assert st == 0
-    rows, cols = sample_positions(M, N, 3000, seed=44)
-    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 1, 0, 1.0, 1.0, C0)
-    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    ok, info = check16_logical(C, A, B, kind, 1.0, 1.0, C0, exact=True)
     assert ok, info
 
 
@@ -173,17 +179,14 @@ def test_gemm16_ragged_large_integer_sampled(sg, kind):
 def test_gemm16_big_tiles_with_edges(sg, kind, form):
     """Shapes with at least 256 tiles of 256 x 256 (the larger-tile kernel)
     whose M and N are not tile multiples, beta != 0 (the edge epilogue reads
-    and writes C through the buffer resource), checked on samples that include
-    the first and last rows and columns."""
+    and writes C through the buffer resource), every element checked."""
     ta, tb = form
     M, N, K = 4100, 4000, 256
     say(f"[g16_big_edges] kind={kind} {form}")
     A, B, C0 = _inputs16(M, N, K, "uniform", kind, 45 + 2 * ta + tb)
     st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.5, -0.5)
     assert st == 0 and np.all(np.isfinite(C))
-    rows, cols = sample_positions(M, N, 3000, seed=46)
-    vals, absab = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, ta, tb, 1.5, -0.5, C0)
-    ok, info = oracle.check_within_bound(C[rows, cols], vals, oracle.error_bound(absab, 1.5, -0.5, C0[rows, cols]))
+    ok, info = check16_logical(C, A, B, kind, 1.5, -0.5, C0, exact=False)
     assert ok, info
 
 
@@ -193,9 +196,7 @@ def test_gemm16_big_tiles_integer_bitexact(sg, kind):
     A, B, C0 = _inputs16(M, N, K, "int4", kind, 47)
     st, C, As, Bs = run16(sg, kind, 0, 1, A, B, C0, 1.0, -1.0)
     assert st == 0
-    rows, cols = sample_positions(M, N, 3000, seed=48)
-    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, kind, rows, cols, 0, 1, 1.0, -1.0, C0)
-    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    ok, info = check16_logical(C, A, B, kind, 1.0, -1.0, C0, exact=True)
     assert ok, info
 
 
@@ -209,7 +210,22 @@ def test_gemm16_big_tiles_short_k_bitexact(sg, K):
     A, B, C0 = _inputs16(M, N, K, "int4", 1, 60 + K)
     st, C, As, Bs = run16(sg, 1, 0, 1, A, B, C0, 1.0, -1.0)
     assert st == 0
-    rows, cols = sample_positions(M, N, 3000, seed=61)
-    vals, _ = oracle.sgemm_ref_lowp_entries(As, Bs, 1, rows, cols, 0, 1, 1.0, -1.0, C0)
-    ok, info = oracle.check_bitexact(C[rows, cols], vals)
+    ok, info = check16_logical(C, A, B, 1, 1.0, -1.0, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("shape", [(150, 140, 96), (4096, 4096, 64)], ids=["small_grid", "big_tiles"])
+def test_gemm16_negative_alpha_zero_sums_bitexact(sg, kind, shape):
+    """alpha < 0 with beta = 0: exactly zero sums are alpha * (+0) = -0, the
+    oracle's value, on both kernels."""
+    from gpu_helpers import zero_sum_integers
+    M, N, K = shape
+    say(f"[g16_neg_alpha_zero] kind={kind} {shape}")
+    Af, Bf = zero_sum_integers(M, N, K, 72)
+    A, B = workloads.to_16bit(Af, kind), workloads.to_16bit(Bf, kind)
+    st, C, _, _ = run16(sg, kind, 0, 1, A, B, None, -1.0, 0.0, c_fill=np.nan)
+    assert st == 0
+    assert np.all(np.signbit(C[1, :])) and np.all(C[1, :] == 0)
+    ok, info = check16_logical(C, A, B, kind, -1.0, 0.0, None, exact=True)
     assert ok, info

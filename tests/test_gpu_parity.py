@@ -3,8 +3,7 @@
 Real-valued inputs must satisfy |C - Cref| <= 2e-5 * (|alpha|*(|A||B|)_ij +
 |beta|*|C0_ij|) element by element; integer-valued inputs (exact in FP32) must
 match bit for bit.  Sizes span several tiles with ragged tails; the full-size
-workloads are checked on sampled entries (plus whole rows and columns) that the
-oracle computes one by one, and on row and column sums of the whole result.
+workloads are checked element by element against the full oracle as well.
 """
 from __future__ import annotations
 
@@ -14,8 +13,7 @@ import torch
 
 import oracle
 import workloads
-from gpu_helpers import (check_full, check_row_col_sums, check_sampled, run_lib,
-                         sample_positions, say)
+from gpu_helpers import check_full, run_lib, say, zero_sum_integers
 
 pytestmark = pytest.mark.gpu
 
@@ -294,10 +292,10 @@ def test_non_default_stream_ordering(sg):
 
 # ---------------------------------------------------------------------------
 # The named workloads at their full sizes, through sgemm_f32 (the launch the
-# benchmark times).
+# benchmark times), every element against the full oracle.
 # ---------------------------------------------------------------------------
-SMALL_FULL = ["square128", "square128_int", "square1024", "skinny16x4096x4096"]
-LARGE_SAMPLED = ["square4092", "square4096_ab", "square8192", "wide4096x11008x512"]
+WORKLOAD_NAMES = ["square128", "square128_int", "square1024", "skinny16x4096x4096",
+                  "square4092", "square4096_ab", "square8192", "wide4096x11008x512"]
 
 
 def _run_workload(sg, w, dist=None):
@@ -310,37 +308,38 @@ def _run_workload(sg, w, dist=None):
     return w, A, B, C0, C
 
 
-@pytest.mark.parametrize("name", SMALL_FULL)
+@pytest.mark.parametrize("name", WORKLOAD_NAMES)
 def test_workload_full_oracle(sg, name):
     w = workloads.WORKLOADS[name]
-    say(f"[workload_full] {name}")
+    say(f"[workload_full] {name} {w.M}x{w.N}x{w.K} alpha={w.alpha} beta={w.beta}")
     w, A, B, C0, C = _run_workload(sg, w)
     ok, info = check_full(C, A, B, w.alpha, w.beta, C0, exact=(w.dist == "int4"))
-    assert ok, info
-
-
-@pytest.mark.parametrize("name", LARGE_SAMPLED)
-def test_workload_sampled(sg, name):
-    w = workloads.WORKLOADS[name]
-    say(f"[workload_sampled] {name}")
-    w, A, B, C0, C = _run_workload(sg, w)
-    assert np.all(np.isfinite(C)), "unwritten or non-finite entries"
-    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
-    ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols)
-    assert ok, info
-    ok, info = check_row_col_sums(C, A, B, w.alpha, w.beta, C0)
+    say(f"[workload_full] {name} {info}")
     assert ok, info
 
 
 @pytest.mark.parametrize("name", ["square4096_ab", "square4092"])
-def test_workload_integer_bitexact_sampled(sg, name):
+def test_workload_integer_bitexact_full(sg, name):
     """Integer-valued inputs of the full shape: every partial sum stays below
-    2**24, so the GPU result is exact and must match bit for bit."""
+    2**24, so the GPU result is exact and must match bit for bit everywhere."""
     w = workloads.WORKLOADS[name]
     say(f"[workload_int] {name}")
     w, A, B, C0, C = _run_workload(sg, w, dist="int4")
-    rows, cols = sample_positions(w.M, w.N, 4096, seed=w.cid)
-    ok, info = check_sampled(C, A, B, w.alpha, w.beta, C0, rows, cols, exact=True)
+    ok, info = check_full(C, A, B, w.alpha, w.beta, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("variant", GENERAL + ["skinny"])
+def test_negative_alpha_zero_sums_bitexact(sg, variant):
+    """alpha < 0, beta = 0: exactly zero sums come out as alpha * (+0) = -0,
+    the oracle's value; every other entry is exact as well (integer inputs)."""
+    M = 16 if variant == "skinny" else 150
+    N, K = 140, 90
+    A, B = zero_sum_integers(M, N, K, 70)
+    st, C, _ = run_lib(sg, VID[variant], A, B, None, -1.0, 0.0, c_fill=np.nan)
+    assert st == 0
+    assert np.all(np.signbit(C[1, :])) and np.all(C[1, :] == 0)
+    ok, info = check_full(C, A, B, -1.0, 0.0, None, exact=True)
     assert ok, info
 
 

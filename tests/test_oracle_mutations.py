@@ -11,14 +11,16 @@ from oracle_pins import PINS
 
 MUTATIONS = {
     # name: list of (original text, replacement)
-    "drop_beta_term": [("const double old = (beta == 0.0f) ? 0.0 : b_s * (double)C0[(long)i * ldc + j];",
+    "drop_beta_term": [("const double old = (double)beta * (double)C0[at];",
                         "const double old = 0.0;")],
-    "sign_of_beta_term": [("b_s * (double)C0[(long)i * ldc + j];\n                Cref[(long)i * N + j] = prod + old;",
-                           "b_s * (double)C0[(long)i * ldc + j];\n                Cref[(long)i * N + j] = prod - old;")],
-    "op_sign_of_beta_term": [("(double)beta * (double)C0[(long)i * ldc + j];\n            Cref[(long)i * N + j] = prod + old;",
-                              "(double)beta * (double)C0[(long)i * ldc + j];\n            Cref[(long)i * N + j] = prod - old;")],
-    "ignore_alpha": [("const double prod = use_product ? a_s * acc[j] : 0.0;",
-                      "const double prod = use_product ? acc[j] : 0.0;")],
+    "sign_of_beta_term": [("return use_product ? alpha * acc + old : old;",
+                           "return use_product ? alpha * acc - old : old;")],
+    "beta_zero_adds_plus_zero": [("return use_product ? alpha * acc : 0.0;",
+                                  "return use_product ? alpha * acc + 0.0 : 0.0;")],
+    "no_product_adds_plus_zero": [("return use_product ? alpha * acc + old : old;",
+                                   "return use_product ? alpha * acc + old : 0.0 + old;")],
+    "ignore_alpha": [("combine(use_product, a_s, acc[j], beta, C0,",
+                      "combine(use_product, 1.0, acc[j], beta, C0,")],
     "drop_last_k": [("for (int k = 0; k < K; ++k) {\n                    const double a",
                      "for (int k = 0; k < K - 1; ++k) {\n                    const double a")],
     "reversed_k_in_A": [("const double a = (double)A[(long)i * lda + k];",
@@ -35,11 +37,11 @@ MUTATIONS = {
     "op_drop_first_k": [("for (int k = 0; k < K; ++k) {\n        const double p = op_elem",
                          "for (int k = 1; k < K; ++k) {\n        const double p = op_elem")],
     "op_entries_beta_dropped": [("op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);\n"
-                                 "        const double prod = use_product ? (double)alpha * acc : 0.0;\n"
-                                 "        const double old = (beta == 0.0f) ? 0.0 : (double)beta * (double)C0[i * ldc + j];",
+                                 "        out[t] = combine(use_product, (double)alpha, acc, beta, C0,",
                                  "op_dot(trans_a, trans_b, K, A, lda, B, ldb, i, j, &acc, &aac);\n"
-                                 "        const double prod = use_product ? (double)alpha * acc : 0.0;\n"
-                                 "        const double old = 0.0;")],
+                                 "        out[t] = combine(use_product, (double)alpha, acc, 0.0f, C0,")],
+    "op_full_alpha_ignored": [("Cref[(long)i * N + j] = combine(use_product, (double)alpha, acc, beta, C0,",
+                               "Cref[(long)i * N + j] = combine(use_product, 1.0, acc, beta, C0,")],
     "bf16_bias_126": [("decode_16(in[t], 8, 7, 127)", "decode_16(in[t], 8, 7, 126)")],
     "f16_no_subnormals": [("x = ldexp((double)f / scale, 1 - bias);", "x = 0.0;")],
     "subnormal_exponent_off_by_one": [("x = ldexp((double)f / scale, 1 - bias);", "x = ldexp((double)f / scale, -bias);")],
