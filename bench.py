@@ -7,16 +7,29 @@ place), with all inputs resident in device memory.  Prints one JSON line.
 ``--operands nt|tn|tt`` stores A and/or B transposed and times ``sgemm_f32_ex``
 on the same product.
 
-Timing: W untimed warm-up steps, then K timed steps bracketed by device
-synchronisation; each launch is also bracketed by HIP events recorded on the
-stream the kernel runs on, which give the kernel's average duration for the
-roofline figure.  The FLOP count is 2*M*N*K per step (the scaling by alpha and
-beta is not counted, "How a Matmul Kernel Gets Fast", section 1 and "Writing a
-Fast Matmul in CUDA, Step by Step", section "Step 1").
+Timing follows the pages' method ("Writing a Fast Matmul in CUDA, Step by
+Step", section "Step 1: the problem and the yardstick"): the GPU starts in a
+low-power state, so the step is first launched back to back for a fixed time
+(``--prewarm-seconds``, 0.6 s by default) before anything is counted.  Then W
+untimed warm-up steps and K timed steps bracketed by device synchronisation
+give ``value``; each timed launch is also bracketed by HIP events recorded on
+the stream the kernel runs on, which give the kernel's average duration for the
+roofline figure and the median of the last three quarters of the launches.
+Three further rounds of back-to-back launches (events around each, the median
+of each round's last three quarters, then the median over rounds) are run for
+this library and, interleaved with it under the same warm state, for the
+vendor libraries as context.  The FLOP count is 2*M*N*K per step (the scaling
+by alpha and beta is not counted, "How a Matmul Kernel Gets Fast", section 1
+and the same page's "Step 1").
 
-The CPU baseline is the float64 oracle timed on the host's cores on a bounded
-sample of the same product (its first rows), reported beside the GPU number.
-As context (not the product), the same product on the same inputs and stream
+Parity in the same run: after the timing, C is reset to its initial contents,
+the step runs once more, and every element of C is compared with the float64
+oracle (within the error bound, or bit for bit for integer-valued inputs), as
+the pages check each kernel against a float64 evaluation.  That oracle run is
+also the CPU baseline: the oracle timed on the host's cores on the whole
+product, plus one thread on a bounded part of it.
+
+Context (not the product): the same product on the same inputs and stream
 through rocBLAS ``sgemm`` and through torch's FP32 ``addmm`` (hipBLASLt), and
 the GPU's shader clock read with amd-smi while the kernel runs, which gives the
 clock-adjusted FP32 peak (256 CUs x 256 FLOP per clock x clock).
@@ -92,31 +105,64 @@ def measured_traffic():
         return None
 
 
-# --- vendor libraries on the same GPU (context, not the product) ---------------------
-def _time_launches(torch, stream, call, steps, warmup):
-    """Mean and median per-launch duration (ms), each launch between its own
-    pair of events on `stream`."""
+# --- launch timing -------------------------------------------------------------------
+def prewarm(torch, stream, call, seconds: float) -> float:
+    """Launches `call` back to back on `stream` until `seconds` of wall time
+    (synchronised) have passed; returns the time spent."""
+    t0 = time.perf_counter()
+    batch = 1
     with torch.cuda.stream(stream):
-        for _ in range(warmup):
-            call()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    torch.cuda.synchronize()
+        while True:
+            for _ in range(batch):
+                call()
+            stream.synchronize()
+            dt = time.perf_counter() - t0
+            if dt >= seconds:
+                return dt
+            batch = min(batch * 2, 256)
+
+
+def event_launches(torch, stream, call, n: int):
+    """`n` launches back to back, each between its own pair of events on
+    `stream`; returns the per-launch durations in ms, in launch order."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    stream.synchronize()
     with torch.cuda.stream(stream):
         for a, b in evs:
             a.record(stream)
             call()
             b.record(stream)
-    torch.cuda.synchronize()
-    ms = sorted(a.elapsed_time(b) for a, b in evs)
-    return sum(ms) / len(ms), ms[len(ms) // 2]
+    stream.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
 
 
-def library_context16(torch, w, ta, tb, dA, dBs, kind16, stream, steps, warmup):
+def median_last_three_quarters(ms):
+    """The pages' statistic: the median of the launches after the first quarter."""
+    tail = sorted(ms[len(ms) // 4:])
+    return tail[len(tail) // 2]
+
+
+def timed_rounds(torch, stream, calls: dict, est_ms: dict, round_s: float, rounds: int = 3,
+                 max_launches: int = 2000):
+    """Interleaved rounds: in each round every call in `calls` runs back to
+    back for about `round_s` seconds (at most `max_launches` launches).
+    Returns {name: {"rounds_ms": [median of last 3/4 per round], "all_ms": [...]}}."""
+    out = {k: {"rounds_ms": [], "all_ms": []} for k in calls}
+    for _ in range(rounds):
+        for name, call in calls.items():
+            n = int(min(max_launches, max(20, round_s / max(est_ms[name] * 1e-3, 1e-7))))
+            ms = event_launches(torch, stream, call, n)
+            out[name]["rounds_ms"].append(median_last_three_quarters(ms))
+            out[name]["all_ms"].extend(ms)
+    return out
+
+
+# --- vendor libraries on the same GPU (context, not the product) ---------------------
+def library_calls16(torch, w, ta, tb, dA, dBs, kind16):
     """torch's matmul of the same 16-bit operand views with an FP32 output
-    (hipBLASLt), on the same stream.  It computes the plain product (alpha 1,
-    beta 0: torch's mm with an FP32 output of 16-bit inputs takes neither), so
-    it does less work than a workload with beta != 0."""
-    flops = gemm_flops(w.M, w.N, w.K)
+    (hipBLASLt).  It computes the plain product (alpha 1, beta 0: torch's mm
+    with an FP32 output of 16-bit inputs takes neither), so it does less work
+    than a workload with beta != 0."""
     dt = torch.bfloat16 if kind16 == 1 else torch.float16
     Aop = dA.view(dt).t() if ta else dA.view(dt)
     Bops = [b.view(dt).t() if tb else b.view(dt) for b in dBs]
@@ -128,25 +174,24 @@ def library_context16(torch, w, ta, tb, dA, dBs, kind16, stream, steps, warmup):
         turn[0] += 1
         torch.mm(Aop, b, out_dtype=torch.float32, out=out_c)
     try:
-        mean, med = _time_launches(torch, stream, tm, steps, warmup)
+        tm()
+        torch.cuda.synchronize()
     except (RuntimeError, TypeError) as e:
-        return {"torch_mm_fp32_out": {"error": str(e)[:200]}}
-    return {"torch_mm_fp32_out": {"value": round(flops / mean / 1e9, 3), "median_launch": round(flops / med / 1e9, 3),
-                                  "unit": "TFLOP/s", "kernel_avg_ms": round(mean, 5),
-                                  "note": "plain product (alpha 1, beta 0)"}}
+        return {}, {"torch_mm_fp32_out": {"error": str(e)[:200]}}
+    return {"torch_mm_fp32_out": tm}, {"torch_mm_fp32_out": {"note": "plain product (alpha 1, beta 0)"}}
 
 
-def library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream, steps, warmup):
-    """rocBLAS sgemm and torch's FP32 matmul (hipBLASLt) on the same product,
-    inputs and stream.  rocBLAS is column-major: the row-major product
-    C = op(A) op(B) is the column-major C^T = op(B)^T op(A)^T, so B is passed
-    first with its own transpose flag (rocBLAS operation 111 = none, 112 =
-    transpose).  Each library call takes the next of the B copies in turn, as
-    the timed steps do."""
+def library_calls(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream):
+    """rocBLAS sgemm and torch's FP32 addmm (hipBLASLt) on the same product,
+    inputs and stream, as callables, plus notes.  rocBLAS is column-major: the
+    row-major product C = op(A) op(B) is the column-major C^T = op(B)^T op(A)^T,
+    so B is passed first with its own transpose flag (rocBLAS operation 111 =
+    none, 112 = transpose); its operand mapping is checked once against
+    torch's product of the same views.  Each library call takes the next of the
+    B copies in turn, as the timed steps do."""
     import ctypes
 
-    flops = gemm_flops(w.M, w.N, w.K)
-    out = {}
+    calls, notes = {}, {}
     dB = dBs[0]
     turn = [0]
 
@@ -173,9 +218,6 @@ def library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream, steps, warm
             if st != 0:
                 raise RuntimeError(f"rocblas_sgemm returned {st}")
 
-        mean, med = _time_launches(torch, stream, roc, steps, warmup)
-        # The operand mapping is checked once: rocBLAS with beta 0 against
-        # torch's product of the same views.
         z = ctypes.c_float(0.0)
         with torch.cuda.stream(stream):
             lib.rocblas_sgemm(handle, op_b, op_a, w.N, w.M, w.K, ctypes.byref(al), dB.data_ptr(), ldb,
@@ -183,12 +225,11 @@ def library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream, steps, warm
             ref = w.alpha * ((dA.t() if ta else dA) @ (dB.t() if tb else dB))
         torch.cuda.synchronize()
         agree = bool(((dC - ref).abs().max() <= 1e-3 * ref.abs().max().clamp_min(1e-30)).item())
-        lib.rocblas_destroy_handle(handle)
-        out["rocblas_sgemm"] = {"value": round(flops / mean / 1e9, 3), "median_launch": round(flops / med / 1e9, 3),
-                                "unit": "TFLOP/s", "kernel_avg_ms": round(mean, 5), "same_product": agree}
         del ref
+        calls["rocblas_sgemm"] = roc
+        notes["rocblas_sgemm"] = {"same_product": agree}
     except (OSError, AttributeError, RuntimeError) as e:
-        out["rocblas_sgemm"] = {"error": str(e)}
+        notes["rocblas_sgemm"] = {"error": str(e)}
     Aop = dA.t() if ta else dA
     torch.backends.cuda.matmul.allow_tf32 = False
 
@@ -196,10 +237,9 @@ def library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream, steps, warm
         b = next_b()
         dC.addmm_(Aop, b.t() if tb else b, beta=w.beta, alpha=w.alpha)
 
-    mean, med = _time_launches(torch, stream, tm, steps, warmup)
-    out["torch_addmm"] = {"value": round(flops / mean / 1e9, 3), "median_launch": round(flops / med / 1e9, 3),
-                          "unit": "TFLOP/s", "kernel_avg_ms": round(mean, 5)}
-    return out
+    calls["torch_addmm"] = tm
+    notes["torch_addmm"] = {}
+    return calls, notes
 
 
 def gfx_clock_mhz(torch, step, stream, kern_s):
@@ -255,44 +295,57 @@ def gfx_clock_mhz(torch, step, stream, kern_s):
     return sum(flat) / len(flat), readings
 
 
-# --- CPU baseline (the oracle on a bounded sample) -----------------------------------
-def cpu_baseline(A, B, C0, alpha, beta, target_s: float):
+# --- parity in the same run, and the CPU baseline ------------------------------------
+def parity_and_cpu_baseline(A, B, C0, alpha, beta, C_gpu, exact: bool, kind16, single_core_s: float):
+    """Every element of the GPU result against the float64 oracle on the same
+    operands (A, B as they enter the product; 16-bit patterns decoded exactly).
+    Returns (parity, cpu_baseline): the oracle's run on all host cores over the
+    whole product is the CPU baseline, and one thread on the first rows (about
+    `single_core_s` seconds) is a per-core reference."""
+    import numpy as np
+
     import oracle
 
+    if kind16:
+        A = oracle.decode_16(A, kind16)
+        B = oracle.decode_16(B, kind16)
     M, K = A.shape
     N = B.shape[1]
     cores = oracle.num_threads()
-    rows = min(M, max(cores, 8))
     t0 = time.perf_counter()
-    oracle.sgemm_ref(A[:rows], B, alpha, beta, None if C0 is None else C0[:rows])
+    Cref, absab = oracle.sgemm_ref(A, B, alpha, beta, C0)
     dt = time.perf_counter() - t0
-    per_row = dt / rows
-    R = int(min(M, max(rows, target_s / max(per_row, 1e-9))))
-    R = max(cores, (R // cores) * cores) if R >= cores else R
-    R = min(R, M)
-    t0 = time.perf_counter()
-    oracle.sgemm_ref(A[:R], B, alpha, beta, None if C0 is None else C0[:R])
-    dt = time.perf_counter() - t0
-    # Per-core reference: the same routine on one thread, on about a tenth of
-    # the time budget.
+    if exact:
+        ok, info = oracle.check_bitexact(C_gpu, Cref)
+        parity = {"ok": ok, "elements": int(M * N), "check": "bit-exact (integer-valued inputs)",
+                  "n_bad": info["n_bad"]}
+    else:
+        ok, info = oracle.check_within_bound(C_gpu, Cref, oracle.error_bound(absab, alpha, beta, C0))
+        parity = {"ok": ok, "elements": int(M * N),
+                  "check": "|C - Cref| <= 2e-5 (|alpha| |A||B| + |beta| |C0|)",
+                  "n_bad": info["n_bad"], "max_err_over_bound": round(info.get("max_err_over_bound", 0.0), 6)}
+    if "first_bad_index" in info:
+        parity["first_bad_index"] = list(info["first_bad_index"])
+    del Cref, absab
     oracle.set_num_threads(1)
     try:
-        r1 = int(min(M, max(1, (target_s / 10) / max(dt / R * cores, 1e-9))))
+        r1 = int(min(M, max(1, single_core_s / max(dt / M * cores, 1e-9))))
         t0 = time.perf_counter()
         oracle.sgemm_ref(A[:r1], B, alpha, beta, None if C0 is None else C0[:r1])
         dt1 = time.perf_counter() - t0
     finally:
         oracle.set_num_threads(cores)
-    return {
-        "value": round(gemm_flops(R, N, K) / dt / 1e12, 6),
+    base = {
+        "value": round(gemm_flops(M, N, K) / dt / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": cores,
         "kind": "oracle",
-        "sample": f"rows 0..{R - 1} of the {M}x{N}x{K} product ({R * N} outputs, "
-                  f"float64 accumulation, {dt:.1f} s)",
+        "sample": f"the whole {M}x{N}x{K} product ({M * N} outputs, float64 accumulation, "
+                  f"{dt:.1f} s; the run that checks the GPU result)",
         "single_core": {"value": round(gemm_flops(r1, N, K) / dt1 / 1e12, 6), "unit": "TFLOP/s",
                         "sample": f"rows 0..{r1 - 1} of the same product on one thread ({dt1:.1f} s)"},
     }
+    return parity, base
 
 
 def main():
@@ -311,11 +364,17 @@ def main():
     ap.add_argument("--inputs16", default=None, choices=["bf16", "f16"],
                     help="time gemm16_f32 instead: A and B stored in this 16-bit format, "
                          "FP32 accumulation and C")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0,
-                    help="approximate CPU time for the oracle baseline sample")
+    ap.add_argument("--prewarm-seconds", type=float, default=0.6,
+                    help="back-to-back launches before anything is counted (the GPU starts in a "
+                         "low-power state)")
+    ap.add_argument("--round-seconds", type=float, default=0.5,
+                    help="length of each of the three interleaved timing rounds (0: none)")
+    ap.add_argument("--single-core-seconds", type=float, default=1.5,
+                    help="approximate time of the one-thread oracle reference")
     ap.add_argument("--plan", default=None, metavar="CONFIG[:GROUP[:SPLITS]]",
                     help="run one MFMA plan through sgemm_f32_ex_config instead of the automatic choice")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the oracle: no parity check and no CPU baseline (profiling runs)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the rocBLAS / torch timings and the clock reading")
     ap.add_argument("--rotate", type=int, default=1, metavar="COPIES",
@@ -417,6 +476,7 @@ def main():
             raise RuntimeError(f"sgemm_f32 returned {st}")
 
     torch.cuda.synchronize(dev)
+    prewarm_s = prewarm(torch, stream, step, args.prewarm_seconds) if args.prewarm_seconds > 0 else 0.0
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             step()
@@ -439,15 +499,17 @@ def main():
     value = flops * args.steps / elapsed / 1e12
     kern_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     kern_avg_s = float(np.mean(kern_ms)) / 1e3
+    kern_med_s = median_last_three_quarters(kern_ms) / 1e3
     achieved = flops / kern_avg_s / 1e12
 
     peak = PEAK_16BIT_TFLOPS if kind16 else PEAK_FP32_TFLOPS
     memory_bound = arithmetic_intensity(w.M, w.N, w.K, w.beta != 0) < peak * 1e12 / (PEAK_HBM_GBS * 1e9)
+    min_bytes = gemm_min_bytes(w.M, w.N, w.K, w.beta != 0)
     if kind16 and not memory_bound:
         roofline = {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak, "unit": "TFLOP/s",
                     "frac": round(achieved / peak, 4)}
     elif memory_bound:
-        ach_gbs = gemm_min_bytes(w.M, w.N, w.K, w.beta != 0) / kern_avg_s / 1e9
+        ach_gbs = min_bytes / kern_avg_s / 1e9
         roofline = {"bound": "hbm", "achieved": round(ach_gbs, 2), "peak": PEAK_HBM_GBS,
                     "unit": "GB/s", "frac": round(ach_gbs / PEAK_HBM_GBS, 4)}
     else:
@@ -460,6 +522,7 @@ def main():
                        and not kind16 and len(dBs) == 1)
     roofline["traffic"] = measured_traffic() if headline_kernel else None
     roofline["kernel_avg_ms"] = round(kern_avg_s * 1e3, 5)
+    roofline["kernel_median_last_3q_ms"] = round(kern_med_s * 1e3, 5)
 
     if kind16:
         chosen_name = "gemm16_" + args.inputs16
@@ -473,6 +536,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "prewarm_s": round(prewarm_s, 3),
         "ms_per_step": round(elapsed / args.steps * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -486,7 +550,37 @@ def main():
                    "b_copies": len(dBs), "parallelism": "single GPU"},
         "roofline": roofline,
     }
+    if memory_bound:
+        out["gb_per_s"] = round(min_bytes * args.steps / elapsed / 1e9, 2)
     if not args.no_context:
+        if kind16:
+            calls, notes = library_calls16(torch, w, ta, tb, dA, dBs, kind16)
+        else:
+            calls, notes = library_calls(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream)
+        calls = {"this_library": step, **calls}
+        est = {"this_library": kern_avg_s * 1e3}
+        for name, call in calls.items():
+            if name != "this_library":
+                ms = event_launches(torch, stream, call, 5)
+                est[name] = float(np.median(ms))
+        if args.round_seconds > 0:
+            res = timed_rounds(torch, stream, calls, est, args.round_seconds)
+            ctx = {}
+            for name, r in res.items():
+                med = sorted(r["rounds_ms"])[len(r["rounds_ms"]) // 2]
+                entry = {"value": round(flops / (med * 1e-3) / 1e12, 3), "unit": "TFLOP/s",
+                         "rounds": [round(flops / (m * 1e-3) / 1e12, 3) for m in r["rounds_ms"]],
+                         "mean_launch": round(flops / (float(np.mean(r["all_ms"])) * 1e-3) / 1e12, 3),
+                         "launches": len(r["all_ms"])}
+                entry.update(notes.get(name, {}))
+                ctx[name] = entry
+            for name, note in notes.items():
+                if name not in ctx:
+                    ctx[name] = note
+            out["context"] = {"method": "three interleaved rounds of back-to-back launches, each "
+                                        f"about {args.round_seconds} s; per round the median of the "
+                                        "last three quarters; value = median over rounds",
+                              **ctx}
         mhz, readings = gfx_clock_mhz(torch, step, stream, kern_avg_s)
         if mhz is not None:
             # 256 CUs x 4 matrix-core SIMDs x 64 FP32 FLOP per clock each.
@@ -501,14 +595,29 @@ def main():
                 out["clock"]["frac_of_clock_adjusted_16bit_peak"] = round(achieved / adj16, 4)
         else:
             out["clock"] = {"gfx_mhz": None, "note": readings}
-        if not kind16:
-            out["context"] = library_context(torch, w, ta, tb, dA, lda, dBs, ldb, C0, stream,
-                                             min(args.steps, 50), 5)
+    failed = False
+    if not args.no_cpu_baseline:
+        # One more call on the initial C (beta != 0 reads it), with the first B
+        # copy, checked element by element.
+        if C0 is not None:
+            dC.copy_(torch.from_numpy(C0).to(dev))
         else:
-            out["context"] = library_context16(torch, w, ta, tb, dA, dBs, kind16, stream, min(args.steps, 50), 5)
-    if not args.no_cpu_baseline and not kind16:
-        out["cpu_baseline"] = cpu_baseline(A, B, C0, w.alpha, w.beta, args.cpu_seconds)
+            dC.fill_(float("nan"))
+        counter[0] = 0
+        torch.cuda.synchronize(dev)
+        with torch.cuda.stream(stream):
+            step()
+        torch.cuda.synchronize(dev)
+        C_gpu = dC.cpu().numpy()
+        parity, base = parity_and_cpu_baseline(A, B, C0, w.alpha, w.beta, C_gpu, w.dist == "int4", kind16,
+                                               args.single_core_seconds)
+        out["parity"] = parity
+        out["cpu_baseline"] = base
+        failed = not parity["ok"]
     print(json.dumps(out), flush=True)
+    if failed:
+        print("parity check FAILED: the timed result does not match the oracle", file=sys.stderr)
+        sys.exit(3)
 
 
 if __name__ == "__main__":

@@ -455,3 +455,41 @@ def test_big_tiles_for_whole_filled_grids(sg):
             == sg.ERR_NOT_APPLICABLE, (M, N, K)
     assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, 512, 512, 64, 1.0, p + 4, 64, p, 512, 0.0, p, 512, 0) \
         == sg.ERR_NOT_APPLICABLE
+
+
+def test_bench_median_of_last_three_quarters():
+    """The pages' statistic: drop the first quarter of the launches, take the
+    median of the rest (hand-worked: 8 launches, the first 2 dropped)."""
+    import bench
+    ms = [9.0, 8.0, 1.0, 5.0, 3.0, 4.0, 2.0, 6.0]
+    # last three quarters: 1, 5, 3, 4, 2, 6 -> sorted 1 2 3 4 5 6 -> element 3 is 4
+    assert bench.median_last_three_quarters(ms) == 4.0
+    assert bench.median_last_three_quarters([7.0]) == 7.0
+
+
+def test_bench_parity_leg_flags_a_wrong_element():
+    """The benchmark's in-run parity check passes a result within the bound
+    and fails one element moved past it, and reports the whole product."""
+    import numpy as np
+
+    import bench
+    rng = np.random.default_rng(5)
+    A = rng.standard_normal((33, 20)).astype(np.float32)
+    B = rng.standard_normal((20, 17)).astype(np.float32)
+    C0 = rng.standard_normal((33, 17)).astype(np.float32)
+    good = (1.5 * (A.astype(np.float64) @ B.astype(np.float64)) - 0.5 * C0).astype(np.float32)
+    parity, base = bench.parity_and_cpu_baseline(A, B, C0, 1.5, -0.5, good, False, None, 0.01)
+    assert parity["ok"] and parity["elements"] == 33 * 17 and parity["n_bad"] == 0
+    assert base["kind"] == "oracle" and base["cores"] >= 1
+    bad = good.copy()
+    bad[7, 3] += 1e-2
+    parity, _ = bench.parity_and_cpu_baseline(A, B, C0, 1.5, -0.5, bad, False, None, 0.01)
+    assert not parity["ok"] and parity["n_bad"] == 1 and parity["first_bad_index"] == [7, 3]
+    Ai = rng.integers(-4, 5, (9, 11)).astype(np.float32)
+    Bi = rng.integers(-4, 5, (11, 5)).astype(np.float32)
+    exact = (Ai @ Bi).astype(np.float32)
+    parity, _ = bench.parity_and_cpu_baseline(Ai, Bi, None, 1.0, 0.0, exact, True, None, 0.01)
+    assert parity["ok"]
+    exact[0, 0] = np.nextafter(exact[0, 0], np.float32(np.inf))
+    parity, _ = bench.parity_and_cpu_baseline(Ai, Bi, None, 1.0, 0.0, exact, True, None, 0.01)
+    assert not parity["ok"]
