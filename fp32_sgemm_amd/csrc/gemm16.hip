@@ -16,8 +16,8 @@
 // memory and in LDS, and every fragment is one ds_read_b128.  Other operand
 // forms, operands that are not 16-byte aligned, and K not a multiple of the
 // 64-deep slice are first packed by pack16_kernel into a K-major copy with K
-// padded by zeros (adding exact zeros changes no sum), in the stream's
-// workspace.
+// padded by zeros (adding exact zeros changes no sum), in the call's scratch
+// (a stream-ordered allocation, released after the GEMM kernel).
 //
 // Tiles.  A work-group computes a 128 x 128 tile of C with 4 waves of 64 x 64
 // (2 x 2 blocks of 32 x 32).  Slices of 64 k are staged in LDS, double
@@ -541,16 +541,19 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     a.C = g16.C; a.ldc = g16.ldc;
     a.A = static_cast<const uint16_t *>(A); a.lda = g16.lda;
     a.B = static_cast<const uint16_t *>(B); a.ldb = g16.ldb;
+    void *ws = nullptr;
     if (pa || pb) {
-        void *ws = nullptr;
         const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb);
-        hipError_t e = stream_workspace((size_t)bytes, stream, &ws);
+        hipError_t e = scratch_acquire(g16.scratch, (size_t)bytes, stream, &ws);
         if (e != hipSuccess) return e;
         unsigned char *p = static_cast<unsigned char *>(ws);
         if (pa) {
             uint16_t *dst = reinterpret_cast<uint16_t *>(p);
             e = pack(static_cast<const uint16_t *>(A), g16.lda, ta != 0, M, K, dst, Kp, stream);
-            if (e != hipSuccess) return e;
+            if (e != hipSuccess) {
+                scratch_release(g16.scratch, ws, stream);
+                return e;
+            }
             a.A = dst;
             a.lda = Kp;
             p += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
@@ -559,11 +562,15 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             uint16_t *dst = reinterpret_cast<uint16_t *>(p);
             // B as given is K x N: (n, k) at B[k * ldb + n], M/N-major.
             e = pack(static_cast<const uint16_t *>(B), g16.ldb, tb == 0, N, K, dst, Kp, stream);
-            if (e != hipSuccess) return e;
+            if (e != hipSuccess) {
+                scratch_release(g16.scratch, ws, stream);
+                return e;
+            }
             a.B = dst;
             a.ldb = Kp;
         }
     }
+    hipError_t e;
     if (use_big_tiles(M, N, g16.ldc)) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
         const dim3 grid(tiles_m * tiles_n);
@@ -571,15 +578,18 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             hipLaunchKernelGGL(gemm16_dl_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
         else
             hipLaunchKernelGGL(gemm16_dl_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-        return hipGetLastError();
+        e = hipGetLastError();
+    } else {
+        const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+        const dim3 grid(tiles_m * tiles_n);
+        if (kind == GEMM16_F32_F16)
+            hipLaunchKernelGGL(gemm16_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        else
+            hipLaunchKernelGGL(gemm16_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        e = hipGetLastError();
     }
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-    const dim3 grid(tiles_m * tiles_n);
-    if (kind == GEMM16_F32_F16)
-        hipLaunchKernelGGL(gemm16_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-    else
-        hipLaunchKernelGGL(gemm16_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-    return hipGetLastError();
+    const hipError_t r = scratch_release(g16.scratch, ws, stream);
+    return e == hipSuccess ? r : e;
 }
 
 }  // namespace sgemm

@@ -6,6 +6,15 @@
 
 namespace sgemm {
 
+// Where one call's scratch memory comes from: a caller-provided region
+// (`fixed`, `fixed_bytes` long: the allocation-free entry point), or, when
+// `fixed` is null, a stream-ordered allocation from the library's per-device
+// memory pool.
+struct Scratch {
+    void *fixed = nullptr;
+    size_t fixed_bytes = 0;
+};
+
 // Arguments of one C = alpha*op(A)*op(B) + beta*C call, row-major, strides in
 // elements.  trans_a == 0: A is stored M x K; otherwise K x M and op(A) is its
 // transpose.  trans_b == 0: B is stored K x N; otherwise N x K.  Only the MFMA
@@ -18,6 +27,7 @@ struct GemmArgs {
     float *C;
     int64_t lda, ldb, ldc;
     int trans_a = 0, trans_b = 0;
+    Scratch scratch;
 };
 
 // Launchers: each enqueues its kernel(s) on `stream` and returns the HIP error
@@ -36,8 +46,8 @@ hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stre
 // CU).  Configurations 2-9 exist with 16-byte loads only.  `group_m` is the
 // number of tile rows walked together by the tile order (configuration 7 uses
 // 4); `splits` divides K over work-groups (the partial sums go through the
-// stream's workspace and a reduction kernel; not with configurations 5, 7, 8
-// and 9).
+// call's scratch and a reduction kernel; not with configurations 5, 7, 8 and
+// 9).
 constexpr int kNumMfmaConfigs = 10;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
@@ -67,10 +77,20 @@ int64_t gemm16_grid(int M, int N);
 // Whether the 256 x 256 tile kernel takes the product (else 128 x 128).
 bool use_big_tiles(int M, int N, int64_t ldc);
 
-// The workspace of `stream` on the current device, at least `bytes` long.  It
-// stays valid for work queued on that stream until the next call that asks
-// for more.
-hipError_t stream_workspace(size_t bytes, hipStream_t stream, void **out);
+// Scratch of at least `bytes` for the kernels a launcher is about to enqueue on
+// `stream` (sgemm_scratch.hip), and its release after them (stream-ordered; a
+// fixed region is handed out as it is and never released).  A launcher
+// acquires before it enqueues anything, so a failed acquire leaves C alone.
+// With a fixed region, a request larger than it fails with
+// hipErrorOutOfMemory.
+hipError_t scratch_acquire(const Scratch &s, size_t bytes, hipStream_t stream, void **out);
+hipError_t scratch_release(const Scratch &s, void *p, hipStream_t stream);
+
+// Scratch bytes that a launch will acquire (host side, no HIP call except the
+// occupancy query of the stream-K plan): the M <= 16 kernel, an MFMA plan, and
+// the 16-bit GEMM.
+int64_t skinny_scratch_bytes(const GemmArgs &g);
+hipError_t mfma_config_scratch_bytes(const GemmArgs &g, int config, int splits, int64_t *bytes);
 
 // Tile counts that each launcher's grid uses (host side, for the size check).
 int64_t mfma_large_grid(int M, int N);

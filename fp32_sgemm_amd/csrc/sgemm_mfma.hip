@@ -958,23 +958,43 @@ hipError_t resident_groups(int *out) {
     return hipSuccess;
 }
 
+// The stream-K plan's split: whole rounds of P resident work-groups, then the
+// remaining tiles' K slices in equal shares.  With a remainder, the last whole
+// round joins the stream-K part, so each work-group's share is at least one
+// tile's K slices and a tile is cut at most once ("data-parallel plus one-tile
+// stream-K").
+template <class T>
+hipError_t streamk_plan(const GemmArgs &g, StreamK *sk, int *tiles_m, int *tiles_n) {
+    *tiles_m = (g.M + T::BM - 1) / T::BM;
+    *tiles_n = (g.N + T::BN - 1) / T::BN;
+    const int tiles = *tiles_m * *tiles_n;
+    hipError_t e = resident_groups<T>(&sk->P);
+    if (e != hipSuccess) return e;
+    sk->ipt = (g.K + T::BK - 1) / T::BK;
+    sk->rounds = tiles / sk->P;
+    if (sk->rounds > 0 && tiles % sk->P != 0) sk->rounds -= 1;
+    sk->rem_begin = sk->rounds * sk->P;
+    sk->units = (int64_t)(tiles - sk->rem_begin) * sk->ipt;
+    sk->ws = nullptr;
+    return hipSuccess;
+}
+
+template <class T>
+int64_t streamk_scratch_bytes(const StreamK &sk) {
+    return sk.units == 0 ? 0 : (int64_t)2 * sk.P * T::BM * T::BN * (int64_t)sizeof(float);
+}
+
 template <class T>
 hipError_t launch_streamk(const GemmArgs &g, int group_m, hipStream_t stream) {
-    const int tiles_m = (g.M + T::BM - 1) / T::BM;
-    const int tiles_n = (g.N + T::BN - 1) / T::BN;
-    const int tiles = tiles_m * tiles_n;
     StreamK sk;
-    hipError_t e = resident_groups<T>(&sk.P);
+    int tiles_m = 0, tiles_n = 0;
+    hipError_t e = streamk_plan<T>(g, &sk, &tiles_m, &tiles_n);
     if (e != hipSuccess) return e;
-    sk.ipt = (g.K + T::BK - 1) / T::BK;
-    // With a remainder, the last whole round joins the stream-K part, so each
-    // work-group's share is at least one tile's K slices and a tile is cut at
-    // most once ("data-parallel plus one-tile stream-K").
-    sk.rounds = tiles / sk.P;
-    if (sk.rounds > 0 && tiles % sk.P != 0) sk.rounds -= 1;
-    sk.rem_begin = sk.rounds * sk.P;
-    sk.units = (int64_t)(tiles - sk.rem_begin) * sk.ipt;
-    sk.ws = nullptr;
+    if (sk.units > 0) {
+        e = scratch_acquire(g.scratch, (size_t)streamk_scratch_bytes<T>(sk), stream,
+                            reinterpret_cast<void **>(&sk.ws));
+        if (e != hipSuccess) return e;
+    }
     // The whole rounds run as an ordinary grid over their tiles (the grid
     // kernel keeps fewer registers live than the persistent loop); the
     // persistent kernel takes the stream-K part only.
@@ -983,19 +1003,23 @@ hipError_t launch_streamk(const GemmArgs &g, int group_m, hipStream_t stream) {
         hipLaunchKernelGGL((sgemm_mfma_kernel<T, true>), dim3(sk.rounds * sk.P), dim3(T::NT), 0, stream, g,
                            tiles_m, tiles_n, group_m, sk.rounds * sk.P, none);
         e = hipGetLastError();
-        if (e != hipSuccess) return e;
     }
-    if (sk.units == 0) return hipSuccess;
-    sk.rounds = 0;
-    e = stream_workspace((size_t)2 * sk.P * T::BM * T::BN * sizeof(float), stream, reinterpret_cast<void **>(&sk.ws));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((sgemm_mfma_streamk_kernel<T, true>), dim3(sk.P), dim3(T::NT), 0, stream, g, tiles_m,
-                       tiles_n, group_m, sk);
-    e = hipGetLastError();
-    if (e != hipSuccess || sk.P < 2) return e;
-    hipLaunchKernelGGL((streamk_fixup_kernel<T::BM, T::BN>), dim3(sk.P - 1), dim3(256), 0, stream, g, tiles_m,
-                       tiles_n, group_m, sk);
-    return hipGetLastError();
+    if (sk.units > 0) {
+        sk.rounds = 0;
+        if (e == hipSuccess) {
+            hipLaunchKernelGGL((sgemm_mfma_streamk_kernel<T, true>), dim3(sk.P), dim3(T::NT), 0, stream, g,
+                               tiles_m, tiles_n, group_m, sk);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess && sk.P >= 2) {
+            hipLaunchKernelGGL((streamk_fixup_kernel<T::BM, T::BN>), dim3(sk.P - 1), dim3(256), 0, stream, g,
+                               tiles_m, tiles_n, group_m, sk);
+            e = hipGetLastError();
+        }
+        const hipError_t r = scratch_release(g.scratch, sk.ws, stream);
+        if (e == hipSuccess) e = r;
+    }
+    return e;
 }
 
 template <int LA, int LB>
@@ -1051,6 +1075,38 @@ int mfma_effective_splits(int K, int splits, int *k_per) {
     return (K + per - 1) / per;
 }
 
+namespace {
+
+// Scratch of the stream-K plan for operand layouts LA, LB (its occupancy, and
+// so its number of resident work-groups, follows the layouts' LDS use).
+template <int LA, int LB>
+hipError_t streamk_bytes(const GemmArgs &g, int64_t *bytes) {
+    StreamK sk;
+    int tiles_m = 0, tiles_n = 0;
+    const hipError_t e = streamk_plan<LargeTile<LA, LB>>(g, &sk, &tiles_m, &tiles_n);
+    if (e != hipSuccess) return e;
+    *bytes = streamk_scratch_bytes<LargeTile<LA, LB>>(sk);
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t mfma_config_scratch_bytes(const GemmArgs &g, int config, int splits, int64_t *bytes) {
+    *bytes = 0;
+    if (config == 5) {
+        const bool ta = g.trans_a != 0, tb = g.trans_b != 0;
+        if (!ta && !tb) return streamk_bytes<kKMajor, kXMajor>(g, bytes);
+        if (!ta && tb) return streamk_bytes<kKMajor, kKMajor>(g, bytes);
+        if (ta && !tb) return streamk_bytes<kXMajor, kXMajor>(g, bytes);
+        return streamk_bytes<kXMajor, kKMajor>(g, bytes);
+    }
+    if (!mfma_config_splits_ok(config)) return hipSuccess;
+    int k_per = 0;
+    const int eff = mfma_effective_splits(g.K, splits, &k_per);
+    if (eff > 1) *bytes = (int64_t)eff * g.M * g.N * (int64_t)sizeof(float);
+    return hipSuccess;
+}
+
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream) {
     SplitK sk;
@@ -1061,19 +1117,26 @@ hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int
         sk.k_per = g.K;
         return launch_kernel(g, config, vec_loads, group_m, sk, stream);
     }
-    hipError_t e = stream_workspace((size_t)sk.splits * g.M * g.N * sizeof(float), stream,
-                                    reinterpret_cast<void **>(&sk.ws));
+    hipError_t e = scratch_acquire(g.scratch, (size_t)sk.splits * g.M * g.N * sizeof(float), stream,
+                                   reinterpret_cast<void **>(&sk.ws));
     if (e != hipSuccess) return e;
     e = launch_kernel(g, config, vec_loads, group_m, sk, stream);
-    if (e != hipSuccess) return e;
-    const int64_t total = (int64_t)g.M * g.N;
-    const bool vec4 = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
-    int64_t blocks = ((vec4 ? total / 4 : total) + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
-    if (blocks < 1) blocks = 1;
-    if (vec4) hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws, sk.splits);
-    else hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws, sk.splits);
-    return hipGetLastError();
+    if (e == hipSuccess) {
+        const int64_t total = (int64_t)g.M * g.N;
+        const bool vec4 = g.N % 4 == 0 && g.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(g.C) % 16 == 0;
+        int64_t blocks = ((vec4 ? total / 4 : total) + 255) / 256;
+        if (blocks > 8192) blocks = 8192;
+        if (blocks < 1) blocks = 1;
+        if (vec4)
+            hipLaunchKernelGGL(splitk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws,
+                               sk.splits);
+        else
+            hipLaunchKernelGGL(splitk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, g, sk.ws,
+                               sk.splits);
+        e = hipGetLastError();
+    }
+    const hipError_t r = scratch_release(g.scratch, sk.ws, stream);
+    return e == hipSuccess ? r : e;
 }
 
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream) {

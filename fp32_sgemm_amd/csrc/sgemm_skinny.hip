@@ -11,12 +11,19 @@
 //
 // Work decomposition.  A work-group owns a 64-column strip of C and one of
 // `splits` contiguous ranges of K; its 4 waves split that range again.  The
-// partial strips of the splits go to the stream's workspace and a second
-// kernel adds them in split order and finishes C (with one split, the first
-// kernel finishes C itself).  A single-kernel form in which the last arriving
-// work-group of a strip adds the partials measured 3x slower: the device-wide
-// fences it needs to see the other XCDs' partials write back and invalidate
-// whole L2 caches.
+// partial strips of the splits go to the call's scratch and a second kernel
+// adds them in split order and finishes C (with one split, the first kernel
+// finishes C itself).  Measured alternatives (per call, B rotated over six
+// copies, 16 x 4096 x 4096; a plain read of B alone: 13.6 us):
+//   - this form, 8 splits: 25.9 us, its first kernel 19.8 us;
+//   - no split between work-groups (a work-group per strip of 16, 32 or 64
+//     columns with 4-16 waves splitting K, reduced in LDS, no scratch at all):
+//     30-40 us, too few bytes of B in flight per strip;
+//   - wider strips (256 or 512 columns per work-group) or more waves: 26-37 us;
+//   - one kernel in which the last work-group of a strip to finish adds the
+//     partials (a device-scope counter): 25.6-28 us with coherent partial
+//     stores and loads, 38.8 us with release/acquire fences (each fence writes
+//     back or invalidates a whole L2).
 //
 // Inner step.  For a block of 16 rows of B starting at kb, lane l (h = l/16,
 // j = l%16) loads columns 4j..4j+3 of rows kb + 4h + q, q = 0..3 (four 16-byte
@@ -237,10 +244,12 @@ bool skinny_fits(int lda, int ldb) {
     return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < limit && ((int64_t)16 * lda + SK_ROWS) * 4 < limit;
 }
 
-hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
+namespace {
+
+// The K split: about two work-groups per compute unit, every split at least
+// 256 rows long.
+void skinny_split(const GemmArgs &g, int *splits_out, int *split_rows_out) {
     const int strips = (g.N + SK_BN - 1) / SK_BN;
-    // Aim for about two work-groups per compute unit; keep every split at
-    // least 256 rows long.
     const int want = (512 + strips - 1) / strips;
     const int max_splits = (g.K + 255) / 256;
     int splits = want < max_splits ? want : max_splits;
@@ -248,27 +257,45 @@ hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) 
     int split_rows = (g.K + splits - 1) / splits;
     split_rows = (split_rows + SK_ROWS - 1) / SK_ROWS * SK_ROWS;
     splits = (g.K + split_rows - 1) / split_rows;
+    *splits_out = splits;
+    *split_rows_out = splits > 1 ? split_rows : g.K;
+}
 
+}  // namespace
+
+int64_t skinny_scratch_bytes(const GemmArgs &g) {
+    int splits = 1, split_rows = 0;
+    skinny_split(g, &splits, &split_rows);
+    return splits > 1 ? (int64_t)splits * g.M * g.N * (int64_t)sizeof(float) : 0;
+}
+
+hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
+    const int strips = (g.N + SK_BN - 1) / SK_BN;
     SkinnyArgs sa;
     sa.g = g;
     sa.ws = nullptr;
-    sa.splits = splits;
-    sa.split_rows = splits > 1 ? split_rows : g.K;
+    skinny_split(g, &sa.splits, &sa.split_rows);
+    const int splits = sa.splits;
     if (splits > 1) {
-        hipError_t e = stream_workspace((size_t)splits * g.M * g.N * sizeof(float), stream,
-                                        reinterpret_cast<void **>(&sa.ws));
+        hipError_t e = scratch_acquire(g.scratch, (size_t)skinny_scratch_bytes(g), stream,
+                                       reinterpret_cast<void **>(&sa.ws));
         if (e != hipSuccess) return e;
     }
     const dim3 grid(strips * splits);
     if (vec_loads) hipLaunchKernelGGL(sgemm_skinny_kernel<true>, grid, dim3(SK_NT), 0, stream, sa, strips);
     else hipLaunchKernelGGL(sgemm_skinny_kernel<false>, grid, dim3(SK_NT), 0, stream, sa, strips);
     hipError_t e = hipGetLastError();
-    if (splits > 1 && e == hipSuccess) {
-        const int64_t total = (int64_t)g.M * g.N;
-        int64_t blocks = (total + 255) / 256;
-        if (blocks > 4096) blocks = 4096;
-        hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, sa.ws, splits);
-        e = hipGetLastError();
+    if (splits > 1) {
+        if (e == hipSuccess) {
+            const int64_t total = (int64_t)g.M * g.N;
+            int64_t blocks = (total + 255) / 256;
+            if (blocks > 4096) blocks = 4096;
+            hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, sa.ws,
+                               splits);
+            e = hipGetLastError();
+        }
+        const hipError_t r = scratch_release(g.scratch, sa.ws, stream);
+        if (e == hipSuccess) e = r;
     }
     return e;
 }

@@ -29,7 +29,7 @@
  * (B stored N x K) and trans_a == 0, 16-byte aligned operands, row strides that
  * are multiples of 8 elements and K a multiple of 64, A and B are read in
  * place.  Otherwise the operands that do not meet this are first copied into a
- * K-major, zero-padded form in the library's per-(device, stream) workspace
+ * K-major, zero-padded form in the call's scratch, allocated in stream order
  * (see sgemm_f32.h; (M or N) * K rounded up to 64 elements * 2 bytes each),
  * which costs one extra pass over them.
  *

@@ -34,14 +34,16 @@
  *   - The functions hold no per-call state and may be called from several host
  *     threads at once.
  *   - Device memory: none unless the reduction over K is split across
- *     work-groups (the M <= 16 kernel, and MFMA plans with splits > 1 from the
- *     tuning table or sgemm_f32_ex_config).  Those keep one workspace per
- *     (device, stream), allocated with hipMalloc on the first such call on
- *     that stream (at least 4 MiB, at most splits * M * N floats, 1 GiB cap for
- *     MFMA plans).  A call that needs more allocates a block at least twice as
- *     large; the replaced block is kept, not freed (work queued earlier may
- *     still use it), so growing never waits for the stream.  All of it is held
- *     until the process ends.  Calls on different streams never share it.
+ *     work-groups (the M <= 16 kernel, MFMA plans with splits > 1 from the
+ *     tuning table or sgemm_f32_ex_config, and the stream-K configuration).
+ *     Such a call allocates its scratch in stream order: hipMallocFromPoolAsync
+ *     on `stream` before its kernels and hipFreeAsync on `stream` after them,
+ *     from a memory pool the library creates on the first such call on a
+ *     device (at most splits * M * N floats, 1 GiB cap for MFMA plans; the
+ *     pool keeps up to 1 GiB of freed memory for later calls and lives until
+ *     the process ends).  The scratch is valid only for the call's own
+ *     kernels, so calls on different streams never share it and both
+ *     operations can be recorded by graph capture.
  *
  * Special cases:
  *   - M == 0 or N == 0: nothing is done, returns 0.
@@ -222,7 +224,7 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * (wave quantization, "Writing a Fast Matmul in CUDA, Step by Step", section
  * "Size effects"); tiles shared by several work-groups are summed in K order
  * by a second kernel.  It takes no split count (splits must be 1) and uses
- * the stream's workspace (2 * 128 * 128 floats per resident work-group, 64 MiB
+ * the call's scratch (2 * 128 * 128 floats per resident work-group, 64 MiB
  * on MI355X) when tiles are shared.
  * Configuration 7 computes 256 x 256 tiles, one work-group per compute unit,
  * with the operands copied from memory straight into LDS.  It needs M, N and K

@@ -128,7 +128,7 @@ def test_split_odd_n_scalar_reduction(sg):
 
 def test_split_plans_on_two_streams(sg):
     """Two split products in flight on two streams: each stream's partials
-    live in its own workspace."""
+    live in that call's own scratch."""
     M, N, K = 512, 512, 4096
     A1, B1, _ = _inputs(M, N, K, "uniform", 33)
     A2, B2, _ = _inputs(M, N, K, "uniform", 34)

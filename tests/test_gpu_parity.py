@@ -218,11 +218,10 @@ def test_skinny_concurrent_streams(sg):
     assert ok, info
 
 
-def test_workspace_growth_and_host_threads(sg):
-    """Split plans need the stream's workspace: a larger product on the same
-    stream grows it (the replaced block stays valid for work already queued),
-    and host threads calling on their own streams at the same time each get
-    their own workspace."""
+def test_scratch_sizes_and_host_threads(sg):
+    """Split plans take their scratch in stream order: products of different
+    sizes in a row on one stream each get a block of their own size, and host
+    threads calling on their own streams at the same time never share one."""
     import threading
     cases = [(256, 256, 4096, 41), (512, 512, 8192, 42), (256, 256, 4096, 43)]
     data = []
@@ -234,7 +233,7 @@ def test_workspace_growth_and_host_threads(sg):
     torch.cuda.synchronize()
     # configuration 4 (64x64, two slices in flight) with 8 K splits: 8*M*N floats of partials
     for M, N, K, _, _, dA, dB, dC in data:
-        say(f"[ws_growth] {M}x{N}x{K} splits 8")
+        say(f"[scratch_sizes] {M}x{N}x{K} splits 8")
         assert sg.sgemm_f32_ex_config(4, 8, 8, 0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
                                       dC.data_ptr(), N, s.cuda_stream) == 0
     torch.cuda.synchronize()
@@ -258,7 +257,7 @@ def test_workspace_growth_and_host_threads(sg):
         if not ok:
             errors.append(info)
 
-    say("[ws_threads] three host threads, three streams")
+    say("[scratch_threads] three host threads, three streams")
     threads = [threading.Thread(target=worker, args=(i,)) for i in range(3)]
     for t in threads:
         t.start()
@@ -401,3 +400,40 @@ def test_c_leading_dimension_past_32bit_offsets(sg):
     assert ok, info
     del Cbuf
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("case", ["skinny", "splitk"])
+def test_split_plans_in_a_captured_graph(sg, case):
+    """A call whose plan allocates stream-ordered scratch (the M <= 16 split,
+    a tuned split-K plan), recorded into a graph: every replay, with eager
+    work and synchronisation between replays, matches the eager result bit
+    for bit."""
+    M, N, K = (16, 4096, 4096) if case == "skinny" else (512, 512, 8192)
+    say(f"[graph] {case} {M}x{N}x{K}")
+    A, B, _ = _inputs(M, N, K, "uniform", 80, c0=False)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    eager = torch.empty(M, N, device="cuda:0")
+    out = torch.empty(M, N, device="cuda:0")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    assert sg.sgemm_f32(M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, eager.data_ptr(), N,
+                        s.cuda_stream) == 0
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        st = sg.sgemm_f32(M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0, out.data_ptr(), N,
+                          s.cuda_stream)
+    assert st == 0
+    want = eager.cpu().numpy()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"replay {rep}"
+        junk = torch.randn(1024, 1024, device="cuda:0") @ torch.randn(1024, 1024, device="cuda:0")
+        torch.cuda.synchronize()
+        del junk
+    ok, info = check_full(want, A, B, 1.0, 0.0, None)
+    assert ok, info
