@@ -45,13 +45,15 @@ ERR_NOT_APPLICABLE = 21
 ERR_TOO_LARGE = 22
 ERR_TRANS = 23
 ERR_CONFIG = 24
+ERR_SCRATCH = 25
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 GEMM16_BF16 = 1
 GEMM16_F16 = 2
 GEMM16_ERR_ALIGN = 21
 GEMM16_ERR_TYPE = 25
 
-EXPORTED = ("sgemm_f32", "sgemm_f32_variant", "sgemm_f32_select",
+EXPORTED = ("sgemm_f32", "sgemm_f32_noalloc", "sgemm_f32_variant", "sgemm_f32_select",
             "sgemm_f32_ex", "sgemm_f32_ex_variant", "sgemm_f32_ex_select",
             "sgemm_f32_ex_plan", "sgemm_f32_ex_config", "sgemm_f32_config_name",
             "sgemm_f32_tuning_table_present", "sgemm_f32_variant_name", "sgemm_f32_version",
@@ -74,6 +76,8 @@ def _load_library():
     gemm_args = [i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_f32.argtypes = gemm_args
     lib.sgemm_f32.restype = i
+    lib.sgemm_f32_noalloc.argtypes = gemm_args
+    lib.sgemm_f32_noalloc.restype = i
     lib.sgemm_f32_variant.argtypes = [i] + gemm_args
     lib.sgemm_f32_variant.restype = i
     lib.sgemm_f32_select.argtypes = [i, i, i, f, p, i, p, i]
@@ -120,6 +124,14 @@ def sgemm_f32(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ld
     """The C entry point: raw device pointers and a hipStream_t as integers."""
     _ints(M, N, K, lda, ldb, ldc)
     return _lib.sgemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def sgemm_f32_noalloc(M: int, N: int, K: int, alpha: float, A: int, lda: int, B: int, ldb: int,
+                      beta: float, C: int, ldc: int, stream: int = 0) -> int:
+    """sgemm_f32 with no device allocation: split plans use the library's fixed
+    per-device scratch region (calls that overlap on one device race on it)."""
+    _ints(M, N, K, lda, ldb, ldc)
+    return _lib.sgemm_f32_noalloc(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
 def sgemm_f32_variant(variant: int, M: int, N: int, K: int, alpha: float, A: int, lda: int,

@@ -92,6 +92,13 @@ hipError_t scratch_release(const Scratch &s, void *p, hipStream_t stream);
 int64_t skinny_scratch_bytes(const GemmArgs &g);
 hipError_t mfma_config_scratch_bytes(const GemmArgs &g, int config, int splits, int64_t *bytes);
 
+// sgemm_f32's automatic GEMM with the call's scratch taken from `scratch`
+// (sgemm_api.hip): validation, special cases and plan as sgemm_f32; with a
+// fixed region, a plan that needs more scratch than it holds returns
+// SGEMM_F32_ERR_SCRATCH before anything is enqueued.
+int run_auto_with_scratch(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                          float beta, float *C, int ldc, hipStream_t stream, const Scratch &scratch);
+
 // Tile counts that each launcher's grid uses (host side, for the size check).
 int64_t mfma_large_grid(int M, int N);
 int64_t mfma_small_grid(int M, int N);

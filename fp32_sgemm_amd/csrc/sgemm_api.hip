@@ -299,14 +299,28 @@ GemmArgs make_args(int ta, int tb, int M, int N, int K, float alpha, const float
     return g;
 }
 
+// Scratch bytes of a plan (0 for plans without a split), or -1 when the
+// occupancy query of the stream-K plan fails.
+int64_t plan_scratch_bytes(const Plan &p, const GemmArgs &g) {
+    if (p.variant == SGEMM_F32_SKINNY) return sgemm::skinny_scratch_bytes(g);
+    if (p.variant == SGEMM_F32_VALU) return 0;
+    const int config = p.variant == SGEMM_F32_MFMA_TUNED ? p.config : (p.variant == SGEMM_F32_MFMA_SMALL ? 1 : 0);
+    const int splits = p.variant == SGEMM_F32_MFMA_TUNED ? p.splits : 1;
+    int64_t bytes = 0;
+    if (sgemm::mfma_config_scratch_bytes(g, config, splits, &bytes) != hipSuccess) return -1;
+    return bytes;
+}
+
 int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda,
-        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream) {
+        const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
+        const sgemm::Scratch &scratch = sgemm::Scratch{}) {
     if (variant < 0 || variant >= SGEMM_F32_NUM_VARIANTS) return SGEMM_F32_ERR_VARIANT;
     const int bad = validate(ta, tb, M, N, K, alpha, A, lda, B, ldb, C, ldc);
     if (bad) return bad;
     if (M == 0 || N == 0) return 0;
 
-    const GemmArgs g = make_args(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    GemmArgs g = make_args(ta, tb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc);
+    g.scratch = scratch;
     if (alpha == 0.f || K == 0) {
         if ((int64_t)M * N > (int64_t)1 << 62) return SGEMM_F32_ERR_TOO_LARGE;
         return to_status(sgemm::launch_scale_c(g, stream));
@@ -325,6 +339,12 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
     // offsets of configurations 7-9 keeps the register-staged kernels.
     if ((p.config == 7 || p.config == 8) && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
     if (p.config == 9 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, 1};
+    if (scratch.fixed != nullptr) {
+        // A fixed scratch region: refuse, before anything is enqueued, a plan
+        // that needs more of it than there is.
+        const int64_t need = plan_scratch_bytes(p, g);
+        if (need < 0 || need > (int64_t)scratch.fixed_bytes) return SGEMM_F32_ERR_SCRATCH;
+    }
     switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
@@ -353,6 +373,15 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
 bool flags_ok(int ta, int tb) { return (ta == 0 || ta == 1) && (tb == 0 || tb == 1); }
 
 }  // namespace
+
+namespace sgemm {
+
+int run_auto_with_scratch(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
+                          float beta, float *C, int ldc, hipStream_t stream, const Scratch &scratch) {
+    return run(SGEMM_F32_AUTO, 0, 0, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, scratch);
+}
+
+}  // namespace sgemm
 
 extern "C" {
 

@@ -33,7 +33,8 @@
  *     returns without waiting for it.  No host or device synchronisation.
  *   - The functions hold no per-call state and may be called from several host
  *     threads at once.
- *   - Device memory: none unless the reduction over K is split across
+ *   - Device memory (see sgemm_f32_noalloc for the form that allocates
+ *     nothing): none unless the reduction over K is split across
  *     work-groups (the M <= 16 kernel, MFMA plans with splits > 1 from the
  *     tuning table or sgemm_f32_ex_config, and the stream-K configuration).
  *     Such a call allocates its scratch in stream order: hipMallocFromPoolAsync
@@ -63,6 +64,8 @@
  *     SGEMM_F32_ERR_TRANS    (the _ex functions) a transpose flag other than 0 or 1
  *     SGEMM_F32_ERR_CONFIG   (sgemm_f32_ex_config, sgemm_f32_ex_plan) a configuration,
  *                            grouping or split count out of range, or a NULL output
+ *     SGEMM_F32_ERR_SCRATCH  (sgemm_f32_noalloc) the plan needs more scratch than
+ *                            the fixed region holds; nothing was enqueued
  *     < 0                    -(hipError_t) reported by the HIP runtime for the
  *                            launch; the contents of C are then unspecified
  * Nothing is printed and no exception crosses the interface.
@@ -81,6 +84,10 @@ extern "C" {
 #define SGEMM_F32_ERR_TOO_LARGE 22
 #define SGEMM_F32_ERR_TRANS 23
 #define SGEMM_F32_ERR_CONFIG 24
+#define SGEMM_F32_ERR_SCRATCH 25
+
+/* Size of the fixed scratch region that sgemm_f32_noalloc uses on each device. */
+#define SGEMM_F32_NOALLOC_SCRATCH_BYTES (64u << 20)
 
 /* Kernel variants that sgemm_f32_variant can force. */
 enum sgemm_f32_variant_id {
@@ -126,6 +133,30 @@ enum sgemm_f32_config_id {
 int sgemm_f32(int M, int N, int K, float alpha,
               const float *A, int lda, const float *B, int ldb,
               float beta, float *C, int ldc, hipStream_t stream);
+
+/*
+ * sgemm_f32 for callers that cannot allocate device memory: code under graph
+ * capture that must not record allocations, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments, validation, special cases, kernel
+ * plan and results (bit for bit) as sgemm_f32.  It calls no hipMalloc,
+ * hipMallocAsync or hipFree: the plans that need scratch (the M <= 16 split,
+ * tuned split-K plans) use a fixed region of
+ * SGEMM_F32_NOALLOC_SCRATCH_BYTES (64 MiB) in the library's device memory,
+ * one per device, present from the library's loading on that device until
+ * the process ends.  The first call on a device looks up that region's
+ * address (hipGetSymbolAddress, no allocation).
+ *
+ * The region is shared by every sgemm_f32_noalloc call on the device and keeps
+ * the last call's contents (nothing in it needs to start at zero): calls that
+ * overlap in time on one device (on different streams, or from several host
+ * threads without ordering) race on it and give undefined results.  Order
+ * them, for example by issuing them on one stream.  A plan that needs more
+ * than the region holds returns SGEMM_F32_ERR_SCRATCH without enqueueing
+ * anything; C is then unchanged.
+ */
+int sgemm_f32_noalloc(int M, int N, int K, float alpha,
+                      const float *A, int lda, const float *B, int ldb,
+                      float beta, float *C, int ldc, hipStream_t stream);
 
 /*
  * The same operation computed by one forced kernel variant, for comparisons
