@@ -66,12 +66,12 @@ class SgemmError(RuntimeError):
         self.status = status
 
 
-def _load_library():
-    if not os.path.exists(LIB_PATH):
+def _load_library(path: str = LIB_PATH):
+    if not os.path.exists(path):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it first "
+            f"{path} is missing: build it first "
             "(python -c 'import __graft_entry__ as g; g.build()')")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
     gemm_args = [i, i, i, f, p, i, p, i, f, p, i, p]
     lib.sgemm_f32.argtypes = gemm_args
@@ -107,6 +107,13 @@ def _load_library():
 
 
 _lib = _load_library()
+
+
+def lds_poison_library():
+    """The LDS-poisoning debug copy of the library (its kernels fill their LDS
+    with NaN before the first load), bound with the same C signatures; for the
+    tests that check that no LDS stage is read before it is filled."""
+    return _load_library(_build.POISON_LIB_PATH)
 
 _INT_MIN, _INT_MAX = -(1 << 31), (1 << 31) - 1
 

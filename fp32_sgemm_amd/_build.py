@@ -17,6 +17,10 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_DIR = os.path.join(HERE, "_lib")
 LIB_PATH = os.path.join(LIB_DIR, "libsgemm_f32.so")
+# A debug copy of the same library whose kernels fill their LDS with NaN before
+# their first load (SGEMM_LDS_POISON): the tests run it to show that no stage is
+# read before the loads that fill it have landed.  Never loaded by the package.
+POISON_LIB_PATH = os.path.join(LIB_DIR, "libsgemm_f32_lds_poison.so")
 OFFLOAD_ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -34,8 +38,8 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str, obj: str, remarks: bool) -> str:
-    cmd = [HIPCC, *COMMON_FLAGS, "-c", src, "-o", obj]
+def _compile(src: str, obj: str, remarks: bool, extra=()) -> str:
+    cmd = [HIPCC, *COMMON_FLAGS, *extra, "-c", src, "-o", obj]
     if remarks:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     p = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,30 +50,36 @@ def _compile(src: str, obj: str, remarks: bool) -> str:
     return "\n".join(keep)
 
 
-def build_library(jobs: int = 8, remarks: bool = True) -> str:
-    """Compile every csrc/*.hip and link libsgemm_f32.so; returns its path."""
+def build_library(jobs: int = 8, remarks: bool = True, poison: bool = False) -> str:
+    """Compile every csrc/*.hip and link libsgemm_f32.so (with ``poison``, the
+    LDS-poisoning debug copy instead); returns its path."""
     os.makedirs(LIB_DIR, exist_ok=True)
+    lib_path = POISON_LIB_PATH if poison else LIB_PATH
+    tag = ".poison" if poison else ""
+    extra = ("-DSGEMM_LDS_POISON=1",) if poison else ()
     objs, reports = [], []
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         futs = {}
         for src in sources():
-            obj = os.path.join(LIB_DIR, os.path.basename(src)[:-4] + ".o")
+            obj = os.path.join(LIB_DIR, os.path.basename(src)[:-4] + tag + ".o")
             objs.append(obj)
-            futs[ex.submit(_compile, src, obj, remarks)] = src
+            futs[ex.submit(_compile, src, obj, remarks and not poison, extra)] = src
         for f in cf.as_completed(futs):
             reports.append(f"== {os.path.basename(futs[f])}\n{f.result()}")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={OFFLOAD_ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"link failed:\n{p.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     for o in objs:
         os.remove(o)
-    with open(os.path.join(LIB_DIR, "resource_usage.txt"), "w") as f:
-        f.write("\n".join(sorted(reports)) + "\n")
-    return LIB_PATH
+    if not poison:
+        with open(os.path.join(LIB_DIR, "resource_usage.txt"), "w") as f:
+            f.write("\n".join(sorted(reports)) + "\n")
+    return lib_path
 
 
 if __name__ == "__main__":
     print(build_library())
+    print(build_library(poison=True))

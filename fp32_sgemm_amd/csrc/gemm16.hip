@@ -103,6 +103,7 @@ template <bool F16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2))) void gemm16_kernel(Args16 g, int tiles_m,
                                                                                           int tiles_n) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[2 * STAGE];
+    poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, 8, tm, tn);
     const int m0 = tm * BM, n0 = tn * BN;
@@ -343,6 +344,7 @@ template <bool F16>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
     Args16 g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NST * dl::STAGE];
+    poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
     const int m0 = tm * big::BM, n0 = tn * big::BN;

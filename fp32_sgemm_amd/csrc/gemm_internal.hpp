@@ -99,6 +99,26 @@ hipError_t mfma_config_scratch_bytes(const GemmArgs &g, int config, int splits, 
 int run_auto_with_scratch(int M, int N, int K, float alpha, const float *A, int lda, const float *B, int ldb,
                           float beta, float *C, int ldc, hipStream_t stream, const Scratch &scratch);
 
+// LDS poisoning, for a debug copy of the library only (compiled with
+// -DSGEMM_LDS_POISON=1; the product is built without it): a kernel calls
+// poison_lds on its LDS array first thing, which fills it with quiet NaNs and
+// waits for every wave.  A stage that is read before the loads that fill it
+// have landed, or a part of LDS that is read but never written, then turns
+// the result into NaN instead of silently reading stale data or the zeros of a
+// fresh work-group.
+#ifndef SGEMM_LDS_POISON
+#define SGEMM_LDS_POISON 0
+#endif
+template <int BYTES>
+__device__ __forceinline__ void poison_lds(void *lds) {
+    if constexpr (SGEMM_LDS_POISON != 0) {
+        static_assert(BYTES % 4 == 0, "LDS size");
+        float *p = static_cast<float *>(lds);
+        for (int i = threadIdx.x; i < BYTES / 4; i += blockDim.x) p[i] = __builtin_nanf("");
+        __syncthreads();
+    }
+}
+
 // Tile counts that each launcher's grid uses (host side, for the size check).
 int64_t mfma_large_grid(int M, int N);
 int64_t mfma_small_grid(int M, int N);

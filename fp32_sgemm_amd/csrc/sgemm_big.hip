@@ -374,6 +374,7 @@ template <int LA, int LB, int TS>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<TS>, kWavesPerEu<TS>)))
 void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * Geo<TS>::STAGE];
+    poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TS, n0 = tn * TS;

@@ -704,6 +704,7 @@ template <class T, bool VEC>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_kernel(
     GemmArgs g, int tiles_m, int tiles_n, int group_m, int ntiles, SplitK sk) {
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
+    poison_lds<sizeof(smem)>(smem);
 
     int bid = blockIdx.x;
     float *Cbase = g.C;
@@ -768,6 +769,7 @@ template <class T, bool VEC>
 __global__ __launch_bounds__(T::NT) __attribute__((amdgpu_waves_per_eu(2))) void sgemm_mfma_streamk_kernel(
     GemmArgs g, int tiles_m, int tiles_n, int group_m, StreamK sk) {
     __shared__ __attribute__((aligned(16))) float smem[T::SMEM];
+    poison_lds<sizeof(smem)>(smem);
     // Work-groups resident on one XCD take consecutive positions, so they
     // work on neighbouring tiles and share their panels in that XCD's L2.
     const int w = xcd_position(blockIdx.x, sk.P);

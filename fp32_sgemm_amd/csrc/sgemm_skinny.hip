@@ -135,6 +135,7 @@ __device__ __forceinline__ void consume_batch(const Batch &bt, f32x4v (&acc)[4])
 template <bool VEC>
 __global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(SkinnyArgs sa, int strips) {
     __shared__ float red[SK_NW][16 * SK_BN];
+    poison_lds<sizeof(red)>(red);
     const GemmArgs &g = sa.g;
     // Work-group -> (split, strip); consecutive strips stay on one XCD.
     int split, strip;

@@ -66,6 +66,7 @@ __device__ __forceinline__ void vstore_slice(float *stage, int tid, const float4
 template <bool VEC>
 __global__ __launch_bounds__(VNT) void sgemm_valu_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     __shared__ __attribute__((aligned(16))) float smem[2 * VSTAGE];
+    poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * VBM, n0 = tn * VBN;

@@ -52,6 +52,34 @@ def test_library_exports_every_declared_symbol(sg):
     assert set(sg.EXPORTED) == set(_declared_functions())
 
 
+def test_lds_poison_copy_exports_the_same_interface(sg):
+    """The debug copy that the LDS-poisoning GPU tests run is built from the
+    same sources and exports every declared function too."""
+    from fp32_sgemm_amd import _build
+    out = subprocess.run(["nm", "-D", "--defined-only", _build.POISON_LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, flags=re.M))
+    assert set(_declared_functions()) <= exported
+
+
+@pytest.mark.parametrize("src,kernels", [("sgemm_big.hip", 12), ("gemm16.hip", 4)])
+def test_lds_poison_flag_fills_lds_with_nan(tmp_path, src, kernels):
+    """The debug flag really plants the NaN fill: the device code of the
+    kernels built with SGEMM_LDS_POISON holds the quiet-NaN constant once per
+    LDS-using kernel instance (3 tile sizes x 4 operand forms of the
+    direct-to-LDS kernel; 2 kernels x 2 formats of the 16-bit GEMM), and the
+    product build holds none."""
+    from fp32_sgemm_amd import _build
+    counts = []
+    for extra in (["-DSGEMM_LDS_POISON=1"], []):
+        out = tmp_path / f"{src}{len(extra)}.s"
+        cmd = [_build.HIPCC, *_build.COMMON_FLAGS, *extra, "--cuda-device-only", "-S", "-o", str(out),
+               os.path.join(_build.CSRC, src)]
+        subprocess.run(cmd, check=True, capture_output=True)
+        counts.append(out.read_text().count("0x7fc00000"))
+    assert counts == [kernels, 0], counts
+
+
 def test_binding_mirrors_the_c_names(sg):
     for name in _declared_functions():
         assert callable(getattr(sg, name)), name
