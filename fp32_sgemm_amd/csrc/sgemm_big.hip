@@ -1,7 +1,8 @@
 // FP32 GEMM on 256 x 256 tiles, one per CU at a time, for grids whose rounds of
 // 256 tiles lie almost entirely inside C; the same kernel on 128 x 128 tiles
 // (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) and on
-// 64 x 64 tiles (4 waves of 32 x 32, four work-groups per CU) serves whole
+// 64 x 64 tiles (4 waves of 32 x 32, four work-groups per CU; grids of at most
+// one tile per CU run 8 waves per tile, two groups splitting K) serves whole
 // grids of those tiles.  The description below is that of the 256 x 256 form.
 //
 // One work-group per CU, 4 waves of 128 x 128 (4 x 4 blocks of 32x32x2 MFMA,
@@ -45,6 +46,7 @@
 // with that check, so the other iterations keep constant offsets.  Tiles that
 // cross M or N store through a buffer resource over the valid part of C, whose
 // extent drops rows past M and whose out-of-range offsets drop columns past N.
+#include <atomic>
 #include <cstdint>
 #include <type_traits>
 
@@ -204,22 +206,39 @@ __device__ __forceinline__ void read_piece(const unsigned char *panel, const Fra
 template <int L, int TS>
 constexpr int pieces() { return L == kKRows ? Geo<TS>::BLK : 4 * Geo<TS>::BLK; }
 
-// One TS x TS tile at (m0, n0).  EDGE: the tile crosses M or N.
-template <int LA, int LB, bool EDGE, int TS>
-__device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem) {
+// One TS x TS tile at (m0, n0).  EDGE: the tile crosses M or N.  KG: groups
+// of 4 waves that split the tile's K slices between them (KG = 2: waves 4-7
+// take the second half of the slices, in LDS stages of their own; both groups
+// run the same number of iterations, so every s_barrier is met by all eight
+// waves, the group whose range runs past K loading zeros).  At the end the
+// second group hands its sums to the first through LDS, which adds them to its
+// own (its partial first, so the result does not depend on timing) and writes
+// C.  With one work-group per compute unit, the second group doubles the
+// MFMA work between two barriers and gives each SIMD a second wave to issue.
+// Measured on MI355X (per-launch medians, one group -> two): 1024^3 21.16 ->
+// 20.92 µs, 1024 x 1024 x 4096 68.6 -> 66.1 µs; eight LDS stages per group
+// instead of four (seven slices in flight) gained nothing on either.
+template <int LA, int LB, bool EDGE, int TS, int KG = 1>
+__device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem_all) {
     using G = Geo<TS>;
     constexpr int BM = G::BM, BN = G::BN, WT = G::WT, BLK = G::BLK, PANEL = G::PANEL, STAGE = G::STAGE;
     constexpr int LPO = G::LPO, LPS = G::LPS;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, wave8 = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = wave8 & 3, group = KG > 1 ? wave8 >> 2 : 0;
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
+    unsigned char *smem = smem_all + group * (NST * STAGE);
+    // This group's slices: [ks0, ks0 + nk) of the nk_all slices of K.
+    const int nk_all = (g.K + BK - 1) / BK;
+    const int nk = (nk_all + KG - 1) / KG;
+    const int ks0 = group * nk;
 
     const Operand<LA, EDGE, TS> opa(g.A, g.lda, m0, g.M, g.K, wave, lane);
     const Operand<LB, EDGE, TS> opb(g.B, g.ldb, n0, g.N, g.K, wave, lane);
     auto issue_one = [&](auto ck, int slice, int stage, int i) {
         constexpr bool CK = decltype(ck)::value;
-        const int k0 = slice * BK;
+        const int k0 = (ks0 + slice) * BK;
         unsigned char *st = smem + stage * STAGE;
         if (i < LPO) lds_dma16(opa.slice(k0), st + opa.dst[i], opa.template offset<CK>(i, k0));
         else lds_dma16(opb.slice(k0), st + PANEL + opb.dst[i - LPO], opb.template offset<CK>(i - LPO, k0));
@@ -246,7 +265,6 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
         acc[ib][jb] = __builtin_amdgcn_mfma_f32_32x32x2f32(f.a[ib][e], f.b[jb][e], acc[ib][jb], 0, 0, 0);
     };
 
-    const int nk = (g.K + BK - 1) / BK;
     // Slices past the end are loaded again as the last one, into stages that
     // are never read, so every slice issues the same number of loads.
 #pragma unroll
@@ -305,9 +323,11 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
             }
         }
     };
-    // Iteration t loads slice min(t + 3, nk - 1): with a K tail, the
-    // iterations from nk - 4 on load the partial last slice and check k.
-    const int t_split = g.K % BK != 0 ? max(0, nk - NST) : nk;
+    // Iteration t loads slice min(t + 3, nk - 1): the iterations that load a
+    // slice reaching past K (the partial last one, or for the second group
+    // slices wholly past it) check k, from local slice c - 3 on.
+    const int c = (g.K % BK != 0 ? nk_all - 1 : nk_all) - ks0;
+    const int t_split = c <= nk - 1 ? max(0, c - (NST - 1)) : nk;
     slices(std::false_type{}, 0, t_split);
     slices(std::true_type{}, t_split, nk);
 #pragma unroll
@@ -315,6 +335,32 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     // Every load issued (including the repeated last slice) has landed before
     // the work-group can end and its LDS be given to another.
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (KG > 1) {
+        // Every wave is done with its stages; the second group's sums go
+        // through LDS, lane-fastest, to the wave of the first group that owns
+        // the same part of the tile.
+        static_assert(KG == 2, "two groups");
+        constexpr int NACC = BLK * BLK * 16;
+        static_assert(4 * NACC * 64 * 4 <= NST * STAGE, "exchange fits one group's stages");
+        float *xch = reinterpret_cast<float *>(smem_all) + wave * NACC * 64 + lane;
+        __syncthreads();
+        if (group == 1) {
+#pragma unroll
+            for (int ib = 0; ib < BLK; ++ib)
+#pragma unroll
+                for (int jb = 0; jb < BLK; ++jb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) xch[((ib * BLK + jb) * 16 + r) * 64] = acc[ib][jb][r];
+        }
+        __syncthreads();
+        if (group == 1) return;
+#pragma unroll
+        for (int ib = 0; ib < BLK; ++ib)
+#pragma unroll
+            for (int jb = 0; jb < BLK; ++jb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[ib][jb][r] += xch[((ib * BLK + jb) * 16 + r) * 64];
+    }
 
     // Epilogue in BLK passes of one block row (BLK blocks, 16 BLK values per
     // lane): the C reads of a pass are issued together before its stores
@@ -365,28 +411,63 @@ __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsi
     }
 }
 
+// Compute units of the current device (cached per device).
+hipError_t compute_units(int *out) {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64) {
+        const int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) {
+            *out = c;
+            return hipSuccess;
+        }
+    }
+    int cus = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < 64 && cus > 0) cache[dev].store(cus, std::memory_order_relaxed);
+    *out = cus;
+    return hipSuccess;
+}
+
 // Work-groups per CU: TS 256 one (256 accumulators per lane), TS 128 two,
 // TS 64 four (32 KB of LDS each).
 template <int TS>
 constexpr int kWavesPerEu = TS == 256 ? 1 : TS == 128 ? 2 : 4;
 
-template <int LA, int LB, int TS>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<TS>, kWavesPerEu<TS>)))
+template <int LA, int LB, int TS, int KG>
+__global__ __launch_bounds__(NT * KG) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<TS>, kWavesPerEu<TS>)))
 void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[NST * Geo<TS>::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[KG * NST * Geo<TS>::STAGE];
+    static_assert(sizeof(smem) <= 160 * 1024, "LDS");
     poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, group_m, tm, tn);
     const int m0 = tm * TS, n0 = tn * TS;
-    if (m0 + TS > g.M || n0 + TS > g.N) big_tile<LA, LB, true, TS>(g, m0, n0, smem);
-    else big_tile<LA, LB, false, TS>(g, m0, n0, smem);
+    if (m0 + TS > g.M || n0 + TS > g.N) big_tile<LA, LB, true, TS, KG>(g, m0, n0, smem);
+    else big_tile<LA, LB, false, TS, KG>(g, m0, n0, smem);
 }
 
+// Two groups of waves per 64 x 64 tile (KG = 2) when the grid has at most one
+// tile per compute unit of the device.
 template <int LA, int LB, int TS>
 hipError_t launch(const GemmArgs &g, int group_m, hipStream_t stream) {
     const int tiles_m = (g.M + TS - 1) / TS, tiles_n = (g.N + TS - 1) / TS;
-    hipLaunchKernelGGL((sgemm_big_kernel<LA, LB, TS>), dim3(tiles_m * tiles_n), dim3(NT), 0, stream, g, tiles_m,
-                       tiles_n, group_m);
+    const int tiles = tiles_m * tiles_n;
+    if constexpr (TS == 64) {
+        int cus = 0;
+        const hipError_t e = compute_units(&cus);
+        if (e != hipSuccess) return e;
+        if (tiles <= cus) {
+            hipLaunchKernelGGL((sgemm_big_kernel<LA, LB, TS, 2>), dim3(tiles), dim3(2 * NT), 0, stream, g, tiles_m,
+                               tiles_n, group_m);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((sgemm_big_kernel<LA, LB, TS, 1>), dim3(tiles), dim3(NT), 0, stream, g, tiles_m, tiles_n,
+                       group_m);
     return hipGetLastError();
 }
 
