@@ -37,6 +37,8 @@ namespace sgemm {
 namespace {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -85,7 +87,8 @@ struct Args16 {
     int M, N, K;            // K: multiple of BK (packed or checked)
     float alpha, beta;
     const uint16_t *A;      // M x K, K-major, row stride lda (multiple of 8)
-    const uint16_t *B;      // N x K, K-major, row stride ldb
+    const uint16_t *B;      // N x K, K-major, row stride ldb; or, for the kernel
+                            // that reads B as given, K x N, N-major, row stride ldb
     float *C;
     int64_t lda, ldb, ldc;
 };
@@ -321,6 +324,25 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // order), and for its own LDS reads, then joins an s_barrier; past it every
 // wave's part of slice t is in LDS and every wave is done with the stage that
 // slice t+3 is loaded into.
+//
+// B as given (K x N, rows of n; BXM): its slice is kept as it lies in memory,
+// 32 rows of k, each 256 n (512 bytes), filled two rows per load instruction,
+// row r rotated by 64 * (r % 4) bytes.  A lane's B fragment (eight k at one n)
+// then comes from two transposing LDS reads (ds_read_b64_tr_b16): in each
+// group of 16 lanes, lanes 4j .. 4j+3 point at 16 consecutive n of row k + j,
+// and lane i receives column i of those four rows, four consecutive k at one
+// n.  Each half-wave reads 64 bytes of four consecutive rows; the rotation
+// puts them in the four quarters of the 64 banks, so a read takes two LDS
+// cycles with no conflict (rotating odd rows only, by 64 bytes, left two rows
+// on each bank: two conflict cycles per read, 40 % more kernel time).  This
+// replaces a packing pass over B (one read and one write of all of it).
+//
+// The compiler cannot tell which LDS bytes a transposing read touches, so it
+// makes each one wait for every load into LDS it knows to be in flight
+// (vmcnt(0)), which would leave the loads one slice of work instead of three.
+// This kernel's loads are therefore issued in a form the compiler does not
+// track (lds_dma16_untracked); their order is kept by the explicit waits
+// above alone, as it already is for the other reads.
 // ---------------------------------------------------------------------------
 namespace dl {
 constexpr int BK = 32;                           // slice depth in elements
@@ -331,8 +353,15 @@ constexpr int NST = 4;                           // stages
 constexpr int RPI = 1024 / ROW;                  // rows per load instruction: 16
 constexpr int LPO = big::BM / 4 / RPI;           // load instructions per wave and operand per slice: 4
 constexpr int LPS = 2 * LPO;                     // per slice: 8
+constexpr int XROW = big::BN * 2;                // B as given: one row of k, 512 bytes
+constexpr int XROT = 64;                         // rotation of row k: XROT * (k % 4) bytes
 static_assert(NST * STAGE <= 160 * 1024, "LDS");
 }  // namespace dl
+
+// Byte offset of B element (row k, column x) in a stage's B part, B as given.
+__device__ __forceinline__ int dl_xoff(int k, int x) {
+    return k * dl::XROW + ((x * 2 + (k & 3) * dl::XROT) & (dl::XROW - 1));
+}
 
 __device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 2) & 3); }
 
@@ -340,7 +369,18 @@ __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned ch
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
 }
 
-template <bool F16>
+// The same copy written as one instruction the compiler does not see as a
+// memory operation: it inserts no wait for it anywhere, and the caller's own
+// s_waitcnt vmcnt counts order it (the hardware counts it like any other
+// load).  M0 holds the LDS base, set by the compiler through the constraint;
+// one wait state separates that write from the copy.  No register is written.
+__device__ __forceinline__ void lds_dma16_untracked(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, int voffset) {
+    const unsigned at = (unsigned)(size_t)(__attribute__((address_space(3))) unsigned char *)lds;
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voffset), "s"(rs), "{m0}"(at)
+                 : "memory");
+}
+
+template <bool F16, bool BXM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
     Args16 g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NST * dl::STAGE];
@@ -356,17 +396,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int h = lane >> 5, l32 = lane & 31;
     const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
     const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
-    const uint16_t *Bb = g.B + (int64_t)n0 * g.ldb;
+    const uint16_t *Bb = BXM ? g.B + n0 : g.B + (int64_t)n0 * g.ldb;
 
     // Load instruction j of this wave covers rows wave*64 + 16 j + lane/4; the
     // lane's position lane % 4 in its row holds chunk dl_pos(row, lane % 4).
+    // B as given: rows of k wave*8 + 2 j + lane/32, the lane's position
+    // lane % 32 holding the 16-byte chunk that the row's rotation puts there
+    // (columns past N get an out-of-range offset and arrive as zeros).
     int offa[dl::LPO], offb[dl::LPO];
 #pragma unroll
     for (int j = 0; j < dl::LPO; ++j) {
         const int r = wave * 64 + dl::RPI * j + (lane >> 2);
         const int c = dl_pos(r, lane & 3);
         offa[j] = (r * (int)g.lda + c * 8) * 2;
-        offb[j] = (r * (int)g.ldb + c * 8) * 2;
+        if (BXM) {
+            const int k = wave * 8 + 2 * j + (lane >> 5);
+            const int cx = ((lane & 31) - (k & 3) * (dl::XROT / 16)) & 31;
+            offb[j] = 8 * cx < rows_b ? (k * (int)g.ldb + 8 * cx) * 2 : kOutOfRange;
+        } else {
+            offb[j] = (r * (int)g.ldb + c * 8) * 2;
+        }
     }
     // Rows past M (N) lie beyond the resource's extent and arrive as zeros.
     // Load i (< LPS) of a slice into a stage: A's first, then B's.
@@ -375,7 +424,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         unsigned char *st = smem + stage * dl::STAGE + wave * 64 * dl::ROW;
         if (i < dl::LPO) {
             const __amdgpu_buffer_rsrc_t rsa = rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
-            lds_dma16(rsa, st + i * 1024, offa[i]);
+            if (BXM) lds_dma16_untracked(rsa, st + i * 1024, offa[i]);
+            else lds_dma16(rsa, st + i * 1024, offa[i]);
+        } else if (BXM) {
+            const __amdgpu_buffer_rsrc_t rsb =
+                rsrc16(Bb + (int64_t)k0 * g.ldb, (int)(((dl::BK - 1) * g.ldb + rows_b) * 2));
+            lds_dma16_untracked(rsb, st + dl::A_STAGE + (i - dl::LPO) * 1024, offb[i - dl::LPO]);
         } else {
             const __amdgpu_buffer_rsrc_t rsb = rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + dl::BK) * 2));
             lds_dma16(rsb, st + dl::A_STAGE + (i - dl::LPO) * 1024, offb[i - dl::LPO]);
@@ -395,7 +449,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Fragment addresses (stage-relative) of k step s: row x, chunk 2 s + h.
-    int fa_off[2][big::BLK], fb_off[2][big::BLK];
+    // B as given: the two transposing reads q = 0, 1 of k step s, block b; in
+    // lane group g16 = lane / 16 (k half lane / 32, n half g16 % 2), lane
+    // 4 j + qq points at row 16 s + 8 h + 4 q + j, columns from
+    // 32 b + 16 (g16 % 2) + 4 qq of the wave's 128.
+    int fa_off[2][big::BLK], fb_off[2][big::BLK], fbx_off[2][big::BLK][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -403,10 +461,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             const int ra = wm * big::WT + 32 * b + l32, rb = wn * big::WT + 32 * b + l32;
             fa_off[s][b] = ra * dl::ROW + dl_pos(ra, 2 * s + h) * 16;
             fb_off[s][b] = dl::A_STAGE + rb * dl::ROW + dl_pos(rb, 2 * s + h) * 16;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int k = 16 * s + 8 * h + 4 * q + ((lane >> 2) & 3);
+                const int x = wn * big::WT + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+                fbx_off[s][b][q] = dl::A_STAGE + dl_xoff(k, x);
+            }
         }
     auto read_blk = [&](const unsigned char *st, int s, int b, i32x4 (&fa)[big::BLK], i32x4 (&fb)[big::BLK]) {
         fa[b] = *reinterpret_cast<const i32x4 *>(st + fa_off[s][b]);
-        fb[b] = *reinterpret_cast<const i32x4 *>(st + fb_off[s][b]);
+        if (BXM) {
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(st + fbx_off[s][b][0]));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4 *)(st + fbx_off[s][b][1]));
+            const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+            fb[b] = i32x4{l2.x, l2.y, h2.x, h2.y};
+        } else {
+            fb[b] = *reinterpret_cast<const i32x4 *>(st + fb_off[s][b]);
+        }
     };
     auto mfma_one = [&](const i32x4 (&fa)[big::BLK], const i32x4 (&fb)[big::BLK], int i) {
         acc[i / big::BLK][i % big::BLK] = mfma16<F16>(fa[i / big::BLK], fb[i % big::BLK], acc[i / big::BLK][i % big::BLK]);
@@ -502,6 +576,15 @@ bool direct_ok(const void *p, int64_t ld, int K) {
     return aligned16(p) && ld % 8 == 0 && K % BK == 0 && (255 * ld + BK) * 2 < ((int64_t)1 << 31);
 }
 
+// B as given (K x N) read in place by the 256 x 256 kernel: 16-byte aligned,
+// row stride and N multiples of 8 (a 16-byte group never straddles N), K a
+// multiple of the 64 the kernels' slices need, and one slice's 32 rows
+// addressable with 32-bit byte offsets.
+bool direct_xmajor_ok(const void *p, int64_t ld, int N, int K) {
+    return aligned16(p) && ld % 8 == 0 && N % 8 == 0 && K % BK == 0 &&
+           ((dl::BK - 1) * ld + big::BN) * 2 < ((int64_t)1 << 31);
+}
+
 hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint16_t *dst, int Kp,
                 hipStream_t stream) {
     const dim3 grid((X + 63) / 64, (Kp + 63) / 64);
@@ -522,11 +605,11 @@ bool use_big_tiles(int M, int N, int64_t ldc) {
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 int64_t gemm16_workspace_bytes(int ta, int tb, int M, int N, int K, const void *A, int64_t lda, const void *B,
-                               int64_t ldb) {
+                               int64_t ldb, bool bxm) {
     const int64_t Kp = (int64_t)(K + BK - 1) / BK * BK;
     int64_t bytes = 0;
     if (ta || !direct_ok(A, lda, K)) bytes += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
-    if (!tb || !direct_ok(B, ldb, K)) bytes += ((int64_t)N * Kp * 2 + 255) / 256 * 256;
+    if (!bxm && (!tb || !direct_ok(B, ldb, K))) bytes += ((int64_t)N * Kp * 2 + 255) / 256 * 256;
     return bytes;
 }
 
@@ -535,8 +618,10 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     const void *A = g16.A, *B = g16.B;
     const int M = g16.M, N = g16.N, K = g16.K;
     const int Kp = (K + BK - 1) / BK * BK;
+    const bool big_tiles = use_big_tiles(M, N, g16.ldc);
+    const bool bxm = !tb && big_tiles && direct_xmajor_ok(B, g16.ldb, N, K);
     const bool pa = ta || !direct_ok(A, g16.lda, K);
-    const bool pb = !tb || !direct_ok(B, g16.ldb, K);
+    const bool pb = !bxm && (!tb || !direct_ok(B, g16.ldb, K));
     Args16 a;
     a.M = M; a.N = N; a.K = Kp;
     a.alpha = g16.alpha; a.beta = g16.beta;
@@ -545,7 +630,7 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     a.B = static_cast<const uint16_t *>(B); a.ldb = g16.ldb;
     void *ws = nullptr;
     if (pa || pb) {
-        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb);
+        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb, bxm);
         hipError_t e = scratch_acquire(g16.scratch, (size_t)bytes, stream, &ws);
         if (e != hipSuccess) return e;
         unsigned char *p = static_cast<unsigned char *>(ws);
@@ -553,7 +638,7 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             uint16_t *dst = reinterpret_cast<uint16_t *>(p);
             e = pack(static_cast<const uint16_t *>(A), g16.lda, ta != 0, M, K, dst, Kp, stream);
             if (e != hipSuccess) {
-                scratch_release(g16.scratch, ws, stream);
+                (void)scratch_release(g16.scratch, ws, stream);
                 return e;
             }
             a.A = dst;
@@ -565,7 +650,7 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             // B as given is K x N: (n, k) at B[k * ldb + n], M/N-major.
             e = pack(static_cast<const uint16_t *>(B), g16.ldb, tb == 0, N, K, dst, Kp, stream);
             if (e != hipSuccess) {
-                scratch_release(g16.scratch, ws, stream);
+                (void)scratch_release(g16.scratch, ws, stream);
                 return e;
             }
             a.B = dst;
@@ -573,13 +658,16 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
         }
     }
     hipError_t e;
-    if (use_big_tiles(M, N, g16.ldc)) {
+    if (big_tiles) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
         const dim3 grid(tiles_m * tiles_n);
-        if (kind == GEMM16_F32_F16)
-            hipLaunchKernelGGL(gemm16_dl_kernel<true>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-        else
-            hipLaunchKernelGGL(gemm16_dl_kernel<false>, grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        if (kind == GEMM16_F32_F16) {
+            if (bxm) hipLaunchKernelGGL((gemm16_dl_kernel<true, true>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+            else hipLaunchKernelGGL((gemm16_dl_kernel<true, false>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        } else {
+            if (bxm) hipLaunchKernelGGL((gemm16_dl_kernel<false, true>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+            else hipLaunchKernelGGL((gemm16_dl_kernel<false, false>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        }
         e = hipGetLastError();
     } else {
         const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;

@@ -190,25 +190,32 @@ def test_gemm16_big_tiles_with_edges(sg, kind, form):
     assert ok, info
 
 
+@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-def test_gemm16_big_tiles_integer_bitexact(sg, kind):
-    M, N, K = 4350, 3900, 520
+def test_gemm16_big_tiles_integer_bitexact(sg, kind, form):
+    """K = 576 (a multiple of 64): with B as given (NN) the larger-tile kernel
+    reads it in place (transposing LDS reads), N = 3904 leaving a column of
+    edge tiles 64 wide."""
+    M, N, K = 4350, 3904, 576
+    ta, tb = form
     A, B, C0 = _inputs16(M, N, K, "int4", kind, 47)
-    st, C, As, Bs = run16(sg, kind, 0, 1, A, B, C0, 1.0, -1.0)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0)
     assert st == 0
     ok, info = check16_logical(C, A, B, kind, 1.0, -1.0, C0, exact=True)
     assert ok, info
 
 
+@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
 @pytest.mark.parametrize("K", [8, 64, 192])
-def test_gemm16_big_tiles_short_k_bitexact(sg, K):
+def test_gemm16_big_tiles_short_k_bitexact(sg, K, form):
     """The larger-tile kernel fetches three 32-deep slices ahead; with only
     two to six slices (K padded to 64 or 192) the loads past the end repeat
     the last slice into stages that are never read."""
     M, N = 4096, 4096
-    say(f"[g16_big_short_k] K={K}")
+    ta, tb = form
+    say(f"[g16_big_short_k] K={K} {form}")
     A, B, C0 = _inputs16(M, N, K, "int4", 1, 60 + K)
-    st, C, As, Bs = run16(sg, 1, 0, 1, A, B, C0, 1.0, -1.0)
+    st, C, As, Bs = run16(sg, 1, ta, tb, A, B, C0, 1.0, -1.0)
     assert st == 0
     ok, info = check16_logical(C, A, B, 1, 1.0, -1.0, C0, exact=True)
     assert ok, info

@@ -131,21 +131,26 @@ def test_poisoned_valu_and_skinny(plib, variant):
 
 # 16-bit inputs: (M, N, K); 4096 x 4096 runs the larger-tile kernel (at least
 # 256 tiles of 256 x 256), the others the 128 x 128 kernel.
-G16_SHAPES = [(4096, 4096, 8), (4096, 4096, 192), (4096, 4096, 520), (300, 260, 700), (128, 128, 64)]
+G16_SHAPES = [(4096, 4096, 8), (4096, 4096, 192), (4096, 4096, 520), (4096, 3904, 576), (300, 260, 700),
+              (128, 128, 64)]
 
 
+@pytest.mark.parametrize("tb", [1, 0], ids=["nt", "nn"])
 @pytest.mark.parametrize("kind", [1, 2], ids=["bf16", "f16"])
 @pytest.mark.parametrize("shape", G16_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in G16_SHAPES])
-def test_poisoned_16bit_kernels(plib, kind, shape):
+def test_poisoned_16bit_kernels(plib, kind, shape, tb):
+    """NT (B stored N x K) and NN (B as given, K x N; read in place with
+    transposing LDS reads by the larger-tile kernel when K is a multiple of
+    64, packed otherwise)."""
     M, N, K = shape
-    say(f"[poison_16] kind {kind} {shape}")
+    say(f"[poison_16] kind {kind} {shape} tb={tb}")
     w = workloads.custom(M, N, K, dist="int4", seed=1900 + K, c0_dist="int4")
     A16, B16, C0 = workloads.make_inputs_16bit(w, kind)
-    Bt = np.ascontiguousarray(B16.T)        # NT: B stored N x K, read in place when aligned
+    Bs = np.ascontiguousarray(B16.T) if tb else B16
     dA = torch.from_numpy(A16.view(np.int16)).cuda()
-    dB = torch.from_numpy(Bt.view(np.int16)).cuda()
+    dB = torch.from_numpy(Bs.view(np.int16)).cuda()
     dC = torch.from_numpy(C0).cuda()
-    st = plib.gemm16_f32(kind, 0, 1, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), K, dB.data_ptr(), K,
+    st = plib.gemm16_f32(kind, 0, tb, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), K, dB.data_ptr(), Bs.shape[1],
                          ctypes.c_float(-1.0), dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
