@@ -377,6 +377,9 @@ def main():
                     help="skip the oracle: no parity check and no CPU baseline (profiling runs)")
     ap.add_argument("--no-context", action="store_true",
                     help="skip the rocBLAS / torch timings and the clock reading")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the shader-clock reading, which starts amd-smi as a child program "
+                         "(runs under a profiler that preloads itself into every process)")
     ap.add_argument("--rotate", type=int, default=1, metavar="COPIES",
                     help="cycle the steps over this many copies of B (with 5 or more, the "
                          "copies exceed the 256 MB Infinity Cache for the skinny workload)")
@@ -581,7 +584,10 @@ def main():
                                         f"about {args.round_seconds} s; per round the median of the "
                                         "last three quarters; value = median over rounds",
                               **ctx}
-        mhz, readings = gfx_clock_mhz(torch, step, stream, kern_avg_s)
+        if args.no_clock:
+            mhz, readings = None, "not read (--no-clock)"
+        else:
+            mhz, readings = gfx_clock_mhz(torch, step, stream, kern_avg_s)
         if mhz is not None:
             # 256 CUs x 4 matrix-core SIMDs x 64 FP32 FLOP per clock each.
             adj = 256 * 256 * mhz * 1e6 / 1e12

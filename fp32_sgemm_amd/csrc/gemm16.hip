@@ -303,30 +303,38 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // ---------------------------------------------------------------------------
 // 256 x 256 tiles with the operands copied from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the instruction's
-// LDS base + 16 * lane, without passing through registers).  With no staging
-// registers the slices can be fetched further ahead: slices of 32 k in four
-// LDS stages of 32 KB, the loads of slice t+3 issued while slice t is
-// multiplied, so a load has three slices of MFMA work (about 3000 clocks) to
-// arrive instead of part of one.  With one wave per SIMD that latency is not
-// hidden by any other wave.
+// LDS base + 16 * lane, without passing through registers), in slices of 64 k.
 //
-// A slice row is 64 bytes (4 chunks of 16).  One load instruction fills 1 KB
-// of LDS: 16 rows.  Chunk c of row r is stored at position c ^ ((r >> 2) & 3),
-// which leaves the fragment reads (32 rows at one chunk per half-wave) free of
-// bank conflicts (LDS bank-conflict counter: zero; without the swizzle, or
-// with one that changes every row or every second row, 50-75 % of the LDS
-// cycles were conflicts); a lane of a load instruction fetches the chunk that
-// belongs at its position.
+// A slice row is 128 bytes, one whole cache line (8 chunks of 16), and one
+// load instruction fills 1 KB of LDS: 8 rows.  With slices of 32 k (64-byte
+// rows, half a line) every line was requested twice from L2: twice
+// hipBLASLt's L2 read requests for the same bytes, and the texture unit's
+// address queue full for most of the kernel, stalling the load instructions
+// and the MFMAs queued behind them.  Chunk c of row r is stored at position
+// c ^ ((r >> 1) & 7): the 16 rows that one quarter-wave reads at one chunk
+// fill the 64 banks once.  A lane of a load instruction fetches the chunk
+// that belongs at its position.
+//
+// LDS is a ring of five 32 KB units, each holding one operand's slice (160 KB,
+// all of it): A of slice s in unit 2s % 5, B in unit (2s + 1) % 5.  While
+// slice t is multiplied, units 2t+3 and 2t+4 (mod 5), slice t-1's, are free,
+// and the slice issues the loads of B of slice t+1 (into the first, early in
+// the slice: it has about one slice of MFMA work to arrive) and of A of slice
+// t+2 (into the second, spread over the rest: more than a slice).  Spreading
+// the 16 loads of a slice over most of its 64 MFMAs keeps the texture unit's
+// queue from filling; with two 64 KB stages, all loads one slice ahead, that
+// spread left the last loads too little time.  With one wave per SIMD nothing
+// else hides their latency.
 //
 // Ordering without __syncthreads (whose fence would wait for every load in
-// flight): at the top of slice t each wave waits until at most the 16 loads
-// of slices t+1 and t+2 are outstanding (vector-memory counts complete in
-// order), and for its own LDS reads, then joins an s_barrier; past it every
-// wave's part of slice t is in LDS and every wave is done with the stage that
-// slice t+3 is loaded into.
+// flight): at the top of slice t each wave waits until at most the 8 loads of
+// A of slice t+1 (its last-issued ones) are in flight, vector-memory counts
+// completing in order, and for its own LDS reads, then joins an s_barrier;
+// past it every wave's part of slice t is in LDS and every wave is done with
+// slice t-1's units.
 //
 // B as given (K x N, rows of n; BXM): its slice is kept as it lies in memory,
-// 32 rows of k, each 256 n (512 bytes), filled two rows per load instruction,
+// 64 rows of k, each 256 n (512 bytes), filled two rows per load instruction,
 // row r rotated by 64 * (r % 4) bytes.  A lane's B fragment (eight k at one n)
 // then comes from two transposing LDS reads (ds_read_b64_tr_b16): in each
 // group of 16 lanes, lanes 4j .. 4j+3 point at 16 consecutive n of row k + j,
@@ -334,36 +342,37 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // n.  Each half-wave reads 64 bytes of four consecutive rows; the rotation
 // puts them in the four quarters of the 64 banks, so a read takes two LDS
 // cycles with no conflict (rotating odd rows only, by 64 bytes, left two rows
-// on each bank: two conflict cycles per read, 40 % more kernel time).  This
-// replaces a packing pass over B (one read and one write of all of it).
+// on each bank: two conflict cycles per read).  This replaces a packing pass
+// over B (one read and one write of all of it).
 //
 // The compiler cannot tell which LDS bytes a transposing read touches, so it
 // makes each one wait for every load into LDS it knows to be in flight
-// (vmcnt(0)), which would leave the loads one slice of work instead of three.
-// This kernel's loads are therefore issued in a form the compiler does not
-// track (lds_dma16_untracked); their order is kept by the explicit waits
-// above alone, as it already is for the other reads.
+// (vmcnt(0)), which would hold every read until all loads issued so far have
+// landed.  This kernel's loads are therefore issued in a form the compiler
+// does not track (lds_dma16_untracked); their order is kept by the explicit
+// waits above alone, as it already is for the other reads.
 // ---------------------------------------------------------------------------
 namespace dl {
-constexpr int BK = 32;                           // slice depth in elements
-constexpr int ROW = BK * 2;                      // 64 bytes
-constexpr int A_STAGE = big::BM * ROW;           // 16 KB
-constexpr int STAGE = A_STAGE + big::BN * ROW;   // 32 KB
-constexpr int NST = 4;                           // stages
-constexpr int RPI = 1024 / ROW;                  // rows per load instruction: 16
-constexpr int LPO = big::BM / 4 / RPI;           // load instructions per wave and operand per slice: 4
-constexpr int LPS = 2 * LPO;                     // per slice: 8
+constexpr int BK = 64;                           // slice depth in elements
+constexpr int ROW = BK * 2;                      // 128 bytes
+constexpr int UNIT = big::BM * ROW;              // one operand's slice: 32 KB
+constexpr int NU = 5;                            // units in the ring
+constexpr int RPI = 1024 / ROW;                  // rows per load instruction: 8
+constexpr int LPO = big::BM / 4 / RPI;           // load instructions per wave and operand per slice: 8
+constexpr int KS = BK / 16;                      // k steps of one MFMA depth: 4
 constexpr int XROW = big::BN * 2;                // B as given: one row of k, 512 bytes
+constexpr int XRPI = 1024 / XROW;                // its rows per load instruction: 2
 constexpr int XROT = 64;                         // rotation of row k: XROT * (k % 4) bytes
-static_assert(NST * STAGE <= 160 * 1024, "LDS");
+static_assert(big::BM == big::BN && NU * UNIT <= 160 * 1024, "LDS");
+static_assert(BK / 4 == XRPI * LPO, "B as given: a wave's rows of k per slice");
 }  // namespace dl
 
-// Byte offset of B element (row k, column x) in a stage's B part, B as given.
+// Byte offset of B element (row k, column x) in its unit, B as given.
 __device__ __forceinline__ int dl_xoff(int k, int x) {
     return k * dl::XROW + ((x * 2 + (k & 3) * dl::XROT) & (dl::XROW - 1));
 }
 
-__device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 2) & 3); }
+__device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
 
 __device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, unsigned char *lds, int voffset) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
@@ -380,10 +389,26 @@ __device__ __forceinline__ void lds_dma16_untracked(__amdgpu_buffer_rsrc_t rs, u
                  : "memory");
 }
 
+// Which load of a slice follows MFMA `slot` of k step `phase` (the first BLK
+// slots of every step hold fragment reads): 0 .. LPO-1 are B's loads of the
+// next slice, one per MFMA from the first free slot on; LPO .. 2 LPO - 1 are
+// A's loads of the slice after it, one every kAStride MFMAs after them.
+// -1: none.
+constexpr int kAStride = 4;
+__host__ __device__ constexpr int dl_load_of(int phase, int slot) {
+    const int per_step = big::BLK * big::BLK - big::BLK;        // 12 free slots per step
+    if (slot < big::BLK) return -1;
+    const int pos = phase * per_step + (slot - big::BLK);
+    if (pos < dl::LPO) return pos;
+    const int a = pos - (per_step + 0);
+    if (a < 0 || a % kAStride != 0 || a / kAStride >= dl::LPO) return -1;
+    return dl::LPO + a / kAStride;
+}
+
 template <bool F16, bool BXM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
     Args16 g, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NST * dl::STAGE];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * dl::UNIT];
     poison_lds<sizeof(smem)>(smem);
     int tm, tn;
     tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
@@ -398,19 +423,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
     const uint16_t *Bb = BXM ? g.B + n0 : g.B + (int64_t)n0 * g.ldb;
 
-    // Load instruction j of this wave covers rows wave*64 + 16 j + lane/4; the
-    // lane's position lane % 4 in its row holds chunk dl_pos(row, lane % 4).
-    // B as given: rows of k wave*8 + 2 j + lane/32, the lane's position
+    // Load instruction j of this wave covers rows wave*64 + 8 j + lane/8; the
+    // lane's position lane % 8 in its row holds chunk dl_pos(row, lane % 8).
+    // B as given: rows of k wave*16 + 2 j + lane/32, the lane's position
     // lane % 32 holding the 16-byte chunk that the row's rotation puts there
-    // (columns past N get an out-of-range offset and arrive as zeros).
+    // (columns past N get an out-of-range offset and arrive as zeros).  Both
+    // fill 8 KB per wave of their unit.
     int offa[dl::LPO], offb[dl::LPO];
 #pragma unroll
     for (int j = 0; j < dl::LPO; ++j) {
-        const int r = wave * 64 + dl::RPI * j + (lane >> 2);
-        const int c = dl_pos(r, lane & 3);
+        const int r = wave * 64 + dl::RPI * j + (lane >> 3);
+        const int c = dl_pos(r, lane & 7);
         offa[j] = (r * (int)g.lda + c * 8) * 2;
         if (BXM) {
-            const int k = wave * 8 + 2 * j + (lane >> 5);
+            const int k = wave * (dl::BK / 4) + dl::XRPI * j + (lane >> 5);
             const int cx = ((lane & 31) - (k & 3) * (dl::XROT / 16)) & 31;
             offb[j] = 8 * cx < rows_b ? (k * (int)g.ldb + 8 * cx) * 2 : kOutOfRange;
         } else {
@@ -418,26 +444,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     }
     // Rows past M (N) lie beyond the resource's extent and arrive as zeros.
-    // Load i (< LPS) of a slice into a stage: A's first, then B's.
-    auto issue_one = [&](int slice, int stage, int i) {
-        const int k0 = slice * dl::BK;
-        unsigned char *st = smem + stage * dl::STAGE + wave * 64 * dl::ROW;
-        if (i < dl::LPO) {
-            const __amdgpu_buffer_rsrc_t rsa = rsrc16(Ab + k0, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
-            if (BXM) lds_dma16_untracked(rsa, st + i * 1024, offa[i]);
-            else lds_dma16(rsa, st + i * 1024, offa[i]);
-        } else if (BXM) {
-            const __amdgpu_buffer_rsrc_t rsb =
-                rsrc16(Bb + (int64_t)k0 * g.ldb, (int)(((dl::BK - 1) * g.ldb + rows_b) * 2));
-            lds_dma16_untracked(rsb, st + dl::A_STAGE + (i - dl::LPO) * 1024, offb[i - dl::LPO]);
-        } else {
-            const __amdgpu_buffer_rsrc_t rsb = rsrc16(Bb + k0, (int)(((rows_b - 1) * g.ldb + dl::BK) * 2));
-            lds_dma16(rsb, st + dl::A_STAGE + (i - dl::LPO) * 1024, offb[i - dl::LPO]);
-        }
+    auto issue_a = [&](int slice, int unit, int j) {
+        unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
+        const __amdgpu_buffer_rsrc_t rsa =
+            rsrc16(Ab + slice * dl::BK, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
+        if (BXM) lds_dma16_untracked(rsa, dst, offa[j]);
+        else lds_dma16(rsa, dst, offa[j]);
     };
-    auto issue = [&](int slice, int stage) {
-#pragma unroll
-        for (int i = 0; i < dl::LPS; ++i) issue_one(slice, stage, i);
+    auto issue_b = [&](int slice, int unit, int j) {
+        unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
+        if (BXM) {
+            const __amdgpu_buffer_rsrc_t rsb =
+                rsrc16(Bb + (int64_t)slice * dl::BK * g.ldb, (int)(((dl::BK - 1) * g.ldb + rows_b) * 2));
+            lds_dma16_untracked(rsb, dst, offb[j]);
+        } else {
+            const __amdgpu_buffer_rsrc_t rsb =
+                rsrc16(Bb + slice * dl::BK, (int)(((rows_b - 1) * g.ldb + dl::BK) * 2));
+            lds_dma16(rsb, dst, offb[j]);
+        }
     };
 
     f32x16 acc[big::BLK][big::BLK];
@@ -448,38 +472,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-    // Fragment addresses (stage-relative) of k step s: row x, chunk 2 s + h.
-    // B as given: the two transposing reads q = 0, 1 of k step s, block b; in
-    // lane group g16 = lane / 16 (k half lane / 32, n half g16 % 2), lane
-    // 4 j + qq points at row 16 s + 8 h + 4 q + j, columns from
-    // 32 b + 16 (g16 % 2) + 4 qq of the wave's 128.
-    int fa_off[2][big::BLK], fb_off[2][big::BLK], fbx_off[2][big::BLK][2];
+    // Fragment addresses (unit-relative).  K-major: block b of k step s is
+    // row x = w*128 + 32 b + l32 of the operand, chunk 2 s + h; the rows of
+    // the four blocks differ by 32, which leaves (x >> 1) & 7 alone, so the
+    // block only adds 32 rows.  B as given: the two transposing reads q = 0, 1
+    // of k step s, block b; in lane group g16 = lane / 16 (k half lane / 32,
+    // n half g16 % 2), lane 4 j + qq points at row 16 s + 8 h + 4 q + j,
+    // columns from 32 b + 16 (g16 % 2) + 4 qq of the wave's 128; the step and
+    // q only add whole rows.
+    int fa_off[dl::KS], fb_off[dl::KS], fbx_off[big::BLK];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
+    for (int s = 0; s < dl::KS; ++s) {
+        const int pos = dl_pos(l32, 2 * s + h) * 16;
+        fa_off[s] = (wm * big::WT + l32) * dl::ROW + pos;
+        fb_off[s] = (wn * big::WT + l32) * dl::ROW + pos;
+    }
 #pragma unroll
-        for (int b = 0; b < big::BLK; ++b) {
-            const int ra = wm * big::WT + 32 * b + l32, rb = wn * big::WT + 32 * b + l32;
-            fa_off[s][b] = ra * dl::ROW + dl_pos(ra, 2 * s + h) * 16;
-            fb_off[s][b] = dl::A_STAGE + rb * dl::ROW + dl_pos(rb, 2 * s + h) * 16;
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int k = 16 * s + 8 * h + 4 * q + ((lane >> 2) & 3);
-                const int x = wn * big::WT + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-                fbx_off[s][b][q] = dl::A_STAGE + dl_xoff(k, x);
-            }
-        }
-    auto read_blk = [&](const unsigned char *st, int s, int b, i32x4 (&fa)[big::BLK], i32x4 (&fb)[big::BLK]) {
-        fa[b] = *reinterpret_cast<const i32x4 *>(st + fa_off[s][b]);
+    for (int b = 0; b < big::BLK; ++b) {
+        const int k = 8 * h + ((lane >> 2) & 3);
+        const int x = wn * big::WT + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        fbx_off[b] = dl_xoff(k, x);
+    }
+    auto read_blk = [&](const unsigned char *sa, const unsigned char *sb, int s, int b, i32x4 (&fa)[big::BLK],
+                        i32x4 (&fb)[big::BLK]) {
+        fa[b] = *reinterpret_cast<const i32x4 *>(sa + fa_off[s] + 32 * b * dl::ROW);
         if (BXM) {
             typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(st + fbx_off[s][b][0]));
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4 *)(st + fbx_off[s][b][1]));
+            const unsigned char *p = sb + fbx_off[b] + 16 * s * dl::XROW;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * dl::XROW));
             const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
             fb[b] = i32x4{l2.x, l2.y, h2.x, h2.y};
         } else {
-            fb[b] = *reinterpret_cast<const i32x4 *>(st + fb_off[s][b]);
+            fb[b] = *reinterpret_cast<const i32x4 *>(sb + fb_off[s] + 32 * b * dl::ROW);
         }
     };
     auto mfma_one = [&](const i32x4 (&fa)[big::BLK], const i32x4 (&fb)[big::BLK], int i) {
@@ -487,53 +512,79 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     };
 
     const int nk = g.K / dl::BK;
-    // Slices past the end are loaded again as the last one, into stages that
-    // are never read, so every slice issues the same number of loads.
+    // Before the first slice: A and B of slice 0, A of slice 1 (the last
+    // issued, so that slice 0 can start while it is in flight).
 #pragma unroll
-    for (int s = 0; s < dl::NST - 1; ++s) issue(s < nk ? s : nk - 1, s);
+    for (int j = 0; j < dl::LPO; ++j) issue_a(0, 0, j);
+#pragma unroll
+    for (int j = 0; j < dl::LPO; ++j) issue_b(0, 1, j);
+    if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < dl::LPO; ++j) issue_a(1, 2, j);
+    }
 
-    i32x4 f0a[big::BLK], f0b[big::BLK], f1a[big::BLK], f1b[big::BLK];
+    // Fragments of the even (x) and odd (y) k steps.
+    i32x4 fxa[big::BLK], fxb[big::BLK], fya[big::BLK], fyb[big::BLK];
 #pragma unroll
     for (int b = 0; b < big::BLK; ++b) {
-        f1a[b] = i32x4{0, 0, 0, 0};
-        f1b[b] = i32x4{0, 0, 0, 0};
+        fya[b] = i32x4{0, 0, 0, 0};
+        fyb[b] = i32x4{0, 0, 0, 0};
     }
     // One wave per SIMD issues in order, so every other instruction of a
     // slice is placed right after an MFMA and goes out while the matrix core
-    // works; sched_barrier keeps the compiler from regrouping them.
-    //   phase 1: the MFMAs of the previous slice's last k step (zeros before
-    //            the first slice), followed by this slice's first-step
-    //            fragment reads and the loads of slice t+3;
-    //   phase 2: the MFMAs of the first k step, followed by the reads of the
-    //            second, whose MFMAs are held over to the next slice.
-    for (int t = 0; t < nk; ++t) {
-        // vmcnt(16) (two slices still in flight) and lgkmcnt(0); expcnt not waited on.
-        __builtin_amdgcn_s_waitcnt((1 << 14) | (0 << 8) | (7 << 4) | 0);
+    // works; sched_barrier keeps the compiler from regrouping them.  Step p of
+    // slice t runs the MFMAs of the step before it (for p = 0 the previous
+    // slice's last step, zeros before the first slice), each followed by a
+    // fragment read of step p or one of the slice's loads.  LB: B of slice
+    // t+1 is loaded; LA: A of slice t+2; WAIT8: A of slice t+1 may still be
+    // in flight at the top (it is, unless t is the last slice).
+    int ua = 0, ub = 1;   // units of slice t: 2t % 5, (2t + 1) % 5
+    auto slice = [&](int t, auto wait8_tag, auto lb_tag, auto la_tag) {
+        constexpr bool WAIT8 = decltype(wait8_tag)::value;
+        constexpr bool LB = decltype(lb_tag)::value;
+        constexpr bool LA = decltype(la_tag)::value;
+        // vmcnt(8) or vmcnt(0), and lgkmcnt(0); expcnt not waited on.
+        if (WAIT8) __builtin_amdgcn_s_waitcnt((0 << 14) | (0 << 8) | (7 << 4) | 8);
+        else __builtin_amdgcn_s_waitcnt((0 << 14) | (0 << 8) | (7 << 4) | 0);
         __builtin_amdgcn_s_barrier();
-        const int ld_slice = t + dl::NST - 1 < nk ? t + dl::NST - 1 : nk - 1;
-        const int ld_stage = (t + dl::NST - 1) % dl::NST;
-        const unsigned char *st = smem + (t % dl::NST) * dl::STAGE;
+        const unsigned char *sa = smem + ua * dl::UNIT, *sb = smem + ub * dl::UNIT;
+        const int unit_b1 = ub + 2 < dl::NU ? ub + 2 : ub + 2 - dl::NU;   // B of slice t+1
+        const int unit_a2 = ua + 4 < dl::NU ? ua + 4 : ua + 4 - dl::NU;   // A of slice t+2
+        auto step = [&](auto phase_tag, const i32x4 (&ux)[big::BLK], const i32x4 (&uy)[big::BLK],
+                        i32x4 (&rx)[big::BLK], i32x4 (&ry)[big::BLK]) {
+            constexpr int P = decltype(phase_tag)::value;
 #pragma unroll
-        for (int i = 0; i < big::BLK * big::BLK; ++i) {
-            mfma_one(f1a, f1b, i);
-            __builtin_amdgcn_sched_barrier(0);
-            if (i < big::BLK) read_blk(st, 0, i, f0a, f0b);
-            else if (i < big::BLK + dl::LPS) issue_one(ld_slice, ld_stage, i - big::BLK);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int i = 0; i < big::BLK * big::BLK; ++i) {
-            mfma_one(f0a, f0b, i);
-            __builtin_amdgcn_sched_barrier(0);
-            if (i < big::BLK) read_blk(st, 1, i, f1a, f1b);
-            __builtin_amdgcn_sched_barrier(0);
-        }
+            for (int i = 0; i < big::BLK * big::BLK; ++i) {
+                mfma_one(ux, uy, i);
+                __builtin_amdgcn_sched_barrier(0);
+                if (i < big::BLK) {
+                    read_blk(sa, sb, P, i, rx, ry);
+                } else {
+                    const int l = dl_load_of(P, i);
+                    if (LB && l >= 0 && l < dl::LPO) issue_b(t + 1, unit_b1, l);
+                    else if (LA && l >= dl::LPO) issue_a(t + 2, unit_a2, l - dl::LPO);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        step(std::integral_constant<int, 0>(), fya, fyb, fxa, fxb);
+        step(std::integral_constant<int, 1>(), fxa, fxb, fya, fyb);
+        step(std::integral_constant<int, 2>(), fya, fyb, fxa, fxb);
+        step(std::integral_constant<int, 3>(), fxa, fxb, fya, fyb);
+        ua = ua + 2 < dl::NU ? ua + 2 : ua + 2 - dl::NU;
+        ub = ub + 2 < dl::NU ? ub + 2 : ub + 2 - dl::NU;
+    };
+    using yes = std::true_type;
+    using no = std::false_type;
+    int t = 0;
+    for (; t + 2 < nk; ++t) slice(t, yes(), yes(), yes());
+    if (t + 1 < nk) {
+        slice(t, yes(), yes(), no());
+        ++t;
     }
+    slice(t, no(), no(), no());
 #pragma unroll
-    for (int i = 0; i < big::BLK * big::BLK; ++i) mfma_one(f1a, f1b, i);
-    // Every load issued (including the repeated last slice) has landed before
-    // the work-group can end and its LDS be given to another.
-    __builtin_amdgcn_s_waitcnt(0);
+    for (int i = 0; i < big::BLK * big::BLK; ++i) mfma_one(fya, fyb, i);
 
     big_epilogue(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
 }
