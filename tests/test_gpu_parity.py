@@ -402,6 +402,41 @@ def test_c_leading_dimension_past_32bit_offsets(sg):
     torch.cuda.empty_cache()
 
 
+# Shapes for which the automatic choice plans a direct-to-LDS configuration
+# (9: 64x64, 7: 256x256, 8: 128x128 tiles).
+WIDE_LDC = [((128, 8192, 2048), 9), ((256, 65536, 512), 7), ((768, 32768, 512), 8)]
+
+
+@pytest.mark.parametrize("shape,planned", WIDE_LDC, ids=[f"{m}x{n}x{k}-cfg{c}" for (m, n, k), c in WIDE_LDC])
+def test_auto_plan_with_c_stride_past_32bit_offsets(sg, shape, planned):
+    """The direct-to-LDS configurations address a tile of C with 32-bit
+    offsets; with ldc so wide that 255 rows of C span more than 2 GiB the
+    automatic call must switch to a register-staged kernel (64-bit
+    addressing).  Integer inputs, checked bit for bit, with the columns past N
+    left untouched."""
+    M, N, K = shape
+    ldc = 2_105_600
+    assert (255 * ldc + 256) * 4 >= 1 << 31
+    A, B, C0 = _inputs(M, N, K, "int4", 63 + planned)
+    dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    st, _, cfg, _, _ = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N)
+    assert st == 0 and cfg == planned
+    say(f"[wide_ldc] {shape} ldc={ldc} ({M * ldc * 4 / 2**30:.2f} GiB for C), planned configuration {cfg}")
+    dC = torch.full((M, ldc), -7.25, device="cuda")
+    dC[:, :N] = torch.from_numpy(C0).cuda()
+    st = sg.sgemm_f32(M, N, K, 1.5, dA.data_ptr(), K, dB.data_ptr(), N, -0.5, dC.data_ptr(), ldc,
+                      torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    C = dC[:, :N].cpu().numpy()
+    assert np.all(dC[:, N:N + 256].cpu().numpy() == np.float32(-7.25))
+    assert np.all(dC[:, -256:].cpu().numpy() == np.float32(-7.25))
+    del dC
+    torch.cuda.empty_cache()
+    ok, info = check_full(C, A, B, 1.5, -0.5, C0, exact=True)
+    assert ok, info
+
+
 @pytest.mark.parametrize("case", ["skinny", "splitk"])
 def test_split_plans_in_a_captured_graph(sg, case):
     """A call whose plan allocates stream-ordered scratch (the M <= 16 split,
