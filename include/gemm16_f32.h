@@ -29,9 +29,11 @@
  * (B stored N x K) and trans_a == 0, 16-byte aligned operands, row strides that
  * are multiples of 8 elements and K a multiple of 64, A and B are read in
  * place.  Otherwise the operands that do not meet this are first copied into a
- * K-major, zero-padded form in the call's scratch, allocated in stream order
- * (see sgemm_f32.h; (M or N) * K rounded up to 64 elements * 2 bytes each),
- * which costs one extra pass over them.
+ * K-major, zero-padded form in the call's scratch, taken as sgemm_f32.h
+ * describes ((M or N) * K rounded up to 64 elements * 2 bytes each), which
+ * costs one extra pass over them.  B of the NN form (trans_b == 0) is read in
+ * place by the larger-tile kernel when it is aligned as above and N is a
+ * multiple of 8.
  *
  * Ownership and execution: device pointers owned by the caller, asynchronous on
  * `stream`, no synchronisation, thread-safe; as sgemm_f32.

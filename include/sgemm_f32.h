@@ -37,14 +37,21 @@
  *     nothing): none unless the reduction over K is split across
  *     work-groups (the M <= 16 kernel, MFMA plans with splits > 1 from the
  *     tuning table or sgemm_f32_ex_config, and the stream-K configuration).
- *     Such a call allocates its scratch in stream order: hipMallocFromPoolAsync
- *     on `stream` before its kernels and hipFreeAsync on `stream` after them,
- *     from a memory pool the library creates on the first such call on a
- *     device (at most splits * M * N floats, 1 GiB cap for MFMA plans; the
- *     pool keeps up to 1 GiB of freed memory for later calls and lives until
- *     the process ends).  The scratch is valid only for the call's own
- *     kernels, so calls on different streams never share it and both
- *     operations can be recorded by graph capture.
+ *     Such a call needs scratch (at most splits * M * N floats, 1 GiB cap for
+ *     MFMA plans), taken from a memory pool the library creates on the first
+ *     such call on a device (it keeps up to 1 GiB of freed memory and lives
+ *     until the process ends):
+ *       - outside graph capture, up to 64 MiB, on one of the first 8 streams
+ *         (per device) that need scratch: a block the library keeps for that
+ *         stream until the process ends, reused by every later call on it
+ *         (stream order serialises them) and grown in stream order when a
+ *         call needs more.  A block never serves another stream.  A stream
+ *         handle must not name a new stream while work on the old one that
+ *         used it is pending (destroying a HIP stream waits for its work);
+ *       - otherwise (graph capture, larger requests, further streams): in
+ *         stream order, hipMallocFromPoolAsync on `stream` before the call's
+ *         kernels and hipFreeAsync after them, which graph capture records.
+ *     Either way, calls on different streams never share scratch.
  *
  * Special cases:
  *   - M == 0 or N == 0: nothing is done, returns 0.

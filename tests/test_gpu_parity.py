@@ -219,9 +219,9 @@ def test_skinny_concurrent_streams(sg):
 
 
 def test_scratch_sizes_and_host_threads(sg):
-    """Split plans take their scratch in stream order: products of different
-    sizes in a row on one stream each get a block of their own size, and host
-    threads calling on their own streams at the same time never share one."""
+    """Products of different sizes in a row on one stream (its cached scratch
+    block grows in stream order), and host threads calling on their own
+    streams at the same time, which never share a block."""
     import threading
     cases = [(256, 256, 4096, 41), (512, 512, 8192, 42), (256, 256, 4096, 43)]
     data = []
@@ -264,6 +264,45 @@ def test_scratch_sizes_and_host_threads(sg):
     for t in threads:
         t.join()
     assert not errors, errors
+
+
+def test_scratch_cache_many_streams_and_large_requests(sg):
+    """Eager calls keep a scratch block per stream for up to 8 streams, each
+    block at most 64 MiB: here 11 streams have split plans in flight at once
+    (the streams past the cache take stream-ordered pool memory per call), and
+    one stream with a cached block also runs a product whose partial sums need
+    75.5 MB (pool memory) between two that fit its block.  Every result is
+    checked against the oracle."""
+    small, big = (256, 256, 4096), (1536, 1536, 4096)
+    streams = [torch.cuda.Stream() for _ in range(11)]
+    jobs = []
+    for i, st in enumerate(streams):
+        M, N, K = small
+        A, B, _ = _inputs(M, N, K, "uniform", 50 + i, c0=False)
+        jobs.append((st, M, N, K, A, B, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+                     torch.zeros(M, N, device="cuda:0")))
+    M, N, K = big
+    A, B, _ = _inputs(M, N, K, "uniform", 70, c0=False)
+    big_job = (streams[0], M, N, K, A, B, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(),
+               torch.zeros(M, N, device="cuda:0"))
+    torch.cuda.synchronize()
+
+    def launch(job):
+        st, M, N, K, _, _, dA, dB, dC = job
+        # configuration 4 (64x64, two slices in flight) with 8 K splits: 8*M*N floats of partials
+        return sg.sgemm_f32_ex_config(4, 8, 8, 0, 0, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                                      dC.data_ptr(), N, st.cuda_stream)
+
+    say("[scratch_cache] 11 streams, then 75.5 MB of partials on the first")
+    for _ in range(2):
+        for job in jobs:
+            assert launch(job) == 0
+    assert launch(big_job) == 0
+    assert launch(jobs[0]) == 0
+    torch.cuda.synchronize()
+    for _, M, N, K, A, B, _, _, dC in jobs + [big_job]:
+        ok, info = check_full(dC.cpu().numpy(), A, B, 1.0, 0.0, None)
+        assert ok, (M, N, K, info)
 
 
 def test_non_default_stream_ordering(sg):

@@ -52,6 +52,17 @@ def test_library_exports_every_declared_symbol(sg):
     assert set(sg.EXPORTED) == set(_declared_functions())
 
 
+def test_library_loads_after_torch():
+    """In a process that imported torch first, the library's HIP symbols bind
+    to the HIP runtime torch brings (an older one than the system's), so the
+    library may only use entry points that runtime has; a newer one fails the
+    load.  Run in a fresh process to fix the import order."""
+    code = ("import torch, fp32_sgemm_amd as sg; "
+            "assert sg.sgemm_f32_version() > 0; print('ok')")
+    p = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0 and "ok" in p.stdout, p.stderr[-2000:]
+
+
 def test_lds_poison_copy_exports_the_same_interface(sg):
     """The debug copy that the LDS-poisoning GPU tests run is built from the
     same sources and exports every declared function too."""
