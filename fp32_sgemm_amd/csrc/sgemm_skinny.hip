@@ -13,17 +13,28 @@
 // `splits` contiguous ranges of K; its 4 waves split that range again.  The
 // partial strips of the splits go to the call's scratch and a second kernel
 // adds them in split order and finishes C (with one split, the first kernel
-// finishes C itself).  Measured alternatives (per call, B rotated over six
-// copies, 16 x 4096 x 4096; a plain read of B alone: 13.6 us):
-//   - this form, 8 splits: 25.9 us, its first kernel 19.8 us;
+// finishes C itself).  Measured alternatives, 16 x 4096 x 4096 with B over
+// 6-7 copies (past the Infinity Cache).  Calls back to back between one pair
+// of events:
+//   - this form, 8 splits: 18.9-19.0 us per call, its first kernel alone
+//     16.8 us; a kernel that only reads B with the same decomposition takes
+//     14.7 us and the fastest plain read of B found 12.6 us;
+//   - the same kernels fused, the last split of each strip adding the others'
+//     partials once their flags show the call's epoch (agent-scope coherent
+//     stores and loads, no fences): 19.3-19.4 us, the waiting tail costs more
+//     than the second launch;
+//   - A staged in LDS per work-group instead of read with B: 21.9 us (fused);
+//   - 4 batches per wave, or batches interleaved across the waves: 21-22 us;
+//     16 splits: 24.1 us.
+// With events around every call (each pair costs GPU time here):
 //   - no split between work-groups (a work-group per strip of 16, 32 or 64
 //     columns with 4-16 waves splitting K, reduced in LDS, no scratch at all):
 //     30-40 us, too few bytes of B in flight per strip;
 //   - wider strips (256 or 512 columns per work-group) or more waves: 26-37 us;
-//   - one kernel in which the last work-group of a strip to finish adds the
-//     partials (a device-scope counter): 25.6-28 us with coherent partial
-//     stores and loads, 38.8 us with release/acquire fences (each fence writes
-//     back or invalidates a whole L2).
+//   - the last work-group of a strip to finish adding the partials (a
+//     device-scope counter): no gain with coherent partial stores and loads,
+//     38.8 us with release/acquire fences (each fence writes back or
+//     invalidates a whole L2).
 //
 // Inner step.  For a block of 16 rows of B starting at kb, lane l (h = l/16,
 // j = l%16) loads columns 4j..4j+3 of rows kb + 4h + q, q = 0..3 (four 16-byte
