@@ -400,7 +400,7 @@ __host__ __device__ constexpr int dl_load_of(int phase, int slot) {
     if (slot < big::BLK) return -1;
     const int pos = phase * per_step + (slot - big::BLK);
     if (pos < dl::LPO) return pos;
-    const int a = pos - (per_step + 0);
+    const int a = pos - per_step;                               // A's loads start in step 1
     if (a < 0 || a % kAStride != 0 || a / kAStride >= dl::LPO) return -1;
     return dl::LPO + a / kAStride;
 }

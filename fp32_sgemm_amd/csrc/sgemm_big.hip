@@ -217,7 +217,9 @@ constexpr int pieces() { return L == kKRows ? Geo<TS>::BLK : 4 * Geo<TS>::BLK; }
 // MFMA work between two barriers and gives each SIMD a second wave to issue.
 // Measured on MI355X (per-launch medians, one group -> two): 1024^3 21.16 ->
 // 20.92 µs, 1024 x 1024 x 4096 68.6 -> 66.1 µs; eight LDS stages per group
-// instead of four (seven slices in flight) gained nothing on either.
+// instead of four (seven slices in flight) gained nothing on either, and four
+// groups (16 waves per CU, 128 registers each) lost: 1024^3 21.9-22.1 against
+// 20.9-21.0 µs, slower on every grid of at most one tile per CU tried.
 template <int LA, int LB, bool EDGE, int TS, int KG = 1>
 __device__ __forceinline__ void big_tile(const GemmArgs &g, int m0, int n0, unsigned char *smem_all) {
     using G = Geo<TS>;
