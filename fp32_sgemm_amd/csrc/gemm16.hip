@@ -343,14 +343,17 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // puts them in the four quarters of the 64 banks, so a read takes two LDS
 // cycles with no conflict (rotating odd rows only, by 64 bytes, left two rows
 // on each bank: two conflict cycles per read).  This replaces a packing pass
-// over B (one read and one write of all of it).
+// over B (one read and one write of all of it).  A given transposed (K x M,
+// rows of m; AXM) is staged and read the same way: the MFMA takes its A and B
+// fragments in the same lane layout, x standing for m or n.
 //
 // The compiler cannot tell which LDS bytes a transposing read touches, so it
 // makes each one wait for every load into LDS it knows to be in flight
 // (vmcnt(0)), which would hold every read until all loads issued so far have
-// landed.  This kernel's loads are therefore issued in a form the compiler
-// does not track (lds_dma16_untracked); their order is kept by the explicit
-// waits above alone, as it already is for the other reads.
+// landed.  The instances with transposing reads therefore issue their loads in
+// a form the compiler does not track (lds_dma16_untracked); their order is
+// kept by the explicit waits above alone, as it already is for the other
+// reads.
 // ---------------------------------------------------------------------------
 namespace dl {
 constexpr int BK = 64;                           // slice depth in elements
@@ -405,7 +408,7 @@ __host__ __device__ constexpr int dl_load_of(int phase, int slot) {
     return dl::LPO + a / kAStride;
 }
 
-template <bool F16, bool BXM>
+template <bool F16, bool AXM, bool BXM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
     Args16 g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * dl::UNIT];
@@ -420,36 +423,47 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
-    const uint16_t *Ab = g.A + (int64_t)m0 * g.lda;
+    const uint16_t *Ab = AXM ? g.A + m0 : g.A + (int64_t)m0 * g.lda;
     const uint16_t *Bb = BXM ? g.B + n0 : g.B + (int64_t)n0 * g.ldb;
+    // Any transposing read needs every load into LDS untracked (see above).
+    constexpr bool UNTRACKED = AXM || BXM;
 
     // Load instruction j of this wave covers rows wave*64 + 8 j + lane/8; the
     // lane's position lane % 8 in its row holds chunk dl_pos(row, lane % 8).
-    // B as given: rows of k wave*16 + 2 j + lane/32, the lane's position
-    // lane % 32 holding the 16-byte chunk that the row's rotation puts there
-    // (columns past N get an out-of-range offset and arrive as zeros).  Both
-    // fill 8 KB per wave of their unit.
-    int offa[dl::LPO], offb[dl::LPO];
+    // An operand as given along x (A transposed, K x M; B as given, K x N):
+    // rows of k wave*16 + 2 j + lane/32, the lane's position lane % 32 holding
+    // the 16-byte chunk that the row's rotation puts there (x past M or N gets
+    // an out-of-range offset and arrives as zeros).  Both fill 8 KB per wave
+    // of their unit.
+    auto offsets = [&](bool xm, int64_t ld, int rows, int (&off)[dl::LPO]) {
 #pragma unroll
-    for (int j = 0; j < dl::LPO; ++j) {
-        const int r = wave * 64 + dl::RPI * j + (lane >> 3);
-        const int c = dl_pos(r, lane & 7);
-        offa[j] = (r * (int)g.lda + c * 8) * 2;
-        if (BXM) {
-            const int k = wave * (dl::BK / 4) + dl::XRPI * j + (lane >> 5);
-            const int cx = ((lane & 31) - (k & 3) * (dl::XROT / 16)) & 31;
-            offb[j] = 8 * cx < rows_b ? (k * (int)g.ldb + 8 * cx) * 2 : kOutOfRange;
-        } else {
-            offb[j] = (r * (int)g.ldb + c * 8) * 2;
+        for (int j = 0; j < dl::LPO; ++j) {
+            if (xm) {
+                const int k = wave * (dl::BK / 4) + dl::XRPI * j + (lane >> 5);
+                const int cx = ((lane & 31) - (k & 3) * (dl::XROT / 16)) & 31;
+                off[j] = 8 * cx < rows ? (k * (int)ld + 8 * cx) * 2 : kOutOfRange;
+            } else {
+                const int r = wave * 64 + dl::RPI * j + (lane >> 3);
+                off[j] = (r * (int)ld + dl_pos(r, lane & 7) * 8) * 2;
+            }
         }
-    }
+    };
+    int offa[dl::LPO], offb[dl::LPO];
+    offsets(AXM, g.lda, rows_a, offa);
+    offsets(BXM, g.ldb, rows_b, offb);
     // Rows past M (N) lie beyond the resource's extent and arrive as zeros.
     auto issue_a = [&](int slice, int unit, int j) {
         unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
-        const __amdgpu_buffer_rsrc_t rsa =
-            rsrc16(Ab + slice * dl::BK, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
-        if (BXM) lds_dma16_untracked(rsa, dst, offa[j]);
-        else lds_dma16(rsa, dst, offa[j]);
+        if (AXM) {
+            const __amdgpu_buffer_rsrc_t rsa =
+                rsrc16(Ab + (int64_t)slice * dl::BK * g.lda, (int)(((dl::BK - 1) * g.lda + rows_a) * 2));
+            lds_dma16_untracked(rsa, dst, offa[j]);
+        } else {
+            const __amdgpu_buffer_rsrc_t rsa =
+                rsrc16(Ab + slice * dl::BK, (int)(((rows_a - 1) * g.lda + dl::BK) * 2));
+            if (UNTRACKED) lds_dma16_untracked(rsa, dst, offa[j]);
+            else lds_dma16(rsa, dst, offa[j]);
+        }
     };
     auto issue_b = [&](int slice, int unit, int j) {
         unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
@@ -460,7 +474,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         } else {
             const __amdgpu_buffer_rsrc_t rsb =
                 rsrc16(Bb + slice * dl::BK, (int)(((rows_b - 1) * g.ldb + dl::BK) * 2));
-            lds_dma16(rsb, dst, offb[j]);
+            if (UNTRACKED) lds_dma16_untracked(rsb, dst, offb[j]);
+            else lds_dma16(rsb, dst, offb[j]);
         }
     };
 
@@ -475,12 +490,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // Fragment addresses (unit-relative).  K-major: block b of k step s is
     // row x = w*128 + 32 b + l32 of the operand, chunk 2 s + h; the rows of
     // the four blocks differ by 32, which leaves (x >> 1) & 7 alone, so the
-    // block only adds 32 rows.  B as given: the two transposing reads q = 0, 1
-    // of k step s, block b; in lane group g16 = lane / 16 (k half lane / 32,
-    // n half g16 % 2), lane 4 j + qq points at row 16 s + 8 h + 4 q + j,
-    // columns from 32 b + 16 (g16 % 2) + 4 qq of the wave's 128; the step and
-    // q only add whole rows.
-    int fa_off[dl::KS], fb_off[dl::KS], fbx_off[big::BLK];
+    // block only adds 32 rows.  Along x (the MFMA takes A and B fragments of
+    // the same shape): the two transposing reads q = 0, 1 of k step s, block
+    // b; in lane group g16 = lane / 16 (k half lane / 32, x half g16 % 2),
+    // lane 4 j + qq points at row 16 s + 8 h + 4 q + j, x from 32 b +
+    // 16 (g16 % 2) + 4 qq of the wave's 128; the step and q only add whole rows.
+    int fa_off[dl::KS], fb_off[dl::KS], fax_off[big::BLK], fbx_off[big::BLK];
 #pragma unroll
     for (int s = 0; s < dl::KS; ++s) {
         const int pos = dl_pos(l32, 2 * s + h) * 16;
@@ -490,22 +505,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int b = 0; b < big::BLK; ++b) {
         const int k = 8 * h + ((lane >> 2) & 3);
-        const int x = wn * big::WT + 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        fbx_off[b] = dl_xoff(k, x);
+        const int xq = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+        fax_off[b] = dl_xoff(k, wm * big::WT + xq);
+        fbx_off[b] = dl_xoff(k, wn * big::WT + xq);
     }
+    // Eight k at one x from two transposing reads, four rows apart.
+    auto read_tr = [&](const unsigned char *p) {
+        typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * dl::XROW));
+        const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+        return i32x4{l2.x, l2.y, h2.x, h2.y};
+    };
     auto read_blk = [&](const unsigned char *sa, const unsigned char *sb, int s, int b, i32x4 (&fa)[big::BLK],
                         i32x4 (&fb)[big::BLK]) {
-        fa[b] = *reinterpret_cast<const i32x4 *>(sa + fa_off[s] + 32 * b * dl::ROW);
-        if (BXM) {
-            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-            const unsigned char *p = sb + fbx_off[b] + 16 * s * dl::XROW;
-            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
-            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * dl::XROW));
-            const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
-            fb[b] = i32x4{l2.x, l2.y, h2.x, h2.y};
-        } else {
-            fb[b] = *reinterpret_cast<const i32x4 *>(sb + fb_off[s] + 32 * b * dl::ROW);
-        }
+        if (AXM) fa[b] = read_tr(sa + fax_off[b] + 16 * s * dl::XROW);
+        else fa[b] = *reinterpret_cast<const i32x4 *>(sa + fa_off[s] + 32 * b * dl::ROW);
+        if (BXM) fb[b] = read_tr(sb + fbx_off[b] + 16 * s * dl::XROW);
+        else fb[b] = *reinterpret_cast<const i32x4 *>(sb + fb_off[s] + 32 * b * dl::ROW);
     };
     auto mfma_one = [&](const i32x4 (&fa)[big::BLK], const i32x4 (&fb)[big::BLK], int i) {
         acc[i / big::BLK][i % big::BLK] = mfma16<F16>(fa[i / big::BLK], fb[i % big::BLK], acc[i / big::BLK][i % big::BLK]);
@@ -627,10 +644,11 @@ bool direct_ok(const void *p, int64_t ld, int K) {
     return aligned16(p) && ld % 8 == 0 && K % BK == 0 && (255 * ld + BK) * 2 < ((int64_t)1 << 31);
 }
 
-// B as given (K x N) read in place by the 256 x 256 kernel: 16-byte aligned,
-// row stride and N multiples of 8 (a 16-byte group never straddles N), K a
-// multiple of the 64 the kernels' slices need, and one slice's 32 rows
-// addressable with 32-bit byte offsets.
+// An operand along x (B as given, K x N; A transposed, K x M) read in place by
+// the 256 x 256 kernel: 16-byte aligned, row stride and extent (N or M)
+// multiples of 8 (a 16-byte group never straddles it), K a multiple of the 64
+// the kernels' slices need, and one slice's rows addressable with 32-bit byte
+// offsets.
 bool direct_xmajor_ok(const void *p, int64_t ld, int N, int K) {
     return aligned16(p) && ld % 8 == 0 && N % 8 == 0 && K % BK == 0 &&
            ((dl::BK - 1) * ld + big::BN) * 2 < ((int64_t)1 << 31);
@@ -656,10 +674,10 @@ bool use_big_tiles(int M, int N, int64_t ldc) {
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 int64_t gemm16_workspace_bytes(int ta, int tb, int M, int N, int K, const void *A, int64_t lda, const void *B,
-                               int64_t ldb, bool bxm) {
+                               int64_t ldb, bool axm, bool bxm) {
     const int64_t Kp = (int64_t)(K + BK - 1) / BK * BK;
     int64_t bytes = 0;
-    if (ta || !direct_ok(A, lda, K)) bytes += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
+    if (!axm && (ta || !direct_ok(A, lda, K))) bytes += ((int64_t)M * Kp * 2 + 255) / 256 * 256;
     if (!bxm && (!tb || !direct_ok(B, ldb, K))) bytes += ((int64_t)N * Kp * 2 + 255) / 256 * 256;
     return bytes;
 }
@@ -670,8 +688,11 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     const int M = g16.M, N = g16.N, K = g16.K;
     const int Kp = (K + BK - 1) / BK * BK;
     const bool big_tiles = use_big_tiles(M, N, g16.ldc);
+    // Operands along x (A transposed, B as given) are read in place by the
+    // 256 x 256 kernel when they allow it, packed otherwise.
+    const bool axm = ta && big_tiles && direct_xmajor_ok(A, g16.lda, M, K);
     const bool bxm = !tb && big_tiles && direct_xmajor_ok(B, g16.ldb, N, K);
-    const bool pa = ta || !direct_ok(A, g16.lda, K);
+    const bool pa = !axm && (ta || !direct_ok(A, g16.lda, K));
     const bool pb = !bxm && (!tb || !direct_ok(B, g16.ldb, K));
     Args16 a;
     a.M = M; a.N = N; a.K = Kp;
@@ -681,7 +702,7 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     a.B = static_cast<const uint16_t *>(B); a.ldb = g16.ldb;
     void *ws = nullptr;
     if (pa || pb) {
-        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb, bxm);
+        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb, axm, bxm);
         hipError_t e = scratch_acquire(g16.scratch, (size_t)bytes, stream, &ws);
         if (e != hipSuccess) return e;
         unsigned char *p = static_cast<unsigned char *>(ws);
@@ -712,13 +733,20 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     if (big_tiles) {
         const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
         const dim3 grid(tiles_m * tiles_n);
-        if (kind == GEMM16_F32_F16) {
-            if (bxm) hipLaunchKernelGGL((gemm16_dl_kernel<true, true>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-            else hipLaunchKernelGGL((gemm16_dl_kernel<true, false>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-        } else {
-            if (bxm) hipLaunchKernelGGL((gemm16_dl_kernel<false, true>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-            else hipLaunchKernelGGL((gemm16_dl_kernel<false, false>), grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
-        }
+        auto go = [&](auto f16, auto ax, auto bx) {
+            hipLaunchKernelGGL((gemm16_dl_kernel<decltype(f16)::value, decltype(ax)::value, decltype(bx)::value>),
+                               grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+        };
+        auto pick_b = [&](auto f16, auto ax) {
+            if (bxm) go(f16, ax, std::true_type());
+            else go(f16, ax, std::false_type());
+        };
+        auto pick_a = [&](auto f16) {
+            if (axm) pick_b(f16, std::true_type());
+            else pick_b(f16, std::false_type());
+        };
+        if (kind == GEMM16_F32_F16) pick_a(std::true_type());
+        else pick_a(std::false_type());
         e = hipGetLastError();
     } else {
         const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;

@@ -31,9 +31,10 @@
  * place.  Otherwise the operands that do not meet this are first copied into a
  * K-major, zero-padded form in the call's scratch, taken as sgemm_f32.h
  * describes ((M or N) * K rounded up to 64 elements * 2 bytes each), which
- * costs one extra pass over them.  B of the NN form (trans_b == 0) is read in
- * place by the larger-tile kernel when it is aligned as above and N is a
- * multiple of 8.
+ * costs one extra pass over them.  On grids of at least 256 tiles of 256 x 256
+ * (the larger-tile kernel) an operand given along M or N, A transposed
+ * (trans_a == 1, K x M) or B as given (trans_b == 0, K x N), is read in place
+ * too when it is aligned as above and its M or N is a multiple of 8.
  *
  * Ownership and execution: device pointers owned by the caller, asynchronous on
  * `stream`, no synchronisation, thread-safe; as sgemm_f32.

@@ -150,10 +150,11 @@ def test_gemm16_alpha_zero_and_k_zero(sg):
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
+@pytest.mark.parametrize("form", [(0, 1), (0, 0), (1, 1)], ids=["nt", "nn", "tt"])
 def test_gemm16_headline_shape(sg, kind, form):
-    """4096^3 with alpha 1.5, beta -0.5 on N(0,1) inputs stored in 16 bits: NT
-    read in place, NN through the packed path."""
+    """4096^3 with alpha 1.5, beta -0.5 on N(0,1) inputs stored in 16 bits,
+    every operand read in place by the larger-tile kernel (A transposed and B
+    as given through transposing LDS reads)."""
     ta, tb = form
     w = workloads.WORKLOADS["square4096_ab"]
     say(f"[g16_headline] kind={kind} {form}")
@@ -190,13 +191,13 @@ def test_gemm16_big_tiles_with_edges(sg, kind, form):
     assert ok, info
 
 
-@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
 def test_gemm16_big_tiles_integer_bitexact(sg, kind, form):
-    """K = 576 (a multiple of 64): with B as given (NN) the larger-tile kernel
-    reads it in place (transposing LDS reads), N = 3904 leaving a column of
-    edge tiles 64 wide."""
-    M, N, K = 4350, 3904, 576
+    """K = 576 (a multiple of 64): the larger-tile kernel reads A transposed
+    and B as given in place (transposing LDS reads); M = 4344 and N = 3904
+    leave a row of edge tiles 248 high and a column 64 wide."""
+    M, N, K = 4344, 3904, 576
     ta, tb = form
     A, B, C0 = _inputs16(M, N, K, "int4", kind, 47)
     st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0)
@@ -205,12 +206,12 @@ def test_gemm16_big_tiles_integer_bitexact(sg, kind, form):
     assert ok, info
 
 
-@pytest.mark.parametrize("form", [(0, 1), (0, 0)], ids=["nt", "nn"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("K", [8, 64, 192])
 def test_gemm16_big_tiles_short_k_bitexact(sg, K, form):
-    """The larger-tile kernel fetches three 32-deep slices ahead; with only
-    two to six slices (K padded to 64 or 192) the loads past the end repeat
-    the last slice into stages that are never read."""
+    """The larger-tile kernel loads B one 64-deep slice ahead and A two;
+    with one to three slices (K padded to 64, or 192) the first and last
+    slices' special cases (no A two ahead, nothing to load) all run."""
     M, N = 4096, 4096
     ta, tb = form
     say(f"[g16_big_short_k] K={K} {form}")

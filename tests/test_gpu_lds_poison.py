@@ -135,23 +135,25 @@ G16_SHAPES = [(4096, 4096, 8), (4096, 4096, 192), (4096, 4096, 520), (4096, 3904
               (128, 128, 64)]
 
 
-@pytest.mark.parametrize("tb", [1, 0], ids=["nt", "nn"])
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("kind", [1, 2], ids=["bf16", "f16"])
 @pytest.mark.parametrize("shape", G16_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in G16_SHAPES])
-def test_poisoned_16bit_kernels(plib, kind, shape, tb):
-    """NT (B stored N x K) and NN (B as given, K x N; read in place with
-    transposing LDS reads by the larger-tile kernel when K is a multiple of
-    64, packed otherwise)."""
+def test_poisoned_16bit_kernels(plib, kind, shape, form):
+    """All four operand forms: A transposed (K x M) and B as given (K x N)
+    are read in place with transposing LDS reads by the larger-tile kernel
+    when K is a multiple of 64, packed otherwise."""
     M, N, K = shape
-    say(f"[poison_16] kind {kind} {shape} tb={tb}")
+    ta, tb = form
+    say(f"[poison_16] kind {kind} {shape} form={form}")
     w = workloads.custom(M, N, K, dist="int4", seed=1900 + K, c0_dist="int4")
     A16, B16, C0 = workloads.make_inputs_16bit(w, kind)
+    As = np.ascontiguousarray(A16.T) if ta else A16
     Bs = np.ascontiguousarray(B16.T) if tb else B16
-    dA = torch.from_numpy(A16.view(np.int16)).cuda()
+    dA = torch.from_numpy(As.view(np.int16)).cuda()
     dB = torch.from_numpy(Bs.view(np.int16)).cuda()
     dC = torch.from_numpy(C0).cuda()
-    st = plib.gemm16_f32(kind, 0, tb, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), K, dB.data_ptr(), Bs.shape[1],
-                         ctypes.c_float(-1.0), dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    st = plib.gemm16_f32(kind, ta, tb, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), As.shape[1], dB.data_ptr(),
+                         Bs.shape[1], ctypes.c_float(-1.0), dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
     C = dC.cpu().numpy()
