@@ -256,37 +256,48 @@ constexpr int WT = 128;                          // wave tile
 constexpr int BLK = WT / 32;                     // 4 blocks per wave and direction
 }  // namespace big
 
-// Epilogue of a 256 x 256 tile in four passes of one block row (4 blocks, 64
-// values per lane): the C reads of a pass are issued together before its
+// Tile geometry of the direct-to-LDS kernel below: TS x TS tiles, 4 waves of
+// TS/2 x TS/2, BLK x BLK blocks of 32 x 32 each (TS 256: the tiles above, one
+// work-group per CU; TS 128: 2 x 2 blocks, two work-groups per CU, for grids
+// with fewer than 256 tiles of 256 x 256).
+template <int TS>
+struct TG {
+    static constexpr int BM = TS, BN = TS, WT = TS / 2, BLK = WT / 32;
+};
+
+// Epilogue of a TS x TS tile in BLK passes of one block row (BLK blocks, 16
+// BLK values per lane): the C reads of a pass are issued together before its
 // stores.  Edge tiles go through a buffer resource over the tile's valid part
 // of C (rows past M beyond its extent, columns past N out-of-range offsets).
+template <int TS>
 __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, int rows_a, int rows_b, int wm, int wn,
-                                             int h, int l32, const f32x16 (&acc)[big::BLK][big::BLK]) {
-    const bool edge = rows_a < big::BM || rows_b < big::BN;
+                                             int h, int l32, const f32x16 (&acc)[TG<TS>::BLK][TG<TS>::BLK]) {
+    using G = TG<TS>;
+    const bool edge = rows_a < G::BM || rows_b < G::BN;
     float *Cb = g.C + (int64_t)m0 * g.ldc + n0;
     const __amdgpu_buffer_rsrc_t rc = rsrc16(reinterpret_cast<const uint16_t *>(Cb),
                                              (int)(((int64_t)(rows_a - 1) * g.ldc + rows_b) * 4));
     const float alpha = g.alpha, beta = g.beta;
     auto pass = [&](int ib, auto edge_tag) {
         constexpr bool EDGE = decltype(edge_tag)::value;
-        float cv[big::BLK][16];
+        float cv[G::BLK][16];
         if (beta != 0.f) {
 #pragma unroll
-            for (int jb = 0; jb < big::BLK; ++jb)
+            for (int jb = 0; jb < G::BLK; ++jb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const int cc = wn * big::WT + 32 * jb + l32;
+                    const int rr = wm * G::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const int cc = wn * G::WT + 32 * jb + l32;
                     cv[jb][r] = EDGE ? raw_buffer_load_f32(rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0)
                                      : Cb[(int64_t)rr * g.ldc + cc];
                 }
         }
 #pragma unroll
-        for (int jb = 0; jb < big::BLK; ++jb)
+        for (int jb = 0; jb < G::BLK; ++jb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int rr = wm * big::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
-                const int cc = wn * big::WT + 32 * jb + l32;
+                const int rr = wm * G::WT + 32 * ib + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int cc = wn * G::WT + 32 * jb + l32;
                 float v = alpha * acc[ib][jb][r];
                 if (beta != 0.f) v = fmaf(beta, cv[jb][r], v);
                 if (EDGE) raw_buffer_store_f32(v, rc, cc < rows_b ? (int)((rr * g.ldc + cc) * 4) : kOutOfRange, 0, 0);
@@ -294,16 +305,19 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
             }
     };
 #pragma unroll
-    for (int ib = 0; ib < big::BLK; ++ib) {
+    for (int ib = 0; ib < G::BLK; ++ib) {
         if (edge) pass(ib, std::true_type());
         else pass(ib, std::false_type());
     }
 }
 
 // ---------------------------------------------------------------------------
-// 256 x 256 tiles with the operands copied from memory straight into LDS
+// TS x TS tiles with the operands copied from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the instruction's
 // LDS base + 16 * lane, without passing through registers), in slices of 64 k.
+// The figures below are those of TS = 256 (one work-group per CU); TS = 128
+// halves every unit and load count and runs two work-groups per CU, for grids
+// with too few 256 x 256 tiles to give every CU one.
 //
 // A slice row is 128 bytes, one whole cache line (8 chunks of 16), and one
 // load instruction fills 1 KB of LDS: 8 rows.  With slices of 32 k (64-byte
@@ -327,8 +341,8 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // else hides their latency.
 //
 // Ordering without __syncthreads (whose fence would wait for every load in
-// flight): at the top of slice t each wave waits until at most the 8 loads of
-// A of slice t+1 (its last-issued ones) are in flight, vector-memory counts
+// flight): at the top of slice t each wave waits until at most the LPO loads
+// of A of slice t+1 (its last-issued ones) are in flight, vector-memory counts
 // completing in order, and for its own LDS reads, then joins an s_barrier;
 // past it every wave's part of slice t is in LDS and every wave is done with
 // slice t-1's units.
@@ -358,21 +372,31 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 namespace dl {
 constexpr int BK = 64;                           // slice depth in elements
 constexpr int ROW = BK * 2;                      // 128 bytes
-constexpr int UNIT = big::BM * ROW;              // one operand's slice: 32 KB
 constexpr int NU = 5;                            // units in the ring
-constexpr int RPI = 1024 / ROW;                  // rows per load instruction: 8
-constexpr int LPO = big::BM / 4 / RPI;           // load instructions per wave and operand per slice: 8
+constexpr int RPI = 1024 / ROW;                  // K-major rows per load instruction: 8
 constexpr int KS = BK / 16;                      // k steps of one MFMA depth: 4
-constexpr int XROW = big::BN * 2;                // B as given: one row of k, 512 bytes
-constexpr int XRPI = 1024 / XROW;                // its rows per load instruction: 2
-constexpr int XROT = 64;                         // rotation of row k: XROT * (k % 4) bytes
-static_assert(big::BM == big::BN && NU * UNIT <= 160 * 1024, "LDS");
-static_assert(BK / 4 == XRPI * LPO, "B as given: a wave's rows of k per slice");
+constexpr int XROT = 64;                         // along x: rotation of row k, XROT * (k % 4) bytes
 }  // namespace dl
 
-// Byte offset of B element (row k, column x) in its unit, B as given.
+// Ring geometry for TS x TS tiles: a unit holds one operand's slice; a load
+// instruction fills 1 KB (8 K-major rows, or XRPI rows of k along x, each
+// XROW bytes and XLANES lanes).
+template <int TS>
+struct DLG {
+    static constexpr int UNIT = TS * dl::ROW;            // 32 KB (TS 256) or 16 KB
+    static constexpr int LPO = TS / 4 / dl::RPI;         // load instructions per wave and operand per slice
+    static constexpr int XROW = TS * 2;                  // along x: one row of k, 512 or 256 bytes
+    static constexpr int XRPI = 1024 / XROW;             // its rows per load instruction
+    static constexpr int XLANES = XROW / 16;             // lanes per row
+    static_assert(dl::NU * UNIT <= 160 * 1024, "LDS");
+    static_assert(dl::BK / 4 == XRPI * LPO, "along x: a wave's rows of k per slice");
+};
+
+// Byte offset of an along-x element (row k, column x) in its unit.
+template <int TS>
 __device__ __forceinline__ int dl_xoff(int k, int x) {
-    return k * dl::XROW + ((x * 2 + (k & 3) * dl::XROT) & (dl::XROW - 1));
+    constexpr int XROW = DLG<TS>::XROW;
+    return k * XROW + ((x * 2 + (k & 3) * dl::XROT) & (XROW - 1));
 }
 
 __device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
@@ -395,65 +419,77 @@ __device__ __forceinline__ void lds_dma16_untracked(__amdgpu_buffer_rsrc_t rs, u
 // Which load of a slice follows MFMA `slot` of k step `phase` (the first BLK
 // slots of every step hold fragment reads): 0 .. LPO-1 are B's loads of the
 // next slice, one per MFMA from the first free slot on; LPO .. 2 LPO - 1 are
-// A's loads of the slice after it, one every kAStride MFMAs after them.
-// -1: none.
+// A's loads of the slice after it, from step 1 on (TS 256: one every
+// kAStride MFMAs; TS 128, 2 free slots per step: one per MFMA).  -1: none.
 constexpr int kAStride = 4;
+template <int TS>
 __host__ __device__ constexpr int dl_load_of(int phase, int slot) {
-    const int per_step = big::BLK * big::BLK - big::BLK;        // 12 free slots per step
-    if (slot < big::BLK) return -1;
-    const int pos = phase * per_step + (slot - big::BLK);
-    if (pos < dl::LPO) return pos;
-    const int a = pos - per_step;                               // A's loads start in step 1
-    if (a < 0 || a % kAStride != 0 || a / kAStride >= dl::LPO) return -1;
-    return dl::LPO + a / kAStride;
+    constexpr int BLK = TG<TS>::BLK, LPO = DLG<TS>::LPO;
+    constexpr int per_step = BLK * BLK - BLK;                   // free slots per step
+    constexpr int a0 = per_step > LPO ? per_step : LPO;         // A's first position
+    constexpr int stride = (4 * per_step - a0) / LPO < kAStride ? (4 * per_step - a0) / LPO : kAStride;
+    static_assert(stride >= 1 && a0 + (LPO - 1) * stride < 4 * per_step, "the loads fit the slots");
+    if (slot < BLK) return -1;
+    const int pos = phase * per_step + (slot - BLK);
+    if (pos < LPO) return pos;
+    const int a = pos - a0;
+    if (a < 0 || a % stride != 0 || a / stride >= LPO) return -1;
+    return LPO + a / stride;
 }
 
-template <bool F16, bool AXM, bool BXM>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm16_dl_kernel(
-    Args16 g, int tiles_m, int tiles_n) {
-    __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * dl::UNIT];
+// Work-groups per CU: one with 256 x 256 tiles (160 KB of LDS), two with
+// 128 x 128 (80 KB each).
+template <int TS>
+constexpr int kDlPerCu = TS == 256 ? 1 : 2;
+
+template <int TS, bool F16, bool AXM, bool BXM>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kDlPerCu<TS>, kDlPerCu<TS>))) void
+gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
+    using G = TG<TS>;
+    using D = DLG<TS>;
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * D::UNIT];
     poison_lds<sizeof(smem)>(smem);
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, 4, tm, tn);
-    const int m0 = tm * big::BM, n0 = tn * big::BN;
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, TS == 256 ? 4 : 8, tm, tn);
+    const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int tid = threadIdx.x;
     // The wave index is uniform: kept in a scalar register, the LDS bases of
     // the loads need no per-load transfer from a vector register.
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
-    const int rows_a = min(big::BM, g.M - m0), rows_b = min(big::BN, g.N - n0);
+    const int rows_a = min(G::BM, g.M - m0), rows_b = min(G::BN, g.N - n0);
     const uint16_t *Ab = AXM ? g.A + m0 : g.A + (int64_t)m0 * g.lda;
     const uint16_t *Bb = BXM ? g.B + n0 : g.B + (int64_t)n0 * g.ldb;
     // Any transposing read needs every load into LDS untracked (see above).
     constexpr bool UNTRACKED = AXM || BXM;
 
-    // Load instruction j of this wave covers rows wave*64 + 8 j + lane/8; the
-    // lane's position lane % 8 in its row holds chunk dl_pos(row, lane % 8).
+    // Load instruction j of this wave covers rows wave*TS/4 + 8 j + lane/8;
+    // the lane's position lane % 8 in its row holds chunk dl_pos(row, lane % 8).
     // An operand as given along x (A transposed, K x M; B as given, K x N):
-    // rows of k wave*16 + 2 j + lane/32, the lane's position lane % 32 holding
-    // the 16-byte chunk that the row's rotation puts there (x past M or N gets
-    // an out-of-range offset and arrives as zeros).  Both fill 8 KB per wave
-    // of their unit.
-    auto offsets = [&](bool xm, int64_t ld, int rows, int (&off)[dl::LPO]) {
+    // rows of k wave*16 + XRPI j + lane/XLANES, the lane's position
+    // lane % XLANES holding the 16-byte chunk that the row's rotation puts
+    // there (x past M or N gets an out-of-range offset and arrives as zeros).
+    // Both fill a quarter of their unit per wave.
+    auto offsets = [&](bool xm, int64_t ld, int rows, int (&off)[D::LPO]) {
 #pragma unroll
-        for (int j = 0; j < dl::LPO; ++j) {
+        for (int j = 0; j < D::LPO; ++j) {
             if (xm) {
-                const int k = wave * (dl::BK / 4) + dl::XRPI * j + (lane >> 5);
-                const int cx = ((lane & 31) - (k & 3) * (dl::XROT / 16)) & 31;
+                const int k = wave * (dl::BK / 4) + D::XRPI * j + lane / D::XLANES;
+                const int cx = (lane % D::XLANES - (k & 3) * (dl::XROT / 16)) & (D::XLANES - 1);
                 off[j] = 8 * cx < rows ? (k * (int)ld + 8 * cx) * 2 : kOutOfRange;
             } else {
-                const int r = wave * 64 + dl::RPI * j + (lane >> 3);
+                const int r = wave * (G::BM / 4) + dl::RPI * j + (lane >> 3);
                 off[j] = (r * (int)ld + dl_pos(r, lane & 7) * 8) * 2;
             }
         }
     };
-    int offa[dl::LPO], offb[dl::LPO];
+    int offa[D::LPO], offb[D::LPO];
     offsets(AXM, g.lda, rows_a, offa);
     offsets(BXM, g.ldb, rows_b, offb);
     // Rows past M (N) lie beyond the resource's extent and arrive as zeros.
     auto issue_a = [&](int slice, int unit, int j) {
-        unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
+        unsigned char *dst = smem + unit * D::UNIT + wave * (D::UNIT / 4) + j * 1024;
         if (AXM) {
             const __amdgpu_buffer_rsrc_t rsa =
                 rsrc16(Ab + (int64_t)slice * dl::BK * g.lda, (int)(((dl::BK - 1) * g.lda + rows_a) * 2));
@@ -466,7 +502,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     };
     auto issue_b = [&](int slice, int unit, int j) {
-        unsigned char *dst = smem + unit * dl::UNIT + wave * (dl::UNIT / 4) + j * 1024;
+        unsigned char *dst = smem + unit * D::UNIT + wave * (D::UNIT / 4) + j * 1024;
         if (BXM) {
             const __amdgpu_buffer_rsrc_t rsb =
                 rsrc16(Bb + (int64_t)slice * dl::BK * g.ldb, (int)(((dl::BK - 1) * g.ldb + rows_b) * 2));
@@ -479,71 +515,71 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     };
 
-    f32x16 acc[big::BLK][big::BLK];
+    f32x16 acc[G::BLK][G::BLK];
 #pragma unroll
-    for (int i = 0; i < big::BLK; ++i)
+    for (int i = 0; i < G::BLK; ++i)
 #pragma unroll
-        for (int j = 0; j < big::BLK; ++j)
+        for (int j = 0; j < G::BLK; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // Fragment addresses (unit-relative).  K-major: block b of k step s is
-    // row x = w*128 + 32 b + l32 of the operand, chunk 2 s + h; the rows of
+    // row x = w*WT + 32 b + l32 of the operand, chunk 2 s + h; the rows of
     // the four blocks differ by 32, which leaves (x >> 1) & 7 alone, so the
     // block only adds 32 rows.  Along x (the MFMA takes A and B fragments of
     // the same shape): the two transposing reads q = 0, 1 of k step s, block
     // b; in lane group g16 = lane / 16 (k half lane / 32, x half g16 % 2),
     // lane 4 j + qq points at row 16 s + 8 h + 4 q + j, x from 32 b +
-    // 16 (g16 % 2) + 4 qq of the wave's 128; the step and q only add whole rows.
-    int fa_off[dl::KS], fb_off[dl::KS], fax_off[big::BLK], fbx_off[big::BLK];
+    // 16 (g16 % 2) + 4 qq of the wave's WT; the step and q only add whole rows.
+    int fa_off[dl::KS], fb_off[dl::KS], fax_off[G::BLK], fbx_off[G::BLK];
 #pragma unroll
     for (int s = 0; s < dl::KS; ++s) {
         const int pos = dl_pos(l32, 2 * s + h) * 16;
-        fa_off[s] = (wm * big::WT + l32) * dl::ROW + pos;
-        fb_off[s] = (wn * big::WT + l32) * dl::ROW + pos;
+        fa_off[s] = (wm * G::WT + l32) * dl::ROW + pos;
+        fb_off[s] = (wn * G::WT + l32) * dl::ROW + pos;
     }
 #pragma unroll
-    for (int b = 0; b < big::BLK; ++b) {
+    for (int b = 0; b < G::BLK; ++b) {
         const int k = 8 * h + ((lane >> 2) & 3);
         const int xq = 32 * b + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-        fax_off[b] = dl_xoff(k, wm * big::WT + xq);
-        fbx_off[b] = dl_xoff(k, wn * big::WT + xq);
+        fax_off[b] = dl_xoff<TS>(k, wm * G::WT + xq);
+        fbx_off[b] = dl_xoff<TS>(k, wn * G::WT + xq);
     }
     // Eight k at one x from two transposing reads, four rows apart.
     auto read_tr = [&](const unsigned char *p) {
         typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)p);
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * dl::XROW));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(p + 4 * D::XROW));
         const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
         return i32x4{l2.x, l2.y, h2.x, h2.y};
     };
-    auto read_blk = [&](const unsigned char *sa, const unsigned char *sb, int s, int b, i32x4 (&fa)[big::BLK],
-                        i32x4 (&fb)[big::BLK]) {
-        if (AXM) fa[b] = read_tr(sa + fax_off[b] + 16 * s * dl::XROW);
+    auto read_blk = [&](const unsigned char *sa, const unsigned char *sb, int s, int b, i32x4 (&fa)[G::BLK],
+                        i32x4 (&fb)[G::BLK]) {
+        if (AXM) fa[b] = read_tr(sa + fax_off[b] + 16 * s * D::XROW);
         else fa[b] = *reinterpret_cast<const i32x4 *>(sa + fa_off[s] + 32 * b * dl::ROW);
-        if (BXM) fb[b] = read_tr(sb + fbx_off[b] + 16 * s * dl::XROW);
+        if (BXM) fb[b] = read_tr(sb + fbx_off[b] + 16 * s * D::XROW);
         else fb[b] = *reinterpret_cast<const i32x4 *>(sb + fb_off[s] + 32 * b * dl::ROW);
     };
-    auto mfma_one = [&](const i32x4 (&fa)[big::BLK], const i32x4 (&fb)[big::BLK], int i) {
-        acc[i / big::BLK][i % big::BLK] = mfma16<F16>(fa[i / big::BLK], fb[i % big::BLK], acc[i / big::BLK][i % big::BLK]);
+    auto mfma_one = [&](const i32x4 (&fa)[G::BLK], const i32x4 (&fb)[G::BLK], int i) {
+        acc[i / G::BLK][i % G::BLK] = mfma16<F16>(fa[i / G::BLK], fb[i % G::BLK], acc[i / G::BLK][i % G::BLK]);
     };
 
     const int nk = g.K / dl::BK;
     // Before the first slice: A and B of slice 0, A of slice 1 (the last
     // issued, so that slice 0 can start while it is in flight).
 #pragma unroll
-    for (int j = 0; j < dl::LPO; ++j) issue_a(0, 0, j);
+    for (int j = 0; j < D::LPO; ++j) issue_a(0, 0, j);
 #pragma unroll
-    for (int j = 0; j < dl::LPO; ++j) issue_b(0, 1, j);
+    for (int j = 0; j < D::LPO; ++j) issue_b(0, 1, j);
     if (nk > 1) {
 #pragma unroll
-        for (int j = 0; j < dl::LPO; ++j) issue_a(1, 2, j);
+        for (int j = 0; j < D::LPO; ++j) issue_a(1, 2, j);
     }
 
     // Fragments of the even (x) and odd (y) k steps.
-    i32x4 fxa[big::BLK], fxb[big::BLK], fya[big::BLK], fyb[big::BLK];
+    i32x4 fxa[G::BLK], fxb[G::BLK], fya[G::BLK], fyb[G::BLK];
 #pragma unroll
-    for (int b = 0; b < big::BLK; ++b) {
+    for (int b = 0; b < G::BLK; ++b) {
         fya[b] = i32x4{0, 0, 0, 0};
         fyb[b] = i32x4{0, 0, 0, 0};
     }
@@ -560,26 +596,26 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         constexpr bool WAIT8 = decltype(wait8_tag)::value;
         constexpr bool LB = decltype(lb_tag)::value;
         constexpr bool LA = decltype(la_tag)::value;
-        // vmcnt(8) or vmcnt(0), and lgkmcnt(0); expcnt not waited on.
-        if (WAIT8) __builtin_amdgcn_s_waitcnt((0 << 14) | (0 << 8) | (7 << 4) | 8);
+        // vmcnt(LPO) or vmcnt(0), and lgkmcnt(0); expcnt not waited on.
+        if (WAIT8) __builtin_amdgcn_s_waitcnt((0 << 14) | (0 << 8) | (7 << 4) | D::LPO);
         else __builtin_amdgcn_s_waitcnt((0 << 14) | (0 << 8) | (7 << 4) | 0);
         __builtin_amdgcn_s_barrier();
-        const unsigned char *sa = smem + ua * dl::UNIT, *sb = smem + ub * dl::UNIT;
+        const unsigned char *sa = smem + ua * D::UNIT, *sb = smem + ub * D::UNIT;
         const int unit_b1 = ub + 2 < dl::NU ? ub + 2 : ub + 2 - dl::NU;   // B of slice t+1
         const int unit_a2 = ua + 4 < dl::NU ? ua + 4 : ua + 4 - dl::NU;   // A of slice t+2
-        auto step = [&](auto phase_tag, const i32x4 (&ux)[big::BLK], const i32x4 (&uy)[big::BLK],
-                        i32x4 (&rx)[big::BLK], i32x4 (&ry)[big::BLK]) {
+        auto step = [&](auto phase_tag, const i32x4 (&ux)[G::BLK], const i32x4 (&uy)[G::BLK],
+                        i32x4 (&rx)[G::BLK], i32x4 (&ry)[G::BLK]) {
             constexpr int P = decltype(phase_tag)::value;
 #pragma unroll
-            for (int i = 0; i < big::BLK * big::BLK; ++i) {
+            for (int i = 0; i < G::BLK * G::BLK; ++i) {
                 mfma_one(ux, uy, i);
                 __builtin_amdgcn_sched_barrier(0);
-                if (i < big::BLK) {
+                if (i < G::BLK) {
                     read_blk(sa, sb, P, i, rx, ry);
                 } else {
-                    const int l = dl_load_of(P, i);
-                    if (LB && l >= 0 && l < dl::LPO) issue_b(t + 1, unit_b1, l);
-                    else if (LA && l >= dl::LPO) issue_a(t + 2, unit_a2, l - dl::LPO);
+                    const int l = dl_load_of<TS>(P, i);
+                    if (LB && l >= 0 && l < D::LPO) issue_b(t + 1, unit_b1, l);
+                    else if (LA && l >= D::LPO) issue_a(t + 2, unit_a2, l - D::LPO);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
@@ -601,9 +637,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
     slice(t, no(), no(), no());
 #pragma unroll
-    for (int i = 0; i < big::BLK * big::BLK; ++i) mfma_one(fya, fyb, i);
+    for (int i = 0; i < G::BLK * G::BLK; ++i) mfma_one(fya, fyb, i);
 
-    big_epilogue(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
+    big_epilogue<TS>(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
 }
 
 // K-major, K-padded copy of a 16-bit operand: dst[x * Kp + k] = op(x, k) for
@@ -645,7 +681,7 @@ bool direct_ok(const void *p, int64_t ld, int K) {
 }
 
 // An operand along x (B as given, K x N; A transposed, K x M) read in place by
-// the 256 x 256 kernel: 16-byte aligned, row stride and extent (N or M)
+// the direct-to-LDS kernel: 16-byte aligned, row stride and extent (N or M)
 // multiples of 8 (a 16-byte group never straddles it), K a multiple of the 64
 // the kernels' slices need, and one slice's rows addressable with 32-bit byte
 // offsets.
@@ -664,11 +700,15 @@ hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint
 
 }  // namespace
 
+// The direct-to-LDS kernel's epilogue addresses a tile of C with 32-bit
+// offsets (bounded by a 256-row tile).
+bool c_tile_fits(int64_t ldc) { return (255 * ldc + big::BN) * 4 < ((int64_t)1 << 31); }
+
 // 256 x 256 tiles when they still give every one of the 256 CUs a tile, and
 // 256 rows of C are addressable with 32-bit byte offsets (edge epilogue).
 bool use_big_tiles(int M, int N, int64_t ldc) {
     const int64_t tiles = (int64_t)((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
-    return tiles >= 256 && (255 * ldc + big::BN) * 4 < ((int64_t)1 << 31);
+    return tiles >= 256 && c_tile_fits(ldc);
 }
 
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
@@ -687,11 +727,15 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     const void *A = g16.A, *B = g16.B;
     const int M = g16.M, N = g16.N, K = g16.K;
     const int Kp = (K + BK - 1) / BK * BK;
+    // The direct-to-LDS kernel with 256 x 256 tiles when they fill the
+    // device, with 128 x 128 otherwise; the register-staged 128 x 128 kernel
+    // only when C's stride is too wide for its 32-bit tile offsets.
     const bool big_tiles = use_big_tiles(M, N, g16.ldc);
+    const bool ring = big_tiles || c_tile_fits(g16.ldc);
     // Operands along x (A transposed, B as given) are read in place by the
-    // 256 x 256 kernel when they allow it, packed otherwise.
-    const bool axm = ta && big_tiles && direct_xmajor_ok(A, g16.lda, M, K);
-    const bool bxm = !tb && big_tiles && direct_xmajor_ok(B, g16.ldb, N, K);
+    // direct-to-LDS kernel when they allow it, packed otherwise.
+    const bool axm = ta && ring && direct_xmajor_ok(A, g16.lda, M, K);
+    const bool bxm = !tb && ring && direct_xmajor_ok(B, g16.ldb, N, K);
     const bool pa = !axm && (ta || !direct_ok(A, g16.lda, K));
     const bool pb = !bxm && (!tb || !direct_ok(B, g16.ldb, K));
     Args16 a;
@@ -730,23 +774,28 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
         }
     }
     hipError_t e;
-    if (big_tiles) {
-        const int tiles_m = (M + big::BM - 1) / big::BM, tiles_n = (N + big::BN - 1) / big::BN;
-        const dim3 grid(tiles_m * tiles_n);
-        auto go = [&](auto f16, auto ax, auto bx) {
-            hipLaunchKernelGGL((gemm16_dl_kernel<decltype(f16)::value, decltype(ax)::value, decltype(bx)::value>),
-                               grid, dim3(NT), 0, stream, a, tiles_m, tiles_n);
+    if (ring) {
+        auto go = [&](auto ts, auto f16, auto ax, auto bx) {
+            constexpr int TS = decltype(ts)::value;
+            const int tiles_m = (M + TS - 1) / TS, tiles_n = (N + TS - 1) / TS;
+            hipLaunchKernelGGL(
+                (gemm16_dl_kernel<TS, decltype(f16)::value, decltype(ax)::value, decltype(bx)::value>),
+                dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a, tiles_m, tiles_n);
         };
-        auto pick_b = [&](auto f16, auto ax) {
-            if (bxm) go(f16, ax, std::true_type());
-            else go(f16, ax, std::false_type());
+        auto pick_b = [&](auto ts, auto f16, auto ax) {
+            if (bxm) go(ts, f16, ax, std::true_type());
+            else go(ts, f16, ax, std::false_type());
         };
-        auto pick_a = [&](auto f16) {
-            if (axm) pick_b(f16, std::true_type());
-            else pick_b(f16, std::false_type());
+        auto pick_a = [&](auto ts, auto f16) {
+            if (axm) pick_b(ts, f16, std::true_type());
+            else pick_b(ts, f16, std::false_type());
         };
-        if (kind == GEMM16_F32_F16) pick_a(std::true_type());
-        else pick_a(std::false_type());
+        auto pick_f = [&](auto ts) {
+            if (kind == GEMM16_F32_F16) pick_a(ts, std::true_type());
+            else pick_a(ts, std::false_type());
+        };
+        if (big_tiles) pick_f(std::integral_constant<int, 256>());
+        else pick_f(std::integral_constant<int, 128>());
         e = hipGetLastError();
     } else {
         const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
