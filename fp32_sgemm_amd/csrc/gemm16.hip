@@ -731,7 +731,7 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     // device, with 128 x 128 otherwise; the register-staged 128 x 128 kernel
     // only when C's stride is too wide for its 32-bit tile offsets.
     const bool big_tiles = use_big_tiles(M, N, g16.ldc);
-    const bool ring = big_tiles || c_tile_fits(g16.ldc);
+    const bool ring = c_tile_fits(g16.ldc);
     // Operands along x (A transposed, B as given) are read in place by the
     // direct-to-LDS kernel when they allow it, packed otherwise.
     const bool axm = ta && ring && direct_xmajor_ok(A, g16.lda, M, K);

@@ -31,10 +31,11 @@
  * place.  Otherwise the operands that do not meet this are first copied into a
  * K-major, zero-padded form in the call's scratch, taken as sgemm_f32.h
  * describes ((M or N) * K rounded up to 64 elements * 2 bytes each), which
- * costs one extra pass over them.  On grids of at least 256 tiles of 256 x 256
- * (the larger-tile kernel) an operand given along M or N, A transposed
- * (trans_a == 1, K x M) or B as given (trans_b == 0, K x N), is read in place
- * too when it is aligned as above and its M or N is a multiple of 8.
+ * costs one extra pass over them.  An operand given along M or N, A
+ * transposed (trans_a == 1, K x M) or B as given (trans_b == 0, K x N), is
+ * read in place too when it is aligned as above, its M or N is a multiple of
+ * 8 and ldc is below about 2.1 million (256 rows of C addressable with 32-bit
+ * byte offsets).
  *
  * Ownership and execution: device pointers owned by the caller, asynchronous on
  * `stream`, no synchronisation, thread-safe; as sgemm_f32.

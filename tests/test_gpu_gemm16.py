@@ -46,20 +46,25 @@ def _dev16(X, ld, offset=0):
     return buf, buf.data_ptr() + 2 * offset
 
 
-def run16(sg, kind, ta, tb, A, B, C0, alpha, beta, pad=(0, 0), offs=(0, 0), c_fill=np.nan):
+def run16(sg, kind, ta, tb, A, B, C0, alpha, beta, pad=(0, 0), offs=(0, 0), c_fill=np.nan, ldc=None):
     """A (M x K) and B (K x N) are op(A) and op(B) as uint16 patterns."""
     M, K = A.shape
     N = B.shape[1]
     As, Bs = _stored(A, ta), _stored(B, tb)
     lda, ldb = max(As.shape[1], 1) + pad[0], max(Bs.shape[1], 1) + pad[1]
+    ldc = max(N, 1) if ldc is None else ldc
     bA, pA = _dev16(As, lda, offs[0])
     bB, pB = _dev16(Bs, ldb, offs[1])
     Cinit = C0 if C0 is not None else np.full((M, N), c_fill, np.float32)
-    bC, pC, _ = to_device_padded(Cinit, max(N, 1), fill=np.float32(-7.25))
-    st = sg.gemm16_f32(kind, ta, tb, M, N, K, float(alpha), pA, lda, pB, ldb, float(beta), pC, max(N, 1),
+    bC, pC, _ = to_device_padded(Cinit, ldc, fill=np.float32(-7.25))
+    st = sg.gemm16_f32(kind, ta, tb, M, N, K, float(alpha), pA, lda, pB, ldb, float(beta), pC, ldc,
                        torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
-    return st, from_device_padded(bC, M, N, max(N, 1)), As, Bs
+    if ldc > N and M > 1:
+        # The gap between one row of C and the next is left alone.
+        gap = bC[N:N + (M - 1) * ldc].view(M - 1, ldc)[:, :ldc - N].cpu().numpy()
+        assert np.all(gap == np.float32(-7.25)), "C written between its rows"
+    return st, from_device_padded(bC, M, N, ldc), As, Bs
 
 
 def _inputs16(M, N, K, dist, kind, seed):
@@ -126,6 +131,25 @@ def test_gemm16_misaligned_and_padded_strides(sg, kind):
     st, C, As, Bs = run16(sg, kind, 0, 1, A, B, C0, 0.5, 0.25, pad=(3, 5), offs=(1, 3))
     assert st == 0
     ok, info = check16(C, As, Bs, kind, 0, 1, 0.5, 0.25, C0, exact=False)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("K", [200, 256])
+def test_gemm16_c_stride_past_32bit_tile_offsets(sg, kind, form, K):
+    """ldc = 2,200,000: a 256-row tile of C would span more than 2 GiB, past
+    the direct-to-LDS kernel's 32-bit epilogue offsets, so the register-staged
+    kernel (64-bit C offsets) takes the product, here on 5 rows of C (K = 256
+    with NT reads the operands in place, the other cases pack them first);
+    the gaps between the rows stay untouched."""
+    M, N = 5, 300
+    ta, tb = form
+    say(f"[g16_wide_ldc] kind={kind} {form} K={K}")
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 1700 + K + 2 * ta + tb)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0, ldc=2_200_000)
+    assert st == 0
+    ok, info = check16(C, As, Bs, kind, ta, tb, 1.0, -1.0, C0, exact=True)
     assert ok, info
 
 
