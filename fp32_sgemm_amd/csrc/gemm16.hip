@@ -258,8 +258,9 @@ constexpr int BLK = WT / 32;                     // 4 blocks per wave and direct
 
 // Tile geometry of the direct-to-LDS kernel below: TS x TS tiles, 4 waves of
 // TS/2 x TS/2, BLK x BLK blocks of 32 x 32 each (TS 256: the tiles above, one
-// work-group per CU; TS 128: 2 x 2 blocks, two work-groups per CU, for grids
-// with fewer than 256 tiles of 256 x 256).
+// work-group per CU; TS 192: 3 x 3 blocks, one work-group per CU; TS 128:
+// 2 x 2 blocks, two work-groups per CU; the smaller two for grids with too
+// few tiles of 256 x 256 to fill the device).
 template <int TS>
 struct TG {
     static constexpr int BM = TS, BN = TS, WT = TS / 2, BLK = WT / 32;
@@ -315,9 +316,9 @@ __device__ __forceinline__ void big_epilogue(const Args16 &g, int m0, int n0, in
 // TS x TS tiles with the operands copied from memory straight into LDS
 // (buffer_load_dwordx4 ... lds: each lane's 16 bytes land at the instruction's
 // LDS base + 16 * lane, without passing through registers), in slices of 64 k.
-// The figures below are those of TS = 256 (one work-group per CU); TS = 128
-// halves every unit and load count and runs two work-groups per CU, for grids
-// with too few 256 x 256 tiles to give every CU one.
+// The figures below are those of TS = 256 (one work-group per CU); TS = 192
+// and 128 scale every unit and load count by 3/4 and 1/2, and TS = 128 runs
+// two work-groups per CU.
 //
 // A slice row is 128 bytes, one whole cache line (8 chunks of 16), and one
 // load instruction fills 1 KB of LDS: 8 rows.  With slices of 32 k (64-byte
@@ -375,28 +376,37 @@ constexpr int ROW = BK * 2;                      // 128 bytes
 constexpr int NU = 5;                            // units in the ring
 constexpr int RPI = 1024 / ROW;                  // K-major rows per load instruction: 8
 constexpr int KS = BK / 16;                      // k steps of one MFMA depth: 4
-constexpr int XROT = 64;                         // along x: rotation of row k, XROT * (k % 4) bytes
 }  // namespace dl
 
 // Ring geometry for TS x TS tiles: a unit holds one operand's slice; a load
-// instruction fills 1 KB (8 K-major rows, or XRPI rows of k along x, each
-// XROW bytes and XLANES lanes).
+// instruction fills 1 KB (8 K-major rows of 128 bytes; along x, the next 1024
+// bytes of the wave's rows of k, XROW bytes each, laid end to end).
 template <int TS>
 struct DLG {
-    static constexpr int UNIT = TS * dl::ROW;            // 32 KB (TS 256) or 16 KB
+    static constexpr int UNIT = TS * dl::ROW;            // 32, 24 or 16 KB
     static constexpr int LPO = TS / 4 / dl::RPI;         // load instructions per wave and operand per slice
-    static constexpr int XROW = TS * 2;                  // along x: one row of k, 512 or 256 bytes
-    static constexpr int XRPI = 1024 / XROW;             // its rows per load instruction
-    static constexpr int XLANES = XROW / 16;             // lanes per row
+    static constexpr int XROW = TS * 2;                  // along x: one row of k, 512, 384 or 256 bytes
+    static constexpr int XCH = XROW / 16;                // its 16-byte chunks
     static_assert(dl::NU * UNIT <= 160 * 1024, "LDS");
-    static_assert(dl::BK / 4 == XRPI * LPO, "along x: a wave's rows of k per slice");
+    static_assert(dl::BK / 4 * XROW == LPO * 1024, "along x: a wave's 16 rows of k fill its LPO loads");
 };
+
+// Along x, row k is rotated by dl_xrot(k) bytes (a multiple of 64) so that the
+// four consecutive rows one half-wave's transposing read touches fall in four
+// different quarters of the 64 banks: 64 (k % 4) bytes for rows of 512 and 256
+// bytes (a multiple of the 256 bank bytes apart), 64 ((k / 2) % 2) for rows of
+// 384 (alternately half the banks apart), the only pattern of this form that
+// leaves no conflict at every x a read starts at.
+template <int TS>
+__device__ __forceinline__ int dl_xrot(int k) {
+    return TS == 192 ? 64 * ((k >> 1) & 1) : 64 * (k & 3);
+}
 
 // Byte offset of an along-x element (row k, column x) in its unit.
 template <int TS>
 __device__ __forceinline__ int dl_xoff(int k, int x) {
     constexpr int XROW = DLG<TS>::XROW;
-    return k * XROW + ((x * 2 + (k & 3) * dl::XROT) & (XROW - 1));
+    return k * XROW + (x * 2 + dl_xrot<TS>(k)) % XROW;
 }
 
 __device__ __forceinline__ int dl_pos(int row, int c) { return c ^ ((row >> 1) & 7); }
@@ -419,8 +429,9 @@ __device__ __forceinline__ void lds_dma16_untracked(__amdgpu_buffer_rsrc_t rs, u
 // Which load of a slice follows MFMA `slot` of k step `phase` (the first BLK
 // slots of every step hold fragment reads): 0 .. LPO-1 are B's loads of the
 // next slice, one per MFMA from the first free slot on; LPO .. 2 LPO - 1 are
-// A's loads of the slice after it, from step 1 on (TS 256: one every
-// kAStride MFMAs; TS 128, 2 free slots per step: one per MFMA).  -1: none.
+// A's loads of the slice after it, once B's are out (TS 256: one every
+// kAStride MFMAs; TS 192: every third; TS 128, 2 free slots per step: one
+// per MFMA).  -1: none.
 constexpr int kAStride = 4;
 template <int TS>
 __host__ __device__ constexpr int dl_load_of(int phase, int slot) {
@@ -437,10 +448,10 @@ __host__ __device__ constexpr int dl_load_of(int phase, int slot) {
     return LPO + a / stride;
 }
 
-// Work-groups per CU: one with 256 x 256 tiles (160 KB of LDS), two with
-// 128 x 128 (80 KB each).
+// Work-groups per CU: one with 256 x 256 tiles (160 KB of LDS) or 192 x 192
+// (120 KB), two with 128 x 128 (80 KB each).
 template <int TS>
-constexpr int kDlPerCu = TS == 256 ? 1 : 2;
+constexpr int kDlPerCu = TS == 128 ? 2 : 1;
 
 template <int TS, bool F16, bool AXM, bool BXM>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(kDlPerCu<TS>, kDlPerCu<TS>))) void
@@ -450,7 +461,7 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
     __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * D::UNIT];
     poison_lds<sizeof(smem)>(smem);
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, TS == 256 ? 4 : 8, tm, tn);
+    tile_of_block(blockIdx.x, tiles_m, tiles_n, TS == 128 ? 8 : 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
     const int tid = threadIdx.x;
     // The wave index is uniform: kept in a scalar register, the LDS bases of
@@ -467,16 +478,19 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
     // Load instruction j of this wave covers rows wave*TS/4 + 8 j + lane/8;
     // the lane's position lane % 8 in its row holds chunk dl_pos(row, lane % 8).
     // An operand as given along x (A transposed, K x M; B as given, K x N):
-    // rows of k wave*16 + XRPI j + lane/XLANES, the lane's position
-    // lane % XLANES holding the 16-byte chunk that the row's rotation puts
-    // there (x past M or N gets an out-of-range offset and arrives as zeros).
-    // Both fill a quarter of their unit per wave.
+    // the wave's rows of k wave*16 .. wave*16 + 15 lie end to end, and the
+    // lane's 16 bytes, byte 1024 j + 16 lane of them, are position p of row
+    // k, which holds the chunk that the row's rotation puts there (x past M
+    // or N gets an out-of-range offset and arrives as zeros).  Both fill a
+    // quarter of their unit per wave.
     auto offsets = [&](bool xm, int64_t ld, int rows, int (&off)[D::LPO]) {
 #pragma unroll
         for (int j = 0; j < D::LPO; ++j) {
             if (xm) {
-                const int k = wave * (dl::BK / 4) + D::XRPI * j + lane / D::XLANES;
-                const int cx = (lane % D::XLANES - (k & 3) * (dl::XROT / 16)) & (D::XLANES - 1);
+                const int b = 1024 * j + 16 * lane;
+                const int k = wave * (dl::BK / 4) + b / D::XROW;
+                const int p = b % D::XROW / 16;
+                const int cx = (p - dl_xrot<TS>(k) / 16 + D::XCH) % D::XCH;
                 off[j] = 8 * cx < rows ? (k * (int)ld + 8 * cx) * 2 : kOutOfRange;
             } else {
                 const int r = wave * (G::BM / 4) + dl::RPI * j + (lane >> 3);
@@ -704,11 +718,39 @@ hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint
 // offsets (bounded by a 256-row tile).
 bool c_tile_fits(int64_t ldc) { return (255 * ldc + big::BN) * 4 < ((int64_t)1 << 31); }
 
-// 256 x 256 tiles when they still give every one of the 256 CUs a tile, and
-// 256 rows of C are addressable with 32-bit byte offsets (edge epilogue).
-bool use_big_tiles(int M, int N, int64_t ldc) {
-    const int64_t tiles = (int64_t)((M + big::BM - 1) / big::BM) * ((N + big::BN - 1) / big::BN);
-    return tiles >= 256 && c_tile_fits(ldc);
+namespace {
+
+// Time per unit of K of one tile size's grid, from measurement (bf16, beta 0,
+// nanoseconds per k): `slots` work-groups run at once (256 CUs times the
+// work-groups per CU); each whole round costs `full`; a last partial round
+// costs `alone` while it fills at most `knee` of the slots (its tiles run at
+// the speed of a CU with little contention for memory, and the rate of one
+// tile does not depend on how many others run), rising linearly to `full`.
+struct RingCost {
+    int slots;
+    double full, alone, knee;
+    double of(int64_t tiles) const {
+        const int64_t rem = tiles % slots;
+        double t = (double)(tiles / slots) * full;
+        if (rem > 0) {
+            const double fill = (double)rem / slots;
+            t += fill <= knee ? alone : alone + (full - alone) * (fill - knee) / (1.0 - knee);
+        }
+        return t;
+    }
+};
+
+}  // namespace
+
+// Tile size of the direct-to-LDS kernel: the one with the least estimated
+// time (ties to the larger tile).
+int gemm16_ring_tile(int M, int N) {
+    auto tiles = [&](int ts) { return (int64_t)((M + ts - 1) / ts) * ((N + ts - 1) / ts); };
+    const double t256 = RingCost{256, 25.7, 19.5, 0.6}.of(tiles(256));
+    const double t192 = RingCost{256, 15.0, 12.7, 0.5}.of(tiles(192));
+    const double t128 = RingCost{512, 14.7, 10.5, 0.5}.of(tiles(128));
+    if (t256 <= t192 && t256 <= t128) return 256;
+    return t192 <= t128 ? 192 : 128;
 }
 
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
@@ -727,10 +769,9 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     const void *A = g16.A, *B = g16.B;
     const int M = g16.M, N = g16.N, K = g16.K;
     const int Kp = (K + BK - 1) / BK * BK;
-    // The direct-to-LDS kernel with 256 x 256 tiles when they fill the
-    // device, with 128 x 128 otherwise; the register-staged 128 x 128 kernel
-    // only when C's stride is too wide for its 32-bit tile offsets.
-    const bool big_tiles = use_big_tiles(M, N, g16.ldc);
+    // The direct-to-LDS kernel, its tile size from gemm16_ring_tile; the
+    // register-staged 128 x 128 kernel only when C's stride is too wide for
+    // the former's 32-bit tile offsets.
     const bool ring = c_tile_fits(g16.ldc);
     // Operands along x (A transposed, B as given) are read in place by the
     // direct-to-LDS kernel when they allow it, packed otherwise.
@@ -794,7 +835,9 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             if (kind == GEMM16_F32_F16) pick_a(ts, std::true_type());
             else pick_a(ts, std::false_type());
         };
-        if (big_tiles) pick_f(std::integral_constant<int, 256>());
+        const int ts = gemm16_ring_tile(M, N);
+        if (ts == 256) pick_f(std::integral_constant<int, 256>());
+        else if (ts == 192) pick_f(std::integral_constant<int, 192>());
         else pick_f(std::integral_constant<int, 128>());
         e = hipGetLastError();
     } else {

@@ -74,8 +74,8 @@ hipError_t launch_scale_c(const GemmArgs &g, hipStream_t stream);
 // 16-bit operands; kind is GEMM16_F32_BF16 or GEMM16_F32_F16.
 hipError_t launch_gemm16(int kind, const GemmArgs &g, hipStream_t stream);
 int64_t gemm16_grid(int M, int N);
-// Whether the 256 x 256 tile kernel takes the product (else 128 x 128).
-bool use_big_tiles(int M, int N, int64_t ldc);
+// Tile size (256, 192 or 128) of the direct-to-LDS kernel for an M x N grid.
+int gemm16_ring_tile(int M, int N);
 
 // Scratch of at least `bytes` for the kernels a launcher is about to enqueue on
 // `stream` (sgemm_scratch.hip), and its release after them (stream-ordered; a

@@ -202,11 +202,12 @@ def test_gemm16_ragged_large_integer(sg, kind):
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_gemm16_big_tiles_with_edges(sg, kind, form):
-    """Shapes with at least 256 tiles of 256 x 256 (the larger-tile kernel)
-    whose M and N are not tile multiples, beta != 0 (the edge epilogue reads
-    and writes C through the buffer resource), every element checked."""
+    """A grid of 256 tiles of 256 x 256 (the larger tile) whose M and N are
+    not tile multiples (edge tiles 160 and 120 wide), beta != 0 (the edge
+    epilogue reads and writes C through the buffer resource), every element
+    checked."""
     ta, tb = form
-    M, N, K = 4100, 4000, 256
+    M, N, K = 4000, 3960, 256
     say(f"[g16_big_edges] kind={kind} {form}")
     A, B, C0 = _inputs16(M, N, K, "uniform", kind, 45 + 2 * ta + tb)
     st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.5, -0.5)
@@ -219,14 +220,50 @@ def test_gemm16_big_tiles_with_edges(sg, kind, form):
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
 def test_gemm16_big_tiles_integer_bitexact(sg, kind, form):
     """K = 576 (a multiple of 64): the larger-tile kernel reads A transposed
-    and B as given in place (transposing LDS reads); M = 4344 and N = 3904
-    leave a row of edge tiles 248 high and a column 64 wide."""
-    M, N, K = 4344, 3904, 576
+    and B as given in place (transposing LDS reads); M = 3832 and N = 3904
+    (240 tiles of 256 x 256) leave a row of edge tiles 248 high and a column
+    64 wide."""
+    M, N, K = 3832, 3904, 576
     ta, tb = form
     A, B, C0 = _inputs16(M, N, K, "int4", kind, 47)
     st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0)
     assert st == 0
     ok, info = check16_logical(C, A, B, kind, 1.0, -1.0, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("shape", [(2900, 3000, 576), (3072, 3072, 64), (2880, 2888, 1000)],
+                         ids=["edges", "one_slice", "ragged_k"])
+def test_gemm16_192_tiles_bitexact(sg, kind, form, shape):
+    """Grids of 224 to 256 tiles of 192 x 192 (and fewer than 256 of
+    256 x 256) run the direct-to-LDS kernel on 192 x 192 tiles, whose rows of
+    k along x are 384 bytes with their own rotation: edge tiles in M and N,
+    a single slice, and K = 1000 (packed, padded to 1024)."""
+    M, N, K = shape
+    ta, tb = form
+    say(f"[g16_192] kind={kind} {form} {shape}")
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 80 + K + 2 * ta + tb)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0)
+    assert st == 0
+    ok, info = check16_logical(C, A, B, kind, 1.0, -1.0, C0, exact=True)
+    assert ok, info
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+def test_gemm16_192_tiles_real(sg, kind, form):
+    """3072^3 with alpha 1.5, beta -0.5 on N(0,1) inputs: 256 tiles of
+    192 x 192, every element within the bound."""
+    ta, tb = form
+    M = N = K = 3072
+    say(f"[g16_192_real] kind={kind} {form}")
+    w = workloads.custom(M, N, K, dist="normal", seed=91, c0_dist="normal")
+    A, B, C0 = workloads.make_inputs_16bit(w, kind)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check16_logical(C, A, B, kind, 1.5, -0.5, C0, exact=False)
     assert ok, info
 
 
