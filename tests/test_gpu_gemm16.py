@@ -154,8 +154,13 @@ def test_gemm16_c_stride_past_32bit_tile_offsets(sg, kind, form, K):
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-def test_gemm16_beta_zero_ignores_nan_c(sg, kind):
-    A, B, _ = _inputs16(140, 130, 128, "uniform", kind, 42)
+@pytest.mark.parametrize("shape", [(140, 130, 128), (3072, 3000, 128), (4096, 4096, 128)],
+                         ids=["tile128", "tile192", "tile256"])
+def test_gemm16_beta_zero_ignores_nan_c(sg, kind, shape):
+    """beta = 0: C is written without being read (NaN there stays out of the
+    result) on each tile size of the direct-to-LDS kernel."""
+    M, N, K = shape
+    A, B, _ = _inputs16(M, N, K, "uniform", kind, 42)
     st, C, As, Bs = run16(sg, kind, 0, 1, A, B, None, 1.0, 0.0, c_fill=np.nan)
     assert st == 0 and np.all(np.isfinite(C))
     ok, info = check16(C, As, Bs, kind, 0, 1, 1.0, 0.0, None, exact=False)
@@ -284,10 +289,11 @@ def test_gemm16_big_tiles_short_k_bitexact(sg, K, form):
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-@pytest.mark.parametrize("shape", [(150, 140, 96), (4096, 4096, 64)], ids=["small_grid", "big_tiles"])
+@pytest.mark.parametrize("shape", [(150, 140, 96), (3072, 3072, 64), (4096, 4096, 64)],
+                         ids=["small_grid", "tile192", "big_tiles"])
 def test_gemm16_negative_alpha_zero_sums_bitexact(sg, kind, shape):
     """alpha < 0 with beta = 0: exactly zero sums are alpha * (+0) = -0, the
-    oracle's value, on both kernels."""
+    oracle's value, on each tile size of the direct-to-LDS kernel."""
     from gpu_helpers import zero_sum_integers
     M, N, K = shape
     say(f"[g16_neg_alpha_zero] kind={kind} {shape}")
