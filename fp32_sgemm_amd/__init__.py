@@ -38,7 +38,8 @@ CFG_64x64_BK64 = 6
 CFG_256x256 = 7
 CFG_128x128_DL = 8
 CFG_64x64_DL = 9
-NUM_CONFIGS = 10
+CFG_192x192_DL = 10
+NUM_CONFIGS = 11
 
 ERR_VARIANT = 20
 ERR_NOT_APPLICABLE = 21

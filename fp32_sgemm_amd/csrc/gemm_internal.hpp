@@ -42,13 +42,13 @@ hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stre
 // in rounds, then equal shares of the remaining tiles' K slices; split tiles
 // are summed by a fix-up kernel), 6 = 64x64 with slices of 64, 7 = 256x256
 // (sgemm_big.hip: one work-group per CU, operands copied straight into LDS),
-// 8 = 128x128 and 9 = 64x64 by the same kernel (two and four work-groups per
-// CU).  Configurations 2-9 exist with 16-byte loads only.  `group_m` is the
-// number of tile rows walked together by the tile order (configuration 7 uses
-// 4); `splits` divides K over work-groups (the partial sums go through the
-// call's scratch and a reduction kernel; not with configurations 5, 7, 8 and
-// 9).
-constexpr int kNumMfmaConfigs = 10;
+// 8 = 128x128, 9 = 64x64 and 10 = 192x192 by the same kernel (two, four and
+// one work-groups per CU).  Configurations 2-10 exist with 16-byte loads only.
+// `group_m` is the number of tile rows walked together by the tile order
+// (configuration 7 uses 4); `splits` divides K over work-groups (the partial
+// sums go through the call's scratch and a reduction kernel; not with
+// configurations 5 and 7-10).
+constexpr int kNumMfmaConfigs = 11;
 hipError_t launch_mfma_config(const GemmArgs &g, int config, bool vec_loads, int group_m, int splits,
                               hipStream_t stream);
 int64_t mfma_config_tiles(int config, int M, int N);
@@ -59,11 +59,12 @@ bool mfma_config_splits_ok(int config);
 int mfma_effective_splits(int K, int splits, int *k_per);
 // 256 x 256 tiles, one work-group per CU (sgemm_big.hip): whether the
 // product fits them (M, N, K multiples of 4, aligned operands), their count,
-// and the launchers of the 256 x 256 and 128 x 128 grids.
+// and the launchers of the 256 x 256, 192 x 192, 128 x 128 and 64 x 64 grids.
 bool big_tile_fits(const GemmArgs &g);   // operands (C's stride: big_tile_c_fits)
 bool big_tile_c_fits(int64_t ldc);
 int64_t big_tiles(int M, int N);
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream);
+hipError_t launch_dl192(const GemmArgs &g, int group_m, hipStream_t stream);
 hipError_t launch_dl128(const GemmArgs &g, int group_m, hipStream_t stream);
 hipError_t launch_dl64(const GemmArgs &g, int group_m, hipStream_t stream);
 hipError_t launch_valu(const GemmArgs &g, bool vec_loads, hipStream_t stream);

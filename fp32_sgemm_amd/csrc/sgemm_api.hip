@@ -245,12 +245,38 @@ Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const f
     return Plan{SGEMM_F32_MFMA_TUNED, p.config == 0 ? 8 : 9, p.group_m, 1};
 }
 
+// 192x192 tiles (configuration 10: the same kernel, one work-group per compute
+// unit) for grids of 250 to 256 such tiles and K of at least 1024, where they
+// fill one round that 64x64 or 128x128 tiles would cover in several.  Same-box
+// medians (microseconds, configuration 4 / the automatic plan -> 10, NN, alpha
+// 1, beta 0): 3000^3 405.7 -> 394.0; 3072^3 409.8 -> 402.8; 3072 x 3072 x 8192
+// 1085.9 -> 1056.8; 1536 x 6144 x 4096 542.8 -> 531.5; 3072 x 3072 x 1024
+// 141.1 -> 140.4; 2976^3 388.8 -> 388.4; and the other way 3072 x 2880 x 2048
+// (240 tiles) 269.1 -> 270.4, 2880^3 (225) 346.9 -> 376.0, 3584^3 (361, two
+// rounds) 678.5 -> 921.6, 4096 x 11008 x 512 339.5 -> 358.5.
+constexpr int64_t kRound192Min = 250;
+Plan round192_plan(const Plan &p, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B,
+                   int ldb) {
+    if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.splits > 1) return p;
+    if (p.config != 0 && p.config != 4) return p;
+    const int64_t tiles = sgemm::mfma_config_tiles(10, M, N);
+    if (K < 1024 || tiles < kRound192Min || tiles > kResidentBigTiles) return p;
+    sgemm::GemmArgs g{};
+    g.M = M; g.N = N; g.K = K;
+    g.A = A; g.B = B;
+    g.lda = lda; g.ldb = ldb;
+    g.trans_a = ta; g.trans_b = tb;
+    if (!sgemm::big_tile_fits(g)) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 10, 8, 1};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill
-// theirs, and from the 128x128 and 64x64 kernels to configurations 8 and 9
-// (reported as SGEMM_F32_MFMA_TUNED when the plan differs from the default).
+// theirs, to 192x192 tiles for grids of one round of them, and from the
+// 128x128 and 64x64 kernels to configurations 8 and 9 (reported as
+// SGEMM_F32_MFMA_TUNED when the plan differs from the default).
 // Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
@@ -268,6 +294,7 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
         }
     }
     p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
+    p = round192_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
     return direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
 }
 
@@ -337,7 +364,8 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
     }
     // The plan does not see C: a row stride of C too wide for the 32-bit
     // offsets of configurations 7-9 keeps the register-staged kernels.
-    if ((p.config == 7 || p.config == 8) && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
+    if ((p.config == 7 || p.config == 8 || p.config == 10) && !sgemm::big_tile_c_fits(ldc))
+        p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
     if (p.config == 9 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, 1};
     if (scratch.fixed != nullptr) {
         // A fixed scratch region: refuse, before anything is enqueued, a plan
@@ -467,6 +495,7 @@ const char *sgemm_f32_config_name(int config) {
         case 7: return "256x256";
         case 8: return "128x128_dl";
         case 9: return "64x64_dl";
+        case 10: return "192x192_dl";
         default: return nullptr;
     }
 }

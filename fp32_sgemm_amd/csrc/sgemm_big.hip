@@ -1,6 +1,7 @@
 // FP32 GEMM on 256 x 256 tiles, one per CU at a time, for grids whose rounds of
-// 256 tiles lie almost entirely inside C; the same kernel on 128 x 128 tiles
-// (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) and on
+// 256 tiles lie almost entirely inside C; the same kernel on 192 x 192 tiles
+// (4 waves of 96 x 96, one work-group per CU, 96 KB of LDS), on 128 x 128
+// tiles (4 waves of 64 x 64, two work-groups per CU, 64 KB of LDS each) and on
 // 64 x 64 tiles (4 waves of 32 x 32, four work-groups per CU; grids of at most
 // one tile per CU run 8 waves per tile, two groups splitting K) serves whole
 // grids of those tiles.  The description below is that of the 256 x 256 form.
@@ -33,9 +34,11 @@
 //   c ^ ((x >> 2) & 3), which keeps the 16-byte fragment reads free of bank
 //   conflicts.  One load instruction fills 16 rows.
 //   rows of x (B as given, A given transposed): 16 rows of 256 floats (1 KB,
-//   one load instruction each); rows 8..15, read by the second half-wave,
-//   are rotated by 32 floats so that the two half-waves, which read rows
-//   k and k + 8 at the same x, fall in opposite halves of the bank space.
+//   one load instruction each; smaller tiles lay their shorter rows end to
+//   end, each instruction filling the next 1 KB); rows 8..15, read by the
+//   second half-wave, are rotated by 32 floats so that the two half-waves,
+//   which read rows k and k + 8 at the same x, fall in opposite halves of the
+//   bank space (every row length here is a multiple of the 64 banks).
 //
 // Edges.  M, N and K are multiples of 4, so a 16-byte group never straddles
 // an edge.  Tiles that cross M or N give each group outside M or N an
@@ -66,8 +69,9 @@ constexpr int BK = 16;                   // slice depth
 constexpr int NT = 256;                  // 4 waves in a 2 x 2 arrangement
 constexpr int NST = 4;                   // LDS stages
 
-// Geometry of a TS x TS tile (TS = 256: one work-group per CU; TS = 128: the
-// same kernel on 128 x 128 tiles, two work-groups per CU).
+// Geometry of a TS x TS tile (TS = 256: one work-group per CU; the same
+// kernel on 192 x 192 tiles, one work-group per CU, on 128 x 128, two, and on
+// 64 x 64, four).
 template <int TS>
 struct Geo {
     static constexpr int BM = TS, BN = TS;
@@ -78,9 +82,10 @@ struct Geo {
     static constexpr int LPO = TS / 64;           // load instructions per wave, operand and slice
     static constexpr int LPS = 2 * LPO;
     static constexpr int XROW = TS * 4;           // bytes of one LDS row of an operand stored along x
-    static constexpr int XLANES = TS / 4;         // lanes per such row in one load instruction
+    static constexpr int XLANES = TS / 4;         // its 16-byte chunks
     static constexpr int KROWS_W = TS / 4;        // rows of an operand stored along k per wave
     static_assert(NST * STAGE <= 160 * 1024, "LDS");
+    static_assert(BK * XROW == 4 * LPO * 1024, "rows of x: the 4 waves' loads fill a panel");
 };
 
 __device__ float raw_buffer_load_f32(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset, int aux)
@@ -132,13 +137,25 @@ struct Operand {
                 gx[j] = x;
                 gk[j] = 4 * c;
             } else {
-                // 1 KB per instruction: 1024 / XROW rows of k
-                const int row0 = (wave * G::LPO + j) * (1024 / G::XROW);
-                const int k = row0 + lane / G::XLANES;
-                const int p = lane % G::XLANES;
+                // The panel's 16 rows of k lie end to end; instruction j of
+                // the wave fills its next 1 KB, the lane's 16 bytes at byte
+                // b: row k, position p, which holds chunk c (rows 8..15
+                // rotated by 32 floats).  Rows of 1 KB or a power-of-two part
+                // of it keep whole rows per instruction, in that form.
+                int k, p;
+                if constexpr (1024 % G::XROW == 0) {
+                    const int row0 = (wave * G::LPO + j) * (1024 / G::XROW);
+                    k = row0 + lane / G::XLANES;
+                    p = lane % G::XLANES;
+                    dst[j] = row0 * G::XROW;
+                } else {
+                    const int b = (wave * G::LPO + j) * 1024 + 16 * lane;
+                    k = b / G::XROW;
+                    p = b % G::XROW / 16;
+                    dst[j] = (wave * G::LPO + j) * 1024;
+                }
                 const int c = k >= BK / 2 ? (p + 8) % G::XLANES : p;
                 off[j] = (k * (int)ld_ + 4 * c) * 4;
-                dst[j] = row0 * G::XROW;
                 gx[j] = 4 * c;
                 gk[j] = k;
             }
@@ -172,7 +189,8 @@ struct FragAddr {
         for (int b = 0; b < G::BLK; ++b) {
             const int x = xw + 32 * b + l32;
             if (L == kKRows) a[b] = x * BK * 4 + ((2 * h) ^ ((x >> 2) & 3)) * 16;
-            else a[b] = (8 * h) * G::XROW + ((x - 32 * h) & (TS - 1)) * 4;
+            else if ((TS & (TS - 1)) == 0) a[b] = (8 * h) * G::XROW + ((x - 32 * h) & (TS - 1)) * 4;
+            else a[b] = (8 * h) * G::XROW + (x - 32 * h + TS) % TS * 4;
         }
     }
 };
@@ -434,10 +452,10 @@ hipError_t compute_units(int *out) {
     return hipSuccess;
 }
 
-// Work-groups per CU: TS 256 one (256 accumulators per lane), TS 128 two,
-// TS 64 four (32 KB of LDS each).
+// Work-groups per CU: TS 256 one (256 accumulators per lane), TS 192 one (96
+// KB of LDS), TS 128 two, TS 64 four (32 KB of LDS each).
 template <int TS>
-constexpr int kWavesPerEu = TS == 256 ? 1 : TS == 128 ? 2 : 4;
+constexpr int kWavesPerEu = TS == 256 || TS == 192 ? 1 : TS == 128 ? 2 : 4;
 
 template <int LA, int LB, int TS, int KG>
 __global__ __launch_bounds__(NT * KG) __attribute__((amdgpu_waves_per_eu(kWavesPerEu<TS>, kWavesPerEu<TS>)))
@@ -508,6 +526,8 @@ hipError_t launch_ts(const GemmArgs &g, int group_m, hipStream_t stream) {
 }  // namespace
 
 hipError_t launch_big(const GemmArgs &g, hipStream_t stream) { return launch_ts<256>(g, 4, stream); }
+
+hipError_t launch_dl192(const GemmArgs &g, int group_m, hipStream_t stream) { return launch_ts<192>(g, group_m, stream); }
 
 hipError_t launch_dl128(const GemmArgs &g, int group_m, hipStream_t stream) { return launch_ts<128>(g, group_m, stream); }
 

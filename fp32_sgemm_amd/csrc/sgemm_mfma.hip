@@ -919,8 +919,8 @@ using SmallTile2 = MfmaTile<64, 64, 32, 32, 32, 2, LA, LB>;
 template <int LA, int LB>
 using SmallTileK64 = MfmaTile<64, 64, 64, 32, 32, 2, LA, LB>;
 
-constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128, 64, 256, 128, 64};
-constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128, 64, 256, 128, 64};
+constexpr int kTileBM[kNumMfmaConfigs] = {128, 64, 128, 64, 64, 128, 64, 256, 128, 64, 192};
+constexpr int kTileBN[kNumMfmaConfigs] = {128, 64, 64, 128, 64, 128, 64, 256, 128, 64, 192};
 constexpr int kTileBK = 32;
 
 template <class T, bool VEC>
@@ -1042,6 +1042,7 @@ hipError_t launch_layouts(const GemmArgs &g, int config, bool vec, int group_m, 
         case 7: return launch_big(g, stream);
         case 8: return launch_dl128(g, group_m, stream);
         case 9: return launch_dl64(g, group_m, stream);
+        case 10: return launch_dl192(g, group_m, stream);
         default: return hipErrorInvalidValue;
     }
 }

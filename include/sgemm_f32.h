@@ -128,7 +128,9 @@ enum sgemm_f32_config_id {
                                      CU; its conditions, no K split */
     SGEMM_F32_CFG_64x64_DL = 9,   /* 64x64 by the kernel of configuration 7, four work-groups per
                                      CU; its conditions, no K split */
-    SGEMM_F32_NUM_CONFIGS = 10
+    SGEMM_F32_CFG_192x192_DL = 10, /* 192x192 by the kernel of configuration 7, one work-group per
+                                      CU; its conditions, no K split */
+    SGEMM_F32_NUM_CONFIGS = 11
 };
 
 /*
@@ -275,14 +277,17 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * part of its rounds (256 tiles each) that lies inside C is at least 93 % and
  * within 2 % of the 128 x 128 grid's (a C stride too wide for it at call time
  * keeps the 128 x 128 grid).
- * Configurations 8 and 9 run the kernel of configuration 7 on 128 x 128 and on
- * 64 x 64 tiles (two and four work-groups per compute unit) with the same
- * conditions; they honour the grouping and take no split count (splits must
- * be 1).  The automatic choice takes configuration 8 in place of the 128 x 128
+ * Configurations 8, 9 and 10 run the kernel of configuration 7 on 128 x 128,
+ * 64 x 64 and 192 x 192 tiles (two, four and one work-groups per compute unit)
+ * with the same conditions; they honour the grouping and take no split count
+ * (splits must be 1).  The automatic choice takes configuration 8 in place of the 128 x 128
  * grid and 9 in place of configuration 4, each without a split, when those
  * conditions hold, for configuration 9 also M and N multiples of 64 with at
  * most 1024 tiles (again, a C stride too wide at call time keeps the plan's
- * register-staged kernel).
+ * register-staged kernel).  It takes configuration 10 in place of an unsplit
+ * 128 x 128 or 64 x 64 plan when the 192 x 192 grid has 250 to 256 tiles (one
+ * round) and K is at least 1024 (a C stride too wide keeps the 128 x 128
+ * grid).
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

@@ -256,18 +256,20 @@ def test_streamk_repeat_bitwise_identical(sg):
 
 
 # ---------------------------------------------------------------------------
-# Configurations 7, 8 and 9: the kernel that copies the operands straight
-# into LDS, on 256x256, 128x128 and 64x64 tiles.  M, N and K multiples of 4;
+# Configurations 7, 8, 9 and 10: the kernel that copies the operands straight
+# into LDS, on 256x256, 128x128, 64x64 and 192x192 tiles.  M, N and K multiples of 4;
 # edge tiles get zeros past M, N and K in LDS and masked stores.  One slice is
 # 16 deep and three are fetched ahead, so short K exercises the repeated loads
 # past the end.
 # ---------------------------------------------------------------------------
-BIG_CFGS = [7, 8, 9]
+BIG_CFGS = [7, 8, 9, 10]
 BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024), (128, 384, 32),
               (64, 192, 64),
               # edge tiles: M, N not multiples of the tile, K not of 16 (multiples of 4)
               (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52), (124, 132, 16),
-              (68, 60, 28)]
+              (68, 60, 28),
+              # 192x192 tiles: whole, and edges of 4 to 188
+              (384, 576, 48), (196, 388, 20), (580, 200, 116)]
 
 
 @pytest.mark.parametrize("cfg", BIG_CFGS)
@@ -308,7 +310,7 @@ def test_big_kernel_beta_zero_ignores_nan_c(sg, cfg):
     assert ok, info
 
 
-@pytest.mark.parametrize("cfg", [8, 9])
+@pytest.mark.parametrize("cfg", [8, 9, 10])
 def test_direct_lds_grouping_bitwise(sg, cfg):
     """The grouping changes only the order of the tiles: every grouping gives
     the same bits."""
@@ -370,7 +372,7 @@ def test_big_kernel_long_k_bitexact(sg, cfg, K):
     assert ok, info
 
 
-ALL_CFGS = [(c, 1) for c in range(10)] + [(c, 3) for c in GRID_CFGS]
+ALL_CFGS = [(c, 1) for c in range(11)] + [(c, 3) for c in GRID_CFGS]
 
 
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)

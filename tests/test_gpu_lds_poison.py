@@ -66,10 +66,10 @@ def _exact(C, A, B, alpha, beta, C0):
 
 BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024), (128, 384, 32),
               (64, 192, 64), (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52),
-              (124, 132, 16), (68, 60, 28)]
+              (124, 132, 16), (68, 60, 28), (384, 576, 48), (196, 388, 20)]
 
 
-@pytest.mark.parametrize("cfg", [7, 8, 9])
+@pytest.mark.parametrize("cfg", [7, 8, 9, 10])
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("shape", BIG_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in BIG_SHAPES])
 def test_poisoned_direct_lds_kernel(plib, cfg, form, shape):
@@ -83,7 +83,7 @@ def test_poisoned_direct_lds_kernel(plib, cfg, form, shape):
     assert ok, info
 
 
-@pytest.mark.parametrize("cfg", [7, 8, 9])
+@pytest.mark.parametrize("cfg", [7, 8, 9, 10])
 @pytest.mark.parametrize("K", [65536, 65540])
 def test_poisoned_direct_lds_kernel_long_k(plib, cfg, K):
     M, N = 256, 512

@@ -442,8 +442,8 @@ def test_c_leading_dimension_past_32bit_offsets(sg):
 
 
 # Shapes for which the automatic choice plans a direct-to-LDS configuration
-# (9: 64x64, 7: 256x256, 8: 128x128 tiles).
-WIDE_LDC = [((128, 8192, 2048), 9), ((256, 65536, 512), 7), ((768, 32768, 512), 8)]
+# (9: 64x64, 7: 256x256, 8: 128x128, 10: 192x192 tiles).
+WIDE_LDC = [((128, 8192, 2048), 9), ((256, 65536, 512), 7), ((768, 32768, 512), 8), ((192, 49152, 1024), 10)]
 
 
 @pytest.mark.parametrize("shape,planned", WIDE_LDC, ids=[f"{m}x{n}x{k}-cfg{c}" for (m, n, k), c in WIDE_LDC])

@@ -73,11 +73,11 @@ def test_lds_poison_copy_exports_the_same_interface(sg):
     assert set(_declared_functions()) <= exported
 
 
-@pytest.mark.parametrize("src,kernels", [("sgemm_big.hip", 16), ("gemm16.hip", 26)])
+@pytest.mark.parametrize("src,kernels", [("sgemm_big.hip", 20), ("gemm16.hip", 26)])
 def test_lds_poison_flag_fills_lds_with_nan(tmp_path, src, kernels):
     """The debug flag really plants the NaN fill: the device code of the
     kernels built with SGEMM_LDS_POISON holds the quiet-NaN constant once per
-    LDS-using kernel instance (3 tile sizes x 4 operand forms of the
+    LDS-using kernel instance (4 tile sizes x 4 operand forms of the
     direct-to-LDS kernel, plus its two-group 64x64 form x 4; in the 16-bit
     GEMM, the register-staged 128 x 128 kernel x 2 formats and the
     direct-to-LDS kernel x 3 tile sizes x 2 formats x A and B each K-major or
@@ -227,7 +227,7 @@ def test_variant_names_and_version(sg):
     assert sg.sgemm_f32_variant_name(sg.NUM_VARIANTS) is None
     cfgs = [sg.sgemm_f32_config_name(i) for i in range(sg.NUM_CONFIGS)]
     assert cfgs == ["128x128", "64x64", "128x64", "64x128", "64x64_pf2", "128x128_streamk", "64x64_bk64", "256x256",
-                    "128x128_dl", "64x64_dl"]
+                    "128x128_dl", "64x64_dl", "192x192_dl"]
     assert sg.sgemm_f32_config_name(sg.NUM_CONFIGS) is None and sg.sgemm_f32_config_name(-1) is None
     assert sg.sgemm_f32_version() >= 300
 
@@ -275,15 +275,20 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     # 64x64 tiles: loaded straight into LDS (configuration 9) when M and N are
     # multiples of 64 and the grid has at most 1024 tiles (one round), else
     # with two slices in flight.
-    for shape in [(3000, 3000, 3000), (3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
+    for shape in [(3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
                   (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
-                  (2560, 2560, 2560), (3008, 3008, 3008)]:
+                  (2560, 2560, 2560), (3072, 2880, 2048), (3072, 3072, 512)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
+    # One round of 250 to 256 tiles of 192x192 (K >= 1024): configuration 10.
+    for shape in [(3000, 3000, 3000), (3008, 3008, 3008), (3072, 3072, 1024), (2976, 2976, 2976),
+                  (1536, 6144, 4096), (2880, 3264, 2048)]:
+        assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_192x192_DL, 8, 1), shape
     for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096)]:
         assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL), shape
     assert plan(2048, 2048, 2044)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL)
     assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
-    assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
+    assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_192x192_DL)
+    assert plan(3002, 3000, 3000)[1:3] != (sg.MFMA_TUNED, sg.CFG_192x192_DL)   # M not a multiple of 4
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
     for shape in [(7000, 7000, 1024), (7040, 7000, 1024), (10000, 10000, 1024)]:
