@@ -6,6 +6,7 @@
 // kernels ("Learn: Optimizing GEMM", section 8; "Writing a Fast Matmul in CUDA,
 // Step by Step", section "In the real world"); this library picks among its own
 // few kernels by shape and operand alignment, on the host, before one launch.
+#include <cmath>
 #include <cstdint>
 
 #include "gemm_internal.hpp"
@@ -270,13 +271,45 @@ Plan round192_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
     return Plan{SGEMM_F32_MFMA_TUNED, 10, 8, 1};
 }
 
+// A 64x64 grid that runs unevenly on the compute units (configuration 9: the
+// busiest CU holds at least kSplitImbalance times the mean number of tiles)
+// with K of at least kSplitMinK goes back to configuration 4 with K split in 2
+// or 3, whichever spreads the tile-splits more evenly (2 on a tie).  Same-box
+// TFLOP/s, configuration 9 -> split: 1152 x 1152 x 4096 88.9 -> 117.5 (3);
+// 1152 x 1152 x 2048 86.6 -> 105.4 (3); 1280 x 1280 x 4096 109.2 -> 117.7 (3);
+// 1536 x 1536 x 2048 105.1 -> 111.5 (3); 1536 x 1536 x 4096 108.6 -> 128.2
+// (3); 1536 x 1536 x 8192 108.9 -> 125.3 (3); 1792 x 1792 x 4096 109.9 ->
+// 119.7 (3); 1600 x 1600 x 4096 116.1 -> 121.1 (2); 1536 x 1024 x 4096 105.0
+// -> 123.3 (2); 1024 x 1536 x 3072 104.2 -> 119.9 (2); 1280 x 1280 x 2048
+// 106.2 -> 106.1 (3); 1536^3 103.9 -> 109.0 (3); 1792^3 108.1 -> 111.7 (3);
+// 1600^3 111.2 -> 111.3 (2).  Evenly spread grids lost (1408 x 1408 x 4096,
+// 1.06 tiles per CU over the mean, 128.3 -> 121.8; 1664 x 1664 x 4096, 1.14,
+// 124.2 -> 120.4), and so did K below 1536 (1280^3 103.2 -> 96.3).  Through
+// the automatic plan on another box, against torch's FP32 mm (TFLOP/s):
+// 1152 x 1152 x 4096 119.8 / 112.4, 1536 x 1536 x 4096 124.8 / 132.7, 1792 x
+// 1792 x 4096 122.0 / 121.7, 1600 x 1600 x 4096 126.9 / 126.0.
+constexpr double kSplitImbalance = 1.2;
+constexpr int kSplitMinK = 1536;
+double cu_imbalance(int64_t units) {
+    const double per = (double)units / kResidentBigTiles;
+    return std::ceil(per) / per;
+}
+Plan balance_split_plan(const Plan &p, int M, int N, int K) {
+    if (p.variant != SGEMM_F32_MFMA_TUNED || p.config != 9 || p.splits > 1 || K < kSplitMinK) return p;
+    const int64_t tiles = sgemm::mfma_config_tiles(9, M, N);
+    if (cu_imbalance(tiles) < kSplitImbalance) return p;
+    const int splits = cu_imbalance(3 * tiles) < cu_imbalance(2 * tiles) ? 3 : 2;
+    return Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, splits};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill
-// theirs, to 192x192 tiles for grids of one round of them, and from the
-// 128x128 and 64x64 kernels to configurations 8 and 9 (reported as
-// SGEMM_F32_MFMA_TUNED when the plan differs from the default).
+// theirs, to 192x192 tiles for grids of one round of them, from the 128x128
+// and 64x64 kernels to configurations 8 and 9, and from an unevenly spread
+// configuration 9 back to a K split (reported as SGEMM_F32_MFMA_TUNED when the
+// plan differs from the default).
 // Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
@@ -295,7 +328,7 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
     }
     p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
     p = round192_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
-    return direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
+    return balance_split_plan(direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb), M, N, K);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }
