@@ -302,14 +302,30 @@ Plan balance_split_plan(const Plan &p, int M, int N, int K) {
     return Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, splits};
 }
 
+// A 64x64 grid of configuration 9 that is also one round of 250 to 256
+// 128x128 tiles (one per compute unit) with K of at least 1024 goes to those
+// tiles (configuration 8).  Same-box TFLOP/s, configuration 9 -> 8: 2048^3
+// 136.8 -> 139.6; 2048 x 2048 x 4096 138.6 -> 143.2; 1024 x 4096 x 4096
+// 139.3 -> 143.2; 4096 x 1024 x 4096 138.7 -> 143.5; 2048 x 2048 x 1024
+// 131.7 -> 132.6; with fewer 128x128 tiles configuration 8 leaves CUs idle
+// (256 x 4096 x 4096, 64 tiles: 134.1 -> 36.2).
+constexpr int64_t kRound128Min = 250;
+Plan round128_plan(const Plan &p, int M, int N, int K) {
+    if (p.variant != SGEMM_F32_MFMA_TUNED || p.config != 9 || p.splits > 1 || K < 1024) return p;
+    const int64_t tiles = sgemm::mfma_config_tiles(8, M, N);
+    if (tiles < kRound128Min || tiles > kResidentBigTiles) return p;
+    return Plan{SGEMM_F32_MFMA_TUNED, 8, p.group_m, 1};
+}
+
 // The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill
 // theirs, to 192x192 tiles for grids of one round of them, from the 128x128
-// and 64x64 kernels to configurations 8 and 9, and from an unevenly spread
-// configuration 9 back to a K split (reported as SGEMM_F32_MFMA_TUNED when the
-// plan differs from the default).
+// and 64x64 kernels to configurations 8 and 9, from an unevenly spread
+// configuration 9 back to a K split, and from a configuration 9 grid that is
+// one round of 128x128 tiles to those (reported as SGEMM_F32_MFMA_TUNED when
+// the plan differs from the default).
 // Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
@@ -328,7 +344,8 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
     }
     p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
     p = round192_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
-    return balance_split_plan(direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb), M, N, K);
+    p = balance_split_plan(direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb), M, N, K);
+    return round128_plan(p, M, N, K);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }

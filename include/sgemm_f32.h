@@ -289,7 +289,9 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * round) and K is at least 1024 (a C stride too wide keeps the 128 x 128
  * grid).  A configuration 9 grid that spreads unevenly over the compute units
  * (the busiest holds at least 1.2 times the mean number of tiles) with K of
- * at least 1536 goes back to configuration 4 with K split in 2 or 3.
+ * at least 1536 goes back to configuration 4 with K split in 2 or 3, and one
+ * that is also one round of 250 to 256 tiles of 128 x 128 with K of at least
+ * 1024 goes to configuration 8.
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */

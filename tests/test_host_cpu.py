@@ -283,9 +283,8 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     for shape in [(3000, 3000, 3000), (3008, 3008, 3008), (3072, 3072, 1024), (2976, 2976, 2976),
                   (1536, 6144, 4096), (2880, 3264, 2048)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_192x192_DL, 8, 1), shape
-    for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096)]:
-        assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL), shape
-    assert plan(2048, 2048, 2044)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL)
+    for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096), (2048, 2048, 2044)]:
+        assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL), shape
     assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
     # 64x64 grids spread unevenly over the CUs (1.2 times the mean or more)
     # with K >= 1536: back to configuration 4 with K split in 2 or 3.
@@ -293,9 +292,13 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
                           ((1792, 1792, 4096), 3), ((1600, 1600, 4096), 2), ((1536, 1024, 4096), 2),
                           ((1536, 1536, 1536), 3), ((1600, 1600, 1600), 2)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, splits), shape
-    for shape in [(1280, 1280, 1280), (1408, 1408, 4096), (1664, 1664, 4096),
-                  (1024, 4096, 4096), (2048, 2048, 2048)]:
+    for shape in [(1280, 1280, 1280), (1408, 1408, 4096), (1664, 1664, 4096), (256, 4096, 4096),
+                  (2048, 2048, 512)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_DL, 8, 1), shape
+    # A configuration 9 grid that is one round of 128x128 tiles (K >= 1024):
+    # configuration 8.
+    for shape in [(2048, 2048, 2048), (1024, 4096, 4096), (4096, 1024, 4096), (2048, 2048, 1024)]:
+        assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_128x128_DL, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_192x192_DL)
     assert plan(3002, 3000, 3000)[1:3] != (sg.MFMA_TUNED, sg.CFG_192x192_DL)   # M not a multiple of 4
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
