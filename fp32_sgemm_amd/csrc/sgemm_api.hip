@@ -247,8 +247,15 @@ Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const f
 }
 
 // 192x192 tiles (configuration 10: the same kernel, one work-group per compute
-// unit) for grids of 250 to 256 such tiles and K of at least 1024, where they
-// fill one round that 64x64 or 128x128 tiles would cover in several.  Same-box
+// unit) for grids of whole rounds of such tiles (at most 6 short of a multiple
+// of 256) and K of at least 1024: one round in place of 64x64 or 128x128
+// tiles, several in place of 64x64 tiles (the plan for 128x128 grids that
+// fill their rounds poorly).  Several rounds, same box, configuration 4 -> 10
+// (TFLOP/s): 6144 x 3072 x 2048 140.2 -> 143.6, 6144 x 3072 x 1024 136.4 ->
+// 139.5, 4608 x 6144 x 2048 141.1 -> 144.0, 9216 x 3072 x 2048 140.6 ->
+// 144.0, 6144 x 4608 x 4096 143.1 -> 145.8, 3072 x 9216 x 1024 137.5 ->
+// 140.4; but 4608 x 4608 x 4096 (2.25 rounds) 139.4 -> 109.4, and 6144^3
+// (four rounds, configuration 8) 149.3 -> 147.0.  One round, same box
 // medians (microseconds, configuration 4 / the automatic plan -> 10, NN, alpha
 // 1, beta 0): 3000^3 405.7 -> 394.0; 3072^3 409.8 -> 402.8; 3072 x 3072 x 8192
 // 1085.9 -> 1056.8; 1536 x 6144 x 4096 542.8 -> 531.5; 3072 x 3072 x 1024
@@ -261,7 +268,9 @@ Plan round192_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
     if ((p.variant != SGEMM_F32_MFMA_LARGE && p.variant != SGEMM_F32_MFMA_TUNED) || p.splits > 1) return p;
     if (p.config != 0 && p.config != 4) return p;
     const int64_t tiles = sgemm::mfma_config_tiles(10, M, N);
-    if (K < 1024 || tiles < kRound192Min || tiles > kResidentBigTiles) return p;
+    const int64_t rounds = (tiles + kResidentBigTiles - 1) / kResidentBigTiles;
+    if (K < 1024 || tiles < rounds * kResidentBigTiles - (kResidentBigTiles - kRound192Min)) return p;
+    if (rounds > 1 && p.config != 4) return p;
     sgemm::GemmArgs g{};
     g.M = M; g.N = N; g.K = K;
     g.A = A; g.B = B;

@@ -286,8 +286,9 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * most 1024 tiles (again, a C stride too wide at call time keeps the plan's
  * register-staged kernel).  It takes configuration 10 in place of an unsplit
  * 128 x 128 or 64 x 64 plan when the 192 x 192 grid has 250 to 256 tiles (one
- * round) and K is at least 1024 (a C stride too wide keeps the 128 x 128
- * grid).  A configuration 9 grid that spreads unevenly over the compute units
+ * round), and in place of an unsplit 64 x 64 plan when it has whole rounds
+ * (at most 6 tiles short of a multiple of 256), K being at least 1024 (a C
+ * stride too wide keeps the 128 x 128 grid).  A configuration 9 grid that spreads unevenly over the compute units
  * (the busiest holds at least 1.2 times the mean number of tiles) with K of
  * at least 1536 goes back to configuration 4 with K split in 2 or 3, and one
  * that is also one round of 250 to 256 tiles of 128 x 128 with K of at least

@@ -160,7 +160,7 @@ def test_split_repeat_bitwise_identical(sg):
 
 TUNED_SHAPES = [(1024, 1024, 1024), (2048, 2048, 2048), (512, 512, 8192), (4096, 1024, 256),
                 (256, 4096, 4096), (2048, 2048, 512), (3000, 3000, 3000), (5000, 3000, 200),
-                (1536, 1536, 4096), (1600, 1600, 4096)]
+                (1536, 1536, 4096), (1600, 1600, 4096), (6144, 3072, 1024)]
 
 
 @pytest.mark.parametrize("shape", TUNED_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in TUNED_SHAPES])

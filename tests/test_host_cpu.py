@@ -279,10 +279,15 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
                   (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
                   (2560, 2560, 2560), (3072, 2880, 2048), (3072, 3072, 512)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1), shape
-    # One round of 250 to 256 tiles of 192x192 (K >= 1024): configuration 10.
+    # One round of 250 to 256 tiles of 192x192 (K >= 1024), or whole rounds in
+    # place of 64x64 tiles: configuration 10.
     for shape in [(3000, 3000, 3000), (3008, 3008, 3008), (3072, 3072, 1024), (2976, 2976, 2976),
-                  (1536, 6144, 4096), (2880, 3264, 2048)]:
+                  (1536, 6144, 4096), (2880, 3264, 2048), (6144, 3072, 2048), (4608, 6144, 2048),
+                  (9216, 3072, 2048), (3072, 9216, 1024)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_192x192_DL, 8, 1), shape
+    assert plan(4608, 4608, 4096)[2] == sg.CFG_64x64_PF2      # 2.25 rounds
+    assert plan(6144, 6144, 4096)[2] == sg.CFG_128x128_DL     # four rounds, well-filled 128x128 grid
+    assert plan(6144, 3072, 512)[2] != sg.CFG_192x192_DL      # short K
     for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096), (2048, 2048, 2044)]:
         assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL), shape
     assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
