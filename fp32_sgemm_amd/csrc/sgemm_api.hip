@@ -330,7 +330,7 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill
-// theirs, to 192x192 tiles for grids of one round of them, from the 128x128
+// theirs, to 192x192 tiles for grids of whole rounds of them, from the 128x128
 // and 64x64 kernels to configurations 8 and 9, from an unevenly spread
 // configuration 9 back to a K split, and from a configuration 9 grid that is
 // one round of 128x128 tiles to those (reported as SGEMM_F32_MFMA_TUNED when
