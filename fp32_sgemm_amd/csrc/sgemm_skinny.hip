@@ -10,15 +10,24 @@
 // Matmul Kernel Gets Fast", section 15.)
 //
 // Work decomposition.  A work-group owns a 64-column strip of C and one of
-// `splits` contiguous ranges of K; its 4 waves split that range again.  The
+// `splits` contiguous ranges of K; its 4 waves split that range again, each
+// streaming its part in batches of 16 rows, two batches in flight.  The
 // partial strips of the splits go to the call's scratch and a second kernel
 // adds them in split order and finishes C (with one split, the first kernel
-// finishes C itself).  Measured alternatives, 16 x 4096 x 4096 with B over
-// 6-7 copies (past the Infinity Cache).  Calls back to back between one pair
-// of events:
+// finishes C itself).  B is read once, so its loads are marked non-temporal:
+// through the library, 16 x 4096 x 4096 with B over 7 copies (past the
+// Infinity Cache), calls back to back between one pair of events, 20.6-20.9
+// us per call with plain loads and batches of 32 rows, 19.2-19.7 with
+// non-temporal loads, 17.7-18.6 with batches of 16 rows as well (8 x 4096 x
+// 4096: 20.1 -> 17.5-17.6; 16 x 11008 x 4096: 49.0 -> 46.4; bit for bit the
+// same sums on the 4096-wide shapes); batches of 48 or 64 rows were slower
+// (19.3, 24.9), and so were four work-groups per CU (21.4) or one (21.3),
+// except at N = 11008 (42.9 with four).  Measured alternatives before those
+// changes, the same workload:
 //   - this form, 8 splits: 18.9-19.0 us per call, its first kernel alone
 //     16.8 us; a kernel that only reads B with the same decomposition takes
-//     14.7 us and the fastest plain read of B found 12.6 us;
+//     14.7 us and the fastest plain read of B found 12.6 us (12.3 with
+//     non-temporal loads);
 //   - the same kernels fused, the last split of each strip adding the others'
 //     partials once their flags show the call's epoch (agent-scope coherent
 //     stores and loads, no fences): 19.3-19.4 us, the waiting tail costs more
@@ -71,7 +80,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t sk_rsrc(const float *base, int
 constexpr int SK_NW = 4;                 // waves per work-group
 constexpr int SK_NT = SK_NW * 64;
 constexpr int SK_BN = 64;                // columns of C per work-group
-constexpr int SK_U = 2;                  // 16-row blocks per batch
+constexpr int SK_U = 1;                  // 16-row blocks per batch
 constexpr int SK_ROWS = SK_U * 16;       // rows of B per batch
 
 struct SkinnyArgs {
@@ -83,23 +92,27 @@ struct SkinnyArgs {
 
 // Four consecutive elements of one row at byte offset `off` of resource `r`,
 // starting `col` elements into the row; elements at or past `limit` read as
-// zero.  VEC: one 16-byte load when the group lies inside.
-template <bool VEC>
+// zero.  VEC: one 16-byte load when the group lies inside.  AUX: the loads'
+// cache-policy bits.
+template <bool VEC, int AUX>
 __device__ __forceinline__ float4 load_group(__amdgpu_buffer_rsrc_t r, int off, int col, int limit) {
     float4 v;
     if (VEC && col + 3 < limit) {
-        const f32x4v w = sk_buffer_load_v4f32(r, off, 0, 0);
+        const f32x4v w = sk_buffer_load_v4f32(r, off, 0, AUX);
         v = make_float4(w[0], w[1], w[2], w[3]);
     } else if (VEC && col >= limit) {
         v = make_float4(0.f, 0.f, 0.f, 0.f);
     } else {
-        v.x = sk_buffer_load_f32(r, col + 0 < limit ? off + 0 : kOff, 0, 0);
-        v.y = sk_buffer_load_f32(r, col + 1 < limit ? off + 4 : kOff, 0, 0);
-        v.z = sk_buffer_load_f32(r, col + 2 < limit ? off + 8 : kOff, 0, 0);
-        v.w = sk_buffer_load_f32(r, col + 3 < limit ? off + 12 : kOff, 0, 0);
+        v.x = sk_buffer_load_f32(r, col + 0 < limit ? off + 0 : kOff, 0, AUX);
+        v.y = sk_buffer_load_f32(r, col + 1 < limit ? off + 4 : kOff, 0, AUX);
+        v.z = sk_buffer_load_f32(r, col + 2 < limit ? off + 8 : kOff, 0, AUX);
+        v.w = sk_buffer_load_f32(r, col + 3 < limit ? off + 12 : kOff, 0, AUX);
     }
     return v;
 }
+
+// B is read once: its loads are marked non-temporal.
+constexpr int kStreamAux = 2;
 
 struct Batch {
     float4 a[SK_U];
@@ -121,10 +134,10 @@ __device__ __forceinline__ void load_batch(const GemmArgs &g, int n0, int kb, in
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = u * 16 + 4 * h + q;                  // row of B within the batch
-            bt.b[u][q] = load_group<VEC>(rb, (int)((r * g.ldb + 4 * j) * 4), 4 * j, r < rows ? cols : 0);
+            bt.b[u][q] = load_group<VEC, kStreamAux>(rb, (int)((r * g.ldb + 4 * j) * 4), 4 * j, r < rows ? cols : 0);
         }
         const int k = u * 16 + 4 * h;                          // first k of this lane's A group
-        bt.a[u] = load_group<VEC>(ra, (int)((j * g.lda + k) * 4), k, j < g.M ? rows : 0);
+        bt.a[u] = load_group<VEC, 0>(ra, (int)((j * g.lda + k) * 4), k, j < g.M ? rows : 0);
     }
 }
 
