@@ -470,17 +470,20 @@ void sgemm_big_kernel(GemmArgs g, int tiles_m, int tiles_n, int group_m) {
     else big_tile<LA, LB, false, TS, KG>(g, m0, n0, smem);
 }
 
-// Two groups of waves per 64 x 64 tile (KG = 2) when the grid has at most one
-// tile per compute unit of the device.
+// Two groups of waves per tile (KG = 2) when the grid has at most one tile per
+// compute unit of the device: on 64 x 64 tiles, and on 128 x 128 tiles with K
+// of at least 2048 (there, same box, TFLOP/s, one group -> two: 2048 x 2048 x
+// 4096 143.2 -> 145.0, 1024 x 4096 x 4096 143.2 -> 145.3, 4096 x 1024 x 4096
+// 143.5 -> 145.3, 2048^3 139.6 -> 140.4; at K = 1024 132.6 -> 131.6).
 template <int LA, int LB, int TS>
 hipError_t launch(const GemmArgs &g, int group_m, hipStream_t stream) {
     const int tiles_m = (g.M + TS - 1) / TS, tiles_n = (g.N + TS - 1) / TS;
     const int tiles = tiles_m * tiles_n;
-    if constexpr (TS == 64) {
+    if constexpr (TS == 64 || TS == 128) {
         int cus = 0;
         const hipError_t e = compute_units(&cus);
         if (e != hipSuccess) return e;
-        if (tiles <= cus) {
+        if (tiles <= cus && (TS == 64 || g.K >= 2048)) {
             hipLaunchKernelGGL((sgemm_big_kernel<LA, LB, TS, 2>), dim3(tiles), dim3(2 * NT), 0, stream, g, tiles_m,
                                tiles_n, group_m);
             return hipGetLastError();

@@ -270,7 +270,10 @@ BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024),
               (260, 516, 20), (252, 256, 36), (516, 260, 100), (4, 8, 4), (132, 388, 52), (124, 132, 16),
               (68, 60, 28),
               # 192x192 tiles: whole, and edges of 4 to 188
-              (384, 576, 48), (196, 388, 20), (580, 200, 116)]
+              (384, 576, 48), (196, 388, 20), (580, 200, 116),
+              # K >= 2048 on a grid of at most one tile per CU: two groups of
+              # waves per 128x128 tile (and per 64x64 tile)
+              (384, 640, 2068)]
 
 
 @pytest.mark.parametrize("cfg", BIG_CFGS)

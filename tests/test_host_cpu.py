@@ -73,12 +73,12 @@ def test_lds_poison_copy_exports_the_same_interface(sg):
     assert set(_declared_functions()) <= exported
 
 
-@pytest.mark.parametrize("src,kernels", [("sgemm_big.hip", 20), ("gemm16.hip", 26)])
+@pytest.mark.parametrize("src,kernels", [("sgemm_big.hip", 24), ("gemm16.hip", 26)])
 def test_lds_poison_flag_fills_lds_with_nan(tmp_path, src, kernels):
     """The debug flag really plants the NaN fill: the device code of the
     kernels built with SGEMM_LDS_POISON holds the quiet-NaN constant once per
     LDS-using kernel instance (4 tile sizes x 4 operand forms of the
-    direct-to-LDS kernel, plus its two-group 64x64 form x 4; in the 16-bit
+    direct-to-LDS kernel, plus its two-group 64x64 and 128x128 forms x 4; in the 16-bit
     GEMM, the register-staged 128 x 128 kernel x 2 formats and the
     direct-to-LDS kernel x 3 tile sizes x 2 formats x A and B each K-major or
     read along x), and the product build holds none."""
