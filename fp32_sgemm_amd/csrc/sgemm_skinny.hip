@@ -22,7 +22,8 @@
 // 4096: 20.1 -> 17.5-17.6; 16 x 11008 x 4096: 49.0 -> 46.4; bit for bit the
 // same sums on the 4096-wide shapes); batches of 48 or 64 rows were slower
 // (19.3, 24.9), and so were four work-groups per CU (21.4) or one (21.3),
-// except at N = 11008 (42.9 with four).  Measured alternatives before those
+// except at N = 11008 (42.9 with four), and 2 or 8 waves per work-group
+// (23.6, 19.1).  Measured alternatives before those
 // changes, the same workload:
 //   - this form, 8 splits: 18.9-19.0 us per call, its first kernel alone
 //     16.8 us; a kernel that only reads B with the same decomposition takes
