@@ -91,6 +91,12 @@ struct Args16 {
                             // that reads B as given, K x N, N-major, row stride ldb
     float *C;
     int64_t lda, ldb, ldc;
+    // Direct-to-LDS kernel, K split over work-groups: work-group split s of a
+    // tile takes k in [s k_split, (s + 1) k_split) (a multiple of BK) and
+    // writes its partial tile at C + s c_split.  Without a split k_split = K
+    // and c_split = 0.
+    int k_split;
+    int64_t c_split;
 };
 
 template <bool F16>
@@ -460,9 +466,14 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
     using D = DLG<TS>;
     __shared__ __attribute__((aligned(1024))) unsigned char smem[dl::NU * D::UNIT];
     poison_lds<sizeof(smem)>(smem);
+    // Work-group -> (split of K, tile): the splits of one tile are whole
+    // grids apart.
+    const int tiles = tiles_m * tiles_n;
+    const int split = blockIdx.x / tiles;
     int tm, tn;
-    tile_of_block(blockIdx.x, tiles_m, tiles_n, TS == 128 ? 8 : 4, tm, tn);
+    tile_of_block(blockIdx.x - split * tiles, tiles_m, tiles_n, TS == 128 ? 8 : 4, tm, tn);
     const int m0 = tm * G::BM, n0 = tn * G::BN;
+    const int k0 = split * g.k_split;
     const int tid = threadIdx.x;
     // The wave index is uniform: kept in a scalar register, the LDS bases of
     // the loads need no per-load transfer from a vector register.
@@ -470,8 +481,8 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
     const int wm = wave >> 1, wn = wave & 1;
     const int h = lane >> 5, l32 = lane & 31;
     const int rows_a = min(G::BM, g.M - m0), rows_b = min(G::BN, g.N - n0);
-    const uint16_t *Ab = AXM ? g.A + m0 : g.A + (int64_t)m0 * g.lda;
-    const uint16_t *Bb = BXM ? g.B + n0 : g.B + (int64_t)n0 * g.ldb;
+    const uint16_t *Ab = AXM ? g.A + m0 + (int64_t)k0 * g.lda : g.A + (int64_t)m0 * g.lda + k0;
+    const uint16_t *Bb = BXM ? g.B + n0 + (int64_t)k0 * g.ldb : g.B + (int64_t)n0 * g.ldb + k0;
     // Any transposing read needs every load into LDS untracked (see above).
     constexpr bool UNTRACKED = AXM || BXM;
 
@@ -578,7 +589,7 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
         acc[i / G::BLK][i % G::BLK] = mfma16<F16>(fa[i / G::BLK], fb[i % G::BLK], acc[i / G::BLK][i % G::BLK]);
     };
 
-    const int nk = g.K / dl::BK;
+    const int nk = min(g.k_split, g.K - k0) / dl::BK;
     // Before the first slice: A and B of slice 0, A of slice 1 (the last
     // issued, so that slice 0 can start while it is in flight).
 #pragma unroll
@@ -653,7 +664,9 @@ gemm16_dl_kernel(Args16 g, int tiles_m, int tiles_n) {
 #pragma unroll
     for (int i = 0; i < G::BLK * G::BLK; ++i) mfma_one(fya, fyb, i);
 
-    big_epilogue<TS>(g, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
+    Args16 gc = g;
+    gc.C = g.C + split * g.c_split;
+    big_epilogue<TS>(gc, m0, n0, rows_a, rows_b, wm, wn, h, l32, acc);
 }
 
 // K-major, K-padded copy of a 16-bit operand: dst[x * Kp + k] = op(x, k) for
@@ -712,6 +725,31 @@ hipError_t pack(const uint16_t *src, int64_t ld, bool xmajor, int X, int K, uint
     return hipGetLastError();
 }
 
+// C = alpha * (the splits' partial products, added in split order) + beta * C,
+// C read only when beta != 0.  The partials' loads go out eight at a time
+// before their additions.
+__global__ __launch_bounds__(256) void reduce16_kernel(const float *ws, int splits, int M, int N, float alpha,
+                                                       float beta, float *C, int64_t ldc) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+         t += (int64_t)gridDim.x * blockDim.x) {
+        float s = 0.f;
+        for (int sp0 = 0; sp0 < splits; sp0 += 8) {
+            float v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) v[j] = ws[(int64_t)(sp0 + j < splits ? sp0 + j : splits - 1) * total + t];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) s += v[j];
+        }
+        const int64_t i = t / N, jj = t - i * N;
+        float *p = C + i * ldc + jj;
+        float r = alpha * s;
+        if (beta != 0.f) r = fmaf(beta, *p, r);
+        *p = r;
+    }
+}
+
 }  // namespace
 
 // The direct-to-LDS kernel's epilogue addresses a tile of C with 32-bit
@@ -753,6 +791,30 @@ int gemm16_ring_tile(int M, int N) {
     return t192 <= t128 ? 192 : 128;
 }
 
+// K split of a 128 x 128 grid of fewer than 128 tiles: splits of at least
+// kSplit16MinK of K each, about one work-group per CU in all, and at most as
+// many as keep the partial products (written once, read once) within half
+// the operands' bytes.  Same-box microseconds, bf16 NT, beta 0, no split ->
+// this rule (a first rule with up to two work-groups per CU and partials up
+// to the operands' bytes in brackets): 16 x 4096 x 4096 33.3 -> 12.4 (13.2);
+// 1 x 4096 x 4096 31.2 -> 12.2; 16 x 8192 x 8192 56.1 -> 26.1 (26.2); 64 x
+// 4096 x 4096 33.9 -> 14.7 (16.9); 128 x 4096 x 4096 34.3 -> 18.0 (24.1); 256
+// x 4096 x 4096 34.0 -> 21.9 (33.5); 256 x 256 x 4096 23.1 -> 11.8 (11.6);
+// 128 x 8192 x 4096 -> 22.9 (29.0); 512 x 1024 x 4096 -> 19.9 (33.6).  torch's
+// mm of the same operands took 24-29 us on each.
+constexpr int kSplit16Slots = 256;
+constexpr int kSplit16MinK = 256;
+int gemm16_splits(int M, int N, int Kp) {
+    const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+    if (tiles >= kSplit16Slots / 2) return 1;
+    int64_t splits = (kSplit16Slots + tiles - 1) / tiles;
+    if (splits > Kp / kSplit16MinK) splits = Kp / kSplit16MinK;
+    const int64_t cap = ((int64_t)M + N) * Kp * 2 / ((int64_t)2 * M * N * 4);
+    if (splits > cap) splits = cap;
+    if (splits < 2) return 1;
+    return (int)splits;
+}
+
 int64_t gemm16_grid(int M, int N) { return (int64_t)((M + BM - 1) / BM) * ((N + BN - 1) / BN); }
 
 int64_t gemm16_workspace_bytes(int ta, int tb, int M, int N, int K, const void *A, int64_t lda, const void *B,
@@ -785,11 +847,34 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     a.C = g16.C; a.ldc = g16.ldc;
     a.A = static_cast<const uint16_t *>(A); a.lda = g16.lda;
     a.B = static_cast<const uint16_t *>(B); a.ldb = g16.ldb;
+    a.k_split = Kp;
+    a.c_split = 0;
+    // Tile size, and a K split for small 128 x 128 grids (the partial tiles
+    // go to the call's scratch, after any packed operands).
+    const int ts = ring ? gemm16_ring_tile(M, N) : 0;
+    int splits = ts == 128 && c_tile_fits(N) ? gemm16_splits(M, N, Kp) : 1;
+    if (splits > 1) {
+        a.k_split = (Kp / splits + BK - 1) / BK * BK;
+        splits = (Kp + a.k_split - 1) / a.k_split;
+    }
+    const int64_t pack_bytes = pa || pb ? gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb, axm, bxm) : 0;
+    const int64_t part_bytes = splits > 1 ? (int64_t)splits * M * N * 4 : 0;
     void *ws = nullptr;
-    if (pa || pb) {
-        const int64_t bytes = gemm16_workspace_bytes(ta, tb, M, N, K, A, g16.lda, B, g16.ldb, axm, bxm);
-        hipError_t e = scratch_acquire(g16.scratch, (size_t)bytes, stream, &ws);
+    if (pack_bytes + part_bytes > 0) {
+        hipError_t e = scratch_acquire(g16.scratch, (size_t)(pack_bytes + part_bytes), stream, &ws);
         if (e != hipSuccess) return e;
+    }
+    float *partials = nullptr;
+    if (splits > 1) {
+        partials = reinterpret_cast<float *>(static_cast<unsigned char *>(ws) + pack_bytes);
+        a.C = partials;
+        a.ldc = N;
+        a.alpha = 1.f;
+        a.beta = 0.f;
+        a.c_split = (int64_t)M * N;
+    }
+    if (pa || pb) {
+        hipError_t e;
         unsigned char *p = static_cast<unsigned char *>(ws);
         if (pa) {
             uint16_t *dst = reinterpret_cast<uint16_t *>(p);
@@ -816,12 +901,12 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
     }
     hipError_t e;
     if (ring) {
-        auto go = [&](auto ts, auto f16, auto ax, auto bx) {
-            constexpr int TS = decltype(ts)::value;
+        auto go = [&](auto tsc, auto f16, auto ax, auto bx) {
+            constexpr int TS = decltype(tsc)::value;
             const int tiles_m = (M + TS - 1) / TS, tiles_n = (N + TS - 1) / TS;
             hipLaunchKernelGGL(
                 (gemm16_dl_kernel<TS, decltype(f16)::value, decltype(ax)::value, decltype(bx)::value>),
-                dim3(tiles_m * tiles_n), dim3(NT), 0, stream, a, tiles_m, tiles_n);
+                dim3(tiles_m * tiles_n * splits), dim3(NT), 0, stream, a, tiles_m, tiles_n);
         };
         auto pick_b = [&](auto ts, auto f16, auto ax) {
             if (bxm) go(ts, f16, ax, std::true_type());
@@ -835,11 +920,18 @@ hipError_t launch_gemm16(int kind, const GemmArgs &g16, hipStream_t stream) {
             if (kind == GEMM16_F32_F16) pick_a(ts, std::true_type());
             else pick_a(ts, std::false_type());
         };
-        const int ts = gemm16_ring_tile(M, N);
         if (ts == 256) pick_f(std::integral_constant<int, 256>());
         else if (ts == 192) pick_f(std::integral_constant<int, 192>());
         else pick_f(std::integral_constant<int, 128>());
         e = hipGetLastError();
+        if (e == hipSuccess && splits > 1) {
+            const int64_t total = (int64_t)M * N;
+            int64_t blocks = (total + 255) / 256;
+            if (blocks > 4096) blocks = 4096;
+            hipLaunchKernelGGL(reduce16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, partials, splits, M, N,
+                               g16.alpha, g16.beta, g16.C, (int64_t)g16.ldc);
+            e = hipGetLastError();
+        }
     } else {
         const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
         const dim3 grid(tiles_m * tiles_n);

@@ -35,7 +35,10 @@
  * transposed (trans_a == 1, K x M) or B as given (trans_b == 0, K x N), is
  * read in place too when it is aligned as above, its M or N is a multiple of
  * 8 and ldc is below about 2.1 million (256 rows of C addressable with 32-bit
- * byte offsets).
+ * byte offsets).  Grids of fewer than 128 tiles of 128 x 128 (small M or N)
+ * split K over work-groups: their FP32 partial products, splits x M x N
+ * floats, take scratch the same way, and a second kernel adds them in split
+ * order and applies alpha and beta.
  *
  * Ownership and execution: device pointers owned by the caller, asynchronous on
  * `stream`, no synchronisation, thread-safe; as sgemm_f32.

@@ -154,8 +154,8 @@ def test_gemm16_c_stride_past_32bit_tile_offsets(sg, kind, form, K):
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-@pytest.mark.parametrize("shape", [(140, 130, 128), (3072, 3000, 128), (4096, 4096, 128)],
-                         ids=["tile128", "tile192", "tile256"])
+@pytest.mark.parametrize("shape", [(140, 130, 128), (3072, 3000, 128), (4096, 4096, 128), (16, 4096, 4096)],
+                         ids=["tile128", "tile192", "tile256", "split_k"])
 def test_gemm16_beta_zero_ignores_nan_c(sg, kind, shape):
     """beta = 0: C is written without being read (NaN there stays out of the
     result) on each tile size of the direct-to-LDS kernel."""
@@ -272,6 +272,32 @@ def test_gemm16_192_tiles_real(sg, kind, form):
     assert ok, info
 
 
+SPLIT_SHAPES = [(16, 4096, 4096), (1, 1000, 2048), (64, 2048, 8192)]
+
+
+@pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
+@pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
+@pytest.mark.parametrize("shape", SPLIT_SHAPES, ids=[f"{m}x{n}x{k}" for m, n, k in SPLIT_SHAPES])
+def test_gemm16_split_k(sg, kind, form, shape):
+    """Grids of few 128 x 128 tiles split K over work-groups (8 or 16
+    splits here): partial tiles in the call's scratch, added in split order
+    by a second kernel, which applies alpha and beta.  Integer inputs bit for
+    bit, real inputs within the bound."""
+    M, N, K = shape
+    ta, tb = form
+    say(f"[g16_split] kind={kind} {form} {shape}")
+    A, B, C0 = _inputs16(M, N, K, "int4", kind, 90 + M + 2 * ta + tb)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.0, -1.0)
+    assert st == 0
+    ok, info = check16_logical(C, A, B, kind, 1.0, -1.0, C0, exact=True)
+    assert ok, info
+    A, B, C0 = _inputs16(M, N, K, "normal", kind, 95 + M + 2 * ta + tb)
+    st, C, As, Bs = run16(sg, kind, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check16_logical(C, A, B, kind, 1.5, -0.5, C0, exact=False)
+    assert ok, info
+
+
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 @pytest.mark.parametrize("K", [8, 64, 192])
 def test_gemm16_big_tiles_short_k_bitexact(sg, K, form):
@@ -289,8 +315,8 @@ def test_gemm16_big_tiles_short_k_bitexact(sg, K, form):
 
 
 @pytest.mark.parametrize("kind", KINDS, ids=KIND_IDS)
-@pytest.mark.parametrize("shape", [(150, 140, 96), (3072, 3072, 64), (4096, 4096, 64)],
-                         ids=["small_grid", "tile192", "big_tiles"])
+@pytest.mark.parametrize("shape", [(150, 140, 96), (3072, 3072, 64), (4096, 4096, 64), (16, 2048, 2048)],
+                         ids=["small_grid", "tile192", "big_tiles", "split_k"])
 def test_gemm16_negative_alpha_zero_sums_bitexact(sg, kind, shape):
     """alpha < 0 with beta = 0: exactly zero sums are alpha * (+0) = -0, the
     oracle's value, on each tile size of the direct-to-LDS kernel."""

@@ -132,7 +132,7 @@ def test_poisoned_valu_and_skinny(plib, variant):
 # 16-bit inputs: (M, N, K); 4096 x 4096 runs the larger-tile kernel (at least
 # 256 tiles of 256 x 256), the others the 128 x 128 kernel.
 G16_SHAPES = [(4096, 4096, 8), (4096, 4096, 192), (4096, 4096, 520), (4096, 3904, 576), (300, 260, 700),
-              (128, 128, 64), (1000, 1000, 576), (2048, 1040, 192), (3000, 2904, 192)]
+              (128, 128, 64), (1000, 1000, 576), (2048, 1040, 192), (3000, 2904, 192), (16, 2048, 2048)]
 
 
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
@@ -144,7 +144,7 @@ def test_poisoned_16bit_kernels(plib, kind, shape, form):
     when K is a multiple of 64, packed otherwise; 256 x 256 tiles on the
     4096-wide grids, 192 x 192 on 3000 x 2904, 128 x 128 tiles (two
     work-groups per CU) on the others, with edge tiles and one to nine
-    slices."""
+    slices; 16 x 2048 x 2048 splits K over 8 work-groups per tile."""
     M, N, K = shape
     ta, tb = form
     say(f"[poison_16] kind {kind} {shape} form={form}")
