@@ -88,7 +88,7 @@ hipError_t scratch_acquire(const Scratch &s, size_t bytes, hipStream_t stream, v
 hipError_t scratch_release(const Scratch &s, void *p, hipStream_t stream);
 
 // Scratch bytes that a launch will acquire (host side, no HIP call except the
-// occupancy query of the stream-K plan): the M <= 16 kernel, an MFMA plan, and
+// occupancy query of the stream-K plan): the M <= 32 kernel, an MFMA plan, and
 // the 16-bit GEMM.
 int64_t skinny_scratch_bytes(const GemmArgs &g);
 hipError_t mfma_config_scratch_bytes(const GemmArgs &g, int config, int splits, int64_t *bytes);
@@ -128,7 +128,7 @@ int64_t skinny_grid(int M, int N);
 
 // Largest M the skinny kernel handles, and whether its 32-bit offsets cover
 // the strides.
-constexpr int kSkinnyMaxM = 16;
+constexpr int kSkinnyMaxM = 32;
 bool skinny_fits(int lda, int ldb);
 
 // ---------------------------------------------------------------------------

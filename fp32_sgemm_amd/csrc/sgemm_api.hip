@@ -326,7 +326,7 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
     return Plan{SGEMM_F32_MFMA_TUNED, 8, p.group_m, 1};
 }
 
-// The automatic choice: the M <= 16 kernel and the 4-byte-load kernels as in
+// The automatic choice: the M <= 32 kernel and the 4-byte-load kernels as in
 // default_plan; for 16-byte-aligned operands the tuning table's entry for the
 // shape class when there is one, then the switch to 64x64 tiles for 128x128
 // grids that fill their rounds poorly, to 256x256 tiles for grids that fill

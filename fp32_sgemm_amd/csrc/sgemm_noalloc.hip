@@ -1,5 +1,5 @@
 // The allocation-free entry point: sgemm_f32 whose scratch (the split partial
-// sums of the M <= 16 kernel and of tuned split-K plans) is a fixed array in
+// sums of the M <= 32 kernel and of tuned split-K plans) is a fixed array in
 // the library's device memory instead of a stream-ordered allocation.
 //
 // `scratch` below is a device variable: in host code its name is only a

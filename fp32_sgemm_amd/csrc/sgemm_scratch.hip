@@ -1,4 +1,4 @@
-// Scratch memory of one call (split partial sums of the M <= 16 kernel and of
+// Scratch memory of one call (split partial sums of the M <= 32 kernel and of
 // split-K plans, the stream-K plan's partial tiles, the 16-bit GEMM's packed
 // operands).
 //

@@ -1,4 +1,4 @@
-// FP32 GEMM for M <= 16 (a short, wide A times a tall B), on 16x16x4 MFMA.
+// FP32 GEMM for M <= 32 (a short, wide A times a tall B), on 16x16x4 MFMA.
 //
 // With M = 16 and N = K = 4096 the product does 8 FLOP per byte of B it must
 // stream, below the MI355X ridge point of about 20 FLOP per byte, so the kernel
@@ -45,6 +45,19 @@
 //     device-scope counter): no gain with coherent partial stores and loads,
 //     38.8 us with release/acquire fences (each fence writes back or
 //     invalidates a whole L2).
+//
+// M = 17..32 takes two blocks of 16 rows of A (twice the MFMAs per byte of B;
+// at 32 rows the fp32 MFMA work per SIMD is about 80 % of the time the SIMD's
+// share of HBM bandwidth takes to stream the batches, so loads must stay in
+// flight under the MFMAs).  Grids of at most 64 strips keep three batches in
+// flight per wave, wider grids two.  Per call, B over 7 copies, against the
+// plan such shapes took before (64 x 64 MFMA tiles, K split 4 or 8 ways): 17 x 4096 x 4096
+// 24.2 -> 20.1 us, 32 x 4096 x 4096 24.1 -> 21.5, 32 x 2048 x 8192 27.4 ->
+// 22.1, 32 x 4096 x 11008 51.5 -> 45.4, 20 x 11008 x 4096 54.4 -> 55.6; two
+// batches in flight everywhere: 21.6, 23.0, 23.5, 46.1, 54.5; three
+// everywhere with two work-groups per CU (182 registers per lane): 20 x 11008
+// x 4096 at 66.2 (516 work-groups, 4 past one round).  M <= 16 with three in
+// flight: 8 x 4096 x 4096 18.1 -> 17.2 us, 16 x 4096 x 4096 17.9 -> 17.6.
 //
 // Inner step.  For a block of 16 rows of B starting at kb, lane l (h = l/16,
 // j = l%16) loads columns 4j..4j+3 of rows kb + 4h + q, q = 0..3 (four 16-byte
@@ -115,15 +128,22 @@ __device__ __forceinline__ float4 load_group(__amdgpu_buffer_rsrc_t r, int off, 
 // B is read once: its loads are marked non-temporal.
 constexpr int kStreamAux = 2;
 
+// Grids of at most this many strips keep three batches in flight per wave,
+// wider ones two (their splits are longer and the third batch's registers
+// cost more than it hides).
+constexpr int kDeepStrips = 64;
+
+// MB blocks of 16 rows of A (M <= 16 MB); row m of A is lane m % 16's in block m / 16.
+template <int MB>
 struct Batch {
-    float4 a[SK_U];
+    float4 a[SK_U][MB];
     float4 b[SK_U][4];
 };
 
 // Loads the batch whose first row of B (column of A) is kb; rows at or past
 // kend belong to another split or lie past K and read as zero.
-template <bool VEC>
-__device__ __forceinline__ void load_batch(const GemmArgs &g, int n0, int kb, int kend, int lane, Batch &bt) {
+template <bool VEC, int MB>
+__device__ __forceinline__ void load_batch(const GemmArgs &g, int n0, int kb, int kend, int lane, Batch<MB> &bt) {
     const int rows = min(SK_ROWS, kend - kb);
     const int cols = min(SK_BN, g.N - n0);
     const __amdgpu_buffer_rsrc_t rb = sk_rsrc(g.B + (int64_t)kb * g.ldb + n0,
@@ -137,29 +157,40 @@ __device__ __forceinline__ void load_batch(const GemmArgs &g, int n0, int kb, in
             const int r = u * 16 + 4 * h + q;                  // row of B within the batch
             bt.b[u][q] = load_group<VEC, kStreamAux>(rb, (int)((r * g.ldb + 4 * j) * 4), 4 * j, r < rows ? cols : 0);
         }
-        const int k = u * 16 + 4 * h;                          // first k of this lane's A group
-        bt.a[u] = load_group<VEC, 0>(ra, (int)((j * g.lda + k) * 4), k, j < g.M ? rows : 0);
-    }
-}
-
-__device__ __forceinline__ void consume_batch(const Batch &bt, f32x4v (&acc)[4]) {
+        const int k = u * 16 + 4 * h;                          // first k of this lane's A groups
 #pragma unroll
-    for (int u = 0; u < SK_U; ++u) {
-        const float av[4] = {bt.a[u].x, bt.a[u].y, bt.a[u].z, bt.a[u].w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float4 b = bt.b[u][q];
-            acc[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.x, acc[0], 0, 0, 0);
-            acc[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.y, acc[1], 0, 0, 0);
-            acc[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.z, acc[2], 0, 0, 0);
-            acc[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.w, acc[3], 0, 0, 0);
+        for (int mb = 0; mb < MB; ++mb) {
+            const int m = 16 * mb + j;
+            bt.a[u][mb] = load_group<VEC, 0>(ra, (int)((m * g.lda + k) * 4), k, m < g.M ? rows : 0);
         }
     }
 }
 
-template <bool VEC>
-__global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(SkinnyArgs sa, int strips) {
-    __shared__ float red[SK_NW][16 * SK_BN];
+template <int MB>
+__device__ __forceinline__ void consume_batch(const Batch<MB> &bt, f32x4v (&acc)[MB][4]) {
+#pragma unroll
+    for (int u = 0; u < SK_U; ++u) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            const float av[4] = {bt.a[u][mb].x, bt.a[u][mb].y, bt.a[u][mb].z, bt.a[u][mb].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const float4 b = bt.b[u][q];
+                acc[mb][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.x, acc[mb][0], 0, 0, 0);
+                acc[mb][1] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.y, acc[mb][1], 0, 0, 0);
+                acc[mb][2] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.z, acc[mb][2], 0, 0, 0);
+                acc[mb][3] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], b.w, acc[mb][3], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// DEPTH batches in flight per wave (2 or 3).  Two blocks of A with three
+// batches in flight would take 182 registers per lane and fit only two
+// work-groups per compute unit: the launch bound asks for three.
+template <bool VEC, int MB, int DEPTH>
+__global__ __launch_bounds__(SK_NT, MB == 2 ? 3 : 1) void sgemm_skinny_kernel(SkinnyArgs sa, int strips) {
+    __shared__ float red[SK_NW][16 * MB * SK_BN];
     poison_lds<sizeof(red)>(red);
     const GemmArgs &g = sa.g;
     // Work-group -> (split, strip); consecutive strips stay on one XCD.
@@ -177,32 +208,56 @@ __global__ __launch_bounds__(SK_NT) void sgemm_skinny_kernel(SkinnyArgs sa, int 
     const int bbeg = wave * per_wave;
     const int bend = min(batches, bbeg + per_wave);
 
-    f32x4v acc[4];
+    f32x4v acc[MB][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    Batch b0, b1;
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[mb][e] = f32x4v{0.f, 0.f, 0.f, 0.f};
     int b = bbeg;
-    if (b < bend) load_batch<VEC>(g, n0, kbeg + b * SK_ROWS, kend, lane, b0);
-    // The loads in the loop are unconditional (past the end they re-read the
+    // The loads in the loops are unconditional (past the end they re-read the
     // wave's last batch, which is then not consumed) so the wait counts stay
     // exact.
-    for (; b + 1 < bend; b += 2) {
-        load_batch<VEC>(g, n0, kbeg + (b + 1) * SK_ROWS, kend, lane, b1);
-        consume_batch(b0, acc);
-        load_batch<VEC>(g, n0, kbeg + (b + 2 < bend ? b + 2 : bend - 1) * SK_ROWS, kend, lane, b0);
-        consume_batch(b1, acc);
+    auto kof = [&](int bi) { return kbeg + (bi < bend ? bi : bend - 1) * SK_ROWS; };
+    if constexpr (DEPTH == 2) {
+        Batch<MB> b0, b1;
+        if (b < bend) load_batch<VEC>(g, n0, kof(b), kend, lane, b0);
+        for (; b + 1 < bend; b += 2) {
+            load_batch<VEC>(g, n0, kof(b + 1), kend, lane, b1);
+            consume_batch(b0, acc);
+            load_batch<VEC>(g, n0, kof(b + 2), kend, lane, b0);
+            consume_batch(b1, acc);
+        }
+        if (b < bend) consume_batch(b0, acc);
+    } else {
+        // Three batches in flight: two loaded ahead of the one consumed.
+        Batch<MB> b0, b1, b2;
+        if (b < bend) {
+            load_batch<VEC>(g, n0, kof(b), kend, lane, b0);
+            load_batch<VEC>(g, n0, kof(b + 1), kend, lane, b1);
+        }
+        for (; b + 2 < bend; b += 3) {
+            load_batch<VEC>(g, n0, kof(b + 2), kend, lane, b2);
+            consume_batch(b0, acc);
+            load_batch<VEC>(g, n0, kof(b + 3), kend, lane, b0);
+            consume_batch(b1, acc);
+            load_batch<VEC>(g, n0, kof(b + 4), kend, lane, b1);
+            consume_batch(b2, acc);
+        }
+        if (b < bend) consume_batch(b0, acc);
+        if (b + 1 < bend) consume_batch(b1, acc);
     }
-    if (b < bend) consume_batch(b0, acc);
 
-    // acc[e] register r of lane l holds row 4*(l/16) + r, strip column
-    // 4*(l%16) + e.  Add the waves' partials in wave order.
+    // acc[mb][e] register r of lane l holds row 16*mb + 4*(l/16) + r, strip
+    // column 4*(l%16) + e.  Add the waves' partials in wave order.
     const int h = lane >> 4, j = lane & 15;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][(4 * h + r) * SK_BN + 4 * j + e] = acc[e][r];
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) red[wave][(16 * mb + 4 * h + r) * SK_BN + 4 * j + e] = acc[mb][e][r];
     __syncthreads();
-    constexpr int PER_T = 16 * SK_BN / SK_NT;   // strip elements per thread
+    constexpr int PER_T = 16 * MB * SK_BN / SK_NT;   // strip elements per thread
     float part[PER_T];
 #pragma unroll
     for (int t = 0; t < PER_T; ++t) {
@@ -264,19 +319,24 @@ int64_t skinny_grid(int M, int N) {
 }
 
 bool skinny_fits(int lda, int ldb) {
-    // One batch of B and all 16 rows of A must be addressable with 32-bit
-    // byte offsets.
+    // One batch of B and all kSkinnyMaxM rows of A must be addressable with
+    // 32-bit byte offsets.
     const int64_t limit = (int64_t)1 << 31;
-    return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < limit && ((int64_t)16 * lda + SK_ROWS) * 4 < limit;
+    return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < limit && ((int64_t)kSkinnyMaxM * lda + SK_ROWS) * 4 < limit;
 }
 
 namespace {
+
+// Work-groups wanted per call, for one and for two blocks of 16 rows of A.
+constexpr int kSkinnySlots1 = 512;
+constexpr int kSkinnySlots2 = 512;
 
 // The K split: about two work-groups per compute unit, every split at least
 // 256 rows long.
 void skinny_split(const GemmArgs &g, int *splits_out, int *split_rows_out) {
     const int strips = (g.N + SK_BN - 1) / SK_BN;
-    const int want = (512 + strips - 1) / strips;
+    const int slots = g.M > 16 ? kSkinnySlots2 : kSkinnySlots1;
+    const int want = (slots + strips - 1) / strips;
     const int max_splits = (g.K + 255) / 256;
     int splits = want < max_splits ? want : max_splits;
     if (splits < 1) splits = 1;
@@ -308,8 +368,19 @@ hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) 
         if (e != hipSuccess) return e;
     }
     const dim3 grid(strips * splits);
-    if (vec_loads) hipLaunchKernelGGL(sgemm_skinny_kernel<true>, grid, dim3(SK_NT), 0, stream, sa, strips);
-    else hipLaunchKernelGGL(sgemm_skinny_kernel<false>, grid, dim3(SK_NT), 0, stream, sa, strips);
+    // One block of 16 rows of A for M <= 16, two for 16 < M <= 32; three
+    // batches in flight on grids of at most kDeepStrips strips.
+    const int mb = g.M > 16 ? 2 : 1;
+    const int depth = strips <= kDeepStrips ? 3 : 2;
+    using Kern = void (*)(SkinnyArgs, int);
+    Kern k;
+    if (vec_loads)
+        k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<true, 2, 3> : sgemm_skinny_kernel<true, 2, 2>)
+                    : (depth == 3 ? sgemm_skinny_kernel<true, 1, 3> : sgemm_skinny_kernel<true, 1, 2>);
+    else
+        k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<false, 2, 3> : sgemm_skinny_kernel<false, 2, 2>)
+                    : (depth == 3 ? sgemm_skinny_kernel<false, 1, 3> : sgemm_skinny_kernel<false, 1, 2>);
+    hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, sa, strips);
     hipError_t e = hipGetLastError();
     if (splits > 1) {
         if (e == hipSuccess) {

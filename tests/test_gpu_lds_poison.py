@@ -114,11 +114,11 @@ def test_poisoned_register_staged_kernels(plib, cfg, splits, shape):
         assert ok, (ta, tb, info)
 
 
-@pytest.mark.parametrize("variant", [3, 4])   # the VALU kernel, the M <= 16 kernel
-def test_poisoned_valu_and_skinny(plib, variant):
-    M = 16 if variant == 4 else 300
-    N, K = 1000, 3000
-    say(f"[poison_variant] {variant}")
+@pytest.mark.parametrize("variant,M,N", [(3, 300, 1000), (4, 16, 1000), (4, 24, 1000), (4, 20, 4200)],
+                         ids=["valu", "skinny16", "skinny24", "skinny20_wide"])   # the VALU kernel, the M <= 32 kernel
+def test_poisoned_valu_and_skinny(plib, variant, M, N):
+    K = 3000
+    say(f"[poison_variant] {variant} M={M} N={N}")
     A, B, C0 = _int_inputs(M, N, K, 1800 + variant)
     dA, dB, dC = (torch.from_numpy(x).cuda() for x in (A, B, C0))
     st = plib.sgemm_f32_variant(variant, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), K, dB.data_ptr(), N,

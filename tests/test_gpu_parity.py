@@ -65,7 +65,12 @@ def test_ragged_integer_bitexact(sg, variant, shape):
 
 SKINNY = [(1, 1, 1), (16, 16, 16), (16, 4096, 64), (3, 33, 100), (16, 100, 4099),
           (7, 257, 513), (16, 16, 17), (12, 64, 2000), (5, 130, 777), (16, 65, 1000),
-          (1, 1, 5000), (16, 4096, 300), (16, 2050, 8191)]
+          (1, 1, 5000), (16, 4096, 300), (16, 2050, 8191),
+          # 16 < M <= 32: two blocks of 16 rows of A per work-group
+          (17, 4096, 4096), (24, 100, 4099), (32, 2050, 1000), (20, 130, 777), (32, 16, 17),
+          # 5 and 7 batches per wave (three in flight), and grids of more
+          # than 64 strips (two in flight)
+          (16, 4096, 2560), (31, 4093, 3584), (27, 64, 128), (17, 4160, 1000), (16, 8200, 3000), (9, 4097, 5)]
 
 
 @pytest.mark.parametrize("variant", ["skinny", "auto", "mfma_scalar", "valu"])
@@ -87,13 +92,13 @@ def test_skinny_shapes(sg, variant, shape):
 
 @pytest.mark.parametrize("variant", GENERAL + ["skinny"])
 def test_beta_zero_ignores_nan_c(sg, variant):
-    M = 16 if variant == "skinny" else 150
-    A, B, _ = _inputs(M, 140, 90, "uniform", 11, c0=False)
-    st, C, _ = run_lib(sg, VID[variant], A, B, None, 1.0, 0.0, c_fill=np.nan)
-    assert st == 0
-    assert np.all(np.isfinite(C))
-    ok, info = check_full(C, A, B, 1.0, 0.0, None)
-    assert ok, info
+    for M in ((16, 27) if variant == "skinny" else (150,)):   # one and two blocks of 16 rows
+        A, B, _ = _inputs(M, 140, 90, "uniform", 11, c0=False)
+        st, C, _ = run_lib(sg, VID[variant], A, B, None, 1.0, 0.0, c_fill=np.nan)
+        assert st == 0
+        assert np.all(np.isfinite(C))
+        ok, info = check_full(C, A, B, 1.0, 0.0, None)
+        assert ok, info
 
 
 @pytest.mark.parametrize("variant", GENERAL + ["skinny"])

@@ -145,6 +145,8 @@ def test_kernel_selection(sg):
     assert sg.sgemm_f32_select(1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
     assert sg.sgemm_f32_select(128, 128, 128, 1.0, al, 128, al, 128) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
     assert sg.sgemm_f32_select(16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
+    assert sg.sgemm_f32_select(32, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY   # two blocks of 16 rows
+    assert sg.sgemm_f32_select(33, 4096, 4096, 1.0, al, 4096, al, 4096) != sg.SKINNY
     assert sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096) == sg.MFMA_SCALAR
     assert sg.sgemm_f32_select(4096, 4096, 4097, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
     assert sg.sgemm_f32_select(4096, 4096, 4096, 0.0, al, 4096, al, 4096) == 0
@@ -349,7 +351,7 @@ def test_plan_follows_the_tuning_table(sg):
     for e in table["entries"]:
         M, N, K = e["shape"]
         st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, al, K, al, N)
-        if M <= 16:
+        if M <= 32:
             assert v == sg.SKINNY
             continue
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
