@@ -124,12 +124,18 @@ __device__ __forceinline__ void poison_lds(void *lds) {
 int64_t mfma_large_grid(int M, int N);
 int64_t mfma_small_grid(int M, int N);
 int64_t valu_grid(int M, int N);
-int64_t skinny_grid(int M, int N);
+int64_t skinny_grid(const GemmArgs &g);
 
-// Largest M the skinny kernel handles, and whether its 32-bit offsets cover
-// the strides.
+// The streaming kernels for a few rows of one side: which form serves a
+// product (the plain form with rows of B streamed for M <= kSkinnyMaxM, B
+// given N x K streamed along k for M <= 16, or A streamed along k for N <= 16
+// with C written transposed), or -1 when none does or their 32-bit offsets do
+// not cover the strides.
 constexpr int kSkinnyMaxM = 32;
-bool skinny_fits(int lda, int ldb);
+constexpr int kSkinnyRowsOfB = 0;
+constexpr int kSkinnyBKMajor = 1;
+constexpr int kSkinnyAKMajor = 2;
+int skinny_form(int ta, int tb, int M, int N, int K, int64_t lda, int64_t ldb);
 
 // ---------------------------------------------------------------------------
 // Work-group to output-tile mapping.

@@ -109,9 +109,8 @@ struct Plan {
     int splits;
 };
 
-Plan default_plan(int ta, int tb, int M, int N, const float *A, int lda, const float *B, int ldb) {
-    if (!ta && !tb && M <= sgemm::kSkinnyMaxM && sgemm::skinny_fits(lda, ldb))
-        return Plan{SGEMM_F32_SKINNY, 0, 0, 0};
+Plan default_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
+    if (sgemm::skinny_form(ta, tb, M, N, K, lda, ldb) >= 0) return Plan{SGEMM_F32_SKINNY, 0, 0, 0};
     const int config = prefer_small_tiles(M, N) ? 1 : 0;
     if (!vec_aligned(ta, tb, A, lda, B, ldb)) return Plan{SGEMM_F32_MFMA_SCALAR, config, 8, 1};
     // With 16-byte loads the small tile keeps two slices in flight
@@ -337,7 +336,7 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
 // the plan differs from the default).
 // Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
-    const Plan d = default_plan(ta, tb, M, N, A, lda, B, ldb);
+    const Plan d = default_plan(ta, tb, M, N, K, A, lda, B, ldb);
     if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
     Plan p = d;
     if (kHaveTunedTable) {
@@ -448,9 +447,8 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
             if (sgemm::valu_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
             return to_status(sgemm::launch_valu(g, vec, stream));
         case SGEMM_F32_SKINNY:
-            if (!plain || M > sgemm::kSkinnyMaxM || !sgemm::skinny_fits(lda, ldb))
-                return SGEMM_F32_ERR_NOT_APPLICABLE;
-            if (sgemm::skinny_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
+            if (sgemm::skinny_form(ta, tb, M, N, K, lda, ldb) < 0) return SGEMM_F32_ERR_NOT_APPLICABLE;
+            if (sgemm::skinny_grid(g) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
             return to_status(sgemm::launch_skinny(g, aligned16(A, lda, B, ldb), stream));
         default:
             return SGEMM_F32_ERR_VARIANT;

@@ -285,6 +285,163 @@ __global__ __launch_bounds__(SK_NT, MB == 2 ? 3 : 1) void sgemm_skinny_kernel(Sk
     }
 }
 
+// ---------------------------------------------------------------------------
+// Streamed operand with rows contiguous in k.  D(i, r) = sum_k X(i, k) W(r, k)
+// for at most 16 rows i of a small operand X and many rows r of W:
+//   - B given N x K (NT, TT) with M <= 16: X = op(A), W = B as stored, D = C;
+//   - A as given with N <= 16 (NN, NT): X = op(B) transposed, W = A, D = C
+//     transposed.
+// A work-group owns 32 rows of W (two groups of 16) and one range of K, split
+// again over its 4 waves in batches of 64 k.  In a batch, lane l (h = l/16,
+// j = l%16) loads W(r0 + 16 g + j, kb + 16 q + 4 h .. +3) for g = 0, 1 and
+// q = 0..3 (each load: 16 rows x 64 bytes, a row's 256 bytes over the four
+// q) and X(j, the same k) likewise.  Component e of the q-th groups is the
+// k = kb + 16 q + 4 h + e operand of one 16x16x4 MFMA per g: lane
+// (j, h) supplies row j of X and column j of W at the h-th k, so the product
+// needs no reshuffling.  X given transposed (k-major) is read element by
+// element.  Partial sums go to scratch in C's order when K is split over
+// work-groups, and the same ordered reduction finishes C.
+constexpr int KM_RW = 32;                // rows of W per work-group
+constexpr int KM_G = KM_RW / 16;         // groups of 16 rows of W
+constexpr int KM_BK = 64;                // k per batch
+constexpr int KM_RED = KM_RW + 1;        // padded row of the LDS reduction
+constexpr int kKMajorMaxRows = 16;       // rows of X
+
+struct KmajArgs {
+    const float *W;
+    int64_t ldw;
+    int R;                // rows of W
+    const float *X;
+    int64_t x_si, x_sk;   // X(i, k) at X[i * x_si + k * x_sk]
+    int MX;               // rows of X (<= 16)
+    int K;
+    float alpha, beta;
+    float *C;
+    int64_t c_si, c_sr;   // D(i, r) at C[i * c_si + r * c_sr]
+    float *ws;            // splits x MX x R partial sums in C's order
+    int64_t w_si, w_sr;
+    int splits;
+    int split_rows;       // k per split, a multiple of KM_BK
+};
+
+struct KBatch {
+    float4 w[KM_G][4];
+    float4 x[4];
+};
+
+template <bool VEC, bool XT>
+__device__ __forceinline__ void kmaj_load(const KmajArgs &a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
+                                          int rows, int kb, int kend, int h, int j, KBatch &bt) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = kb + 16 * q + 4 * h;       // first k of this lane's groups
+#pragma unroll
+        for (int g = 0; g < KM_G; ++g) {
+            const int r = 16 * g + j;            // row of W within the work-group's rows
+            bt.w[g][q] = load_group<VEC, 0>(rw, (int)((r * a.ldw + k) * 4), k, r < rows ? kend : 0);
+        }
+        if (XT) {                                // X(j, k..k+3) lies down a column
+            float v[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                v[e] = sk_buffer_load_f32(rx, j < a.MX && k + e < kend ? (int)(((k + e) * a.x_sk + j) * 4) : kOff, 0, 0);
+            bt.x[q] = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+            bt.x[q] = load_group<VEC, 0>(rx, (int)((j * a.x_si + k) * 4), k, j < a.MX ? kend : 0);
+        }
+    }
+}
+
+__device__ __forceinline__ float comp(const float4 &v, int e) {
+    return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w;
+}
+
+__device__ __forceinline__ void kmaj_consume(const KBatch &bt, f32x4v (&acc)[KM_G]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float x = comp(bt.x[q], e);
+#pragma unroll
+            for (int g = 0; g < KM_G; ++g)
+                acc[g] = __builtin_amdgcn_mfma_f32_16x16x4f32(x, comp(bt.w[g][q], e), acc[g], 0, 0, 0);
+        }
+}
+
+// TOUT: D is C transposed (consecutive threads then write consecutive i).
+template <bool VEC, bool XT, bool TOUT>
+__global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int strips) {
+    __shared__ float red[SK_NW][16 * KM_RED];
+    poison_lds<sizeof(red)>(red);
+    int split, strip;
+    tile_of_block(blockIdx.x, a.splits, strips, 1, split, strip);
+    const int r0 = strip * KM_RW;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int h = lane >> 4, j = lane & 15;
+
+    const int kbeg = split * a.split_rows;
+    const int kend = min(a.K, kbeg + a.split_rows);
+    const int batches = (kend - kbeg + KM_BK - 1) / KM_BK;
+    const int per_wave = (batches + SK_NW - 1) / SK_NW;
+    const int bbeg = wave * per_wave;
+    const int bend = min(batches, bbeg + per_wave);
+
+    // Resources over this work-group's rows of W and over all of X: rows
+    // past R and k past the range read as zero.
+    const int rows = min(KM_RW, a.R - r0);
+    const __amdgpu_buffer_rsrc_t rw = sk_rsrc(a.W + (int64_t)r0 * a.ldw, (int)(((rows - 1) * a.ldw + a.K) * 4));
+    const __amdgpu_buffer_rsrc_t rx =
+        sk_rsrc(a.X, XT ? (int)(((a.K - 1) * a.x_sk + a.MX) * 4) : (int)(((a.MX - 1) * a.x_si + a.K) * 4));
+
+    f32x4v acc[KM_G];
+#pragma unroll
+    for (int g = 0; g < KM_G; ++g) acc[g] = f32x4v{0.f, 0.f, 0.f, 0.f};
+    KBatch b0, b1;
+    int b = bbeg;
+    // As in the other kernel: unconditional loads in the loop, past the end
+    // re-reading the wave's last batch, which is then not consumed.
+    auto kof = [&](int bi) { return kbeg + (bi < bend ? bi : bend - 1) * KM_BK; };
+    if (b < bend) kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+    for (; b + 1 < bend; b += 2) {
+        kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+        kmaj_consume(b0, acc);
+        kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
+        kmaj_consume(b1, acc);
+    }
+    if (b < bend) kmaj_consume(b0, acc);
+
+    // acc[g] register r of lane (j, h) holds i = 4 h + r, row r0 + 16 g + j
+    // of W.  The waves' partials are added in wave order.
+#pragma unroll
+    for (int g = 0; g < KM_G; ++g)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][(4 * h + r) * KM_RED + 16 * g + j] = acc[g][r];
+    __syncthreads();
+    constexpr int NI = 16;
+    constexpr int PER_T = NI * KM_RW / SK_NT;
+#pragma unroll
+    for (int t = 0; t < PER_T; ++t) {
+        const int idx = threadIdx.x + t * SK_NT;
+        const int i = TOUT ? idx % NI : idx / KM_RW;
+        const int c = TOUT ? idx / NI : idx % KM_RW;
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < SK_NW; ++w) s += red[w][i * KM_RED + c];
+        if (i < a.MX && r0 + c < a.R) {
+            const int64_t r = r0 + c;
+            if (a.splits > 1) {
+                a.ws[(int64_t)split * a.MX * a.R + i * a.w_si + r * a.w_sr] = s;
+            } else {
+                float *p = a.C + i * a.c_si + r * a.c_sr;
+                float v = a.alpha * s;
+                if (a.beta != 0.f) v = fmaf(a.beta, *p, v);
+                *p = v;
+            }
+        }
+    }
+}
+
 // C = alpha * (sum of the split partials, in split order) + beta * C.  The
 // partials' loads go out eight at a time before their additions (with a
 // run-time loop bound each addition would wait for its own load, one memory
@@ -313,85 +470,162 @@ __global__ __launch_bounds__(256) void skinny_reduce_kernel(GemmArgs g, const fl
 
 }  // namespace
 
-int64_t skinny_grid(int M, int N) {
-    (void)M;
-    return (N + SK_BN - 1) / SK_BN;
-}
+namespace {
 
-bool skinny_fits(int lda, int ldb) {
+constexpr int64_t kOffsetLimit = (int64_t)1 << 31;
+
+bool rows_fit(int64_t lda, int64_t ldb) {
     // One batch of B and all kSkinnyMaxM rows of A must be addressable with
     // 32-bit byte offsets.
-    const int64_t limit = (int64_t)1 << 31;
-    return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < limit && ((int64_t)kSkinnyMaxM * lda + SK_ROWS) * 4 < limit;
+    return ((int64_t)SK_ROWS * ldb + SK_BN) * 4 < kOffsetLimit && ((int64_t)kSkinnyMaxM * lda + SK_ROWS) * 4 < kOffsetLimit;
+}
+
+// A work-group's rows of W, and all of X (MX rows, given k-major when xt),
+// must be addressable with 32-bit byte offsets.
+bool kmaj_fits(int64_t ldw, int64_t ldx, bool xt, int MX, int K) {
+    const bool w_ok = ((int64_t)(KM_RW - 1) * ldw + K) * 4 < kOffsetLimit;
+    const bool x_ok = xt ? ((int64_t)(K - 1) * ldx + MX) * 4 < kOffsetLimit
+                         : ((int64_t)(MX - 1) * ldx + K) * 4 < kOffsetLimit;
+    return w_ok && x_ok;
+}
+
+}  // namespace
+
+int skinny_form(int ta, int tb, int M, int N, int K, int64_t lda, int64_t ldb) {
+    if (!ta && !tb && M <= kSkinnyMaxM && rows_fit(lda, ldb)) return kSkinnyRowsOfB;
+    if (tb && M <= kKMajorMaxRows && kmaj_fits(ldb, lda, ta != 0, M, K)) return kSkinnyBKMajor;
+    if (!ta && N <= kKMajorMaxRows && kmaj_fits(lda, ldb, tb == 0, N, K)) return kSkinnyAKMajor;
+    return -1;
+}
+
+int64_t skinny_grid(const GemmArgs &g) {
+    const int form = skinny_form(g.trans_a, g.trans_b, g.M, g.N, g.K, g.lda, g.ldb);
+    if (form == kSkinnyRowsOfB) return (g.N + SK_BN - 1) / SK_BN;
+    return ((form == kSkinnyBKMajor ? g.N : g.M) + (int64_t)KM_RW - 1) / KM_RW;
 }
 
 namespace {
 
-// Work-groups wanted per call, for one and for two blocks of 16 rows of A.
-constexpr int kSkinnySlots1 = 512;
-constexpr int kSkinnySlots2 = 512;
+// Work-groups wanted per call: two per compute unit.
+constexpr int kSkinnySlots = 512;
 
-// The K split: about two work-groups per compute unit, every split at least
-// 256 rows long.
-void skinny_split(const GemmArgs &g, int *splits_out, int *split_rows_out) {
-    const int strips = (g.N + SK_BN - 1) / SK_BN;
-    const int slots = g.M > 16 ? kSkinnySlots2 : kSkinnySlots1;
-    const int want = (slots + strips - 1) / strips;
-    const int max_splits = (g.K + 255) / 256;
+// The K split over `strips` work-group columns: about kSkinnySlots work-groups,
+// every split at least 256 k long and a whole number of batches of `unit` k.
+void skinny_split(int strips, int K, int unit, int *splits_out, int *split_rows_out) {
+    const int want = (kSkinnySlots + strips - 1) / strips;
+    const int max_splits = (K + 255) / 256;
     int splits = want < max_splits ? want : max_splits;
     if (splits < 1) splits = 1;
-    int split_rows = (g.K + splits - 1) / splits;
-    split_rows = (split_rows + SK_ROWS - 1) / SK_ROWS * SK_ROWS;
-    splits = (g.K + split_rows - 1) / split_rows;
+    int split_rows = (K + splits - 1) / splits;
+    split_rows = (split_rows + unit - 1) / unit * unit;
+    splits = (K + split_rows - 1) / split_rows;
     *splits_out = splits;
-    *split_rows_out = splits > 1 ? split_rows : g.K;
+    *split_rows_out = splits > 1 ? split_rows : K;
+}
+
+void form_split(const GemmArgs &g, int form, int *splits, int *split_rows) {
+    skinny_split((int)skinny_grid(g), g.K, form == kSkinnyRowsOfB ? SK_ROWS : KM_BK, splits, split_rows);
+}
+
+using RowsKern = void (*)(SkinnyArgs, int);
+using KmajKern = void (*)(KmajArgs, int);
+
+bool aligned16(const float *p, int64_t ld) { return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0; }
+
+// The streamed operand W and the small operand X of the K-major forms.
+KmajArgs kmaj_args(const GemmArgs &g, int form, float *ws, int splits, int split_rows, bool *xt) {
+    const bool bw = form == kSkinnyBKMajor;   // W = B (N x K); else W = A (M x K), D = C transposed
+    KmajArgs a;
+    a.W = bw ? g.B : g.A;
+    a.ldw = bw ? g.ldb : g.lda;
+    a.R = bw ? g.N : g.M;
+    a.X = bw ? g.A : g.B;
+    a.MX = bw ? g.M : g.N;
+    a.K = g.K;
+    // X given k-major: A stored K x M (TT), or B as given, K x N (NN).
+    *xt = bw ? g.trans_a != 0 : g.trans_b == 0;
+    const int64_t ldx = bw ? g.lda : g.ldb;
+    a.x_si = *xt ? 1 : ldx;
+    a.x_sk = *xt ? ldx : 1;
+    a.alpha = g.alpha;
+    a.beta = g.beta;
+    a.C = g.C;
+    a.c_si = bw ? g.ldc : 1;
+    a.c_sr = bw ? 1 : g.ldc;
+    a.ws = ws;
+    a.w_si = bw ? g.N : 1;                      // partials in C's order, rows of N
+    a.w_sr = bw ? 1 : g.N;
+    a.splits = splits;
+    a.split_rows = split_rows;
+    return a;
 }
 
 }  // namespace
 
 int64_t skinny_scratch_bytes(const GemmArgs &g) {
+    const int form = skinny_form(g.trans_a, g.trans_b, g.M, g.N, g.K, g.lda, g.ldb);
+    if (form < 0) return 0;
     int splits = 1, split_rows = 0;
-    skinny_split(g, &splits, &split_rows);
+    form_split(g, form, &splits, &split_rows);
     return splits > 1 ? (int64_t)splits * g.M * g.N * (int64_t)sizeof(float) : 0;
 }
 
 hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) {
-    const int strips = (g.N + SK_BN - 1) / SK_BN;
-    SkinnyArgs sa;
-    sa.g = g;
-    sa.ws = nullptr;
-    skinny_split(g, &sa.splits, &sa.split_rows);
-    const int splits = sa.splits;
+    const int form = skinny_form(g.trans_a, g.trans_b, g.M, g.N, g.K, g.lda, g.ldb);
+    if (form < 0) return hipErrorInvalidValue;
+    const int strips = (int)skinny_grid(g);
+    int splits = 1, split_rows = 0;
+    form_split(g, form, &splits, &split_rows);
+    float *ws = nullptr;
     if (splits > 1) {
         hipError_t e = scratch_acquire(g.scratch, (size_t)skinny_scratch_bytes(g), stream,
-                                       reinterpret_cast<void **>(&sa.ws));
+                                       reinterpret_cast<void **>(&ws));
         if (e != hipSuccess) return e;
     }
     const dim3 grid(strips * splits);
-    // One block of 16 rows of A for M <= 16, two for 16 < M <= 32; three
-    // batches in flight on grids of at most kDeepStrips strips.
-    const int mb = g.M > 16 ? 2 : 1;
-    const int depth = strips <= kDeepStrips ? 3 : 2;
-    using Kern = void (*)(SkinnyArgs, int);
-    Kern k;
-    if (vec_loads)
-        k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<true, 2, 3> : sgemm_skinny_kernel<true, 2, 2>)
-                    : (depth == 3 ? sgemm_skinny_kernel<true, 1, 3> : sgemm_skinny_kernel<true, 1, 2>);
-    else
-        k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<false, 2, 3> : sgemm_skinny_kernel<false, 2, 2>)
-                    : (depth == 3 ? sgemm_skinny_kernel<false, 1, 3> : sgemm_skinny_kernel<false, 1, 2>);
-    hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, sa, strips);
+    if (form == kSkinnyRowsOfB) {
+        SkinnyArgs sa;
+        sa.g = g;
+        sa.ws = ws;
+        sa.splits = splits;
+        sa.split_rows = split_rows;
+        // One block of 16 rows of A for M <= 16, two for 16 < M <= 32; three
+        // batches in flight on grids of at most kDeepStrips strips.
+        const int mb = g.M > 16 ? 2 : 1;
+        const int depth = strips <= kDeepStrips ? 3 : 2;
+        RowsKern k;
+        if (vec_loads)
+            k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<true, 2, 3> : sgemm_skinny_kernel<true, 2, 2>)
+                        : (depth == 3 ? sgemm_skinny_kernel<true, 1, 3> : sgemm_skinny_kernel<true, 1, 2>);
+        else
+            k = mb == 2 ? (depth == 3 ? sgemm_skinny_kernel<false, 2, 3> : sgemm_skinny_kernel<false, 2, 2>)
+                        : (depth == 3 ? sgemm_skinny_kernel<false, 1, 3> : sgemm_skinny_kernel<false, 1, 2>);
+        hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, sa, strips);
+    } else {
+        bool xt = false;
+        const KmajArgs a = kmaj_args(g, form, ws, splits, split_rows, &xt);
+        const bool tout = form == kSkinnyAKMajor;
+        // 16-byte loads of W, and of X where X is read along k.
+        const bool vec = aligned16(a.W, a.ldw) && (xt || aligned16(a.X, a.x_si));
+        KmajKern k;
+        if (vec)
+            k = xt ? (tout ? sgemm_kmaj_kernel<true, true, true> : sgemm_kmaj_kernel<true, true, false>)
+                   : (tout ? sgemm_kmaj_kernel<true, false, true> : sgemm_kmaj_kernel<true, false, false>);
+        else
+            k = xt ? (tout ? sgemm_kmaj_kernel<false, true, true> : sgemm_kmaj_kernel<false, true, false>)
+                   : (tout ? sgemm_kmaj_kernel<false, false, true> : sgemm_kmaj_kernel<false, false, false>);
+        hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, a, strips);
+    }
     hipError_t e = hipGetLastError();
     if (splits > 1) {
         if (e == hipSuccess) {
             const int64_t total = (int64_t)g.M * g.N;
             int64_t blocks = (total + 255) / 256;
             if (blocks > 4096) blocks = 4096;
-            hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, sa.ws,
-                               splits);
+            hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, g, ws, splits);
             e = hipGetLastError();
         }
-        const hipError_t r = scratch_release(g.scratch, sa.ws, stream);
+        const hipError_t r = scratch_release(g.scratch, ws, stream);
         if (e == hipSuccess) e = r;
     }
     return e;

@@ -35,7 +35,7 @@
  *     threads at once.
  *   - Device memory (see sgemm_f32_noalloc for the form that allocates
  *     nothing): none unless the reduction over K is split across
- *     work-groups (the M <= 32 kernel, MFMA plans with splits > 1 from the
+ *     work-groups (the streaming kernels, MFMA plans with splits > 1 from the
  *     tuning table or sgemm_f32_ex_config, and the stream-K configuration).
  *     Such a call needs scratch (at most splits * M * N floats, 1 GiB cap for
  *     MFMA plans), taken from a memory pool the library creates on the first
@@ -102,7 +102,8 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_MFMA_LARGE = 1,     /* FP32 MFMA, 128x128 block tile */
     SGEMM_F32_MFMA_SMALL = 2,     /* FP32 MFMA, 64x64 block tile (small shapes) */
     SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
-    SGEMM_F32_SKINNY = 4,         /* M <= 32: FP32 MFMA streaming kernel */
+    SGEMM_F32_SKINNY = 4,         /* FP32 MFMA streaming kernels: M <= 32 (plain form), or
+                                     M <= 16 with B transposed, or N <= 16 with A as given */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
     SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
                                      64x64 tiles with two slices in flight, 256x256 tiles, or
@@ -148,7 +149,7 @@ int sgemm_f32(int M, int N, int K, float alpha,
  * capture that must not record allocations, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments, validation, special cases, kernel
  * plan and results (bit for bit) as sgemm_f32.  It calls no hipMalloc,
- * hipMallocAsync or hipFree: the plans that need scratch (the M <= 32 split,
+ * hipMallocAsync or hipFree: the plans that need scratch (the streaming kernels' split,
  * tuned split-K plans) use a fixed region of
  * SGEMM_F32_NOALLOC_SCRATCH_BYTES (64 MiB) in the library's device memory,
  * one per device, present from the library's loading on that device until
@@ -171,7 +172,7 @@ int sgemm_f32_noalloc(int M, int N, int K, float alpha,
  * The same operation computed by one forced kernel variant, for comparisons
  * between variants and for tests.  Arguments after `variant` are those of
  * sgemm_f32.  Returns SGEMM_F32_ERR_NOT_APPLICABLE when the variant cannot
- * handle the request (SGEMM_F32_SKINNY with M > 32; a vector-load variant with
+ * handle the request (SGEMM_F32_SKINNY on a shape none of its forms covers; a vector-load variant with
  * a pointer not 16-byte aligned, lda or ldb not a multiple of 4, or row strides
  * so large that 128 rows of A or 32 rows of B span 2 GiB or more).
  */
@@ -210,8 +211,13 @@ int sgemm_f32_select(int M, int N, int K, float alpha,
  * with the column-major leading dimensions.
  *
  * Transposed operands run on the MFMA variants (SGEMM_F32_MFMA_LARGE, _SMALL,
- * _SCALAR); SGEMM_F32_VALU and SGEMM_F32_SKINNY take neither operand
- * transposed and return SGEMM_F32_ERR_NOT_APPLICABLE otherwise.  For the
+ * _SCALAR); SGEMM_F32_VALU takes neither operand transposed and returns
+ * SGEMM_F32_ERR_NOT_APPLICABLE otherwise.  SGEMM_F32_SKINNY (and the automatic
+ * choice) streams the large operand when its rows run along K: B transposed
+ * with M <= 16 (NT, TT), or A as given with N <= 16 (NN, NT; C is then
+ * written through its transpose); A transposed with B as given has no
+ * streaming form.  Its offsets are 32-bit: 32 rows of the streamed operand,
+ * and all of the small one, must span less than 2 GiB.  For the
  * 16-byte-load variants the stored rows one slice touches must span less than
  * 2 GiB: 128 rows of an operand stored along K (A as given, B transposed) and
  * 32 rows of one stored along M or N (B as given, A transposed).

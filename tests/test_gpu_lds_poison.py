@@ -6,8 +6,8 @@ s_barrier), or a part of LDS that is read but never written, would turn entries
 of C into NaN.  On integer-valued inputs the result is exact, so every case is
 compared bit for bit with the oracle: short K (slices loaded past the end),
 edge tiles, long K (thousands of slices through the stages), all four operand
-forms, every tile configuration, the VALU and M <= 16 kernels, and both 16-bit
-kernels.  Calls go through the debug library's C interface."""
+forms, every tile configuration, the VALU kernel, the streaming kernels for
+M <= 32 (plain form) and M or N <= 16 (rows along k), and both 16-bit kernels.  Calls go through the debug library's C interface."""
 from __future__ import annotations
 
 import ctypes
@@ -123,6 +123,25 @@ def test_poisoned_valu_and_skinny(plib, variant, M, N):
     dA, dB, dC = (torch.from_numpy(x).cuda() for x in (A, B, C0))
     st = plib.sgemm_f32_variant(variant, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), K, dB.data_ptr(), N,
                                 ctypes.c_float(1.0), dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    ok, info = _exact(dC.cpu().numpy(), A, B, 1.0, 1.0, C0)
+    assert ok, info
+
+
+@pytest.mark.parametrize("case", [(0, 1, 16, 1000, 3000), (1, 1, 13, 1000, 3000), (0, 0, 1000, 16, 3000),
+                                  (0, 1, 4, 16384, 2000)], ids=["nt", "tt", "nn_tall", "nt_long_k"])
+def test_poisoned_skinny_kmajor(plib, case):
+    """The streaming kernel for operands whose rows run along k (B given
+    N x K with M <= 16, A as given with N <= 16)."""
+    ta, tb, M, N, K = case
+    say(f"[poison_kmaj] {case}")
+    A, B, C0 = _int_inputs(M, N, K, 1850 + M + N)
+    As, Bs = _stored(A, ta), _stored(B, tb)
+    dA, dB, dC = (torch.from_numpy(x).cuda() for x in (As, Bs, C0))
+    st = plib.sgemm_f32_ex_variant(4, ta, tb, M, N, K, ctypes.c_float(1.0), dA.data_ptr(), As.shape[1],
+                                   dB.data_ptr(), Bs.shape[1], ctypes.c_float(1.0), dC.data_ptr(), N,
+                                   torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0
     ok, info = _exact(dC.cpu().numpy(), A, B, 1.0, 1.0, C0)

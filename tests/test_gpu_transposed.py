@@ -133,13 +133,79 @@ def test_beta_zero_ignores_nan_c(sg, form):
     assert ok, info
 
 
+def test_skinny_kmajor_refuses_more_than_16_rows(sg):
+    for ta, tb, M, N in ((0, 1, 17, 64), (1, 1, 17, 64), (0, 0, 64, 17), (0, 1, 64, 17)):
+        A, B, C0 = _inputs(M, N, 64, "uniform", 25)
+        st, _, _, _ = run_ex(sg, VID["skinny"], ta, tb, A, B, C0, 1.0, 0.0)
+        assert st == sg.ERR_NOT_APPLICABLE, (ta, tb, M, N)
+
+
 @pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])
 def test_unsupported_variants_refuse(sg, form):
     ta, tb = form
     A, B, C0 = _inputs(16, 64, 64, "uniform", 21)
-    for v in ("valu", "skinny"):
-        st, _, _, _ = run_ex(sg, VID[v], ta, tb, A, B, C0, 1.0, 0.0)
-        assert st == sg.ERR_NOT_APPLICABLE, v
+    st, _, _, _ = run_ex(sg, VID["valu"], ta, tb, A, B, C0, 1.0, 0.0)
+    assert st == sg.ERR_NOT_APPLICABLE
+    if form == (1, 0):   # A transposed with B as given: no streaming form
+        st, _, _, _ = run_ex(sg, VID["skinny"], ta, tb, A, B, C0, 1.0, 0.0)
+        assert st == sg.ERR_NOT_APPLICABLE
+
+
+# The streaming kernel on operands whose rows run along k: B given N x K with
+# M <= 16 (NT, TT), and A as given with N <= 16 (NN, NT; C written
+# transposed).  (ta, tb, M, N, K): ragged row counts of the streamed side
+# (edge work-groups of 32 rows), K tails inside a 64-deep batch, splits of K
+# over work-groups with 0 to 8 batches per wave.
+SKINNY_KMAJ = [(0, 1, 16, 4096, 300), (0, 1, 1, 1, 1), (0, 1, 3, 33, 100), (0, 1, 16, 2050, 1000),
+               (0, 1, 13, 4093, 777), (0, 1, 16, 100, 4099), (0, 1, 15, 16, 17), (0, 1, 16, 200, 8191),
+               (1, 1, 16, 4096, 300), (1, 1, 5, 130, 777), (1, 1, 16, 257, 513), (1, 1, 1, 4097, 65),
+               (0, 0, 4096, 16, 300), (0, 0, 1000, 1, 77), (0, 0, 2050, 16, 1000), (0, 0, 33, 11, 4099),
+               (0, 0, 4093, 14, 777), (0, 0, 100, 3, 8191), (0, 1, 4096, 16, 300), (0, 1, 130, 9, 2000),
+               (0, 1, 2051, 16, 64), (0, 1, 4, 16384, 2000), (0, 0, 16384, 8, 1280), (1, 1, 12, 16000, 700),
+               (0, 0, 4096, 1, 300)]
+KMAJ_IDS = [f"{FORM_IDS[2 * ta + tb]}-{m}x{n}x{k}" for ta, tb, m, n, k in SKINNY_KMAJ]
+
+
+@pytest.mark.parametrize("variant", ["skinny", "auto"])
+@pytest.mark.parametrize("case", SKINNY_KMAJ, ids=KMAJ_IDS)
+def test_skinny_kmajor_forms(sg, variant, case):
+    ta, tb, M, N, K = case
+    say(f"[t_skinny_kmaj] {variant} {case}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 700 + M + N + K)
+    st, C, As, Bs = run_ex(sg, VID[variant], ta, tb, A, B, C0, -0.75, 2.0)
+    assert st == 0
+    ok, info = check_op_full(C, As, Bs, ta, tb, -0.75, 2.0, C0)
+    assert ok, info
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 800 + M + N + K, c0=False)
+    st, C, As, Bs = run_ex(sg, VID[variant], ta, tb, Ai, Bi, None, 1.0, 0.0)
+    assert st == 0
+    ok, info = check_op_full(C, As, Bs, ta, tb, 1.0, 0.0, None, exact=True)
+    assert ok, info
+    if variant == "auto":
+        lda, ldb = As.shape[1], Bs.shape[1]
+        assert sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, 256, (lda + 3) // 4 * 4, 256,
+                                    (ldb + 3) // 4 * 4)[1] == sg.SKINNY
+
+
+@pytest.mark.parametrize("case", [(0, 1, 16, 97, 61), (1, 1, 14, 130, 200), (0, 0, 141, 16, 61),
+                                  (0, 1, 141, 7, 130)], ids=["nt", "tt", "nn-tall", "nt-tall"])
+def test_skinny_kmajor_odd_strides_and_beta_zero(sg, case):
+    """Misaligned operands and odd strides (element-by-element loads), then
+    beta = 0 over a C of NaNs, which must not be read."""
+    ta, tb, M, N, K = case
+    say(f"[t_skinny_kmaj_odd] {case}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 24)
+    wa = M if ta else K
+    wb = K if tb else N
+    st, C, As, Bs = run_ex(sg, VID["skinny"], ta, tb, A, B, C0, 0.5, 0.25, lda=wa + 1, ldb=wb + 3,
+                           ldc=N + 2, offs=(1, 3, 1))
+    assert st == 0
+    ok, info = check_op_full(C, As, Bs, ta, tb, 0.5, 0.25, C0)
+    assert ok, info
+    st, C, As, Bs = run_ex(sg, VID["skinny"], ta, tb, A, B, None, 1.0, 0.0, c_fill=np.nan)
+    assert st == 0 and np.all(np.isfinite(C))
+    ok, info = check_op_full(C, As, Bs, ta, tb, 1.0, 0.0, None)
+    assert ok, info
 
 
 def test_tensor_helper_takes_transpose_views(sg):

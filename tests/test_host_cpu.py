@@ -166,12 +166,25 @@ def test_transposed_argument_errors_without_touching_the_gpu(sg):
     # The widths the untransposed forms would need are not required.
     assert f(1, 1, 2, 5, 9, 1.0, p, 2, p, 9, 0.0, 0, 5, 0) == 10     # only C is missing
     assert sg.sgemm_f32_ex_variant(sg.NUM_VARIANTS, 1, 0, 2, 2, 2, 1.0, p, 2, p, 2, 0.0, p, 2, 0) == sg.ERR_VARIANT
-    # The VALU and M <= 16 kernels take neither operand transposed.
+    # The VALU kernel takes neither operand transposed; the streaming kernels
+    # take every form but A transposed with B as given, and A transposed
+    # when only N is small.
     al = 0x100000
     for ta, tb in ((1, 0), (0, 1), (1, 1)):
-        for v in (sg.VALU, sg.SKINNY):
-            assert sg.sgemm_f32_ex_variant(v, ta, tb, 16, 64, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
-                == sg.ERR_NOT_APPLICABLE, (v, ta, tb)
+        assert sg.sgemm_f32_ex_variant(sg.VALU, ta, tb, 16, 64, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+            == sg.ERR_NOT_APPLICABLE, (ta, tb)
+    assert sg.sgemm_f32_ex_variant(sg.SKINNY, 1, 0, 16, 64, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+        == sg.ERR_NOT_APPLICABLE
+    for tb in (0, 1):
+        assert sg.sgemm_f32_ex_variant(sg.SKINNY, 1, tb, 64, 16, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+            == sg.ERR_NOT_APPLICABLE, tb
+        assert sg.sgemm_f32_ex_variant(sg.SKINNY, 0, tb, 64, 17, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+            == sg.ERR_NOT_APPLICABLE, tb
+    for ta in (0, 1):
+        assert sg.sgemm_f32_ex_variant(sg.SKINNY, ta, 1, 17, 64, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+            == sg.ERR_NOT_APPLICABLE, ta
+    assert sg.sgemm_f32_ex_variant(sg.SKINNY, 0, 0, 33, 33, 64, 1.0, al, 64, al, 64, 0.0, al, 64, 0) \
+        == sg.ERR_NOT_APPLICABLE
 
 
 def test_transposed_kernel_selection(sg):
@@ -189,9 +202,28 @@ def test_transposed_kernel_selection(sg):
         assert sg.sgemm_f32_ex_plan(ta, tb, 7000, 7000, 1000, 1.0, al, 7000 if ta else 1000, al,
                                     1000 if tb else 7000)[2] == sg.CFG_128x128_DL
         assert sel(ta, tb, 1024, 1024, 1024, 1.0, al, 1024, al, 1024) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
-        assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) in (sg.MFMA_SMALL, sg.MFMA_TUNED)
+        # M <= 16 with B given N x K streams B along k; A transposed with B as
+        # given stays on tiles.
+        assert sel(ta, tb, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == \
+            (sg.SKINNY if tb else sg.MFMA_TUNED)
+        assert sel(ta, tb, 1, 4096, 4096, 1.0, al, 4096, al, 4096) == \
+            (sg.SKINNY if tb else sg.MFMA_TUNED)
+        assert sel(ta, tb, 17, 4096, 4096, 1.0, al, 4096, al, 4096) != sg.SKINNY
+        # N <= 16 with A as given streams A along k (C written transposed).
+        assert sel(ta, tb, 4096, 16, 4096, 1.0, al, 4096, al, 4096) == \
+            (sg.MFMA_TUNED if ta else sg.SKINNY)
+        assert sel(ta, tb, 4096, 17, 4096, 1.0, al, 4096, al, 4096) != sg.SKINNY
         assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
     assert sel(0, 0, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
+    assert sel(0, 0, 4096, 16, 4096, 1.0, al, 4096, al, 16) == sg.SKINNY
+    assert sel(0, 0, 4096, 1, 4096, 1.0, al, 4096, al, 1) == sg.SKINNY
+    # The streamed operand's 32 rows, and all of the small one, must lie within
+    # 32-bit byte offsets: B's stride too wide for 32 rows keeps the tiles.
+    wide = (1 << 31) // 4 // 31 + 4
+    assert sel(0, 1, 16, 4096, 4096, 1.0, al, 4096, al, wide - wide % 4) != sg.SKINNY
+    assert sel(0, 1, 16, 4096, 4096, 1.0, al, 4096, al, (1 << 31) // 4 // 32 - 1024) == sg.SKINNY
+    # A given K x M (k-major) spans K rows of its stride.
+    assert sel(1, 1, 16, 4096, 65536, 1.0, al, 16384, al, 65536) != sg.SKINNY
     assert sel(0, 0, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == \
         sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al, 4096, al, 4096)
     assert sel(2, 0, 4096, 4096, 4096, 1.0, al, 4096, al, 4096) == 0
@@ -351,7 +383,7 @@ def test_plan_follows_the_tuning_table(sg):
     for e in table["entries"]:
         M, N, K = e["shape"]
         st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, al, K, al, N)
-        if M <= 32:
+        if M <= 32 or N <= 16:
             assert v == sg.SKINNY
             continue
         assert st == 0 and v in (sg.MFMA_LARGE, sg.MFMA_SMALL, sg.MFMA_TUNED), e
