@@ -109,10 +109,27 @@ struct Plan {
     int splits;
 };
 
+// Operands that 16-byte loads cannot read take the 4-byte-load tiles; on a
+// grid of fewer than 256 of them K is split until about kScalarSplitSlots
+// work-groups run, every split at least 256 deep (4096 x 17 x 4096 with ldb =
+// 17: 64 tiles of 64 x 64, 157 us in one pass).
+constexpr int kScalarSplitSlots = 512;
+
+int scalar_splits(int M, int N, int K, int config) {
+    const int64_t tiles = config == 1 ? sgemm::mfma_small_grid(M, N) : sgemm::mfma_large_grid(M, N);
+    if (tiles >= 256) return 1;
+    int64_t splits = (kScalarSplitSlots + tiles - 1) / tiles;
+    if (splits > K / 256) splits = K / 256;
+    if (splits > 32) splits = 32;
+    while (splits > 1 && splits * M * N * 4 > kMaxSplitBytes) --splits;
+    return splits < 1 ? 1 : (int)splits;
+}
+
 Plan default_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     if (sgemm::skinny_form(ta, tb, M, N, K, lda, ldb) >= 0) return Plan{SGEMM_F32_SKINNY, 0, 0, 0};
     const int config = prefer_small_tiles(M, N) ? 1 : 0;
-    if (!vec_aligned(ta, tb, A, lda, B, ldb)) return Plan{SGEMM_F32_MFMA_SCALAR, config, 8, 1};
+    if (!vec_aligned(ta, tb, A, lda, B, ldb))
+        return Plan{SGEMM_F32_MFMA_SCALAR, config, 8, scalar_splits(M, N, K, config)};
     // With 16-byte loads the small tile keeps two slices in flight
     // (configuration 4): one work-group per compute unit or fewer leaves the
     // memory latency to the pipeline alone.
@@ -389,8 +406,9 @@ GemmArgs make_args(int ta, int tb, int M, int N, int K, float alpha, const float
 int64_t plan_scratch_bytes(const Plan &p, const GemmArgs &g) {
     if (p.variant == SGEMM_F32_SKINNY) return sgemm::skinny_scratch_bytes(g);
     if (p.variant == SGEMM_F32_VALU) return 0;
-    const int config = p.variant == SGEMM_F32_MFMA_TUNED ? p.config : (p.variant == SGEMM_F32_MFMA_SMALL ? 1 : 0);
-    const int splits = p.variant == SGEMM_F32_MFMA_TUNED ? p.splits : 1;
+    int config = p.variant == SGEMM_F32_MFMA_TUNED ? p.config : (p.variant == SGEMM_F32_MFMA_SMALL ? 1 : 0);
+    if (p.variant == SGEMM_F32_MFMA_SCALAR) config = prefer_small_tiles(g.M, g.N) ? 1 : 0;
+    const int splits = p.variant == SGEMM_F32_MFMA_TUNED || p.variant == SGEMM_F32_MFMA_SCALAR ? p.splits : 1;
     int64_t bytes = 0;
     if (sgemm::mfma_config_scratch_bytes(g, config, splits, &bytes) != hipSuccess) return -1;
     return bytes;
@@ -441,7 +459,7 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         case SGEMM_F32_MFMA_TUNED:
             return run_mfma(g, p.config, vec, p.group_m, p.splits, stream);
         case SGEMM_F32_MFMA_SCALAR:
-            return run_mfma(g, prefer_small_tiles(M, N) ? 1 : 0, false, 8, 1, stream);
+            return run_mfma(g, prefer_small_tiles(M, N) ? 1 : 0, false, 8, p.splits, stream);
         case SGEMM_F32_VALU:
             if (!plain) return SGEMM_F32_ERR_NOT_APPLICABLE;
             if (sgemm::valu_grid(M, N) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;

@@ -104,7 +104,8 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_VALU = 3,           /* FP32 FMA on the vector ALUs, 128x128 tile, 8x8 per thread */
     SGEMM_F32_SKINNY = 4,         /* FP32 MFMA streaming kernels: M <= 32 (plain form), or
                                      M <= 16 with B transposed, or N <= 16 with A as given */
-    SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride */
+    SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride (the
+                                     automatic choice splits K on grids of fewer than 256 tiles) */
     SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
                                      64x64 tiles with two slices in flight, 256x256 tiles, or
                                      128x128 or 64x64 tiles loaded straight into LDS (16-byte

@@ -90,6 +90,30 @@ def test_skinny_shapes(sg, variant, shape):
     assert ok, info
 
 
+# Row strides that 16-byte loads cannot take, on grids of few tiles: the
+# automatic plan splits K over the 4-byte-load tiles.
+UNALIGNED_FEW = [(4096, 17, 4096, None, None), (1000, 33, 3001, None, None), (300, 100, 2001, 2003, None),
+                 (130, 250, 5000, None, 251), (64, 64, 256, 257, None)]
+
+
+@pytest.mark.parametrize("case", UNALIGNED_FEW, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in UNALIGNED_FEW])
+def test_unaligned_few_tiles_split(sg, case):
+    M, N, K, lda, ldb = case
+    say(f"[unaligned_split] {case}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 40 + M)
+    st, C, _ = run_lib(sg, VID["auto"], A, B, C0, 1.25, -0.5, lda=lda, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.25, -0.5, C0)
+    assert ok, info
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 50 + M, c0=False)
+    st, C, _ = run_lib(sg, VID["auto"], Ai, Bi, None, -1.0, 0.0, lda=lda, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, Ai, Bi, -1.0, 0.0, None, exact=True)
+    assert ok, info
+    plan = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, 256, lda or K, 256, ldb or N)
+    assert plan[1] == sg.MFMA_SCALAR and (plan[4] > 1) == (K >= 512), plan
+
+
 @pytest.mark.parametrize("variant", GENERAL + ["skinny"])
 def test_beta_zero_ignores_nan_c(sg, variant):
     for M in ((16, 27) if variant == "skinny" else (150,)):   # one and two blocks of 16 rows

@@ -369,6 +369,11 @@ def test_plan_follows_the_tuning_table(sg):
     assert (st, v) == (0, sg.SKINNY)
     st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4097, 1.0, al, 4097, al, 4096)
     assert (st, v, sp) == (0, sg.MFMA_SCALAR, 1)
+    # Few tiles with 4-byte loads: K split to about 512 work-groups, each split
+    # at least 256 deep.
+    assert sg.sgemm_f32_ex_plan(0, 0, 4096, 17, 4096, 1.0, al, 4096, al, 17) == (0, sg.MFMA_SCALAR, 1, 8, 8)
+    assert sg.sgemm_f32_ex_plan(0, 0, 1000, 33, 3001, 1.0, al, 3001, al, 36)[4] == 11
+    assert sg.sgemm_f32_ex_plan(0, 0, 64, 64, 511, 1.0, al, 511, al, 64)[4] == 1
     path = os.path.join(os.path.dirname(sg.__file__), "tuning_table.json")
     if not sg.sgemm_f32_tuning_table_present():
         assert not os.path.exists(path)

@@ -53,11 +53,13 @@ def _both(sg, A, B, C0, alpha, beta, stream):
 
 # (first, second) products: the second is smaller.  The automatic plans: the
 # M <= 16 split (scratch), a tuned split-K plan (scratch), the 64x64
-# direct-to-LDS grid (no scratch).
+# direct-to-LDS grid (no scratch), the 4-byte-load tiles with K split (an
+# odd row stride of B or A).
 CASES = {
     "skinny": ((16, 4096, 4096), (8, 1000, 3000)),
     "splitk": ((512, 512, 8192), (256, 256, 4096)),
     "grid": ((1024, 1024, 1024), (256, 384, 512)),
+    "unaligned": ((4096, 17, 4096), (1000, 33, 3001)),
 }
 
 
@@ -69,7 +71,7 @@ def test_noalloc_matches_sgemm_f32(sg, case, dist):
         variant, config, splits = _plan(sg, M, N, K)
         say(f"[noalloc] {case} call {idx + 1}: {M}x{N}x{K} {dist} plan variant={variant} config={config} "
             f"splits={splits}")
-        if case == "splitk":
+        if case in ("splitk", "unaligned"):
             assert splits > 1, "the case needs a plan with a K split"
         A, B, C0 = _inputs(M, N, K, dist, 500 + 10 * idx + len(case))
         alpha, beta = (1.5, -0.5) if idx == 0 else (-1.0, 0.0)
