@@ -34,6 +34,10 @@ struct GemmArgs {
 // of the launch.  Callers have validated the arguments, excluded M == 0,
 // N == 0, and routed alpha == 0 / K == 0 to launch_scale_c.
 hipError_t launch_mfma_large(const GemmArgs &g, bool vec_loads, hipStream_t stream);
+// Copies rows x cols floats (row stride ld) into rows of ld2 floats at dst
+// (16-byte aligned, ld2 a multiple of 4 and at least cols).
+hipError_t launch_pack_rows(const float *src, int64_t ld, int rows, int cols, float *dst, int64_t ld2,
+                            hipStream_t stream);
 hipError_t launch_mfma_small(const GemmArgs &g, bool vec_loads, hipStream_t stream);
 
 // MFMA tile configurations: 0 = 128x128 (the large tile), 1 = 64x64 (the

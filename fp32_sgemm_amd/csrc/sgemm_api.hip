@@ -107,6 +107,7 @@ struct Plan {
     int config;    // MFMA tile configuration (MFMA variants)
     int group_m;
     int splits;
+    int pack = 0;  // operands first copied to aligned scratch rows: 1 = A, 2 = B
 };
 
 // Operands that 16-byte loads cannot read take the 4-byte-load tiles; on a
@@ -352,9 +353,63 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
 // one round of 128x128 tiles to those (reported as SGEMM_F32_MFMA_TUNED when
 // the plan differs from the default).
 // Transposed operands use the same entries.
+Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb);
+
+// Operands that 16-byte loads cannot take, on a product of at least 2^32
+// FLOP that the 4-byte-load tiles would run without a split: the operand (or
+// both) is first copied into scratch rows padded to a multiple of 4 floats,
+// and the product runs the plan aligned operands get, when that plan needs no
+// scratch of its own and the copies fit in SGEMM_F32_NOALLOC_SCRATCH_BYTES
+// (so the allocation-free entry point takes the same plan).  Per call, 4-byte
+// loads -> copies and 64x64 tiles with two slices in flight (odd extents keep
+// the direct-to-LDS tiles out): 2047^3 195.7 -> 167.4 us, 3001 x 2001 x 1001
+// 154.9 -> 121.2, 2048 x 2048 x 2047 154.6 -> 136.4; 1023^3 lost (42.6 ->
+// 47.3), hence the lower bound.
+constexpr int64_t kPackMinFlop = (int64_t)1 << 32;
+constexpr int64_t kPackMaxBytes = SGEMM_F32_NOALLOC_SCRATCH_BYTES;
+
+struct PackShape {
+    int a_rows, a_cols, b_rows, b_cols;
+    int64_t lda2, ldb2, a_bytes, b_bytes;   // a_bytes, b_bytes rounded up to 256
+};
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+PackShape pack_shape(int pack, int ta, int tb, int M, int N, int K, int64_t lda, int64_t ldb) {
+    PackShape s;
+    s.a_rows = ta ? K : M;
+    s.a_cols = ta ? M : K;
+    s.b_rows = tb ? N : K;
+    s.b_cols = tb ? K : N;
+    s.lda2 = (pack & 1) ? round_up(s.a_cols, 4) : lda;
+    s.ldb2 = (pack & 2) ? round_up(s.b_cols, 4) : ldb;
+    s.a_bytes = (pack & 1) ? round_up((int64_t)s.a_rows * s.lda2 * 4, 256) : 0;
+    s.b_bytes = (pack & 2) ? round_up((int64_t)s.b_rows * s.ldb2 * 4, 256) : 0;
+    return s;
+}
+
+Plan pack_plan(const Plan &d, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
+    if (d.splits > 1 || 2 * (int64_t)M * N * K < kPackMinFlop) return d;
+    const bool pa = !(aligned16(A, lda, A, 0) && slice_fits(!ta, lda));
+    const bool pb = !(aligned16(B, ldb, B, 0) && slice_fits(tb, ldb));
+    if (!pa && !pb) return d;
+    const int pack = (pa ? 1 : 0) | (pb ? 2 : 0);
+    const PackShape s = pack_shape(pack, ta, tb, M, N, K, lda, ldb);
+    if (s.lda2 > INT32_MAX || s.ldb2 > INT32_MAX || s.a_bytes + s.b_bytes > kPackMaxBytes) return d;
+    const float *aligned_stand_in = reinterpret_cast<const float *>((uintptr_t)256);
+    Plan p = auto_plan(ta, tb, M, N, K, pa ? aligned_stand_in : A, (int)s.lda2, pb ? aligned_stand_in : B,
+                       (int)s.ldb2);
+    if (p.variant == SGEMM_F32_MFMA_SCALAR || p.variant == SGEMM_F32_SKINNY || p.variant == SGEMM_F32_VALU ||
+        p.splits > 1 || p.config == 5)
+        return d;
+    p.pack = pack;
+    return p;
+}
+
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
     const Plan d = default_plan(ta, tb, M, N, K, A, lda, B, ldb);
-    if (d.variant == SGEMM_F32_SKINNY || d.variant == SGEMM_F32_MFMA_SCALAR) return d;
+    if (d.variant == SGEMM_F32_SKINNY) return d;
+    if (d.variant == SGEMM_F32_MFMA_SCALAR) return pack_plan(d, ta, tb, M, N, K, A, lda, B, ldb);
     Plan p = d;
     if (kHaveTunedTable) {
         const TunedEntry e = kTunedTable[shape_class(M)][shape_class(N)][shape_class(K)];
@@ -404,6 +459,10 @@ GemmArgs make_args(int ta, int tb, int M, int N, int K, float alpha, const float
 // Scratch bytes of a plan (0 for plans without a split), or -1 when the
 // occupancy query of the stream-K plan fails.
 int64_t plan_scratch_bytes(const Plan &p, const GemmArgs &g) {
+    if (p.pack) {   // the copies only: a plan on packed operands needs no other scratch
+        const PackShape s = pack_shape(p.pack, g.trans_a, g.trans_b, g.M, g.N, g.K, g.lda, g.ldb);
+        return s.a_bytes + s.b_bytes;
+    }
     if (p.variant == SGEMM_F32_SKINNY) return sgemm::skinny_scratch_bytes(g);
     if (p.variant == SGEMM_F32_VALU) return 0;
     int config = p.variant == SGEMM_F32_MFMA_TUNED ? p.config : (p.variant == SGEMM_F32_MFMA_SMALL ? 1 : 0);
@@ -413,6 +472,8 @@ int64_t plan_scratch_bytes(const Plan &p, const GemmArgs &g) {
     if (sgemm::mfma_config_scratch_bytes(g, config, splits, &bytes) != hipSuccess) return -1;
     return bytes;
 }
+
+int dispatch(const Plan &p, const GemmArgs &g, bool vec, bool plain, hipStream_t stream);
 
 int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const float *A, int lda,
         const float *B, int ldb, float beta, float *C, int ldc, hipStream_t stream,
@@ -429,7 +490,7 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         return to_status(sgemm::launch_scale_c(g, stream));
     }
 
-    const bool vec = vec_aligned(ta, tb, A, lda, B, ldb);
+    bool vec = vec_aligned(ta, tb, A, lda, B, ldb);
     const bool plain = !ta && !tb;
     Plan p{variant, 0, 8, 1};
     if (variant == SGEMM_F32_AUTO) {
@@ -441,14 +502,51 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
     // The plan does not see C: a row stride of C too wide for the 32-bit
     // offsets of configurations 7-9 keeps the register-staged kernels.
     if ((p.config == 7 || p.config == 8 || p.config == 10) && !sgemm::big_tile_c_fits(ldc))
-        p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1};
-    if (p.config == 9 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, 1};
+        p = Plan{SGEMM_F32_MFMA_LARGE, 0, 8, 1, p.pack};
+    if (p.config == 9 && !sgemm::big_tile_c_fits(ldc)) p = Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, 1, p.pack};
     if (scratch.fixed != nullptr) {
         // A fixed scratch region: refuse, before anything is enqueued, a plan
         // that needs more of it than there is.
         const int64_t need = plan_scratch_bytes(p, g);
         if (need < 0 || need > (int64_t)scratch.fixed_bytes) return SGEMM_F32_ERR_SCRATCH;
     }
+    void *pack_ws = nullptr;
+    if (p.pack) {
+        // Copy the operands that 16-byte loads cannot take into aligned rows
+        // of the call's scratch, in stream order before the product.
+        const PackShape sh = pack_shape(p.pack, ta, tb, M, N, K, lda, ldb);
+        hipError_t e = sgemm::scratch_acquire(g.scratch, (size_t)(sh.a_bytes + sh.b_bytes), stream, &pack_ws);
+        if (e != hipSuccess) return to_status(e);
+        float *base = static_cast<float *>(pack_ws);
+        if (p.pack & 1) {
+            e = sgemm::launch_pack_rows(A, lda, sh.a_rows, sh.a_cols, base, sh.lda2, stream);
+            g.A = base;
+            g.lda = sh.lda2;
+        }
+        if (e == hipSuccess && (p.pack & 2)) {
+            float *bp = base + sh.a_bytes / 4;
+            e = sgemm::launch_pack_rows(B, ldb, sh.b_rows, sh.b_cols, bp, sh.ldb2, stream);
+            g.B = bp;
+            g.ldb = sh.ldb2;
+        }
+        if (e != hipSuccess) {
+            sgemm::scratch_release(g.scratch, pack_ws, stream);
+            return to_status(e);
+        }
+        vec = true;
+    }
+    const int st = dispatch(p, g, vec, plain, stream);
+    if (pack_ws != nullptr) {
+        const hipError_t r = sgemm::scratch_release(g.scratch, pack_ws, stream);
+        if (st == 0 && r != hipSuccess) return to_status(r);
+    }
+    return st;
+}
+
+// Runs a plan on the call's arguments (operands already packed where the plan says so).
+int dispatch(const Plan &p, const GemmArgs &g, bool vec, bool plain, hipStream_t stream) {
+    const int M = g.M, N = g.N, K = g.K, ta = g.trans_a, tb = g.trans_b;
+    const int64_t lda = g.lda, ldb = g.ldb;
     switch (p.variant) {
         case SGEMM_F32_MFMA_LARGE:
             if (!vec) return SGEMM_F32_ERR_NOT_APPLICABLE;
@@ -467,7 +565,7 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         case SGEMM_F32_SKINNY:
             if (sgemm::skinny_form(ta, tb, M, N, K, lda, ldb) < 0) return SGEMM_F32_ERR_NOT_APPLICABLE;
             if (sgemm::skinny_grid(g) > kMaxGrid) return SGEMM_F32_ERR_TOO_LARGE;
-            return to_status(sgemm::launch_skinny(g, aligned16(A, lda, B, ldb), stream));
+            return to_status(sgemm::launch_skinny(g, aligned16(g.A, (int)lda, g.B, (int)ldb), stream));
         default:
             return SGEMM_F32_ERR_VARIANT;
     }

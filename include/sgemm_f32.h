@@ -36,9 +36,10 @@
  *   - Device memory (see sgemm_f32_noalloc for the form that allocates
  *     nothing): none unless the reduction over K is split across
  *     work-groups (the streaming kernels, MFMA plans with splits > 1 from the
- *     tuning table or sgemm_f32_ex_config, and the stream-K configuration).
- *     Such a call needs scratch (at most splits * M * N floats, 1 GiB cap for
- *     MFMA plans), taken from a memory pool the library creates on the first
+ *     tuning table or sgemm_f32_ex_config, and the stream-K configuration)
+ *     or the automatic choice copies misaligned operands to aligned rows
+ *     (at most 64 MiB).  Such a call needs scratch (at most splits * M * N
+ *     floats, 1 GiB cap for MFMA plans), taken from a memory pool the library creates on the first
  *     such call on a device (it keeps up to 1 GiB of freed memory and lives
  *     until the process ends):
  *       - outside graph capture, up to 64 MiB, on one of the first 8 streams
@@ -105,7 +106,10 @@ enum sgemm_f32_variant_id {
     SGEMM_F32_SKINNY = 4,         /* FP32 MFMA streaming kernels: M <= 32 (plain form), or
                                      M <= 16 with B transposed, or N <= 16 with A as given */
     SGEMM_F32_MFMA_SCALAR = 5,    /* FP32 MFMA with 4-byte loads: any alignment and stride (the
-                                     automatic choice splits K on grids of fewer than 256 tiles) */
+                                     automatic choice splits K on grids of fewer than 256 tiles;
+                                     on products of at least 2^32 FLOP it copies such operands,
+                                     up to 64 MiB, to aligned scratch rows and runs the plan
+                                     aligned operands get) */
     SGEMM_F32_MFMA_TUNED = 6,     /* FP32 MFMA with the automatic plan: the tuning table's,
                                      64x64 tiles with two slices in flight, 256x256 tiles, or
                                      128x128 or 64x64 tiles loaded straight into LDS (16-byte

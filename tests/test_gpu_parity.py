@@ -114,6 +114,40 @@ def test_unaligned_few_tiles_split(sg, case):
     assert plan[1] == sg.MFMA_SCALAR and (plan[4] > 1) == (K >= 512), plan
 
 
+# Odd row strides on larger products: the operands that 16-byte loads cannot
+# take are copied into aligned scratch rows first (A, B or both).
+PACKED = [(2047, 2047, 2047, None, None), (2048, 2048, 2047, None, 2048), (1300, 2001, 1999, 2000, None),
+          (1500, 1600, 1999, None, 1601)]
+
+
+@pytest.mark.parametrize("case", PACKED, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in PACKED])
+def test_unaligned_operands_packed(sg, case):
+    M, N, K, lda, ldb = case
+    say(f"[packed] {case}")
+    plan = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, 256, lda or K, 256, ldb or N)
+    assert plan[1] != sg.MFMA_SCALAR, plan
+    A, B, C0 = _inputs(M, N, K, "uniform", 60 + M)
+    st, C, _ = run_lib(sg, VID["auto"], A, B, C0, 1.25, -0.5, lda=lda, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.25, -0.5, C0)
+    assert ok, info
+    # The same plan on aligned copies gives the same bits.
+    dA = torch.from_numpy(np.pad(A, ((0, 0), (0, (-K) % 4)))).cuda()
+    dB = torch.from_numpy(np.pad(B, ((0, 0), (0, (-N) % 4)))).cuda()
+    dC = torch.from_numpy(C0).cuda()
+    st = sg.sgemm_f32_ex_config(plan[2], plan[3], plan[4], 0, 0, M, N, K, 1.25, dA.data_ptr(), dA.shape[1],
+                                dB.data_ptr(), dB.shape[1], -0.5, dC.data_ptr(), N,
+                                torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0
+    assert np.array_equal(dC.cpu().numpy().view(np.uint32), C.view(np.uint32))
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 70 + M, c0=False)
+    st, C, _ = run_lib(sg, VID["auto"], Ai, Bi, None, -1.0, 0.0, lda=lda, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, Ai, Bi, -1.0, 0.0, None, exact=True)
+    assert ok, info
+
+
 @pytest.mark.parametrize("variant", GENERAL + ["skinny"])
 def test_beta_zero_ignores_nan_c(sg, variant):
     for M in ((16, 27) if variant == "skinny" else (150,)):   # one and two blocks of 16 rows

@@ -123,6 +123,23 @@ def test_odd_strides_and_misaligned(sg, form, variant):
     assert ok, info
 
 
+@pytest.mark.parametrize("form", FORMS[1:], ids=FORM_IDS[1:])
+def test_unaligned_operands_packed(sg, form):
+    """Odd row strides of transposed operands on a larger product: copied
+    into aligned scratch rows first."""
+    ta, tb = form
+    M, N, K = 1700, 1500, 1600
+    A, B, C0 = _inputs(M, N, K, "uniform", 26)
+    wa = M if ta else K
+    wb = K if tb else N
+    say(f"[t_packed] {form}")
+    st, C, As, Bs = run_ex(sg, VID["auto"], ta, tb, A, B, C0, 0.75, 0.5, lda=wa + 1, ldb=wb + 1)
+    assert st == 0
+    assert sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, 256, wa + 1, 256, wb + 1)[1] != sg.MFMA_SCALAR
+    ok, info = check_op_full(C, As, Bs, ta, tb, 0.75, 0.5, C0)
+    assert ok, info
+
+
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_beta_zero_ignores_nan_c(sg, form):
     ta, tb = form

@@ -147,7 +147,11 @@ def test_kernel_selection(sg):
     assert sg.sgemm_f32_select(16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
     assert sg.sgemm_f32_select(32, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY   # two blocks of 16 rows
     assert sg.sgemm_f32_select(33, 4096, 4096, 1.0, al, 4096, al, 4096) != sg.SKINNY
-    assert sg.sgemm_f32_select(4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096) == sg.MFMA_SCALAR
+    # A misaligned A of 64 MiB is copied to aligned rows and takes the 256x256
+    # tiles; one past the copies' 64 MiB keeps the 4-byte loads.
+    assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096)[1:3] == \
+        (sg.MFMA_TUNED, sg.CFG_256x256)
+    assert sg.sgemm_f32_select(4097, 4096, 4096, 1.0, al + 4, 4096, al, 4096) == sg.MFMA_SCALAR
     assert sg.sgemm_f32_select(4096, 4096, 4097, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
     assert sg.sgemm_f32_select(4096, 4096, 4096, 0.0, al, 4096, al, 4096) == 0
     assert sg.sgemm_f32_select(4096, 4096, 0, 1.0, al, 1, al, 4096) == 0
@@ -213,7 +217,10 @@ def test_transposed_kernel_selection(sg):
         assert sel(ta, tb, 4096, 16, 4096, 1.0, al, 4096, al, 4096) == \
             (sg.MFMA_TUNED if ta else sg.SKINNY)
         assert sel(ta, tb, 4096, 17, 4096, 1.0, al, 4096, al, 4096) != sg.SKINNY
-        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_SCALAR
+        # An odd stride of A: copied to aligned rows when the copy fits in
+        # 64 MiB, 4-byte loads beyond.
+        assert sel(ta, tb, 4096, 4096, 4096, 1.0, al, 4097, al, 4096) == sg.MFMA_TUNED
+        assert sel(ta, tb, 4096, 4096, 4100, 1.0, al, 4101, al, 4100) == sg.MFMA_SCALAR
     assert sel(0, 0, 16, 4096, 4096, 1.0, al, 4096, al, 4096) == sg.SKINNY
     assert sel(0, 0, 4096, 16, 4096, 1.0, al, 4096, al, 16) == sg.SKINNY
     assert sel(0, 0, 4096, 1, 4096, 1.0, al, 4096, al, 1) == sg.SKINNY
@@ -230,7 +237,9 @@ def test_transposed_kernel_selection(sg):
     # 2 GiB rule: an operand stored along K spans 128 rows per slice, one
     # stored along M or N 32 rows.
     big = (1 << 31) // 4 // 100          # 128 rows of this stride exceed 2 GiB, 32 rows do not
-    assert sel(0, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_SCALAR
+    assert sel(0, 0, 4096, 4096, 4100, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_SCALAR
+    # ... unless the rows fit in 64 MiB once copied to aligned rows of their own.
+    assert sel(0, 0, 4096, 4096, 4096, 1.0, al, big - big % 4, al, 4096) == sg.MFMA_TUNED
     # A stored transposed (along M): 16-byte loads; the 256x256 tiles read 16 of its rows per slice.
     ld = big - big % 4
     assert sel(1, 0, 4096, 4096, 4096, 1.0, al, ld, al, 4096) == sg.MFMA_TUNED
@@ -354,9 +363,10 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     # The persistent stream-K configuration is never chosen automatically.
     for shape in [(3000, 3000, 3000), (2900, 4100, 2048), (5000, 5000, 1000)]:
         assert plan(*shape)[2] != sg.CFG_128x128_STREAMK, shape
-    # 4-byte loads keep their kernel.
-    st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 3000, 3000, 3001, 1.0, al, 3001, al, 3000)
+    # 4-byte loads keep their kernel where the aligned copy would exceed 64 MiB.
+    st, v, cfg, gm, sp = sg.sgemm_f32_ex_plan(0, 0, 4100, 4100, 4101, 1.0, al, 4101, al, 4100)
     assert (v, cfg) == (sg.MFMA_SCALAR, 0)
+    assert sg.sgemm_f32_ex_plan(0, 0, 3000, 3000, 3001, 1.0, al, 3001, al, 3000)[1] == sg.MFMA_TUNED
 
 
 def test_plan_follows_the_tuning_table(sg):
@@ -374,6 +384,14 @@ def test_plan_follows_the_tuning_table(sg):
     assert sg.sgemm_f32_ex_plan(0, 0, 4096, 17, 4096, 1.0, al, 4096, al, 17) == (0, sg.MFMA_SCALAR, 1, 8, 8)
     assert sg.sgemm_f32_ex_plan(0, 0, 1000, 33, 3001, 1.0, al, 3001, al, 36)[4] == 11
     assert sg.sgemm_f32_ex_plan(0, 0, 64, 64, 511, 1.0, al, 511, al, 64)[4] == 1
+    # Many tiles with 4-byte loads: operands copied to aligned rows first when
+    # the copies fit in 64 MiB and the product is at least 2^32 FLOP; the plan
+    # reported is the one that then runs.
+    assert sg.sgemm_f32_ex_plan(0, 0, 2047, 2047, 2047, 1.0, al, 2047, al, 2047) == \
+        (0, sg.MFMA_TUNED, sg.CFG_64x64_PF2, 8, 1)
+    assert sg.sgemm_f32_ex_plan(1, 1, 1700, 1500, 1600, 1.0, al, 1701, al, 1601)[1] == sg.MFMA_TUNED
+    assert sg.sgemm_f32_ex_plan(0, 0, 1023, 1023, 1023, 1.0, al, 1023, al, 1023)[1] == sg.MFMA_SCALAR
+    assert sg.sgemm_f32_ex_plan(0, 0, 4095, 4095, 4095, 1.0, al, 4095, al, 4095)[1] == sg.MFMA_SCALAR
     path = os.path.join(os.path.dirname(sg.__file__), "tuning_table.json")
     if not sg.sgemm_f32_tuning_table_present():
         assert not os.path.exists(path)
@@ -548,7 +566,7 @@ def test_big_tiles_for_whole_filled_grids(sg):
     # M, N or K not a multiple of 4, misaligned, too few or poorly filled rounds.
     assert plan(0, 0, 4094, 4096, 4096, 4096, 4096)[2] != sg.CFG_256x256
     assert plan(0, 0, 4096, 4096, 4098, 4098, 4096)[2] != sg.CFG_256x256
-    assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4096, 1.0, al + 4, 4096, al, 4096)[1] == sg.MFMA_SCALAR
+    assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4100, 1.0, al + 4, 4100, al, 4096)[1] == sg.MFMA_SCALAR
     assert plan(0, 0, 2048, 2048, 2048, 2048, 2048)[2] != sg.CFG_256x256
     assert plan(0, 0, 6144, 6144, 2048, 2048, 6144)[2] != sg.CFG_256x256     # 576 tiles: 75 % of 3 rounds
     p = 0x100000

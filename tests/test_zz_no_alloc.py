@@ -54,12 +54,14 @@ def _both(sg, A, B, C0, alpha, beta, stream):
 # (first, second) products: the second is smaller.  The automatic plans: the
 # M <= 16 split (scratch), a tuned split-K plan (scratch), the 64x64
 # direct-to-LDS grid (no scratch), the 4-byte-load tiles with K split (an
-# odd row stride of B or A).
+# odd row stride of B or A), and operands copied to aligned scratch rows
+# before a 64x64 plan (odd row strides on a larger product).
 CASES = {
     "skinny": ((16, 4096, 4096), (8, 1000, 3000)),
     "splitk": ((512, 512, 8192), (256, 256, 4096)),
     "grid": ((1024, 1024, 1024), (256, 384, 512)),
     "unaligned": ((4096, 17, 4096), (1000, 33, 3001)),
+    "packed": ((2047, 2047, 2047), (1500, 1600, 1999)),
 }
 
 
