@@ -306,6 +306,12 @@ constexpr int KM_G = KM_RW / 16;         // groups of 16 rows of W
 constexpr int KM_BK = 64;                // k per batch
 constexpr int KM_RED = KM_RW + 1;        // padded row of the LDS reduction
 constexpr int kKMajorMaxRows = 16;       // rows of X
+// Three batches in flight per wave where each wave streams at least
+// kDeepBatches batches of its split, two otherwise (per call, both operands
+// cycled past the Infinity Cache, two -> three: NT 16 x 11008 x 4096 53.3 ->
+// 50.4 us, NN 11008 x 16 x 4096 50.2 -> 46.9, with 8 batches per wave; NT
+// 16 x 4096 x 4096 22.8 -> 23.7 with 4).
+constexpr int kDeepBatches = 6;
 
 struct KmajArgs {
     const float *W;
@@ -369,7 +375,7 @@ __device__ __forceinline__ void kmaj_consume(const KBatch &bt, f32x4v (&acc)[KM_
 }
 
 // TOUT: D is C transposed (consecutive threads then write consecutive i).
-template <bool VEC, bool XT, bool TOUT>
+template <bool VEC, bool XT, bool TOUT, int DEPTH>
 __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int strips) {
     __shared__ float red[SK_NW][16 * KM_RED];
     poison_lds<sizeof(red)>(red);
@@ -397,19 +403,37 @@ __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int st
     f32x4v acc[KM_G];
 #pragma unroll
     for (int g = 0; g < KM_G; ++g) acc[g] = f32x4v{0.f, 0.f, 0.f, 0.f};
-    KBatch b0, b1;
     int b = bbeg;
-    // As in the other kernel: unconditional loads in the loop, past the end
+    // As in the other kernel: unconditional loads in the loops, past the end
     // re-reading the wave's last batch, which is then not consumed.
     auto kof = [&](int bi) { return kbeg + (bi < bend ? bi : bend - 1) * KM_BK; };
-    if (b < bend) kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
-    for (; b + 1 < bend; b += 2) {
-        kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
-        kmaj_consume(b0, acc);
-        kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
-        kmaj_consume(b1, acc);
+    if constexpr (DEPTH == 2) {
+        KBatch b0, b1;
+        if (b < bend) kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+        for (; b + 1 < bend; b += 2) {
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+            kmaj_consume(b0, acc);
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
+            kmaj_consume(b1, acc);
+        }
+        if (b < bend) kmaj_consume(b0, acc);
+    } else {
+        KBatch b0, b1, b2;
+        if (b < bend) {
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+        }
+        for (; b + 2 < bend; b += 3) {
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b2);
+            kmaj_consume(b0, acc);
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 3), kend, h, j, b0);
+            kmaj_consume(b1, acc);
+            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 4), kend, h, j, b1);
+            kmaj_consume(b2, acc);
+        }
+        if (b < bend) kmaj_consume(b0, acc);
+        if (b + 1 < bend) kmaj_consume(b1, acc);
     }
-    if (b < bend) kmaj_consume(b0, acc);
 
     // acc[g] register r of lane (j, h) holds i = 4 h + r, row r0 + 16 g + j
     // of W.  The waves' partials are added in wave order.
@@ -532,6 +556,15 @@ using KmajKern = void (*)(KmajArgs, int);
 
 bool aligned16(const float *p, int64_t ld) { return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0; }
 
+template <int DEPTH>
+KmajKern kmaj_instance(bool vec, bool xt, bool tout) {
+    if (vec)
+        return xt ? (tout ? sgemm_kmaj_kernel<true, true, true, DEPTH> : sgemm_kmaj_kernel<true, true, false, DEPTH>)
+                  : (tout ? sgemm_kmaj_kernel<true, false, true, DEPTH> : sgemm_kmaj_kernel<true, false, false, DEPTH>);
+    return xt ? (tout ? sgemm_kmaj_kernel<false, true, true, DEPTH> : sgemm_kmaj_kernel<false, true, false, DEPTH>)
+              : (tout ? sgemm_kmaj_kernel<false, false, true, DEPTH> : sgemm_kmaj_kernel<false, false, false, DEPTH>);
+}
+
 // The streamed operand W and the small operand X of the K-major forms.
 KmajArgs kmaj_args(const GemmArgs &g, int form, float *ws, int splits, int split_rows, bool *xt) {
     const bool bw = form == kSkinnyBKMajor;   // W = B (N x K); else W = A (M x K), D = C transposed
@@ -607,13 +640,8 @@ hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) 
         const bool tout = form == kSkinnyAKMajor;
         // 16-byte loads of W, and of X where X is read along k.
         const bool vec = aligned16(a.W, a.ldw) && (xt || aligned16(a.X, a.x_si));
-        KmajKern k;
-        if (vec)
-            k = xt ? (tout ? sgemm_kmaj_kernel<true, true, true> : sgemm_kmaj_kernel<true, true, false>)
-                   : (tout ? sgemm_kmaj_kernel<true, false, true> : sgemm_kmaj_kernel<true, false, false>);
-        else
-            k = xt ? (tout ? sgemm_kmaj_kernel<false, true, true> : sgemm_kmaj_kernel<false, true, false>)
-                   : (tout ? sgemm_kmaj_kernel<false, false, true> : sgemm_kmaj_kernel<false, false, false>);
+        const bool deep = (int64_t)split_rows >= (int64_t)kDeepBatches * KM_BK * SK_NW;
+        const KmajKern k = deep ? kmaj_instance<3>(vec, xt, tout) : kmaj_instance<2>(vec, xt, tout);
         hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, a, strips);
     }
     hipError_t e = hipGetLastError();

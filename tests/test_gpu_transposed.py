@@ -172,14 +172,14 @@ def test_unsupported_variants_refuse(sg, form):
 # M <= 16 (NT, TT), and A as given with N <= 16 (NN, NT; C written
 # transposed).  (ta, tb, M, N, K): ragged row counts of the streamed side
 # (edge work-groups of 32 rows), K tails inside a 64-deep batch, splits of K
-# over work-groups with 0 to 8 batches per wave.
+# over work-groups with 0 to 8 batches per wave (two or three in flight).
 SKINNY_KMAJ = [(0, 1, 16, 4096, 300), (0, 1, 1, 1, 1), (0, 1, 3, 33, 100), (0, 1, 16, 2050, 1000),
                (0, 1, 13, 4093, 777), (0, 1, 16, 100, 4099), (0, 1, 15, 16, 17), (0, 1, 16, 200, 8191),
                (1, 1, 16, 4096, 300), (1, 1, 5, 130, 777), (1, 1, 16, 257, 513), (1, 1, 1, 4097, 65),
                (0, 0, 4096, 16, 300), (0, 0, 1000, 1, 77), (0, 0, 2050, 16, 1000), (0, 0, 33, 11, 4099),
                (0, 0, 4093, 14, 777), (0, 0, 100, 3, 8191), (0, 1, 4096, 16, 300), (0, 1, 130, 9, 2000),
                (0, 1, 2051, 16, 64), (0, 1, 4, 16384, 2000), (0, 0, 16384, 8, 1280), (1, 1, 12, 16000, 700),
-               (0, 0, 4096, 1, 300)]
+               (0, 0, 4096, 1, 300), (0, 0, 16400, 5, 1700)]
 KMAJ_IDS = [f"{FORM_IDS[2 * ta + tb]}-{m}x{n}x{k}" for ta, tb, m, n, k in SKINNY_KMAJ]
 
 
