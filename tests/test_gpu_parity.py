@@ -539,13 +539,18 @@ def test_auto_plan_with_c_stride_past_32bit_offsets(sg, shape, planned):
     assert ok, info
 
 
-@pytest.mark.parametrize("case", ["skinny", "splitk"])
+GRAPH_CASES = {"skinny": (16, 4096, 4096), "splitk": (512, 512, 8192), "kmajor": (4096, 16, 4096),
+               "unaligned_split": (4096, 17, 4096), "packed": (2047, 2047, 2047)}
+
+
+@pytest.mark.parametrize("case", sorted(GRAPH_CASES))
 def test_split_plans_in_a_captured_graph(sg, case):
     """A call whose plan allocates stream-ordered scratch (the M <= 16 split,
-    a tuned split-K plan), recorded into a graph: every replay, with eager
-    work and synchronisation between replays, matches the eager result bit
-    for bit."""
-    M, N, K = (16, 4096, 4096) if case == "skinny" else (512, 512, 8192)
+    a tuned split-K plan, the N <= 16 streaming kernel's split, the 4-byte-load
+    tiles with K split, operands copied to aligned rows), recorded into a
+    graph: every replay, with eager work and synchronisation between replays,
+    matches the eager result bit for bit."""
+    M, N, K = GRAPH_CASES[case]
     say(f"[graph] {case} {M}x{N}x{K}")
     A, B, _ = _inputs(M, N, K, "uniform", 80, c0=False)
     dA, dB = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
