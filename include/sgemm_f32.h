@@ -304,6 +304,10 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * at least 1536 goes back to configuration 4 with K split in 2 or 3, and one
  * that is also one round of 250 to 256 tiles of 128 x 128 with K of at least
  * 1024 goes to configuration 8.
+ * Where the automatic choice first copies misaligned operands to aligned
+ * rows (SGEMM_F32_MFMA_SCALAR above), sgemm_f32_ex_plan reports the plan that
+ * then runs on the copies; sgemm_f32_ex_config with that plan on the original
+ * operands returns SGEMM_F32_ERR_NOT_APPLICABLE where it needs 16-byte loads.
  * A split plan whose partials exceed 1 GiB returns SGEMM_F32_ERR_TOO_LARGE.
  * Other arguments and return codes are those of sgemm_f32_ex.
  */
