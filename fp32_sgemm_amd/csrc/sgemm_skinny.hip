@@ -312,6 +312,16 @@ constexpr int kKMajorMaxRows = 16;       // rows of X
 // 50.4 us, NN 11008 x 16 x 4096 50.2 -> 46.9, with 8 batches per wave; NT
 // 16 x 4096 x 4096 22.8 -> 23.7 with 4).
 constexpr int kDeepBatches = 6;
+// Splits of 512 to KM_XL_ROWS k with X read along k stage each wave's part
+// of X in LDS (rows of KM_XS floats: the part's KM_XL_ROWS / 4 k and a pad
+// that spreads the 16 rows over the banks): per call, both operands cycled,
+// NT 16 x 4096 x 4096 22.9 -> 21.0 us, NT 16 x 2048 x 8192 23.2 -> 21.0, NT
+// 4096 x 16 x 4096 23.0 -> 21.0.  Staging k-major X (16 scalar loads per k
+// row pass, written across rows) lost: TT 16 x 4096 x 4096 21.2 -> 26.0, NN
+// 4096 x 16 x 4096 21.3 -> 26.3; so did one batch per wave (NT 8 x 1024 x
+// 1024 7.2 -> 8.8).
+constexpr int KM_XL_ROWS = 1024;
+constexpr int KM_XS = KM_XL_ROWS / SK_NW + 4;
 
 struct KmajArgs {
     const float *W;
@@ -335,7 +345,7 @@ struct KBatch {
     float4 x[4];
 };
 
-template <bool VEC, bool XT>
+template <bool VEC, bool XT, bool XL>
 __device__ __forceinline__ void kmaj_load(const KmajArgs &a, __amdgpu_buffer_rsrc_t rw, __amdgpu_buffer_rsrc_t rx,
                                           int rows, int kb, int kend, int h, int j, KBatch &bt) {
 #pragma unroll
@@ -346,7 +356,8 @@ __device__ __forceinline__ void kmaj_load(const KmajArgs &a, __amdgpu_buffer_rsr
             const int r = 16 * g + j;            // row of W within the work-group's rows
             bt.w[g][q] = load_group<VEC, 0>(rw, (int)((r * a.ldw + k) * 4), k, r < rows ? kend : 0);
         }
-        if (XT) {                                // X(j, k..k+3) lies down a column
+        if (XL) {                                // X comes from the wave's LDS slice
+        } else if (XT) {                         // X(j, k..k+3) lies down a column
             float v[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e)
@@ -375,10 +386,18 @@ __device__ __forceinline__ void kmaj_consume(const KBatch &bt, f32x4v (&acc)[KM_
 }
 
 // TOUT: D is C transposed (consecutive threads then write consecutive i).
-template <bool VEC, bool XT, bool TOUT, int DEPTH>
+// MODE 0: two batches in flight; 1: three; 2: two, with X (read along k)
+// staged once per wave in LDS (splits of at most KM_XL_ROWS k: a wave's part
+// is at most KM_XL_ROWS / 4 k).
+template <bool VEC, bool XT, bool TOUT, int MODE>
 __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int strips) {
-    __shared__ float red[SK_NW][16 * KM_RED];
-    poison_lds<sizeof(red)>(red);
+    constexpr bool XL = MODE == 2;
+    constexpr int DEPTH = MODE == 1 ? 3 : 2;
+    // Per wave: its X slice (16 rows of KM_XS floats) when staged, then the
+    // partial strip for the reduction (which overwrites the slice).
+    constexpr int WSTRIDE = XL ? 16 * KM_XS : 16 * KM_RED;
+    __shared__ __align__(16) float lds[SK_NW * WSTRIDE];
+    poison_lds<sizeof(lds)>(lds);
     int split, strip;
     tile_of_block(blockIdx.x, a.splits, strips, 1, split, strip);
     const int r0 = strip * KM_RW;
@@ -407,28 +426,66 @@ __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int st
     // As in the other kernel: unconditional loads in the loops, past the end
     // re-reading the wave's last batch, which is then not consumed.
     auto kof = [&](int bi) { return kbeg + (bi < bend ? bi : bend - 1) * KM_BK; };
-    if constexpr (DEPTH == 2) {
+    float *xs = lds + wave * WSTRIDE;
+    if constexpr (XL) {
+        static_assert(!XT, "X is staged where it is read along k");
+        // This wave's X(0..15, ks .. ks + KM_XL_ROWS / 4), zero past its
+        // range and past MX, read with whole-row loads (64 lanes x 16 bytes of
+        // one row of X) and written to LDS as rows of KM_XS floats.  Only
+        // this wave reads it, so no barrier orders it.
         KBatch b0, b1;
-        if (b < bend) kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+        if (b < bend) {
+            const int ks = kbeg + bbeg * KM_BK;
+            const int ke = min(kend, kbeg + bend * KM_BK);
+            float4 v[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                v[i] = load_group<VEC, 0>(rx, (int)((i * a.x_si + ks + 4 * lane) * 4), ks + 4 * lane,
+                                          i < a.MX ? ke : 0);
+            // The first batch of W goes out before the X rows are written.
+            kmaj_load<VEC, XT, true>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) *reinterpret_cast<float4 *>(xs + i * KM_XS + 4 * lane) = v[i];
+        }
+        auto xfrag = [&](int bi, KBatch &bt) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                bt.x[q] = *reinterpret_cast<const float4 *>(xs + j * KM_XS + (bi - bbeg) * KM_BK + 16 * q + 4 * h);
+        };
         for (; b + 1 < bend; b += 2) {
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+            kmaj_load<VEC, XT, true>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+            xfrag(b, b0);
             kmaj_consume(b0, acc);
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
+            kmaj_load<VEC, XT, true>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
+            xfrag(b + 1, b1);
+            kmaj_consume(b1, acc);
+        }
+        if (b < bend) {
+            xfrag(b, b0);
+            kmaj_consume(b0, acc);
+        }
+    } else if constexpr (DEPTH == 2) {
+        KBatch b0, b1;
+        if (b < bend) kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+        for (; b + 1 < bend; b += 2) {
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+            kmaj_consume(b0, acc);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 2), kend, h, j, b0);
             kmaj_consume(b1, acc);
         }
         if (b < bend) kmaj_consume(b0, acc);
     } else {
         KBatch b0, b1, b2;
         if (b < bend) {
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b), kend, h, j, b0);
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b), kend, h, j, b0);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 1), kend, h, j, b1);
         }
         for (; b + 2 < bend; b += 3) {
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 2), kend, h, j, b2);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 2), kend, h, j, b2);
             kmaj_consume(b0, acc);
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 3), kend, h, j, b0);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 3), kend, h, j, b0);
             kmaj_consume(b1, acc);
-            kmaj_load<VEC, XT>(a, rw, rx, rows, kof(b + 4), kend, h, j, b1);
+            kmaj_load<VEC, XT, false>(a, rw, rx, rows, kof(b + 4), kend, h, j, b1);
             kmaj_consume(b2, acc);
         }
         if (b < bend) kmaj_consume(b0, acc);
@@ -440,7 +497,7 @@ __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int st
 #pragma unroll
     for (int g = 0; g < KM_G; ++g)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][(4 * h + r) * KM_RED + 16 * g + j] = acc[g][r];
+        for (int r = 0; r < 4; ++r) xs[(4 * h + r) * KM_RED + 16 * g + j] = acc[g][r];
     __syncthreads();
     constexpr int NI = 16;
     constexpr int PER_T = NI * KM_RW / SK_NT;
@@ -451,7 +508,7 @@ __global__ __launch_bounds__(SK_NT, 2) void sgemm_kmaj_kernel(KmajArgs a, int st
         const int c = TOUT ? idx / NI : idx % KM_RW;
         float s = 0.f;
 #pragma unroll
-        for (int w = 0; w < SK_NW; ++w) s += red[w][i * KM_RED + c];
+        for (int w = 0; w < SK_NW; ++w) s += lds[w * WSTRIDE + i * KM_RED + c];
         if (i < a.MX && r0 + c < a.R) {
             const int64_t r = r0 + c;
             if (a.splits > 1) {
@@ -556,6 +613,11 @@ using KmajKern = void (*)(KmajArgs, int);
 
 bool aligned16(const float *p, int64_t ld) { return reinterpret_cast<uintptr_t>(p) % 16 == 0 && ld % 4 == 0; }
 
+KmajKern kmaj_staged_instance(bool vec, bool tout) {
+    if (vec) return tout ? sgemm_kmaj_kernel<true, false, true, 2> : sgemm_kmaj_kernel<true, false, false, 2>;
+    return tout ? sgemm_kmaj_kernel<false, false, true, 2> : sgemm_kmaj_kernel<false, false, false, 2>;
+}
+
 template <int DEPTH>
 KmajKern kmaj_instance(bool vec, bool xt, bool tout) {
     if (vec)
@@ -641,7 +703,10 @@ hipError_t launch_skinny(const GemmArgs &g, bool vec_loads, hipStream_t stream) 
         // 16-byte loads of W, and of X where X is read along k.
         const bool vec = aligned16(a.W, a.ldw) && (xt || aligned16(a.X, a.x_si));
         const bool deep = (int64_t)split_rows >= (int64_t)kDeepBatches * KM_BK * SK_NW;
-        const KmajKern k = deep ? kmaj_instance<3>(vec, xt, tout) : kmaj_instance<2>(vec, xt, tout);
+        // X read along k is staged in LDS when each wave has 2 to 4 batches.
+        const bool staged = !xt && split_rows >= 2 * KM_BK * SK_NW && split_rows <= KM_XL_ROWS;
+        const KmajKern k = deep ? kmaj_instance<1>(vec, xt, tout)
+                                : staged ? kmaj_staged_instance(vec, tout) : kmaj_instance<0>(vec, xt, tout);
         hipLaunchKernelGGL(k, grid, dim3(SK_NT), 0, stream, a, strips);
     }
     hipError_t e = hipGetLastError();

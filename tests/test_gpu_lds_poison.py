@@ -130,7 +130,8 @@ def test_poisoned_valu_and_skinny(plib, variant, M, N):
 
 
 @pytest.mark.parametrize("case", [(0, 1, 16, 1000, 3000), (1, 1, 13, 1000, 3000), (0, 0, 1000, 16, 3000),
-                                  (0, 1, 4, 16384, 2000)], ids=["nt", "tt", "nn_tall", "nt_long_k"])
+                                  (0, 1, 4, 16384, 2000), (0, 1, 16, 4096, 2048), (0, 1, 4096, 13, 2000)],
+                         ids=["nt", "tt", "nn_tall", "nt_long_k", "nt_staged", "nt_tall_staged"])
 def test_poisoned_skinny_kmajor(plib, case):
     """The streaming kernel for operands whose rows run along k (B given
     N x K with M <= 16, A as given with N <= 16)."""

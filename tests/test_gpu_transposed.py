@@ -179,7 +179,9 @@ SKINNY_KMAJ = [(0, 1, 16, 4096, 300), (0, 1, 1, 1, 1), (0, 1, 3, 33, 100), (0, 1
                (0, 0, 4096, 16, 300), (0, 0, 1000, 1, 77), (0, 0, 2050, 16, 1000), (0, 0, 33, 11, 4099),
                (0, 0, 4093, 14, 777), (0, 0, 100, 3, 8191), (0, 1, 4096, 16, 300), (0, 1, 130, 9, 2000),
                (0, 1, 2051, 16, 64), (0, 1, 4, 16384, 2000), (0, 0, 16384, 8, 1280), (1, 1, 12, 16000, 700),
-               (0, 0, 4096, 1, 300), (0, 0, 16400, 5, 1700)]
+               (0, 0, 4096, 1, 300), (0, 0, 16400, 5, 1700),
+               # X read along k staged in LDS (splits of 512 to 1024 k)
+               (0, 1, 16, 4096, 4096), (0, 1, 13, 4093, 2000), (0, 1, 4093, 11, 3000)]
 KMAJ_IDS = [f"{FORM_IDS[2 * ta + tb]}-{m}x{n}x{k}" for ta, tb, m, n, k in SKINNY_KMAJ]
 
 
@@ -205,7 +207,8 @@ def test_skinny_kmajor_forms(sg, variant, case):
 
 
 @pytest.mark.parametrize("case", [(0, 1, 16, 97, 61), (1, 1, 14, 130, 200), (0, 0, 141, 16, 61),
-                                  (0, 1, 141, 7, 130)], ids=["nt", "tt", "nn-tall", "nt-tall"])
+                                  (0, 1, 141, 7, 130), (0, 1, 16, 4096, 2500)],
+                         ids=["nt", "tt", "nn-tall", "nt-tall", "nt-staged"])
 def test_skinny_kmajor_odd_strides_and_beta_zero(sg, case):
     """Misaligned operands and odd strides (element-by-element loads), then
     beta = 0 over a C of NaNs, which must not be read."""
