@@ -240,7 +240,12 @@ Plan big_tile_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 // kResidentSmallTiles tiles (one round): 1024^3 87.8
 // -> 92.5, TN 93.6 -> 101.9; 1536^3 97.6 -> 101.5; 2048^3 TN 135.4 -> 139.1;
 // 2048 x 2048 x 1024 127.0 -> 128.0; 512 x 512 x 8192 (no split) 31.8 -> 33.3,
-// TN 30.1 -> 33.6; 2048 x 2000 x 2048 122.6 -> 125.7, TN 121.5 -> 127.8.
+// TN 30.1 -> 33.6; 2048 x 2000 x 2048 122.6 -> 125.7, TN 121.5 -> 127.8; with
+// edge tiles (M, N multiples of 4), same box, forced plans: 500 x 2000 x 4096
+// 109.0 -> 124.3, 1000^3 94.8 -> 104.1, 700 x 900 x 3000 69.9 -> 79.5, 100 x
+// 5000 x 2048 54.4 -> 61.8, 1020^3 98.9 -> 107.1, 2044^3 131.7 -> 135.1, 1500 x
+// 1500 x 2000 96.9 -> 100.8, 2000 x 2000 x 8192 134.7 -> 135.5, 1000 x 1000 x
+// 256 66.3 -> 66.5 (twelve shapes, none lost).
 // Grids of several rounds did not gain: 2560^3 127.5 -> 126.7, TN 126.8 ->
 // 128.9; 4608 x 4608 x 2048 135.8 -> 134.9, TN 135.5 -> 138.2; 3008^3 121.4
 // -> 109.5, TN 127.8 -> 121.1; and with edge tiles and a K tail 3000^3 130.6
@@ -258,8 +263,7 @@ Plan direct_lds_plan(const Plan &p, int ta, int tb, int M, int N, int K, const f
     g.lda = lda; g.ldb = ldb;
     g.trans_a = ta; g.trans_b = tb;
     if (!sgemm::big_tile_fits(g)) return p;
-    if (p.config == 4 && (M % 64 != 0 || N % 64 != 0 || (int64_t)(M / 64) * (N / 64) > kResidentSmallTiles))
-        return p;
+    if (p.config == 4 && (int64_t)((M + 63) / 64) * ((N + 63) / 64) > kResidentSmallTiles) return p;
     return Plan{SGEMM_F32_MFMA_TUNED, p.config == 0 ? 8 : 9, p.group_m, 1};
 }
 
@@ -356,11 +360,12 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb);
 
 // Operands that 16-byte loads cannot take, on a product of at least 2^32
-// FLOP that the 4-byte-load tiles would run without a split: the operand (or
-// both) is first copied into scratch rows padded to a multiple of 4 floats,
-// and the product runs the plan aligned operands get, when that plan needs no
-// scratch of its own and the copies fit in SGEMM_F32_NOALLOC_SCRATCH_BYTES
-// (so the allocation-free entry point takes the same plan).  Per call, 4-byte
+// FLOP: the operand (or both) is first copied into scratch rows padded to a
+// multiple of 4 floats, and the product runs the plan aligned operands get
+// (not stream-K), when the copies and that plan's split partials fit in
+// SGEMM_F32_NOALLOC_SCRATCH_BYTES together (so the allocation-free entry
+// point takes the same plan); one acquisition holds both, the partials after
+// the copies.  Per call, 4-byte
 // loads -> copies and 64x64 tiles with two slices in flight (odd extents keep
 // the direct-to-LDS tiles out): 2047^3 195.7 -> 167.4 us, 3001 x 2001 x 1001
 // 154.9 -> 121.2, 2048 x 2048 x 2047 154.6 -> 136.4; 1023^3 lost (42.6 ->
@@ -388,8 +393,16 @@ PackShape pack_shape(int pack, int ta, int tb, int M, int N, int K, int64_t lda,
     return s;
 }
 
+// Split partials of an MFMA plan on packed operands (bytes; 0 without a split).
+int64_t packed_partial_bytes(const Plan &p, int M, int N, int K) {
+    if (p.splits <= 1) return 0;
+    int k_per = 0;
+    const int splits = sgemm::mfma_effective_splits(K, p.splits, &k_per);
+    return splits > 1 ? round_up((int64_t)splits * M * N * 4, 256) : 0;
+}
+
 Plan pack_plan(const Plan &d, int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb) {
-    if (d.splits > 1 || 2 * (int64_t)M * N * K < kPackMinFlop) return d;
+    if (2 * (int64_t)M * N * K < kPackMinFlop) return d;
     const bool pa = !(aligned16(A, lda, A, 0) && slice_fits(!ta, lda));
     const bool pb = !(aligned16(B, ldb, B, 0) && slice_fits(tb, ldb));
     if (!pa && !pb) return d;
@@ -400,7 +413,7 @@ Plan pack_plan(const Plan &d, int ta, int tb, int M, int N, int K, const float *
     Plan p = auto_plan(ta, tb, M, N, K, pa ? aligned_stand_in : A, (int)s.lda2, pb ? aligned_stand_in : B,
                        (int)s.ldb2);
     if (p.variant == SGEMM_F32_MFMA_SCALAR || p.variant == SGEMM_F32_SKINNY || p.variant == SGEMM_F32_VALU ||
-        p.splits > 1 || p.config == 5)
+        p.config == 5 || s.a_bytes + s.b_bytes + packed_partial_bytes(p, M, N, K) > kPackMaxBytes)
         return d;
     p.pack = pack;
     return p;
@@ -459,9 +472,9 @@ GemmArgs make_args(int ta, int tb, int M, int N, int K, float alpha, const float
 // Scratch bytes of a plan (0 for plans without a split), or -1 when the
 // occupancy query of the stream-K plan fails.
 int64_t plan_scratch_bytes(const Plan &p, const GemmArgs &g) {
-    if (p.pack) {   // the copies only: a plan on packed operands needs no other scratch
+    if (p.pack) {   // the copies, then the plan's split partials
         const PackShape s = pack_shape(p.pack, g.trans_a, g.trans_b, g.M, g.N, g.K, g.lda, g.ldb);
-        return s.a_bytes + s.b_bytes;
+        return s.a_bytes + s.b_bytes + packed_partial_bytes(p, g.M, g.N, g.K);
     }
     if (p.variant == SGEMM_F32_SKINNY) return sgemm::skinny_scratch_bytes(g);
     if (p.variant == SGEMM_F32_VALU) return 0;
@@ -515,9 +528,18 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
         // Copy the operands that 16-byte loads cannot take into aligned rows
         // of the call's scratch, in stream order before the product.
         const PackShape sh = pack_shape(p.pack, ta, tb, M, N, K, lda, ldb);
-        hipError_t e = sgemm::scratch_acquire(g.scratch, (size_t)(sh.a_bytes + sh.b_bytes), stream, &pack_ws);
+        const int64_t copies = sh.a_bytes + sh.b_bytes;
+        const int64_t partials = packed_partial_bytes(p, M, N, K);
+        hipError_t e = sgemm::scratch_acquire(scratch, (size_t)(copies + partials), stream, &pack_ws);
         if (e != hipSuccess) return to_status(e);
         float *base = static_cast<float *>(pack_ws);
+        // The plan's own scratch: the rest of the same block, handed to it as
+        // a fixed region (a second acquisition on this stream could return
+        // the same cached block).
+        if (partials > 0) {
+            g.scratch.fixed = static_cast<char *>(pack_ws) + copies;
+            g.scratch.fixed_bytes = (size_t)partials;
+        }
         if (p.pack & 1) {
             e = sgemm::launch_pack_rows(A, lda, sh.a_rows, sh.a_cols, base, sh.lda2, stream);
             g.A = base;
@@ -530,14 +552,14 @@ int run(int variant, int ta, int tb, int M, int N, int K, float alpha, const flo
             g.ldb = sh.ldb2;
         }
         if (e != hipSuccess) {
-            sgemm::scratch_release(g.scratch, pack_ws, stream);
+            sgemm::scratch_release(scratch, pack_ws, stream);
             return to_status(e);
         }
         vec = true;
     }
     const int st = dispatch(p, g, vec, plain, stream);
     if (pack_ws != nullptr) {
-        const hipError_t r = sgemm::scratch_release(g.scratch, pack_ws, stream);
+        const hipError_t r = sgemm::scratch_release(scratch, pack_ws, stream);
         if (st == 0 && r != hipSuccess) return to_status(r);
     }
     return st;

@@ -293,8 +293,8 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * with the same conditions; they honour the grouping and take no split count
  * (splits must be 1).  The automatic choice takes configuration 8 in place of the 128 x 128
  * grid and 9 in place of configuration 4, each without a split, when those
- * conditions hold, for configuration 9 also M and N multiples of 64 with at
- * most 1024 tiles (again, a C stride too wide at call time keeps the plan's
+ * conditions hold, for configuration 9 also at most 1024 tiles of 64 x 64
+ * (edge tiles included) (again, a C stride too wide at call time keeps the plan's
  * register-staged kernel).  It takes configuration 10 in place of an unsplit
  * 128 x 128 or 64 x 64 plan when the 192 x 192 grid has 250 to 256 tiles (one
  * round), and in place of an unsplit 64 x 64 plan when it has whole rounds

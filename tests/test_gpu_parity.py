@@ -90,6 +90,28 @@ def test_skinny_shapes(sg, variant, shape):
     assert ok, info
 
 
+# Grids with edge tiles (M, N multiples of 4 but not of 64) through the
+# automatic plan: 64x64 direct-to-LDS tiles, one round of 128x128 ones, and a
+# K split where the 64x64 grid spreads unevenly.
+AUTO_EDGE = [(500, 2000, 4096), (1020, 1020, 1020), (2044, 2044, 2044), (700, 900, 3000), (100, 5000, 2048)]
+
+
+@pytest.mark.parametrize("shape", AUTO_EDGE, ids=[f"{m}x{n}x{k}" for m, n, k in AUTO_EDGE])
+def test_auto_plans_with_edge_tiles(sg, shape):
+    M, N, K = shape
+    say(f"[auto_edge] {shape}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 90 + M)
+    st, C, _ = run_lib(sg, VID["auto"], A, B, C0, 1.25, -0.5)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.25, -0.5, C0)
+    assert ok, info
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 95 + M, c0=False)
+    st, C, _ = run_lib(sg, VID["auto"], Ai, Bi, None, -1.0, 0.0)
+    assert st == 0
+    ok, info = check_full(C, Ai, Bi, -1.0, 0.0, None, exact=True)
+    assert ok, info
+
+
 # Row strides that 16-byte loads cannot take, on grids of few tiles: the
 # automatic plan splits K over the 4-byte-load tiles.
 UNALIGNED_FEW = [(4096, 17, 4096, None, None), (1000, 33, 3001, None, None), (300, 100, 2001, 2003, None),

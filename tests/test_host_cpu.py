@@ -333,7 +333,10 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     assert plan(6144, 3072, 512)[2] != sg.CFG_192x192_DL      # short K
     for shape in [(2048, 2048, 2048), (2048, 2048, 1024), (2048, 2048, 4096), (2048, 2048, 2044)]:
         assert plan(*shape)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL), shape
-    assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_PF2)
+    # Edge tiles (M, N multiples of 4): the 64x64 direct-to-LDS grid, here one
+    # round of 128x128 tiles in turn.
+    assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL)
+    assert plan(500, 2000, 4096)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL)
     # 64x64 grids spread unevenly over the CUs (1.2 times the mean or more)
     # with K >= 1536: back to configuration 4 with K split in 2 or 3.
     for shape, splits in [((1152, 1152, 4096), 3), ((1280, 1280, 2048), 3), ((1536, 1536, 4096), 3),
