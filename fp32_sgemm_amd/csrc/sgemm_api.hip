@@ -359,6 +359,27 @@ Plan round128_plan(const Plan &p, int M, int N, int K) {
 // Transposed operands use the same entries.
 Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, const float *B, int ldb);
 
+// An operand read along M or N whose extent is not a multiple of 4 (B as
+// given with N % 4 != 0, A transposed with M % 4 != 0) has 16-byte groups
+// straddling the edge of the last tiles, which load them element by element
+// on every slice; on a grid of one round those tiles set the time.  The
+// unsplit 64x64 grid with two slices in flight then splits K: in 3 up to 256
+// tiles, in 2 up to 512, with K of at least 2048 (same box, TFLOP/s, 1 -> 3
+// splits: 512 x 2047 x 4096 66.1 -> 113.2, 1000 x 1001 x 2048 60.7 -> 95.4,
+// 300 x 3001 x 4096 56.2 -> 87.9; 2048 x 1023 x 2048, 512 tiles, 96.7 -> 105.3
+// with 2; with K = 1024 or about 1000 tiles splits lost: 1024 x 1023 x 1024
+// 86.9 -> 73.3, 4000 x 999 x 2048 112.8 -> 105.1).
+Plan straddle_split_plan(const Plan &p, int ta, int tb, int M, int N, int K) {
+    if (p.variant != SGEMM_F32_MFMA_TUNED || p.config != 4 || p.splits > 1 || K < 2048) return p;
+    const bool straddle = (!tb && N % 4 != 0) || (ta && M % 4 != 0);
+    const int64_t tiles = sgemm::mfma_small_grid(M, N);
+    if (!straddle || tiles > 512) return p;
+    Plan q = p;
+    q.splits = tiles <= 256 ? 3 : 2;
+    if ((int64_t)q.splits * M * N * 4 > kMaxSplitBytes) return p;
+    return q;
+}
+
 // Operands that 16-byte loads cannot take, on a product of at least 2^32
 // FLOP: the operand (or both) is first copied into scratch rows padded to a
 // multiple of 4 floats, and the product runs the plan aligned operands get
@@ -438,7 +459,7 @@ Plan auto_plan(int ta, int tb, int M, int N, int K, const float *A, int lda, con
     p = big_tile_plan(quantization_plan(p, M, N, K), ta, tb, M, N, K, A, lda, B, ldb);
     p = round192_plan(p, ta, tb, M, N, K, A, lda, B, ldb);
     p = balance_split_plan(direct_lds_plan(p, ta, tb, M, N, K, A, lda, B, ldb), M, N, K);
-    return round128_plan(p, M, N, K);
+    return straddle_split_plan(round128_plan(p, M, N, K), ta, tb, M, N, K);
 }
 
 int to_status(hipError_t e) { return e == hipSuccess ? 0 : -static_cast<int>(e); }

@@ -112,6 +112,30 @@ def test_auto_plans_with_edge_tiles(sg, shape):
     assert ok, info
 
 
+# N not a multiple of 4 with B as given (16-byte groups straddle the N edge):
+# K split over a grid of one round; with an odd row stride of B as well, B is
+# first copied to aligned rows and the split partials share that scratch.
+STRADDLE = [(512, 2047, 4096, 2048), (300, 3001, 4096, None), (2048, 1023, 2048, 1024)]
+
+
+@pytest.mark.parametrize("case", STRADDLE, ids=[f"{c[0]}x{c[1]}x{c[2]}" for c in STRADDLE])
+def test_auto_straddling_edge_split(sg, case):
+    M, N, K, ldb = case
+    say(f"[straddle] {case}")
+    plan = sg.sgemm_f32_ex_plan(0, 0, M, N, K, 1.0, 256, K, 256, ldb or N)
+    assert plan[4] > 1, plan
+    A, B, C0 = _inputs(M, N, K, "uniform", 97 + M)
+    st, C, _ = run_lib(sg, VID["auto"], A, B, C0, 1.25, -0.5, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, A, B, 1.25, -0.5, C0)
+    assert ok, info
+    Ai, Bi, _ = _inputs(M, N, K, "int4", 98 + M, c0=False)
+    st, C, _ = run_lib(sg, VID["auto"], Ai, Bi, None, -1.0, 0.0, ldb=ldb)
+    assert st == 0
+    ok, info = check_full(C, Ai, Bi, -1.0, 0.0, None, exact=True)
+    assert ok, info
+
+
 # Row strides that 16-byte loads cannot take, on grids of few tiles: the
 # automatic plan splits K over the 4-byte-load tiles.
 UNALIGNED_FEW = [(4096, 17, 4096, None, None), (1000, 33, 3001, None, None), (300, 100, 2001, 2003, None),

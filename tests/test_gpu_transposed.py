@@ -140,6 +140,19 @@ def test_unaligned_operands_packed(sg, form):
     assert ok, info
 
 
+def test_transposed_a_straddling_edge_split(sg):
+    """A stored K x M with M not a multiple of 4 (its 16-byte groups straddle
+    the M edge): the automatic plan splits K."""
+    M, N, K = 2047, 512, 4096
+    say("[t_straddle] tn 2047x512x4096")
+    assert sg.sgemm_f32_ex_plan(1, 0, M, N, K, 1.0, 256, 2048, 256, N)[4] > 1
+    A, B, C0 = _inputs(M, N, K, "uniform", 27)
+    st, C, As, Bs = run_ex(sg, VID["auto"], 1, 0, A, B, C0, 0.75, 0.5, lda=2048)
+    assert st == 0
+    ok, info = check_op_full(C, As, Bs, 1, 0, 0.75, 0.5, C0)
+    assert ok, info
+
+
 @pytest.mark.parametrize("form", FORMS, ids=FORM_IDS)
 def test_beta_zero_ignores_nan_c(sg, form):
     ta, tb = form

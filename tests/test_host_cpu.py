@@ -315,8 +315,8 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     al = 0x100000
     plan = lambda M, N, K, ta=0, tb=0: sg.sgemm_f32_ex_plan(ta, tb, M, N, K, 1.0, al, M if ta else K, al,
                                                             K if tb else N)
-    # 64x64 tiles: loaded straight into LDS (configuration 9) when M and N are
-    # multiples of 64 and the grid has at most 1024 tiles (one round), else
+    # 64x64 tiles: loaded straight into LDS (configuration 9) when the grid has
+    # at most 1024 tiles (one round), edge tiles included, else
     # with two slices in flight.
     for shape in [(3500, 3500, 3500), (5000, 5000, 1000), (4608, 4608, 2048),
                   (7168, 7168, 1024), (2048, 2560, 2048), (2304, 2304, 4096), (2048, 3072, 1024),
@@ -337,6 +337,11 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     # round of 128x128 tiles in turn.
     assert plan(2040, 2048, 2048)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL)
     assert plan(500, 2000, 4096)[1:3] == (sg.MFMA_TUNED, sg.CFG_64x64_DL)
+    # N not a multiple of 4 with B as given: K split on one round of 64x64 tiles.
+    assert sg.sgemm_f32_ex_plan(0, 0, 512, 2047, 4096, 1.0, al, 4096, al, 2048)[1:] == (sg.MFMA_TUNED, 4, 8, 3)
+    assert sg.sgemm_f32_ex_plan(0, 0, 2048, 1023, 2048, 1.0, al, 2048, al, 1024)[4] == 2
+    assert sg.sgemm_f32_ex_plan(0, 0, 1024, 1023, 1024, 1.0, al, 1024, al, 1024)[4] == 1
+    assert sg.sgemm_f32_ex_plan(0, 1, 512, 2047, 4096, 1.0, al, 4096, al, 4096)[4] == 1
     # 64x64 grids spread unevenly over the CUs (1.2 times the mean or more)
     # with K >= 1536: back to configuration 4 with K split in 2 or 3.
     for shape, splits in [((1152, 1152, 4096), 3), ((1280, 1280, 2048), 3), ((1536, 1536, 4096), 3),

@@ -55,13 +55,15 @@ def _both(sg, A, B, C0, alpha, beta, stream):
 # M <= 16 split (scratch), a tuned split-K plan (scratch), the 64x64
 # direct-to-LDS grid (no scratch), the 4-byte-load tiles with K split (an
 # odd row stride of B or A), and operands copied to aligned scratch rows
-# before a 64x64 plan (odd row strides on a larger product).
+# before a 64x64 plan (odd row strides on a larger product), without and with
+# a K split whose partials share the copies' scratch.
 CASES = {
     "skinny": ((16, 4096, 4096), (8, 1000, 3000)),
     "splitk": ((512, 512, 8192), (256, 256, 4096)),
     "grid": ((1024, 1024, 1024), (256, 384, 512)),
     "unaligned": ((4096, 17, 4096), (1000, 33, 3001)),
     "packed": ((2047, 2047, 2047), (1500, 1600, 1999)),
+    "packed_split": ((300, 3001, 4096), (512, 2047, 4096)),
 }
 
 
@@ -73,7 +75,7 @@ def test_noalloc_matches_sgemm_f32(sg, case, dist):
         variant, config, splits = _plan(sg, M, N, K)
         say(f"[noalloc] {case} call {idx + 1}: {M}x{N}x{K} {dist} plan variant={variant} config={config} "
             f"splits={splits}")
-        if case in ("splitk", "unaligned"):
+        if case in ("splitk", "unaligned", "packed_split"):
             assert splits > 1, "the case needs a plan with a K split"
         A, B, C0 = _inputs(M, N, K, dist, 500 + 10 * idx + len(case))
         alpha, beta = (1.5, -0.5) if idx == 0 else (-1.0, 0.0)
