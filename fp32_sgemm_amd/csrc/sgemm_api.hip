@@ -301,8 +301,9 @@ Plan round192_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
     return Plan{SGEMM_F32_MFMA_TUNED, 10, 8, 1};
 }
 
-// A 64x64 grid that runs unevenly on the compute units (configuration 9: the
-// busiest CU holds at least kSplitImbalance times the mean number of tiles)
+// A 64x64 grid that runs unevenly on the compute units (configuration 9, or
+// 4 without a split: the busiest CU holds at least kSplitImbalance times the
+// mean number of tiles)
 // with K of at least kSplitMinK goes back to configuration 4 with K split in 2
 // or 3, whichever spreads the tile-splits more evenly (2 on a tie).  Same-box
 // TFLOP/s, configuration 9 -> split: 1152 x 1152 x 4096 88.9 -> 117.5 (3);
@@ -317,7 +318,11 @@ Plan round192_plan(const Plan &p, int ta, int tb, int M, int N, int K, const flo
 // 124.2 -> 120.4), and so did K below 1536 (1280^3 103.2 -> 96.3).  Through
 // the automatic plan on another box, against torch's FP32 mm (TFLOP/s):
 // 1152 x 1152 x 4096 119.8 / 112.4, 1536 x 1536 x 4096 124.8 / 132.7, 1792 x
-// 1792 x 4096 122.0 / 121.7, 1600 x 1600 x 4096 126.9 / 126.0.
+// 1792 x 4096 122.0 / 121.7, 1600 x 1600 x 4096 126.9 / 126.0.  The same
+// rule on an unsplit configuration-4 grid (extents that keep the
+// direct-to-LDS tiles out), same box: 131 x 6000 x 2048 49.6 -> 65.3 (3),
+// 1001 x 1500 x 2048 93.9 -> 110.0 (2), 3001 x 700 x 2000 90.0 -> 101.3 (3),
+// 601 x 2500 x 4096 98.0 -> 102.6 (3), 255 x 3000 x 4096 84.4 -> 86.1 (2).
 constexpr double kSplitImbalance = 1.2;
 constexpr int kSplitMinK = 1536;
 double cu_imbalance(int64_t units) {
@@ -325,8 +330,9 @@ double cu_imbalance(int64_t units) {
     return std::ceil(per) / per;
 }
 Plan balance_split_plan(const Plan &p, int M, int N, int K) {
-    if (p.variant != SGEMM_F32_MFMA_TUNED || p.config != 9 || p.splits > 1 || K < kSplitMinK) return p;
-    const int64_t tiles = sgemm::mfma_config_tiles(9, M, N);
+    if (p.variant != SGEMM_F32_MFMA_TUNED || (p.config != 9 && p.config != 4) || p.splits > 1 || K < kSplitMinK)
+        return p;
+    const int64_t tiles = sgemm::mfma_config_tiles(p.config, M, N);
     if (cu_imbalance(tiles) < kSplitImbalance) return p;
     const int splits = cu_imbalance(3 * tiles) < cu_imbalance(2 * tiles) ? 3 : 2;
     return Plan{SGEMM_F32_MFMA_TUNED, 4, p.group_m, splits};

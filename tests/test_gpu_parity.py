@@ -90,10 +90,11 @@ def test_skinny_shapes(sg, variant, shape):
     assert ok, info
 
 
-# Grids with edge tiles (M, N multiples of 4 but not of 64) through the
-# automatic plan: 64x64 direct-to-LDS tiles, one round of 128x128 ones, and a
-# K split where the 64x64 grid spreads unevenly.
-AUTO_EDGE = [(500, 2000, 4096), (1020, 1020, 1020), (2044, 2044, 2044), (700, 900, 3000), (100, 5000, 2048)]
+# Grids with edge tiles through the automatic plan: 64x64 direct-to-LDS tiles
+# (M, N multiples of 4), one round of 128x128 ones, and a K split where the
+# 64x64 grid spreads unevenly (also with odd M).
+AUTO_EDGE = [(500, 2000, 4096), (1020, 1020, 1020), (2044, 2044, 2044), (700, 900, 3000), (100, 5000, 2048),
+             (131, 6000, 2048), (1001, 1500, 2048)]
 
 
 @pytest.mark.parametrize("shape", AUTO_EDGE, ids=[f"{m}x{n}x{k}" for m, n, k in AUTO_EDGE])

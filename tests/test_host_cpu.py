@@ -342,6 +342,10 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     assert sg.sgemm_f32_ex_plan(0, 0, 2048, 1023, 2048, 1.0, al, 2048, al, 1024)[4] == 2
     assert sg.sgemm_f32_ex_plan(0, 0, 1024, 1023, 1024, 1.0, al, 1024, al, 1024)[4] == 1
     assert sg.sgemm_f32_ex_plan(0, 1, 512, 2047, 4096, 1.0, al, 4096, al, 4096)[4] == 1
+    # An unevenly spread 64x64 grid that cannot take the direct-to-LDS tiles (M
+    # odd): split as configuration 9 grids are.
+    assert plan(131, 6000, 2048)[1:] == (sg.MFMA_TUNED, 4, 8, 3)
+    assert plan(2001, 1000, 1600)[4] == 1
     # 64x64 grids spread unevenly over the CUs (1.2 times the mean or more)
     # with K >= 1536: back to configuration 4 with K split in 2 or 3.
     for shape, splits in [((1152, 1152, 4096), 3), ((1280, 1280, 2048), 3), ((1536, 1536, 4096), 3),
