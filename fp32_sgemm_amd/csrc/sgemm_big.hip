@@ -40,9 +40,10 @@
 //   which read rows k and k + 8 at the same x, fall in opposite halves of the
 //   bank space (every row length here is a multiple of the 64 banks).
 //
-// Edges.  M, N and K are multiples of 4, so a 16-byte group never straddles
-// an edge.  Tiles that cross M or N give each group outside M or N an
-// out-of-range lane offset: the load writes zeros to LDS without touching
+// Edges.  K, and the x extent of an operand stored along x, are multiples of
+// 4, so a 16-byte group never straddles an edge (groups of an operand stored
+// along k lie in one row, whole rows past its x edge).  Tiles that cross M or
+// N give each group outside M or N an out-of-range lane offset: the load writes zeros to LDS without touching
 // memory (adding exact zeros changes no sum).  When K is not a multiple of 16
 // the loads of the partial last slice do the same for groups past K; they are
 // issued by the last iterations of the slice loop, which run a copy of the loop
@@ -498,11 +499,14 @@ bool aligned16(const void *p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0;
 
 }  // namespace
 
-// M, N and K multiples of 4 (the 16-byte groups never straddle an edge),
-// 16-byte aligned operands with row strides that are multiples of 4, and
-// operand slices that fit the 32-bit buffer offsets.
+// K, and the extent of each operand stored along x (M of A given
+// transposed, N of B as given), multiples of 4, so that no 16-byte group
+// straddles an edge (an operand stored along k has whole rows past its x
+// edge, which read as zeros, so its x extent may be anything); 16-byte
+// aligned operands with row strides that are multiples of 4, and operand
+// slices that fit the 32-bit buffer offsets.
 bool big_tile_fits(const GemmArgs &g) {
-    if (g.M % 4 || g.N % 4 || g.K % 4 || g.K < 4) return false;
+    if ((g.trans_a && g.M % 4) || (!g.trans_b && g.N % 4) || g.K % 4 || g.K < 4) return false;
     if (!aligned16(g.A) || !aligned16(g.B) || g.lda % 4 || g.ldb % 4) return false;
     const int64_t lim = (int64_t)1 << 31;
     // (the spans of 256-wide tiles bound those of 128-wide ones)

@@ -127,8 +127,9 @@ enum sgemm_f32_config_id {
     SGEMM_F32_CFG_128x128_STREAMK = 5, /* 128x128, persistent with stream-K; 16-byte loads only */
     SGEMM_F32_CFG_64x64_BK64 = 6, /* 64x64, slices of 64, two in flight; 16-byte loads only */
     SGEMM_F32_CFG_256x256 = 7,    /* 256x256, one work-group per CU, operands loaded straight into
-                                     LDS; M, N and K multiples of 4 (edge tiles read zeros past
-                                     the matrices), 16-byte loads, no K split, group_m ignored
+                                     LDS; K and the extent of an operand read along M or N
+                                     multiples of 4 (edge tiles read zeros past the matrices),
+                                     16-byte loads, no K split, group_m ignored
                                      (4 is used) */
     SGEMM_F32_CFG_128x128_DL = 8, /* 128x128 by the kernel of configuration 7, two work-groups per
                                      CU; its conditions, no K split */
@@ -278,8 +279,9 @@ int sgemm_f32_ex_select(int trans_a, int trans_b, int M, int N, int K, float alp
  * the call's scratch (2 * 128 * 128 floats per resident work-group, 64 MiB
  * on MI355X) when tiles are shared.
  * Configuration 7 computes 256 x 256 tiles, one work-group per compute unit,
- * with the operands copied from memory straight into LDS.  It needs M, N and K
- * multiples of 4, the 16-byte-load conditions, 256 stored rows of an operand
+ * with the operands copied from memory straight into LDS.  It needs K, M of A
+ * given transposed and N of B as given multiples of 4 (M of A as given and N
+ * of B given transposed may be anything), the 16-byte-load conditions, 256 stored rows of an operand
  * read along k (16 of one read along M or N) spanning less than 2 GiB, and 256
  * rows of C spanning less than 2 GiB; SGEMM_F32_ERR_NOT_APPLICABLE otherwise.
  * It takes no split count (splits must be 1) and ignores the grouping.  The

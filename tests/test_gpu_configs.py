@@ -264,6 +264,30 @@ def test_streamk_repeat_bitwise_identical(sg):
 # past the end.
 # ---------------------------------------------------------------------------
 BIG_CFGS = [7, 8, 9, 10]
+
+# Extents that are not multiples of 4 on operands stored along k (M of A as
+# given, N of B given transposed): (form, M, N, K).  Rows past the edge read
+# as zeros; the other extents stay multiples of 4.
+ODD_KROWS = [((0, 0), 257, 512, 64), ((0, 1), 131, 133, 36), ((0, 0), 511, 260, 1028), ((0, 1), 258, 515, 48),
+             ((1, 1), 256, 515, 20), ((0, 0), 1, 388, 16), ((1, 1), 200, 3, 100)]
+
+
+@pytest.mark.parametrize("cfg", BIG_CFGS)
+@pytest.mark.parametrize("case", ODD_KROWS, ids=[f"{FORM_IDS[2 * f[0] + f[1]]}-{m}x{n}x{k}" for f, m, n, k in ODD_KROWS])
+def test_big_configs_odd_extents_along_k(sg, cfg, case):
+    (ta, tb), M, N, K = case
+    say(f"[big_odd] cfg {cfg} {case}")
+    A, B, C0 = _inputs(M, N, K, "uniform", 40 + M + N)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, 1.5, -0.5, C0, exact=False)
+    assert ok, info
+    Ai, Bi, Ci = _inputs(M, N, K, "int4", 50 + M + N)
+    st, C, As, Bs = run_cfg(sg, cfg, 8, 1, ta, tb, Ai, Bi, Ci, -1.0, 1.0)
+    assert st == 0
+    ok, info = check(C, As, Bs, ta, tb, -1.0, 1.0, Ci, exact=True)
+    assert ok, info
+
 BIG_SHAPES = [(256, 512, 16), (512, 256, 48), (768, 512, 272), (512, 768, 1024), (128, 384, 32),
               (64, 192, 64),
               # edge tiles: M, N not multiples of the tile, K not of 16 (multiples of 4)
@@ -356,10 +380,12 @@ def test_big_kernel_padded_strides(sg, cfg, form):
 
 @pytest.mark.parametrize("cfg", BIG_CFGS)
 def test_big_kernel_rejects_what_it_cannot_cover(sg, cfg):
-    """M, N or K not a multiple of 4: refused before any launch."""
-    A, B, C0 = _inputs(258, 256, 64, "uniform", 913)
-    st, _, _, _ = run_cfg(sg, cfg, 8, 1, 0, 0, A, B, C0, 1.0, 0.0)
-    assert st == sg.ERR_NOT_APPLICABLE
+    """K, or the extent of an operand stored along M or N (N of B as given,
+    M of A given transposed), not a multiple of 4: refused before any launch."""
+    for (ta, tb), (M, N, K) in (((0, 0), (256, 258, 64)), ((1, 1), (258, 256, 64)), ((0, 1), (256, 256, 66))):
+        A, B, C0 = _inputs(M, N, K, "uniform", 913)
+        st, _, _, _ = run_cfg(sg, cfg, 8, 1, ta, tb, A, B, C0, 1.0, 0.0)
+        assert st == sg.ERR_NOT_APPLICABLE, (ta, tb, M, N, K)
 
 
 @pytest.mark.parametrize("cfg", BIG_CFGS)

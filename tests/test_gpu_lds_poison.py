@@ -83,6 +83,22 @@ def test_poisoned_direct_lds_kernel(plib, cfg, form, shape):
     assert ok, info
 
 
+# Extents that are not multiples of 4 on operands stored along k: (form, M, N, K).
+ODD_KROWS = [((0, 0), 257, 512, 64), ((0, 1), 131, 133, 36), ((1, 1), 256, 515, 20), ((0, 0), 511, 260, 1028)]
+
+
+@pytest.mark.parametrize("cfg", [7, 8, 9, 10])
+@pytest.mark.parametrize("case", ODD_KROWS, ids=[f"{FORM_IDS[2 * f[0] + f[1]]}-{m}x{n}x{k}" for f, m, n, k in ODD_KROWS])
+def test_poisoned_direct_lds_kernel_odd_extents(plib, cfg, case):
+    (ta, tb), M, N, K = case
+    say(f"[poison_big_odd] cfg {cfg} {case}")
+    A, B, C0 = _int_inputs(M, N, K, 1550 + M + N)
+    st, C = _run_config(plib, cfg, 8, 1, ta, tb, A, B, C0, 1.5, -0.5)
+    assert st == 0
+    ok, info = _exact(C, A, B, 1.5, -0.5, C0)
+    assert ok, info
+
+
 @pytest.mark.parametrize("cfg", [7, 8, 9, 10])
 @pytest.mark.parametrize("K", [65536, 65540])
 def test_poisoned_direct_lds_kernel_long_k(plib, cfg, K):

@@ -360,15 +360,18 @@ def test_small_tiles_for_poorly_filled_rounds(sg):
     for shape in [(2048, 2048, 2048), (1024, 4096, 4096), (4096, 1024, 4096), (2048, 2048, 1024)]:
         assert plan(*shape)[1:] == (sg.MFMA_TUNED, sg.CFG_128x128_DL, 8, 1), shape
     assert plan(3000, 3000, 3000, 1, 1)[1:3] == (sg.MFMA_TUNED, sg.CFG_192x192_DL)
-    assert plan(3002, 3000, 3000)[1:3] != (sg.MFMA_TUNED, sg.CFG_192x192_DL)   # M not a multiple of 4
+    assert plan(3000, 3002, 3000)[1:3] != (sg.MFMA_TUNED, sg.CFG_192x192_DL)   # N of B as given not a multiple of 4
+    assert plan(3002, 3000, 3000)[1:3] == (sg.MFMA_TUNED, sg.CFG_192x192_DL)   # M of A as given: rows read as zero
     for shape in [(6144, 6144, 2048), (4096, 11008, 512), (10240, 10240, 1024), (2816, 2816, 2816)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
     for shape in [(7000, 7000, 1024), (7040, 7000, 1024), (10000, 10000, 1024)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
     for shape in [(7040, 7040, 1000), (7000, 7000, 1000)]:
         assert plan(*shape)[2] == sg.CFG_128x128_DL, shape
-    # M not a multiple of 4: the register-staged 128x128 kernel
-    assert plan(7002, 7000, 1024)[1:3] == (sg.MFMA_LARGE, sg.CFG_128x128)
+    # N of B as given not a multiple of 4: the register-staged 128x128 kernel;
+    # M of A as given may be anything.
+    assert plan(7000, 7002, 1024)[1:3] == (sg.MFMA_LARGE, sg.CFG_128x128)
+    assert plan(7002, 7000, 1024)[1:3] == (sg.MFMA_TUNED, sg.CFG_128x128_DL)
     # Well-filled 256x256 grids take the larger tile.
     for shape in [(4096, 4096, 4096), (8192, 8192, 8192), (4092, 4092, 4092)]:
         assert plan(*shape)[2] == sg.CFG_256x256, shape
@@ -575,14 +578,17 @@ def test_big_tiles_for_whole_filled_grids(sg):
     # Edge tiles are covered when M, N and K are multiples of 4 (4092^3: 16 x 16 tiles, the last 252 wide).
     assert plan(0, 0, 4092, 4092, 4092, 4092, 4092)[2] == sg.CFG_256x256
     assert plan(1, 1, 4092, 4092, 4092, 4092, 4092)[2] == sg.CFG_256x256
-    # M, N or K not a multiple of 4, misaligned, too few or poorly filled rounds.
-    assert plan(0, 0, 4094, 4096, 4096, 4096, 4096)[2] != sg.CFG_256x256
+    # N of B as given, M of A transposed or K not a multiple of 4, misaligned,
+    # too few or poorly filled rounds; M of A as given may be anything.
+    assert plan(0, 0, 4096, 4094, 4096, 4096, 4096)[2] != sg.CFG_256x256
+    assert plan(1, 0, 4094, 4096, 4096, 4096, 4096)[2] != sg.CFG_256x256
+    assert plan(0, 0, 4094, 4096, 4096, 4096, 4096)[2] == sg.CFG_256x256
     assert plan(0, 0, 4096, 4096, 4098, 4098, 4096)[2] != sg.CFG_256x256
     assert sg.sgemm_f32_ex_plan(0, 0, 4096, 4096, 4100, 1.0, al + 4, 4100, al, 4096)[1] == sg.MFMA_SCALAR
     assert plan(0, 0, 2048, 2048, 2048, 2048, 2048)[2] != sg.CFG_256x256
     assert plan(0, 0, 6144, 6144, 2048, 2048, 6144)[2] != sg.CFG_256x256     # 576 tiles: 75 % of 3 rounds
     p = 0x100000
-    for M, N, K in ((4094, 4096, 4096), (4096, 4098, 4096), (4096, 4096, 4098), (4096, 4096, 2)):
+    for M, N, K in ((4096, 4094, 4096), (4096, 4098, 4096), (4096, 4096, 4098), (4096, 4096, 2)):
         assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, M, N, K, 1.0, p, K + K % 4, p, N + N % 4, 0.0, p, N, 0) \
             == sg.ERR_NOT_APPLICABLE, (M, N, K)
     assert sg.sgemm_f32_ex_config(7, 8, 1, 0, 0, 512, 512, 64, 1.0, p + 4, 64, p, 512, 0.0, p, 512, 0) \
